@@ -1,0 +1,196 @@
+/*
+ * lmoe.h — C ABI of the latent-MoE feed-forward block for AMD Instinct MI355X (gfx950).
+ *
+ * The block is the one the Edge0-145B model-detail page describes in section "模型架构"
+ * (Fig. 3 caption and the paragraph after it): a per-layer matrix D projects each token's
+ * hidden state (2560-d) to the latent width l (1792); a router picks top_k (10) of
+ * n_experts (512) experts; each picked expert is a SwiGLU l -> ffn (640) -> l; one shared
+ * expert runs alongside; the merged result is projected back to the hidden width by the
+ * per-layer matrix U.  Only the experts live in latent space; D and U are shared by all of
+ * a layer's experts.
+ *
+ * Readings where the page is silent (stated once here, used by every call):
+ *   - router logits = z . Wr^T + br (br optional), computed from the fp32 latent z;
+ *   - top_k selection: largest logits, a lower expert id wins an exact tie; the ids of a
+ *     token are returned in ascending expert id;
+ *   - routing weights = softmax over the top_k selected logits (equivalently a softmax over
+ *     all experts renormalised over the selected ones), so they sum to 1;
+ *   - SwiGLU(z) = (SiLU(z gate^T) * (z up^T)) down^T, SiLU(v) = v / (1 + exp(-v)), no biases;
+ *   - shared expert: weight 1, added to the routed sum before U;
+ *   - merged m_t = shared_t + sum over slots (ascending expert id) of w_{t,s} * expert_s(z_t).
+ *
+ * Conventions for every call
+ *   - Every tensor argument is a caller-owned DEVICE pointer, row-major with the innermost
+ *     dimension contiguous, 16-byte aligned.  Every weight matrix is stored output-major
+ *     with its reduction dimension contiguous:
+ *         D  [latent][hidden]     U  [hidden][latent]     Wr [n_experts][latent]
+ *   - An expert record (routed experts and the shared expert) is contiguous:
+ *         F32/BF16: gate [ffn][latent], up [ffn][latent], down [latent][ffn] elements;
+ *         MXFP4 (routed experts only): gate nibbles [ffn][latent/2], up nibbles
+ *             [ffn][latent/2], down nibbles [latent][ffn/2], then gate scales
+ *             [ffn][latent/32], up scales [ffn][latent/32], down scales [latent][ffn/32].
+ *             Elements are OCP MX FP4 E2M1 (low nibble = even K index), one E8M0 scale
+ *             byte (value 2^(byte-127)) per 32 consecutive K values.
+ *     Routed experts are n_experts records back to back.  The shared expert record uses
+ *     the dense dtype and shared_ffn in place of ffn.
+ *   - BF16 tensors hold raw bf16 bit patterns (uint16).
+ *   - All calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the
+ *     null stream), allocate nothing, never synchronise, keep no per-call state, and may be
+ *     captured into a HIP graph.  Calls that share a workspace must be ordered.
+ *   - Arguments are validated on the host before anything is enqueued.  On an error
+ *     nothing is enqueued and no output is touched; lmoe_last_error() describes it.
+ *     Launch failures reported by the HIP runtime map to LMOE_ERR_HIP.  Faults that
+ *     happen while kernels run surface at the caller's next synchronisation.
+ *   - NaN/Inf inputs are not checked; outputs are then undefined, but every kernel stays
+ *     within the bounds of the buffers described here.
+ *   - For identical inputs, configuration, T and device, outputs are bitwise identical
+ *     (no floating-point atomics, fixed reduction orders).
+ *
+ * Supported dtype combinations (others return LMOE_ERR_UNSUPPORTED):
+ *   act F32,  dense F32,  expert F32     (plain fp32 path)
+ *   act BF16, dense BF16, expert BF16    (bf16 storage, fp32 accumulation)
+ *   act BF16, dense BF16, expert MXFP4
+ * Dimension limits: hidden, latent, ffn, shared_ffn multiples of 64 (shared_ffn may be 0);
+ * 1 <= top_k <= 16; top_k <= n_experts <= 1024; 0 <= T <= 2^20 with T*top_k < 2^31.
+ */
+#ifndef LMOE_H
+#define LMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LMOE_OK = 0,
+    LMOE_ERR_NULL = 1,        /* a required pointer is NULL */
+    LMOE_ERR_SHAPE = 2,       /* a dimension is out of range or inconsistent */
+    LMOE_ERR_DTYPE = 3,       /* an unknown dtype code */
+    LMOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    LMOE_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the size query returns */
+    LMOE_ERR_UNSUPPORTED = 6, /* valid but unsupported combination (dtypes, options) */
+    LMOE_ERR_HIP = 7          /* the HIP runtime reported an error while enqueuing */
+} lmoe_status;
+
+typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1, LMOE_MXFP4 = 2 } lmoe_dtype;
+
+typedef struct {
+    int32_t hidden;       /* H: token width outside the expert pool (2560) */
+    int32_t latent;       /* l: latent width (1792) */
+    int32_t n_experts;    /* E: routed experts per layer (512) */
+    int32_t top_k;        /* k: routed experts per token (10) */
+    int32_t ffn;          /* F: routed expert SwiGLU width (640) */
+    int32_t shared_ffn;   /* shared expert SwiGLU width (640); 0 = no shared expert */
+    int32_t act_dtype;    /* lmoe_dtype of x, y (and of the block's internal activations) */
+    int32_t dense_dtype;  /* lmoe_dtype of D, U, Wr and the shared expert */
+    int32_t expert_dtype; /* lmoe_dtype of the routed expert records */
+} lmoe_config;
+
+typedef struct {
+    const void* D;        /* [latent][hidden], dense dtype */
+    const void* U;        /* [hidden][latent], dense dtype */
+    const void* Wr;       /* [n_experts][latent], dense dtype */
+    const float* br;      /* [n_experts] fp32 router bias, or NULL for none */
+    const void* shared;   /* one record (dense dtype, shared_ffn), or NULL iff shared_ffn == 0 */
+    const void* experts;  /* n_experts records (expert dtype) */
+} lmoe_weights;
+
+/* Stages of lmoe_forward, in launch order (for lmoe_forward_opts.stage_events). */
+typedef enum {
+    LMOE_STAGE_PRENORM = 0,     /* RMSNorm of the fp32 residual into the bf16 block input */
+    LMOE_STAGE_D = 1,           /* z = x D^T */
+    LMOE_STAGE_ROUTER = 2,      /* logits = z Wr^T + br */
+    LMOE_STAGE_TOPK = 3,        /* top_k + softmax over the kept logits */
+    LMOE_STAGE_PERMUTE = 4,     /* token -> expert segments and the work list */
+    LMOE_STAGE_EXPERT_UP = 5,   /* fused SwiGLU gate/up of every segment (shared expert included) */
+    LMOE_STAGE_EXPERT_DOWN = 6, /* down projections */
+    LMOE_STAGE_COMBINE = 7,     /* weighted merge */
+    LMOE_STAGE_U = 8,           /* y = m U^T */
+    LMOE_N_STAGES = 9
+} lmoe_stage;
+
+typedef struct {
+    /* prenorm = 1: x is an fp32 residual stream h [T][hidden]; the block input is
+     * bf16(RMSNorm(h)) with unit gain and eps 1e-6 (requires act BF16). */
+    int32_t prenorm;
+    /* residual = 1: y is fp32 [T][hidden] and is updated in place, y += block output.
+     * With prenorm and residual both set, x and y may be the same buffer. */
+    int32_t residual;
+    /* Optional exports (NULL = skip), all device buffers: */
+    float* aux_z;          /* [T][latent] fp32 latent z = x D^T (router input) */
+    int32_t* aux_ids;      /* [T][top_k] chosen experts, ascending id */
+    float* aux_w;          /* [T][top_k] routing weights, same order */
+    int32_t* aux_offsets;  /* [n_experts + 1] segment starts of the permutation */
+    int32_t* aux_perm;     /* [T * top_k] the permutation (see lmoe_permute) */
+    /* Optional timing hook: NULL, or an array of 2 * LMOE_N_STAGES hipEvent_t handles
+     * (created by the caller; NULL entries are skipped).  Event 2s is recorded on `stream`
+     * just before stage s is enqueued and event 2s+1 just after it; under stream capture
+     * they are recorded as external event nodes, so each graph replay re-records them. */
+    void* const* stage_events;
+} lmoe_forward_opts;
+
+/* Bytes of one routed expert record (shared = 0) or of the shared expert record (shared = 1).
+ * Returns 0 for an invalid configuration. */
+size_t lmoe_expert_record_bytes(const lmoe_config* cfg, int32_t shared);
+
+/* Workspace bytes lmoe_forward needs for T tokens (monotone in T). */
+lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes);
+
+/* Workspace bytes lmoe_permute needs for T tokens. */
+lmoe_status lmoe_permute_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes);
+
+/*
+ * Router (page: "the router picks 10 of 512 experts", Fig. 3 caption).
+ *   z   [T][latent] fp32 latent states;
+ *   ids [T][top_k] int32 out: the top_k experts of each token, ascending id;
+ *   w   [T][top_k] fp32 out: softmax over the selected logits, same order.
+ * Uses weights->Wr (dense dtype) and weights->br (may be NULL); other weight pointers are
+ * ignored.  ws/ws_bytes: workspace of at least T * n_experts * 4 bytes, where the logits are
+ * staged (lmoe_workspace_bytes(cfg, T) is always enough).
+ */
+lmoe_status lmoe_route(const lmoe_config* cfg, const lmoe_weights* weights, const float* z, int32_t T,
+                       int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Token -> expert permutation used to group each expert's tokens into one contiguous
+ * segment.  Flat slot index f = t*top_k + s.
+ *   ids     [T][top_k] int32 in: expert of each slot; the ids of one token must be distinct.
+ *   offsets [n_experts + 1] int32 out: offsets[e] = first position of expert e's segment
+ *           (exclusive prefix sum of the per-expert counts), offsets[n_experts] = number of
+ *           valid slots;
+ *   perm    [T*top_k] int32 out: perm[p] = the slot f at position p; inside a segment the
+ *           slots are in ascending f (a stable sort, so the result is unique);
+ *   inv     [T*top_k] int32 out: inv[f] = p with perm[p] = f.
+ * Slots whose id is outside [0, n_experts) are dropped: inv = -1 for them and positions
+ * at or after offsets[n_experts] hold -1.  Duplicate ids inside one token give undefined
+ * (but in-bounds) contents.
+ */
+lmoe_status lmoe_permute(const lmoe_config* cfg, const int32_t* ids, int32_t T, int32_t* offsets, int32_t* perm,
+                         int32_t* inv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole block for T tokens.
+ *   x [T][hidden] in: act dtype (fp32 when opts->prenorm);
+ *   y [T][hidden] out: act dtype, or fp32 accumulated in place when opts->residual.
+ * x and y must not overlap, except x == y with prenorm and residual both set.
+ * opts may be NULL (plain block, no exports).  ws: lmoe_workspace_bytes(cfg, T) bytes.
+ */
+lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* weights, const void* x, int32_t T, void* y,
+                         const lmoe_forward_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* lmoe_status_str(lmoe_status status);
+
+/* Text of the last error reported by a call on this thread ("" if none). */
+const char* lmoe_last_error(void);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int32_t lmoe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMOE_H */

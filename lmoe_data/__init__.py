@@ -83,7 +83,7 @@ WORKLOADS = {
     "prefill_t4096": Workload(3, "prefill_t4096", EDGE0_145B, 4096, "bf16", "bf16", "bf16", "zero"),
     "prefill_t16384": Workload(4, "prefill_t16384", EDGE0_145B, 16384, "bf16", "bf16", "bf16", "zipf"),
     "stack48_mxfp4_t8": Workload(5, "stack48_mxfp4_t8", EDGE0_145B, 8, "bf16", "bf16", "mxfp4", "zipf",
-                                 layers=48, expert_banks=4),
+                                 layers=48, expert_banks=2),
 }
 
 
@@ -204,9 +204,31 @@ def router_bias(wl: Workload, layer: int) -> np.ndarray:
     return (-wl.zipf_s * np.log1p(pi.astype(np.float64))).astype(np.float32)
 
 
-def make_layer(wl: Workload, layer: int = 0, threads: Optional[int] = None) -> LayerWeights:
+def make_experts(wl: Workload, bank: int, threads: Optional[int] = None) -> np.ndarray:
+    """All routed expert records of one layer (or expert bank): [E][record]."""
     s = wl.shape
-    H, L, E, F = s.hidden, s.latent, s.n_experts, s.ffn
+    rec0 = expert_record(s, rng_for(wl.wid, bank, T_EXPERT, 0), wl.expert)
+    experts = np.empty((s.n_experts, rec0.size), dtype=rec0.dtype)
+    experts[0] = rec0
+
+    def fill(e):
+        experts[e] = expert_record(s, rng_for(wl.wid, bank, T_EXPERT, e), wl.expert)
+
+    with ThreadPoolExecutor(threads or n_threads()) as ex:
+        list(ex.map(fill, range(1, s.n_experts)))
+    return experts
+
+
+def expert_bank(wl: Workload, layer: int) -> int:
+    return layer % wl.expert_banks if wl.expert_banks else layer
+
+
+def make_layer(wl: Workload, layer: int = 0, threads: Optional[int] = None,
+               experts: Optional[np.ndarray] = None) -> LayerWeights:
+    """One layer's weights.  `experts` may pass in the already drawn records of this layer's
+    expert bank (expert_bank(wl, layer)) so that banks shared by several layers are drawn once."""
+    s = wl.shape
+    H, L, E = s.hidden, s.latent, s.n_experts
     D = _encode(normal_f32(rng_for(wl.wid, layer, T_D), L * H, 1.0 / np.sqrt(H)), wl.dense).reshape(L, H)
     U = _encode(normal_f32(rng_for(wl.wid, layer, T_U), H * L, 1.0 / np.sqrt(L)), wl.dense).reshape(H, L)
     Wr = _encode(normal_f32(rng_for(wl.wid, layer, T_WR), E * L, 1.0 / np.sqrt(L)), wl.dense).reshape(E, L)
@@ -214,16 +236,9 @@ def make_layer(wl: Workload, layer: int = 0, threads: Optional[int] = None) -> L
     shared = None
     if s.shared_ffn > 0:
         shared = expert_record(s, rng_for(wl.wid, layer, T_SHARED), wl.dense, ffn=s.shared_ffn)
-    bank = layer % wl.expert_banks if wl.expert_banks else layer
-    rec0 = expert_record(s, rng_for(wl.wid, bank, T_EXPERT, 0), wl.expert)
-    experts = np.empty((E, rec0.size), dtype=rec0.dtype)
-    experts[0] = rec0
-
-    def fill(e):
-        experts[e] = expert_record(s, rng_for(wl.wid, bank, T_EXPERT, e), wl.expert)
-
-    with ThreadPoolExecutor(threads or n_threads()) as ex:
-        list(ex.map(fill, range(1, E)))
+    bank = expert_bank(wl, layer)
+    if experts is None:
+        experts = make_experts(wl, bank, threads)
     return LayerWeights(s, wl.dense, wl.expert, D, U, Wr, br, shared, experts,
                         meta={"workload": wl.name, "layer": layer, "bank": bank})
 

@@ -158,6 +158,16 @@ class Layer:
             self._cache[e] = expert_matrices(self._lw.experts[e], self._lw.expert, s.latent, s.ffn)
         return self._cache[e]
 
+    def prefetch(self, experts, threads: int = 8):
+        """Decode the given experts up front, several at a time (decoding only; no arithmetic
+        of the block)."""
+        from concurrent.futures import ThreadPoolExecutor
+        todo = sorted(set(int(e) for e in np.asarray(experts).ravel()) - set(self._cache))
+        s = self.shape
+        with ThreadPoolExecutor(threads) as ex:
+            mats = list(ex.map(lambda e: expert_matrices(self._lw.experts[e], self._lw.expert, s.latent, s.ffn), todo))
+        self._cache.update(zip(todo, mats))
+
 
 def block_forward(layer: Layer, x: np.ndarray, forced_ids: dict | None = None):
     """The latent-MoE block for the tokens in x (float64 [T][hidden]).

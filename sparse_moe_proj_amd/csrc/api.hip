@@ -1,0 +1,348 @@
+// C ABI of the latent-MoE block: argument validation, workspace layout and launch order.
+// Everything here runs on the host and only enqueues work on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "lmoe.h"
+
+using namespace lmoe;
+
+namespace {
+
+thread_local std::string g_err;
+
+lmoe_status fail(lmoe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+lmoe_status hip_fail(hipError_t e, const char* where) {
+    return fail(LMOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+struct Dims {
+    int H, L, E, k, F, Fs;
+    bool f32;  // fp32 storage end to end
+    bool mx;   // MXFP4 routed experts
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+lmoe_status check_config(const lmoe_config* cfg, Dims& d) {
+    if (!cfg) return fail(LMOE_ERR_NULL, "cfg is NULL");
+    const int a = cfg->act_dtype, dn = cfg->dense_dtype, ex = cfg->expert_dtype;
+    if (a < 0 || a > 2 || dn < 0 || dn > 2 || ex < 0 || ex > 2) return fail(LMOE_ERR_DTYPE, "unknown dtype code");
+    const bool f32 = a == LMOE_F32 && dn == LMOE_F32 && ex == LMOE_F32;
+    const bool bf = a == LMOE_BF16 && dn == LMOE_BF16 && (ex == LMOE_BF16 || ex == LMOE_MXFP4);
+    if (!f32 && !bf)
+        return fail(LMOE_ERR_UNSUPPORTED, "dtype combination act=%d dense=%d expert=%d is not supported", a, dn, ex);
+    d.H = cfg->hidden;
+    d.L = cfg->latent;
+    d.E = cfg->n_experts;
+    d.k = cfg->top_k;
+    d.F = cfg->ffn;
+    d.Fs = cfg->shared_ffn;
+    d.f32 = f32;
+    d.mx = ex == LMOE_MXFP4;
+    if (d.H <= 0 || d.L <= 0 || d.F <= 0 || d.H % 64 || d.L % 64 || d.F % 64)
+        return fail(LMOE_ERR_SHAPE, "hidden, latent and ffn must be positive multiples of 64 (got %d, %d, %d)", d.H, d.L,
+                    d.F);
+    if (d.Fs < 0 || d.Fs % 64) return fail(LMOE_ERR_SHAPE, "shared_ffn must be 0 or a multiple of 64 (got %d)", d.Fs);
+    if (d.k < 1 || d.k > 16) return fail(LMOE_ERR_SHAPE, "top_k must be in [1, 16] (got %d)", d.k);
+    if (d.E < d.k || d.E > 1024) return fail(LMOE_ERR_SHAPE, "n_experts must be in [top_k, 1024] (got %d)", d.E);
+    if ((long)d.H * d.L > (1L << 30) || (long)d.F * d.L > (1L << 30) || (long)d.Fs * d.L > (1L << 30))
+        return fail(LMOE_ERR_SHAPE, "a weight matrix exceeds 2^30 elements");
+    return LMOE_OK;
+}
+
+lmoe_status check_T(const Dims& d, int32_t T) {
+    if (T < 0 || T > (1 << 20)) return fail(LMOE_ERR_SHAPE, "T must be in [0, 2^20] (got %d)", T);
+    if ((long)T * d.k >= (1L << 31) - (1L << 24)) return fail(LMOE_ERR_SHAPE, "T * top_k too large");
+    return LMOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t x16, z32, z16, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, m, total;
+    bool stream_path;
+    int max_tiles, BM, Hs, R;
+};
+
+Layout plan(const Dims& d, int T) {
+    Layout lo{};
+    const size_t act = d.f32 ? 4 : 2;
+    const int has_shared = d.Fs > 0;
+    lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx);
+    lo.BM = expert_tile_rows(lo.stream_path);
+    lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path);
+    lo.Hs = std::max(d.F, d.Fs);
+    lo.R = T * d.k + (has_shared ? T : 0);
+    const size_t nb = (size_t)perm_blocks(T);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += up(bytes);
+        return at;
+    };
+    lo.x16 = take(d.f32 ? 0 : (size_t)T * d.H * 2);
+    lo.z32 = take((size_t)T * d.L * 4);
+    lo.z16 = take(d.f32 ? 0 : (size_t)T * d.L * 2);
+    lo.logits = take((size_t)T * d.E * 4);
+    lo.ids = take((size_t)T * d.k * 4);
+    lo.w = take((size_t)T * d.k * 4);
+    lo.offsets = take((size_t)(d.E + 1) * 4);
+    lo.perm = take((size_t)T * d.k * 4);
+    lo.inv = take((size_t)T * d.k * 4);
+    lo.hist = take(nb * d.E * 4);
+    lo.base = take(nb * d.E * 4);
+    lo.tiles = take((size_t)lo.max_tiles * sizeof(Tile));
+    lo.ntiles = take(4);
+    lo.H = take((size_t)lo.R * lo.Hs * act);
+    lo.Y = take((size_t)lo.R * d.L * 4);
+    lo.m = take((size_t)T * d.L * act);
+    lo.total = o;
+    return lo;
+}
+
+size_t permute_ws(const Dims& d, int T) {
+    const size_t nb = (size_t)perm_blocks(T);
+    return nb <= 1 ? 0 : 2 * up(nb * d.E * 4);
+}
+
+size_t record_bytes(const Dims& d, bool shared) {
+    const size_t F = shared ? d.Fs : d.F;
+    if (shared || !d.mx) return 3 * F * d.L * (d.f32 ? 4 : 2);
+    return 3 * (F * d.L / 2) + 3 * (F * d.L / 32);
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lmoe_expert_record_bytes(const lmoe_config* cfg, int32_t shared) {
+    Dims d;
+    if (check_config(cfg, d) != LMOE_OK) return 0;
+    if (shared && d.Fs == 0) return 0;
+    return record_bytes(d, shared != 0);
+}
+
+lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes) {
+    Dims d;
+    lmoe_status st = check_config(cfg, d);
+    if (st != LMOE_OK) return st;
+    if ((st = check_T(d, T)) != LMOE_OK) return st;
+    if (!bytes) return fail(LMOE_ERR_NULL, "bytes is NULL");
+    *bytes = plan(d, T).total;
+    return LMOE_OK;
+}
+
+lmoe_status lmoe_permute_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes) {
+    Dims d;
+    lmoe_status st = check_config(cfg, d);
+    if (st != LMOE_OK) return st;
+    if ((st = check_T(d, T)) != LMOE_OK) return st;
+    if (!bytes) return fail(LMOE_ERR_NULL, "bytes is NULL");
+    *bytes = permute_ws(d, T);
+    return LMOE_OK;
+}
+
+lmoe_status lmoe_route(const lmoe_config* cfg, const lmoe_weights* weights, const float* z, int32_t T, int32_t* ids,
+                       float* w, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    lmoe_status st = check_config(cfg, d);
+    if (st != LMOE_OK) return st;
+    if ((st = check_T(d, T)) != LMOE_OK) return st;
+    if (!weights) return fail(LMOE_ERR_NULL, "weights is NULL");
+    if (T == 0) return LMOE_OK;
+    if (!weights->Wr || !z || !ids || !w || !ws) return fail(LMOE_ERR_NULL, "Wr, z, ids, w and ws must be non-NULL");
+    if (!aligned16(weights->Wr) || !aligned16(z) || !aligned16(ids) || !aligned16(w) || !aligned16(ws) ||
+        (reinterpret_cast<uintptr_t>(weights->br) & 3u))
+        return fail(LMOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned (br 4-byte)");
+    const size_t need = (size_t)T * d.E * 4;
+    if (ws_bytes < need) return fail(LMOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* logits = static_cast<float*>(ws);
+    hipError_t e = d.f32 ? launch_proj_f32(z, static_cast<const float*>(weights->Wr), weights->br, T, d.E, d.L, 0, logits, s)
+                         : launch_router_bf16(z, static_cast<const uint16_t*>(weights->Wr), weights->br, T, d.E, d.L,
+                                              logits, s);
+    if (e != hipSuccess) return hip_fail(e, "router logits");
+    if ((e = launch_topk(logits, T, d.E, d.k, ids, w, s)) != hipSuccess) return hip_fail(e, "top-k");
+    return LMOE_OK;
+}
+
+lmoe_status lmoe_permute(const lmoe_config* cfg, const int32_t* ids, int32_t T, int32_t* offsets, int32_t* perm,
+                         int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    lmoe_status st = check_config(cfg, d);
+    if (st != LMOE_OK) return st;
+    if ((st = check_T(d, T)) != LMOE_OK) return st;
+    if (!offsets) return fail(LMOE_ERR_NULL, "offsets is NULL");
+    if (T > 0 && (!ids || !perm || !inv)) return fail(LMOE_ERR_NULL, "ids, perm and inv must be non-NULL");
+    if (!aligned16(ids) || !aligned16(offsets) || !aligned16(perm) || !aligned16(inv) || !aligned16(ws))
+        return fail(LMOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const size_t need = permute_ws(d, T);
+    if (need && (!ws || ws_bytes < need))
+        return fail(LMOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* hist = static_cast<int32_t*>(ws);
+    int32_t* base = need ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2) : nullptr;
+    const hipError_t e = launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, 16, nullptr, nullptr, 0, s);
+    if (e != hipSuccess) return hip_fail(e, "permute");
+    return LMOE_OK;
+}
+
+lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const void* x, int32_t T, void* y,
+                         const lmoe_forward_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    lmoe_status st = check_config(cfg, d);
+    if (st != LMOE_OK) return st;
+    if ((st = check_T(d, T)) != LMOE_OK) return st;
+    if (!wt) return fail(LMOE_ERR_NULL, "weights is NULL");
+    const lmoe_forward_opts none{};
+    const lmoe_forward_opts& o = opts ? *opts : none;
+    if (o.prenorm && d.f32) return fail(LMOE_ERR_UNSUPPORTED, "prenorm needs act BF16 (the block input is bf16(RMSNorm(h)))");
+    if (T == 0) return LMOE_OK;
+    if (!x || !y || !wt->D || !wt->U || !wt->Wr || !wt->experts)
+        return fail(LMOE_ERR_NULL, "x, y, D, U, Wr and experts must be non-NULL");
+    if (d.Fs > 0 && !wt->shared) return fail(LMOE_ERR_NULL, "shared_ffn > 0 but the shared expert record is NULL");
+    const void* ptrs[] = {x, y, wt->D, wt->U, wt->Wr, wt->experts, wt->shared, ws, o.aux_z, o.aux_ids, o.aux_w,
+                          o.aux_offsets, o.aux_perm};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(LMOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(wt->br) & 3u) return fail(LMOE_ERR_ALIGN, "br must be 4-byte aligned");
+    const size_t xbytes = (size_t)T * d.H * ((o.prenorm || d.f32) ? 4 : 2);
+    const size_t ybytes = (size_t)T * d.H * ((o.residual || d.f32) ? 4 : 2);
+    if (overlap(x, xbytes, y, ybytes) && !(x == y && o.prenorm && o.residual))
+        return fail(LMOE_ERR_UNSUPPORTED, "x and y overlap (only x == y with prenorm and residual is allowed)");
+    const Layout lo = plan(d, T);
+    if (!ws || ws_bytes < lo.total)
+        return fail(LMOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, lo.total);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    StageEvents ev(o.stage_events, s);
+    char* W = static_cast<char*>(ws);
+    auto at = [&](size_t off) { return static_cast<void*>(W + off); };
+    float* z32 = o.aux_z ? o.aux_z : static_cast<float*>(at(lo.z32));
+    float* logits = static_cast<float*>(at(lo.logits));
+    int32_t* ids = o.aux_ids ? o.aux_ids : static_cast<int32_t*>(at(lo.ids));
+    float* wts = o.aux_w ? o.aux_w : static_cast<float*>(at(lo.w));
+    int32_t* offsets = o.aux_offsets ? o.aux_offsets : static_cast<int32_t*>(at(lo.offsets));
+    int32_t* perm = o.aux_perm ? o.aux_perm : static_cast<int32_t*>(at(lo.perm));
+    int32_t* inv = static_cast<int32_t*>(at(lo.inv));
+    int32_t* hist = static_cast<int32_t*>(at(lo.hist));
+    int32_t* base = static_cast<int32_t*>(at(lo.base));
+    Tile* tiles = static_cast<Tile*>(at(lo.tiles));
+    int32_t* ntiles = static_cast<int32_t*>(at(lo.ntiles));
+    float* Y = static_cast<float*>(at(lo.Y));
+    const int has_shared = d.Fs > 0;
+    hipError_t e;
+
+    if (d.f32) {
+        const float* xf = static_cast<const float*>(x);
+        ev.begin(LMOE_STAGE_D);
+        if ((e = launch_proj_f32(xf, static_cast<const float*>(wt->D), nullptr, T, d.L, d.H, 0, z32, s)) != hipSuccess)
+            return hip_fail(e, "D projection");
+        ev.end(LMOE_STAGE_D);
+        ev.begin(LMOE_STAGE_ROUTER);
+        if ((e = launch_proj_f32(z32, static_cast<const float*>(wt->Wr), wt->br, T, d.E, d.L, 0, logits, s)) != hipSuccess)
+            return hip_fail(e, "router logits");
+        ev.end(LMOE_STAGE_ROUTER);
+        ev.begin(LMOE_STAGE_TOPK);
+        if ((e = launch_topk(logits, T, d.E, d.k, ids, wts, s)) != hipSuccess) return hip_fail(e, "top-k");
+        ev.end(LMOE_STAGE_TOPK);
+        ev.begin(LMOE_STAGE_PERMUTE);
+        if ((e = launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, lo.BM, nullptr, nullptr, has_shared,
+                                s)) != hipSuccess)
+            return hip_fail(e, "permute");
+        ev.end(LMOE_STAGE_PERMUTE);
+        F32ExpertArgs a{z32, ids, perm, static_cast<const float*>(wt->experts), static_cast<const float*>(wt->shared),
+                        T, d.k, d.L, d.F, d.Fs, lo.Hs, static_cast<float*>(at(lo.H)), Y};
+        if ((e = launch_experts_f32(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
+        float* m = static_cast<float*>(at(lo.m));
+        ev.begin(LMOE_STAGE_COMBINE);
+        if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, false, m, s)) != hipSuccess) return hip_fail(e, "combine");
+        ev.end(LMOE_STAGE_COMBINE);
+        ev.begin(LMOE_STAGE_U);
+        if ((e = launch_proj_f32(m, static_cast<const float*>(wt->U), nullptr, T, d.H, d.L, o.residual ? 2 : 0,
+                                 static_cast<float*>(y), s)) != hipSuccess)
+            return hip_fail(e, "U projection");
+        ev.end(LMOE_STAGE_U);
+        return ev.err != hipSuccess ? hip_fail(ev.err, "stage event record") : LMOE_OK;
+    }
+
+    const uint16_t* x16 = static_cast<const uint16_t*>(x);
+    if (o.prenorm) {
+        uint16_t* xn = static_cast<uint16_t*>(at(lo.x16));
+        ev.begin(LMOE_STAGE_PRENORM);
+        if ((e = launch_rmsnorm(static_cast<const float*>(x), T, d.H, xn, s)) != hipSuccess) return hip_fail(e, "rmsnorm");
+        ev.end(LMOE_STAGE_PRENORM);
+        x16 = xn;
+    }
+    uint16_t* z16 = static_cast<uint16_t*>(at(lo.z16));
+    ev.begin(LMOE_STAGE_D);
+    if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s)) != hipSuccess)
+        return hip_fail(e, "D projection");
+    ev.end(LMOE_STAGE_D);
+    ev.begin(LMOE_STAGE_ROUTER);
+    if ((e = launch_router_bf16(z32, static_cast<const uint16_t*>(wt->Wr), wt->br, T, d.E, d.L, logits, s)) != hipSuccess)
+        return hip_fail(e, "router logits");
+    ev.end(LMOE_STAGE_ROUTER);
+    ev.begin(LMOE_STAGE_TOPK);
+    if ((e = launch_topk(logits, T, d.E, d.k, ids, wts, s)) != hipSuccess) return hip_fail(e, "top-k");
+    ev.end(LMOE_STAGE_TOPK);
+    ev.begin(LMOE_STAGE_PERMUTE);
+    if ((e = launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, lo.BM, tiles, ntiles, has_shared, s)) !=
+        hipSuccess)
+        return hip_fail(e, "permute");
+    ev.end(LMOE_STAGE_PERMUTE);
+    ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
+                 wt->shared, static_cast<uint16_t*>(at(lo.H)), Y, lo.max_tiles, lo.stream_path, d.mx};
+    if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
+    uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
+    ev.begin(LMOE_STAGE_COMBINE);
+    if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, true, m16, s)) != hipSuccess) return hip_fail(e, "combine");
+    ev.end(LMOE_STAGE_COMBINE);
+    ev.begin(LMOE_STAGE_U);
+    if ((e = launch_proj_bf16(m16, static_cast<const uint16_t*>(wt->U), T, d.H, d.L, o.residual ? 2 : 1,
+                              static_cast<float*>(y), static_cast<uint16_t*>(y), s)) != hipSuccess)
+        return hip_fail(e, "U projection");
+    ev.end(LMOE_STAGE_U);
+    return ev.err != hipSuccess ? hip_fail(ev.err, "stage event record") : LMOE_OK;
+}
+
+const char* lmoe_status_str(lmoe_status status) {
+    switch (status) {
+        case LMOE_OK: return "ok";
+        case LMOE_ERR_NULL: return "required pointer is NULL";
+        case LMOE_ERR_SHAPE: return "dimension out of range or inconsistent";
+        case LMOE_ERR_DTYPE: return "unknown dtype";
+        case LMOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case LMOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case LMOE_ERR_UNSUPPORTED: return "unsupported combination";
+        case LMOE_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* lmoe_last_error(void) { return g_err.c_str(); }
+
+int32_t lmoe_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Shared device definitions for the latent-MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------------------------------------
+// scalar conversions
+// ----------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+// 16 bytes reinterpreted as 8 bf16 MFMA operands.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Split an fp32 value into hi = bf16(v) and lo = bf16(v - hi); hi + lo carries ~16 significand
+// bits, enough for router logits that must stay within ~1e-5 of their fp32 value.
+__device__ __forceinline__ void split_hi_lo(float v, uint32_t& hi, uint32_t& lo) {
+    hi = f2bf(v);
+    lo = f2bf(v - bf2f(hi));
+}
+
+// ----------------------------------------------------------------------------------------------
+// MFMA wrappers (CDNA4 dense bf16, fp32 accumulate)
+//   32x32x16: A lane l holds row (l%32), k = 8*(l/32)+0..7; B lane l holds col (l%32), same k;
+//             D register r of lane l is row 8*(r/4) + 4*(l/32) + (r%4), col l%32.
+//   16x16x32: A lane l holds row (l%16), k = 8*(l/16)+0..7; B lane l holds col (l%16), same k;
+//             D register r of lane l is row 4*(l/16) + r, col l%16.
+// ----------------------------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------------------------
+// MXFP4 decoding: 8 E2M1 nibbles (one 32-bit word, low nibble first) times 2^(scale-127)
+// -> 8 bf16 values (16 bytes, the layout of one MFMA operand).
+// ----------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint4 mxfp4_to_bf16x8(uint32_t nib8, uint32_t scale_byte) {
+    // E2M1 magnitude by 3-bit code as bf16 bits: 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    // value = sign * mag * 2^(s-127): the scale multiplies exactly as an exponent add,
+    // done here in fp32 (products of a 2-bit significand and a power of two are exact).
+    const float scale = __uint_as_float((scale_byte == 0 ? 0x00400000u : (scale_byte << 23)));
+    uint32_t out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t n0 = (nib8 >> (8 * i)) & 0xFu;
+        uint32_t n1 = (nib8 >> (8 * i + 4)) & 0xFu;
+        // magnitudes as fp32 from the code: code c = e*2 + m (e: 2-bit exponent, m: mantissa)
+        auto mag = [](uint32_t c) -> float {
+            uint32_t e = (c >> 1) & 3u, m = c & 1u;
+            // e == 0: subnormal m * 0.5; else (1 + m/2) * 2^(e-1)
+            return e == 0 ? 0.5f * (float)m : __uint_as_float(((126u + e) << 23) | (m << 22));
+        };
+        float v0 = mag(n0) * scale;
+        float v1 = mag(n1) * scale;
+        v0 = (n0 & 8u) ? -v0 : v0;
+        v1 = (n1 & 8u) ? -v1 : v1;
+        out[i] = pack_bf2(v0, v1);
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// ----------------------------------------------------------------------------------------------
+// work lists
+// ----------------------------------------------------------------------------------------------
+// One tile of a grouped GEMM: `seg` is the expert id (n_experts = the shared expert),
+// rows [row0, row0 + nrows) of the segment-ordered row space.
+struct Tile {
+    int32_t seg;
+    int32_t row0;
+    int32_t nrows;
+    int32_t pad;
+};
+
+}  // namespace lmoe

@@ -1,0 +1,532 @@
+// Kernels of the latent-MoE block other than the MFMA GEMM templates, and the host-side
+// launch wrappers for everything (no allocation, no synchronisation: enqueue only).
+#include <limits.h>
+
+#include "gemm_stream.hpp"
+#include "gemm_tile.hpp"
+#include "launch.hpp"
+#include "problems.hpp"
+
+namespace lmoe {
+
+// ==============================================================================================
+// block-wide helpers
+// ==============================================================================================
+
+// Exclusive prefix sum over the block (one value per thread, blockDim a multiple of 64, at
+// most 2048 threads).  tmp needs 33 ints of LDS.  Every thread must call it.
+__device__ int block_excl_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) tmp[w] = x;
+    __syncthreads();
+    if (w == 0) {
+        int t = lane < nw ? tmp[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(t, o);
+            if (lane >= o) t += y;
+        }
+        if (lane < nw) tmp[lane] = t;
+        if (lane == 63) tmp[32] = t;
+    }
+    __syncthreads();
+    *total = tmp[32];
+    return x - v + (w > 0 ? tmp[w - 1] : 0);
+}
+
+// Sum over the block in a fixed order (wave butterflies, then wave 0..n-1).  red: 16 floats.
+__device__ float block_sum(float v, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.f;
+    for (int i = 0; i < nw; ++i) s += red[i];
+    return s;
+}
+
+// ==============================================================================================
+// RMSNorm prologue: x16[t] = bf16(h[t] / sqrt(mean(h[t]^2) + eps))  (unit gain)
+// ==============================================================================================
+__global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* __restrict__ h, int H, float eps,
+                                                           uint16_t* __restrict__ x16) {
+    __shared__ float red[16];
+    const float* row = h + (size_t)blockIdx.x * H;
+    float s = 0.f;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) s += row[i] * row[i];
+    const float tot = block_sum(s, red);
+    const float r = 1.0f / sqrtf(tot / (float)H + eps);
+    for (int i = threadIdx.x; i < H; i += blockDim.x) x16[(size_t)blockIdx.x * H + i] = (uint16_t)f2bf(row[i] * r);
+}
+
+// ==============================================================================================
+// top-k + softmax over the kept logits: one wave per token.  Each lane holds the logits of
+// ids lane, lane+64, ... (E <= 1024).  k rounds of a wave arg-max (larger value, then lower id
+// wins) remove one id each; the kept ids are written in ascending order with their weights.
+// ==============================================================================================
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                   int32_t* __restrict__ ids, float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* row = logits + (size_t)t * E;
+    float v[16];
+    uint32_t removed = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int id = lane + 64 * j;
+        float x = -INFINITY;
+        if (id < E) {
+            x = row[id];
+            if (!(x == x)) x = -INFINITY;  // NaN never wins (and never breaks the selection)
+        } else {
+            removed |= 1u << j;
+        }
+        v[j] = x;
+    }
+    float sv[16];
+    int sid[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        sv[r] = -INFINITY;
+        sid[r] = INT_MAX;
+        if (r < k) {
+            float bv = -INFINITY;
+            int bid = INT_MAX;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int id = lane + 64 * j;
+                if (!((removed >> j) & 1u) && (v[j] > bv || (v[j] == bv && id < bid))) {
+                    bv = v[j];
+                    bid = id;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const float ov = __shfl_xor(bv, o);
+                const int oid = __shfl_xor(bid, o);
+                if (ov > bv || (ov == bv && oid < bid)) {
+                    bv = ov;
+                    bid = oid;
+                }
+            }
+            if (bid != INT_MAX && (bid & 63) == lane) removed |= 1u << (bid >> 6);
+            sv[r] = bv;
+            sid[r] = bid;
+        }
+    }
+    if (lane < k) {
+        int myid = 0;
+        float myv = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (r == lane) {
+                myid = sid[r];
+                myv = sv[r];
+            }
+        const float mx = sv[0];  // the first pick is the largest kept logit
+        int rank = 0;
+        float den = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (r < k) {
+                rank += sid[r] < myid;
+                den += expf(sv[r] - mx);
+            }
+        }
+        ids[(size_t)t * k + rank] = myid;
+        w[(size_t)t * k + rank] = expf(myv - mx) / den;
+    }
+}
+
+// ==============================================================================================
+// Permutation.  Tokens are cut into blocks of 64; inside a block, bit tl of bm[2e + tl/32] marks
+// that token tl chose expert e.  Because a token's ids are distinct, the stable rank of slot
+// (t, s) inside expert e's segment is (slots of e in earlier blocks) + popcount of the bits of
+// earlier tokens of the same block, so no sort is needed and the result is unique.
+// ==============================================================================================
+constexpr int kPermTB = 64;
+
+__device__ void perm_bitmap(const int32_t* __restrict__ ids, int T, int k, int E, int b, uint32_t* bm) {
+    const int t0 = b * kPermTB;
+    const int nt = min(kPermTB, T - t0);
+    for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) bm[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+        const int e = ids[(size_t)t0 * k + i];
+        if (e >= 0 && e < E) {
+            const int tl = i / k;
+            atomicOr(&bm[e * 2 + (tl >> 5)], 1u << (tl & 31));
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ int bits_below(const uint32_t* bm, int e, int tl) {
+    const uint32_t w0 = bm[2 * e], w1 = bm[2 * e + 1];
+    return tl < 32 ? __popc(w0 & ((1u << tl) - 1u)) : __popc(w0) + __popc(w1 & ((1u << (tl - 32)) - 1u));
+}
+
+__device__ void perm_scatter_block(const int32_t* __restrict__ ids, int T, int k, int E, int b, const uint32_t* bm,
+                                   const int* seg_base /* per expert: first position for this block */,
+                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    const int t0 = b * kPermTB;
+    const int nt = min(kPermTB, T - t0);
+    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+        const size_t f = (size_t)t0 * k + i;
+        const int e = ids[f];
+        if (e < 0 || e >= E) {
+            inv[f] = -1;
+            continue;
+        }
+        const int pos = seg_base[e] + bits_below(bm, e, i / k);
+        perm[pos] = (int32_t)f;
+        inv[f] = pos;
+    }
+}
+
+// Work list of <= BM-row tiles: routed segments in expert order, then the shared segment.
+__device__ void write_tiles(int e_cnt, int e_off, int e, int E, int T, int k, int BM, int has_shared, Tile* tiles,
+                            int32_t* ntiles, int* tmp) {
+    const int nt = e < E ? (e_cnt + BM - 1) / BM : 0;
+    int ntot;
+    const int ts = block_excl_scan(nt, tmp, &ntot);
+    for (int j = 0; j < nt; ++j) tiles[ts + j] = Tile{e, e_off + j * BM, min(BM, e_cnt - j * BM), 0};
+    const int nsh = has_shared ? (T + BM - 1) / BM : 0;
+    for (int j = threadIdx.x; j < nsh; j += blockDim.x) tiles[ntot + j] = Tile{E, T * k + j * BM, min(BM, T - j * BM), 0};
+    if (threadIdx.x == 0) *ntiles = ntot + nsh;
+}
+
+// Whole permutation in one workgroup (T <= 64 tokens).
+__global__ __launch_bounds__(1024) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ inv, int BM, Tile* tiles,
+                                                           int32_t* ntiles, int has_shared) {
+    __shared__ uint32_t bm[2 * 1024];
+    __shared__ int soff[1024];
+    __shared__ int tmp[33];
+    perm_bitmap(ids, T, k, E, 0, bm);
+    const int e = threadIdx.x;
+    const int cnt = e < E ? __popc(bm[2 * e]) + __popc(bm[2 * e + 1]) : 0;
+    int total;
+    const int off = block_excl_scan(cnt, tmp, &total);
+    if (e < E) {
+        offsets[e] = off;
+        soff[e] = off;
+    }
+    if (e == 0) offsets[E] = total;
+    for (int i = total + threadIdx.x; i < T * k; i += blockDim.x) perm[i] = -1;
+    if (tiles) write_tiles(cnt, off, e, E, T, k, BM, has_shared, tiles, ntiles, tmp);
+    __syncthreads();
+    perm_scatter_block(ids, T, k, E, 0, bm, soff, perm, inv);
+}
+
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                        int32_t* __restrict__ hist) {
+    __shared__ uint32_t bm[2 * 1024];
+    perm_bitmap(ids, T, k, E, blockIdx.x, bm);
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        hist[(size_t)blockIdx.x * E + e] = __popc(bm[2 * e]) + __popc(bm[2 * e + 1]);
+}
+
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int nb, int T, int k, int E,
+                                                         int32_t* __restrict__ base, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ perm, int BM, Tile* tiles,
+                                                         int32_t* ntiles, int has_shared) {
+    __shared__ int tmp[33];
+    const int e = threadIdx.x;
+    int cnt = 0;
+    if (e < E) {
+        for (int b = 0; b < nb; ++b) {
+            base[(size_t)b * E + e] = cnt;
+            cnt += hist[(size_t)b * E + e];
+        }
+    }
+    int total;
+    const int off = block_excl_scan(e < E ? cnt : 0, tmp, &total);
+    if (e < E) offsets[e] = off;
+    if (e == 0) offsets[E] = total;
+    for (int i = total + threadIdx.x; i < T * k; i += blockDim.x) perm[i] = -1;
+    if (tiles) write_tiles(cnt, off, e, E, T, k, BM, has_shared, tiles, ntiles, tmp);
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                           const int32_t* __restrict__ base,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ uint32_t bm[2 * 1024];
+    __shared__ int sbase[1024];
+    perm_bitmap(ids, T, k, E, blockIdx.x, bm);
+    for (int e = threadIdx.x; e < E; e += blockDim.x) sbase[e] = offsets[e] + base[(size_t)blockIdx.x * E + e];
+    __syncthreads();
+    perm_scatter_block(ids, T, k, E, blockIdx.x, bm, sbase, perm, inv);
+}
+
+// ==============================================================================================
+// combine: m[t] = Y[T*k + t] (shared, weight 1) + sum_s w[t][s] * Y[t*k + s], slots in order
+// ==============================================================================================
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y, const float* __restrict__ w, int T,
+                                                      int k, int L, int has_shared, void* __restrict__ m) {
+    const int t = blockIdx.y;
+    const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (c >= L) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (has_shared) acc = *reinterpret_cast<const float4*>(Y + ((size_t)T * k + t) * L + c);
+    for (int s = 0; s < k; ++s) {
+        const float ws = w[(size_t)t * k + s];
+        const float4 y = *reinterpret_cast<const float4*>(Y + ((size_t)t * k + s) * L + c);
+        acc.x += ws * y.x;
+        acc.y += ws * y.y;
+        acc.z += ws * y.z;
+        acc.w += ws * y.w;
+    }
+    if (OUT_BF16) {
+        uint2 o = make_uint2(pack_bf2(acc.x, acc.y), pack_bf2(acc.z, acc.w));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(m) + (size_t)t * L + c) = o;
+    } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(m) + (size_t)t * L + c) = acc;
+    }
+}
+
+// ==============================================================================================
+// plain fp32 path (fp32 storage end to end): one thread per output element, sequential K.
+// ==============================================================================================
+// mode 0: out = x.W^T ; 2: out += x.W^T ; bias (router) optional
+__global__ __launch_bounds__(256) void f32_proj_kernel(const float* __restrict__ x, const float* __restrict__ W,
+                                                       const float* __restrict__ bias, int T, int N, int K, int mode,
+                                                       float* __restrict__ out) {
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        const float* xr = x + (size_t)t * K;
+        const float* wr = W + (size_t)n * K;
+        float acc = 0.f;
+        for (int i = 0; i < K; ++i) acc = fmaf(xr[i], wr[i], acc);
+        if (bias) acc += bias[n];
+        float* o = out + (size_t)t * N + n;
+        if (mode == 2)
+            *o += acc;
+        else
+            *o = acc;
+    }
+}
+
+struct F32Seg {
+    const float* z;
+    const int32_t* ids;
+    const int32_t* perm;
+    const float* experts;
+    const float* shared;
+    int T, k, L, F, Fs, Hs;
+    // resolve segment row p: token, width and the expert record; false if p is a dropped slot
+    __device__ bool resolve(int p, int& token, int& Fseg, const float*& rec) const {
+        if (p < T * k) {
+            const int slot = perm[p];
+            if (slot < 0) return false;
+            token = slot / k;
+            Fseg = F;
+            rec = experts + (size_t)ids[slot] * 3 * F * L;
+        } else {
+            token = p - T * k;
+            Fseg = Fs;
+            rec = shared;
+        }
+        return true;
+    }
+};
+
+__global__ __launch_bounds__(256) void f32_up_kernel(const F32Seg s, int R, float* __restrict__ H) {
+    const int f = blockIdx.x * blockDim.x + threadIdx.x;
+    for (int p = blockIdx.y; p < R; p += gridDim.y) {
+        int token, Fseg;
+        const float* g;
+        if (!s.resolve(p, token, Fseg, g) || f >= Fseg) continue;
+        const float* u = g + (size_t)Fseg * s.L;
+        const float* zr = s.z + (size_t)token * s.L;
+        float a = 0.f, b = 0.f;
+        for (int i = 0; i < s.L; ++i) {
+            a = fmaf(zr[i], g[(size_t)f * s.L + i], a);
+            b = fmaf(zr[i], u[(size_t)f * s.L + i], b);
+        }
+        H[(size_t)p * s.Hs + f] = a / (1.0f + expf(-a)) * b;
+    }
+}
+
+__global__ __launch_bounds__(256) void f32_down_kernel(const F32Seg s, int R, const float* __restrict__ H,
+                                                       float* __restrict__ Y) {
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= s.L) return;
+    for (int p = blockIdx.y; p < R; p += gridDim.y) {
+        int token, Fseg;
+        const float* g;
+        if (!s.resolve(p, token, Fseg, g)) continue;
+        const float* d = g + 2 * (size_t)Fseg * s.L + (size_t)n * Fseg;
+        const float* hr = H + (size_t)p * s.Hs;
+        float acc = 0.f;
+        for (int f = 0; f < Fseg; ++f) acc = fmaf(hr[f], d[f], acc);
+        const int dest = p < s.T * s.k ? s.perm[p] : p;
+        Y[(size_t)dest * s.L + n] = acc;
+    }
+}
+
+// ==============================================================================================
+// launch wrappers
+// ==============================================================================================
+namespace {
+inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
+inline hipError_t last() { return hipGetLastError(); }
+constexpr int kStreamKS = 8;
+}  // namespace
+
+hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream_t s) {
+    hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3(T), dim3(256), 0, s, h, H, 1e-6f, x16);
+    return last();
+}
+
+hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
+                            uint16_t* out16, hipStream_t s) {
+    if (T <= kStreamMaxT) {
+        StreamProj p{x, W, T, N, K, mode, out32, out16};
+        hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 1, StreamProj>), dim3(cdiv(T, 16), cdiv(N, 16)),
+                           dim3(64 * kStreamKS), 0, s, p);
+    } else {
+        TileProj p{x, W, T, N, K, mode, out32, out16};
+        hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileProj>), dim3(cdiv(T, 128), cdiv(N, 128)), dim3(256), 0, s, p);
+    }
+    return last();
+}
+
+hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
+                              hipStream_t s) {
+    if (T <= kStreamMaxT) {
+        StreamRouter p{z, Wr, br, T, E, L, logits};
+        hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 1, StreamRouter>), dim3(cdiv(T, 16), cdiv(E, 16)),
+                           dim3(64 * kStreamKS), 0, s, p);
+    } else {
+        TileRouter p{z, Wr, br, T, E, L, logits};
+        hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileRouter>), dim3(cdiv(T, 128), cdiv(E, 128)), dim3(256), 0, s,
+                           p);
+    }
+    return last();
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+    hipLaunchKernelGGL(topk_kernel, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, ids, w);
+    return last();
+}
+
+int perm_blocks(int T) { return (int)cdiv(T, kPermTB); }
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist, int32_t* base, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
+                          hipStream_t s) {
+    const int nb = perm_blocks(T);
+    if (nb <= 1) {
+        hipLaunchKernelGGL(perm_single_kernel, dim3(1), dim3(1024), 0, s, ids, T, k, E, offsets, perm, inv, BM, tiles,
+                           ntiles, has_shared);
+        return last();
+    }
+    hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, hist);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, T, k, E, base, offsets, perm, BM, tiles,
+                       ntiles, has_shared);
+    err = last();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, base, offsets, perm, inv);
+    return last();
+}
+
+int expert_tile_rows(bool stream_path) { return stream_path ? 16 : 128; }
+
+int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
+    const long BM = expert_tile_rows(stream_path);
+    const long tk = (long)T * k;
+    return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
+}
+
+hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {
+    const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E};
+    const int Fmax = std::max(a.F, a.Fs);
+    const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
+    hipError_t err;
+    ev.begin(kStageUp);
+    if (a.stream_path) {
+        const dim3 grid(a.max_tiles, cdiv(Fmax, 16)), block(64 * kStreamKS);
+        if (a.mxfp4) {
+            StreamUp<true> up{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.H};
+            hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 2, StreamUp<true>>), grid, block, 0, s, up);
+        } else {
+            StreamUp<false> up{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.H};
+            hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 2, StreamUp<false>>), grid, block, 0, s, up);
+        }
+    } else {
+        if (a.mxfp4) return hipErrorInvalidValue;  // the tile path takes bf16 experts only
+        TileUp up{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H};
+        hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileUp>), dim3(a.max_tiles, cdiv(Fmax, 64)), dim3(256), 0, s, up);
+    }
+    if ((err = last()) != hipSuccess) return err;
+    ev.end(kStageUp);
+    ev.begin(kStageDown);
+    if (a.stream_path) {
+        const dim3 grid(a.max_tiles, cdiv(a.L, 16)), block(64 * kStreamKS);
+        if (a.mxfp4) {
+            StreamDown<true> dn{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y};
+            hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 1, StreamDown<true>>), grid, block, 0, s, dn);
+        } else {
+            StreamDown<false> dn{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y};
+            hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 1, StreamDown<false>>), grid, block, 0, s, dn);
+        }
+    } else {
+        TileDown dn{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y};
+        hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileDown>), dim3(a.max_tiles, cdiv(a.L, 128)), dim3(256), 0, s, dn);
+    }
+    if ((err = last()) != hipSuccess) return err;
+    ev.end(kStageDown);
+    return hipSuccess;
+}
+
+hipError_t launch_combine(const float* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
+                          hipStream_t s) {
+    const dim3 grid(cdiv(L / 4, 256), T);
+    if (out_bf16)
+        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, Y, w, T, k, L, has_shared, m);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, Y, w, T, k, L, has_shared, m);
+    return last();
+}
+
+hipError_t launch_proj_f32(const float* x, const float* W, const float* bias, int T, int N, int K, int mode, float* out,
+                           hipStream_t s) {
+    hipLaunchKernelGGL(f32_proj_kernel, dim3(cdiv(N, 256), std::min(T, 65535)), dim3(256), 0, s, x, W, bias, T, N, K,
+                       mode, out);
+    return last();
+}
+
+hipError_t launch_experts_f32(const F32ExpertArgs& a, hipStream_t s, StageEvents& ev) {
+    const F32Seg seg{a.z, a.ids, a.perm, a.experts, a.shared, a.T, a.k, a.L, a.F, a.Fs, a.Hs};
+    const int R = a.T * a.k + (a.Fs > 0 ? a.T : 0);
+    const int gy = std::min(R, 65535);
+    ev.begin(kStageUp);
+    hipLaunchKernelGGL(f32_up_kernel, dim3(cdiv(std::max(a.F, a.Fs), 256), gy), dim3(256), 0, s, seg, R, a.H);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    ev.end(kStageUp);
+    ev.begin(kStageDown);
+    hipLaunchKernelGGL(f32_down_kernel, dim3(cdiv(a.L, 256), gy), dim3(256), 0, s, seg, R, a.H, a.Y);
+    err = last();
+    ev.end(kStageDown);
+    return err;
+}
+
+}  // namespace lmoe

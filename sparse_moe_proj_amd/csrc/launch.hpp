@@ -1,0 +1,97 @@
+// Host-side launch wrappers of the latent-MoE kernels (enqueue only; no allocation, no sync).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace lmoe {
+
+struct Tile;
+
+// Optional per-stage event records (the lmoe_forward_opts.stage_events hook).
+struct StageEvents {
+    void* const* ev;
+    hipStream_t s;
+    bool capturing = false;
+    hipError_t err = hipSuccess;
+    StageEvents(void* const* events, hipStream_t stream) : ev(events), s(stream) {
+        if (ev) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(s, &cs) == hipSuccess) capturing = cs == hipStreamCaptureStatusActive;
+        }
+    }
+    void rec(int i) {
+        if (!ev || !ev[i]) return;
+        hipEvent_t e = static_cast<hipEvent_t>(ev[i]);
+        const hipError_t r = capturing ? hipEventRecordWithFlags(e, s, hipEventRecordExternal) : hipEventRecord(e, s);
+        if (r != hipSuccess && err == hipSuccess) err = r;
+    }
+    void begin(int stage) { rec(2 * stage); }
+    void end(int stage) { rec(2 * stage + 1); }
+};
+constexpr int kStageUp = 5, kStageDown = 6;  // LMOE_STAGE_EXPERT_UP / _DOWN
+
+// Batches of at most this many tokens use the weight-streaming (decode) kernels.
+constexpr int kStreamMaxT = 16;
+
+hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream_t s);
+
+// mode 0: out32 = xW^T and out16 = bf16(out32); 1: out16 = bf16(xW^T); 2: out32 += xW^T
+hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
+                            uint16_t* out16, hipStream_t s);
+
+hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
+                              hipStream_t s);
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+
+int perm_blocks(int T);
+
+// tiles may be null (no work list).  hist/base: [perm_blocks(T)][E] ints (unused when T <= 64).
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist, int32_t* base, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
+                          hipStream_t s);
+
+int expert_tile_rows(bool stream_path);
+int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path);
+
+struct ExpertArgs {
+    const Tile* tiles;
+    const int32_t* ntiles;
+    const int32_t* perm;
+    int T, k, E, L, F, Fs, Hs;
+    const uint16_t* z16;
+    const void* experts;
+    size_t rec_bytes;
+    const void* shared;
+    uint16_t* H;
+    float* Y;
+    int max_tiles;
+    bool stream_path;
+    bool mxfp4;
+};
+hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
+
+hipError_t launch_combine(const float* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
+                          hipStream_t s);
+
+// fp32 path. mode 0: out = xW^T (+bias); 2: out += xW^T
+hipError_t launch_proj_f32(const float* x, const float* W, const float* bias, int T, int N, int K, int mode, float* out,
+                           hipStream_t s);
+
+struct F32ExpertArgs {
+    const float* z;
+    const int32_t* ids;
+    const int32_t* perm;
+    const float* experts;
+    const float* shared;
+    int T, k, L, F, Fs, Hs;
+    float* H;
+    float* Y;
+};
+hipError_t launch_experts_f32(const F32ExpertArgs& a, hipStream_t s, StageEvents& ev);
+
+}  // namespace lmoe

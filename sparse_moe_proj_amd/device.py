@@ -1,0 +1,81 @@
+"""Device-memory plumbing around the C ABI: upload host weight arrays into torch tensors on
+the GPU, size and hold the workspace, and call lmoe_forward on the current stream.
+
+Host arrays follow the storage layout of include/lmoe.h (bf16 as uint16 bit patterns,
+MXFP4 records as bytes).  No arithmetic of the block happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (LMOE_OK, check, lmoe_forward, lmoe_workspace_bytes, make_config, make_opts,  # noqa: F401
+               make_weights)
+
+
+def to_device(a, device="cuda"):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16))
+    else:
+        t = torch.from_numpy(a)
+    return t.to(device)
+
+
+class DeviceLayer:
+    """One layer's weights resident in HBM (tensors kept alive by this object)."""
+
+    def __init__(self, lw=None, act="bf16", device="cuda", _copy_of=None):
+        if _copy_of is not None:
+            src = _copy_of
+            self.shape, self.act, self.dense, self.expert = src.shape, src.act, src.dense, src.expert
+            for n in ("D", "U", "Wr", "br", "shared", "experts"):
+                t = getattr(src, n)
+                setattr(self, n, None if t is None else t.clone())
+        else:
+            self.shape, self.act, self.dense, self.expert = lw.shape, act, lw.dense, lw.expert
+            self.D = to_device(lw.D, device)
+            self.U = to_device(lw.U, device)
+            self.Wr = to_device(lw.Wr, device)
+            self.br = to_device(np.asarray(lw.br, dtype=np.float32), device)
+            self.shared = to_device(lw.shared, device)
+            self.experts = to_device(lw.experts, device)
+        s = self.shape
+        self.cfg = make_config(s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn, self.act, self.dense,
+                               self.expert)
+        self.weights = make_weights(self.D, self.U, self.Wr, self.br, self.shared, self.experts)
+
+    def clone(self) -> "DeviceLayer":
+        """A byte-identical copy at other HBM addresses."""
+        return DeviceLayer(_copy_of=self)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.D, self.U, self.Wr, self.br, self.shared, self.experts)
+                   if t is not None)
+
+
+class Workspace:
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        nbytes = max(256, int(nbytes))
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def forward(layer: DeviceLayer, x, y=None, opts=None, ws: Workspace | None = None, stream=None):
+    """y = block(x) on the current stream; returns y (allocated when not given)."""
+    T = x.shape[0]
+    if y is None:
+        dt = torch.float32 if (layer.act == "f32" or (opts is not None and opts.residual)) else torch.int16
+        y = torch.empty((T, layer.shape.hidden), dtype=dt, device=x.device)
+    ws = ws or Workspace(x.device)
+    nb = lmoe_workspace_bytes(layer.cfg, T)
+    buf = ws.get(nb)
+    check(lmoe_forward(layer.cfg, layer.weights, x, T, y, opts, buf, buf.numel(), stream))
+    return y

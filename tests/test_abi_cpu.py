@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/lmoe.h
+declares, answers size queries, and rejects bad arguments on the host before enqueuing
+anything (fake device addresses are never dereferenced because validation fails first)."""
+import ctypes
+
+import pytest
+
+import lmoe_data as gen
+import sparse_moe_proj_amd as lm
+
+S = gen.EDGE0_145B
+FAKE = 1 << 40  # a 16-byte aligned address that is never dereferenced
+
+
+def cfg(**kw):
+    base = dict(hidden=S.hidden, latent=S.latent, n_experts=S.n_experts, top_k=S.top_k, ffn=S.ffn,
+                shared_ffn=S.shared_ffn, act="bf16", dense="bf16", expert="bf16")
+    base.update(kw)
+    return lm.make_config(**base)
+
+
+def full_weights():
+    return lm.make_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_every_header_symbol_is_exported():
+    syms = lm.header_symbols()
+    assert {"lmoe_route", "lmoe_permute", "lmoe_forward"} <= set(syms)
+    for name in syms:
+        assert hasattr(lm.lib, name), name
+        assert ctypes.cast(getattr(lm.lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    assert lm.lmoe_version() >= 100
+    for st in range(8):
+        assert lm.lmoe_status_str(st)
+    assert lm.lmoe_status_str(99) == "unknown status"
+
+
+def test_record_sizes():
+    assert lm.lmoe_expert_record_bytes(cfg(), 0) == 3 * 640 * 1792 * 2
+    assert lm.lmoe_expert_record_bytes(cfg(expert="mxfp4"), 0) == S.mxfp4_record_bytes() == 1827840
+    assert lm.lmoe_expert_record_bytes(cfg(expert="mxfp4"), 1) == 3 * 640 * 1792 * 2  # shared stays bf16
+    t = gen.TINY
+    c = lm.make_config(t.hidden, t.latent, t.n_experts, t.top_k, t.ffn, t.shared_ffn, "f32", "f32", "f32")
+    assert lm.lmoe_expert_record_bytes(c, 0) == 3 * 64 * 128 * 4
+    assert lm.lmoe_expert_record_bytes(cfg(shared_ffn=0), 1) == 0
+
+
+def test_workspace_sizes_monotone():
+    c = cfg()
+    prev = 0
+    for T in (0, 1, 8, 16, 17, 64, 65, 4096, 16384):
+        n = lm.lmoe_workspace_bytes(c, T)
+        assert n >= prev
+        prev = n
+    assert lm.lmoe_permute_workspace_bytes(c, 64) == 0
+    assert lm.lmoe_permute_workspace_bytes(c, 65) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=100), lm.LMOE_ERR_SHAPE),
+    (dict(latent=0), lm.LMOE_ERR_SHAPE),
+    (dict(top_k=0), lm.LMOE_ERR_SHAPE),
+    (dict(top_k=17, n_experts=64), lm.LMOE_ERR_SHAPE),
+    (dict(n_experts=5, top_k=10), lm.LMOE_ERR_SHAPE),
+    (dict(n_experts=2048), lm.LMOE_ERR_SHAPE),
+    (dict(shared_ffn=32), lm.LMOE_ERR_SHAPE),
+    (dict(act="f32"), lm.LMOE_ERR_UNSUPPORTED),
+    (dict(expert="f32"), lm.LMOE_ERR_UNSUPPORTED),
+])
+def test_bad_config_rejected(kw, code):
+    n = ctypes.c_size_t(0)
+    assert lm.lib.lmoe_workspace_bytes(ctypes.byref(cfg(**kw)), 8, ctypes.byref(n)) == code
+    assert lm.lmoe_forward(cfg(**kw), full_weights(), FAKE, 8, FAKE + 4096, None, FAKE, 1 << 40, 0) == code
+    assert lm.last_error()
+
+
+def test_bad_dtype_code():
+    c = cfg()
+    c.expert_dtype = 7
+    assert lm.lmoe_forward(c, full_weights(), FAKE, 8, FAKE, None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_DTYPE
+
+
+def test_null_config_and_pointers():
+    assert lm.lib.lmoe_forward(None, None, None, 8, None, None, None, 0, None) == lm.LMOE_ERR_NULL
+    w = full_weights()
+    w.Wr = None
+    assert lm.lmoe_forward(cfg(), w, FAKE, 8, FAKE + (1 << 30), None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_NULL
+    w = full_weights()
+    w.shared = None
+    assert lm.lmoe_forward(cfg(), w, FAKE, 8, FAKE + (1 << 30), None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_NULL
+    assert lm.lmoe_route(cfg(), full_weights(), None, 8, FAKE, FAKE, FAKE, 1 << 30, 0) == lm.LMOE_ERR_NULL
+    assert lm.lmoe_permute(cfg(), None, 8, FAKE, FAKE, FAKE, None, 0, 0) == lm.LMOE_ERR_NULL
+
+
+def test_misaligned_pointers():
+    assert lm.lmoe_forward(cfg(), full_weights(), FAKE + 2, 8, FAKE + (1 << 30), None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_ALIGN
+    w = full_weights()
+    w.experts = FAKE + 8
+    assert lm.lmoe_forward(cfg(), w, FAKE, 8, FAKE + (1 << 30), None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_ALIGN
+    assert lm.lmoe_permute(cfg(), FAKE + 4, 8, FAKE, FAKE, FAKE, None, 0, 0) == lm.LMOE_ERR_ALIGN
+
+
+def test_workspace_too_small():
+    need = lm.lmoe_workspace_bytes(cfg(), 8)
+    assert lm.lmoe_forward(cfg(), full_weights(), FAKE, 8, FAKE + (1 << 30), None, FAKE, need - 1, 0) == lm.LMOE_ERR_WORKSPACE
+    assert lm.lmoe_forward(cfg(), full_weights(), FAKE, 8, FAKE + (1 << 30), None, None, need, 0) == lm.LMOE_ERR_WORKSPACE
+    assert lm.lmoe_route(cfg(), full_weights(), FAKE, 8, FAKE, FAKE, FAKE, 8 * 512 * 4 - 1, 0) == lm.LMOE_ERR_WORKSPACE
+    assert lm.lmoe_permute(cfg(), FAKE, 65, FAKE, FAKE, FAKE, None, 0, 0) == lm.LMOE_ERR_WORKSPACE
+
+
+def test_overlapping_x_y_rejected_and_options_checked():
+    assert lm.lmoe_forward(cfg(), full_weights(), FAKE, 8, FAKE + 64, None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_UNSUPPORTED
+    t = gen.TINY
+    c = lm.make_config(t.hidden, t.latent, t.n_experts, t.top_k, t.ffn, t.shared_ffn, "f32", "f32", "f32")
+    o = lm.make_opts(prenorm=1)
+    assert lm.lmoe_forward(c, full_weights(), FAKE, 8, FAKE + (1 << 30), o, FAKE, 1 << 40, 0) == lm.LMOE_ERR_UNSUPPORTED
+
+
+def test_bad_T():
+    assert lm.lmoe_forward(cfg(), full_weights(), FAKE, -1, FAKE, None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_SHAPE
+    assert lm.lmoe_forward(cfg(), full_weights(), FAKE, (1 << 20) + 1, FAKE, None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_SHAPE
+
+
+def test_zero_tokens_is_a_noop_without_device_access():
+    # T = 0 returns OK before any pointer is used (all NULL here)
+    nothing = lm.make_weights(None, None, None, None, None, None)
+    assert lm.lmoe_forward(cfg(), nothing, None, 0, None, None, None, 0, 0) == lm.LMOE_OK
+    assert lm.lmoe_route(cfg(), nothing, None, 0, None, None, None, 0, 0) == lm.LMOE_OK

@@ -1,0 +1,161 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Covers the five workloads at full size (routing and permutation on every token, outputs on
+every token up to T=8 and on sampled tokens beyond), plus small shapes that exercise ragged
+tiles, both kernel paths, MXFP4 records, no shared expert, E == k and E == k == 1.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lmoe_data as gen
+import oracle
+import sparse_moe_proj_amd as lm
+from parity import (check_block, host, log, run_forward, sample_tokens, small_layer, upload_tokens, TOL,
+                    check_routing, normwise_rel, act_to_f64)
+from sparse_moe_proj_amd.device import DeviceLayer, Workspace, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ws():
+    return Workspace("cuda")
+
+
+def _workload_case(name, n_sample, ws):
+    wl = gen.WORKLOADS[name]
+    log(f"[{name}] generating layer")
+    lw = gen.make_layer(wl, 0)
+    dl = DeviceLayer(lw, act=wl.act)
+    x = gen.make_tokens(wl)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    sample = sample_tokens(wl.T, n_sample)
+    return check_block(lw, x, wl.act, out, sample=sample, label=name)
+
+
+def test_tiny_f32_full(ws):
+    _workload_case("tiny_f32", 32, ws)
+
+
+def test_decode_t8_full(ws):
+    _workload_case("decode_t8", 8, ws)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_t4096_sampled(ws):
+    _workload_case("prefill_t4096", 96, ws)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_t16384_sampled(ws):
+    _workload_case("prefill_t16384", 96, ws)
+
+
+SMALL = gen.Shape(hidden=256, latent=192, n_experts=24, top_k=3, ffn=128, shared_ffn=64)
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 100, 300])
+def test_small_bf16_ragged(T, ws):
+    wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"small_bf16 T={T}")
+
+
+@pytest.mark.parametrize("T", [3, 16, 40])
+def test_small_mxfp4(T, ws):
+    wl, lw = small_layer(SMALL, "bf16", "bf16", "mxfp4")
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"small_mxfp4 T={T}")
+
+
+@pytest.mark.parametrize("T", [7, 70])
+def test_small_f32(T, ws):
+    wl, lw = small_layer(SMALL, "f32", "f32", "f32")
+    dl = DeviceLayer(lw, act="f32")
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "f32", out, label=f"small_f32 T={T}")
+
+
+@pytest.mark.parametrize("shape_kw,T", [
+    (dict(shared_ffn=0), 9),                       # no shared expert
+    (dict(shared_ffn=0), 130),
+    (dict(n_experts=4, top_k=4), 11),              # every expert used
+    (dict(n_experts=4, top_k=4), 70),
+    (dict(n_experts=1, top_k=1, shared_ffn=0), 5),  # dense SwiGLU
+    (dict(n_experts=1, top_k=1, shared_ffn=0), 200),
+    (dict(top_k=16, n_experts=20), 33),            # largest k
+    (dict(ffn=64, shared_ffn=128), 24),            # shared wider than routed
+])
+def test_degenerate_shapes(shape_kw, T, ws):
+    base = dict(hidden=128, latent=128, n_experts=12, top_k=2, ffn=128, shared_ffn=64)
+    base.update(shape_kw)
+    shape = gen.Shape(**base)
+    wl, lw = small_layer(shape, "bf16", "bf16", "bf16", wid=78)
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"degenerate {shape_kw} T={T}")
+
+
+def test_identical_experts_output_independent_of_routing(ws):
+    shape = gen.Shape(hidden=128, latent=128, n_experts=16, top_k=4, ffn=64, shared_ffn=64)
+    wl, lw = small_layer(shape, "bf16", "bf16", "bf16", wid=79)
+    lw.experts[:] = lw.experts[0]
+    x = gen.make_tokens(wl, T=12)
+    xt = upload_tokens(x)
+    dl = DeviceLayer(lw, act="bf16")
+    a = run_forward(dl, xt, ws)
+    lw.br = np.linspace(4, -4, 16).astype(np.float32)
+    dl2 = DeviceLayer(lw, act="bf16")
+    b = run_forward(dl2, xt, ws)
+    torch.cuda.synchronize()
+    assert not np.array_equal(host(a["ids"]), host(b["ids"]))
+    ya = act_to_f64(host(a["y"]), "bf16")
+    yb = act_to_f64(host(b["y"]), "bf16")
+    assert normwise_rel(yb, ya).max() < 1e-2
+
+
+def test_determinism_and_batch_invariance(ws):
+    wl = gen.WORKLOADS["decode_t8"]
+    for T, sub in ((8, 3), (300, 120)):
+        wl2, lw = small_layer(SMALL, "bf16", "bf16", "bf16", wid=80)
+        dl = DeviceLayer(lw, act="bf16")
+        x = gen.make_tokens(wl2, T=T, salt=1)
+        xt = upload_tokens(x)
+        a = run_forward(dl, xt, ws)
+        b = run_forward(dl, xt, ws)
+        torch.cuda.synchronize()
+        for key in ("y", "z", "ids", "w", "offsets", "perm"):
+            assert torch.equal(a[key], b[key]), f"run-to-run difference in {key} (T={T})"
+        # the first `sub` tokens alone (same kernel path) give bitwise the same rows
+        if sub > 16 or T <= 16:
+            c = run_forward(dl, xt[:sub].contiguous(), ws)
+            torch.cuda.synchronize()
+            assert torch.equal(c["y"], a["y"][:sub]), f"batch invariance (T={T}, sub={sub})"
+        # permuting tokens permutes outputs bitwise
+        p = torch.randperm(T, generator=torch.Generator().manual_seed(0)).cuda()
+        d = run_forward(dl, xt[p].contiguous(), ws)
+        torch.cuda.synchronize()
+        assert torch.equal(d["y"], a["y"][p]), f"token permutation (T={T})"
+
+
+def test_zero_tokens_noop(ws):
+    wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
+    dl = DeviceLayer(lw, act="bf16")
+    y = torch.full((4, SMALL.hidden), 7, dtype=torch.int16, device="cuda")
+    x = torch.zeros((4, SMALL.hidden), dtype=torch.int16, device="cuda")
+    buf = ws.get(1 << 20)
+    assert lm.lmoe_forward(dl.cfg, dl.weights, x, 0, y, None, buf, buf.numel()) == lm.LMOE_OK
+    torch.cuda.synchronize()
+    assert torch.all(y == 7)
