@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of one Edge0-145B-shaped latent-MoE layer on one MI355X; prints one JSON line.
+
+A step is one lmoe_forward (D projection, router, top-k, permutation, expert SwiGLU with the
+shared expert, combine, U projection) over one batch of synthetic tokens already resident
+in HBM.  Each timed step replays its own captured HIP graph; the graphs cycle through
+`--rotate` byte-identical copies of the layer's weights at different HBM addresses so that
+the 256 MB last-level cache cannot serve a step from the previous one.  The dominant
+kernel's duration is read from event-record nodes inside every replayed graph.
+
+Workloads (lmoe_data.WORKLOADS): decode_t8 (default, HBM-bound), prefill_t4096,
+prefill_t16384 (MFMA-bound; measured as the secondary line by default), stack48_mxfp4_t8.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "latent-MoE layer tok/s: decode T=8 (%HBM BW), 16K prefill (%MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+STAGE_UP = 5
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent handles for the stage-event hook (created through the HIP runtime)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, f"hipEventElapsedTime {rc}"
+        return ms.value
+
+
+def algorithmic_counts(wl, ids: np.ndarray):
+    """Bytes and flops the method itself needs for one layer step, from the step's own routing."""
+    s = wl.shape
+    T, H, L, E, k, F, Fs = wl.T, s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn
+    nd = int(np.unique(ids).size)
+    wb = 2  # bf16 dense weights
+    rec = s.mxfp4_record_bytes() if wl.expert == "mxfp4" else 3 * F * L * 2
+    up_w = (2 * F * L // 2 + 2 * F * L // 32) if wl.expert == "mxfp4" else 2 * F * L * 2
+    dense = (2 * H * L + E * L) * wb + E * 4 + 3 * Fs * L * wb
+    xin = T * H * (4 if wl.layers > 1 else 2)
+    yout = T * H * (4 if wl.layers > 1 else 2)
+    layer_bytes = dense + nd * rec + xin + yout
+    flops_tok = 2 * (H * L + L * E + k * 3 * F * L + 3 * Fs * L + L * H)
+    rows = T * k + (T if Fs else 0)
+    up_bytes = nd * up_w + 2 * Fs * L * wb + T * L * 2 + rows * max(F, Fs) * 2
+    up_flops = 2 * (T * k * 2 * F * L + (T * 2 * Fs * L if Fs else 0))
+    return dict(n_distinct_experts=nd, layer_bytes=layer_bytes, layer_flops=flops_tok * T, up_bytes=up_bytes,
+                up_flops=up_flops)
+
+
+def measure(wl, steps, warmup, rotate, profile_stages=True):
+    import torch
+
+    import lmoe_data as gen
+    import sparse_moe_proj_amd as lm
+    from sparse_moe_proj_amd.device import DeviceLayer, Workspace, to_device
+
+    hip = Hip()
+    t0 = time.time()
+    lw = gen.make_layer(wl, 0)
+    log(f"[bench] {wl.name}: generated layer in {time.time() - t0:.1f}s")
+    base = DeviceLayer(lw, act=wl.act)
+    del lw
+    copies = [base] + [base.clone() for _ in range(rotate - 1)]
+    x = to_device(gen.make_tokens(wl))
+    T = wl.T
+    y = torch.empty((T, wl.shape.hidden), dtype=torch.int16, device="cuda")
+    ids = torch.empty((T, wl.shape.top_k), dtype=torch.int32, device="cuda")
+    nbytes = lm.lmoe_workspace_bytes(base.cfg, T)
+    ws = Workspace("cuda").get(nbytes)
+
+    def fwd(dl, opts=None):
+        lm.check(lm.lmoe_forward(dl.cfg, dl.weights, x, T, y, opts, ws, ws.numel()))
+
+    fwd(base, lm.make_opts(aux_ids=ids))
+    torch.cuda.synchronize()
+    counts = algorithmic_counts(wl, ids.cpu().numpy())
+    for i in range(warmup):
+        fwd(copies[i % rotate])
+    torch.cuda.synchronize()
+
+    # per-stage breakdown (eager, untimed): every stage bracketed by events
+    stages_us = {}
+    if profile_stages:
+        evs = [hip.event() for _ in range(2 * lm.LMOE_N_STAGES)]
+        arr = (ctypes.c_void_p * len(evs))(*evs)
+        acc = np.zeros(lm.LMOE_N_STAGES)
+        n = max(rotate, 4)
+        for i in range(n):
+            fwd(copies[i % rotate], lm.make_opts(stage_events=arr))
+            torch.cuda.synchronize()
+            for s_ in range(1, lm.LMOE_N_STAGES):
+                acc[s_] += hip.elapsed_ms(evs[2 * s_], evs[2 * s_ + 1])
+        stages_us = {lm.STAGES[s_]: round(1e3 * acc[s_] / n, 2) for s_ in range(1, lm.LMOE_N_STAGES)}
+
+    # one graph per timed step, each with its own events around the dominant stage
+    stream = torch.cuda.Stream()
+    graphs, ev_pairs, keep = [], [], []
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            e0, e1 = hip.event(), hip.event()
+            arr = (ctypes.c_void_p * (2 * lm.LMOE_N_STAGES))()
+            arr[2 * STAGE_UP], arr[2 * STAGE_UP + 1] = e0, e1
+            opts = lm.make_opts(stage_events=arr)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fwd(copies[i % rotate], opts)
+            graphs.append(g)
+            ev_pairs.append((e0, e1))
+            keep.append(arr)
+    torch.cuda.synchronize()
+    for g in graphs[: min(len(graphs), warmup)]:
+        g.replay()
+    torch.cuda.synchronize()
+
+    t_start = time.perf_counter()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = 1e3 * (t_end - t_start) / steps
+    up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev_pairs]))
+    return dict(ms_per_step=ms_per_step, tok_s=T / (ms_per_step / 1e3), up_ms=up_ms, counts=counts,
+                stages_us=stages_us, weight_bytes_per_copy=base.nbytes())
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle as it stands (float64 numpy), on the host's cores, on whole decode steps."""
+    import lmoe_data as gen
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    lw = gen.make_layer(wl, 0)
+    x = oracle.decode(gen.make_tokens(wl), wl.act)
+    reps, tok = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        L = oracle.Layer(lw)  # includes promoting the touched weights to float64
+        oracle.block_forward(L, x)
+        reps += 1
+        tok += x.shape[0]
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(tok / dt, 3), "unit": "tok/s per layer", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} whole {wl.name} steps (T={x.shape[0]}), float64 numpy, weights promoted per step",
+            "seconds": round(dt, 2)}
+
+
+def roofline_hbm(counts, up_ms):
+    achieved = counts["up_bytes"] / (up_ms / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": "expert gate/up (stream_gemm StreamUp)", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": counts["up_bytes"], "avg_launch_us": round(up_ms * 1e3, 2)}
+
+
+def roofline_mfma(counts, up_ms):
+    achieved = counts["up_flops"] / (up_ms / 1e3) / 1e12
+    return {"bound": "mfma", "kernel": "expert gate/up (tile_gemm TileUp)", "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "flops_per_launch": counts["up_flops"], "avg_launch_us": round(up_ms * 1e3, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_t8")
+    ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--secondary", default="prefill_t16384", help="second workload line ('' = none)")
+    ap.add_argument("--secondary-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the latent-MoE block is built and measured on a single MI355X "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import lmoe_data as gen
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = gen.WORKLOADS[args.workload]
+    assert wl.layers == 1, "the stack workload is measured by its own test"
+    m = measure(wl, args.steps, args.warmup, args.rotate)
+    c = m["counts"]
+    mfma_bound = c["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > c["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
+    rl = roofline_mfma(c, m["up_ms"]) if mfma_bound else roofline_hbm(c, m["up_ms"])
+    layer_s = m["ms_per_step"] / 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(m["tok_s"], 1),
+        "unit": "tok/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens, Zipf(1.1) router bias)",
+        "config": {"workload": wl.name, "T": wl.T, "hidden": wl.shape.hidden, "latent": wl.shape.latent,
+                   "n_experts": wl.shape.n_experts, "top_k": wl.shape.top_k, "ffn": wl.shape.ffn,
+                   "shared_ffn": wl.shape.shared_ffn, "router_bias": wl.bias, "weights": wl.expert,
+                   "weight_copies": args.rotate, "hip_graph_per_step": True},
+        "roofline": rl,
+        "layer": {"bytes": c["layer_bytes"], "flops": c["layer_flops"], "n_distinct_experts": c["n_distinct_experts"],
+                  "hbm_frac": round(c["layer_bytes"] / layer_s / (HBM_PEAK_GBS * 1e9), 4),
+                  "mfma_frac": round(c["layer_flops"] / layer_s / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)},
+        "stages_us": m["stages_us"],
+    }
+    if args.secondary:
+        del m
+        torch.cuda.empty_cache()
+        wl2 = gen.WORKLOADS[args.secondary]
+        m2 = measure(wl2, args.secondary_steps, 3, 2)
+        c2 = m2["counts"]
+        s2 = m2["ms_per_step"] / 1e3
+        out["secondary"] = {
+            "workload": wl2.name, "T": wl2.T, "value": round(m2["tok_s"], 1), "unit": "tok/s per layer",
+            "ms_per_step": round(m2["ms_per_step"], 4),
+            "roofline": roofline_mfma(c2, m2["up_ms"]),
+            "layer": {"flops": c2["layer_flops"], "bytes": c2["layer_bytes"],
+                      "n_distinct_experts": c2["n_distinct_experts"],
+                      "mfma_frac": round(c2["layer_flops"] / s2 / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+                      "hbm_frac": round(c2["layer_bytes"] / s2 / (HBM_PEAK_GBS * 1e9), 4)},
+            "stages_us": m2["stages_us"],
+        }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
