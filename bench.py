@@ -3,10 +3,11 @@
 
 A step is one lmoe_forward (D projection, router, top-k, permutation, expert SwiGLU with the
 shared expert, combine, U projection) over one batch of synthetic tokens already resident
-in HBM.  Each timed step replays its own captured HIP graph; the graphs cycle through
-`--rotate` byte-identical copies of the layer's weights at different HBM addresses so that
-the 256 MB last-level cache cannot serve a step from the previous one.  The dominant
-kernel's duration is read from event-record nodes inside every replayed graph.
+in HBM.  The timed steps are enqueued back to back on one stream and cycle through
+`--rotate` byte-identical copies of the layer's weights at different HBM addresses, so the
+256 MB last-level cache cannot serve a step from the previous one.  HIP events recorded by
+the library around the dominant kernel of every timed step give its duration.  The same
+steps replayed from captured HIP graphs are timed afterwards and reported beside it.
 
 Workloads (lmoe_data.WORKLOADS): decode_t8 (default, HBM-bound), prefill_t4096,
 prefill_t16384 (MFMA-bound; measured as the secondary line by default), stack48_mxfp4_t8.
@@ -121,35 +122,43 @@ def measure(wl, steps, warmup, rotate, profile_stages=True):
                 acc[s_] += hip.elapsed_ms(evs[2 * s_], evs[2 * s_ + 1])
         stages_us = {lm.STAGES[s_]: round(1e3 * acc[s_] / n, 2) for s_ in range(1, lm.LMOE_N_STAGES)}
 
-    # one graph per timed step, each with its own events around the dominant stage
-    stream = torch.cuda.Stream()
-    graphs, ev_pairs, keep = [], [], []
-    with torch.cuda.stream(stream):
-        for i in range(steps):
-            e0, e1 = hip.event(), hip.event()
-            arr = (ctypes.c_void_p * (2 * lm.LMOE_N_STAGES))()
-            arr[2 * STAGE_UP], arr[2 * STAGE_UP + 1] = e0, e1
-            opts = lm.make_opts(stage_events=arr)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                fwd(copies[i % rotate], opts)
-            graphs.append(g)
-            ev_pairs.append((e0, e1))
-            keep.append(arr)
+    # timed region: K eager steps on one stream, events around the dominant stage of each
+    stream = torch.cuda.current_stream()
+    ev_pairs, keep = [], []
+    for i in range(steps):
+        e0, e1 = hip.event(), hip.event()
+        arr = (ctypes.c_void_p * (2 * lm.LMOE_N_STAGES))()
+        arr[2 * STAGE_UP], arr[2 * STAGE_UP + 1] = e0, e1
+        ev_pairs.append((e0, e1))
+        keep.append((arr, lm.make_opts(stage_events=arr)))
     torch.cuda.synchronize()
-    for g in graphs[: min(len(graphs), warmup)]:
-        g.replay()
-    torch.cuda.synchronize()
-
     t_start = time.perf_counter()
-    for g in graphs:
-        g.replay()
+    for i in range(steps):
+        fwd(copies[i % rotate], keep[i][1])
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = 1e3 * (t_end - t_start) / steps
     up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev_pairs]))
+
+    # the same steps replayed from captured HIP graphs (one per weight copy), for comparison
+    graphs = []
+    for r in range(rotate):
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=s2):
+            fwd(copies[r])
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    g0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % rotate].replay()
+    torch.cuda.synchronize()
+    graph_ms = 1e3 * (time.perf_counter() - g0) / steps
     return dict(ms_per_step=ms_per_step, tok_s=T / (ms_per_step / 1e3), up_ms=up_ms, counts=counts,
-                stages_us=stages_us, weight_bytes_per_copy=base.nbytes())
+                stages_us=stages_us, weight_bytes_per_copy=base.nbytes(), graph_ms_per_step=graph_ms)
 
 
 def cpu_baseline(wl, seconds):
@@ -236,12 +245,13 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "hidden": wl.shape.hidden, "latent": wl.shape.latent,
                    "n_experts": wl.shape.n_experts, "top_k": wl.shape.top_k, "ffn": wl.shape.ffn,
                    "shared_ffn": wl.shape.shared_ffn, "router_bias": wl.bias, "weights": wl.expert,
-                   "weight_copies": args.rotate, "hip_graph_per_step": True},
+                   "weight_copies": args.rotate, "timed": "eager lmoe_forward calls on one stream"},
         "roofline": rl,
         "layer": {"bytes": c["layer_bytes"], "flops": c["layer_flops"], "n_distinct_experts": c["n_distinct_experts"],
                   "hbm_frac": round(c["layer_bytes"] / layer_s / (HBM_PEAK_GBS * 1e9), 4),
                   "mfma_frac": round(c["layer_flops"] / layer_s / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)},
         "stages_us": m["stages_us"],
+        "graph_ms_per_step": round(m["graph_ms_per_step"], 5),
     }
     if args.secondary:
         del m
@@ -259,6 +269,7 @@ def main():
                       "mfma_frac": round(c2["layer_flops"] / s2 / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
                       "hbm_frac": round(c2["layer_bytes"] / s2 / (HBM_PEAK_GBS * 1e9), 4)},
             "stages_us": m2["stages_us"],
+            "graph_ms_per_step": round(m2["graph_ms_per_step"], 4),
         }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -50,7 +50,8 @@
  *   act F32,  dense F32,  expert F32     (plain fp32 path)
  *   act BF16, dense BF16, expert BF16    (bf16 storage, fp32 accumulation)
  *   act BF16, dense BF16, expert MXFP4
- * Dimension limits: hidden, latent, ffn, shared_ffn multiples of 64 (shared_ffn may be 0);
+ * Dimension limits: hidden, latent, ffn, shared_ffn multiples of 64 (shared_ffn may be 0;
+ * with MXFP4 experts latent, ffn and shared_ffn must be multiples of 128);
  * 1 <= top_k <= 16; top_k <= n_experts <= 1024; 0 <= T <= 2^20 with T*top_k < 2^31.
  */
 #ifndef LMOE_H
@@ -126,8 +127,8 @@ typedef struct {
     int32_t* aux_perm;     /* [T * top_k] the permutation (see lmoe_permute) */
     /* Optional timing hook: NULL, or an array of 2 * LMOE_N_STAGES hipEvent_t handles
      * (created by the caller; NULL entries are skipped).  Event 2s is recorded on `stream`
-     * just before stage s is enqueued and event 2s+1 just after it; under stream capture
-     * they are recorded as external event nodes, so each graph replay re-records them. */
+     * just before stage s is enqueued and event 2s+1 just after it.  The hook is ignored
+     * while `stream` is being captured into a graph. */
     void* const* stage_events;
 } lmoe_forward_opts;
 

@@ -57,6 +57,8 @@ lmoe_status check_config(const lmoe_config* cfg, Dims& d) {
         return fail(LMOE_ERR_SHAPE, "hidden, latent and ffn must be positive multiples of 64 (got %d, %d, %d)", d.H, d.L,
                     d.F);
     if (d.Fs < 0 || d.Fs % 64) return fail(LMOE_ERR_SHAPE, "shared_ffn must be 0 or a multiple of 64 (got %d)", d.Fs);
+    if (d.mx && (d.L % 128 || d.F % 128 || d.Fs % 128))
+        return fail(LMOE_ERR_SHAPE, "MXFP4 experts need latent, ffn and shared_ffn to be multiples of 128");
     if (d.k < 1 || d.k > 16) return fail(LMOE_ERR_SHAPE, "top_k must be in [1, 16] (got %d)", d.k);
     if (d.E < d.k || d.E > 1024) return fail(LMOE_ERR_SHAPE, "n_experts must be in [top_k, 1024] (got %d)", d.E);
     if ((long)d.H * d.L > (1L << 30) || (long)d.F * d.L > (1L << 30) || (long)d.Fs * d.L > (1L << 30))

@@ -69,82 +69,76 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* __restri
 }
 
 // ==============================================================================================
-// top-k + softmax over the kept logits: one wave per token.  Each lane holds the logits of
-// ids lane, lane+64, ... (E <= 1024).  k rounds of a wave arg-max (larger value, then lower id
-// wins) remove one id each; the kept ids are written in ascending order with their weights.
+// top-k + softmax over the kept logits: one wave per token.  Lane l holds the logits of ids
+// l, l+64, ... (NV per lane, E <= 64*NV).  k rounds of a wave arg-max (larger value, then lower
+// id wins) each remove one id; lane r keeps the r-th pick.  The rounds are a rolled loop so the
+// kernel stays small (a few hundred instructions).
 // ==============================================================================================
+__device__ __forceinline__ bool beats(float v, int id, float bv, int bid) { return v > bv || (v == bv && id < bid); }
+
+template <int NV>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int32_t* __restrict__ ids, float* __restrict__ w) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const float* row = logits + (size_t)t * E;
-    float v[16];
-    uint32_t removed = 0;
+    float v[NV];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < NV; ++j) {
         const int id = lane + 64 * j;
         float x = -INFINITY;
         if (id < E) {
             x = row[id];
-            if (!(x == x)) x = -INFINITY;  // NaN never wins (and never breaks the selection)
-        } else {
-            removed |= 1u << j;
+            if (!(x == x)) x = -INFINITY;  // NaN never wins and never breaks the selection
         }
         v[j] = x;
     }
-    float sv[16];
-    int sid[16];
+    uint32_t removed = 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        sv[r] = -INFINITY;
-        sid[r] = INT_MAX;
-        if (r < k) {
-            float bv = -INFINITY;
-            int bid = INT_MAX;
+    for (int j = 0; j < NV; ++j)
+        if (lane + 64 * j >= E) removed |= 1u << j;
+
+    int my_id = INT_MAX;
+    float my_v = -INFINITY, top = -INFINITY;
+#pragma unroll 1
+    for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int bid = INT_MAX;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int id = lane + 64 * j;
-                if (!((removed >> j) & 1u) && (v[j] > bv || (v[j] == bv && id < bid))) {
-                    bv = v[j];
-                    bid = id;
-                }
+        for (int j = 0; j < NV; ++j)
+            if (!((removed >> j) & 1u) && beats(v[j], lane + 64 * j, bv, bid)) {
+                bv = v[j];
+                bid = lane + 64 * j;
             }
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float ov = __shfl_xor(bv, o);
-                const int oid = __shfl_xor(bid, o);
-                if (ov > bv || (ov == bv && oid < bid)) {
-                    bv = ov;
-                    bid = oid;
-                }
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(bv, o);
+            const int oid = __shfl_xor(bid, o);
+            if (beats(ov, oid, bv, bid)) {
+                bv = ov;
+                bid = oid;
             }
-            if (bid != INT_MAX && (bid & 63) == lane) removed |= 1u << (bid >> 6);
-            sv[r] = bv;
-            sid[r] = bid;
         }
+        if (bid != INT_MAX && (bid & 63) == lane) removed |= 1u << (bid >> 6);
+        if (r == lane) {
+            my_id = bid;
+            my_v = bv;
+        }
+        if (r == 0) top = bv;  // the first pick is the largest kept logit
     }
+    // weights: softmax over the kept logits (a fixed-order butterfly sum over lanes < k)
+    float e = lane < k ? expf(my_v - top) : 0.f;
+    float den = e;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+    // rank of my pick among the k picks in ascending id
+    int rank = 0;
+#pragma unroll 1
+    for (int r = 0; r < k; ++r) rank += __shfl(my_id, r) < my_id;
     if (lane < k) {
-        int myid = 0;
-        float myv = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (r == lane) {
-                myid = sid[r];
-                myv = sv[r];
-            }
-        const float mx = sv[0];  // the first pick is the largest kept logit
-        int rank = 0;
-        float den = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            if (r < k) {
-                rank += sid[r] < myid;
-                den += expf(sv[r] - mx);
-            }
-        }
-        ids[(size_t)t * k + rank] = myid;
-        w[(size_t)t * k + rank] = expf(myv - mx) / den;
+        ids[(size_t)t * k + rank] = my_id;
+        w[(size_t)t * k + rank] = e / den;
     }
 }
 
@@ -385,7 +379,43 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const F32Seg s, int R, co
 namespace {
 inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 inline hipError_t last() { return hipGetLastError(); }
-constexpr int kStreamKS = 8;
+
+// Shapes of the weight-streaming kernels (waves per workgroup, K slices per row block).
+#ifndef LMOE_PROJ_WAVES
+#define LMOE_PROJ_WAVES 8
+#endif
+#ifndef LMOE_PROJ_KS
+#define LMOE_PROJ_KS 8
+#endif
+#ifndef LMOE_UP_WAVES
+#define LMOE_UP_WAVES 4
+#endif
+#ifndef LMOE_UP_KS
+#define LMOE_UP_KS 1
+#endif
+#ifndef LMOE_DOWN_WAVES
+#define LMOE_DOWN_WAVES 4
+#endif
+#ifndef LMOE_DOWN_KS
+#define LMOE_DOWN_KS 1
+#endif
+#ifndef LMOE_BATCH
+#define LMOE_BATCH 8
+#endif
+constexpr int kPW = LMOE_PROJ_WAVES, kPKS = LMOE_PROJ_KS;
+constexpr int kUW = LMOE_UP_WAVES, kUKS = LMOE_UP_KS;
+constexpr int kDW = LMOE_DOWN_WAVES, kDKS = LMOE_DOWN_KS;
+constexpr int kBatch = LMOE_BATCH;
+constexpr size_t kMaxLds = 64 * 1024;  // token operand staged in LDS when it fits
+
+inline size_t tok_lds(int ntl, int K, int planes) { return (size_t)planes * ntl * (K + 8) * 2; }
+
+template <int W, int KS, int NMAT, class P>
+hipError_t launch_stream(const P& p, unsigned gx, int nrows_max, size_t lds, hipStream_t s) {
+    const dim3 grid(gx, cdiv(nrows_max, 16 * (W / KS))), block(64 * W);
+    hipLaunchKernelGGL((stream_gemm_kernel<W, KS, NMAT, kBatch, P>), grid, block, P::kXLds ? lds : 0, s, p);
+    return last();
+}
 }  // namespace
 
 hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream_t s) {
@@ -396,32 +426,46 @@ hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                             uint16_t* out16, hipStream_t s) {
     if (T <= kStreamMaxT) {
-        StreamProj p{x, W, T, N, K, mode, out32, out16};
-        hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 1, StreamProj>), dim3(cdiv(T, 16), cdiv(N, 16)),
-                           dim3(64 * kStreamKS), 0, s, p);
-    } else {
-        TileProj p{x, W, T, N, K, mode, out32, out16};
-        hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileProj>), dim3(cdiv(T, 128), cdiv(N, 128)), dim3(256), 0, s, p);
+        const int ntl = std::min(16, T);
+        const size_t lds = tok_lds(ntl, K, 1);
+        if (lds <= kMaxLds)
+            return launch_stream<kPW, kPKS, 1>(StreamProj<true>{x, W, T, N, K, mode, ntl, out32, out16}, cdiv(T, 16), N,
+                                               lds, s);
+        return launch_stream<kPW, kPKS, 1>(StreamProj<false>{x, W, T, N, K, mode, ntl, out32, out16}, cdiv(T, 16), N, 0,
+                                           s);
     }
+    TileProj p{x, W, T, N, K, mode, out32, out16};
+    hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileProj>), dim3(cdiv(T, 128), cdiv(N, 128)), dim3(256), 0, s, p);
     return last();
 }
 
 hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
                               hipStream_t s) {
     if (T <= kStreamMaxT) {
-        StreamRouter p{z, Wr, br, T, E, L, logits};
-        hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 1, StreamRouter>), dim3(cdiv(T, 16), cdiv(E, 16)),
-                           dim3(64 * kStreamKS), 0, s, p);
-    } else {
-        TileRouter p{z, Wr, br, T, E, L, logits};
-        hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileRouter>), dim3(cdiv(T, 128), cdiv(E, 128)), dim3(256), 0, s,
-                           p);
+        const int ntl = std::min(16, T);
+        const size_t lds = tok_lds(ntl, L, 2);
+        if (lds <= kMaxLds)
+            return launch_stream<kPW, kPKS, 1>(StreamRouter<true>{z, Wr, br, T, E, L, ntl, logits}, cdiv(T, 16), E, lds,
+                                               s);
+        return launch_stream<kPW, kPKS, 1>(StreamRouter<false>{z, Wr, br, T, E, L, ntl, logits}, cdiv(T, 16), E, 0, s);
     }
+    TileRouter p{z, Wr, br, T, E, L, logits};
+    hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileRouter>), dim3(cdiv(T, 128), cdiv(E, 128)), dim3(256), 0, s, p);
     return last();
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
-    hipLaunchKernelGGL(topk_kernel, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, ids, w);
+    const dim3 g(cdiv(T, 4)), b(256);
+    if (E <= 64)
+        hipLaunchKernelGGL(topk_kernel<1>, g, b, 0, s, logits, T, E, k, ids, w);
+    else if (E <= 128)
+        hipLaunchKernelGGL(topk_kernel<2>, g, b, 0, s, logits, T, E, k, ids, w);
+    else if (E <= 256)
+        hipLaunchKernelGGL(topk_kernel<4>, g, b, 0, s, logits, T, E, k, ids, w);
+    else if (E <= 512)
+        hipLaunchKernelGGL(topk_kernel<8>, g, b, 0, s, logits, T, E, k, ids, w);
+    else
+        hipLaunchKernelGGL(topk_kernel<16>, g, b, 0, s, logits, T, E, k, ids, w);
     return last();
 }
 
@@ -455,42 +499,54 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
 }
 
-hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {
-    const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E};
+template <bool MX>
+hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
+    const int ntl = std::min(16, a.T);
     hipError_t err;
     ev.begin(kStageUp);
-    if (a.stream_path) {
-        const dim3 grid(a.max_tiles, cdiv(Fmax, 16)), block(64 * kStreamKS);
-        if (a.mxfp4) {
-            StreamUp<true> up{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.H};
-            hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 2, StreamUp<true>>), grid, block, 0, s, up);
-        } else {
-            StreamUp<false> up{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.H};
-            hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 2, StreamUp<false>>), grid, block, 0, s, up);
-        }
-    } else {
-        if (a.mxfp4) return hipErrorInvalidValue;  // the tile path takes bf16 experts only
-        TileUp up{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H};
-        hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileUp>), dim3(a.max_tiles, cdiv(Fmax, 64)), dim3(256), 0, s, up);
-    }
-    if ((err = last()) != hipSuccess) return err;
+    const size_t lu = tok_lds(ntl, a.L, 1);
+    if (lu <= kMaxLds)
+        err = launch_stream<kUW, kUKS, 2>(
+            StreamUp<MX, true>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, ntl, a.H}, a.max_tiles,
+            Fmax, lu, s);
+    else
+        err = launch_stream<kUW, kUKS, 2>(
+            StreamUp<MX, false>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, ntl, a.H}, a.max_tiles,
+            Fmax, 0, s);
+    if (err != hipSuccess) return err;
     ev.end(kStageUp);
     ev.begin(kStageDown);
-    if (a.stream_path) {
-        const dim3 grid(a.max_tiles, cdiv(a.L, 16)), block(64 * kStreamKS);
-        if (a.mxfp4) {
-            StreamDown<true> dn{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y};
-            hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 1, StreamDown<true>>), grid, block, 0, s, dn);
-        } else {
-            StreamDown<false> dn{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y};
-            hipLaunchKernelGGL((stream_gemm_kernel<kStreamKS, 1, StreamDown<false>>), grid, block, 0, s, dn);
-        }
-    } else {
-        TileDown dn{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y};
-        hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileDown>), dim3(a.max_tiles, cdiv(a.L, 128)), dim3(256), 0, s, dn);
-    }
+    const size_t ld = tok_lds(ntl, Fmax, 1);
+    if (ld <= kMaxLds)
+        err = launch_stream<kDW, kDKS, 1>(
+            StreamDown<MX, true>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, ntl, a.Y}, a.max_tiles,
+            a.L, ld, s);
+    else
+        err = launch_stream<kDW, kDKS, 1>(
+            StreamDown<MX, false>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, ntl, a.Y}, a.max_tiles,
+            a.L, 0, s);
+    if (err != hipSuccess) return err;
+    ev.end(kStageDown);
+    return hipSuccess;
+}
+
+hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {
+    const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E};
+    if (a.stream_path) return a.mxfp4 ? launch_stream_experts<true>(a, seg, s, ev) : launch_stream_experts<false>(a, seg, s, ev);
+    if (a.mxfp4) return hipErrorInvalidValue;  // the tile path takes bf16 experts only
+    const int Fmax = std::max(a.F, a.Fs);
+    const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
+    ev.begin(kStageUp);
+    TileUp up{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H};
+    hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileUp>), dim3(a.max_tiles, cdiv(Fmax, 64)), dim3(256), 0, s, up);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    ev.end(kStageUp);
+    ev.begin(kStageDown);
+    TileDown dn{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y};
+    hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileDown>), dim3(a.max_tiles, cdiv(a.L, 128)), dim3(256), 0, s, dn);
     if ((err = last()) != hipSuccess) return err;
     ev.end(kStageDown);
     return hipSuccess;

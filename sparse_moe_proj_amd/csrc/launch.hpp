@@ -23,10 +23,11 @@ struct StageEvents {
             if (hipStreamIsCapturing(s, &cs) == hipSuccess) capturing = cs == hipStreamCaptureStatusActive;
         }
     }
+    // Timing events are not recorded while the stream is being captured: this HIP runtime
+    // rejects event-record nodes for timing events inside a capture.
     void rec(int i) {
-        if (!ev || !ev[i]) return;
-        hipEvent_t e = static_cast<hipEvent_t>(ev[i]);
-        const hipError_t r = capturing ? hipEventRecordWithFlags(e, s, hipEventRecordExternal) : hipEventRecord(e, s);
+        if (!ev || !ev[i] || capturing) return;
+        const hipError_t r = hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
         if (r != hipSuccess && err == hipSuccess) err = r;
     }
     void begin(int stage) { rec(2 * stage); }

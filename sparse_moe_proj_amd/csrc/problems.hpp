@@ -251,22 +251,46 @@ struct TileDown {
 };
 
 // =============================================================================================
-// Stream (decode) problems: 16 weight rows x up to 16 tokens, K in 32-wide steps.
+// Stream (decode) problems: blocks of 16 weight rows x up to 16 tokens, K in 32-wide steps.
+// With kXLds the tile's tokens are staged in LDS: `ntl` rows of (K + 8) bf16 (per plane).
 // =============================================================================================
 
+// LDS token row stride in elements (16-byte pad: consecutive rows start 4 banks apart)
+__device__ __forceinline__ int xpitch(int K) { return K + 8; }
+
+// Copy `n` token rows of K bf16 (row j at rowp(j)) into LDS rows [0, ntl), zero-filling the rest.
+template <class RowFn>
+__device__ __forceinline__ void stage_rows(uint8_t* lds, int ntl, int n, int K, RowFn rowp) {
+    const int cpr = K / 8;  // 16-byte chunks per row
+    for (int c = threadIdx.x; c < ntl * cpr; c += blockDim.x) {
+        const int jj = c / cpr, kc = c - jj * cpr;
+        uint4 v = zero4();
+        if (jj < n) v = ld16(rowp(jj) + kc * 8);
+        *reinterpret_cast<uint4*>(lds + ((size_t)jj * xpitch(K) + kc * 8) * 2) = v;
+    }
+}
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* lds, int j, int pitch, int k) {
+    return *reinterpret_cast<const uint4*>(lds + ((size_t)j * pitch + k) * 2);
+}
+
 // Dense projection over token blocks of 16: mode 0 z32+z16, 1 bf16 out, 2 fp32 += out.
+template <bool XLDS>
 struct StreamProj {
+    static constexpr bool kXLds = XLDS;
+    static constexpr int kSPL = 1;
+    typedef uint4 WRaw;
+    typedef uint4 XFrag;
+    typedef const uint16_t* RowW;
+    typedef const uint16_t* RowX;
     const uint16_t* x;  // [T][K]
     const uint16_t* W;  // [N][K]
-    int T, N, K, mode;
+    int T, N, K, mode, ntl;
     float* out32;
     uint16_t* out16;
     struct Ctx { int t0, nt; };
-    typedef const uint16_t* RowW;
-    typedef const uint16_t* RowX;
-    typedef uint4 XFrag;
-    __device__ bool tile(int by, Ctx& c) const {
-        c.t0 = by * 16;
+    __device__ bool tile(int bx, Ctx& c) const {
+        c.t0 = bx * 16;
         c.nt = min(16, T - c.t0);
         return c.nt > 0;
     }
@@ -274,9 +298,16 @@ struct StreamProj {
     __device__ int k_steps(const Ctx&) const { return K / 32; }
     __device__ RowW row_w(const Ctx&, int n) const { return n < N ? W + (size_t)n * K : nullptr; }
     __device__ RowX row_x(const Ctx& c, int j) const { return j < c.nt ? x + (size_t)(c.t0 + j) * K : nullptr; }
-    __device__ uint4 load_w(const Ctx&, RowW r, int, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
-    __device__ XFrag load_x(const Ctx&, RowX r, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
-    __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag x) { return mfma16(w, x, a); }
+    __device__ WRaw load_w(const Ctx&, RowW r, int, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
+    __device__ uint4 wfrag_ctx(const Ctx&, const WRaw& w, int) const { return w; }
+    __device__ XFrag load_x(const Ctx&, RowX r, int k) const { return r ? ld16(r + k) : zero4(); }
+    __device__ void stage_x(const Ctx& c, uint8_t* lds) const {
+        stage_rows(lds, ntl, c.nt, K, [&](int jj) { return x + (size_t)(c.t0 + jj) * K; });
+    }
+    __device__ XFrag lds_frag(const Ctx& c, const uint8_t* lds, int j, int k) const {
+        return j < c.nt ? lds16(lds, j, xpitch(K), k) : zero4();
+    }
+    __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv, a); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n >= N || j >= c.nt) return;
         const size_t o = (size_t)(c.t0 + j) * N + n;
@@ -293,19 +324,24 @@ struct StreamProj {
 
 struct HiLo { uint4 hi, lo; };
 
-// Router logits from fp32 z (hi/lo bf16 split of the token operand).
+// Router logits from fp32 z (hi/lo bf16 split of the token operand; LDS holds the hi plane
+// then the lo plane, ntl rows each).
+template <bool XLDS>
 struct StreamRouter {
+    static constexpr bool kXLds = XLDS;
+    static constexpr int kSPL = 1;
+    typedef uint4 WRaw;
+    typedef HiLo XFrag;
+    typedef const uint16_t* RowW;
+    typedef const float* RowX;
     const float* z;
     const uint16_t* W;
     const float* bias;
-    int T, N, K;
+    int T, N, K, ntl;
     float* logits;
     struct Ctx { int t0, nt; };
-    typedef const uint16_t* RowW;
-    typedef const float* RowX;
-    typedef HiLo XFrag;
-    __device__ bool tile(int by, Ctx& c) const {
-        c.t0 = by * 16;
+    __device__ bool tile(int bx, Ctx& c) const {
+        c.t0 = bx * 16;
         c.nt = min(16, T - c.t0);
         return c.nt > 0;
     }
@@ -313,180 +349,240 @@ struct StreamRouter {
     __device__ int k_steps(const Ctx&) const { return K / 32; }
     __device__ RowW row_w(const Ctx&, int n) const { return n < N ? W + (size_t)n * K : nullptr; }
     __device__ RowX row_x(const Ctx& c, int j) const { return j < c.nt ? z + (size_t)(c.t0 + j) * K : nullptr; }
-    __device__ uint4 load_w(const Ctx&, RowW r, int, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
-    __device__ XFrag load_x(const Ctx&, RowX r, int s, int kq) const {
+    __device__ WRaw load_w(const Ctx&, RowW r, int, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
+    __device__ uint4 wfrag_ctx(const Ctx&, const WRaw& w, int) const { return w; }
+    __device__ XFrag load_x(const Ctx&, RowX r, int k) const {
         HiLo h;
         if (!r) {
             h.hi = h.lo = zero4();
         } else {
-            h.hi = f32x8_to_bf16_part(r + s * 32 + kq * 8, false);
-            h.lo = f32x8_to_bf16_part(r + s * 32 + kq * 8, true);
+            h.hi = f32x8_to_bf16_part(r + k, false);
+            h.lo = f32x8_to_bf16_part(r + k, true);
         }
         return h;
     }
-    __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag x) { return mfma16(w, x.lo, mfma16(w, x.hi, a)); }
+    __device__ void stage_x(const Ctx& c, uint8_t* lds) const {
+        const int cpr = K / 8;
+        const size_t plane = (size_t)ntl * xpitch(K) * 2;
+        for (int q = threadIdx.x; q < ntl * cpr; q += blockDim.x) {
+            const int jj = q / cpr, kc = q - jj * cpr;
+            uint4 hi = zero4(), lo = zero4();
+            if (jj < c.nt) {
+                const float* src = z + (size_t)(c.t0 + jj) * K + kc * 8;
+                hi = f32x8_to_bf16_part(src, false);
+                lo = f32x8_to_bf16_part(src, true);
+            }
+            const size_t off = ((size_t)jj * xpitch(K) + kc * 8) * 2;
+            *reinterpret_cast<uint4*>(lds + off) = hi;
+            *reinterpret_cast<uint4*>(lds + plane + off) = lo;
+        }
+    }
+    __device__ XFrag lds_frag(const Ctx& c, const uint8_t* lds, int j, int k) const {
+        HiLo h;
+        if (j < c.nt) {
+            h.hi = lds16(lds, j, xpitch(K), k);
+            h.lo = lds16(lds + (size_t)ntl * xpitch(K) * 2, j, xpitch(K), k);
+        } else {
+            h.hi = h.lo = zero4();
+        }
+        return h;
+    }
+    __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv.lo, mfma16(w, xv.hi, a)); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n < N && j < c.nt) logits[(size_t)(c.t0 + j) * N + n] = v[0] + (bias ? bias[n] : 0.f);
     }
 };
 
-// Weight-row addressing for one expert matrix in bf16 or MXFP4.
+// ---------------------------------------------------------------------------------------------
+// Expert weights for the stream kernels.
+//   bf16 records: one MFMA step per load (kSPL 1), 16 bytes per lane.
+//   MXFP4 records: four MFMA steps per load (kSPL 4): lane (row, kq) reads 16 bytes of packed
+//   nibbles = the 32 values k in [128g + 32kq, +32) and their one scale byte; step t of the
+//   group uses values 8t..8t+7 of them.  In MXFP4 kernels the (bf16) shared expert is read in
+//   the same k order: 64 bytes per lane per group.
+// ---------------------------------------------------------------------------------------------
+struct WRaw4 { uint4 a[4]; };
+
 template <bool MX>
-struct WRow;
+struct ExpertRows;
+
 template <>
-struct WRow<false> {
-    const uint16_t* p;
-    __device__ uint4 load(int s, int kq) const { return p ? ld16(p + s * 32 + kq * 8) : zero4(); }
+struct ExpertRows<false> {
+    static constexpr int kSPL = 1;
+    typedef uint4 WRaw;
+    struct Mat { const uint16_t* p; };     // matrix base, rows of K elements
+    struct Row { const uint16_t* p; };
+    __device__ static Row row(const Mat& m, int n, int K) { return Row{m.p ? m.p + (size_t)n * K : nullptr}; }
+    __device__ static WRaw load(const Row& r, bool, int s, int kq) { return r.p ? ld16(r.p + s * 32 + kq * 8) : zero4(); }
+    __device__ static uint4 frag(const WRaw& w, bool, int) { return w; }
 };
+
 template <>
-struct WRow<true> {
-    const uint8_t* nib;  // row's packed nibbles (K/2 bytes)
-    const uint8_t* sc;   // row's scale bytes (K/32)
-    __device__ uint4 load(int s, int kq) const {
-        if (!nib) return zero4();
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(nib + s * 16 + kq * 4);
-        return mxfp4_to_bf16x8(w, sc[s]);
+struct ExpertRows<true> {
+    static constexpr int kSPL = 4;
+    typedef WRaw4 WRaw;
+    struct Mat { const uint8_t* p; const uint8_t* sc; };  // sc == null: bf16 matrix (shared expert)
+    struct Row { const uint8_t* p; const uint8_t* sc; };
+    __device__ static Row row(const Mat& m, int n, int K) {
+        if (!m.p) return Row{nullptr, nullptr};
+        if (m.sc) return Row{m.p + (size_t)n * (K / 2), m.sc + (size_t)n * (K / 32)};
+        return Row{m.p + (size_t)n * K * 2, nullptr};
+    }
+    __device__ static WRaw load(const Row& r, bool mx, int g, int kq) {
+        WRaw w;
+        if (!r.p) {
+            w.a[0] = w.a[1] = w.a[2] = w.a[3] = zero4();
+        } else if (mx) {
+            w.a[0] = ld16(r.p + g * 64 + kq * 16);
+            w.a[1] = make_uint4(r.sc[g * 4 + kq], 0, 0, 0);
+        } else {
+            const uint8_t* b = r.p + (size_t)(g * 128 + kq * 32) * 2;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) w.a[t] = ld16(b + t * 16);
+        }
+        return w;
+    }
+    __device__ static uint4 frag(const WRaw& w, bool mx, int t) {
+        if (!mx) return w.a[t];
+        const uint32_t nib = t == 0 ? w.a[0].x : t == 1 ? w.a[0].y : t == 2 ? w.a[0].z : w.a[0].w;
+        return mxfp4_to_bf16x8(nib, w.a[1].x);
     }
 };
 
-// Locations of one routed expert's three matrices.
+// Matrices of the segment a tile belongs to: the routed expert `seg` or the shared expert.
 template <bool MX>
-struct ExpertMats;
-template <>
-struct ExpertMats<false> {
-    const uint16_t *g, *u, *d;
-    __device__ static ExpertMats make(const void* base, size_t rec_bytes, int e, int F, int L) {
-        const uint16_t* b = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + (size_t)e * rec_bytes);
-        return ExpertMats{b, b + (size_t)F * L, b + 2 * (size_t)F * L};
+__device__ __forceinline__ void segment_mats(const void* experts, size_t rec_bytes, const uint16_t* shared, int seg,
+                                             int E, int F, int Fs, int L, typename ExpertRows<MX>::Mat (&m)[3],
+                                             int& Fseg, bool& mx) {
+    if (seg == E) {
+        Fseg = Fs;
+        mx = false;
+        const size_t fl = (size_t)Fs * L;
+        if constexpr (MX) {
+            const uint8_t* b = reinterpret_cast<const uint8_t*>(shared);
+            m[0] = {b, nullptr};
+            m[1] = {b + fl * 2, nullptr};
+            m[2] = {b + 2 * fl * 2, nullptr};
+        } else {
+            m[0] = {shared};
+            m[1] = {shared + fl};
+            m[2] = {shared + 2 * fl};
+        }
+    } else {
+        Fseg = F;
+        mx = MX;
+        const uint8_t* b = reinterpret_cast<const uint8_t*>(experts) + (size_t)seg * rec_bytes;
+        const size_t fl = (size_t)F * L;
+        if constexpr (MX) {
+            const size_t nb = fl / 2, sb = fl / 32;
+            m[0] = {b, b + 3 * nb};
+            m[1] = {b + nb, b + 3 * nb + sb};
+            m[2] = {b + 2 * nb, b + 3 * nb + 2 * sb};
+        } else {
+            const uint16_t* h = reinterpret_cast<const uint16_t*>(b);
+            m[0] = {h};
+            m[1] = {h + fl};
+            m[2] = {h + 2 * fl};
+        }
     }
-    __device__ WRow<false> gate(int n, int L) const { return WRow<false>{g + (size_t)n * L}; }
-    __device__ WRow<false> up(int n, int L) const { return WRow<false>{u + (size_t)n * L}; }
-    __device__ WRow<false> down(int n, int F) const { return WRow<false>{d + (size_t)n * F}; }
-};
-template <>
-struct ExpertMats<true> {
-    const uint8_t *g, *u, *d, *gs, *us, *ds;
-    __device__ static ExpertMats make(const void* base, size_t rec_bytes, int e, int F, int L) {
-        const uint8_t* b = reinterpret_cast<const uint8_t*>(base) + (size_t)e * rec_bytes;
-        const size_t nb = (size_t)F * L / 2, sb = (size_t)F * L / 32;
-        return ExpertMats{b, b + nb, b + 2 * nb, b + 3 * nb, b + 3 * nb + sb, b + 3 * nb + 2 * sb};
-    }
-    __device__ WRow<true> gate(int n, int L) const { return WRow<true>{g + (size_t)n * (L / 2), gs + (size_t)n * (L / 32)}; }
-    __device__ WRow<true> up(int n, int L) const { return WRow<true>{u + (size_t)n * (L / 2), us + (size_t)n * (L / 32)}; }
-    __device__ WRow<true> down(int n, int F) const { return WRow<true>{d + (size_t)n * (F / 2), ds + (size_t)n * (F / 32)}; }
-};
+}
 
-// Fused gate/up (NMAT = 2) over a work list of <= 16-row tiles; MX: routed experts in MXFP4
-// (the shared expert is always bf16).
-template <bool MX>
+// Fused gate/up (NMAT = 2) over a work list of <= 16-row tiles: H = SiLU(z gate^T) * (z up^T).
+template <bool MX, bool XLDS>
 struct StreamUp {
+    using ER = ExpertRows<MX>;
+    static constexpr bool kXLds = XLDS;
+    static constexpr int kSPL = ER::kSPL;
+    typedef typename ER::WRaw WRaw;
+    typedef uint4 XFrag;
+    struct RowW { typename ER::Row g, u; };
+    typedef const uint16_t* RowX;
     SegSpace seg;
     const uint16_t* z16;
     const void* experts;
     size_t rec_bytes;
     const uint16_t* shared;
-    int L, F, Fs, Hs;
+    int L, F, Fs, Hs, ntl;
     uint16_t* H;
-    struct Ctx { int seg, row0, nrows, F; ExpertMats<MX> em; ExpertMats<false> sm; };
-    struct RowW { WRow<MX> g, u; WRow<false> sg, su; bool sh; };
-    typedef const uint16_t* RowX;
-    typedef uint4 XFrag;
-    __device__ bool tile(int by, Ctx& c) const {
-        if (by >= *seg.ntiles) return false;
-        const Tile t = seg.tiles[by];
+    struct Ctx { int seg, row0, nrows, F; bool mx; typename ER::Mat m[3]; };
+    __device__ bool tile(int bx, Ctx& c) const {
+        if (bx >= *seg.ntiles) return false;
+        const Tile t = seg.tiles[bx];
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
-        if (t.seg == seg.E) {
-            c.F = Fs;
-            c.sm = ExpertMats<false>{shared, shared + (size_t)Fs * L, shared + 2 * (size_t)Fs * L};
-        } else {
-            c.F = F;
-            c.em = ExpertMats<MX>::make(experts, rec_bytes, t.seg, F, L);
-        }
+        segment_mats<MX>(experts, rec_bytes, shared, t.seg, seg.E, F, Fs, L, c.m, c.F, c.mx);
         return true;
     }
     __device__ int n_rows(const Ctx& c) const { return c.F; }
     __device__ int k_steps(const Ctx&) const { return L / 32; }
     __device__ RowW row_w(const Ctx& c, int n) const {
-        RowW r;
-        r.sh = c.seg == seg.E;
-        if (n >= c.F) {
-            r.g = WRow<MX>{};
-            r.u = WRow<MX>{};
-            r.sg = r.su = WRow<false>{nullptr};
-            r.sh = true;
-        } else if (r.sh) {
-            r.sg = c.sm.gate(n, L);
-            r.su = c.sm.up(n, L);
-        } else {
-            r.g = c.em.gate(n, L);
-            r.u = c.em.up(n, L);
-        }
-        return r;
+        if (n >= c.F) return RowW{ER::row(typename ER::Mat{}, 0, L), ER::row(typename ER::Mat{}, 0, L)};
+        return RowW{ER::row(c.m[0], n, L), ER::row(c.m[1], n, L)};
     }
     __device__ RowX row_x(const Ctx& c, int j) const {
         return j < c.nrows ? z16 + (size_t)seg.token_of(c.seg, c.row0 + j) * L : nullptr;
     }
-    __device__ uint4 load_w(const Ctx&, const RowW& r, int m, int s, int kq) const {
-        if (r.sh) return m == 0 ? r.sg.load(s, kq) : r.su.load(s, kq);
-        return m == 0 ? r.g.load(s, kq) : r.u.load(s, kq);
+    __device__ WRaw load_w(const Ctx& c, const RowW& r, int m, int g, int kq) const {
+        return ER::load(m == 0 ? r.g : r.u, c.mx, g, kq);
     }
-    __device__ XFrag load_x(const Ctx&, RowX r, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
-    __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag x) { return mfma16(w, x, a); }
+    __device__ uint4 wfrag_ctx(const Ctx& c, const WRaw& w, int t) const { return ER::frag(w, c.mx, t); }
+    __device__ XFrag load_x(const Ctx&, RowX r, int k) const { return r ? ld16(r + k) : zero4(); }
+    __device__ void stage_x(const Ctx& c, uint8_t* lds) const {
+        stage_rows(lds, ntl, c.nrows, L, [&](int jj) { return z16 + (size_t)seg.token_of(c.seg, c.row0 + jj) * L; });
+    }
+    __device__ XFrag lds_frag(const Ctx& c, const uint8_t* lds, int j, int k) const {
+        return j < c.nrows ? lds16(lds, j, xpitch(L), k) : zero4();
+    }
+    __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv, a); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n < c.F && j < c.nrows) H[(size_t)(c.row0 + j) * Hs + n] = (uint16_t)f2bf(silu(v[0]) * v[1]);
     }
 };
 
-template <bool MX>
+// Down projection over a work list: Y[dest(p)][n] = H[p] . down[n].
+template <bool MX, bool XLDS>
 struct StreamDown {
+    using ER = ExpertRows<MX>;
+    static constexpr bool kXLds = XLDS;
+    static constexpr int kSPL = ER::kSPL;
+    typedef typename ER::WRaw WRaw;
+    typedef uint4 XFrag;
+    typedef typename ER::Row RowW;
+    typedef const uint16_t* RowX;
     SegSpace seg;
     const uint16_t* H;
     const void* experts;
     size_t rec_bytes;
     const uint16_t* shared;
-    int L, F, Fs, Hs;
+    int L, F, Fs, Hs, ntl;
     float* Y;
-    struct Ctx { int seg, row0, nrows, F; ExpertMats<MX> em; ExpertMats<false> sm; };
-    struct RowW { WRow<MX> d; WRow<false> sd; bool sh; };
-    typedef const uint16_t* RowX;
-    typedef uint4 XFrag;
-    __device__ bool tile(int by, Ctx& c) const {
-        if (by >= *seg.ntiles) return false;
-        const Tile t = seg.tiles[by];
+    struct Ctx { int seg, row0, nrows, F; bool mx; typename ER::Mat m[3]; };
+    __device__ bool tile(int bx, Ctx& c) const {
+        if (bx >= *seg.ntiles) return false;
+        const Tile t = seg.tiles[bx];
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
-        if (t.seg == seg.E) {
-            c.F = Fs;
-            c.sm = ExpertMats<false>{shared, shared + (size_t)Fs * L, shared + 2 * (size_t)Fs * L};
-        } else {
-            c.F = F;
-            c.em = ExpertMats<MX>::make(experts, rec_bytes, t.seg, F, L);
-        }
+        segment_mats<MX>(experts, rec_bytes, shared, t.seg, seg.E, F, Fs, L, c.m, c.F, c.mx);
         return true;
     }
     __device__ int n_rows(const Ctx&) const { return L; }
     __device__ int k_steps(const Ctx& c) const { return c.F / 32; }
     __device__ RowW row_w(const Ctx& c, int n) const {
-        RowW r;
-        r.sh = c.seg == seg.E;
-        if (n >= L) {
-            r.d = WRow<MX>{};
-            r.sd = WRow<false>{nullptr};
-            r.sh = true;
-        } else if (r.sh) {
-            r.sd = c.sm.down(n, c.F);
-        } else {
-            r.d = c.em.down(n, c.F);
-        }
-        return r;
+        return n < L ? ER::row(c.m[2], n, c.F) : ER::row(typename ER::Mat{}, 0, c.F);
     }
     __device__ RowX row_x(const Ctx& c, int j) const { return j < c.nrows ? H + (size_t)(c.row0 + j) * Hs : nullptr; }
-    __device__ uint4 load_w(const Ctx&, const RowW& r, int, int s, int kq) const { return r.sh ? r.sd.load(s, kq) : r.d.load(s, kq); }
-    __device__ XFrag load_x(const Ctx&, RowX r, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
-    __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag x) { return mfma16(w, x, a); }
+    __device__ WRaw load_w(const Ctx& c, const RowW& r, int, int g, int kq) const { return ER::load(r, c.mx, g, kq); }
+    __device__ uint4 wfrag_ctx(const Ctx& c, const WRaw& w, int t) const { return ER::frag(w, c.mx, t); }
+    __device__ XFrag load_x(const Ctx&, RowX r, int k) const { return r ? ld16(r + k) : zero4(); }
+    __device__ void stage_x(const Ctx& c, uint8_t* lds) const {
+        stage_rows(lds, ntl, c.nrows, c.F, [&](int jj) { return H + (size_t)(c.row0 + jj) * Hs; });
+    }
+    __device__ XFrag lds_frag(const Ctx& c, const uint8_t* lds, int j, int k) const {
+        return j < c.nrows ? lds16(lds, j, xpitch(c.F), k) : zero4();
+    }
+    __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv, a); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n >= L || j >= c.nrows) return;
         const int drow = seg.dest_of(c.seg, c.row0 + j);

@@ -67,6 +67,8 @@ def test_workspace_sizes_monotone():
     (dict(n_experts=5, top_k=10), lm.LMOE_ERR_SHAPE),
     (dict(n_experts=2048), lm.LMOE_ERR_SHAPE),
     (dict(shared_ffn=32), lm.LMOE_ERR_SHAPE),
+    (dict(expert="mxfp4", latent=192), lm.LMOE_ERR_SHAPE),
+    (dict(expert="mxfp4", shared_ffn=64), lm.LMOE_ERR_SHAPE),
     (dict(act="f32"), lm.LMOE_ERR_UNSUPPORTED),
     (dict(expert="f32"), lm.LMOE_ERR_UNSUPPORTED),
 ])

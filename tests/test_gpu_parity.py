@@ -66,9 +66,12 @@ def test_small_bf16_ragged(T, ws):
     check_block(lw, x, "bf16", out, label=f"small_bf16 T={T}")
 
 
+SMALL_MX = gen.Shape(hidden=256, latent=256, n_experts=24, top_k=3, ffn=128, shared_ffn=128)
+
+
 @pytest.mark.parametrize("T", [3, 16, 40])
 def test_small_mxfp4(T, ws):
-    wl, lw = small_layer(SMALL, "bf16", "bf16", "mxfp4")
+    wl, lw = small_layer(SMALL_MX, "bf16", "bf16", "mxfp4")
     dl = DeviceLayer(lw, act="bf16")
     x = gen.make_tokens(wl, T=T, salt=T)
     out = run_forward(dl, upload_tokens(x), ws)
