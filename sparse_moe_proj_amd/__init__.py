@@ -47,6 +47,10 @@ class lmoe_forward_opts(ctypes.Structure):
 
 
 def _load():
+    # torch is imported first so that its HIP runtime is the one in the process: liblmoe.so
+    # then binds to it (same soname) instead of loading a second runtime that would not share
+    # torch's device memory and streams.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_moe_proj_amd.build` "
                           "(or __graft_entry__.build()) first")

@@ -131,3 +131,10 @@ def test_zero_tokens_is_a_noop_without_device_access():
     nothing = lm.make_weights(None, None, None, None, None, None)
     assert lm.lmoe_forward(cfg(), nothing, None, 0, None, None, None, 0, 0) == lm.LMOE_OK
     assert lm.lmoe_route(cfg(), nothing, None, 0, None, None, None, 0, 0) == lm.LMOE_OK
+
+
+def test_single_hip_runtime_in_process():
+    """The library must share torch's HIP runtime: one libamdhip64 mapped in the process."""
+    with open("/proc/self/maps") as f:
+        libs = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(libs) == 1, libs
