@@ -212,6 +212,8 @@ def main():
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB once (calibrates HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the latent-MoE block is built and measured on a single MI355X "
@@ -271,6 +273,13 @@ def main():
             "stages_us": m2["stages_us"],
             "graph_ms_per_step": round(m2["graph_ms_per_step"], 4),
         }
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

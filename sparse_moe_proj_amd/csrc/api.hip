@@ -76,7 +76,8 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t x16, z32, z16, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, m, total;
+    size_t x16, z32, z16, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, counters, H, Y, m, total;
+    int ncounters;  // fused small-batch expert launch: per-tile and per-row-group counters, then status
     bool stream_path;
     int max_tiles, BM, Hs, R;
 };
@@ -110,6 +111,8 @@ Layout plan(const Dims& d, int T) {
     lo.base = take(nb * d.E * 4);
     lo.tiles = take((size_t)lo.max_tiles * sizeof(Tile));
     lo.ntiles = take(4);
+    lo.ncounters = lo.stream_path ? lo.max_tiles + fused_down_groups(d.L) + 1 : 0;
+    lo.counters = take((size_t)lo.ncounters * 4);
     lo.H = take((size_t)lo.R * lo.Hs * act);
     lo.Y = take((size_t)lo.R * d.L * 4);
     lo.m = take((size_t)T * d.L * act);
@@ -205,7 +208,8 @@ lmoe_status lmoe_permute(const lmoe_config* cfg, const int32_t* ids, int32_t T, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* hist = static_cast<int32_t*>(ws);
     int32_t* base = need ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2) : nullptr;
-    const hipError_t e = launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, 16, nullptr, nullptr, 0, s);
+    const hipError_t e =
+        launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, 16, nullptr, nullptr, 0, nullptr, 0, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "permute");
     return LMOE_OK;
 }
@@ -225,7 +229,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         return fail(LMOE_ERR_NULL, "x, y, D, U, Wr and experts must be non-NULL");
     if (d.Fs > 0 && !wt->shared) return fail(LMOE_ERR_NULL, "shared_ffn > 0 but the shared expert record is NULL");
     const void* ptrs[] = {x, y, wt->D, wt->U, wt->Wr, wt->experts, wt->shared, ws, o.aux_z, o.aux_ids, o.aux_w,
-                          o.aux_offsets, o.aux_perm};
+                          o.aux_offsets, o.aux_perm, o.aux_status};
     for (const void* p : ptrs)
         if (!aligned16(p)) return fail(LMOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(wt->br) & 3u) return fail(LMOE_ERR_ALIGN, "br must be 4-byte aligned");
@@ -271,7 +275,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         ev.end(LMOE_STAGE_TOPK);
         ev.begin(LMOE_STAGE_PERMUTE);
         if ((e = launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, lo.BM, nullptr, nullptr, has_shared,
-                                s)) != hipSuccess)
+                                nullptr, 0, o.aux_status, s)) != hipSuccess)
             return hip_fail(e, "permute");
         ev.end(LMOE_STAGE_PERMUTE);
         F32ExpertArgs a{z32, ids, perm, static_cast<const float*>(wt->experts), static_cast<const float*>(wt->shared),
@@ -306,21 +310,25 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     if ((e = launch_router_bf16(z32, static_cast<const uint16_t*>(wt->Wr), wt->br, T, d.E, d.L, logits, s)) != hipSuccess)
         return hip_fail(e, "router logits");
     ev.end(LMOE_STAGE_ROUTER);
+    // top-k and permutation (one launch for small batches: the TOPK stage events bracket both)
+    int32_t* counters = static_cast<int32_t*>(at(lo.counters));
+    int32_t* status = o.aux_status ? o.aux_status : (lo.ncounters ? counters + lo.ncounters - 1 : nullptr);
     ev.begin(LMOE_STAGE_TOPK);
-    if ((e = launch_topk(logits, T, d.E, d.k, ids, wts, s)) != hipSuccess) return hip_fail(e, "top-k");
+    if ((e = launch_topk_permute(logits, T, d.E, d.k, ids, wts, hist, base, offsets, perm, inv, lo.BM, tiles, ntiles,
+                                 has_shared, counters, lo.ncounters, o.aux_status, s)) != hipSuccess)
+        return hip_fail(e, "top-k / permute");
     ev.end(LMOE_STAGE_TOPK);
-    ev.begin(LMOE_STAGE_PERMUTE);
-    if ((e = launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, lo.BM, tiles, ntiles, has_shared, s)) !=
-        hipSuccess)
-        return hip_fail(e, "permute");
-    ev.end(LMOE_STAGE_PERMUTE);
-    ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
-                 wt->shared, static_cast<uint16_t*>(at(lo.H)), Y, lo.max_tiles, lo.stream_path, d.mx};
-    if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
-    ev.begin(LMOE_STAGE_COMBINE);
-    if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, true, m16, s)) != hipSuccess) return hip_fail(e, "combine");
-    ev.end(LMOE_STAGE_COMBINE);
+    ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
+                 wt->shared, static_cast<uint16_t*>(at(lo.H)), Y, lo.max_tiles, lo.stream_path, d.mx,
+                 counters, status, wts, m16};
+    if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
+    if (!lo.stream_path) {  // the small-batch expert launch merges in place
+        ev.begin(LMOE_STAGE_COMBINE);
+        if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, true, m16, s)) != hipSuccess)
+            return hip_fail(e, "combine");
+        ev.end(LMOE_STAGE_COMBINE);
+    }
     ev.begin(LMOE_STAGE_U);
     if ((e = launch_proj_bf16(m16, static_cast<const uint16_t*>(wt->U), T, d.H, d.L, o.residual ? 2 : 1,
                               static_cast<float*>(y), static_cast<uint16_t*>(y), s)) != hipSuccess)

@@ -2,6 +2,7 @@
 // launch wrappers for everything (no allocation, no synchronisation: enqueue only).
 #include <limits.h>
 
+#include "fused_experts.hpp"
 #include "gemm_stream.hpp"
 #include "gemm_tile.hpp"
 #include "launch.hpp"
@@ -69,20 +70,66 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* __restri
 }
 
 // ==============================================================================================
-// top-k + softmax over the kept logits: one wave per token.  Lane l holds the logits of ids
-// l, l+64, ... (NV per lane, E <= 64*NV).  k rounds of a wave arg-max (larger value, then lower
-// id wins) each remove one id; lane r keeps the r-th pick.  The rounds are a rolled loop so the
-// kernel stays small (a few hundred instructions).
+// top-k + softmax over the kept logits, one wave per token.  Lane l holds the logits of ids
+// l, l+64, ... (NV per lane, E <= 64*NV) as order-preserving 32-bit keys.  A most-significant-
+// bit-first radix select finds the k-th largest key with one ballot + popcount per value and
+// bit (no cross-lane data movement); every larger key is kept, plus the lowest ids among the
+// keys equal to it, which is "larger value wins, lower id wins a tie".  The kept ids are written
+// in ascending order with softmax weights over their logits.
 // ==============================================================================================
-__device__ __forceinline__ bool beats(float v, int id, float bv, int bid) { return v > bv || (v == bv && id < bid); }
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+// Selects the top k of a wave's NV-per-lane logits.  Returns, per value j, whether it is kept
+// and its rank among the kept ids (ascending id).  Also returns the largest kept logit.
+template <int NV>
+__device__ __forceinline__ void wave_topk(const float (&v)[NV], int E, int k, bool (&keep)[NV], int (&pos)[NV],
+                                          float& vmax) {
+    const int lane = threadIdx.x & 63;
+    uint32_t key[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) key[j] = (lane + 64 * j < E) ? order_key(v[j]) : 0u;  // valid keys are > 0
+    uint32_t prefix = 0;
+    int remaining = k;
+#pragma unroll 1
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t want = (prefix >> b) | 1u;
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) cnt += popc64(__ballot((key[j] >> b) == want));
+        if (cnt >= remaining)
+            prefix |= 1u << b;
+        else
+            remaining -= cnt;
+    }
+    // prefix is the k-th largest key; `remaining` keys equal to it are kept (lowest ids first)
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int eq_before = 0, sel_before = 0;
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const uint64_t eq = __ballot(key[j] == prefix);
+        const bool take_eq = key[j] == prefix && eq_before + popc64(eq & lt) < remaining;
+        eq_before += popc64(eq);
+        keep[j] = key[j] > prefix || take_eq;
+        const uint64_t sel = __ballot(keep[j]);
+        pos[j] = sel_before + popc64(sel & lt);
+        sel_before += popc64(sel);
+        if (keep[j]) m = fmaxf(m, v[j]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    vmax = m;
+}
 
 template <int NV>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                   int32_t* __restrict__ ids, float* __restrict__ w) {
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids,
+                                           float* __restrict__ w) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float* row = logits + (size_t)t * E;
     float v[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -94,52 +141,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         }
         v[j] = x;
     }
-    uint32_t removed = 0;
+    bool keep[NV];
+    int pos[NV];
+    float vmax;
+    wave_topk<NV>(v, E, k, keep, pos, vmax);
+    float e[NV], s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        e[j] = keep[j] ? expf(v[j] - vmax) : 0.f;
+        s += e[j];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-        if (lane + 64 * j >= E) removed |= 1u << j;
+        if (keep[j]) {
+            ids[pos[j]] = lane + 64 * j;
+            w[pos[j]] = e[j] / s;
+        }
+}
 
-    int my_id = INT_MAX;
-    float my_v = -INFINITY, top = -INFINITY;
-#pragma unroll 1
-    for (int r = 0; r < k; ++r) {
-        float bv = -INFINITY;
-        int bid = INT_MAX;
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-            if (!((removed >> j) & 1u) && beats(v[j], lane + 64 * j, bv, bid)) {
-                bv = v[j];
-                bid = lane + 64 * j;
-            }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(bv, o);
-            const int oid = __shfl_xor(bid, o);
-            if (beats(ov, oid, bv, bid)) {
-                bv = ov;
-                bid = oid;
-            }
-        }
-        if (bid != INT_MAX && (bid & 63) == lane) removed |= 1u << (bid >> 6);
-        if (r == lane) {
-            my_id = bid;
-            my_v = bv;
-        }
-        if (r == 0) top = bv;  // the first pick is the largest kept logit
-    }
-    // weights: softmax over the kept logits (a fixed-order butterfly sum over lanes < k)
-    float e = lane < k ? expf(my_v - top) : 0.f;
-    float den = e;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
-    // rank of my pick among the k picks in ascending id
-    int rank = 0;
-#pragma unroll 1
-    for (int r = 0; r < k; ++r) rank += __shfl(my_id, r) < my_id;
-    if (lane < k) {
-        ids[(size_t)t * k + rank] = my_id;
-        w[(size_t)t * k + rank] = e / den;
-    }
+template <int NV>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                   int32_t* __restrict__ ids, float* __restrict__ w) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    topk_token<NV>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
 // ==============================================================================================
@@ -200,14 +227,13 @@ __device__ void write_tiles(int e_cnt, int e_off, int e, int E, int T, int k, in
     if (threadIdx.x == 0) *ntiles = ntot + nsh;
 }
 
-// Whole permutation in one workgroup (T <= 64 tokens).
-__global__ __launch_bounds__(1024) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                           int32_t* __restrict__ inv, int BM, Tile* tiles,
-                                                           int32_t* ntiles, int has_shared) {
-    __shared__ uint32_t bm[2 * 1024];
-    __shared__ int soff[1024];
-    __shared__ int tmp[33];
+// Whole permutation in one workgroup (T <= 64 tokens); every thread of the block must call it.
+__device__ void perm_single_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
+                                 int32_t* __restrict__ perm, int32_t* __restrict__ inv, int BM, Tile* tiles,
+                                 int32_t* ntiles, int has_shared, uint32_t* bm, int* soff, int* tmp, int32_t* zero,
+                                 int nzero, int32_t* status) {
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;  // counters of the expert launch
+    if (status && threadIdx.x == 0) *status = 0;
     perm_bitmap(ids, T, k, E, 0, bm);
     const int e = threadIdx.x;
     const int cnt = e < E ? __popc(bm[2 * e]) + __popc(bm[2 * e + 1]) : 0;
@@ -224,6 +250,39 @@ __global__ __launch_bounds__(1024) void perm_single_kernel(const int32_t* __rest
     perm_scatter_block(ids, T, k, E, 0, bm, soff, perm, inv);
 }
 
+__global__ __launch_bounds__(1024) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ inv, int BM, Tile* tiles,
+                                                           int32_t* ntiles, int has_shared, int32_t* zero, int nzero,
+                                                           int32_t* status) {
+    __shared__ uint32_t bm[2 * 1024];
+    __shared__ int soff[1024];
+    __shared__ int tmp[33];
+    perm_single_body(ids, T, k, E, offsets, perm, inv, BM, tiles, ntiles, has_shared, bm, soff, tmp, zero, nzero,
+                     status);
+}
+
+// Routing and permutation of a small batch (T <= 64) in one workgroup of 16 waves: each wave
+// selects the experts of its tokens into LDS, then the block builds the segments.
+template <int NV>
+__global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                                int32_t* __restrict__ ids, float* __restrict__ w,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                                int BM, Tile* tiles, int32_t* ntiles, int has_shared,
+                                                                int32_t* zero, int nzero, int32_t* status) {
+    __shared__ uint32_t bm[2 * 1024];
+    __shared__ int soff[1024];
+    __shared__ int tmp[33];
+    __shared__ int32_t sids[64 * 16];
+    for (int t = threadIdx.x >> 6; t < T; t += 16)
+        topk_token<NV>(logits + (size_t)t * E, E, k, sids + t * k, w + (size_t)t * k);
+    __syncthreads();
+    for (int i = threadIdx.x; i < T * k; i += blockDim.x) ids[i] = sids[i];
+    perm_single_body(sids, T, k, E, offsets, perm, inv, BM, tiles, ntiles, has_shared, bm, soff, tmp, zero, nzero,
+                     status);
+}
+
 __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
                                                         int32_t* __restrict__ hist) {
     __shared__ uint32_t bm[2 * 1024];
@@ -235,8 +294,11 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int nb, int T, int k, int E,
                                                          int32_t* __restrict__ base, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ perm, int BM, Tile* tiles,
-                                                         int32_t* ntiles, int has_shared) {
+                                                         int32_t* ntiles, int has_shared, int32_t* zero, int nzero,
+                                                         int32_t* status) {
     __shared__ int tmp[33];
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
+    if (status && threadIdx.x == 0) *status = 0;
     const int e = threadIdx.x;
     int cnt = 0;
     if (e < E) {
@@ -380,7 +442,8 @@ namespace {
 inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 inline hipError_t last() { return hipGetLastError(); }
 
-// Shapes of the weight-streaming kernels (waves per workgroup, K slices per row block).
+// Shapes of the weight-streaming kernels: waves per workgroup, K slices per 16-row block, and
+// weight loads per matrix in one pipelined chunk.
 #ifndef LMOE_PROJ_WAVES
 #define LMOE_PROJ_WAVES 8
 #endif
@@ -399,21 +462,25 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_DOWN_KS
 #define LMOE_DOWN_KS 1
 #endif
-#ifndef LMOE_BATCH
-#define LMOE_BATCH 8
+#ifndef LMOE_CHUNK
+#define LMOE_CHUNK 4
+#endif
+#ifndef LMOE_STREAM_GRID
+#define LMOE_STREAM_GRID 2048
 #endif
 constexpr int kPW = LMOE_PROJ_WAVES, kPKS = LMOE_PROJ_KS;
 constexpr int kUW = LMOE_UP_WAVES, kUKS = LMOE_UP_KS;
 constexpr int kDW = LMOE_DOWN_WAVES, kDKS = LMOE_DOWN_KS;
-constexpr int kBatch = LMOE_BATCH;
-constexpr size_t kMaxLds = 64 * 1024;  // token operand staged in LDS when it fits
+constexpr int kChunk = LMOE_CHUNK;
 
-inline size_t tok_lds(int ntl, int K, int planes) { return (size_t)planes * ntl * (K + 8) * 2; }
-
+// Persistent launch: at most LMOE_STREAM_GRID workgroups walk max_tiles x row-group items.
 template <int W, int KS, int NMAT, class P>
-hipError_t launch_stream(const P& p, unsigned gx, int nrows_max, size_t lds, hipStream_t s) {
-    const dim3 grid(gx, cdiv(nrows_max, 16 * (W / KS))), block(64 * W);
-    hipLaunchKernelGGL((stream_gemm_kernel<W, KS, NMAT, kBatch, P>), grid, block, P::kXLds ? lds : 0, s, p);
+hipError_t launch_stream(const P& p, int max_tiles, int nrows_max, hipStream_t s) {
+    constexpr int CH = P::kSPL == 1 ? kChunk : 1;
+    const int rgroups = (int)cdiv(nrows_max, 16 * (W / KS));
+    const long items = (long)max_tiles * rgroups;
+    const dim3 grid((unsigned)std::min<long>(items, LMOE_STREAM_GRID)), block(64 * W);
+    hipLaunchKernelGGL((stream_gemm_kernel<W, KS, NMAT, CH, P>), grid, block, 0, s, p, rgroups);
     return last();
 }
 }  // namespace
@@ -425,15 +492,8 @@ hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                             uint16_t* out16, hipStream_t s) {
-    if (T <= kStreamMaxT) {
-        const int ntl = std::min(16, T);
-        const size_t lds = tok_lds(ntl, K, 1);
-        if (lds <= kMaxLds)
-            return launch_stream<kPW, kPKS, 1>(StreamProj<true>{x, W, T, N, K, mode, ntl, out32, out16}, cdiv(T, 16), N,
-                                               lds, s);
-        return launch_stream<kPW, kPKS, 1>(StreamProj<false>{x, W, T, N, K, mode, ntl, out32, out16}, cdiv(T, 16), N, 0,
-                                           s);
-    }
+    if (T <= kStreamMaxT)
+        return launch_stream<kPW, kPKS, 1>(StreamProj{x, W, T, N, K, mode, out32, out16}, (int)cdiv(T, 16), N, s);
     TileProj p{x, W, T, N, K, mode, out32, out16};
     hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileProj>), dim3(cdiv(T, 128), cdiv(N, 128)), dim3(256), 0, s, p);
     return last();
@@ -441,14 +501,8 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
 
 hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
                               hipStream_t s) {
-    if (T <= kStreamMaxT) {
-        const int ntl = std::min(16, T);
-        const size_t lds = tok_lds(ntl, L, 2);
-        if (lds <= kMaxLds)
-            return launch_stream<kPW, kPKS, 1>(StreamRouter<true>{z, Wr, br, T, E, L, ntl, logits}, cdiv(T, 16), E, lds,
-                                               s);
-        return launch_stream<kPW, kPKS, 1>(StreamRouter<false>{z, Wr, br, T, E, L, ntl, logits}, cdiv(T, 16), E, 0, s);
-    }
+    if (T <= kStreamMaxT)
+        return launch_stream<kPW, kPKS, 1>(StreamRouter{z, Wr, br, T, E, L, logits}, (int)cdiv(T, 16), E, s);
     TileRouter p{z, Wr, br, T, E, L, logits};
     hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileRouter>), dim3(cdiv(T, 128), cdiv(E, 128)), dim3(256), 0, s, p);
     return last();
@@ -471,23 +525,31 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 
 int perm_blocks(int T) { return (int)cdiv(T, kPermTB); }
 
-hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist, int32_t* base, int32_t* offsets,
-                          int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
-                          hipStream_t s) {
-    const int nb = perm_blocks(T);
-    if (nb <= 1) {
-        hipLaunchKernelGGL(perm_single_kernel, dim3(1), dim3(1024), 0, s, ids, T, k, E, offsets, perm, inv, BM, tiles,
-                           ntiles, has_shared);
-        return last();
+hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
+                               int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
+                               int32_t* ntiles, int has_shared, int32_t* zero, int nzero, int32_t* status,
+                               hipStream_t s) {
+    if (T > kPermTB) {
+        hipError_t e = launch_topk(logits, T, E, k, ids, w, s);
+        if (e != hipSuccess) return e;
+        return launch_permute(ids, T, k, E, hist, base, offsets, perm, inv, BM, tiles, ntiles, has_shared, zero, nzero,
+                              status, s);
     }
-    hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, hist);
-    hipError_t err = last();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, T, k, E, base, offsets, perm, BM, tiles,
-                       ntiles, has_shared);
-    err = last();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, base, offsets, perm, inv);
+    const dim3 g(1), b(1024);
+#define LMOE_TOPK_PERM(NV)                                                                                          \
+    hipLaunchKernelGGL(topk_perm_single_kernel<NV>, g, b, 0, s, logits, T, E, k, ids, w, offsets, perm, inv, BM, tiles, \
+                       ntiles, has_shared, zero, nzero, status)
+    if (E <= 64)
+        LMOE_TOPK_PERM(1);
+    else if (E <= 128)
+        LMOE_TOPK_PERM(2);
+    else if (E <= 256)
+        LMOE_TOPK_PERM(4);
+    else if (E <= 512)
+        LMOE_TOPK_PERM(8);
+    else
+        LMOE_TOPK_PERM(16);
+#undef LMOE_TOPK_PERM
     return last();
 }
 
@@ -499,37 +561,44 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
 }
 
+// Workgroups of `kernel` that fit on the current device at once (cached per device).
+template <class K>
+int resident_blocks(K kernel, int threads) {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+        cache[dev] = per_cu * cus;
+    }
+    return cache[dev];
+}
+
+constexpr int kFusedWaves = 4;
+
+int fused_down_groups(int L) { return (L + 16 * kFusedWaves - 1) / (16 * kFusedWaves); }
+
 template <bool MX>
 hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
-    const int ntl = std::min(16, a.T);
-    hipError_t err;
+    constexpr int W = kFusedWaves;
+    constexpr int MAXG = MX ? 2 : 8;
+    FusedExperts<MX> f{StreamUp<MX>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.H},
+                       StreamDown<MX>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y},
+                       (int)cdiv(Fmax, 16 * W), fused_down_groups(a.L), a.counters, a.counters + a.max_tiles,
+                       a.status, a.w, a.T, a.k, a.Fs > 0 ? 1 : 0, a.m16};
+    auto kern = fused_experts_kernel<W, (MX ? 1 : kChunk), MAXG, MX>;
+    const long items = (long)a.max_tiles * std::max(f.up_rg, f.dn_rg);
+    const int grid = (int)std::min<long>(items, resident_blocks(kern, 64 * W));
     ev.begin(kStageUp);
-    const size_t lu = tok_lds(ntl, a.L, 1);
-    if (lu <= kMaxLds)
-        err = launch_stream<kUW, kUKS, 2>(
-            StreamUp<MX, true>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, ntl, a.H}, a.max_tiles,
-            Fmax, lu, s);
-    else
-        err = launch_stream<kUW, kUKS, 2>(
-            StreamUp<MX, false>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, ntl, a.H}, a.max_tiles,
-            Fmax, 0, s);
-    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), 0, s, f);
+    hipError_t err = last();
     ev.end(kStageUp);
-    ev.begin(kStageDown);
-    const size_t ld = tok_lds(ntl, Fmax, 1);
-    if (ld <= kMaxLds)
-        err = launch_stream<kDW, kDKS, 1>(
-            StreamDown<MX, true>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, ntl, a.Y}, a.max_tiles,
-            a.L, ld, s);
-    else
-        err = launch_stream<kDW, kDKS, 1>(
-            StreamDown<MX, false>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, ntl, a.Y}, a.max_tiles,
-            a.L, 0, s);
-    if (err != hipSuccess) return err;
-    ev.end(kStageDown);
-    return hipSuccess;
+    return err;
 }
 
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {

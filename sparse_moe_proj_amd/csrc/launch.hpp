@@ -52,9 +52,19 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 int perm_blocks(int T);
 
 // tiles may be null (no work list).  hist/base: [perm_blocks(T)][E] ints (unused when T <= 64).
+// zero/nzero: a region of int32 counters cleared by the permutation launch.
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist, int32_t* base, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
-                          hipStream_t s);
+                          int32_t* zero, int nzero, int32_t* status, hipStream_t s);
+
+// top-k followed by the permutation; one fused launch when T <= 64.
+hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
+                               int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
+                               int32_t* ntiles, int has_shared, int32_t* zero, int nzero, int32_t* status,
+                               hipStream_t s);
+
+// Row groups of the down projection in the fused small-batch expert launch.
+int fused_down_groups(int L);
 
 int expert_tile_rows(bool stream_path);
 int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path);
@@ -73,6 +83,11 @@ struct ExpertArgs {
     int max_tiles;
     bool stream_path;
     bool mxfp4;
+    // fused small-batch path: counters (max_tiles + fused_down_groups(L)), status, merge inputs/output
+    int32_t* counters;
+    int32_t* status;
+    const float* w;
+    uint16_t* m16;
 };
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 

@@ -252,61 +252,46 @@ struct TileDown {
 
 // =============================================================================================
 // Stream (decode) problems: blocks of 16 weight rows x up to 16 tokens, K in 32-wide steps.
-// With kXLds the tile's tokens are staged in LDS: `ntl` rows of (K + 8) bf16 (per plane).
+// Token column j reads a valid row (clamped) and is zeroed by a select when j is past the batch.
 // =============================================================================================
 
-// LDS token row stride in elements (16-byte pad: consecutive rows start 4 banks apart)
-__device__ __forceinline__ int xpitch(int K) { return K + 8; }
+__device__ __forceinline__ uint4 sel4(bool keep, uint4 v) { return keep ? v : zero4(); }
 
-// Copy `n` token rows of K bf16 (row j at rowp(j)) into LDS rows [0, ntl), zero-filling the rest.
-template <class RowFn>
-__device__ __forceinline__ void stage_rows(uint8_t* lds, int ntl, int n, int K, RowFn rowp) {
-    const int cpr = K / 8;  // 16-byte chunks per row
-    for (int c = threadIdx.x; c < ntl * cpr; c += blockDim.x) {
-        const int jj = c / cpr, kc = c - jj * cpr;
-        uint4 v = zero4();
-        if (jj < n) v = ld16(rowp(jj) + kc * 8);
-        *reinterpret_cast<uint4*>(lds + ((size_t)jj * xpitch(K) + kc * 8) * 2) = v;
-    }
-}
-
-__device__ __forceinline__ uint4 lds16(const uint8_t* lds, int j, int pitch, int k) {
-    return *reinterpret_cast<const uint4*>(lds + ((size_t)j * pitch + k) * 2);
-}
+struct TokRow {
+    const uint16_t* p;  // a valid row
+    bool ok;            // column inside the batch
+};
 
 // Dense projection over token blocks of 16: mode 0 z32+z16, 1 bf16 out, 2 fp32 += out.
-template <bool XLDS>
 struct StreamProj {
-    static constexpr bool kXLds = XLDS;
+    static constexpr bool kMixed = false;
     static constexpr int kSPL = 1;
     typedef uint4 WRaw;
+    typedef uint4 XRaw;
     typedef uint4 XFrag;
     typedef const uint16_t* RowW;
-    typedef const uint16_t* RowX;
+    typedef TokRow XRow;
     const uint16_t* x;  // [T][K]
     const uint16_t* W;  // [N][K]
-    int T, N, K, mode, ntl;
+    int T, N, K, mode;
     float* out32;
     uint16_t* out16;
     struct Ctx { int t0, nt; };
-    __device__ bool tile(int bx, Ctx& c) const {
-        c.t0 = bx * 16;
+    __device__ int num_tiles() const { return (T + 15) / 16; }
+    __device__ void tile(int t, Ctx& c) const {
+        c.t0 = t * 16;
         c.nt = min(16, T - c.t0);
-        return c.nt > 0;
     }
     __device__ int n_rows(const Ctx&) const { return N; }
     __device__ int k_steps(const Ctx&) const { return K / 32; }
-    __device__ RowW row_w(const Ctx&, int n) const { return n < N ? W + (size_t)n * K : nullptr; }
-    __device__ RowX row_x(const Ctx& c, int j) const { return j < c.nt ? x + (size_t)(c.t0 + j) * K : nullptr; }
-    __device__ WRaw load_w(const Ctx&, RowW r, int, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
-    __device__ uint4 wfrag_ctx(const Ctx&, const WRaw& w, int) const { return w; }
-    __device__ XFrag load_x(const Ctx&, RowX r, int k) const { return r ? ld16(r + k) : zero4(); }
-    __device__ void stage_x(const Ctx& c, uint8_t* lds) const {
-        stage_rows(lds, ntl, c.nt, K, [&](int jj) { return x + (size_t)(c.t0 + jj) * K; });
-    }
-    __device__ XFrag lds_frag(const Ctx& c, const uint8_t* lds, int j, int k) const {
-        return j < c.nt ? lds16(lds, j, xpitch(K), k) : zero4();
-    }
+    __device__ RowW row_w(const Ctx&, int n) const { return W + (size_t)n * K; }
+    __device__ XRow x_row(const Ctx& c, int j) const { return TokRow{x + (size_t)(c.t0 + min(j, c.nt - 1)) * K, j < c.nt}; }
+    template <bool>
+    __device__ WRaw load_w(const Ctx&, RowW r, int, int s, int kq) const { return ld16(r + s * 32 + kq * 8); }
+    template <bool>
+    __device__ static uint4 wfrag(const WRaw& w, int) { return w; }
+    __device__ XRaw load_x(const Ctx&, const XRow& r, int k) const { return ld16(r.p + k); }
+    __device__ XFrag x_frag(const XRow& r, const XRaw& v) const { return sel4(r.ok, v); }
     __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv, a); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n >= N || j >= c.nt) return;
@@ -323,69 +308,52 @@ struct StreamProj {
 };
 
 struct HiLo { uint4 hi, lo; };
+struct F8 { float4 a, b; };
 
-// Router logits from fp32 z (hi/lo bf16 split of the token operand; LDS holds the hi plane
-// then the lo plane, ntl rows each).
-template <bool XLDS>
+// Router logits from fp32 z: the token operand is split into hi = bf16(z), lo = bf16(z - hi),
+// each multiplied by the same bf16 weights.
 struct StreamRouter {
-    static constexpr bool kXLds = XLDS;
+    static constexpr bool kMixed = false;
     static constexpr int kSPL = 1;
     typedef uint4 WRaw;
+    typedef F8 XRaw;
     typedef HiLo XFrag;
     typedef const uint16_t* RowW;
-    typedef const float* RowX;
+    struct XRow { const float* p; bool ok; };
     const float* z;
     const uint16_t* W;
     const float* bias;
-    int T, N, K, ntl;
+    int T, N, K;
     float* logits;
     struct Ctx { int t0, nt; };
-    __device__ bool tile(int bx, Ctx& c) const {
-        c.t0 = bx * 16;
+    __device__ int num_tiles() const { return (T + 15) / 16; }
+    __device__ void tile(int t, Ctx& c) const {
+        c.t0 = t * 16;
         c.nt = min(16, T - c.t0);
-        return c.nt > 0;
     }
     __device__ int n_rows(const Ctx&) const { return N; }
     __device__ int k_steps(const Ctx&) const { return K / 32; }
-    __device__ RowW row_w(const Ctx&, int n) const { return n < N ? W + (size_t)n * K : nullptr; }
-    __device__ RowX row_x(const Ctx& c, int j) const { return j < c.nt ? z + (size_t)(c.t0 + j) * K : nullptr; }
-    __device__ WRaw load_w(const Ctx&, RowW r, int, int s, int kq) const { return r ? ld16(r + s * 32 + kq * 8) : zero4(); }
-    __device__ uint4 wfrag_ctx(const Ctx&, const WRaw& w, int) const { return w; }
-    __device__ XFrag load_x(const Ctx&, RowX r, int k) const {
-        HiLo h;
-        if (!r) {
-            h.hi = h.lo = zero4();
-        } else {
-            h.hi = f32x8_to_bf16_part(r + k, false);
-            h.lo = f32x8_to_bf16_part(r + k, true);
-        }
-        return h;
+    __device__ RowW row_w(const Ctx&, int n) const { return W + (size_t)n * K; }
+    __device__ XRow x_row(const Ctx& c, int j) const { return XRow{z + (size_t)(c.t0 + min(j, c.nt - 1)) * K, j < c.nt}; }
+    template <bool>
+    __device__ WRaw load_w(const Ctx&, RowW r, int, int s, int kq) const { return ld16(r + s * 32 + kq * 8); }
+    template <bool>
+    __device__ static uint4 wfrag(const WRaw& w, int) { return w; }
+    __device__ XRaw load_x(const Ctx&, const XRow& r, int k) const {
+        return F8{*reinterpret_cast<const float4*>(r.p + k), *reinterpret_cast<const float4*>(r.p + k + 4)};
     }
-    __device__ void stage_x(const Ctx& c, uint8_t* lds) const {
-        const int cpr = K / 8;
-        const size_t plane = (size_t)ntl * xpitch(K) * 2;
-        for (int q = threadIdx.x; q < ntl * cpr; q += blockDim.x) {
-            const int jj = q / cpr, kc = q - jj * cpr;
-            uint4 hi = zero4(), lo = zero4();
-            if (jj < c.nt) {
-                const float* src = z + (size_t)(c.t0 + jj) * K + kc * 8;
-                hi = f32x8_to_bf16_part(src, false);
-                lo = f32x8_to_bf16_part(src, true);
-            }
-            const size_t off = ((size_t)jj * xpitch(K) + kc * 8) * 2;
-            *reinterpret_cast<uint4*>(lds + off) = hi;
-            *reinterpret_cast<uint4*>(lds + plane + off) = lo;
+    __device__ XFrag x_frag(const XRow& r, const XRaw& v) const {
+        const float f[8] = {v.a.x, v.a.y, v.a.z, v.a.w, v.b.x, v.b.y, v.b.z, v.b.w};
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t h0, l0, h1, l1;
+            split_hi_lo(f[2 * i], h0, l0);
+            split_hi_lo(f[2 * i + 1], h1, l1);
+            h[i] = h0 | (h1 << 16);
+            l[i] = l0 | (l1 << 16);
         }
-    }
-    __device__ XFrag lds_frag(const Ctx& c, const uint8_t* lds, int j, int k) const {
-        HiLo h;
-        if (j < c.nt) {
-            h.hi = lds16(lds, j, xpitch(K), k);
-            h.lo = lds16(lds + (size_t)ntl * xpitch(K) * 2, j, xpitch(K), k);
-        } else {
-            h.hi = h.lo = zero4();
-        }
-        return h;
+        return HiLo{sel4(r.ok, make_uint4(h[0], h[1], h[2], h[3])), sel4(r.ok, make_uint4(l[0], l[1], l[2], l[3]))};
     }
     __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv.lo, mfma16(w, xv.hi, a)); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
@@ -412,9 +380,11 @@ struct ExpertRows<false> {
     typedef uint4 WRaw;
     struct Mat { const uint16_t* p; };     // matrix base, rows of K elements
     struct Row { const uint16_t* p; };
-    __device__ static Row row(const Mat& m, int n, int K) { return Row{m.p ? m.p + (size_t)n * K : nullptr}; }
-    __device__ static WRaw load(const Row& r, bool, int s, int kq) { return r.p ? ld16(r.p + s * 32 + kq * 8) : zero4(); }
-    __device__ static uint4 frag(const WRaw& w, bool, int) { return w; }
+    __device__ static Row row(const Mat& m, int n, int K) { return Row{m.p + (size_t)n * K}; }
+    template <bool>
+    __device__ static WRaw load(const Row& r, int s, int kq) { return ld16(r.p + s * 32 + kq * 8); }
+    template <bool>
+    __device__ static uint4 frag(const WRaw& w, int) { return w; }
 };
 
 template <>
@@ -424,17 +394,16 @@ struct ExpertRows<true> {
     struct Mat { const uint8_t* p; const uint8_t* sc; };  // sc == null: bf16 matrix (shared expert)
     struct Row { const uint8_t* p; const uint8_t* sc; };
     __device__ static Row row(const Mat& m, int n, int K) {
-        if (!m.p) return Row{nullptr, nullptr};
         if (m.sc) return Row{m.p + (size_t)n * (K / 2), m.sc + (size_t)n * (K / 32)};
         return Row{m.p + (size_t)n * K * 2, nullptr};
     }
-    __device__ static WRaw load(const Row& r, bool mx, int g, int kq) {
+    template <bool MXR>
+    __device__ static WRaw load(const Row& r, int g, int kq) {
         WRaw w;
-        if (!r.p) {
-            w.a[0] = w.a[1] = w.a[2] = w.a[3] = zero4();
-        } else if (mx) {
+        if constexpr (MXR) {
             w.a[0] = ld16(r.p + g * 64 + kq * 16);
             w.a[1] = make_uint4(r.sc[g * 4 + kq], 0, 0, 0);
+            w.a[2] = w.a[3] = zero4();
         } else {
             const uint8_t* b = r.p + (size_t)(g * 128 + kq * 32) * 2;
 #pragma unroll
@@ -442,10 +411,14 @@ struct ExpertRows<true> {
         }
         return w;
     }
-    __device__ static uint4 frag(const WRaw& w, bool mx, int t) {
-        if (!mx) return w.a[t];
-        const uint32_t nib = t == 0 ? w.a[0].x : t == 1 ? w.a[0].y : t == 2 ? w.a[0].z : w.a[0].w;
-        return mxfp4_to_bf16x8(nib, w.a[1].x);
+    template <bool MXR>
+    __device__ static uint4 frag(const WRaw& w, int t) {
+        if constexpr (!MXR) {
+            return w.a[t];
+        } else {
+            const uint32_t nib = t == 0 ? w.a[0].x : t == 1 ? w.a[0].y : t == 2 ? w.a[0].z : w.a[0].w;
+            return mxfp4_to_bf16x8(nib, w.a[1].x);
+        }
     }
 };
 
@@ -488,52 +461,49 @@ __device__ __forceinline__ void segment_mats(const void* experts, size_t rec_byt
 }
 
 // Fused gate/up (NMAT = 2) over a work list of <= 16-row tiles: H = SiLU(z gate^T) * (z up^T).
-template <bool MX, bool XLDS>
+template <bool MX>
 struct StreamUp {
     using ER = ExpertRows<MX>;
-    static constexpr bool kXLds = XLDS;
+    static constexpr bool kMixed = MX;
     static constexpr int kSPL = ER::kSPL;
     typedef typename ER::WRaw WRaw;
+    typedef uint4 XRaw;
     typedef uint4 XFrag;
+    typedef TokRow XRow;
     struct RowW { typename ER::Row g, u; };
-    typedef const uint16_t* RowX;
     SegSpace seg;
     const uint16_t* z16;
     const void* experts;
     size_t rec_bytes;
     const uint16_t* shared;
-    int L, F, Fs, Hs, ntl;
+    int L, F, Fs, Hs;
     uint16_t* H;
     struct Ctx { int seg, row0, nrows, F; bool mx; typename ER::Mat m[3]; };
-    __device__ bool tile(int bx, Ctx& c) const {
-        if (bx >= *seg.ntiles) return false;
+    __device__ int num_tiles() const { return *seg.ntiles; }
+    __device__ void tile(int bx, Ctx& c) const {
         const Tile t = seg.tiles[bx];
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
         segment_mats<MX>(experts, rec_bytes, shared, t.seg, seg.E, F, Fs, L, c.m, c.F, c.mx);
-        return true;
     }
+    __device__ bool mx_rows(const Ctx& c) const { return c.mx; }
     __device__ int n_rows(const Ctx& c) const { return c.F; }
+    __device__ int n_rows_for(int sg) const { return sg == seg.E ? Fs : F; }
     __device__ int k_steps(const Ctx&) const { return L / 32; }
-    __device__ RowW row_w(const Ctx& c, int n) const {
-        if (n >= c.F) return RowW{ER::row(typename ER::Mat{}, 0, L), ER::row(typename ER::Mat{}, 0, L)};
-        return RowW{ER::row(c.m[0], n, L), ER::row(c.m[1], n, L)};
+    __device__ RowW row_w(const Ctx& c, int n) const { return RowW{ER::row(c.m[0], n, L), ER::row(c.m[1], n, L)}; }
+    __device__ XRow x_row(const Ctx& c, int j) const {
+        const int tok = seg.token_of(c.seg, c.row0 + min(j, c.nrows - 1));
+        return TokRow{z16 + (size_t)tok * L, j < c.nrows};
     }
-    __device__ RowX row_x(const Ctx& c, int j) const {
-        return j < c.nrows ? z16 + (size_t)seg.token_of(c.seg, c.row0 + j) * L : nullptr;
+    template <bool MXR>
+    __device__ WRaw load_w(const Ctx&, const RowW& r, int m, int g, int kq) const {
+        return ER::template load<MXR>(m == 0 ? r.g : r.u, g, kq);
     }
-    __device__ WRaw load_w(const Ctx& c, const RowW& r, int m, int g, int kq) const {
-        return ER::load(m == 0 ? r.g : r.u, c.mx, g, kq);
-    }
-    __device__ uint4 wfrag_ctx(const Ctx& c, const WRaw& w, int t) const { return ER::frag(w, c.mx, t); }
-    __device__ XFrag load_x(const Ctx&, RowX r, int k) const { return r ? ld16(r + k) : zero4(); }
-    __device__ void stage_x(const Ctx& c, uint8_t* lds) const {
-        stage_rows(lds, ntl, c.nrows, L, [&](int jj) { return z16 + (size_t)seg.token_of(c.seg, c.row0 + jj) * L; });
-    }
-    __device__ XFrag lds_frag(const Ctx& c, const uint8_t* lds, int j, int k) const {
-        return j < c.nrows ? lds16(lds, j, xpitch(L), k) : zero4();
-    }
+    template <bool MXR>
+    __device__ static uint4 wfrag(const WRaw& w, int t) { return ER::template frag<MXR>(w, t); }
+    __device__ XRaw load_x(const Ctx&, const XRow& r, int k) const { return ld16(r.p + k); }
+    __device__ XFrag x_frag(const XRow& r, const XRaw& v) const { return sel4(r.ok, v); }
     __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv, a); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n < c.F && j < c.nrows) H[(size_t)(c.row0 + j) * Hs + n] = (uint16_t)f2bf(silu(v[0]) * v[1]);
@@ -541,47 +511,45 @@ struct StreamUp {
 };
 
 // Down projection over a work list: Y[dest(p)][n] = H[p] . down[n].
-template <bool MX, bool XLDS>
+template <bool MX>
 struct StreamDown {
     using ER = ExpertRows<MX>;
-    static constexpr bool kXLds = XLDS;
+    static constexpr bool kMixed = MX;
     static constexpr int kSPL = ER::kSPL;
     typedef typename ER::WRaw WRaw;
+    typedef uint4 XRaw;
     typedef uint4 XFrag;
+    typedef TokRow XRow;
     typedef typename ER::Row RowW;
-    typedef const uint16_t* RowX;
     SegSpace seg;
     const uint16_t* H;
     const void* experts;
     size_t rec_bytes;
     const uint16_t* shared;
-    int L, F, Fs, Hs, ntl;
+    int L, F, Fs, Hs;
     float* Y;
     struct Ctx { int seg, row0, nrows, F; bool mx; typename ER::Mat m[3]; };
-    __device__ bool tile(int bx, Ctx& c) const {
-        if (bx >= *seg.ntiles) return false;
+    __device__ int num_tiles() const { return *seg.ntiles; }
+    __device__ void tile(int bx, Ctx& c) const {
         const Tile t = seg.tiles[bx];
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
         segment_mats<MX>(experts, rec_bytes, shared, t.seg, seg.E, F, Fs, L, c.m, c.F, c.mx);
-        return true;
     }
+    __device__ bool mx_rows(const Ctx& c) const { return c.mx; }
     __device__ int n_rows(const Ctx&) const { return L; }
     __device__ int k_steps(const Ctx& c) const { return c.F / 32; }
-    __device__ RowW row_w(const Ctx& c, int n) const {
-        return n < L ? ER::row(c.m[2], n, c.F) : ER::row(typename ER::Mat{}, 0, c.F);
+    __device__ RowW row_w(const Ctx& c, int n) const { return ER::row(c.m[2], n, c.F); }
+    __device__ XRow x_row(const Ctx& c, int j) const {
+        return TokRow{H + (size_t)(c.row0 + min(j, c.nrows - 1)) * Hs, j < c.nrows};
     }
-    __device__ RowX row_x(const Ctx& c, int j) const { return j < c.nrows ? H + (size_t)(c.row0 + j) * Hs : nullptr; }
-    __device__ WRaw load_w(const Ctx& c, const RowW& r, int, int g, int kq) const { return ER::load(r, c.mx, g, kq); }
-    __device__ uint4 wfrag_ctx(const Ctx& c, const WRaw& w, int t) const { return ER::frag(w, c.mx, t); }
-    __device__ XFrag load_x(const Ctx&, RowX r, int k) const { return r ? ld16(r + k) : zero4(); }
-    __device__ void stage_x(const Ctx& c, uint8_t* lds) const {
-        stage_rows(lds, ntl, c.nrows, c.F, [&](int jj) { return H + (size_t)(c.row0 + jj) * Hs; });
-    }
-    __device__ XFrag lds_frag(const Ctx& c, const uint8_t* lds, int j, int k) const {
-        return j < c.nrows ? lds16(lds, j, xpitch(c.F), k) : zero4();
-    }
+    template <bool MXR>
+    __device__ WRaw load_w(const Ctx&, const RowW& r, int, int g, int kq) const { return ER::template load<MXR>(r, g, kq); }
+    template <bool MXR>
+    __device__ static uint4 wfrag(const WRaw& w, int t) { return ER::template frag<MXR>(w, t); }
+    __device__ XRaw load_x(const Ctx&, const XRow& r, int k) const { return ld16(r.p + k); }
+    __device__ XFrag x_frag(const XRow& r, const XRaw& v) const { return sel4(r.ok, v); }
     __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv, a); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n >= L || j >= c.nrows) return;
