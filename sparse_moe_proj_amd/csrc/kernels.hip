@@ -525,6 +525,26 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 
 int perm_blocks(int T) { return (int)cdiv(T, kPermTB); }
 
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist, int32_t* base, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
+                          int32_t* zero, int nzero, int32_t* status, hipStream_t s) {
+    const int nb = perm_blocks(T);
+    if (nb <= 1) {
+        hipLaunchKernelGGL(perm_single_kernel, dim3(1), dim3(1024), 0, s, ids, T, k, E, offsets, perm, inv, BM, tiles,
+                           ntiles, has_shared, zero, nzero, status);
+        return last();
+    }
+    hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, hist);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, T, k, E, base, offsets, perm, BM, tiles,
+                       ntiles, has_shared, zero, nzero, status);
+    err = last();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, base, offsets, perm, inv);
+    return last();
+}
+
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
                                int32_t* ntiles, int has_shared, int32_t* zero, int nzero, int32_t* status,
