@@ -52,7 +52,7 @@ def _load():
     # torch's device memory and streams.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_moe_proj_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python sparse_moe_proj_amd/build.py` "
                           "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t

@@ -1,7 +1,9 @@
 """Build liblmoe.so (gfx950) in-tree with hipcc: one object per .hip source, compiled in
 parallel, then linked into sparse_moe_proj_amd/liblmoe.so.
 
-    python -m sparse_moe_proj_amd.build [--verbose]
+    python sparse_moe_proj_amd/build.py [--verbose]
+
+Run it as a script (not `-m sparse_moe_proj_amd.build`): importing the package loads the library.
 """
 from __future__ import annotations
 
