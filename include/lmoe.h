@@ -106,9 +106,9 @@ typedef enum {
     LMOE_STAGE_TOPK = 3,        /* top_k + softmax over the kept logits, and the permutation */
     LMOE_STAGE_PERMUTE = 4,     /* (not recorded: the permutation belongs to the TOPK stage) */
     LMOE_STAGE_EXPERT_UP = 5,   /* SwiGLU gate/up of every segment (shared expert included); for
-                                   small batches also the down projections and the merge */
-    LMOE_STAGE_EXPERT_DOWN = 6, /* down projections (large batches) */
-    LMOE_STAGE_COMBINE = 7,     /* weighted merge (large batches) */
+                                   T <= 16 also the down projections, per slice of the SwiGLU width */
+    LMOE_STAGE_EXPERT_DOWN = 6, /* down projections (T > 16) */
+    LMOE_STAGE_COMBINE = 7,     /* weighted merge (for T <= 16 it also sums the slices) */
     LMOE_STAGE_U = 8,           /* y = m U^T */
     LMOE_N_STAGES = 9
 } lmoe_stage;
@@ -131,10 +131,6 @@ typedef struct {
      * just before stage s is enqueued and event 2s+1 just after it.  The hook is ignored
      * while `stream` is being captured into a graph. */
     void* const* stage_events;
-    /* Optional device int32: set to 0 by the call, and to 1 if a bounded device-side wait of the
-     * small-batch (T <= 16, or MXFP4) expert launch ran out, which can only happen when other work
-     * occupies the GPU's compute units during the call; the outputs of that call are then invalid. */
-    int32_t* aux_status;
 } lmoe_forward_opts;
 
 /* Bytes of one routed expert record (shared = 0) or of the shared expert record (shared = 1).

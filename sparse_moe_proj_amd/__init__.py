@@ -43,7 +43,7 @@ class lmoe_weights(ctypes.Structure):
 class lmoe_forward_opts(ctypes.Structure):
     _fields_ = [("prenorm", ctypes.c_int32), ("residual", ctypes.c_int32), ("aux_z", ctypes.c_void_p),
                 ("aux_ids", ctypes.c_void_p), ("aux_w", ctypes.c_void_p), ("aux_offsets", ctypes.c_void_p),
-                ("aux_perm", ctypes.c_void_p), ("stage_events", ctypes.c_void_p), ("aux_status", ctypes.c_void_p)]
+                ("aux_perm", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
 
 
 def _load():
@@ -116,11 +116,11 @@ STAGES = ("prenorm", "D", "router", "topk", "permute", "expert_up", "expert_down
 
 
 def make_opts(prenorm=0, residual=0, aux_z=None, aux_ids=None, aux_w=None, aux_offsets=None, aux_perm=None,
-              stage_events=None, aux_status=None):
+              stage_events=None):
     """stage_events: None or a ctypes array of 2 * LMOE_N_STAGES hipEvent_t handles (keep it alive)."""
     ev = ctypes.cast(stage_events, ctypes.c_void_p).value if stage_events is not None else None
     return lmoe_forward_opts(int(prenorm), int(residual), _p(aux_z), _p(aux_ids), _p(aux_w), _p(aux_offsets),
-                             _p(aux_perm), ev, _p(aux_status))
+                             _p(aux_perm), ev)
 
 
 def last_error() -> str:

@@ -76,9 +76,8 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t x16, z32, z16, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, counters, H, Y, m, total;
-    int ncounters;  // fused small-batch expert launch: per-tile and per-row-group counters, then status
-    bool stream_path;
+    size_t x16, z32, z16, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, P, m, total;
+    bool stream_path, decode_path;
     int max_tiles, BM, Hs, R;
 };
 
@@ -87,6 +86,7 @@ Layout plan(const Dims& d, int T) {
     const size_t act = d.f32 ? 4 : 2;
     const int has_shared = d.Fs > 0;
     lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx);
+    lo.decode_path = !d.f32 && T <= kStreamMaxT;
     lo.BM = expert_tile_rows(lo.stream_path);
     lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path);
     lo.Hs = std::max(d.F, d.Fs);
@@ -111,10 +111,9 @@ Layout plan(const Dims& d, int T) {
     lo.base = take(nb * d.E * 4);
     lo.tiles = take((size_t)lo.max_tiles * sizeof(Tile));
     lo.ntiles = take(4);
-    lo.ncounters = lo.stream_path ? lo.max_tiles + fused_down_groups(d.L) + 1 : 0;
-    lo.counters = take((size_t)lo.ncounters * 4);
-    lo.H = take((size_t)lo.R * lo.Hs * act);
-    lo.Y = take((size_t)lo.R * d.L * 4);
+    lo.H = take(lo.decode_path ? 0 : (size_t)lo.R * lo.Hs * act);
+    lo.Y = take(lo.decode_path ? 0 : (size_t)lo.R * d.L * 4);
+    lo.P = take(lo.decode_path ? (size_t)lo.R * decode_slices(d.F, d.Fs, d.mx) * d.L * 4 : 0);
     lo.m = take((size_t)T * d.L * act);
     lo.total = o;
     return lo;
@@ -154,7 +153,9 @@ lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* byte
     if (st != LMOE_OK) return st;
     if ((st = check_T(d, T)) != LMOE_OK) return st;
     if (!bytes) return fail(LMOE_ERR_NULL, "bytes is NULL");
-    *bytes = plan(d, T).total;
+    // the small-batch partials can exceed what a slightly larger batch needs: report the maximum
+    // over every T' <= T so that one workspace sized for a largest batch serves all smaller ones
+    *bytes = std::max(plan(d, T).total, plan(d, std::min<int32_t>(T, kStreamMaxT)).total);
     return LMOE_OK;
 }
 
@@ -209,7 +210,7 @@ lmoe_status lmoe_permute(const lmoe_config* cfg, const int32_t* ids, int32_t T, 
     int32_t* hist = static_cast<int32_t*>(ws);
     int32_t* base = need ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2) : nullptr;
     const hipError_t e =
-        launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, 16, nullptr, nullptr, 0, nullptr, 0, nullptr, s);
+        launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, 16, nullptr, nullptr, 0, s);
     if (e != hipSuccess) return hip_fail(e, "permute");
     return LMOE_OK;
 }
@@ -229,7 +230,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         return fail(LMOE_ERR_NULL, "x, y, D, U, Wr and experts must be non-NULL");
     if (d.Fs > 0 && !wt->shared) return fail(LMOE_ERR_NULL, "shared_ffn > 0 but the shared expert record is NULL");
     const void* ptrs[] = {x, y, wt->D, wt->U, wt->Wr, wt->experts, wt->shared, ws, o.aux_z, o.aux_ids, o.aux_w,
-                          o.aux_offsets, o.aux_perm, o.aux_status};
+                          o.aux_offsets, o.aux_perm};
     for (const void* p : ptrs)
         if (!aligned16(p)) return fail(LMOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(wt->br) & 3u) return fail(LMOE_ERR_ALIGN, "br must be 4-byte aligned");
@@ -275,7 +276,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         ev.end(LMOE_STAGE_TOPK);
         ev.begin(LMOE_STAGE_PERMUTE);
         if ((e = launch_permute(ids, T, d.k, d.E, hist, base, offsets, perm, inv, lo.BM, nullptr, nullptr, has_shared,
-                                nullptr, 0, o.aux_status, s)) != hipSuccess)
+                                s)) != hipSuccess)
             return hip_fail(e, "permute");
         ev.end(LMOE_STAGE_PERMUTE);
         F32ExpertArgs a{z32, ids, perm, static_cast<const float*>(wt->experts), static_cast<const float*>(wt->shared),
@@ -311,19 +312,17 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         return hip_fail(e, "router logits");
     ev.end(LMOE_STAGE_ROUTER);
     // top-k and permutation (one launch for small batches: the TOPK stage events bracket both)
-    int32_t* counters = static_cast<int32_t*>(at(lo.counters));
-    int32_t* status = o.aux_status ? o.aux_status : (lo.ncounters ? counters + lo.ncounters - 1 : nullptr);
     ev.begin(LMOE_STAGE_TOPK);
     if ((e = launch_topk_permute(logits, T, d.E, d.k, ids, wts, hist, base, offsets, perm, inv, lo.BM, tiles, ntiles,
-                                 has_shared, counters, lo.ncounters, o.aux_status, s)) != hipSuccess)
+                                 has_shared, s)) != hipSuccess)
         return hip_fail(e, "top-k / permute");
     ev.end(LMOE_STAGE_TOPK);
     uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
-                 wt->shared, static_cast<uint16_t*>(at(lo.H)), Y, lo.max_tiles, lo.stream_path, d.mx,
-                 counters, status, wts, m16};
+                 wt->shared, static_cast<uint16_t*>(at(lo.H)), Y, lo.max_tiles, lo.stream_path,
+                 lo.decode_path, d.mx, static_cast<float*>(at(lo.P)), wts, m16};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
-    if (!lo.stream_path) {  // the small-batch expert launch merges in place
+    if (!lo.decode_path) {  // the small-batch expert path has its own merge launch
         ev.begin(LMOE_STAGE_COMBINE);
         if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, true, m16, s)) != hipSuccess)
             return hip_fail(e, "combine");

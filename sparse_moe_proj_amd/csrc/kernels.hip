@@ -2,7 +2,7 @@
 // launch wrappers for everything (no allocation, no synchronisation: enqueue only).
 #include <limits.h>
 
-#include "fused_experts.hpp"
+#include "decode_experts.hpp"
 #include "gemm_stream.hpp"
 #include "gemm_tile.hpp"
 #include "launch.hpp"
@@ -230,10 +230,7 @@ __device__ void write_tiles(int e_cnt, int e_off, int e, int E, int T, int k, in
 // Whole permutation in one workgroup (T <= 64 tokens); every thread of the block must call it.
 __device__ void perm_single_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
                                  int32_t* __restrict__ perm, int32_t* __restrict__ inv, int BM, Tile* tiles,
-                                 int32_t* ntiles, int has_shared, uint32_t* bm, int* soff, int* tmp, int32_t* zero,
-                                 int nzero, int32_t* status) {
-    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;  // counters of the expert launch
-    if (status && threadIdx.x == 0) *status = 0;
+                                 int32_t* ntiles, int has_shared, uint32_t* bm, int* soff, int* tmp) {
     perm_bitmap(ids, T, k, E, 0, bm);
     const int e = threadIdx.x;
     const int cnt = e < E ? __popc(bm[2 * e]) + __popc(bm[2 * e + 1]) : 0;
@@ -253,13 +250,11 @@ __device__ void perm_single_body(const int32_t* ids, int T, int k, int E, int32_
 __global__ __launch_bounds__(1024) void perm_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ inv, int BM, Tile* tiles,
-                                                           int32_t* ntiles, int has_shared, int32_t* zero, int nzero,
-                                                           int32_t* status) {
+                                                           int32_t* ntiles, int has_shared) {
     __shared__ uint32_t bm[2 * 1024];
     __shared__ int soff[1024];
     __shared__ int tmp[33];
-    perm_single_body(ids, T, k, E, offsets, perm, inv, BM, tiles, ntiles, has_shared, bm, soff, tmp, zero, nzero,
-                     status);
+    perm_single_body(ids, T, k, E, offsets, perm, inv, BM, tiles, ntiles, has_shared, bm, soff, tmp);
 }
 
 // Routing and permutation of a small batch (T <= 64) in one workgroup of 16 waves: each wave
@@ -269,8 +264,7 @@ __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __r
                                                                 int32_t* __restrict__ ids, float* __restrict__ w,
                                                                 int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-                                                                int BM, Tile* tiles, int32_t* ntiles, int has_shared,
-                                                                int32_t* zero, int nzero, int32_t* status) {
+                                                                int BM, Tile* tiles, int32_t* ntiles, int has_shared) {
     __shared__ uint32_t bm[2 * 1024];
     __shared__ int soff[1024];
     __shared__ int tmp[33];
@@ -279,8 +273,7 @@ __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __r
         topk_token<NV>(logits + (size_t)t * E, E, k, sids + t * k, w + (size_t)t * k);
     __syncthreads();
     for (int i = threadIdx.x; i < T * k; i += blockDim.x) ids[i] = sids[i];
-    perm_single_body(sids, T, k, E, offsets, perm, inv, BM, tiles, ntiles, has_shared, bm, soff, tmp, zero, nzero,
-                     status);
+    perm_single_body(sids, T, k, E, offsets, perm, inv, BM, tiles, ntiles, has_shared, bm, soff, tmp);
 }
 
 __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
@@ -294,11 +287,8 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int nb, int T, int k, int E,
                                                          int32_t* __restrict__ base, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ perm, int BM, Tile* tiles,
-                                                         int32_t* ntiles, int has_shared, int32_t* zero, int nzero,
-                                                         int32_t* status) {
+                                                         int32_t* ntiles, int has_shared) {
     __shared__ int tmp[33];
-    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
-    if (status && threadIdx.x == 0) *status = 0;
     const int e = threadIdx.x;
     int cnt = 0;
     if (e < E) {
@@ -465,6 +455,9 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_CHUNK
 #define LMOE_CHUNK 4
 #endif
+#ifndef LMOE_DECODE_WAVES
+#define LMOE_DECODE_WAVES 4
+#endif
 #ifndef LMOE_STREAM_GRID
 #define LMOE_STREAM_GRID 2048
 #endif
@@ -526,19 +519,18 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 int perm_blocks(int T) { return (int)cdiv(T, kPermTB); }
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist, int32_t* base, int32_t* offsets,
-                          int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
-                          int32_t* zero, int nzero, int32_t* status, hipStream_t s) {
+                          int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared, hipStream_t s) {
     const int nb = perm_blocks(T);
     if (nb <= 1) {
         hipLaunchKernelGGL(perm_single_kernel, dim3(1), dim3(1024), 0, s, ids, T, k, E, offsets, perm, inv, BM, tiles,
-                           ntiles, has_shared, zero, nzero, status);
+                           ntiles, has_shared);
         return last();
     }
     hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, hist);
     hipError_t err = last();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, T, k, E, base, offsets, perm, BM, tiles,
-                       ntiles, has_shared, zero, nzero, status);
+                       ntiles, has_shared);
     err = last();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, base, offsets, perm, inv);
@@ -547,18 +539,16 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist
 
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
-                               int32_t* ntiles, int has_shared, int32_t* zero, int nzero, int32_t* status,
-                               hipStream_t s) {
+                               int32_t* ntiles, int has_shared, hipStream_t s) {
     if (T > kPermTB) {
         hipError_t e = launch_topk(logits, T, E, k, ids, w, s);
         if (e != hipSuccess) return e;
-        return launch_permute(ids, T, k, E, hist, base, offsets, perm, inv, BM, tiles, ntiles, has_shared, zero, nzero,
-                              status, s);
+        return launch_permute(ids, T, k, E, hist, base, offsets, perm, inv, BM, tiles, ntiles, has_shared, s);
     }
     const dim3 g(1), b(1024);
 #define LMOE_TOPK_PERM(NV)                                                                                          \
     hipLaunchKernelGGL(topk_perm_single_kernel<NV>, g, b, 0, s, logits, T, E, k, ids, w, offsets, perm, inv, BM, tiles, \
-                       ntiles, has_shared, zero, nzero, status)
+                       ntiles, has_shared)
     if (E <= 64)
         LMOE_TOPK_PERM(1);
     else if (E <= 128)
@@ -581,48 +571,56 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
 }
 
-// Workgroups of `kernel` that fit on the current device at once (cached per device).
-template <class K>
-int resident_blocks(K kernel, int threads) {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cache[dev]) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
-            per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-        cache[dev] = per_cu * cus;
-    }
-    return cache[dev];
+constexpr int decode_waves(bool mx) { return mx ? 8 : LMOE_DECODE_WAVES; }
+
+int decode_slices(int F, int Fs, bool mx) { return std::max(F, Fs) / (16 * decode_waves(mx)); }
+
+// Small batches: gate/up, SwiGLU and down per (tile, F slice) in one launch, then the merge.
+template <bool MX>
+hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
+    constexpr int W = decode_waves(MX);
+    constexpr int FS = 16 * W;
+    const int nslices = decode_slices(a.F, a.Fs, MX);
+    DecodeExperts<MX> d{seg, a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs,
+                        nslices, a.P};
+    const long items = (long)a.max_tiles * nslices;
+    ev.begin(kStageUp);
+    hipLaunchKernelGGL((decode_experts_kernel<W, (MX ? 1 : kChunk), MX>), dim3((unsigned)std::min<long>(items, LMOE_STREAM_GRID)),
+                       dim3(64 * W), 0, s, d);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    ev.end(kStageUp);
+    ev.begin(kStageCombine);
+    hipLaunchKernelGGL(merge_slices_kernel, dim3(cdiv(a.L, 256), a.T), dim3(64 * kMergeRows), 0, s, a.P, a.w, a.T, a.k, a.L,
+                       nslices, a.F / FS, a.Fs / FS, a.m16);
+    if ((err = last()) != hipSuccess) return err;
+    ev.end(kStageCombine);
+    return hipSuccess;
 }
 
-constexpr int kFusedWaves = 4;
-
-int fused_down_groups(int L) { return (L + 16 * kFusedWaves - 1) / (16 * kFusedWaves); }
-
+// Larger MXFP4 batches: persistent weight-streaming gate/up, then down (the combine follows).
 template <bool MX>
 hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
-    constexpr int W = kFusedWaves;
-    constexpr int MAXG = MX ? 2 : 8;
-    FusedExperts<MX> f{StreamUp<MX>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.H},
-                       StreamDown<MX>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y},
-                       (int)cdiv(Fmax, 16 * W), fused_down_groups(a.L), a.counters, a.counters + a.max_tiles,
-                       a.status, a.w, a.T, a.k, a.Fs > 0 ? 1 : 0, a.m16};
-    auto kern = fused_experts_kernel<W, (MX ? 1 : kChunk), MAXG, MX>;
-    const long items = (long)a.max_tiles * std::max(f.up_rg, f.dn_rg);
-    const int grid = (int)std::min<long>(items, resident_blocks(kern, 64 * W));
     ev.begin(kStageUp);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * W), 0, s, f);
-    hipError_t err = last();
+    hipError_t err = launch_stream<kUW, kUKS, 2>(StreamUp<MX>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs,
+                                                              a.Hs, a.H},
+                                                 a.max_tiles, Fmax, s);
+    if (err != hipSuccess) return err;
     ev.end(kStageUp);
-    return err;
+    ev.begin(kStageDown);
+    err = launch_stream<kDW, kDKS, 1>(StreamDown<MX>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y},
+                                      a.max_tiles, a.L, s);
+    if (err != hipSuccess) return err;
+    ev.end(kStageDown);
+    return hipSuccess;
 }
 
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {
     const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E};
+    if (a.decode_path)
+        return a.mxfp4 ? launch_decode_experts<true>(a, seg, s, ev) : launch_decode_experts<false>(a, seg, s, ev);
     if (a.stream_path) return a.mxfp4 ? launch_stream_experts<true>(a, seg, s, ev) : launch_stream_experts<false>(a, seg, s, ev);
     if (a.mxfp4) return hipErrorInvalidValue;  // the tile path takes bf16 experts only
     const int Fmax = std::max(a.F, a.Fs);

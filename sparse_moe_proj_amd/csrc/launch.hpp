@@ -33,7 +33,7 @@ struct StageEvents {
     void begin(int stage) { rec(2 * stage); }
     void end(int stage) { rec(2 * stage + 1); }
 };
-constexpr int kStageUp = 5, kStageDown = 6;  // LMOE_STAGE_EXPERT_UP / _DOWN
+constexpr int kStageUp = 5, kStageDown = 6, kStageCombine = 7;  // LMOE_STAGE_EXPERT_UP / _DOWN / COMBINE
 
 // Batches of at most this many tokens use the weight-streaming (decode) kernels.
 constexpr int kStreamMaxT = 16;
@@ -52,19 +52,17 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 int perm_blocks(int T);
 
 // tiles may be null (no work list).  hist/base: [perm_blocks(T)][E] ints (unused when T <= 64).
-// zero/nzero: a region of int32 counters cleared by the permutation launch.
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist, int32_t* base, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
-                          int32_t* zero, int nzero, int32_t* status, hipStream_t s);
+                          hipStream_t s);
 
 // top-k followed by the permutation; one fused launch when T <= 64.
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
-                               int32_t* ntiles, int has_shared, int32_t* zero, int nzero, int32_t* status,
-                               hipStream_t s);
+                               int32_t* ntiles, int has_shared, hipStream_t s);
 
-// Row groups of the down projection in the fused small-batch expert launch.
-int fused_down_groups(int L);
+// Slices of the SwiGLU width in the small-batch expert launch (partial rows per routed row).
+int decode_slices(int F, int Fs, bool mx);
 
 int expert_tile_rows(bool stream_path);
 int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path);
@@ -82,10 +80,9 @@ struct ExpertArgs {
     float* Y;
     int max_tiles;
     bool stream_path;
+    bool decode_path;  // T <= kStreamMaxT: one launch per (tile, F slice), partials P, merge into m16
     bool mxfp4;
-    // fused small-batch path: counters (max_tiles + fused_down_groups(L)), status, merge inputs/output
-    int32_t* counters;
-    int32_t* status;
+    float* P;          // [T*k + T][decode_slices][L]
     const float* w;
     uint16_t* m16;
 };
