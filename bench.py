@@ -198,6 +198,22 @@ def cpu_baseline(wl, seconds):
             "seconds": round(dt, 2)}
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the decode expert kernel from the committed rocprofv3 counter passes
+    (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None when the kernel's sources
+    have changed since the counters were taken or no pass covers this workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_decode_experts_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, "sparse_moe_proj_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def roofline_hbm(counts, up_ms, traffic=None):
     achieved = counts["expert_bytes"] / (up_ms / 1e3) / 1e9
     return {"bound": "hbm", "kernel": "decode_experts_kernel (gate/up, SwiGLU, down per F slice)",
@@ -241,7 +257,7 @@ def main():
     m = measure(wl, args.steps, args.warmup, args.rotate)
     c = m["counts"]
     mfma_bound = c["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > c["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
-    rl = roofline_mfma(c, m["up_ms"]) if mfma_bound else roofline_hbm(c, m["up_ms"])
+    rl = roofline_mfma(c, m["up_ms"]) if mfma_bound else roofline_hbm(c, m["up_ms"], measured_traffic(wl.name))
     layer_s = m["ms_per_step"] / 1e3
     out = {
         "metric": METRIC,
