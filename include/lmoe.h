@@ -33,6 +33,14 @@
  *             byte (value 2^(byte-127)) per 32 consecutive K values.
  *     Routed experts are n_experts records back to back.  The shared expert record uses
  *     the dense dtype and shared_ffn in place of ffn.
+ *   - lmoe_forward reads BF16 and MXFP4 records in the PACKED layout that lmoe_pack_experts
+ *     writes (same size; F32 records stay row-major).  Packing permutes each matrix into
+ *     1 KB tiles of 16 rows: BF16 tiles hold 16 rows x 32 columns, the 16-byte unit of row j
+ *     and columns 8q..8q+7 at position 16q + j, tiles ordered by (row block, column step);
+ *     MXFP4 nibble tiles hold 16 rows x 128 values (unit of row j, values 32q..32q+31 at
+ *     position 16q + j) and each has a 64-byte scale tile in the same order.  A tile is the
+ *     register image of one matrix-core operand, so the kernels read it with contiguous 1 KB
+ *     wave loads.
  *   - BF16 tensors hold raw bf16 bit patterns (uint16).
  *   - All calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the
  *     null stream), allocate nothing, never synchronise, keep no per-call state, and may be
@@ -94,8 +102,8 @@ typedef struct {
     const void* U;        /* [hidden][latent], dense dtype */
     const void* Wr;       /* [n_experts][latent], dense dtype */
     const float* br;      /* [n_experts] fp32 router bias, or NULL for none */
-    const void* shared;   /* one record (dense dtype, shared_ffn), or NULL iff shared_ffn == 0 */
-    const void* experts;  /* n_experts records (expert dtype) */
+    const void* shared;   /* one packed record (dense dtype, shared_ffn), or NULL iff shared_ffn == 0 */
+    const void* experts;  /* n_experts packed records (expert dtype; F32: row-major) */
 } lmoe_weights;
 
 /* Stages of lmoe_forward, in launch order (for lmoe_forward_opts.stage_events). */
@@ -144,7 +152,19 @@ lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* byte
 lmoe_status lmoe_permute_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes);
 
 /*
- * Router (page: "the router picks 10 of 512 experts", Fig. 3 caption).
+ * Expert record packing (a layout step before lmoe_forward; no arithmetic).
+ *   shared = 0: n_records routed records (expert dtype); shared = 1: the shared record
+ *   (dense dtype, shared_ffn; n_records <= 1).
+ *   src: n_records row-major records; dst: the same number of packed records.  src and dst
+ *   must not overlap.  F32 configurations return LMOE_ERR_UNSUPPORTED (their records are
+ *   read row-major).
+ */
+lmoe_status lmoe_pack_experts(const lmoe_config* cfg, int32_t shared, const void* src, void* dst, int32_t n_records,
+                              void* stream);
+
+/*
+ * Router (the model-detail page's architecture section: the router selects 10 of the 512
+ * experts, Fig. 3 caption).
  *   z   [T][latent] fp32 latent states;
  *   ids [T][top_k] int32 out: the top_k experts of each token, ascending id;
  *   w   [T][top_k] fp32 out: softmax over the selected logits, same order.

@@ -65,6 +65,7 @@ def _load():
         "lmoe_route": (I32, [cfgp, wp, P, I32, P, P, P, SZ, P]),
         "lmoe_permute": (I32, [cfgp, P, I32, P, P, P, P, SZ, P]),
         "lmoe_forward": (I32, [cfgp, wp, P, I32, P, ctypes.POINTER(lmoe_forward_opts), P, SZ, P]),
+        "lmoe_pack_experts": (I32, [cfgp, I32, P, P, I32, P]),
         "lmoe_status_str": (ctypes.c_char_p, [I32]),
         "lmoe_last_error": (ctypes.c_char_p, []),
         "lmoe_version": (I32, []),
@@ -161,6 +162,10 @@ def lmoe_permute(cfg, ids, T, offsets, perm, inv, ws, ws_bytes, stream=None) -> 
 def lmoe_forward(cfg, weights, x, T, y, opts, ws, ws_bytes, stream=None) -> int:
     return lib.lmoe_forward(ctypes.byref(cfg), ctypes.byref(weights), _p(x), int(T), _p(y),
                             ctypes.byref(opts) if opts is not None else None, _p(ws), int(ws_bytes), _stream(stream))
+
+
+def lmoe_pack_experts(cfg, shared, src, dst, n_records, stream=None) -> int:
+    return lib.lmoe_pack_experts(ctypes.byref(cfg), int(shared), _p(src), _p(dst), int(n_records), _stream(stream))
 
 
 def lmoe_status_str(status: int) -> str:

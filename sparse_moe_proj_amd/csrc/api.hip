@@ -86,7 +86,7 @@ Layout plan(const Dims& d, int T) {
     const size_t act = d.f32 ? 4 : 2;
     const int has_shared = d.Fs > 0;
     lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx);
-    lo.decode_path = !d.f32 && T <= kStreamMaxT;
+    lo.decode_path = !d.f32 && T <= kStreamMaxT && decode_fits(d.F, d.Fs, d.mx);
     lo.BM = expert_tile_rows(lo.stream_path);
     lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path);
     lo.Hs = std::max(d.F, d.Fs);
@@ -145,6 +145,27 @@ size_t lmoe_expert_record_bytes(const lmoe_config* cfg, int32_t shared) {
     if (check_config(cfg, d) != LMOE_OK) return 0;
     if (shared && d.Fs == 0) return 0;
     return record_bytes(d, shared != 0);
+}
+
+lmoe_status lmoe_pack_experts(const lmoe_config* cfg, int32_t shared, const void* src, void* dst, int32_t n_records,
+                              void* stream) {
+    Dims d;
+    lmoe_status st = check_config(cfg, d);
+    if (st != LMOE_OK) return st;
+    if (d.f32) return fail(LMOE_ERR_UNSUPPORTED, "fp32 records are read row-major and are not packed");
+    if (shared && d.Fs == 0) return fail(LMOE_ERR_SHAPE, "shared_ffn is 0: there is no shared record");
+    if (n_records < 0 || n_records > 65535 || (shared && n_records > 1))
+        return fail(LMOE_ERR_SHAPE, "n_records must be in [0, 65535] (at most 1 shared record; got %d)", n_records);
+    if (n_records == 0) return LMOE_OK;
+    if (!src || !dst) return fail(LMOE_ERR_NULL, "src and dst must be non-NULL");
+    if (!aligned16(src) || !aligned16(dst)) return fail(LMOE_ERR_ALIGN, "src and dst must be 16-byte aligned");
+    const size_t rec = record_bytes(d, shared != 0);
+    if (overlap(src, rec * n_records, dst, rec * n_records))
+        return fail(LMOE_ERR_UNSUPPORTED, "src and dst overlap (packing is not in place)");
+    const hipError_t e = launch_pack(src, dst, rec, n_records, shared ? d.Fs : d.F, d.L, d.mx && !shared,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pack experts");
+    return LMOE_OK;
 }
 
 lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes) {

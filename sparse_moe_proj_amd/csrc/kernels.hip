@@ -458,6 +458,9 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_DECODE_WAVES
 #define LMOE_DECODE_WAVES 4
 #endif
+#ifndef LMOE_DECODE_KSU
+#define LMOE_DECODE_KSU 1
+#endif
 #ifndef LMOE_STREAM_GRID
 #define LMOE_STREAM_GRID 2048
 #endif
@@ -571,28 +574,42 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
 }
 
-constexpr int decode_waves(bool mx) { return mx ? 8 : LMOE_DECODE_WAVES; }
+// Small-batch expert launch shape: bf16 LMOE_DECODE_WAVES waves with LMOE_DECODE_KSU waves per
+// row block; MXFP4 slices must hold whole 128-value groups, so 8 waves, one per row block.
+template <bool MX>
+struct DecodeCfg {
+    static constexpr int kWaves = MX ? 8 : LMOE_DECODE_WAVES;
+    static constexpr int kKsu = MX ? 1 : LMOE_DECODE_KSU;
+    static constexpr int kFS = DecodeShape<kWaves, kKsu>::kFS;
+};
 
-int decode_slices(int F, int Fs, bool mx) { return std::max(F, Fs) / (16 * decode_waves(mx)); }
+int decode_slices(int F, int Fs, bool mx) {
+    return std::max(F, Fs) / (mx ? DecodeCfg<true>::kFS : DecodeCfg<false>::kFS);
+}
+
+bool decode_fits(int F, int Fs, bool mx) {
+    const int FS = mx ? DecodeCfg<true>::kFS : DecodeCfg<false>::kFS;
+    return F % FS == 0 && Fs % FS == 0;
+}
 
 // Small batches: gate/up, SwiGLU and down per (tile, F slice) in one launch, then the merge.
 template <bool MX>
 hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
-    constexpr int W = decode_waves(MX);
-    constexpr int FS = 16 * W;
+    using C = DecodeCfg<MX>;
+    constexpr int FS = C::kFS;
     const int nslices = decode_slices(a.F, a.Fs, MX);
     DecodeExperts<MX> d{seg, a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs,
                         nslices, a.P};
     const long items = (long)a.max_tiles * nslices;
     ev.begin(kStageUp);
-    hipLaunchKernelGGL((decode_experts_kernel<W, (MX ? 1 : kChunk), MX>), dim3((unsigned)std::min<long>(items, LMOE_STREAM_GRID)),
-                       dim3(64 * W), 0, s, d);
+    hipLaunchKernelGGL((decode_experts_kernel<C::kWaves, C::kKsu, (MX ? 1 : kChunk), MX>),
+                       dim3((unsigned)std::min<long>(items, LMOE_STREAM_GRID)), dim3(64 * C::kWaves), 0, s, d);
     hipError_t err = last();
     if (err != hipSuccess) return err;
     ev.end(kStageUp);
     ev.begin(kStageCombine);
-    hipLaunchKernelGGL(merge_slices_kernel, dim3(cdiv(a.L, 256), a.T), dim3(64 * kMergeRows), 0, s, a.P, a.w, a.T, a.k, a.L,
-                       nslices, a.F / FS, a.Fs / FS, a.m16);
+    hipLaunchKernelGGL(merge_slices_kernel, dim3(cdiv(a.L, 256), a.T), dim3(64 * kMergeRows), 0, s, a.P, a.w, a.T,
+                       a.k, a.L, nslices, a.F / FS, a.Fs / FS, a.m16);
     if ((err = last()) != hipSuccess) return err;
     ev.end(kStageCombine);
     return hipSuccess;

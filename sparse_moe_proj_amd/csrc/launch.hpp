@@ -63,6 +63,8 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
 
 // Slices of the SwiGLU width in the small-batch expert launch (partial rows per routed row).
 int decode_slices(int F, int Fs, bool mx);
+// Whether the SwiGLU widths split into whole slices (else small batches take the two-launch path).
+bool decode_fits(int F, int Fs, bool mx);
 
 int expert_tile_rows(bool stream_path);
 int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path);
@@ -87,6 +89,9 @@ struct ExpertArgs {
     uint16_t* m16;
 };
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
+
+// Row-major expert records -> packed records (nrec records of rec_bytes; F x L gate/up, L x F down).
+hipError_t launch_pack(const void* src, void* dst, size_t rec_bytes, int nrec, int F, int L, bool mx, hipStream_t s);
 
 hipError_t launch_combine(const float* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
                           hipStream_t s);

@@ -139,6 +139,19 @@ struct TileRouter {
     }
 };
 
+// Expert matrices are stored packed (written by lmoe_pack_experts): a bf16 [N][K] matrix is a
+// sequence of 1 KB tiles, 16 rows x 32 columns each, ordered by (row block, column step); inside
+// a tile the 16-byte unit of row j, columns 8 q .. 8 q + 7 sits at position 16 q + j.  That is
+// the register image of a v_mfma_f32_16x16x32_bf16 A operand, so a wave loads it with one
+// contiguous 1 KB access.  packed_row gives row n's first unit, packed_chunk the unit holding
+// columns 64 kt + 8 lc .. + 7.
+__device__ __forceinline__ const uint16_t* packed_row(const uint16_t* m, int n, int K) {
+    return m + (size_t)(n >> 4) * 16 * K + (n & 15) * 8;
+}
+__device__ __forceinline__ const uint16_t* packed_chunk(const uint16_t* row, int kt, int lc) {
+    return row + (kt * 2 + (lc >> 2)) * 512 + (lc & 3) * 128;
+}
+
 // Fused SwiGLU gate/up over a work list.  The B tile's 128 rows are, for each of the two
 // wave columns, 32 gate rows followed by the same 32 up rows, so every lane ends with g and u
 // of the same (row, f) in acc[i][0] / acc[i][1] and applies SiLU(g) * u in registers.
@@ -177,11 +190,11 @@ struct TileUp {
     __device__ RowB row_b(const Ctx& c, int r) const {
         const int f = c.f0 + (r >> 6) * 32 + (r & 31);
         if (f >= c.F) return nullptr;
-        return ((r >> 5) & 1 ? c.u : c.g) + (size_t)f * L;
+        return packed_row((r >> 5) & 1 ? c.u : c.g, f, L);
     }
     __device__ int k_tiles(const Ctx&) const { return L / 64; }
     __device__ uint4 load_a(const Ctx&, RowA r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
-    __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
+    __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const { return r ? ld16(packed_chunk(r, kt, lc)) : zero4(); }
     template <int MB, int NB>
     __device__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
         static_assert(NB == 2, "gate block + up block per wave column");
@@ -226,10 +239,10 @@ struct TileDown {
         return c.n0 < L;
     }
     __device__ RowA row_a(const Ctx& c, int r) const { return r < c.nrows ? H + (size_t)(c.row0 + r) * Hs : nullptr; }
-    __device__ RowB row_b(const Ctx& c, int r) const { return c.n0 + r < L ? c.d + (size_t)(c.n0 + r) * c.F : nullptr; }
+    __device__ RowB row_b(const Ctx& c, int r) const { return c.n0 + r < L ? packed_row(c.d, c.n0 + r, c.F) : nullptr; }
     __device__ int k_tiles(const Ctx& c) const { return c.F / 64; }
     __device__ uint4 load_a(const Ctx&, RowA r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
-    __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
+    __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const { return r ? ld16(packed_chunk(r, kt, lc)) : zero4(); }
     template <int MB, int NB>
     __device__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
 #pragma unroll
@@ -362,12 +375,14 @@ struct StreamRouter {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Expert weights for the stream kernels.
-//   bf16 records: one MFMA step per load (kSPL 1), 16 bytes per lane.
-//   MXFP4 records: four MFMA steps per load (kSPL 4): lane (row, kq) reads 16 bytes of packed
+// Expert weights for the stream kernels (packed records, see packed_row).
+//   bf16 records: one MFMA step per load (kSPL 1), 16 bytes per lane, 1 KB per wave.
+//   MXFP4 records: four MFMA steps per load (kSPL 4): lane (row, kq) reads 16 bytes of
 //   nibbles = the 32 values k in [128g + 32kq, +32) and their one scale byte; step t of the
-//   group uses values 8t..8t+7 of them.  In MXFP4 kernels the (bf16) shared expert is read in
-//   the same k order: 64 bytes per lane per group.
+//   group uses values 8t..8t+7 of them.  Packed MXFP4 matrices are 1 KB tiles of 16 rows x 128
+//   values (unit of row j, values 32 q .. 32 q + 31 at position 16 q + j), with a 64-byte scale
+//   tile per nibble tile in the same unit order.  In MXFP4 kernels the (bf16) shared expert is
+//   read in the same k order: 64 bytes per lane per group.
 // ---------------------------------------------------------------------------------------------
 struct WRaw4 { uint4 a[4]; };
 
@@ -378,11 +393,13 @@ template <>
 struct ExpertRows<false> {
     static constexpr int kSPL = 1;
     typedef uint4 WRaw;
-    struct Mat { const uint16_t* p; };     // matrix base, rows of K elements
-    struct Row { const uint16_t* p; };
-    __device__ static Row row(const Mat& m, int n, int K) { return Row{m.p + (size_t)n * K}; }
+    struct Mat { const uint16_t* p; };  // packed matrix base (see packed_unit)
+    struct Row { const uint16_t* p; };  // row n: its 16-row block plus (n % 16) lane units
+    __device__ static Row row(const Mat& m, int n, int K) {
+        return Row{m.p + (size_t)(n >> 4) * 16 * K + (n & 15) * 8};
+    }
     template <bool>
-    __device__ static WRaw load(const Row& r, int s, int kq) { return ld16(r.p + s * 32 + kq * 8); }
+    __device__ static WRaw load(const Row& r, int s, int kq) { return ld16(r.p + s * 512 + kq * 128); }
     template <bool>
     __device__ static uint4 frag(const WRaw& w, int) { return w; }
 };
@@ -394,20 +411,22 @@ struct ExpertRows<true> {
     struct Mat { const uint8_t* p; const uint8_t* sc; };  // sc == null: bf16 matrix (shared expert)
     struct Row { const uint8_t* p; const uint8_t* sc; };
     __device__ static Row row(const Mat& m, int n, int K) {
-        if (m.sc) return Row{m.p + (size_t)n * (K / 2), m.sc + (size_t)n * (K / 32)};
-        return Row{m.p + (size_t)n * K * 2, nullptr};
+        if (m.sc) return Row{m.p + (size_t)(n >> 4) * 8 * K + (n & 15) * 16, m.sc + (size_t)(n >> 4) * (K / 2) + (n & 15)};
+        return Row{m.p + ((size_t)(n >> 4) * 16 * K + (n & 15) * 8) * 2, nullptr};
     }
+    // group g (128 values): MXFP4 lane kq holds values 32 kq .. + 32 of the group and their
+    // scale; a bf16 row gives the same values as four 16-byte units (steps 4g + kq, units t)
     template <bool MXR>
     __device__ static WRaw load(const Row& r, int g, int kq) {
         WRaw w;
         if constexpr (MXR) {
-            w.a[0] = ld16(r.p + g * 64 + kq * 16);
-            w.a[1] = make_uint4(r.sc[g * 4 + kq], 0, 0, 0);
+            w.a[0] = ld16(r.p + g * 1024 + kq * 256);
+            w.a[1] = make_uint4(r.sc[g * 64 + kq * 16], 0, 0, 0);
             w.a[2] = w.a[3] = zero4();
         } else {
-            const uint8_t* b = r.p + (size_t)(g * 128 + kq * 32) * 2;
+            const uint8_t* b = r.p + (size_t)(g * 4 + kq) * 1024;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) w.a[t] = ld16(b + t * 16);
+            for (int t = 0; t < 4; ++t) w.a[t] = ld16(b + t * 256);
         }
         return w;
     }

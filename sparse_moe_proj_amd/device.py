@@ -9,8 +9,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (LMOE_OK, check, lmoe_forward, lmoe_workspace_bytes, make_config, make_opts,  # noqa: F401
-               make_weights)
+from . import (LMOE_OK, check, lmoe_expert_record_bytes, lmoe_forward, lmoe_pack_experts,  # noqa: F401
+               lmoe_workspace_bytes, make_config, make_opts, make_weights)
 
 
 def to_device(a, device="cuda"):
@@ -24,10 +24,24 @@ def to_device(a, device="cuda"):
     return t.to(device)
 
 
-class DeviceLayer:
-    """One layer's weights resident in HBM (tensors kept alive by this object)."""
+def pack_records(cfg, records, shared: bool):
+    """Device copy of row-major expert records in the packed layout lmoe_forward reads."""
+    n = 1 if shared else records.shape[0]
+    need = n * lmoe_expert_record_bytes(cfg, int(shared))
+    have = records.numel() * records.element_size()
+    if have != need:
+        raise ValueError(f"expert records hold {have} bytes, {n} records of this configuration need {need}")
+    out = torch.empty_like(records)
+    check(lmoe_pack_experts(cfg, int(shared), records, out, n))
+    return out
 
-    def __init__(self, lw=None, act="bf16", device="cuda", _copy_of=None):
+
+class DeviceLayer:
+    """One layer's weights resident in HBM (tensors kept alive by this object).  Expert records
+    are uploaded row-major and packed on the device (fp32 records stay row-major).  pack=False
+    keeps them as given: only for callers that use the routing entry points alone."""
+
+    def __init__(self, lw=None, act="bf16", device="cuda", _copy_of=None, pack=True):
         if _copy_of is not None:
             src = _copy_of
             self.shape, self.act, self.dense, self.expert = src.shape, src.act, src.dense, src.expert
@@ -45,6 +59,10 @@ class DeviceLayer:
         s = self.shape
         self.cfg = make_config(s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn, self.act, self.dense,
                                self.expert)
+        if _copy_of is None and pack and self.expert != "f32":
+            self.experts = pack_records(self.cfg, self.experts, False)
+            if self.shared is not None:
+                self.shared = pack_records(self.cfg, self.shared, True)
         self.weights = make_weights(self.D, self.U, self.Wr, self.br, self.shared, self.experts)
 
     def clone(self) -> "DeviceLayer":

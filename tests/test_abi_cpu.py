@@ -138,3 +138,18 @@ def test_single_hip_runtime_in_process():
     with open("/proc/self/maps") as f:
         libs = {line.split()[-1] for line in f if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+def test_pack_arguments_checked():
+    c = cfg()
+    rec = lm.lmoe_expert_record_bytes(c, 0)
+    t = gen.TINY
+    f32 = lm.make_config(t.hidden, t.latent, t.n_experts, t.top_k, t.ffn, t.shared_ffn, "f32", "f32", "f32")
+    assert lm.lmoe_pack_experts(f32, 0, FAKE, FAKE + (1 << 30), 4, 0) == lm.LMOE_ERR_UNSUPPORTED
+    assert lm.lmoe_pack_experts(cfg(shared_ffn=0), 1, FAKE, FAKE + (1 << 30), 1, 0) == lm.LMOE_ERR_SHAPE
+    assert lm.lmoe_pack_experts(c, 1, FAKE, FAKE + (1 << 30), 2, 0) == lm.LMOE_ERR_SHAPE
+    assert lm.lmoe_pack_experts(c, 0, FAKE, FAKE + (1 << 30), -1, 0) == lm.LMOE_ERR_SHAPE
+    assert lm.lmoe_pack_experts(c, 0, None, FAKE, 4, 0) == lm.LMOE_ERR_NULL
+    assert lm.lmoe_pack_experts(c, 0, FAKE + 4, FAKE + (1 << 34), 4, 0) == lm.LMOE_ERR_ALIGN
+    assert lm.lmoe_pack_experts(c, 0, FAKE, FAKE + rec, 4, 0) == lm.LMOE_ERR_UNSUPPORTED  # overlap
+    assert lm.lmoe_pack_experts(c, 0, None, None, 0, 0) == lm.LMOE_OK  # nothing to do

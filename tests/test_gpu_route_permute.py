@@ -23,7 +23,7 @@ def test_route_isolated(T):
     x = oracle.decode(gen.make_tokens(wl, T=T, salt=T), "bf16")
     z32 = (x @ L.D.T).astype(np.float32)
     ids_o, w_o, gap_o, logits_o = oracle.route(z32.astype(np.float64), L.Wr, L.br, lw.shape.top_k)
-    dl = DeviceLayer(lw, act="bf16")
+    dl = DeviceLayer(lw, act="bf16", pack=False)
     k = lw.shape.top_k
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
