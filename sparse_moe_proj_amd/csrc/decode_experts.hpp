@@ -236,12 +236,19 @@ __global__ __launch_bounds__(64 * kMergeRows) void merge_slices_kernel(const flo
         const int nq = sh ? ns_shared : ns_routed;
         float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
         if (ok) {
-            for (int q = 0; q < nq; ++q) {
-                const float4 v = *reinterpret_cast<const float4*>(row + (size_t)q * L);
-                y.x += v.x;
-                y.y += v.y;
-                y.z += v.z;
-                y.w += v.w;
+            // slices in batches of 8 loads in flight (clamped addresses), summed in slice order
+            for (int q0 = 0; q0 < nq; q0 += 8) {
+                float4 v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const float4*>(row + (size_t)min(q0 + i, nq - 1) * L);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (q0 + i < nq) {
+                        y.x += v[i].x;
+                        y.y += v[i].y;
+                        y.z += v[i].z;
+                        y.w += v[i].w;
+                    }
             }
             if (!sh) {
                 const float ws = w[(size_t)t * k + r];

@@ -130,16 +130,14 @@ template <int NV>
 __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids,
                                            float* __restrict__ w) {
     const int lane = threadIdx.x & 63;
+    // all loads first (clamped addresses, no branch), so they are in flight together
     float v[NV];
 #pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
+#pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const int id = lane + 64 * j;
-        float x = -INFINITY;
-        if (id < E) {
-            x = row[id];
-            if (!(x == x)) x = -INFINITY;  // NaN never wins and never breaks the selection
-        }
-        v[j] = x;
+        const bool ok = lane + 64 * j < E && v[j] == v[j];  // NaN never wins and never breaks the selection
+        v[j] = ok ? v[j] : -INFINITY;
     }
     bool keep[NV];
     int pos[NV];
@@ -455,9 +453,6 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_CHUNK
 #define LMOE_CHUNK 4
 #endif
-#ifndef LMOE_DECODE_WAVES
-#define LMOE_DECODE_WAVES 4
-#endif
 #ifndef LMOE_DECODE_KSU
 #define LMOE_DECODE_KSU 1
 #endif
@@ -574,36 +569,33 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
 }
 
-// Small-batch expert launch shape: bf16 LMOE_DECODE_WAVES waves with LMOE_DECODE_KSU waves per
-// row block; MXFP4 slices must hold whole 128-value groups, so 8 waves, one per row block.
-template <bool MX>
-struct DecodeCfg {
-    static constexpr int kWaves = MX ? 8 : LMOE_DECODE_WAVES;
-    static constexpr int kKsu = MX ? 1 : LMOE_DECODE_KSU;
-    static constexpr int kFS = DecodeShape<kWaves, kKsu>::kFS;
-};
+// Small-batch expert launch shape: 8 waves, one 16-row block each, so a slice is 128 columns of
+// F (MXFP4 slices must hold whole 128-value groups); bf16 widths that are not multiples of 128
+// use 4 waves (64-column slices).
+constexpr int kDecodeKsu = LMOE_DECODE_KSU;
 
-int decode_slices(int F, int Fs, bool mx) {
-    return std::max(F, Fs) / (mx ? DecodeCfg<true>::kFS : DecodeCfg<false>::kFS);
+int decode_waves(int F, int Fs, bool mx) {
+    return mx || (F % (128 * kDecodeKsu) == 0 && Fs % (128 * kDecodeKsu) == 0) ? 8 : 4;
 }
 
+int decode_slices(int F, int Fs, bool mx) { return std::max(F, Fs) / (16 * decode_waves(F, Fs, mx) / kDecodeKsu); }
+
 bool decode_fits(int F, int Fs, bool mx) {
-    const int FS = mx ? DecodeCfg<true>::kFS : DecodeCfg<false>::kFS;
+    const int FS = 16 * decode_waves(F, Fs, mx) / kDecodeKsu;
     return F % FS == 0 && Fs % FS == 0;
 }
 
 // Small batches: gate/up, SwiGLU and down per (tile, F slice) in one launch, then the merge.
-template <bool MX>
+template <bool MX, int W>
 hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
-    using C = DecodeCfg<MX>;
-    constexpr int FS = C::kFS;
+    constexpr int FS = DecodeShape<W, kDecodeKsu>::kFS;
     const int nslices = decode_slices(a.F, a.Fs, MX);
     DecodeExperts<MX> d{seg, a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs,
                         nslices, a.P};
     const long items = (long)a.max_tiles * nslices;
     ev.begin(kStageUp);
-    hipLaunchKernelGGL((decode_experts_kernel<C::kWaves, C::kKsu, (MX ? 1 : kChunk), MX>),
-                       dim3((unsigned)std::min<long>(items, LMOE_STREAM_GRID)), dim3(64 * C::kWaves), 0, s, d);
+    hipLaunchKernelGGL((decode_experts_kernel<W, kDecodeKsu, (MX ? 1 : kChunk), MX>),
+                       dim3((unsigned)std::min<long>(items, LMOE_STREAM_GRID)), dim3(64 * W), 0, s, d);
     hipError_t err = last();
     if (err != hipSuccess) return err;
     ev.end(kStageUp);
@@ -613,6 +605,13 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     if ((err = last()) != hipSuccess) return err;
     ev.end(kStageCombine);
     return hipSuccess;
+}
+
+template <bool MX>
+hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
+    if (decode_waves(a.F, a.Fs, MX) == 8) return launch_decode_experts<MX, 8>(a, seg, s, ev);
+    if constexpr (!MX) return launch_decode_experts<MX, 4>(a, seg, s, ev);
+    return hipErrorInvalidValue;  // not reached: MXFP4 always takes 8 waves
 }
 
 // Larger MXFP4 batches: persistent weight-streaming gate/up, then down (the combine follows).
