@@ -84,46 +84,83 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
-// Selects the top k of a wave's NV-per-lane logits.  Returns, per value j, whether it is kept
-// and its rank among the kept ids (ascending id).  Also returns the largest kept logit.
+// Maximum over the wave, returned uniform: DPP within each row of 16 lanes (swap neighbours,
+// swap pairs, rotate by 4, rotate by 8), then the four row maxima through scalar reads.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Sum over the wave in a fixed order (same DPP tree as wave_max_u32), returned uniform.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Selects the top k of a wave's NV-per-lane logits (value j of lane l is expert l + 64 j).
+// k rounds of a wave-wide maximum over order-preserving keys; among equal keys the lowest
+// expert id is taken (lowest j, then lowest lane).  Returns, per value j, whether it is kept
+// and its rank among the kept ids (ascending id), and the largest kept logit.
 template <int NV>
 __device__ __forceinline__ void wave_topk(const float (&v)[NV], int E, int k, bool (&keep)[NV], int (&pos)[NV],
                                           float& vmax) {
     const int lane = threadIdx.x & 63;
     uint32_t key[NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) key[j] = (lane + 64 * j < E) ? order_key(v[j]) : 0u;  // valid keys are > 0
-    uint32_t prefix = 0;
-    int remaining = k;
-#pragma unroll 1
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t want = (prefix >> b) | 1u;
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) cnt += popc64(__ballot((key[j] >> b) == want));
-        if (cnt >= remaining)
-            prefix |= 1u << b;
-        else
-            remaining -= cnt;
+    for (int j = 0; j < NV; ++j) {
+        key[j] = (lane + 64 * j < E) ? order_key(v[j]) : 0u;  // valid keys are > 0
+        keep[j] = false;
     }
-    // prefix is the k-th largest key; `remaining` keys equal to it are kept (lowest ids first)
+    uint32_t first = 0;
+#pragma unroll 1
+    for (int r = 0; r < k; ++r) {
+        uint32_t m = key[0];
+#pragma unroll
+        for (int j = 1; j < NV; ++j) m = max(m, key[j]);
+        m = wave_max_u32(m);
+        if (r == 0) first = m;
+        // the winner: lowest j holding m, then the lowest lane there (uniform scalar choice)
+        uint64_t b[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) b[j] = __ballot(key[j] == m);
+        int wj = NV - 1;
+        uint64_t wb = b[NV - 1];
+#pragma unroll
+        for (int j = NV - 2; j >= 0; --j)
+            if (b[j] != 0ull) {
+                wj = j;
+                wb = b[j];
+            }
+        const bool mine = lane == __ffsll((unsigned long long)wb) - 1;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const bool t = mine && j == wj;
+            keep[j] = keep[j] || t;
+            key[j] = t ? 0u : key[j];
+        }
+    }
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int eq_before = 0, sel_before = 0;
-    float m = -INFINITY;
+    int sel_before = 0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const uint64_t eq = __ballot(key[j] == prefix);
-        const bool take_eq = key[j] == prefix && eq_before + popc64(eq & lt) < remaining;
-        eq_before += popc64(eq);
-        keep[j] = key[j] > prefix || take_eq;
         const uint64_t sel = __ballot(keep[j]);
         pos[j] = sel_before + popc64(sel & lt);
         sel_before += popc64(sel);
-        if (keep[j]) m = fmaxf(m, v[j]);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    vmax = m;
+    // back from the order key to the value
+    vmax = __uint_as_float((first & 0x80000000u) ? (first & 0x7fffffffu) : ~first);
 }
 
 template <int NV>
@@ -149,8 +186,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
         e[j] = keep[j] ? expf(v[j] - vmax) : 0.f;
         s += e[j];
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    s = wave_sum_f32(s);
 #pragma unroll
     for (int j = 0; j < NV; ++j)
         if (keep[j]) {
