@@ -492,6 +492,12 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_DECODE_KSU
 #define LMOE_DECODE_KSU 1
 #endif
+#ifndef LMOE_TILE_M
+#define LMOE_TILE_M 128
+#endif
+#ifndef LMOE_TILE_N
+#define LMOE_TILE_N 128
+#endif
 #ifndef LMOE_STREAM_GRID
 #define LMOE_STREAM_GRID 2048
 #endif
@@ -499,6 +505,8 @@ constexpr int kPW = LMOE_PROJ_WAVES, kPKS = LMOE_PROJ_KS;
 constexpr int kUW = LMOE_UP_WAVES, kUKS = LMOE_UP_KS;
 constexpr int kDW = LMOE_DOWN_WAVES, kDKS = LMOE_DOWN_KS;
 constexpr int kChunk = LMOE_CHUNK;
+// Tile shape of the many-token GEMMs (projections, router, experts): 4 waves of (M/2) x (N/2).
+using TileL = TileShape<LMOE_TILE_M, LMOE_TILE_N, 2, 2>;
 
 // Persistent launch: at most LMOE_STREAM_GRID workgroups walk max_tiles x row-group items.
 template <int W, int KS, int NMAT, class P>
@@ -521,8 +529,9 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
                             uint16_t* out16, hipStream_t s) {
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1>(StreamProj{x, W, T, N, K, mode, out32, out16}, (int)cdiv(T, 16), N, s);
-    TileProj p{x, W, T, N, K, mode, out32, out16};
-    hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileProj>), dim3(cdiv(T, 128), cdiv(N, 128)), dim3(256), 0, s, p);
+    TileProj<TileL> p{x, W, T, N, K, mode, out32, out16};
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileProj<TileL>>), dim3(cdiv(T, TileL::kBM), cdiv(N, TileL::kBN)),
+                       dim3(256), 0, s, p);
     return last();
 }
 
@@ -530,8 +539,9 @@ hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* b
                               hipStream_t s) {
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1>(StreamRouter{z, Wr, br, T, E, L, logits}, (int)cdiv(T, 16), E, s);
-    TileRouter p{z, Wr, br, T, E, L, logits};
-    hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileRouter>), dim3(cdiv(T, 128), cdiv(E, 128)), dim3(256), 0, s, p);
+    TileRouter<TileL> p{z, Wr, br, T, E, L, logits};
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileRouter<TileL>>), dim3(cdiv(T, TileL::kBM), cdiv(E, TileL::kBN)),
+                       dim3(256), 0, s, p);
     return last();
 }
 
@@ -597,7 +607,7 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
     return last();
 }
 
-int expert_tile_rows(bool stream_path) { return stream_path ? 16 : 128; }
+int expert_tile_rows(bool stream_path) { return stream_path ? 16 : TileL::kBM; }
 
 int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     const long BM = expert_tile_rows(stream_path);
@@ -678,14 +688,16 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
     ev.begin(kStageUp);
-    TileUp up{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H};
-    hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileUp>), dim3(a.max_tiles, cdiv(Fmax, 64)), dim3(256), 0, s, up);
+    TileUp<TileL> up{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H};
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileUp<TileL>>), dim3(a.max_tiles, cdiv(Fmax, TileL::kBN / 2)),
+                       dim3(256), 0, s, up);
     hipError_t err = last();
     if (err != hipSuccess) return err;
     ev.end(kStageUp);
     ev.begin(kStageDown);
-    TileDown dn{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y};
-    hipLaunchKernelGGL((tile_gemm_kernel<Tile128, TileDown>), dim3(a.max_tiles, cdiv(a.L, 128)), dim3(256), 0, s, dn);
+    TileDown<TileL> dn{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y};
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileDown<TileL>>), dim3(a.max_tiles, cdiv(a.L, TileL::kBN)),
+                       dim3(256), 0, s, dn);
     if ((err = last()) != hipSuccess) return err;
     ev.end(kStageDown);
     return hipSuccess;

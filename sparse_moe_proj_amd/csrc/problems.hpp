@@ -48,8 +48,10 @@ struct SegSpace {
 // Tile (prefill) problems: 128x128 tiles, 2x2 waves of 64x64.
 // =============================================================================================
 using Tile128 = TileShape<128, 128, 2, 2>;
+using Tile256 = TileShape<256, 256, 2, 2>;
 
 // Dense projection C[t][n] = x[t] . W[n]; mode 0: z32 + z16 (D), 1: bf16 y (U), 2: y += (U, fp32 residual)
+template <class S>
 struct TileProj {
     const uint16_t* x;  // [M][K] bf16
     const uint16_t* W;  // [N][K] bf16
@@ -60,8 +62,8 @@ struct TileProj {
     typedef const uint16_t* RowA;
     typedef const uint16_t* RowB;
     __device__ bool tile(int bx, int by, Ctx& c) const {
-        c.m0 = bx * Tile128::kBM;
-        c.n0 = by * Tile128::kBN;
+        c.m0 = bx * S::kBM;
+        c.n0 = by * S::kBN;
         return c.m0 < M && c.n0 < N;
     }
     __device__ RowA row_a(const Ctx& c, int r) const { return c.m0 + r < M ? x + (size_t)(c.m0 + r) * K : nullptr; }
@@ -96,6 +98,7 @@ struct TileProj {
 };
 
 // Router logits from fp32 z: K doubled, first half multiplies hi(z), second half lo(z), same Wr.
+template <class S>
 struct TileRouter {
     const float* z;      // [M][K] fp32
     const uint16_t* W;   // [E][K] bf16
@@ -106,8 +109,8 @@ struct TileRouter {
     typedef const float* RowA;
     typedef const uint16_t* RowB;
     __device__ bool tile(int bx, int by, Ctx& c) const {
-        c.m0 = bx * Tile128::kBM;
-        c.n0 = by * Tile128::kBN;
+        c.m0 = bx * S::kBM;
+        c.n0 = by * S::kBN;
         return c.m0 < M && c.n0 < N;
     }
     __device__ RowA row_a(const Ctx& c, int r) const { return c.m0 + r < M ? z + (size_t)(c.m0 + r) * K : nullptr; }
@@ -152,10 +155,13 @@ __device__ __forceinline__ const uint16_t* packed_chunk(const uint16_t* row, int
     return row + (kt * 2 + (lc >> 2)) * 512 + (lc & 3) * 128;
 }
 
-// Fused SwiGLU gate/up over a work list.  The B tile's 128 rows are, for each of the two
-// wave columns, 32 gate rows followed by the same 32 up rows, so every lane ends with g and u
-// of the same (row, f) in acc[i][0] / acc[i][1] and applies SiLU(g) * u in registers.
+// Fused SwiGLU gate/up over a work list.  The B tile's rows are, for each wave column of kWN
+// rows, kWN/2 gate rows followed by the same kWN/2 up rows, so every lane ends with g and u of
+// the same (row, f) in acc[i][j] / acc[i][j + NB/2] and applies SiLU(g) * u in registers.
+template <class S>
 struct TileUp {
+    static constexpr int kHalf = S::kWN / 2;        // f per wave column
+    static constexpr int kFPerTile = S::kBN / 2;    // f per tile
     SegSpace seg;
     const uint16_t* z16;      // [T][L]
     const uint16_t* experts;  // E records
@@ -180,7 +186,7 @@ struct TileUp {
             c.g = experts + (size_t)t.seg * rec;
         }
         c.u = c.g + (size_t)c.F * L;
-        c.f0 = by * 64;
+        c.f0 = by * kFPerTile;
         return c.f0 < c.F;
     }
     __device__ RowA row_a(const Ctx& c, int r) const {
@@ -188,29 +194,34 @@ struct TileUp {
         return z16 + (size_t)seg.token_of(c.seg, c.row0 + r) * L;
     }
     __device__ RowB row_b(const Ctx& c, int r) const {
-        const int f = c.f0 + (r >> 6) * 32 + (r & 31);
+        const int wc = r / S::kWN, rr = r % S::kWN;
+        const int f = c.f0 + wc * kHalf + rr % kHalf;
         if (f >= c.F) return nullptr;
-        return packed_row((r >> 5) & 1 ? c.u : c.g, f, L);
+        return packed_row(rr >= kHalf ? c.u : c.g, f, L);
     }
     __device__ int k_tiles(const Ctx&) const { return L / 64; }
     __device__ uint4 load_a(const Ctx&, RowA r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
     __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const { return r ? ld16(packed_chunk(r, kt, lc)) : zero4(); }
     template <int MB, int NB>
     __device__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
-        static_assert(NB == 2, "gate block + up block per wave column");
-        const int f = c.f0 + (cb >> 6) * 32 + frag32_col(lane);
+        static_assert(NB % 2 == 0 && NB * 16 == kHalf, "gate blocks then up blocks per wave column");
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int j = 0; j < NB / 2; ++j) {
+            const int f = c.f0 + (cb / S::kWN) * kHalf + j * 32 + frag32_col(lane);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = rb + i * 32 + frag32_row(r, lane);
-                if (m < c.nrows && f < c.F)
-                    H[(size_t)(c.row0 + m) * Hs + f] = (uint16_t)f2bf(silu(acc[i][0][r]) * acc[i][1][r]);
-            }
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = rb + i * 32 + frag32_row(r, lane);
+                    if (m < c.nrows && f < c.F)
+                        H[(size_t)(c.row0 + m) * Hs + f] = (uint16_t)f2bf(silu(acc[i][j][r]) * acc[i][j + NB / 2][r]);
+                }
+        }
     }
 };
 
 // Down projection over a work list: Y[dest(p)][n] = H[p] . down[n].
+template <class S>
 struct TileDown {
     SegSpace seg;
     const uint16_t* H;
@@ -235,7 +246,7 @@ struct TileDown {
             c.F = F;
             c.d = experts + (size_t)t.seg * rec + 2 * (size_t)F * L;
         }
-        c.n0 = by * Tile128::kBN;
+        c.n0 = by * S::kBN;
         return c.n0 < L;
     }
     __device__ RowA row_a(const Ctx& c, int r) const { return r < c.nrows ? H + (size_t)(c.row0 + r) * Hs : nullptr; }
