@@ -112,7 +112,7 @@ Layout plan(const Dims& d, int T) {
     lo.tiles = take((size_t)lo.max_tiles * sizeof(Tile));
     lo.ntiles = take(4);
     lo.H = take(lo.decode_path ? 0 : (size_t)lo.R * lo.Hs * act);
-    lo.Y = take(lo.decode_path ? 0 : (size_t)lo.R * d.L * 4);
+    lo.Y = take(lo.decode_path ? 0 : (size_t)lo.R * d.L * (d.f32 ? 4 : 2));
     lo.P = take(lo.decode_path ? (size_t)lo.R * decode_slices(d.F, d.Fs, d.mx) * d.L * 4 : 0);
     lo.m = take((size_t)T * d.L * act);
     lo.total = o;
@@ -278,7 +278,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     int32_t* base = static_cast<int32_t*>(at(lo.base));
     Tile* tiles = static_cast<Tile*>(at(lo.tiles));
     int32_t* ntiles = static_cast<int32_t*>(at(lo.ntiles));
-    float* Y = static_cast<float*>(at(lo.Y));
+    void* Y = at(lo.Y);  // fp32 rows on the fp32 path, bf16 rows otherwise
     const int has_shared = d.Fs > 0;
     hipError_t e;
 
@@ -301,7 +301,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
             return hip_fail(e, "permute");
         ev.end(LMOE_STAGE_PERMUTE);
         F32ExpertArgs a{z32, ids, perm, static_cast<const float*>(wt->experts), static_cast<const float*>(wt->shared),
-                        T, d.k, d.L, d.F, d.Fs, lo.Hs, static_cast<float*>(at(lo.H)), Y};
+                        T, d.k, d.L, d.F, d.Fs, lo.Hs, static_cast<float*>(at(lo.H)), static_cast<float*>(Y)};
         if ((e = launch_experts_f32(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
         float* m = static_cast<float*>(at(lo.m));
         ev.begin(LMOE_STAGE_COMBINE);
@@ -340,7 +340,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     ev.end(LMOE_STAGE_TOPK);
     uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
-                 wt->shared, static_cast<uint16_t*>(at(lo.H)), Y, lo.max_tiles, lo.stream_path,
+                 wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
                  lo.decode_path, d.mx, static_cast<float*>(at(lo.P)), wts, m16};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     if (!lo.decode_path) {  // the small-batch expert path has its own merge launch

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lmoe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -93,5 +95,29 @@ struct Tile {
     int32_t nrows;
     int32_t pad;
 };
+
+// Logical tile of this workgroup.  The grid is (N tiles, M tiles); workgroups are handed to the
+// 8 XCDs round-robin, so the linear id is remapped to give each XCD a contiguous run of logical
+// tiles: the N tiles of one M tile (sharing its activation rows) then run on one XCD, one after
+// the other, and its L2 serves the shared operand.
+__device__ __forceinline__ void xcd_tile(int& m_tile, int& n_tile) {
+    const int total = gridDim.x * gridDim.y;
+    const int bid = blockIdx.x + gridDim.x * blockIdx.y;
+    const int per = total / 8, rem = total % 8;
+    const int x = bid % 8, i = bid / 8;
+    const int l = x * per + min(x, rem) + i;
+    n_tile = l % gridDim.x;
+    m_tile = l / gridDim.x;
+}
+
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices, so register arrays
+// indexed with them stay in registers however large the unrolled body gets).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(static_cast<F&&>(f));
+    }
+}
 
 }  // namespace lmoe

@@ -36,7 +36,9 @@ __global__ __launch_bounds__(256) void tile_gemm_kernel(const P p) {
     __shared__ uint4 sB[2][S::kBN * 8];
 
     typename P::Ctx ctx;
-    if (!p.tile(blockIdx.x, blockIdx.y, ctx)) return;
+    int m_tile, n_tile;
+    xcd_tile(m_tile, n_tile);  // grid: (N tiles, M tiles)
+    if (!p.tile(m_tile, n_tile, ctx)) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;

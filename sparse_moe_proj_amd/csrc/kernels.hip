@@ -354,17 +354,29 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 // ==============================================================================================
 // combine: m[t] = Y[T*k + t] (shared, weight 1) + sum_s w[t][s] * Y[t*k + s], slots in order
 // ==============================================================================================
+// Y rows bf16 (BF16: bf16 path, bf16 out) or fp32 (fp32 path, fp32 out)
+template <bool BF16>
+__device__ __forceinline__ float4 load_y4(const void* Y, size_t off) {
+    if constexpr (BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Y) + off);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                           __uint_as_float(u.y & 0xffff0000u));
+    } else {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(Y) + off);
+    }
+}
+
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y, const float* __restrict__ w, int T,
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const float* __restrict__ w, int T,
                                                       int k, int L, int has_shared, void* __restrict__ m) {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (c >= L) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (has_shared) acc = *reinterpret_cast<const float4*>(Y + ((size_t)T * k + t) * L + c);
+    if (has_shared) acc = load_y4<OUT_BF16>(Y, ((size_t)T * k + t) * L + c);
     for (int s = 0; s < k; ++s) {
         const float ws = w[(size_t)t * k + s];
-        const float4 y = *reinterpret_cast<const float4*>(Y + ((size_t)t * k + s) * L + c);
+        const float4 y = load_y4<OUT_BF16>(Y, ((size_t)t * k + s) * L + c);
         acc.x += ws * y.x;
         acc.y += ws * y.y;
         acc.z += ws * y.z;
@@ -498,6 +510,18 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_TILE_N
 #define LMOE_TILE_N 128
 #endif
+#ifndef LMOE_PIPE_M
+#define LMOE_PIPE_M 128
+#endif
+#ifndef LMOE_PIPE_N
+#define LMOE_PIPE_N 256
+#endif
+#ifndef LMOE_PIPE_NS
+#define LMOE_PIPE_NS 3
+#endif
+#ifndef LMOE_PIPE_PROJ
+#define LMOE_PIPE_PROJ 0
+#endif
 #ifndef LMOE_STREAM_GRID
 #define LMOE_STREAM_GRID 2048
 #endif
@@ -507,6 +531,12 @@ constexpr int kDW = LMOE_DOWN_WAVES, kDKS = LMOE_DOWN_KS;
 constexpr int kChunk = LMOE_CHUNK;
 // Tile shape of the many-token GEMMs (projections, router, experts): 4 waves of (M/2) x (N/2).
 using TileL = TileShape<LMOE_TILE_M, LMOE_TILE_N, 2, 2>;
+// Pipelined (global -> LDS copies, LMOE_PIPE_NS stages) GEMM for the experts (and, with
+// LMOE_PIPE_PROJ, the projections).
+#ifndef LMOE_PIPE
+#define LMOE_PIPE 1
+#endif
+using PipeL = PipeShape<LMOE_PIPE_M, LMOE_PIPE_N, LMOE_PIPE_NS>;
 
 // Persistent launch: at most LMOE_STREAM_GRID workgroups walk max_tiles x row-group items.
 template <int W, int KS, int NMAT, class P>
@@ -529,8 +559,14 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
                             uint16_t* out16, hipStream_t s) {
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1>(StreamProj{x, W, T, N, K, mode, out32, out16}, (int)cdiv(T, 16), N, s);
+    if (LMOE_PIPE_PROJ) {
+        PipeProj<PipeL> p{{x, W, T, N, K, mode, out32, out16}};
+        hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeProj<PipeL>>), dim3(cdiv(N, PipeL::kBN), cdiv(T, PipeL::kBM)),
+                           dim3(256), 0, s, p);
+        return last();
+    }
     TileProj<TileL> p{x, W, T, N, K, mode, out32, out16};
-    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileProj<TileL>>), dim3(cdiv(T, TileL::kBM), cdiv(N, TileL::kBN)),
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileProj<TileL>>), dim3(cdiv(N, TileL::kBN), cdiv(T, TileL::kBM)),
                        dim3(256), 0, s, p);
     return last();
 }
@@ -540,7 +576,7 @@ hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* b
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1>(StreamRouter{z, Wr, br, T, E, L, logits}, (int)cdiv(T, 16), E, s);
     TileRouter<TileL> p{z, Wr, br, T, E, L, logits};
-    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileRouter<TileL>>), dim3(cdiv(T, TileL::kBM), cdiv(E, TileL::kBN)),
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileRouter<TileL>>), dim3(cdiv(E, TileL::kBN), cdiv(T, TileL::kBM)),
                        dim3(256), 0, s, p);
     return last();
 }
@@ -607,7 +643,7 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
     return last();
 }
 
-int expert_tile_rows(bool stream_path) { return stream_path ? 16 : TileL::kBM; }
+int expert_tile_rows(bool stream_path) { return stream_path ? 16 : (LMOE_PIPE ? PipeL::kBM : TileL::kBM); }
 
 int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     const long BM = expert_tile_rows(stream_path);
@@ -687,23 +723,39 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
     if (a.mxfp4) return hipErrorInvalidValue;  // the tile path takes bf16 experts only
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
+    if (LMOE_PIPE) {
+        ev.begin(kStageUp);
+        PipeUp<PipeL> up{{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H}};
+        hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeUp<PipeL>>), dim3(cdiv(Fmax, PipeL::kBN / 2), a.max_tiles),
+                           dim3(256), 0, s, up);
+        hipError_t err = last();
+        if (err != hipSuccess) return err;
+        ev.end(kStageUp);
+        ev.begin(kStageDown);
+        PipeDown<PipeL> dn{{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y}};
+        hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeDown<PipeL>>), dim3(cdiv(a.L, PipeL::kBN), a.max_tiles),
+                           dim3(256), 0, s, dn);
+        if ((err = last()) != hipSuccess) return err;
+        ev.end(kStageDown);
+        return hipSuccess;
+    }
     ev.begin(kStageUp);
     TileUp<TileL> up{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H};
-    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileUp<TileL>>), dim3(a.max_tiles, cdiv(Fmax, TileL::kBN / 2)),
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileUp<TileL>>), dim3(cdiv(Fmax, TileL::kBN / 2), a.max_tiles),
                        dim3(256), 0, s, up);
     hipError_t err = last();
     if (err != hipSuccess) return err;
     ev.end(kStageUp);
     ev.begin(kStageDown);
     TileDown<TileL> dn{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y};
-    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileDown<TileL>>), dim3(a.max_tiles, cdiv(a.L, TileL::kBN)),
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileDown<TileL>>), dim3(cdiv(a.L, TileL::kBN), a.max_tiles),
                        dim3(256), 0, s, dn);
     if ((err = last()) != hipSuccess) return err;
     ev.end(kStageDown);
     return hipSuccess;
 }
 
-hipError_t launch_combine(const float* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
+hipError_t launch_combine(const void* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
                           hipStream_t s) {
     const dim3 grid(cdiv(L / 4, 256), T);
     if (out_bf16)

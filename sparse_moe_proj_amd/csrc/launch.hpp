@@ -79,7 +79,7 @@ struct ExpertArgs {
     size_t rec_bytes;
     const void* shared;
     uint16_t* H;
-    float* Y;
+    uint16_t* Y;       // [T*k + T][L] bf16 expert outputs (T > 16)
     int max_tiles;
     bool stream_path;
     bool decode_path;  // T <= kStreamMaxT: one launch per (tile, F slice), partials P, merge into m16
@@ -93,7 +93,8 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
 // Row-major expert records -> packed records (nrec records of rec_bytes; F x L gate/up, L x F down).
 hipError_t launch_pack(const void* src, void* dst, size_t rec_bytes, int nrec, int F, int L, bool mx, hipStream_t s);
 
-hipError_t launch_combine(const float* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
+// Y: bf16 rows when out_bf16 (the bf16 path), else fp32 rows.
+hipError_t launch_combine(const void* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
                           hipStream_t s);
 
 // fp32 path. mode 0: out = xW^T (+bias); 2: out += xW^T

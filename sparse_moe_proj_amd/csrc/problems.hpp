@@ -72,15 +72,14 @@ struct TileProj {
     __device__ uint4 load_a(const Ctx&, RowA r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
     __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
     template <int MB, int NB>
-    __device__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
+    __device__ __forceinline__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
+        static_for<MB>([&](auto i) {
+            static_for<NB>([&](auto j) {
+                __builtin_amdgcn_sched_barrier(0);  // one block at a time (bounded registers)
+                const int n = c.n0 + cb + j * 32 + frag32_col(lane);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = c.m0 + rb + i * 32 + frag32_row(r, lane);
-                    const int n = c.n0 + cb + j * 32 + frag32_col(lane);
                     if (m < M && n < N) {
                         const float v = acc[i][j][r];
                         const size_t o = (size_t)m * N + n;
@@ -94,6 +93,8 @@ struct TileProj {
                         }
                     }
                 }
+            });
+        });
     }
 };
 
@@ -128,17 +129,17 @@ struct TileRouter {
         return ld16(r + (kt >= h ? kt - h : kt) * 64 + lc * 8);
     }
     template <int MB, int NB>
-    __device__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
+    __device__ __forceinline__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
+        static_for<MB>([&](auto i) {
+            static_for<NB>([&](auto j) {
+                const int n = c.n0 + cb + j * 32 + frag32_col(lane);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = c.m0 + rb + i * 32 + frag32_row(r, lane);
-                    const int n = c.n0 + cb + j * 32 + frag32_col(lane);
                     if (m < M && n < N) logits[(size_t)m * N + n] = acc[i][j][r] + (bias ? bias[n] : 0.f);
                 }
+            });
+        });
     }
 };
 
@@ -203,20 +204,21 @@ struct TileUp {
     __device__ uint4 load_a(const Ctx&, RowA r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
     __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const { return r ? ld16(packed_chunk(r, kt, lc)) : zero4(); }
     template <int MB, int NB>
-    __device__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
+    __device__ __forceinline__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
         static_assert(NB % 2 == 0 && NB * 16 == kHalf, "gate blocks then up blocks per wave column");
-#pragma unroll
-        for (int j = 0; j < NB / 2; ++j) {
+        static_for<NB / 2>([&](auto j) {
             const int f = c.f0 + (cb / S::kWN) * kHalf + j * 32 + frag32_col(lane);
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
+            static_for<MB>([&](auto i) {
+                __builtin_amdgcn_sched_barrier(0);  // one block at a time (bounded registers)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = rb + i * 32 + frag32_row(r, lane);
                     if (m < c.nrows && f < c.F)
-                        H[(size_t)(c.row0 + m) * Hs + f] = (uint16_t)f2bf(silu(acc[i][j][r]) * acc[i][j + NB / 2][r]);
+                        H[(size_t)(c.row0 + m) * Hs + f] =
+                            (uint16_t)f2bf(silu(acc[i][j][r]) * acc[i][j + NB / 2][r]);
                 }
-        }
+            });
+        });
     }
 };
 
@@ -229,7 +231,7 @@ struct TileDown {
     const uint16_t* shared;
     size_t rec;
     int L, F, Fs, Hs;
-    float* Y;  // [R][L]
+    uint16_t* Y;  // [R][L] bf16
     struct Ctx { int seg, row0, nrows, F, n0; const uint16_t* d; };
     typedef const uint16_t* RowA;
     typedef const uint16_t* RowB;
@@ -255,22 +257,22 @@ struct TileDown {
     __device__ uint4 load_a(const Ctx&, RowA r, int kt, int lc) const { return r ? ld16(r + kt * 64 + lc * 8) : zero4(); }
     __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const { return r ? ld16(packed_chunk(r, kt, lc)) : zero4(); }
     template <int MB, int NB>
-    __device__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
+    __device__ __forceinline__ void epilogue(const Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb, int lane) const {
+        static_for<MB>([&](auto i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = rb + i * 32 + frag32_row(r, lane);
-                if (m >= c.nrows) continue;
-                const int drow = seg.dest_of(c.seg, c.row0 + m);
-                if (drow < 0) continue;  // a dropped slot owns no output row
-                const size_t dst = (size_t)drow * L;
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const int n = c.n0 + cb + j * 32 + frag32_col(lane);
-                    if (n < L) Y[dst + n] = acc[i][j][r];
+                // a dropped slot (destination -1) owns no output row
+                const int drow = m < c.nrows ? seg.dest_of(c.seg, c.row0 + m) : -1;
+                if (drow >= 0) {
+                    const size_t dst = (size_t)drow * L;
+                    static_for<NB>([&](auto j) {
+                        const int n = c.n0 + cb + j * 32 + frag32_col(lane);
+                        if (n < L) Y[dst + n] = (uint16_t)f2bf(acc[i][j][r]);
+                    });
                 }
             }
+        });
     }
 };
 
@@ -557,7 +559,7 @@ struct StreamDown {
     size_t rec_bytes;
     const uint16_t* shared;
     int L, F, Fs, Hs;
-    float* Y;
+    uint16_t* Y;  // [R][L] bf16
     struct Ctx { int seg, row0, nrows, F; bool mx; typename ER::Mat m[3]; };
     __device__ int num_tiles() const { return *seg.ntiles; }
     __device__ void tile(int bx, Ctx& c) const {
@@ -584,7 +586,81 @@ struct StreamDown {
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n >= L || j >= c.nrows) return;
         const int drow = seg.dest_of(c.seg, c.row0 + j);
-        if (drow >= 0) Y[(size_t)drow * L + n] = v[0];
+        if (drow >= 0) Y[(size_t)drow * L + n] = (uint16_t)f2bf(v[0]);
+    }
+};
+
+}  // namespace lmoe
+
+// =============================================================================================
+// Pipelined (global -> LDS) problems: the tile problems' contexts and epilogues, plus the
+// per-lane source of each 1 KB copy of a stage (row-major operands: 8 rows per copy; packed
+// expert weights: one 16 x 32 tile per copy).  Rows outside the problem are clamped to a valid
+// row.
+// =============================================================================================
+#include "gemm_pipe.hpp"
+
+namespace lmoe {
+
+template <class S>
+struct PipeProj : TileProj<S> {
+    using B = TileProj<S>;
+    static constexpr bool kAPacked = false, kBPacked = false;
+    __device__ int k_stages(const typename B::Ctx&) const { return B::K / 64; }
+    __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
+        return reinterpret_cast<const uint8_t*>(B::x + (size_t)c.m0 * B::K);
+    }
+    __device__ const uint8_t* b_base(const typename B::Ctx& c) const {
+        return reinterpret_cast<const uint8_t*>(B::W + (size_t)c.n0 * B::K);
+    }
+    __device__ uint32_t src_a(const typename B::Ctx& c, int i, int lane) const {
+        const int r = min(rowmajor_row(i, lane), B::M - 1 - c.m0);
+        return rowmajor_off((uint32_t)r * B::K * 2, i, lane);
+    }
+    __device__ uint32_t src_b(const typename B::Ctx& c, int i, int lane) const {
+        const int r = min(rowmajor_row(i, lane), B::N - 1 - c.n0);
+        return rowmajor_off((uint32_t)r * B::K * 2, i, lane);
+    }
+};
+
+template <class S>
+struct PipeUp : TileUp<S> {
+    using B = TileUp<S>;
+    static constexpr bool kAPacked = false, kBPacked = true;
+    __device__ int k_stages(const typename B::Ctx&) const { return B::L / 64; }
+    __device__ const uint8_t* a_base(const typename B::Ctx&) const { return reinterpret_cast<const uint8_t*>(B::z16); }
+    __device__ const uint8_t* b_base(const typename B::Ctx& c) const { return reinterpret_cast<const uint8_t*>(c.g); }
+    // gathered token rows: byte offsets into z16 stay below 2^32 for T <= 2^20 rows of latent <= 2048
+    __device__ uint32_t src_a(const typename B::Ctx& c, int i, int lane) const {
+        const int r = min(rowmajor_row(i, lane), c.nrows - 1);
+        return rowmajor_off((uint32_t)B::seg.token_of(c.seg, c.row0 + r) * B::L * 2, i, lane);
+    }
+    __device__ uint32_t src_b(const typename B::Ctx& c, int i, int lane) const {
+        const int r = (i >> 1) * 16;  // first B-tile row of this copy (16 rows: one matrix, one f block)
+        const int wc = r / S::kWN, rr = r % S::kWN;
+        const int f = c.f0 + wc * B::kHalf + rr % B::kHalf;
+        const int nb = min(f, c.F - 16) >> 4;
+        const uint32_t mat = rr >= B::kHalf ? (uint32_t)c.F * B::L * 2 : 0u;  // up follows gate
+        return mat + packed_off(nb, i, B::L, lane);
+    }
+};
+
+template <class S>
+struct PipeDown : TileDown<S> {
+    using B = TileDown<S>;
+    static constexpr bool kAPacked = false, kBPacked = true;
+    __device__ int k_stages(const typename B::Ctx& c) const { return c.F / 64; }
+    __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
+        return reinterpret_cast<const uint8_t*>(B::H + (size_t)c.row0 * B::Hs);
+    }
+    __device__ const uint8_t* b_base(const typename B::Ctx& c) const { return reinterpret_cast<const uint8_t*>(c.d); }
+    __device__ uint32_t src_a(const typename B::Ctx& c, int i, int lane) const {
+        const int r = min(rowmajor_row(i, lane), c.nrows - 1);
+        return rowmajor_off((uint32_t)r * B::Hs * 2, i, lane);
+    }
+    __device__ uint32_t src_b(const typename B::Ctx& c, int i, int lane) const {
+        const int nb = min(c.n0 + (i >> 1) * 16, B::L - 16) >> 4;
+        return packed_off(nb, i, c.F, lane);
     }
 };
 
