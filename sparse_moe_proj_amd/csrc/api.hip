@@ -76,7 +76,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t x16, z32, z16, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, P, m, total;
+    size_t x16, z32, z16, zlo, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, P, m, total;
     bool stream_path, decode_path;
     int max_tiles, BM, Hs, R;
 };
@@ -101,6 +101,7 @@ Layout plan(const Dims& d, int T) {
     lo.x16 = take(d.f32 ? 0 : (size_t)T * d.H * 2);
     lo.z32 = take((size_t)T * d.L * 4);
     lo.z16 = take(d.f32 ? 0 : (size_t)T * d.L * 2);
+    lo.zlo = take(d.f32 || T <= kStreamMaxT ? 0 : (size_t)T * d.L * 2);  // low bf16 half of z (router input)
     lo.logits = take((size_t)T * d.E * 4);
     lo.ids = take((size_t)T * d.k * 4);
     lo.w = take((size_t)T * d.k * 4);
@@ -325,11 +326,13 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     }
     uint16_t* z16 = static_cast<uint16_t*>(at(lo.z16));
     ev.begin(LMOE_STAGE_D);
-    if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s)) != hipSuccess)
+    uint16_t* zlo = T > kStreamMaxT ? static_cast<uint16_t*>(at(lo.zlo)) : nullptr;
+    if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s, zlo)) != hipSuccess)
         return hip_fail(e, "D projection");
     ev.end(LMOE_STAGE_D);
     ev.begin(LMOE_STAGE_ROUTER);
-    if ((e = launch_router_bf16(z32, static_cast<const uint16_t*>(wt->Wr), wt->br, T, d.E, d.L, logits, s)) != hipSuccess)
+    if ((e = launch_router_bf16(z32, static_cast<const uint16_t*>(wt->Wr), wt->br, T, d.E, d.L, logits, s, zlo ? z16 : nullptr,
+                                zlo)) != hipSuccess)
         return hip_fail(e, "router logits");
     ev.end(LMOE_STAGE_ROUTER);
     // top-k and permutation (one launch for small batches: the TOPK stage events bracket both)

@@ -326,9 +326,17 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
     const int e = threadIdx.x;
     int cnt = 0;
     if (e < E) {
-        for (int b = 0; b < nb; ++b) {
-            base[(size_t)b * E + e] = cnt;
-            cnt += hist[(size_t)b * E + e];
+        // per expert, the running count over token blocks; loads in batches of 32 in flight
+        for (int b0 = 0; b0 < nb; b0 += 32) {
+            int h[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) h[u] = hist[(size_t)min(b0 + u, nb - 1) * E + e];
+#pragma unroll
+            for (int u = 0; u < 32; ++u)
+                if (b0 + u < nb) {
+                    base[(size_t)(b0 + u) * E + e] = cnt;
+                    cnt += h[u];
+                }
         }
     }
     int total;
@@ -556,26 +564,26 @@ hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream
 }
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
-                            uint16_t* out16, hipStream_t s) {
+                            uint16_t* out16, hipStream_t s, uint16_t* out16lo) {
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1>(StreamProj{x, W, T, N, K, mode, out32, out16}, (int)cdiv(T, 16), N, s);
     if (LMOE_PIPE_PROJ) {
-        PipeProj<PipeL> p{{x, W, T, N, K, mode, out32, out16}};
+        PipeProj<PipeL> p{{x, W, T, N, K, mode, out32, out16, out16lo}};
         hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeProj<PipeL>>), dim3(cdiv(N, PipeL::kBN), cdiv(T, PipeL::kBM)),
                            dim3(256), 0, s, p);
         return last();
     }
-    TileProj<TileL> p{x, W, T, N, K, mode, out32, out16};
+    TileProj<TileL> p{x, W, T, N, K, mode, out32, out16, out16lo};
     hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileProj<TileL>>), dim3(cdiv(N, TileL::kBN), cdiv(T, TileL::kBM)),
                        dim3(256), 0, s, p);
     return last();
 }
 
 hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
-                              hipStream_t s) {
+                              hipStream_t s, const uint16_t* zhi, const uint16_t* zlo) {
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1>(StreamRouter{z, Wr, br, T, E, L, logits}, (int)cdiv(T, 16), E, s);
-    TileRouter<TileL> p{z, Wr, br, T, E, L, logits};
+    TileRouter<TileL> p{z, Wr, br, T, E, L, logits, zhi, zlo};
     hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileRouter<TileL>>), dim3(cdiv(E, TileL::kBN), cdiv(T, TileL::kBM)),
                        dim3(256), 0, s, p);
     return last();

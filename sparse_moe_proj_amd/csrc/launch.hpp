@@ -41,11 +41,13 @@ constexpr int kStreamMaxT = 16;
 hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream_t s);
 
 // mode 0: out32 = xW^T and out16 = bf16(out32); 1: out16 = bf16(xW^T); 2: out32 += xW^T
+// out16lo (mode 0, T > kStreamMaxT, optional): also write the low bf16 half of the output.
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
-                            uint16_t* out16, hipStream_t s);
+                            uint16_t* out16, hipStream_t s, uint16_t* out16lo = nullptr);
 
+// zhi/zlo (T > kStreamMaxT, optional): the bf16 halves of z written by the D projection.
 hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
-                              hipStream_t s);
+                              hipStream_t s, const uint16_t* zhi = nullptr, const uint16_t* zlo = nullptr);
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 

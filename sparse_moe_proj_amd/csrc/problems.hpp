@@ -58,6 +58,7 @@ struct TileProj {
     int M, N, K, mode;
     float* out32;
     uint16_t* out16;
+    uint16_t* out16lo;  // mode 0, optional: bf16(v - bf16(v)), the low half of the router input
     struct Ctx { int m0, n0; };
     typedef const uint16_t* RowA;
     typedef const uint16_t* RowB;
@@ -84,8 +85,11 @@ struct TileProj {
                         const float v = acc[i][j][r];
                         const size_t o = (size_t)m * N + n;
                         if (mode == 0) {
+                            uint32_t hi, lo;
+                            split_hi_lo(v, hi, lo);
                             out32[o] = v;
-                            out16[o] = (uint16_t)f2bf(v);
+                            out16[o] = (uint16_t)hi;
+                            if (out16lo) out16lo[o] = (uint16_t)lo;
                         } else if (mode == 1) {
                             out16[o] = (uint16_t)f2bf(v);
                         } else {
@@ -99,6 +103,7 @@ struct TileProj {
 };
 
 // Router logits from fp32 z: K doubled, first half multiplies hi(z), second half lo(z), same Wr.
+// The halves are read from zhi/zlo when given (written by the D projection), else split from z.
 template <class S>
 struct TileRouter {
     const float* z;      // [M][K] fp32
@@ -106,22 +111,26 @@ struct TileRouter {
     const float* bias;   // [E] or null
     int M, N, K;
     float* logits;       // [M][N]
+    const uint16_t* zhi;  // [M][K] bf16(z), or null
+    const uint16_t* zlo;  // [M][K] bf16(z - bf16(z)), or null
     struct Ctx { int m0, n0; };
-    typedef const float* RowA;
+    typedef int RowA;  // row index, -1 outside
     typedef const uint16_t* RowB;
     __device__ bool tile(int bx, int by, Ctx& c) const {
         c.m0 = bx * S::kBM;
         c.n0 = by * S::kBN;
         return c.m0 < M && c.n0 < N;
     }
-    __device__ RowA row_a(const Ctx& c, int r) const { return c.m0 + r < M ? z + (size_t)(c.m0 + r) * K : nullptr; }
+    __device__ RowA row_a(const Ctx& c, int r) const { return c.m0 + r < M ? c.m0 + r : -1; }
     __device__ RowB row_b(const Ctx& c, int r) const { return c.n0 + r < N ? W + (size_t)(c.n0 + r) * K : nullptr; }
     __device__ int k_tiles(const Ctx&) const { return 2 * (K / 64); }
     __device__ uint4 load_a(const Ctx&, RowA r, int kt, int lc) const {
-        if (!r) return zero4();
+        if (r < 0) return zero4();
         const int h = K / 64;
         const bool lo = kt >= h;
-        return f32x8_to_bf16_part(r + (lo ? kt - h : kt) * 64 + lc * 8, lo);
+        const size_t o = (size_t)r * K + (lo ? kt - h : kt) * 64 + lc * 8;
+        if (zhi) return ld16((lo ? zlo : zhi) + o);
+        return f32x8_to_bf16_part(z + o, lo);
     }
     __device__ uint4 load_b(const Ctx&, RowB r, int kt, int lc) const {
         if (!r) return zero4();
