@@ -105,18 +105,14 @@ __device__ __forceinline__ int frag_pos(int row, int u) {
         return row * 8 + (u ^ (row & 7));
 }
 
+// One output tile: the NS-stage copy pipeline over K, then the epilogue.  Every wave of the
+// workgroup calls it; the stage buffers must not be in use by any wave.
 template <class S, class P>
-__global__ __launch_bounds__(256) void pipe_gemm_kernel(const P p) {
+__device__ __forceinline__ void pipe_tile(const P& p, const typename P::Ctx& ctx, uint4* st0, uint4* st1, uint4* st2,
+                                          uint4* st3) {
     constexpr int NS = S::kNS;
     constexpr int LPS = S::kLoadsPerStage;
     static_assert(NS >= 2 && NS <= 4, "two to four stages");
-    __shared__ uint4 st0[S::kStageUnits], st1[S::kStageUnits];
-    __shared__ uint4 st2[NS >= 3 ? S::kStageUnits : 1], st3[NS == 4 ? S::kStageUnits : 1];
-
-    typename P::Ctx ctx;
-    int m_tile, n_tile;
-    xcd_tile(m_tile, n_tile);
-    if (!p.tile(m_tile, n_tile, ctx)) return;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -210,6 +206,40 @@ __global__ __launch_bounds__(256) void pipe_gemm_kernel(const P p) {
 #undef LMOE_PIPE_STEP
 
     p.template epilogue<S::kMB, S::kNB>(ctx, acc, wm * S::kWM, wn * S::kWN, lane);
+}
+
+// One tile per workgroup; grid (N tiles, M tiles upper bound), XCD-aware order.
+template <class S, class P>
+__global__ __launch_bounds__(256) void pipe_gemm_kernel(const P p) {
+    __shared__ uint4 st0[S::kStageUnits], st1[S::kStageUnits];
+    __shared__ uint4 st2[S::kNS >= 3 ? S::kStageUnits : 1], st3[S::kNS == 4 ? S::kStageUnits : 1];
+    typename P::Ctx ctx;
+    int m_tile, n_tile;
+    xcd_tile(m_tile, n_tile);
+    if (!p.tile(m_tile, n_tile, ctx)) return;
+    pipe_tile<S, P>(p, ctx, st0, st1, st2, st3);
+}
+
+// Persistent form: gridDim.x workgroups (about one per CU) walk the tiles that exist (the M-tile
+// count is read on the device).  The tiles are split into g = min(8, gridDim.x) equal contiguous
+// ranges, one per XCD (workgroups are handed to the XCDs round-robin), and a group's workgroups
+// take the tiles of its range in turn, so the N tiles of one M tile run close together on one
+// XCD.  Every tile of every range is taken by some workgroup.
+template <class S, class P>
+__global__ __launch_bounds__(256) void pipe_gemm_persistent(const P p, int n_tiles) {
+    __shared__ uint4 st0[S::kStageUnits], st1[S::kStageUnits];
+    __shared__ uint4 st2[S::kNS >= 3 ? S::kStageUnits : 1], st3[S::kNS == 4 ? S::kStageUnits : 1];
+    const int total = p.m_tiles() * n_tiles;
+    const int g = min(8, (int)gridDim.x);  // groups (XCDs) that have at least one workgroup
+    const int x = blockIdx.x % g, wi = blockIdx.x / g;
+    const int nwx = ((int)gridDim.x - x + g - 1) / g;  // workgroups in this group
+    const int lo = (int)((long)total * x / g), hi = (int)((long)total * (x + 1) / g);
+    for (int l = lo + wi; l < hi; l += nwx) {
+        typename P::Ctx ctx;
+        if (!p.tile(l / n_tiles, l % n_tiles, ctx)) continue;  // uniform over the workgroup
+        stage_barrier();  // every wave is done with the previous tile's stage buffers
+        pipe_tile<S, P>(p, ctx, st0, st1, st2, st3);
+    }
 }
 
 }  // namespace lmoe

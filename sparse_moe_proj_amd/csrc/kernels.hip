@@ -530,6 +530,9 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_PIPE_PROJ
 #define LMOE_PIPE_PROJ 0
 #endif
+#ifndef LMOE_PIPE_PERSIST
+#define LMOE_PIPE_PERSIST 1
+#endif
 #ifndef LMOE_STREAM_GRID
 #define LMOE_STREAM_GRID 2048
 #endif
@@ -723,6 +726,22 @@ hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     return hipSuccess;
 }
 
+// Workgroups of `kernel` that fit on the current device at once (cached per kernel and device).
+template <class K>
+int resident_blocks(K kernel, int threads) {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+        cache[dev] = per_cu * cus;
+    }
+    return cache[dev];
+}
+
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {
     const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E};
     if (a.decode_path)
@@ -734,15 +753,27 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
     if (LMOE_PIPE) {
         ev.begin(kStageUp);
         PipeUp<PipeL> up{{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H}};
-        hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeUp<PipeL>>), dim3(cdiv(Fmax, PipeL::kBN / 2), a.max_tiles),
-                           dim3(256), 0, s, up);
+        const int nn_up = (int)cdiv(Fmax, PipeL::kBN / 2);
+        if (LMOE_PIPE_PERSIST) {
+            auto k = pipe_gemm_persistent<PipeL, PipeUp<PipeL>>;
+            hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, 256), (long)a.max_tiles * nn_up)), dim3(256), 0,
+                               s, up, nn_up);
+        } else {
+            hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeUp<PipeL>>), dim3(nn_up, a.max_tiles), dim3(256), 0, s, up);
+        }
         hipError_t err = last();
         if (err != hipSuccess) return err;
         ev.end(kStageUp);
         ev.begin(kStageDown);
         PipeDown<PipeL> dn{{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y}};
-        hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeDown<PipeL>>), dim3(cdiv(a.L, PipeL::kBN), a.max_tiles),
-                           dim3(256), 0, s, dn);
+        const int nn_dn = (int)cdiv(a.L, PipeL::kBN);
+        if (LMOE_PIPE_PERSIST) {
+            auto k = pipe_gemm_persistent<PipeL, PipeDown<PipeL>>;
+            hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, 256), (long)a.max_tiles * nn_dn)), dim3(256), 0,
+                               s, dn, nn_dn);
+        } else {
+            hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeDown<PipeL>>), dim3(nn_dn, a.max_tiles), dim3(256), 0, s, dn);
+        }
         if ((err = last()) != hipSuccess) return err;
         ev.end(kStageDown);
         return hipSuccess;

@@ -615,6 +615,7 @@ template <class S>
 struct PipeProj : TileProj<S> {
     using B = TileProj<S>;
     static constexpr bool kAPacked = false, kBPacked = false;
+    __device__ int m_tiles() const { return (B::M + S::kBM - 1) / S::kBM; }
     __device__ int k_stages(const typename B::Ctx&) const { return B::K / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
         return reinterpret_cast<const uint8_t*>(B::x + (size_t)c.m0 * B::K);
@@ -636,6 +637,7 @@ template <class S>
 struct PipeUp : TileUp<S> {
     using B = TileUp<S>;
     static constexpr bool kAPacked = false, kBPacked = true;
+    __device__ int m_tiles() const { return *B::seg.ntiles; }
     __device__ int k_stages(const typename B::Ctx&) const { return B::L / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx&) const { return reinterpret_cast<const uint8_t*>(B::z16); }
     __device__ const uint8_t* b_base(const typename B::Ctx& c) const { return reinterpret_cast<const uint8_t*>(c.g); }
@@ -658,6 +660,7 @@ template <class S>
 struct PipeDown : TileDown<S> {
     using B = TileDown<S>;
     static constexpr bool kAPacked = false, kBPacked = true;
+    __device__ int m_tiles() const { return *B::seg.ntiles; }
     __device__ int k_stages(const typename B::Ctx& c) const { return c.F / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
         return reinterpret_cast<const uint8_t*>(B::H + (size_t)c.row0 * B::Hs);
