@@ -105,42 +105,62 @@ __device__ __forceinline__ int frag_pos(int row, int u) {
         return row * 8 + (u ^ (row & 7));
 }
 
-// One output tile: the NS-stage copy pipeline over K, then the epilogue.  Every wave of the
-// workgroup calls it; the stage buffers must not be in use by any wave.
+// Copy sources of one tile for this lane: a uniform base per operand and per-lane 32-bit byte
+// offsets of the stage-0 source of each copy instruction this wave issues.
+template <class S>
+struct PipeCopies {
+    const uint8_t* abase;
+    const uint8_t* bbase;
+    uint32_t as[S::kAIW], bs[S::kBIW];
+};
+
 template <class S, class P>
-__device__ __forceinline__ void pipe_tile(const P& p, const typename P::Ctx& ctx, uint4* st0, uint4* st1, uint4* st2,
-                                          uint4* st3) {
+__device__ __forceinline__ PipeCopies<S> pipe_copies(const P& p, const typename P::Ctx& ctx, int wave, int lane) {
+    PipeCopies<S> c;
+    c.abase = p.a_base(ctx);
+    c.bbase = p.b_base(ctx);
+#pragma unroll
+    for (int i = 0; i < S::kAIW; ++i) c.as[i] = p.src_a(ctx, wave * S::kAIW + i, lane);
+#pragma unroll
+    for (int i = 0; i < S::kBIW; ++i) c.bs[i] = p.src_b(ctx, wave * S::kBIW + i, lane);
+    return c;
+}
+
+// Stage kt of the tile into stage buffer buf (A block of BM rows, then B block of BN rows).
+template <class S, class P>
+__device__ __forceinline__ void pipe_issue(const PipeCopies<S>& c, uint4* buf, int kt, int wave) {
+    constexpr int kAStep = P::kAPacked ? kPackedStep : kRowMajorStep;
+    constexpr int kBStep = P::kBPacked ? kPackedStep : kRowMajorStep;
+#pragma unroll
+    for (int i = 0; i < S::kAIW; ++i)
+        lds_copy16(c.abase + (c.as[i] + (uint32_t)(kt * kAStep)), buf + (wave * S::kAIW + i) * 64);
+#pragma unroll
+    for (int i = 0; i < S::kBIW; ++i)
+        lds_copy16(c.bbase + (c.bs[i] + (uint32_t)(kt * kBStep)), buf + S::kBM * 8 + (wave * S::kBIW + i) * 64);
+}
+
+// Stages 0 .. NS-2 of a tile with nk stages into the first stage buffers.
+template <class S, class P>
+__device__ __forceinline__ void pipe_prologue(const PipeCopies<S>& c, int nk, uint4* st0, uint4* st1, uint4* st2,
+                                              int wave) {
+    if (nk > 0) pipe_issue<S, P>(c, st0, 0, wave);
+    if constexpr (S::kNS >= 3)
+        if (nk > 1) pipe_issue<S, P>(c, st1, 1, wave);
+    if constexpr (S::kNS == 4)
+        if (nk > 2) pipe_issue<S, P>(c, st2, 2, wave);
+}
+
+// The K loop of one tile whose prologue stages are in flight: for stage kt + s, wait for this
+// wave's copies of it, barrier (every wave's copies landed and every wave is done with the
+// previous stage), refill the buffer the previous stage used with stage kt + s + NS - 1,
+// multiply stage kt + s.  Accumulates into acc (zeroed here).
+template <class S, class P>
+__device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x16 (&acc)[S::kMB][S::kNB],
+                                            uint4* st0, uint4* st1, uint4* st2, uint4* st3, int wave, int lane) {
     constexpr int NS = S::kNS;
     constexpr int LPS = S::kLoadsPerStage;
     static_assert(NS >= 2 && NS <= 4, "two to four stages");
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int nk = p.k_stages(ctx);
-
-    constexpr int kAStep = P::kAPacked ? kPackedStep : kRowMajorStep;
-    constexpr int kBStep = P::kBPacked ? kPackedStep : kRowMajorStep;
-    // copy sources: a uniform base per operand and per-lane 32-bit byte offsets
-    const uint8_t* abase = p.a_base(ctx);
-    const uint8_t* bbase = p.b_base(ctx);
-    uint32_t as[S::kAIW], bs[S::kBIW];
-#pragma unroll
-    for (int i = 0; i < S::kAIW; ++i) as[i] = p.src_a(ctx, wave * S::kAIW + i, lane);
-#pragma unroll
-    for (int i = 0; i < S::kBIW; ++i) bs[i] = p.src_b(ctx, wave * S::kBIW + i, lane);
-
-    // stage buffer: A block (BM rows) then B block (BN rows)
-    auto issue = [&](uint4* buf, int kt) {
-#pragma unroll
-        for (int i = 0; i < S::kAIW; ++i)
-            lds_copy16(abase + (as[i] + (uint32_t)(kt * kAStep)), buf + (wave * S::kAIW + i) * 64);
-#pragma unroll
-        for (int i = 0; i < S::kBIW; ++i)
-            lds_copy16(bbase + (bs[i] + (uint32_t)(kt * kBStep)), buf + S::kBM * 8 + (wave * S::kBIW + i) * 64);
-    };
-
-    f32x16 acc[S::kMB][S::kNB];
 #pragma unroll
     for (int i = 0; i < S::kMB; ++i)
 #pragma unroll
@@ -167,22 +187,12 @@ __device__ __forceinline__ void pipe_tile(const P& p, const typename P::Ctx& ctx
         }
     };
 
-    // prologue: stages 0 .. NS-2 in flight
-    if (nk > 0) issue(st0, 0);
-    if constexpr (NS >= 3)
-        if (nk > 1) issue(st1, 1);
-    if constexpr (NS == 4)
-        if (nk > 2) issue(st2, 2);
-
-    // step for stage kt + s: wait for this wave's copies of it, barrier (every wave's copies
-    // landed and every wave is done with the previous stage), refill the buffer the previous
-    // stage used with stage kt + s + NS - 1, multiply stage kt + s
-#define LMOE_PIPE_STEP(S_, CUR_, NEXT_)                              \
-    if (kt + S_ < nk) {                                              \
-        wait_stage<LPS, NS>(min(nk - 1 - (kt + S_), NS - 2));        \
-        stage_barrier();                                             \
-        if (kt + S_ + NS - 1 < nk) issue(NEXT_, kt + S_ + NS - 1);   \
-        compute(CUR_);                                               \
+#define LMOE_PIPE_STEP(S_, CUR_, NEXT_)                                             \
+    if (kt + S_ < nk) {                                                             \
+        wait_stage<LPS, NS>(min(nk - 1 - (kt + S_), NS - 2));                       \
+        stage_barrier();                                                            \
+        if (kt + S_ + NS - 1 < nk) pipe_issue<S, P>(c, NEXT_, kt + S_ + NS - 1, wave); \
+        compute(CUR_);                                                              \
     }
     if constexpr (NS == 4) {
         for (int kt = 0; kt < nk; kt += 4) {
@@ -204,8 +214,6 @@ __device__ __forceinline__ void pipe_tile(const P& p, const typename P::Ctx& ctx
         }
     }
 #undef LMOE_PIPE_STEP
-
-    p.template epilogue<S::kMB, S::kNB>(ctx, acc, wm * S::kWM, wn * S::kWN, lane);
 }
 
 // One tile per workgroup; grid (N tiles, M tiles upper bound), XCD-aware order.
@@ -217,7 +225,15 @@ __global__ __launch_bounds__(256) void pipe_gemm_kernel(const P p) {
     int m_tile, n_tile;
     xcd_tile(m_tile, n_tile);
     if (!p.tile(m_tile, n_tile, ctx)) return;
-    pipe_tile<S, P>(p, ctx, st0, st1, st2, st3);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rb = (wave >> 1) * S::kWM, cb = (wave & 1) * S::kWN;
+    const int nk = p.k_stages(ctx);
+    const PipeCopies<S> c = pipe_copies<S>(p, ctx, wave, lane);
+    pipe_prologue<S, P>(c, nk, st0, st1, st2, wave);
+    f32x16 acc[S::kMB][S::kNB];
+    pipe_k_loop<S, P>(c, nk, acc, st0, st1, st2, st3, wave, lane);
+    const auto prep = p.template prep<S::kMB>(ctx, rb, lane);
+    p.template store<S::kMB, S::kNB>(ctx, acc, prep, rb, cb, lane);
 }
 
 // Persistent form: gridDim.x workgroups (about one per CU) walk the tiles that exist (the M-tile
@@ -225,6 +241,12 @@ __global__ __launch_bounds__(256) void pipe_gemm_kernel(const P p) {
 // ranges, one per XCD (workgroups are handed to the XCDs round-robin), and a group's workgroups
 // take the tiles of its range in turn, so the N tiles of one M tile run close together on one
 // XCD.  Every tile of every range is taken by some workgroup.
+//
+// Tiles overlap: once a tile's K loop is done, the workgroup reads what the epilogue needs
+// (P::prep) and the next tile's copy sources, issues the next tile's first stages, and only then
+// stores the finished tile, so the stores and the next tile's first copies are in flight
+// together.  No global load is issued after the prefetch until the next K loop (a wait for such
+// a load would also wait for the prefetch).
 template <class S, class P>
 __global__ __launch_bounds__(256) void pipe_gemm_persistent(const P p, int n_tiles) {
     __shared__ uint4 st0[S::kStageUnits], st1[S::kStageUnits];
@@ -234,11 +256,42 @@ __global__ __launch_bounds__(256) void pipe_gemm_persistent(const P p, int n_til
     const int x = blockIdx.x % g, wi = blockIdx.x / g;
     const int nwx = ((int)gridDim.x - x + g - 1) / g;  // workgroups in this group
     const int lo = (int)((long)total * x / g), hi = (int)((long)total * (x + 1) / g);
-    for (int l = lo + wi; l < hi; l += nwx) {
-        typename P::Ctx ctx;
-        if (!p.tile(l / n_tiles, l % n_tiles, ctx)) continue;  // uniform over the workgroup
-        stage_barrier();  // every wave is done with the previous tile's stage buffers
-        pipe_tile<S, P>(p, ctx, st0, st1, st2, st3);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rb = (wave >> 1) * S::kWM, cb = (wave & 1) * S::kWN;
+
+    // the next valid tile at or after l (uniform over the workgroup); false when none is left
+    auto next_tile = [&](int& l, typename P::Ctx& ctx) {
+        for (; l < hi; l += nwx)
+            if (p.tile(l / n_tiles, l % n_tiles, ctx)) return true;
+        return false;
+    };
+    int l = lo + wi;
+    typename P::Ctx ctx;
+    if (!next_tile(l, ctx)) return;
+    int nk = p.k_stages(ctx);
+    PipeCopies<S> c = pipe_copies<S>(p, ctx, wave, lane);
+    pipe_prologue<S, P>(c, nk, st0, st1, st2, wave);
+    f32x16 acc[S::kMB][S::kNB];
+    while (true) {
+        pipe_k_loop<S, P>(c, nk, acc, st0, st1, st2, st3, wave, lane);
+        const auto prep = p.template prep<S::kMB>(ctx, rb, lane);
+        int ln = l + nwx;
+        typename P::Ctx nctx;
+        const bool more = next_tile(ln, nctx);
+        int nnk = 0;
+        PipeCopies<S> nc;
+        if (more) {
+            nnk = p.k_stages(nctx);
+            nc = pipe_copies<S>(p, nctx, wave, lane);
+        }
+        stage_barrier();  // every wave is done with this tile's stage buffers
+        if (more) pipe_prologue<S, P>(nc, nnk, st0, st1, st2, wave);
+        p.template store<S::kMB, S::kNB>(ctx, acc, prep, rb, cb, lane);
+        if (!more) break;
+        l = ln;
+        ctx = nctx;
+        nk = nnk;
+        c = nc;
     }
 }
 

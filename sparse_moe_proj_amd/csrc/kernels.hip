@@ -561,6 +561,22 @@ hipError_t launch_stream(const P& p, int max_tiles, int nrows_max, hipStream_t s
 }
 }  // namespace
 
+// Workgroups of `kernel` that fit on the current device at once (cached per kernel and device).
+template <class K>
+int resident_blocks(K kernel, int threads) {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+        cache[dev] = per_cu * cus;
+    }
+    return cache[dev];
+}
+
 hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream_t s) {
     hipLaunchKernelGGL(rmsnorm_bf16_kernel, dim3(T), dim3(256), 0, s, h, H, 1e-6f, x16);
     return last();
@@ -572,8 +588,10 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
         return launch_stream<kPW, kPKS, 1>(StreamProj{x, W, T, N, K, mode, out32, out16}, (int)cdiv(T, 16), N, s);
     if (LMOE_PIPE_PROJ) {
         PipeProj<PipeL> p{{x, W, T, N, K, mode, out32, out16, out16lo}};
-        hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeProj<PipeL>>), dim3(cdiv(N, PipeL::kBN), cdiv(T, PipeL::kBM)),
-                           dim3(256), 0, s, p);
+        const int nn = (int)cdiv(N, PipeL::kBN);
+        auto k = pipe_gemm_persistent<PipeL, PipeProj<PipeL>>;
+        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, 256), (long)cdiv(T, PipeL::kBM) * nn)), dim3(256), 0,
+                           s, p, nn);
         return last();
     }
     TileProj<TileL> p{x, W, T, N, K, mode, out32, out16, out16lo};
@@ -724,22 +742,6 @@ hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     if (err != hipSuccess) return err;
     ev.end(kStageDown);
     return hipSuccess;
-}
-
-// Workgroups of `kernel` that fit on the current device at once (cached per kernel and device).
-template <class K>
-int resident_blocks(K kernel, int threads) {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cache[dev]) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
-            per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-        cache[dev] = per_cu * cus;
-    }
-    return cache[dev];
 }
 
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {

@@ -631,6 +631,14 @@ struct PipeProj : TileProj<S> {
         const int r = min(rowmajor_row(i, lane), B::N - 1 - c.n0);
         return rowmajor_off((uint32_t)r * B::K * 2, i, lane);
     }
+    struct Prep {};
+    template <int MB>
+    __device__ Prep prep(const typename B::Ctx&, int, int) const { return {}; }
+    template <int MB, int NB>
+    __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
+                                          int lane) const {
+        B::template epilogue<MB, NB>(c, acc, rb, cb, lane);
+    }
 };
 
 template <class S>
@@ -654,6 +662,14 @@ struct PipeUp : TileUp<S> {
         const uint32_t mat = rr >= B::kHalf ? (uint32_t)c.F * B::L * 2 : 0u;  // up follows gate
         return mat + packed_off(nb, i, B::L, lane);
     }
+    struct Prep {};
+    template <int MB>
+    __device__ Prep prep(const typename B::Ctx&, int, int) const { return {}; }
+    template <int MB, int NB>
+    __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
+                                          int lane) const {
+        B::template epilogue<MB, NB>(c, acc, rb, cb, lane);
+    }
 };
 
 template <class S>
@@ -673,6 +689,40 @@ struct PipeDown : TileDown<S> {
     __device__ uint32_t src_b(const typename B::Ctx& c, int i, int lane) const {
         const int nb = min(c.n0 + (i >> 1) * 16, B::L - 16) >> 4;
         return packed_off(nb, i, c.F, lane);
+    }
+    // destination row of every accumulator row this lane holds (-1: none), read before the store
+    template <int MB>
+    struct PrepT {
+        int drow[MB][16];
+    };
+    template <int MB>
+    __device__ __forceinline__ PrepT<MB> prep(const typename B::Ctx& c, int rb, int lane) const {
+        PrepT<MB> q;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = rb + i * 32 + frag32_row(r, lane);
+                q.drow[i][r] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
+            }
+        return q;
+    }
+    template <int MB, int NB>
+    __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], const PrepT<MB>& q, int rb,
+                                          int cb, int lane) const {
+        static_for<MB>([&](auto i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int drow = q.drow[i][r];  // a dropped slot (-1) owns no output row
+                if (drow >= 0) {
+                    const size_t dst = (size_t)drow * B::L;
+                    static_for<NB>([&](auto j) {
+                        const int n = c.n0 + cb + j * 32 + frag32_col(lane);
+                        if (n < B::L) B::Y[dst + n] = (uint16_t)f2bf(acc[i][j][r]);
+                    });
+                }
+            }
+        });
     }
 };
 
