@@ -105,6 +105,32 @@ __device__ __forceinline__ int frag_pos(int row, int u) {
         return row * 8 + (u ^ (row & 7));
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint4*)p;
+}
+
+// Fragment reads of one k step: MB + NB ds_read_b128 in one block that also waits for them.
+// The copies into other stage buffers are still in flight at this point; keeping these reads out
+// of the compiler's view stops it from waiting for those copies (it cannot tell the buffers
+// apart across the K loop's back edge).  Outputs are early-clobber, so no register of an address
+// still to be used receives data, and the block returns only once every read has landed.
+template <int MB, int NB>
+__device__ __forceinline__ void lds_read_frags(const uint32_t (&aa)[MB], const uint32_t (&ba)[NB], uint4 (&af)[MB],
+                                               uint4 (&bf)[NB]) {
+    static_assert(MB == 2 && NB == 4, "read block written for a 64 x 128 wave tile");
+    __asm__ volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b128 %2, %8\n\t"
+        "ds_read_b128 %3, %9\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
+        : "v"(aa[0]), "v"(aa[1]), "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]));
+}
+
 // Copy sources of one tile for this lane: a uniform base per operand and per-lane 32-bit byte
 // offsets of the stage-0 source of each copy instruction this wave issues.
 template <class S>
@@ -169,17 +195,18 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
     const int fr = lane & 31;
     const int fq = lane >> 5;
     auto compute = [&](const uint4* buf) {
-        const uint4* A = buf;
-        const uint4* B = buf + S::kBM * 8;
+        const uint32_t A = lds_addr(buf);
+        const uint32_t B = A + S::kBM * 8 * 16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            if constexpr (S::kMB * S::kNB >= 16) __builtin_amdgcn_sched_barrier(0);  // bound live fragments
             const int u = 2 * ks + fq;
+            uint32_t aa[S::kMB], ba[S::kNB];
+#pragma unroll
+            for (int i = 0; i < S::kMB; ++i) aa[i] = A + 16 * frag_pos<P::kAPacked>(wm * S::kWM + i * 32 + fr, u);
+#pragma unroll
+            for (int j = 0; j < S::kNB; ++j) ba[j] = B + 16 * frag_pos<P::kBPacked>(wn * S::kWN + j * 32 + fr, u);
             uint4 af[S::kMB], bfv[S::kNB];
-#pragma unroll
-            for (int i = 0; i < S::kMB; ++i) af[i] = A[frag_pos<P::kAPacked>(wm * S::kWM + i * 32 + fr, u)];
-#pragma unroll
-            for (int j = 0; j < S::kNB; ++j) bfv[j] = B[frag_pos<P::kBPacked>(wn * S::kWN + j * 32 + fr, u)];
+            lds_read_frags<S::kMB, S::kNB>(aa, ba, af, bfv);
 #pragma unroll
             for (int i = 0; i < S::kMB; ++i)
 #pragma unroll
