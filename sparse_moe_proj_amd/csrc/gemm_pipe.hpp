@@ -118,17 +118,53 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
 template <int MB, int NB>
 __device__ __forceinline__ void lds_read_frags(const uint32_t (&aa)[MB], const uint32_t (&ba)[NB], uint4 (&af)[MB],
                                                uint4 (&bf)[NB]) {
-    static_assert(MB == 2 && NB == 4, "read block written for a 64 x 128 wave tile");
-    __asm__ volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %7\n\t"
-        "ds_read_b128 %2, %8\n\t"
-        "ds_read_b128 %3, %9\n\t"
-        "ds_read_b128 %4, %10\n\t"
-        "ds_read_b128 %5, %11\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
-        : "v"(aa[0]), "v"(aa[1]), "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]));
+    if constexpr (MB == 2 && NB == 4) {
+        __asm__ volatile(
+            "ds_read_b128 %0, %6\n\t"
+            "ds_read_b128 %1, %7\n\t"
+            "ds_read_b128 %2, %8\n\t"
+            "ds_read_b128 %3, %9\n\t"
+            "ds_read_b128 %4, %10\n\t"
+            "ds_read_b128 %5, %11\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
+            : "v"(aa[0]), "v"(aa[1]), "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]));
+    } else if constexpr (MB == 4 && NB == 2) {
+        __asm__ volatile(
+            "ds_read_b128 %0, %6\n\t"
+            "ds_read_b128 %1, %7\n\t"
+            "ds_read_b128 %2, %8\n\t"
+            "ds_read_b128 %3, %9\n\t"
+            "ds_read_b128 %4, %10\n\t"
+            "ds_read_b128 %5, %11\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1])
+            : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]), "v"(ba[0]), "v"(ba[1]));
+    } else if constexpr (MB == 2 && NB == 2) {
+        __asm__ volatile(
+            "ds_read_b128 %0, %4\n\t"
+            "ds_read_b128 %1, %5\n\t"
+            "ds_read_b128 %2, %6\n\t"
+            "ds_read_b128 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1])
+            : "v"(aa[0]), "v"(aa[1]), "v"(ba[0]), "v"(ba[1]));
+    } else {
+        static_assert(MB == 4 && NB == 4, "wave tiles of 64 or 128 rows and columns");
+        __asm__ volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %9\n\t"
+            "ds_read_b128 %2, %10\n\t"
+            "ds_read_b128 %3, %11\n\t"
+            "ds_read_b128 %4, %12\n\t"
+            "ds_read_b128 %5, %13\n\t"
+            "ds_read_b128 %6, %14\n\t"
+            "ds_read_b128 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]),
+              "=&v"(bf[3])
+            : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]), "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]));
+    }
 }
 
 // Copy sources of one tile for this lane: a uniform base per operand and per-lane 32-bit byte
