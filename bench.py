@@ -224,7 +224,7 @@ def roofline_hbm(counts, up_ms, traffic=None):
 
 def roofline_mfma(counts, up_ms):
     achieved = counts["up_flops"] / (up_ms / 1e3) / 1e12
-    return {"bound": "mfma", "kernel": "expert gate/up (tile_gemm TileUp)", "achieved": round(achieved, 1),
+    return {"bound": "mfma", "kernel": "expert gate/up (pipe_gemm_persistent PipeUp)", "achieved": round(achieved, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None, "flops_per_launch": counts["up_flops"], "avg_launch_us": round(up_ms * 1e3, 2)}
 
