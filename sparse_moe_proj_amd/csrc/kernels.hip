@@ -509,6 +509,9 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_CHUNK
 #define LMOE_CHUNK 4
 #endif
+#ifndef LMOE_PROJ_CHUNK
+#define LMOE_PROJ_CHUNK 1
+#endif
 #ifndef LMOE_DECODE_KSU
 #define LMOE_DECODE_KSU 1
 #endif
@@ -540,6 +543,7 @@ constexpr int kPW = LMOE_PROJ_WAVES, kPKS = LMOE_PROJ_KS;
 constexpr int kUW = LMOE_UP_WAVES, kUKS = LMOE_UP_KS;
 constexpr int kDW = LMOE_DOWN_WAVES, kDKS = LMOE_DOWN_KS;
 constexpr int kChunk = LMOE_CHUNK;
+constexpr int kProjChunk = LMOE_PROJ_CHUNK;
 // Tile shape of the many-token GEMMs (projections, router, experts): 4 waves of (M/2) x (N/2).
 using TileL = TileShape<LMOE_TILE_M, LMOE_TILE_N, 2, 2>;
 // Pipelined (global -> LDS copies, LMOE_PIPE_NS stages) GEMM for the experts (and, with
@@ -550,9 +554,9 @@ using TileL = TileShape<LMOE_TILE_M, LMOE_TILE_N, 2, 2>;
 using PipeL = PipeShape<LMOE_PIPE_M, LMOE_PIPE_N, LMOE_PIPE_NS>;
 
 // Persistent launch: at most LMOE_STREAM_GRID workgroups walk max_tiles x row-group items.
-template <int W, int KS, int NMAT, class P>
+template <int W, int KS, int NMAT, class P, int CH0 = kChunk>
 hipError_t launch_stream(const P& p, int max_tiles, int nrows_max, hipStream_t s) {
-    constexpr int CH = P::kSPL == 1 ? kChunk : 1;
+    constexpr int CH = P::kSPL == 1 ? CH0 : 1;
     const int rgroups = (int)cdiv(nrows_max, 16 * (W / KS));
     const long items = (long)max_tiles * rgroups;
     const dim3 grid((unsigned)std::min<long>(items, LMOE_STREAM_GRID)), block(64 * W);
@@ -585,7 +589,8 @@ hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                             uint16_t* out16, hipStream_t s, uint16_t* out16lo) {
     if (T <= kStreamMaxT)
-        return launch_stream<kPW, kPKS, 1>(StreamProj{x, W, T, N, K, mode, out32, out16}, (int)cdiv(T, 16), N, s);
+        return launch_stream<kPW, kPKS, 1, StreamProj, kProjChunk>(StreamProj{x, W, T, N, K, mode, out32, out16},
+                                                                   (int)cdiv(T, 16), N, s);
     if (LMOE_PIPE_PROJ) {
         PipeProj<PipeL> p{{x, W, T, N, K, mode, out32, out16, out16lo}};
         const int nn = (int)cdiv(N, PipeL::kBN);
@@ -603,7 +608,8 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
 hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
                               hipStream_t s, const uint16_t* zhi, const uint16_t* zlo) {
     if (T <= kStreamMaxT)
-        return launch_stream<kPW, kPKS, 1>(StreamRouter{z, Wr, br, T, E, L, logits}, (int)cdiv(T, 16), E, s);
+        return launch_stream<kPW, kPKS, 1, StreamRouter, kProjChunk>(StreamRouter{z, Wr, br, T, E, L, logits},
+                                                                     (int)cdiv(T, 16), E, s);
     TileRouter<TileL> p{z, Wr, br, T, E, L, logits, zhi, zlo};
     hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileRouter<TileL>>), dim3(cdiv(E, TileL::kBN), cdiv(T, TileL::kBM)),
                        dim3(256), 0, s, p);
