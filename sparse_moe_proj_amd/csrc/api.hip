@@ -76,7 +76,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t x16, z32, z16, zlo, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, P, m, total;
+    size_t x16, z32, z16, zlo, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, mpart, m, total;
     bool stream_path, decode_path;
     int max_tiles, BM, Hs, R;
 };
@@ -86,7 +86,7 @@ Layout plan(const Dims& d, int T) {
     const size_t act = d.f32 ? 4 : 2;
     const int has_shared = d.Fs > 0;
     lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx);
-    lo.decode_path = !d.f32 && T <= kStreamMaxT && decode_fits(d.F, d.Fs, d.mx);
+    lo.decode_path = !d.f32 && decode_fits(T, d.L, d.F, d.Fs);
     lo.BM = expert_tile_rows(lo.stream_path);
     lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path);
     lo.Hs = std::max(d.F, d.Fs);
@@ -112,10 +112,10 @@ Layout plan(const Dims& d, int T) {
     lo.base = take(nb * d.E * 4);
     lo.tiles = take((size_t)lo.max_tiles * sizeof(Tile));
     lo.ntiles = take(4);
-    lo.H = take(lo.decode_path ? 0 : (size_t)lo.R * lo.Hs * act);
+    lo.H = take((size_t)lo.R * lo.Hs * act);
     lo.Y = take(lo.decode_path ? 0 : (size_t)lo.R * d.L * (d.f32 ? 4 : 2));
-    lo.P = take(lo.decode_path ? (size_t)lo.R * decode_slices(d.F, d.Fs, d.mx) * d.L * 4 : 0);
-    lo.m = take((size_t)T * d.L * act);
+    lo.mpart = take(lo.decode_path ? (size_t)decode_groups() * T * d.L * 4 : 0);
+    lo.m = take(lo.decode_path ? 0 : (size_t)T * d.L * act);
     lo.total = o;
     return lo;
 }
@@ -341,20 +341,28 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
                                  has_shared, s)) != hipSuccess)
         return hip_fail(e, "top-k / permute");
     ev.end(LMOE_STAGE_TOPK);
-    uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
+    float* mpart = static_cast<float*>(at(lo.mpart));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
                  wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
-                 lo.decode_path, d.mx, static_cast<float*>(at(lo.P)), wts, m16};
+                 lo.decode_path, d.mx, mpart, wts};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
-    if (!lo.decode_path) {  // the small-batch expert path has its own merge launch
-        ev.begin(LMOE_STAGE_COMBINE);
-        if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, true, m16, s)) != hipSuccess)
-            return hip_fail(e, "combine");
-        ev.end(LMOE_STAGE_COMBINE);
+    const int umode = o.residual ? 2 : 1;
+    const uint16_t* U = static_cast<const uint16_t*>(wt->U);
+    if (lo.decode_path) {  // the down launch merged the rows into partials; U sums them
+        ev.begin(LMOE_STAGE_U);
+        if ((e = launch_proj_partials(mpart, decode_groups(), U, T, d.H, d.L, umode, static_cast<float*>(y),
+                                      static_cast<uint16_t*>(y), s)) != hipSuccess)
+            return hip_fail(e, "U projection");
+        ev.end(LMOE_STAGE_U);
+        return ev.err != hipSuccess ? hip_fail(ev.err, "stage event record") : LMOE_OK;
     }
+    uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
+    ev.begin(LMOE_STAGE_COMBINE);
+    if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, true, m16, s)) != hipSuccess) return hip_fail(e, "combine");
+    ev.end(LMOE_STAGE_COMBINE);
     ev.begin(LMOE_STAGE_U);
-    if ((e = launch_proj_bf16(m16, static_cast<const uint16_t*>(wt->U), T, d.H, d.L, o.residual ? 2 : 1,
-                              static_cast<float*>(y), static_cast<uint16_t*>(y), s)) != hipSuccess)
+    if ((e = launch_proj_bf16(m16, U, T, d.H, d.L, umode, static_cast<float*>(y), static_cast<uint16_t*>(y), s)) !=
+        hipSuccess)
         return hip_fail(e, "U projection");
     ev.end(LMOE_STAGE_U);
     return ev.err != hipSuccess ? hip_fail(ev.err, "stage event record") : LMOE_OK;

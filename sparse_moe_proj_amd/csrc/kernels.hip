@@ -7,6 +7,7 @@
 #include "gemm_tile.hpp"
 #include "launch.hpp"
 #include "problems.hpp"
+#include "small_proj.hpp"
 
 namespace lmoe {
 
@@ -71,18 +72,21 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* __restri
 
 // ==============================================================================================
 // top-k + softmax over the kept logits, one wave per token.  Lane l holds the logits of ids
-// l, l+64, ... (NV per lane, E <= 64*NV) as order-preserving 32-bit keys.  A most-significant-
-// bit-first radix select finds the k-th largest key with one ballot + popcount per value and
-// bit (no cross-lane data movement); every larger key is kept, plus the lowest ids among the
-// keys equal to it, which is "larger value wins, lower id wins a tie".  The kept ids are written
-// in ascending order with softmax weights over their logits.
+// l, l+64, ... (NV per lane, E <= 64*NV) as order-preserving 32-bit keys.  Each lane sorts its
+// keys in descending order with a stable network (adjacent swaps of strictly smaller keys only,
+// so equal keys keep their ascending-id order); then k rounds take the wave-wide maximum of the
+// lanes' first keys, the winner being the lowest id among equal maxima, and the winning lane
+// drops its first key.  This is "larger value wins, lower id wins a tie".  The kept ids are
+// written in ascending order with softmax weights over their logits.
 // ==============================================================================================
 __device__ __forceinline__ uint32_t order_key(float v) {
     const uint32_t u = __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
 
 // Maximum over the wave, returned uniform: DPP within each row of 16 lanes (swap neighbours,
 // swap pairs, rotate by 4, rotate by 8), then the four row maxima through scalar reads.
@@ -109,90 +113,84 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Selects the top k of a wave's NV-per-lane logits (value j of lane l is expert l + 64 j).
-// k rounds of a wave-wide maximum over order-preserving keys; among equal keys the lowest
-// expert id is taken (lowest j, then lowest lane).  Returns, per value j, whether it is kept
-// and its rank among the kept ids (ascending id), and the largest kept logit.
+// Top k of one token's logits (row of E <= 1024) by one wave.  Lanes 0 .. k-1 return a kept
+// expert as (rank among the kept ids in ascending order) << 16 | id, with its softmax weight;
+// other lanes return -1.
 template <int NV>
-__device__ __forceinline__ void wave_topk(const float (&v)[NV], int E, int k, bool (&keep)[NV], int (&pos)[NV],
-                                          float& vmax) {
-    const int lane = threadIdx.x & 63;
-    uint32_t key[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        key[j] = (lane + 64 * j < E) ? order_key(v[j]) : 0u;  // valid keys are > 0
-        keep[j] = false;
-    }
-    uint32_t first = 0;
-#pragma unroll 1
-    for (int r = 0; r < k; ++r) {
-        uint32_t m = key[0];
-#pragma unroll
-        for (int j = 1; j < NV; ++j) m = max(m, key[j]);
-        m = wave_max_u32(m);
-        if (r == 0) first = m;
-        // the winner: lowest j holding m, then the lowest lane there (uniform scalar choice)
-        uint64_t b[NV];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) b[j] = __ballot(key[j] == m);
-        int wj = NV - 1;
-        uint64_t wb = b[NV - 1];
-#pragma unroll
-        for (int j = NV - 2; j >= 0; --j)
-            if (b[j] != 0ull) {
-                wj = j;
-                wb = b[j];
-            }
-        const bool mine = lane == __ffsll((unsigned long long)wb) - 1;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const bool t = mine && j == wj;
-            keep[j] = keep[j] || t;
-            key[j] = t ? 0u : key[j];
-        }
-    }
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int sel_before = 0;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const uint64_t sel = __ballot(keep[j]);
-        pos[j] = sel_before + popc64(sel & lt);
-        sel_before += popc64(sel);
-    }
-    // back from the order key to the value
-    vmax = __uint_as_float((first & 0x80000000u) ? (first & 0x7fffffffu) : ~first);
-}
-
-template <int NV>
-__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids,
-                                           float* __restrict__ w) {
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int& out, float& out_w) {
     const int lane = threadIdx.x & 63;
     // all loads first (clamped addresses, no branch), so they are in flight together
     float v[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
+    uint32_t key[NV];
+    int id[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const bool ok = lane + 64 * j < E && v[j] == v[j];  // NaN never wins and never breaks the selection
-        v[j] = ok ? v[j] : -INFINITY;
+        // NaN counts as -inf (never ahead of a number); ids past E get key 0, below every value
+        const float x = v[j] == v[j] ? v[j] : -INFINITY;
+        key[j] = lane + 64 * j < E ? order_key(x) : 0u;
+        id[j] = lane + 64 * j;
     }
-    bool keep[NV];
-    int pos[NV];
-    float vmax;
-    wave_topk<NV>(v, E, k, keep, pos, vmax);
-    float e[NV], s = 0.f;
+    // stable descending sort of the lane's keys (odd-even transposition, strict comparisons)
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        e[j] = keep[j] ? expf(v[j] - vmax) : 0.f;
-        s += e[j];
-    }
-    s = wave_sum_f32(s);
+    for (int ph = 0; ph < NV; ++ph)
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        if (keep[j]) {
-            ids[pos[j]] = lane + 64 * j;
-            w[pos[j]] = e[j] / s;
+        for (int j = ph & 1; j + 1 < NV; j += 2) {
+            const bool sw = key[j + 1] > key[j];
+            const uint32_t ka = key[j], kb = key[j + 1];
+            const int ia = id[j], ib = id[j + 1];
+            key[j] = sw ? kb : ka;
+            key[j + 1] = sw ? ka : kb;
+            id[j] = sw ? ib : ia;
+            id[j + 1] = sw ? ia : ib;
         }
+    uint32_t sel_key = 0;
+    int sel_id = -1;
+#pragma unroll 1
+    for (int r = 0; r < k; ++r) {
+        const uint32_t m = wave_max_u32(key[0]);
+        const uint64_t cand = __ballot(key[0] == m);
+        int win = __ffsll((unsigned long long)cand) - 1;
+        if (__popcll(cand) > 1) {  // equal maxima: the lowest id among the candidates
+            const uint32_t lo = ~wave_max_u32(key[0] == m ? ~(uint32_t)id[0] : 0u);
+            win = __ffsll((unsigned long long)__ballot(key[0] == m && (uint32_t)id[0] == lo)) - 1;
+        }
+        const int wid = __builtin_amdgcn_readlane(id[0], win);
+        if (lane == r) {
+            sel_key = m;
+            sel_id = wid;
+        }
+        if (lane == win) {
+#pragma unroll
+            for (int j = 0; j + 1 < NV; ++j) {
+                key[j] = key[j + 1];
+                id[j] = id[j + 1];
+            }
+            key[NV - 1] = 0u;
+        }
+    }
+    // the first winner holds the largest kept logit; weights over the kept logits
+    const float vmax = key_value((uint32_t)__builtin_amdgcn_readlane((int)sel_key, 0));
+    const float e = lane < k ? expf(key_value(sel_key) - vmax) : 0.f;
+    const float s = wave_sum_f32(e);
+    // rank among the kept ids (distinct), ascending
+    int pos = 0;
+    for (int r = 0; r < k; ++r) pos += __builtin_amdgcn_readlane(sel_id, r) < sel_id ? 1 : 0;
+    out = lane < k ? (pos << 16) | sel_id : -1;
+    out_w = lane < k ? e / s : 0.f;
+}
+
+template <int NV>
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids,
+                                           float* __restrict__ w) {
+    int pid;
+    float wt;
+    wave_topk<NV>(row, E, k, pid, wt);
+    if (pid >= 0) {
+        ids[pid >> 16] = pid & 0xffff;
+        w[pid >> 16] = wt;
+    }
 }
 
 template <int NV>
@@ -292,7 +290,10 @@ __global__ __launch_bounds__(1024) void perm_single_kernel(const int32_t* __rest
 }
 
 // Routing and permutation of a small batch (T <= 64) in one workgroup of 16 waves: each wave
-// selects the experts of its tokens into LDS, then the block builds the segments.
+// selects the experts of its tokens and marks them in the per-expert token bitmaps; one block
+// scan of (count | tiles << 16) per expert then gives the segment offsets and the work-list
+// positions together (counts <= 1024 and tile counts <= 1024 never carry into each other), and
+// every slot is placed at its stable rank (earlier tokens first) inside its expert's segment.
 template <int NV>
 __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                                 int32_t* __restrict__ ids, float* __restrict__ w,
@@ -303,11 +304,43 @@ __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __r
     __shared__ int soff[1024];
     __shared__ int tmp[33];
     __shared__ int32_t sids[64 * 16];
-    for (int t = threadIdx.x >> 6; t < T; t += 16)
-        topk_token<NV>(logits + (size_t)t * E, E, k, sids + t * k, w + (size_t)t * k);
+    for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) bm[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < T * k; i += blockDim.x) ids[i] = sids[i];
-    perm_single_body(sids, T, k, E, offsets, perm, inv, BM, tiles, ntiles, has_shared, bm, soff, tmp);
+    for (int t = threadIdx.x >> 6; t < T; t += 16) {
+        int pid;
+        float wt;
+        wave_topk<NV>(logits + (size_t)t * E, E, k, pid, wt);
+        if (pid >= 0) {
+            const int pos = pid >> 16, e = pid & 0xffff;
+            ids[(size_t)t * k + pos] = e;
+            w[(size_t)t * k + pos] = wt;
+            sids[t * k + pos] = e;
+            atomicOr(&bm[2 * e + (t >> 5)], 1u << (t & 31));
+        }
+    }
+    __syncthreads();
+    const int e = threadIdx.x;
+    const int cnt = e < E ? __popc(bm[2 * e]) + __popc(bm[2 * e + 1]) : 0;
+    const int nt = (cnt + BM - 1) / BM;
+    int total;
+    const int packed = block_excl_scan(cnt | (nt << 16), tmp, &total);
+    const int off = packed & 0xffff, ts = packed >> 16;
+    const int nslots = total & 0xffff, ntot = total >> 16;
+    if (e < E) {
+        offsets[e] = off;
+        soff[e] = off;
+        if (tiles)
+            for (int j = 0; j < nt; ++j) tiles[ts + j] = Tile{e, off + j * BM, min(BM, cnt - j * BM), 0};
+    }
+    if (e == 0) offsets[E] = nslots;
+    if (tiles) {
+        const int nsh = has_shared ? (T + BM - 1) / BM : 0;
+        for (int j = threadIdx.x; j < nsh; j += blockDim.x) tiles[ntot + j] = Tile{E, T * k + j * BM, min(BM, T - j * BM), 0};
+        if (threadIdx.x == 0) *ntiles = ntot + nsh;
+    }
+    for (int i = nslots + threadIdx.x; i < T * k; i += blockDim.x) perm[i] = -1;
+    __syncthreads();
+    perm_scatter_block(sids, T, k, E, 0, bm, soff, perm, inv);
 }
 
 __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
@@ -512,8 +545,26 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_PROJ_CHUNK
 #define LMOE_PROJ_CHUNK 1
 #endif
-#ifndef LMOE_DECODE_KSU
-#define LMOE_DECODE_KSU 1
+#ifndef LMOE_GU_WAVES
+#define LMOE_GU_WAVES 2
+#endif
+#ifndef LMOE_GU_CHUNK
+#define LMOE_GU_CHUNK 4
+#endif
+#ifndef LMOE_DC_WAVES
+#define LMOE_DC_WAVES 8
+#endif
+#ifndef LMOE_DC_CHUNK
+#define LMOE_DC_CHUNK 4
+#endif
+#ifndef LMOE_DC_GROUPS
+#define LMOE_DC_GROUPS 2
+#endif
+#ifndef LMOE_SP_WAVES
+#define LMOE_SP_WAVES 8
+#endif
+#ifndef LMOE_SP_SMAX
+#define LMOE_SP_SMAX 10
 #endif
 #ifndef LMOE_TILE_M
 #define LMOE_TILE_M 128
@@ -586,8 +637,27 @@ hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream
     return last();
 }
 
+// Lets a small-batch projection kernel take up to kSmallProjLds bytes of dynamic LDS (once per kernel).
+template <int XM>
+hipError_t small_proj_launch(const SmallProj& p, hipStream_t s) {
+    auto k = small_proj_kernel<LMOE_SP_WAVES, LMOE_SP_SMAX, XM>;
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(k, dim3((unsigned)cdiv(p.N, 16)), dim3(64 * LMOE_SP_WAVES), small_proj_lds(p.T, p.K), s, p);
+    return last();
+}
+
+hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
+                                uint16_t* out16, hipStream_t s) {
+    if (T > kStreamMaxT || small_proj_lds(T, K) > kSmallProjLds) return hipErrorInvalidValue;
+    return small_proj_launch<1>(SmallProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16}, s);
+}
+
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                             uint16_t* out16, hipStream_t s, uint16_t* out16lo) {
+    if (T <= kStreamMaxT && small_proj_lds(T, K) <= kSmallProjLds)
+        return small_proj_launch<0>(SmallProj{x, nullptr, 0, W, T, N, K, mode, out32, out16}, s);
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1, StreamProj, kProjChunk>(StreamProj{x, W, T, N, K, mode, out32, out16},
                                                                    (int)cdiv(T, 16), N, s);
@@ -686,49 +756,37 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
 }
 
-// Small-batch expert launch shape: 8 waves, one 16-row block each, so a slice is 128 columns of
-// F (MXFP4 slices must hold whole 128-value groups); bf16 widths that are not multiples of 128
-// use 4 waves (64-column slices).
-constexpr int kDecodeKsu = LMOE_DECODE_KSU;
+// Small-batch expert launches: gate/up items of LMOE_GU_WAVES x 16 columns, then the down
+// projection and merge over LMOE_DC_GROUPS groups of the work list.
+constexpr int kGuWaves = LMOE_GU_WAVES, kGuChunk = LMOE_GU_CHUNK;
+constexpr int kDcWaves = LMOE_DC_WAVES, kDcChunk = LMOE_DC_CHUNK, kDcGroups = LMOE_DC_GROUPS;
 
-int decode_waves(int F, int Fs, bool mx) {
-    return mx || (F % (128 * kDecodeKsu) == 0 && Fs % (128 * kDecodeKsu) == 0) ? 8 : 4;
-}
+int decode_groups() { return kDcGroups; }
 
-int decode_slices(int F, int Fs, bool mx) { return std::max(F, Fs) / (16 * decode_waves(F, Fs, mx) / kDecodeKsu); }
-
-bool decode_fits(int F, int Fs, bool mx) {
-    const int FS = 16 * decode_waves(F, Fs, mx) / kDecodeKsu;
-    return F % FS == 0 && Fs % FS == 0;
-}
-
-// Small batches: gate/up, SwiGLU and down per (tile, F slice) in one launch, then the merge.
-template <bool MX, int W>
-hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
-    constexpr int FS = DecodeShape<W, kDecodeKsu>::kFS;
-    const int nslices = decode_slices(a.F, a.Fs, MX);
-    DecodeExperts<MX> d{seg, a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs,
-                        nslices, a.P};
-    const long items = (long)a.max_tiles * nslices;
-    ev.begin(kStageUp);
-    hipLaunchKernelGGL((decode_experts_kernel<W, kDecodeKsu, (MX ? 1 : kChunk), MX>),
-                       dim3((unsigned)std::min<long>(items, LMOE_STREAM_GRID)), dim3(64 * W), 0, s, d);
-    hipError_t err = last();
-    if (err != hipSuccess) return err;
-    ev.end(kStageUp);
-    ev.begin(kStageCombine);
-    hipLaunchKernelGGL(merge_slices_kernel, dim3(cdiv(a.L, 256), a.T), dim3(64 * kMergeRows), 0, s, a.P, a.w, a.T,
-                       a.k, a.L, nslices, a.F / FS, a.Fs / FS, a.m16);
-    if ((err = last()) != hipSuccess) return err;
-    ev.end(kStageCombine);
-    return hipSuccess;
+bool decode_fits(int T, int L, int F, int Fs) {
+    // widths in whole 16-row blocks (a gate/up slice may end inside a segment); U stages its input in LDS
+    return T <= kStreamMaxT && F % 16 == 0 && Fs % 16 == 0 && small_proj_lds(T, L) <= kSmallProjLds;
 }
 
 template <bool MX>
 hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
-    if (decode_waves(a.F, a.Fs, MX) == 8) return launch_decode_experts<MX, 8>(a, seg, s, ev);
-    if constexpr (!MX) return launch_decode_experts<MX, 4>(a, seg, s, ev);
-    return hipErrorInvalidValue;  // not reached: MXFP4 always takes 8 waves
+    constexpr int FS = 16 * kGuWaves;
+    const int nslices = (int)cdiv(a.Hs, FS);
+    DecodeExperts<MX> d{seg,   a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs, a.Hs,
+                        nslices, a.H,  a.w,       a.mpart,     kDcGroups};
+    const long items = (long)a.max_tiles * nslices;
+    ev.begin(kStageUp);
+    hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, (MX ? 1 : kGuChunk), MX>),
+                       dim3((unsigned)std::min<long>(items, LMOE_STREAM_GRID)), dim3(64 * kGuWaves), 0, s, d);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    ev.end(kStageUp);
+    ev.begin(kStageDown);
+    hipLaunchKernelGGL((decode_dc_kernel<kDcWaves, (MX ? 1 : kDcChunk), MX>), dim3(a.L / 16, kDcGroups),
+                       dim3(64 * kDcWaves), 0, s, d);
+    if ((err = last()) != hipSuccess) return err;
+    ev.end(kStageDown);
+    return hipSuccess;
 }
 
 // Larger MXFP4 batches: persistent weight-streaming gate/up, then down (the combine follows).

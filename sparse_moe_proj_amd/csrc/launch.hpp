@@ -63,10 +63,14 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
                                int32_t* ntiles, int has_shared, hipStream_t s);
 
-// Slices of the SwiGLU width in the small-batch expert launch (partial rows per routed row).
-int decode_slices(int F, int Fs, bool mx);
-// Whether the SwiGLU widths split into whole slices (else small batches take the two-launch path).
-bool decode_fits(int F, int Fs, bool mx);
+// Whether a batch takes the small-batch expert path (gate/up launch, down + merge launch into
+// decode_groups() partial merged rows, summed by the U projection).
+bool decode_fits(int T, int L, int F, int Fs);
+int decode_groups();
+
+// U projection of a small batch whose input is the sum (in order) of G fp32 partials [G][T][K].
+hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
+                                uint16_t* out16, hipStream_t s);
 
 int expert_tile_rows(bool stream_path);
 int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path);
@@ -84,11 +88,10 @@ struct ExpertArgs {
     uint16_t* Y;       // [T*k + T][L] bf16 expert outputs (T > 16)
     int max_tiles;
     bool stream_path;
-    bool decode_path;  // T <= kStreamMaxT: one launch per (tile, F slice), partials P, merge into m16
+    bool decode_path;  // small batch: gate/up into H, then down + merge into mpart
     bool mxfp4;
-    float* P;          // [T*k + T][decode_slices][L]
+    float* mpart;      // [decode_groups()][T][L] partial merged rows (decode path)
     const float* w;
-    uint16_t* m16;
 };
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 

@@ -1,0 +1,110 @@
+// Dense projection of a small batch (T <= 16 tokens): out[t][n] = sum_k x[t][k] * W[n][k].
+//
+// The work is reading W once from HBM.  A workgroup owns 16 weight rows; its W waves split K
+// into contiguous ranges and each wave requests all weight units of its range (up to SMAX MFMA
+// steps at a time) before anything else, so the whole range is in flight at once.  While those
+// loads travel, the workgroup stages the activations into LDS as bf16 (XM = 0: a bf16 [T][K]
+// input; XM = 1: the sum, in order, of G fp32 partial inputs [G][T][K], rounded once), so the
+// token operand is read from LDS rather than once per wave from L2.  The MFMA is
+// v_mfma_f32_16x16x32_bf16 with the weights as A (16 rows) and the tokens as B (columns past T
+// are zero).  The waves' partial tiles meet in LDS and are summed in wave order.
+#pragma once
+
+#include "problems.hpp"
+
+namespace lmoe {
+
+struct SmallProj {
+    const uint16_t* x16;  // XM 0: [T][K] bf16
+    const float* xpart;   // XM 1: [G][T][K] fp32
+    int G;
+    const uint16_t* W;    // [N][K] bf16
+    int T, N, K, mode;    // mode 0: out32 = v, out16 = bf16(v); 1: out16 = bf16(v); 2: out32 += v
+    float* out32;
+    uint16_t* out16;
+};
+
+// Largest staged-activation LDS a small-batch projection takes (plus W KB of static LDS).
+constexpr size_t kSmallProjLds = 128 * 1024;
+
+// LDS bytes of the staged activations: T rows of K/8 16-byte units plus one unit of padding.
+__host__ __device__ inline size_t small_proj_lds(int T, int K) { return (size_t)T * (K / 8 + 1) * 16; }
+
+template <int W, int SMAX, int XM>
+__global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
+    extern __shared__ uint4 xs[];  // [T][K / 8 + 1]
+    __shared__ float red[W][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kq = lane >> 4, j = lane & 15;
+    const int n0 = blockIdx.x * 16;
+    const int K = p.K, T = p.T;
+    const int ns = K / 32;
+    const int s0 = wave * ns / W, s1 = (wave + 1) * ns / W;
+    const uint16_t* wrow = p.W + (size_t)min(n0 + j, p.N - 1) * K;
+    uint4 wv[SMAX];
+    auto loadw = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < SMAX; ++i) wv[i] = ld16(wrow + min(b + i, s1 - 1) * 32 + kq * 8);
+    };
+    if (s0 < s1) loadw(s0);
+    const int per = K / 8, xst = per + 1;
+    for (int e = threadIdx.x; e < T * per; e += 64 * W) {
+        const int t = e / per, c = e - t * per;
+        uint4 v;
+        if constexpr (XM == 0) {
+            v = ld16(p.x16 + (size_t)t * K + c * 8);
+        } else {
+            float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int g = 0; g < p.G; ++g) {
+                const float* src = p.xpart + ((size_t)g * T + t) * K + c * 8;
+                const float4 u0 = *reinterpret_cast<const float4*>(src);
+                const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+                a[0] += u0.x;
+                a[1] += u0.y;
+                a[2] += u0.z;
+                a[3] += u0.w;
+                a[4] += u1.x;
+                a[5] += u1.y;
+                a[6] += u1.z;
+                a[7] += u1.w;
+            }
+            v = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
+        }
+        xs[t * xst + c] = v;
+    }
+    __syncthreads();
+    f32x4 acc = f32x4{};
+    const bool tok = j < T;
+    for (int b = s0; b < s1; b += SMAX) {
+        if (b != s0) loadw(b);
+#pragma unroll
+        for (int i = 0; i < SMAX; ++i)
+            if (b + i < s1) {
+                const uint4 xv = tok ? xs[j * xst + (b + i) * 4 + kq] : zero4();
+                acc = mfma16(wv[i], xv, acc);
+            }
+    }
+    // lane (kq, j): rows n0 + 4 kq + r, token j
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][(4 * kq + r) * 16 + j] = acc[r];
+    __syncthreads();
+    // thread e: token e / 16, row n0 + e % 16 (16 consecutive outputs of a token per 16 threads)
+    for (int e = threadIdx.x; e < 256; e += 64 * W) {
+        const int t = e >> 4, r = e & 15, n = n0 + r;
+        if (t >= T || n >= p.N) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) v += red[w][r * 16 + t];
+        const size_t o = (size_t)t * p.N + n;
+        if (p.mode == 0) {
+            p.out32[o] = v;
+            p.out16[o] = (uint16_t)f2bf(v);
+        } else if (p.mode == 1) {
+            p.out16[o] = (uint16_t)f2bf(v);
+        } else {
+            p.out32[o] += v;
+        }
+    }
+}
+
+}  // namespace lmoe
