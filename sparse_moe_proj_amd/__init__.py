@@ -37,7 +37,7 @@ class lmoe_config(ctypes.Structure):
 
 class lmoe_weights(ctypes.Structure):
     _fields_ = [("D", ctypes.c_void_p), ("U", ctypes.c_void_p), ("Wr", ctypes.c_void_p), ("br", ctypes.c_void_p),
-                ("shared", ctypes.c_void_p), ("experts", ctypes.c_void_p)]
+                ("shared", ctypes.c_void_p), ("experts", ctypes.c_void_p), ("Gr", ctypes.c_void_p)]
 
 
 class lmoe_forward_opts(ctypes.Structure):
@@ -66,6 +66,8 @@ def _load():
         "lmoe_permute": (I32, [cfgp, P, I32, P, P, P, P, SZ, P]),
         "lmoe_forward": (I32, [cfgp, wp, P, I32, P, ctypes.POINTER(lmoe_forward_opts), P, SZ, P]),
         "lmoe_pack_experts": (I32, [cfgp, I32, P, P, I32, P]),
+        "lmoe_fold_router_bytes": (SZ, [cfgp]),
+        "lmoe_fold_router": (I32, [cfgp, P, P, P, P]),
         "lmoe_status_str": (ctypes.c_char_p, [I32]),
         "lmoe_last_error": (ctypes.c_char_p, []),
         "lmoe_version": (I32, []),
@@ -108,8 +110,8 @@ def make_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, act="bf16", d
     return lmoe_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, DTYPES[act], DTYPES[dense], DTYPES[expert])
 
 
-def make_weights(D, U, Wr, br, shared, experts):
-    return lmoe_weights(_p(D), _p(U), _p(Wr), _p(br), _p(shared), _p(experts))
+def make_weights(D, U, Wr, br, shared, experts, Gr=None):
+    return lmoe_weights(_p(D), _p(U), _p(Wr), _p(br), _p(shared), _p(experts), _p(Gr))
 
 
 LMOE_N_STAGES = 9
@@ -166,6 +168,14 @@ def lmoe_forward(cfg, weights, x, T, y, opts, ws, ws_bytes, stream=None) -> int:
 
 def lmoe_pack_experts(cfg, shared, src, dst, n_records, stream=None) -> int:
     return lib.lmoe_pack_experts(ctypes.byref(cfg), int(shared), _p(src), _p(dst), int(n_records), _stream(stream))
+
+
+def lmoe_fold_router_bytes(cfg) -> int:
+    return int(lib.lmoe_fold_router_bytes(ctypes.byref(cfg)))
+
+
+def lmoe_fold_router(cfg, D, Wr, Gr, stream=None) -> int:
+    return lib.lmoe_fold_router(ctypes.byref(cfg), _p(D), _p(Wr), _p(Gr), _stream(stream))
 
 
 def lmoe_status_str(status: int) -> str:

@@ -77,7 +77,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t x16, z32, z16, zlo, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, mpart, m, total;
-    bool stream_path, decode_path;
+    bool stream_path, decode_path, fused_router;
     int max_tiles, BM, Hs, R;
 };
 
@@ -87,6 +87,7 @@ Layout plan(const Dims& d, int T) {
     const int has_shared = d.Fs > 0;
     lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx);
     lo.decode_path = !d.f32 && decode_fits(T, d.L, d.F, d.Fs);
+    lo.fused_router = !d.f32 && T <= kStreamMaxT && small_proj_fits(T, d.H);
     lo.BM = expert_tile_rows(lo.stream_path);
     lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path);
     lo.Hs = std::max(d.F, d.Fs);
@@ -102,7 +103,7 @@ Layout plan(const Dims& d, int T) {
     lo.z32 = take((size_t)T * d.L * 4);
     lo.z16 = take(d.f32 ? 0 : (size_t)T * d.L * 2);
     lo.zlo = take(d.f32 || T <= kStreamMaxT ? 0 : (size_t)T * d.L * 2);  // low bf16 half of z (router input)
-    lo.logits = take((size_t)T * d.E * 4);
+    lo.logits = take((size_t)T * d.E * 4 * (lo.fused_router ? 2 : 1));  // folded router: hi and lo halves
     lo.ids = take((size_t)T * d.k * 4);
     lo.w = take((size_t)T * d.k * 4);
     lo.offsets = take((size_t)(d.E + 1) * 4);
@@ -166,6 +167,28 @@ lmoe_status lmoe_pack_experts(const lmoe_config* cfg, int32_t shared, const void
     const hipError_t e = launch_pack(src, dst, rec, n_records, shared ? d.Fs : d.F, d.L, d.mx && !shared,
                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "pack experts");
+    return LMOE_OK;
+}
+
+size_t lmoe_fold_router_bytes(const lmoe_config* cfg) {
+    Dims d;
+    if (check_config(cfg, d) != LMOE_OK || d.f32) return 0;
+    return (size_t)d.E * 2 * d.H * 2;
+}
+
+lmoe_status lmoe_fold_router(const lmoe_config* cfg, const void* D, const void* Wr, void* Gr, void* stream) {
+    Dims d;
+    lmoe_status st = check_config(cfg, d);
+    if (st != LMOE_OK) return st;
+    if (d.f32) return fail(LMOE_ERR_UNSUPPORTED, "the folded router is for bf16 dense weights");
+    if (!D || !Wr || !Gr) return fail(LMOE_ERR_NULL, "D, Wr and Gr must be non-NULL");
+    if (!aligned16(D) || !aligned16(Wr) || !aligned16(Gr)) return fail(LMOE_ERR_ALIGN, "D, Wr and Gr must be 16-byte aligned");
+    const size_t gb = (size_t)d.E * 2 * d.H * 2;
+    if (overlap(Gr, gb, D, (size_t)d.L * d.H * 2) || overlap(Gr, gb, Wr, (size_t)d.E * d.L * 2))
+        return fail(LMOE_ERR_UNSUPPORTED, "Gr overlaps D or Wr");
+    const hipError_t e = launch_fold_router(static_cast<const uint16_t*>(D), static_cast<const uint16_t*>(Wr), d.E, d.L,
+                                            d.H, static_cast<uint16_t*>(Gr), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fold router");
     return LMOE_OK;
 }
 
@@ -251,7 +274,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     if (!x || !y || !wt->D || !wt->U || !wt->Wr || !wt->experts)
         return fail(LMOE_ERR_NULL, "x, y, D, U, Wr and experts must be non-NULL");
     if (d.Fs > 0 && !wt->shared) return fail(LMOE_ERR_NULL, "shared_ffn > 0 but the shared expert record is NULL");
-    const void* ptrs[] = {x, y, wt->D, wt->U, wt->Wr, wt->experts, wt->shared, ws, o.aux_z, o.aux_ids, o.aux_w,
+    const void* ptrs[] = {x, y, wt->D, wt->U, wt->Wr, wt->Gr, wt->experts, wt->shared, ws, o.aux_z, o.aux_ids, o.aux_w,
                           o.aux_offsets, o.aux_perm};
     for (const void* p : ptrs)
         if (!aligned16(p)) return fail(LMOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -325,20 +348,30 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         x16 = xn;
     }
     uint16_t* z16 = static_cast<uint16_t*>(at(lo.z16));
-    ev.begin(LMOE_STAGE_D);
-    uint16_t* zlo = T > kStreamMaxT ? static_cast<uint16_t*>(at(lo.zlo)) : nullptr;
-    if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s, zlo)) != hipSuccess)
-        return hip_fail(e, "D projection");
-    ev.end(LMOE_STAGE_D);
-    ev.begin(LMOE_STAGE_ROUTER);
-    if ((e = launch_router_bf16(z32, static_cast<const uint16_t*>(wt->Wr), wt->br, T, d.E, d.L, logits, s, zlo ? z16 : nullptr,
-                                zlo)) != hipSuccess)
-        return hip_fail(e, "router logits");
-    ev.end(LMOE_STAGE_ROUTER);
+    if (wt->Gr && lo.fused_router) {  // z and the logits (folded router) in one launch
+        ev.begin(LMOE_STAGE_D);
+        if ((e = launch_proj_router_bf16(x16, static_cast<const uint16_t*>(wt->D), static_cast<const uint16_t*>(wt->Gr),
+                                         wt->br, T, d.L, d.H, d.E, z32, z16, logits, s)) != hipSuccess)
+            return hip_fail(e, "D projection and router logits");
+        ev.end(LMOE_STAGE_D);
+    } else {
+        ev.begin(LMOE_STAGE_D);
+        uint16_t* zlo = T > kStreamMaxT ? static_cast<uint16_t*>(at(lo.zlo)) : nullptr;
+        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s, zlo)) !=
+            hipSuccess)
+            return hip_fail(e, "D projection");
+        ev.end(LMOE_STAGE_D);
+        ev.begin(LMOE_STAGE_ROUTER);
+        if ((e = launch_router_bf16(z32, static_cast<const uint16_t*>(wt->Wr), wt->br, T, d.E, d.L, logits, s,
+                                    zlo ? z16 : nullptr, zlo)) != hipSuccess)
+            return hip_fail(e, "router logits");
+        ev.end(LMOE_STAGE_ROUTER);
+    }
     // top-k and permutation (one launch for small batches: the TOPK stage events bracket both)
     ev.begin(LMOE_STAGE_TOPK);
+    const float* logits2 = wt->Gr && lo.fused_router ? logits + (size_t)T * d.E : nullptr;
     if ((e = launch_topk_permute(logits, T, d.E, d.k, ids, wts, hist, base, offsets, perm, inv, lo.BM, tiles, ntiles,
-                                 has_shared, s)) != hipSuccess)
+                                 has_shared, s, logits2)) != hipSuccess)
         return hip_fail(e, "top-k / permute");
     ev.end(LMOE_STAGE_TOPK);
     float* mpart = static_cast<float*>(at(lo.mpart));

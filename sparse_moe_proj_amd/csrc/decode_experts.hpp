@@ -1,13 +1,12 @@
 // Expert work of a small batch (decode / speculative verify, T <= 16 tokens) in two launches
 // with no dependency between workgroups inside either launch.
 //
-// 1. Gate/up (decode_gu_kernel).  A work item is (tile, slice): the tile's tokens (<= 16 rows of
-//    one segment) and FS = 16 * W consecutive columns f of the SwiGLU width; wave w computes the
-//    gate and up rows f = slice * FS + 16 w .. + 16 against the tokens (K = latent, weights
-//    streamed from HBM, double buffered) and stores SiLU(g) * u as bf16 into
+// 1. Gate/up (decode_gu_kernel).  A work item is (tile, block): the tile's tokens (<= 16 rows of
+//    one segment) and 16 consecutive columns f of the SwiGLU width; a wave computes the gate and
+//    up rows of the block against the tokens (K = latent, weights streamed from HBM, double
+//    buffered) and stores SiLU(g) * u as bf16 into
 //        H[segment row][f].
-//    Slices are narrow so that the items outnumber the compute units several times over: every
-//    CU streams weights, and a CU finishing early takes the next item.
+//    Items are dealt evenly over the compute units, so every CU streams the same share.
 // 2. Down and merge (decode_dc_kernel).  A workgroup owns 16 latent rows and one group of the
 //    work list (the tiles are split into G contiguous groups).  Its waves take the group's tiles
 //    in turn; for a tile, Y = H(tile rows) . down^T over the full SwiGLU width (weights streamed,
@@ -34,7 +33,7 @@ struct DecodeExperts {
     size_t rec_bytes;
     const uint16_t* shared;
     int L, F, Fs, Hs;  // Hs = max(F, Fs): row pitch of H
-    int nslices;       // gate/up slices per segment: Hs / FS
+    int nblocks;       // 16-row blocks of the widest segment: ceil(Hs / 16)
     uint16_t* H;       // [T*k + T][Hs] bf16, segment-row order
     const float* w;    // [T][k] routing weights (slot order)
     float* mpart;      // [G][T][L]
@@ -98,21 +97,23 @@ __device__ __forceinline__ void gu_item(const DecodeExperts<MX>& d, const Tile& 
     }
 }
 
-// A grid of workgroups walks the items (tile, slice) with a stride; items past the segment's
-// width are skipped.  W waves per item, FS = 16 W columns per slice.
+// Gate/up work items are (tile, 16-row block of the SwiGLU width), in work-list order with the
+// blocks of a tile adjacent.  The grid holds one workgroup per compute unit (W waves, at most
+// one such workgroup fits a CU) and item i goes to workgroup i % grid, wave (i / grid) % W, so
+// every CU streams the same number of items; blocks past the segment's width are skipped.
 template <int W, int CH, bool MX>
 __global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<MX> d) {
     const int wave = threadIdx.x >> 6;
-    const int nitems = *d.seg.ntiles * d.nslices;
-    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-        const int tile = item / d.nslices, slice = item - tile * d.nslices;
+    const int nitems = *d.seg.ntiles * d.nblocks;
+    for (int item = blockIdx.x + gridDim.x * wave; item < nitems; item += gridDim.x * W) {
+        const int tile = item / d.nblocks, blk = item - tile * d.nblocks;
         const Tile tl = d.seg.tiles[tile];
         typename ExpertRows<MX>::Mat mats[3];
         int Fseg;
         bool mx;
         segment_mats<MX>(d.experts, d.rec_bytes, d.shared, tl.seg, d.seg.E, d.F, d.Fs, d.L, mats, Fseg, mx);
-        const int f0 = slice * 16 * W + 16 * wave;
-        if (f0 >= Fseg) continue;  // widths are multiples of 16: a wave's rows are all in or all out
+        const int f0 = blk * 16;
+        if (f0 >= Fseg) continue;  // widths are multiples of 16
         if (mx)
             gu_item<W, CH, MX, MX>(d, tl, f0, mats);
         else

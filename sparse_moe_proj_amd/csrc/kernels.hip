@@ -116,13 +116,22 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 // Top k of one token's logits (row of E <= 1024) by one wave.  Lanes 0 .. k-1 return a kept
 // expert as (rank among the kept ids in ascending order) << 16 | id, with its softmax weight;
 // other lanes return -1.
+// row2 (optional): a second half of the logits, added to row (the folded router's lo half).
 template <int NV>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int& out, float& out_w) {
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, const float* __restrict__ row2, int E, int k,
+                                          int& out, float& out_w) {
     const int lane = threadIdx.x & 63;
     // all loads first (clamped addresses, no branch), so they are in flight together
     float v[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
+    if (row2) {
+        float v2[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v2[j] = row2[min(lane + 64 * j, E - 1)];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] += v2[j];
+    }
     uint32_t key[NV];
     int id[NV];
 #pragma unroll
@@ -186,7 +195,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
                                            float* __restrict__ w) {
     int pid;
     float wt;
-    wave_topk<NV>(row, E, k, pid, wt);
+    wave_topk<NV>(row, nullptr, E, k, pid, wt);
     if (pid >= 0) {
         ids[pid >> 16] = pid & 0xffff;
         w[pid >> 16] = wt;
@@ -295,7 +304,8 @@ __global__ __launch_bounds__(1024) void perm_single_kernel(const int32_t* __rest
 // positions together (counts <= 1024 and tile counts <= 1024 never carry into each other), and
 // every slot is placed at its stable rank (earlier tokens first) inside its expert's segment.
 template <int NV>
-__global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __restrict__ logits,
+                                                                const float* __restrict__ logits2, int T, int E, int k,
                                                                 int32_t* __restrict__ ids, float* __restrict__ w,
                                                                 int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ perm, int32_t* __restrict__ inv,
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __r
     for (int t = threadIdx.x >> 6; t < T; t += 16) {
         int pid;
         float wt;
-        wave_topk<NV>(logits + (size_t)t * E, E, k, pid, wt);
+        wave_topk<NV>(logits + (size_t)t * E, logits2 ? logits2 + (size_t)t * E : nullptr, E, k, pid, wt);
         if (pid >= 0) {
             const int pos = pid >> 16, e = pid & 0xffff;
             ids[(size_t)t * k + pos] = e;
@@ -546,7 +556,7 @@ inline hipError_t last() { return hipGetLastError(); }
 #define LMOE_PROJ_CHUNK 1
 #endif
 #ifndef LMOE_GU_WAVES
-#define LMOE_GU_WAVES 2
+#define LMOE_GU_WAVES 8
 #endif
 #ifndef LMOE_GU_CHUNK
 #define LMOE_GU_CHUNK 4
@@ -616,6 +626,19 @@ hipError_t launch_stream(const P& p, int max_tiles, int nrows_max, hipStream_t s
 }
 }  // namespace
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
 // Workgroups of `kernel` that fit on the current device at once (cached per kernel and device).
 template <class K>
 int resident_blocks(K kernel, int threads) {
@@ -645,6 +668,38 @@ hipError_t small_proj_launch(const SmallProj& p, hipStream_t s) {
         hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(k, dim3((unsigned)cdiv(p.N, 16)), dim3(64 * LMOE_SP_WAVES), small_proj_lds(p.T, p.K), s, p);
+    return last();
+}
+
+hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const uint16_t* Gr, const float* br, int T,
+                                  int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s) {
+    if (T > kStreamMaxT || small_proj_lds(T, H) > kSmallProjLds) return hipErrorInvalidValue;
+    SmallProj p{x, nullptr, 0, D, T, L, H, 0, z32, z16, Gr, br, E, logits};
+    auto k = small_proj_kernel<LMOE_SP_WAVES, LMOE_SP_SMAX, 0>;
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(k, dim3((unsigned)(cdiv(L, 16) + 2 * cdiv(E, 16))), dim3(64 * LMOE_SP_WAVES), small_proj_lds(T, H), s,
+                       p);
+    return last();
+}
+
+// G = Wr . D in fp32 (ascending latent order), stored as hi = bf16(G), lo = bf16(G - hi):
+// Gr [E][2][H].  One thread per (e, h); the block's 256 h share the Wr row.
+__global__ __launch_bounds__(256) void fold_router_kernel(const uint16_t* __restrict__ D, const uint16_t* __restrict__ Wr,
+                                                          int E, int L, int H, uint16_t* __restrict__ Gr) {
+    const int h = blockIdx.x * 256 + threadIdx.x, e = blockIdx.y;
+    if (h >= H) return;
+    const uint16_t* wr = Wr + (size_t)e * L;
+    float acc = 0.f;
+    for (int l = 0; l < L; ++l) acc = fmaf(bf2f(wr[l]), bf2f(D[(size_t)l * H + h]), acc);
+    const uint32_t hi = f2bf(acc);
+    Gr[(size_t)e * 2 * H + h] = (uint16_t)hi;
+    Gr[(size_t)e * 2 * H + H + h] = (uint16_t)f2bf(acc - bf2f(hi));
+}
+
+hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int L, int H, uint16_t* Gr, hipStream_t s) {
+    hipLaunchKernelGGL(fold_router_kernel, dim3((unsigned)cdiv(H, 256), (unsigned)E), dim3(256), 0, s, D, Wr, E, L, H, Gr);
     return last();
 }
 
@@ -724,16 +779,17 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist
 
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
-                               int32_t* ntiles, int has_shared, hipStream_t s) {
+                               int32_t* ntiles, int has_shared, hipStream_t s, const float* logits2) {
     if (T > kPermTB) {
+        if (logits2) return hipErrorInvalidValue;  // split logits come from the small-batch launch only
         hipError_t e = launch_topk(logits, T, E, k, ids, w, s);
         if (e != hipSuccess) return e;
         return launch_permute(ids, T, k, E, hist, base, offsets, perm, inv, BM, tiles, ntiles, has_shared, s);
     }
     const dim3 g(1), b(1024);
 #define LMOE_TOPK_PERM(NV)                                                                                          \
-    hipLaunchKernelGGL(topk_perm_single_kernel<NV>, g, b, 0, s, logits, T, E, k, ids, w, offsets, perm, inv, BM, tiles, \
-                       ntiles, has_shared)
+    hipLaunchKernelGGL(topk_perm_single_kernel<NV>, g, b, 0, s, logits, logits2, T, E, k, ids, w, offsets, perm, inv, BM, \
+                       tiles, ntiles, has_shared)
     if (E <= 64)
         LMOE_TOPK_PERM(1);
     else if (E <= 128)
@@ -756,12 +812,15 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
     return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
 }
 
-// Small-batch expert launches: gate/up items of LMOE_GU_WAVES x 16 columns, then the down
-// projection and merge over LMOE_DC_GROUPS groups of the work list.
+// Small-batch expert launches: gate/up work items of 16 columns dealt over one workgroup of
+// LMOE_GU_WAVES waves per compute unit, then the down projection and merge over LMOE_DC_GROUPS
+// groups of the work list.
 constexpr int kGuWaves = LMOE_GU_WAVES, kGuChunk = LMOE_GU_CHUNK;
 constexpr int kDcWaves = LMOE_DC_WAVES, kDcChunk = LMOE_DC_CHUNK, kDcGroups = LMOE_DC_GROUPS;
 
 int decode_groups() { return kDcGroups; }
+
+bool small_proj_fits(int T, int K) { return T <= kStreamMaxT && small_proj_lds(T, K) <= kSmallProjLds; }
 
 bool decode_fits(int T, int L, int F, int Fs) {
     // widths in whole 16-row blocks (a gate/up slice may end inside a segment); U stages its input in LDS
@@ -770,14 +829,14 @@ bool decode_fits(int T, int L, int F, int Fs) {
 
 template <bool MX>
 hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
-    constexpr int FS = 16 * kGuWaves;
-    const int nslices = (int)cdiv(a.Hs, FS);
-    DecodeExperts<MX> d{seg,   a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs, a.Hs,
-                        nslices, a.H,  a.w,       a.mpart,     kDcGroups};
-    const long items = (long)a.max_tiles * nslices;
+    const int nblocks = (int)cdiv(a.Hs, 16);
+    DecodeExperts<MX> d{seg,    a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs, a.Hs,
+                        nblocks, a.H,  a.w,       a.mpart,     kDcGroups};
+    const long items = (long)a.max_tiles * nblocks;
     ev.begin(kStageUp);
-    hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, (MX ? 1 : kGuChunk), MX>),
-                       dim3((unsigned)std::min<long>(items, LMOE_STREAM_GRID)), dim3(64 * kGuWaves), 0, s, d);
+    const long grid = std::min<long>(cdiv(items, kGuWaves), cu_count());
+    hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, (MX ? 1 : kGuChunk), MX>), dim3((unsigned)std::max<long>(grid, 1)),
+                       dim3(64 * kGuWaves), 0, s, d);
     hipError_t err = last();
     if (err != hipSuccess) return err;
     ev.end(kStageUp);

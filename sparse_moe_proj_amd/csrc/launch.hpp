@@ -58,15 +58,25 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist
                           int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
                           hipStream_t s);
 
-// top-k followed by the permutation; one fused launch when T <= 64.
+// top-k followed by the permutation; one fused launch when T <= 64.  logits2 (T <= 64 only):
+// a second [T][E] half added to logits (the folded router's lo half).
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
-                               int32_t* ntiles, int has_shared, hipStream_t s);
+                               int32_t* ntiles, int has_shared, hipStream_t s, const float* logits2 = nullptr);
 
 // Whether a batch takes the small-batch expert path (gate/up launch, down + merge launch into
 // decode_groups() partial merged rows, summed by the U projection).
 bool decode_fits(int T, int L, int F, int Fs);
+// Whether a T-token projection with reduction width K stages its input in LDS (one launch).
+bool small_proj_fits(int T, int K);
 int decode_groups();
+
+// Small batch: z = x D^T (z32 and bf16 z16) and the folded router's logits in one launch:
+// logits [2][T][E], logits[0] = x hi^T + br, logits[1] = x lo^T (the top-k adds them).
+hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const uint16_t* Gr, const float* br, int T,
+                                  int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s);
+// Gr [E][2][H] = hi and lo bf16 halves of Wr . D (fp32 accumulation).
+hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int L, int H, uint16_t* Gr, hipStream_t s);
 
 // U projection of a small batch whose input is the sum (in order) of G fp32 partials [G][T][K].
 hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,

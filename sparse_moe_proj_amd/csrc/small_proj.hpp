@@ -7,7 +7,8 @@
 // input; XM = 1: the sum, in order, of G fp32 partial inputs [G][T][K], rounded once), so the
 // token operand is read from LDS rather than once per wave from L2.  The MFMA is
 // v_mfma_f32_16x16x32_bf16 with the weights as A (16 rows) and the tokens as B (columns past T
-// are zero).  The waves' partial tiles meet in LDS and are summed in wave order.
+// are zero).  The waves' partial tiles meet in LDS and are summed in wave order.  A second
+// product over the same input (the two halves of the folded router) can share the launch.
 #pragma once
 
 #include "problems.hpp"
@@ -22,6 +23,14 @@ struct SmallProj {
     int T, N, K, mode;    // mode 0: out32 = v, out16 = bf16(v); 1: out16 = bf16(v); 2: out32 += v
     float* out32;
     uint16_t* out16;
+    // Optional second product in the same launch (Gr != null), from Gr [E][2][K] bf16 (hi, lo
+    // halves of each row): logits[h][t][e] = x[t] . Gr[e][h] (+ bias[e] for h = 0), so that
+    // logits[0] + logits[1] are the router logits.  Its 2 * ceil(E / 16) row blocks (the hi
+    // blocks, then the lo blocks) follow the ceil(N / 16) blocks of W.
+    const uint16_t* Gr;
+    const float* bias;
+    int E;
+    float* logits;  // [2][T][E]
 };
 
 // Largest staged-activation LDS a small-batch projection takes (plus W KB of static LDS).
@@ -36,15 +45,22 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
     __shared__ float red[W][256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = lane >> 4, j = lane & 15;
-    const int n0 = blockIdx.x * 16;
     const int K = p.K, T = p.T;
     const int ns = K / 32;
+    const int nbw = (p.N + 15) / 16, nbe = (p.E + 15) / 16;
+    const bool rt = (int)blockIdx.x >= nbw;
+    const int rb = rt ? (int)blockIdx.x - nbw : (int)blockIdx.x;
+    const int half = rt && rb >= nbe ? 1 : 0;  // which half of the Gr rows
+    const int n0 = (rb - half * nbe) * 16;
+    const int nrow = rt ? p.E : p.N;
     const int s0 = wave * ns / W, s1 = (wave + 1) * ns / W;
-    const uint16_t* wrow = p.W + (size_t)min(n0 + j, p.N - 1) * K;
+    const uint16_t* wrow =
+        rt ? p.Gr + ((size_t)min(n0 + j, nrow - 1) * 2 + half) * K : p.W + (size_t)min(n0 + j, nrow - 1) * K;
     uint4 wv[SMAX];
     auto loadw = [&](int b) {
 #pragma unroll
-        for (int i = 0; i < SMAX; ++i) wv[i] = ld16(wrow + min(b + i, s1 - 1) * 32 + kq * 8);
+        for (int i = 0; i < SMAX; ++i)
+            if (b + i < s1) wv[i] = ld16(wrow + (b + i) * 32 + kq * 8);
     };
     if (s0 < s1) loadw(s0);
     const int per = K / 8, xst = per + 1;
@@ -91,10 +107,14 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
     // thread e: token e / 16, row n0 + e % 16 (16 consecutive outputs of a token per 16 threads)
     for (int e = threadIdx.x; e < 256; e += 64 * W) {
         const int t = e >> 4, r = e & 15, n = n0 + r;
-        if (t >= T || n >= p.N) continue;
+        if (t >= T || n >= nrow) continue;
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) v += red[w][r * 16 + t];
+        if (rt) {
+            p.logits[((size_t)half * T + t) * p.E + n] = half == 0 && p.bias ? v + p.bias[n] : v;
+            continue;
+        }
         const size_t o = (size_t)t * p.N + n;
         if (p.mode == 0) {
             p.out32[o] = v;

@@ -9,8 +9,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (LMOE_OK, check, lmoe_expert_record_bytes, lmoe_forward, lmoe_pack_experts,  # noqa: F401
-               lmoe_workspace_bytes, make_config, make_opts, make_weights)
+from . import (LMOE_OK, check, lmoe_expert_record_bytes, lmoe_fold_router, lmoe_fold_router_bytes,  # noqa: F401
+               lmoe_forward, lmoe_pack_experts, lmoe_workspace_bytes, make_config, make_opts, make_weights)
 
 
 def to_device(a, device="cuda"):
@@ -36,16 +36,26 @@ def pack_records(cfg, records, shared: bool):
     return out
 
 
+def fold_router(cfg, D, Wr):
+    """Device copy of the folded router [E][2][hidden] (bf16 hi/lo halves of Wr . D)."""
+    n = lmoe_fold_router_bytes(cfg)
+    out = torch.empty(n // 2, dtype=torch.int16, device=D.device)
+    check(lmoe_fold_router(cfg, D, Wr, out))
+    return out
+
+
 class DeviceLayer:
     """One layer's weights resident in HBM (tensors kept alive by this object).  Expert records
     are uploaded row-major and packed on the device (fp32 records stay row-major).  pack=False
-    keeps them as given: only for callers that use the routing entry points alone."""
+    keeps them as given: only for callers that use the routing entry points alone.  With bf16
+    dense weights the folded router is computed too unless fold=False."""
 
-    def __init__(self, lw=None, act="bf16", device="cuda", _copy_of=None, pack=True):
+    def __init__(self, lw=None, act="bf16", device="cuda", _copy_of=None, pack=True, fold=True):
+        self.Gr = None
         if _copy_of is not None:
             src = _copy_of
             self.shape, self.act, self.dense, self.expert = src.shape, src.act, src.dense, src.expert
-            for n in ("D", "U", "Wr", "br", "shared", "experts"):
+            for n in ("D", "U", "Wr", "br", "shared", "experts", "Gr"):
                 t = getattr(src, n)
                 setattr(self, n, None if t is None else t.clone())
         else:
@@ -63,7 +73,9 @@ class DeviceLayer:
             self.experts = pack_records(self.cfg, self.experts, False)
             if self.shared is not None:
                 self.shared = pack_records(self.cfg, self.shared, True)
-        self.weights = make_weights(self.D, self.U, self.Wr, self.br, self.shared, self.experts)
+        if _copy_of is None and fold and self.dense == "bf16":
+            self.Gr = fold_router(self.cfg, self.D, self.Wr)
+        self.weights = make_weights(self.D, self.U, self.Wr, self.br, self.shared, self.experts, self.Gr)
 
     def clone(self) -> "DeviceLayer":
         """A byte-identical copy at other HBM addresses."""

@@ -140,6 +140,20 @@ def test_single_hip_runtime_in_process():
     assert len(libs) == 1, libs
 
 
+def test_fold_router_arguments_checked():
+    c = cfg()
+    t = gen.TINY
+    f32 = lm.make_config(t.hidden, t.latent, t.n_experts, t.top_k, t.ffn, t.shared_ffn, "f32", "f32", "f32")
+    assert lm.lmoe_fold_router_bytes(c) == c.n_experts * 2 * c.hidden * 2
+    assert lm.lmoe_fold_router_bytes(f32) == 0
+    far = FAKE + (1 << 34)
+    assert lm.lmoe_fold_router(f32, FAKE, FAKE + (1 << 30), far, 0) == lm.LMOE_ERR_UNSUPPORTED
+    assert lm.lmoe_fold_router(c, None, FAKE + (1 << 30), far, 0) == lm.LMOE_ERR_NULL
+    assert lm.lmoe_fold_router(c, FAKE, FAKE + (1 << 30), None, 0) == lm.LMOE_ERR_NULL
+    assert lm.lmoe_fold_router(c, FAKE + 8, FAKE + (1 << 30), far, 0) == lm.LMOE_ERR_ALIGN
+    assert lm.lmoe_fold_router(c, FAKE, FAKE + (1 << 30), FAKE + 256, 0) == lm.LMOE_ERR_UNSUPPORTED  # Gr overlaps D
+
+
 def test_pack_arguments_checked():
     c = cfg()
     rec = lm.lmoe_expert_record_bytes(c, 0)

@@ -66,6 +66,34 @@ def test_small_bf16_ragged(T, ws):
     check_block(lw, x, "bf16", out, label=f"small_bf16 T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_small_bf16_router_unfolded(T, ws):
+    """Small batches without the folded router take the z-based router launch."""
+    wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
+    dl = DeviceLayer(lw, act="bf16", fold=False)
+    assert dl.Gr is None
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"small_bf16 unfolded T={T}")
+
+
+def test_fold_router_halves():
+    """hi + lo of the folded router carries G = Wr . D to the precision the halves allow."""
+    wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
+    dl = DeviceLayer(lw, act="bf16")
+    E, H = SMALL.n_experts, SMALL.hidden
+    gr = dl.Gr.cpu().numpy().view(np.uint16).reshape(E, 2, H)
+    hi, lo = act_to_f64(gr[:, 0], "bf16"), act_to_f64(gr[:, 1], "bf16")
+    Wr, D = act_to_f64(lw.Wr, "bf16"), act_to_f64(lw.D, "bf16")
+    G = Wr @ D                                  # [E][H], exact in fp64 for these sizes
+    bound = np.abs(Wr) @ np.abs(D)              # fp32 accumulation error scale
+    err = np.abs(hi + lo - G)
+    assert np.all(err <= 2.0 ** -16 * np.abs(G) + SMALL.latent * 2.0 ** -24 * bound + 1e-30), err.max()
+    # hi is the bf16 rounding of the fp32 sum: never further than one bf16 half-ulp plus that error
+    assert np.all(np.abs(hi - G) <= 2.0 ** -8 * np.abs(G) + SMALL.latent * 2.0 ** -24 * bound + 1e-30)
+
+
 SMALL_MX = gen.Shape(hidden=256, latent=256, n_experts=24, top_k=3, ffn=128, shared_ffn=128)
 
 
