@@ -76,7 +76,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t x16, z32, z16, zlo, logits, ids, w, offsets, perm, inv, hist, base, tiles, ntiles, H, Y, mpart, m, total;
+    size_t x16, z32, z16, zlo, logits, ids, w, offsets, perm, inv, rowinfo, hist, base, tiles, ntiles, H, Y, mpart, m, total;
     bool stream_path, decode_path, fused_router;
     int max_tiles, BM, Hs, R;
 };
@@ -109,6 +109,7 @@ Layout plan(const Dims& d, int T) {
     lo.offsets = take((size_t)(d.E + 1) * 4);
     lo.perm = take((size_t)T * d.k * 4);
     lo.inv = take((size_t)T * d.k * 4);
+    lo.rowinfo = take(lo.decode_path ? (size_t)T * d.k * 8 : 0);
     lo.hist = take(nb * d.E * 4);
     lo.base = take(nb * d.E * 4);
     lo.tiles = take((size_t)lo.max_tiles * sizeof(Tile));
@@ -370,14 +371,15 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     // top-k and permutation (one launch for small batches: the TOPK stage events bracket both)
     ev.begin(LMOE_STAGE_TOPK);
     const float* logits2 = wt->Gr && lo.fused_router ? logits + (size_t)T * d.E : nullptr;
+    int2* rowinfo = lo.decode_path ? static_cast<int2*>(at(lo.rowinfo)) : nullptr;
     if ((e = launch_topk_permute(logits, T, d.E, d.k, ids, wts, hist, base, offsets, perm, inv, lo.BM, tiles, ntiles,
-                                 has_shared, s, logits2)) != hipSuccess)
+                                 has_shared, s, logits2, rowinfo)) != hipSuccess)
         return hip_fail(e, "top-k / permute");
     ev.end(LMOE_STAGE_TOPK);
     float* mpart = static_cast<float*>(at(lo.mpart));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
                  wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
-                 lo.decode_path, d.mx, mpart, wts};
+                 lo.decode_path, d.mx, mpart, wts, rowinfo};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     const int umode = o.residual ? 2 : 1;
     const uint16_t* U = static_cast<const uint16_t*>(wt->U);

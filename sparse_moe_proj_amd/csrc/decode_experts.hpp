@@ -9,9 +9,10 @@
 //    Items are dealt evenly over the compute units, so every CU streams the same share.
 // 2. Down and merge (decode_dc_kernel).  A workgroup owns 16 latent rows and one group of the
 //    work list (the tiles are split into G contiguous groups).  Its waves take the group's tiles
-//    in turn; for a tile, Y = H(tile rows) . down^T over the full SwiGLU width (weights streamed,
-//    H rows read back from L2), and each row's result is added, times its routing weight (1 for
-//    the shared expert), to the wave's per-token accumulator in LDS.  The waves' accumulators are
+//    in turn as one stream of weight chunks; for a tile, Y = H(tile rows) . down^T over the full
+//    SwiGLU width (weights streamed, H rows read back from L2), and each row's result is added,
+//    times its routing weight (1 for the shared expert), to the wave's per-token accumulator in
+//    LDS.  The waves' accumulators are
 //    then summed in wave order and written as the group's partial merged rows
 //        mpart[g][t][latent]  (fp32).
 //    The U projection sums the G partials (in group order) while staging its input.
@@ -38,6 +39,8 @@ struct DecodeExperts {
     const float* w;    // [T][k] routing weights (slot order)
     float* mpart;      // [G][T][L]
     int groups;        // G
+    const int2* rowinfo;  // [T*k] (token, weight bits) of the routed row at each position
+    int max_tiles;        // work-list capacity (entries past *seg.ntiles are not used)
 };
 
 // ---- gate/up ----------------------------------------------------------------------------------
@@ -122,87 +125,136 @@ __global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<M
 }
 
 // ---- down + merge -----------------------------------------------------------------------------
-// One tile: acc = down(latent rows n0 .. n0 + 15) . H(tile rows)^T over K = Fseg.
-template <int CH, bool MXR, bool MX>
-__device__ __forceinline__ f32x4 dc_tile(const DecodeExperts<MX>& d, const Tile& tl,
-                                         const typename ExpertRows<MX>::Mat& down, int Fseg, int n0) {
-    using ER = ExpertRows<MX>;
-    constexpr int SPL = ER::kSPL;
-    const int lane = threadIdx.x & 63;
-    const int kq = lane >> 4;
-    const int j = lane & 15;
-    const int nrows = tl.nrows;
-    const typename ER::Row rw = ER::row(down, n0 + j, Fseg);
-    const uint16_t* hr = d.H + (size_t)(tl.row0 + min(j, nrows - 1)) * d.Hs;
-    const bool ok = j < nrows;
-    const int groups = Fseg / (32 * SPL);
-    const int nch = (groups + CH - 1) / CH;
-    f32x4 acc = f32x4{};
-    typename ER::WRaw wa[CH], wb[CH];
-    uint4 ha[CH * SPL], hb[CH * SPL];
-    auto load = [&](typename ER::WRaw (&w)[CH], uint4 (&h)[CH * SPL], int c) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int gi = min(c * CH + i, groups - 1);
-            w[i] = ER::template load<MXR>(rw, gi, kq);
-#pragma unroll
-            for (int t = 0; t < SPL; ++t) h[i * SPL + t] = ld16(hr + step_k<SPL>(gi * SPL + t, kq));
-        }
-    };
-    auto compute = [&](const typename ER::WRaw (&w)[CH], const uint4 (&h)[CH * SPL], int c) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-            if (c * CH + i < groups)
-#pragma unroll
-                for (int t = 0; t < SPL; ++t) acc = mfma16(ER::template frag<MXR>(w[i], t), sel4(ok, h[i * SPL + t]), acc);
-    };
-    load(wa, ha, 0);
-    for (int c = 0; c < nch; c += 2) {
-        load(wb, hb, c + 1);
-        compute(wa, ha, c);
-        load(wa, ha, c + 2);
-        if (c + 1 < nch) compute(wb, hb, c + 1);
-    }
-    return acc;
-}
-
-// grid (L / 16, G); W waves.  Every wave must reach the barrier (no early return).
+// grid (L / 16, G); W waves; dynamic LDS: max_tiles Tiles, then T*k int2 row records.
+// A wave's tiles are one stream of chunks (CH weight loads of one tile each) with the next
+// chunk always in flight, across tile boundaries too; the tile list and the rows' tokens and
+// weights are copied to LDS once, so no chunk waits on a descriptor.  Every wave reaches the
+// barriers (no early return).
 template <int W, int CH, bool MX>
 __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<MX> d) {
+    using ER = ExpertRows<MX>;
+    constexpr int SPL = ER::kSPL;
+    extern __shared__ int4 dsm[];
     __shared__ float macc[W][16][17];  // per wave: [token][latent row of the block] (+1 pad)
+    Tile* stiles = reinterpret_cast<Tile*>(dsm);
+    int2* srow = reinterpret_cast<int2*>(dsm + d.max_tiles);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = lane >> 4, j = lane & 15;
     const int n0 = blockIdx.x * 16, grp = blockIdx.y;
     const int T = d.seg.T, k = d.seg.k, E = d.seg.E;
     const int nt = *d.seg.ntiles;
-    const int tb = (int)((long)grp * nt / d.groups), te = (int)((long)(grp + 1) * nt / d.groups);
+    for (int i = threadIdx.x; i < d.max_tiles; i += 64 * W) stiles[i] = d.seg.tiles[i];
+    for (int p = threadIdx.x; p < T * k; p += 64 * W) srow[p] = d.rowinfo[p];
     for (int i = lane; i < 16 * 17; i += 64) (&macc[wave][0][0])[i] = 0.f;
-    // the accumulator is private to the wave (a wave's LDS accesses complete in order)
-    for (int ti = tb + wave; ti < te; ti += W) {
-        const Tile tl = d.seg.tiles[ti];
-        typename ExpertRows<MX>::Mat mats[3];
+    __syncthreads();
+    const int tb = (int)((long)grp * nt / d.groups), te = (int)((long)(grp + 1) * nt / d.groups);
+    const int nmine = te - tb > wave ? (te - tb - wave + W - 1) / W : 0;
+
+    struct Ctx {
+        typename ER::Row rw;
+        const uint16_t* hr;
+        int groups, nch, row0, nrows, seg;
+        bool ok, mx;
+    };
+    auto ctx_of = [&](int i) {
+        const Tile tl = stiles[tb + wave + i * W];
+        typename ER::Mat mats[3];
         int Fseg;
         bool mx;
         segment_mats<MX>(d.experts, d.rec_bytes, d.shared, tl.seg, E, d.F, d.Fs, d.L, mats, Fseg, mx);
-        const f32x4 acc = mx ? dc_tile<CH, MX, MX>(d, tl, mats[2], Fseg, n0) : dc_tile<CH, false, MX>(d, tl, mats[2], Fseg, n0);
-        // lane (kq, j): latent rows n0 + 4 kq + r of segment row j -> its token and weight
-        if (j < tl.nrows) {
-            const int p = tl.row0 + j;
-            int t = -1;
-            float wt = 0.f;
-            if (tl.seg == E) {
-                t = p - T * k;
-                wt = 1.f;
-            } else {
-                const int f = d.seg.perm[p];
-                if (f >= 0) {
-                    t = f / k;
-                    wt = d.w[f];
-                }
-            }
-            if (t >= 0)
+        Ctx c;
+        c.rw = ER::row(mats[2], n0 + j, Fseg);
+        c.hr = d.H + (size_t)(tl.row0 + min(j, tl.nrows - 1)) * d.Hs;
+        c.groups = Fseg / (32 * SPL);
+        c.nch = (c.groups + CH - 1) / CH;
+        c.row0 = tl.row0;
+        c.nrows = tl.nrows;
+        c.seg = tl.seg;
+        c.ok = j < tl.nrows;
+        c.mx = mx;
+        return c;
+    };
+    typedef typename ER::WRaw WR;
+    // every call issues the same number of loads (clamped groups), so the waits stay exact
+    auto load = [&](WR (&w)[CH], uint4 (&h)[CH * SPL], const Ctx& c, int ch) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) macc[wave][t][4 * kq + r] += wt * acc[r];
+        for (int i = 0; i < CH; ++i) {
+            const int gi = min(ch * CH + i, c.groups - 1);
+            w[i] = c.mx ? ER::template load<MX>(c.rw, gi, kq) : ER::template load<false>(c.rw, gi, kq);
+#pragma unroll
+            for (int t = 0; t < SPL; ++t) h[i * SPL + t] = ld16(c.hr + step_k<SPL>(gi * SPL + t, kq));
+        }
+    };
+    auto compute = [&](const WR (&w)[CH], const uint4 (&h)[CH * SPL], const Ctx& c, int ch, f32x4& acc) {
+        if (c.mx) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i)
+                if (ch * CH + i < c.groups)
+#pragma unroll
+                    for (int t = 0; t < SPL; ++t)
+                        acc = mfma16(ER::template frag<MX>(w[i], t), sel4(c.ok, h[i * SPL + t]), acc);
+        } else {
+#pragma unroll
+            for (int i = 0; i < CH; ++i)
+                if (ch * CH + i < c.groups)
+#pragma unroll
+                    for (int t = 0; t < SPL; ++t)
+                        acc = mfma16(ER::template frag<false>(w[i], t), sel4(c.ok, h[i * SPL + t]), acc);
+        }
+    };
+    // lane (kq, j): latent rows n0 + 4 kq + r of segment row j -> its token and weight
+    auto combine = [&](const f32x4& acc, const Ctx& c) {
+        if (!c.ok) return;
+        const int p = c.row0 + j;
+        int t;
+        float wt;
+        if (c.seg == E) {
+            t = p - T * k;
+            wt = 1.f;
+        } else {
+            const int2 ri = srow[p];
+            t = ri.x;
+            wt = __int_as_float(ri.y);
+        }
+        if (t >= 0)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) macc[wave][t][4 * kq + r] += wt * acc[r];
+    };
+
+    if (nmine > 0) {
+        Ctx cur = ctx_of(0), nxt = cur;
+        int i = 0, ch = 0;
+        bool more = true;
+        f32x4 acc = f32x4{};
+        WR wa[CH], wb[CH];
+        uint4 ha[CH * SPL], hb[CH * SPL];
+        // buffers x hold chunk (cur, ch): request the chunk after it into y, then use x
+        auto step = [&](WR (&wx)[CH], uint4 (&hx)[CH * SPL], WR (&wy)[CH], uint4 (&hy)[CH * SPL]) {
+            const bool last = ch + 1 >= cur.nch;
+            const bool next_tile = last && i + 1 < nmine;
+            if (next_tile) nxt = ctx_of(i + 1);
+            // past the wave's last chunk the request repeats the current one (never used)
+            load(wy, hy, next_tile ? nxt : cur, next_tile ? 0 : (last ? ch : ch + 1));
+            compute(wx, hx, cur, ch, acc);
+            if (last) {
+                combine(acc, cur);
+                acc = f32x4{};
+                if (next_tile) {
+                    cur = nxt;
+                    ++i;
+                    ch = 0;
+                } else {
+                    more = false;
+                }
+            } else {
+                ++ch;
+            }
+        };
+        load(wa, ha, cur, 0);
+        while (more) {
+            step(wa, ha, wb, hb);
+            if (!more) break;
+            step(wb, hb, wa, ha);
         }
     }
     __syncthreads();

@@ -238,9 +238,12 @@ __device__ __forceinline__ int bits_below(const uint32_t* bm, int e, int tl) {
     return tl < 32 ? __popc(w0 & ((1u << tl) - 1u)) : __popc(w0) + __popc(w1 & ((1u << (tl - 32)) - 1u));
 }
 
+// rowinfo (optional, with the block's weights w): rowinfo[pos] = (token, weight bits) of the
+// slot placed at pos.
 __device__ void perm_scatter_block(const int32_t* __restrict__ ids, int T, int k, int E, int b, const uint32_t* bm,
                                    const int* seg_base /* per expert: first position for this block */,
-                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv, const float* w = nullptr,
+                                   int2* __restrict__ rowinfo = nullptr) {
     const int t0 = b * kPermTB;
     const int nt = min(kPermTB, T - t0);
     for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
@@ -253,6 +256,7 @@ __device__ void perm_scatter_block(const int32_t* __restrict__ ids, int T, int k
         const int pos = seg_base[e] + bits_below(bm, e, i / k);
         perm[pos] = (int32_t)f;
         inv[f] = pos;
+        if (rowinfo) rowinfo[pos] = make_int2(t0 + i / k, __float_as_int(w[i]));
     }
 }
 
@@ -309,11 +313,13 @@ __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __r
                                                                 int32_t* __restrict__ ids, float* __restrict__ w,
                                                                 int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-                                                                int BM, Tile* tiles, int32_t* ntiles, int has_shared) {
+                                                                int BM, Tile* tiles, int32_t* ntiles, int has_shared,
+                                                                int2* rowinfo) {
     __shared__ uint32_t bm[2 * 1024];
     __shared__ int soff[1024];
     __shared__ int tmp[33];
     __shared__ int32_t sids[64 * 16];
+    __shared__ float sw[64 * 16];
     for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) bm[i] = 0;
     __syncthreads();
     for (int t = threadIdx.x >> 6; t < T; t += 16) {
@@ -325,6 +331,7 @@ __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __r
             ids[(size_t)t * k + pos] = e;
             w[(size_t)t * k + pos] = wt;
             sids[t * k + pos] = e;
+            sw[t * k + pos] = wt;
             atomicOr(&bm[2 * e + (t >> 5)], 1u << (t & 31));
         }
     }
@@ -348,9 +355,12 @@ __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __r
         for (int j = threadIdx.x; j < nsh; j += blockDim.x) tiles[ntot + j] = Tile{E, T * k + j * BM, min(BM, T - j * BM), 0};
         if (threadIdx.x == 0) *ntiles = ntot + nsh;
     }
-    for (int i = nslots + threadIdx.x; i < T * k; i += blockDim.x) perm[i] = -1;
+    for (int i = nslots + threadIdx.x; i < T * k; i += blockDim.x) {
+        perm[i] = -1;
+        if (rowinfo) rowinfo[i] = make_int2(-1, 0);
+    }
     __syncthreads();
-    perm_scatter_block(sids, T, k, E, 0, bm, soff, perm, inv);
+    perm_scatter_block(sids, T, k, E, 0, bm, soff, perm, inv, sw, rowinfo);
 }
 
 __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
@@ -779,9 +789,9 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist
 
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
-                               int32_t* ntiles, int has_shared, hipStream_t s, const float* logits2) {
+                               int32_t* ntiles, int has_shared, hipStream_t s, const float* logits2, int2* rowinfo) {
     if (T > kPermTB) {
-        if (logits2) return hipErrorInvalidValue;  // split logits come from the small-batch launch only
+        if (logits2 || rowinfo) return hipErrorInvalidValue;  // small-batch launch only
         hipError_t e = launch_topk(logits, T, E, k, ids, w, s);
         if (e != hipSuccess) return e;
         return launch_permute(ids, T, k, E, hist, base, offsets, perm, inv, BM, tiles, ntiles, has_shared, s);
@@ -789,7 +799,7 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
     const dim3 g(1), b(1024);
 #define LMOE_TOPK_PERM(NV)                                                                                          \
     hipLaunchKernelGGL(topk_perm_single_kernel<NV>, g, b, 0, s, logits, logits2, T, E, k, ids, w, offsets, perm, inv, BM, \
-                       tiles, ntiles, has_shared)
+                       tiles, ntiles, has_shared, rowinfo)
     if (E <= 64)
         LMOE_TOPK_PERM(1);
     else if (E <= 128)
@@ -831,7 +841,7 @@ template <bool MX>
 hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
     const int nblocks = (int)cdiv(a.Hs, 16);
     DecodeExperts<MX> d{seg,    a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs, a.Hs,
-                        nblocks, a.H,  a.w,       a.mpart,     kDcGroups};
+                        nblocks, a.H,  a.w,       a.mpart,     kDcGroups, a.rowinfo, a.max_tiles};
     const long items = (long)a.max_tiles * nblocks;
     ev.begin(kStageUp);
     const long grid = std::min<long>(cdiv(items, kGuWaves), cu_count());
@@ -841,8 +851,9 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     if (err != hipSuccess) return err;
     ev.end(kStageUp);
     ev.begin(kStageDown);
+    const size_t lds = (size_t)a.max_tiles * sizeof(Tile) + (size_t)a.T * a.k * sizeof(int2);
     hipLaunchKernelGGL((decode_dc_kernel<kDcWaves, (MX ? 1 : kDcChunk), MX>), dim3(a.L / 16, kDcGroups),
-                       dim3(64 * kDcWaves), 0, s, d);
+                       dim3(64 * kDcWaves), lds, s, d);
     if ((err = last()) != hipSuccess) return err;
     ev.end(kStageDown);
     return hipSuccess;

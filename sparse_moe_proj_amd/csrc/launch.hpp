@@ -59,10 +59,12 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist
                           hipStream_t s);
 
 // top-k followed by the permutation; one fused launch when T <= 64.  logits2 (T <= 64 only):
-// a second [T][E] half added to logits (the folded router's lo half).
+// a second [T][E] half added to logits (the folded router's lo half).  rowinfo (T <= 64
+// only): [T*k] (token, weight bits) of the slot at each permuted position, (-1, 0) if none.
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
-                               int32_t* ntiles, int has_shared, hipStream_t s, const float* logits2 = nullptr);
+                               int32_t* ntiles, int has_shared, hipStream_t s, const float* logits2 = nullptr,
+                               int2* rowinfo = nullptr);
 
 // Whether a batch takes the small-batch expert path (gate/up launch, down + merge launch into
 // decode_groups() partial merged rows, summed by the U projection).
@@ -102,6 +104,7 @@ struct ExpertArgs {
     bool mxfp4;
     float* mpart;      // [decode_groups()][T][L] partial merged rows (decode path)
     const float* w;
+    const int2* rowinfo;  // decode path: [T*k] (token, weight bits) per permuted position
 };
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 
