@@ -77,11 +77,10 @@ def algorithmic_counts(wl, ids: np.ndarray):
     rows = T * k + (T if Fs else 0)
     up_bytes = nd * up_w + 2 * Fs * L * wb + T * L * 2 + rows * max(F, Fs) * 2
     up_flops = 2 * (T * k * 2 * F * L + (T * 2 * Fs * L if Fs else 0))
-    # small-batch expert launch (gate/up, SwiGLU and down of every touched expert and the shared
-    # expert): every touched weight once, the latent tokens in, one fp32 latent row out per routed row
-    expert_bytes = nd * rec + 3 * Fs * L * wb + T * L * 2 + rows * L * 4
+    # gate/up launch: the gate and up rows of every touched expert and of the shared expert once,
+    # the latent tokens in, SiLU(g) * u out (bf16, one row of the SwiGLU width per segment row)
     return dict(n_distinct_experts=nd, layer_bytes=layer_bytes, layer_flops=flops_tok * T, up_bytes=up_bytes,
-                up_flops=up_flops, expert_bytes=expert_bytes)
+                up_flops=up_flops)
 
 
 def measure(wl, steps, warmup, rotate, profile_stages=True):
@@ -199,11 +198,11 @@ def cpu_baseline(wl, seconds):
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch of the decode expert kernel from the committed rocprofv3 counter passes
-    (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None when the kernel's sources
-    have changed since the counters were taken or no pass covers this workload."""
+    """HBM bytes per launch of the small-batch gate/up kernel from the committed rocprofv3 counter
+    passes (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None when the kernel's
+    sources have changed since the counters were taken or no pass covers this workload."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{workload}_decode_experts_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{workload}_decode_gu_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -215,11 +214,11 @@ def measured_traffic(workload):
 
 
 def roofline_hbm(counts, up_ms, traffic=None):
-    achieved = counts["expert_bytes"] / (up_ms / 1e3) / 1e9
-    return {"bound": "hbm", "kernel": "decode_experts_kernel (gate/up, SwiGLU, down per F slice)",
+    achieved = counts["up_bytes"] / (up_ms / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": "decode_gu_kernel (expert gate/up and SwiGLU)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "bytes_per_launch": counts["expert_bytes"], "avg_launch_us": round(up_ms * 1e3, 2)}
+            "bytes_per_launch": counts["up_bytes"], "avg_launch_us": round(up_ms * 1e3, 2)}
 
 
 def roofline_mfma(counts, up_ms):
