@@ -368,18 +368,23 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
             return hip_fail(e, "router logits");
         ev.end(LMOE_STAGE_ROUTER);
     }
-    // top-k and permutation (one launch for small batches: the TOPK stage events bracket both)
-    ev.begin(LMOE_STAGE_TOPK);
+    // top-k and permutation: for small batches inside the gate/up launch, else one launch for
+    // T <= 64 (the TOPK stage events bracket both) or several
     const float* logits2 = wt->Gr && lo.fused_router ? logits + (size_t)T * d.E : nullptr;
     int2* rowinfo = lo.decode_path ? static_cast<int2*>(at(lo.rowinfo)) : nullptr;
-    if ((e = launch_topk_permute(logits, T, d.E, d.k, ids, wts, hist, base, offsets, perm, inv, lo.BM, tiles, ntiles,
-                                 has_shared, s, logits2, rowinfo)) != hipSuccess)
-        return hip_fail(e, "top-k / permute");
-    ev.end(LMOE_STAGE_TOPK);
+    const ExpertRoute route{logits, logits2, lo.BM, has_shared, RouteOut{ids, wts, offsets, perm, inv, tiles, ntiles, rowinfo}};
+    const bool route_in_experts = lo.decode_path && kRouteInExperts;
+    if (!route_in_experts) {
+        ev.begin(LMOE_STAGE_TOPK);
+        if ((e = launch_topk_permute(logits, T, d.E, d.k, ids, wts, hist, base, offsets, perm, inv, lo.BM, tiles, ntiles,
+                                     has_shared, s, logits2, rowinfo)) != hipSuccess)
+            return hip_fail(e, "top-k / permute");
+        ev.end(LMOE_STAGE_TOPK);
+    }
     float* mpart = static_cast<float*>(at(lo.mpart));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
                  wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
-                 lo.decode_path, d.mx, mpart, wts, rowinfo};
+                 lo.decode_path, d.mx, mpart, wts, rowinfo, route_in_experts ? &route : nullptr};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     const int umode = o.residual ? 2 : 1;
     const uint16_t* U = static_cast<const uint16_t*>(wt->U);

@@ -23,6 +23,7 @@
 
 #include "gemm_stream.hpp"
 #include "problems.hpp"
+#include "route.hpp"
 
 namespace lmoe {
 
@@ -44,9 +45,10 @@ struct DecodeExperts {
 };
 
 // ---- gate/up ----------------------------------------------------------------------------------
+// tok: the token of this lane's segment row (row0 + min(j, nrows - 1)).
 template <int W, int CH, bool MXR, bool MX>
 __device__ __forceinline__ void gu_item(const DecodeExperts<MX>& d, const Tile& tl, int f0,
-                                        const typename ExpertRows<MX>::Mat (&mats)[3]) {
+                                        const typename ExpertRows<MX>::Mat (&mats)[3], int tok) {
     using ER = ExpertRows<MX>;
     constexpr int SPL = ER::kSPL;
     const int lane = threadIdx.x & 63;
@@ -55,7 +57,6 @@ __device__ __forceinline__ void gu_item(const DecodeExperts<MX>& d, const Tile& 
     const int L = d.L;
     const int nrows = tl.nrows;
     const typename ER::Row rg = ER::row(mats[0], f0 + j, L), ru = ER::row(mats[1], f0 + j, L);
-    const int tok = d.seg.token_of(tl.seg, tl.row0 + min(j, nrows - 1));
     const uint16_t* xr = d.z16 + (size_t)tok * L;
     const bool xok = j < nrows;
     const int groups = L / (32 * SPL);
@@ -100,27 +101,64 @@ __device__ __forceinline__ void gu_item(const DecodeExperts<MX>& d, const Tile& 
     }
 }
 
+// Routing inputs of a gate/up launch that routes the batch itself (small T): every workgroup
+// runs route_block on the logits into LDS (identical results in all of them), and workgroup 0
+// also writes the routing outputs that later launches and the caller read.
+struct GuRoute {
+    const float* logits;   // [T][E] (hi half with a folded router)
+    const float* logits2;  // [T][E] lo half, or null
+    int BM, has_shared;
+    RouteOut out;
+};
+
 // Gate/up work items are (tile, 16-row block of the SwiGLU width), in work-list order with the
 // blocks of a tile adjacent.  The grid holds one workgroup per compute unit (W waves, at most
 // one such workgroup fits a CU) and item i goes to workgroup i % grid, wave (i / grid) % W, so
 // every CU streams the same number of items; blocks past the segment's width are skipped.
-template <int W, int CH, bool MX>
-__global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<MX> d) {
-    const int wave = threadIdx.x >> 6;
-    const int nitems = *d.seg.ntiles * d.nblocks;
+// RNV > 0: the launch routes the batch first (route_block with RNV logits per lane; dynamic LDS
+// holds the work list, max_tiles entries); RNV = 0: the work list comes from global memory.
+template <int W, int CH, bool MX, int RNV>
+__global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<MX> d, const GuRoute r) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15;
+    const int T = d.seg.T, k = d.seg.k;
+    extern __shared__ int4 gdsm[];
+    __shared__ typename std::conditional<(RNV > 0), RouteScratch, int>::type sm;
+    __shared__ int sntiles;
+    Tile* stiles = reinterpret_cast<Tile*>(gdsm);
+    int nt;
+    const Tile* tiles;
+    if constexpr (RNV > 0) {
+        RouteOut out{};
+        if (blockIdx.x == 0) out = r.out;
+        route_block<RNV>(r.logits, r.logits2, T, d.seg.E, k, r.BM, r.has_shared, out, sm, stiles, &sntiles);
+        __syncthreads();
+        nt = sntiles;
+        tiles = stiles;
+    } else {
+        nt = *d.seg.ntiles;
+        tiles = d.seg.tiles;
+    }
+    const int nitems = nt * d.nblocks;
     for (int item = blockIdx.x + gridDim.x * wave; item < nitems; item += gridDim.x * W) {
         const int tile = item / d.nblocks, blk = item - tile * d.nblocks;
-        const Tile tl = d.seg.tiles[tile];
+        const Tile tl = tiles[tile];
         typename ExpertRows<MX>::Mat mats[3];
         int Fseg;
         bool mx;
         segment_mats<MX>(d.experts, d.rec_bytes, d.shared, tl.seg, d.seg.E, d.F, d.Fs, d.L, mats, Fseg, mx);
         const int f0 = blk * 16;
         if (f0 >= Fseg) continue;  // widths are multiples of 16
-        if (mx)
-            gu_item<W, CH, MX, MX>(d, tl, f0, mats);
+        const int p = tl.row0 + min(j, tl.nrows - 1);
+        int tok;
+        if constexpr (RNV > 0)
+            tok = tl.seg == d.seg.E ? p - T * k : sm.stok[p];
         else
-            gu_item<W, CH, false, MX>(d, tl, f0, mats);
+            tok = d.seg.token_of(tl.seg, p);
+        if (mx)
+            gu_item<W, CH, MX, MX>(d, tl, f0, mats, tok);
+        else
+            gu_item<W, CH, false, MX>(d, tl, f0, mats, tok);
     }
 }
 

@@ -7,6 +7,7 @@
 #include "gemm_tile.hpp"
 #include "launch.hpp"
 #include "problems.hpp"
+#include "route.hpp"
 #include "small_proj.hpp"
 
 namespace lmoe {
@@ -14,34 +15,6 @@ namespace lmoe {
 // ==============================================================================================
 // block-wide helpers
 // ==============================================================================================
-
-// Exclusive prefix sum over the block (one value per thread, blockDim a multiple of 64, at
-// most 2048 threads).  tmp needs 33 ints of LDS.  Every thread must call it.
-__device__ int block_excl_scan(int v, int* tmp, int* total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    __syncthreads();
-    if (lane == 63) tmp[w] = x;
-    __syncthreads();
-    if (w == 0) {
-        int t = lane < nw ? tmp[lane] : 0;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(t, o);
-            if (lane >= o) t += y;
-        }
-        if (lane < nw) tmp[lane] = t;
-        if (lane == 63) tmp[32] = t;
-    }
-    __syncthreads();
-    *total = tmp[32];
-    return x - v + (w > 0 ? tmp[w - 1] : 0);
-}
 
 // Sum over the block in a fixed order (wave butterflies, then wave 0..n-1).  red: 16 floats.
 __device__ float block_sum(float v, float* red) {
@@ -70,126 +43,6 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* __restri
     for (int i = threadIdx.x; i < H; i += blockDim.x) x16[(size_t)blockIdx.x * H + i] = (uint16_t)f2bf(row[i] * r);
 }
 
-// ==============================================================================================
-// top-k + softmax over the kept logits, one wave per token.  Lane l holds the logits of ids
-// l, l+64, ... (NV per lane, E <= 64*NV) as order-preserving 32-bit keys.  Each lane sorts its
-// keys in descending order with a stable network (adjacent swaps of strictly smaller keys only,
-// so equal keys keep their ascending-id order); then k rounds take the wave-wide maximum of the
-// lanes' first keys, the winner being the lowest id among equal maxima, and the winning lane
-// drops its first key.  This is "larger value wins, lower id wins a tie".  The kept ids are
-// written in ascending order with softmax weights over their logits.
-// ==============================================================================================
-__device__ __forceinline__ uint32_t order_key(float v) {
-    const uint32_t u = __float_as_uint(v);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_value(uint32_t key) {
-    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
-// Maximum over the wave, returned uniform: DPP within each row of 16 lanes (swap neighbours,
-// swap pairs, rotate by 4, rotate by 8), then the four row maxima through scalar reads.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
-    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
-    return max(max(r0, r1), max(r2, r3));
-}
-
-// Sum over the wave in a fixed order (same DPP tree as wave_max_u32), returned uniform.
-__device__ __forceinline__ float wave_sum_f32(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
-}
-
-// Top k of one token's logits (row of E <= 1024) by one wave.  Lanes 0 .. k-1 return a kept
-// expert as (rank among the kept ids in ascending order) << 16 | id, with its softmax weight;
-// other lanes return -1.
-// row2 (optional): a second half of the logits, added to row (the folded router's lo half).
-template <int NV>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, const float* __restrict__ row2, int E, int k,
-                                          int& out, float& out_w) {
-    const int lane = threadIdx.x & 63;
-    // all loads first (clamped addresses, no branch), so they are in flight together
-    float v[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
-    if (row2) {
-        float v2[NV];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) v2[j] = row2[min(lane + 64 * j, E - 1)];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) v[j] += v2[j];
-    }
-    uint32_t key[NV];
-    int id[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        // NaN counts as -inf (never ahead of a number); ids past E get key 0, below every value
-        const float x = v[j] == v[j] ? v[j] : -INFINITY;
-        key[j] = lane + 64 * j < E ? order_key(x) : 0u;
-        id[j] = lane + 64 * j;
-    }
-    // stable descending sort of the lane's keys (odd-even transposition, strict comparisons)
-#pragma unroll
-    for (int ph = 0; ph < NV; ++ph)
-#pragma unroll
-        for (int j = ph & 1; j + 1 < NV; j += 2) {
-            const bool sw = key[j + 1] > key[j];
-            const uint32_t ka = key[j], kb = key[j + 1];
-            const int ia = id[j], ib = id[j + 1];
-            key[j] = sw ? kb : ka;
-            key[j + 1] = sw ? ka : kb;
-            id[j] = sw ? ib : ia;
-            id[j + 1] = sw ? ia : ib;
-        }
-    uint32_t sel_key = 0;
-    int sel_id = -1;
-#pragma unroll 1
-    for (int r = 0; r < k; ++r) {
-        const uint32_t m = wave_max_u32(key[0]);
-        const uint64_t cand = __ballot(key[0] == m);
-        int win = __ffsll((unsigned long long)cand) - 1;
-        if (__popcll(cand) > 1) {  // equal maxima: the lowest id among the candidates
-            const uint32_t lo = ~wave_max_u32(key[0] == m ? ~(uint32_t)id[0] : 0u);
-            win = __ffsll((unsigned long long)__ballot(key[0] == m && (uint32_t)id[0] == lo)) - 1;
-        }
-        const int wid = __builtin_amdgcn_readlane(id[0], win);
-        if (lane == r) {
-            sel_key = m;
-            sel_id = wid;
-        }
-        if (lane == win) {
-#pragma unroll
-            for (int j = 0; j + 1 < NV; ++j) {
-                key[j] = key[j + 1];
-                id[j] = id[j + 1];
-            }
-            key[NV - 1] = 0u;
-        }
-    }
-    // the first winner holds the largest kept logit; weights over the kept logits
-    const float vmax = key_value((uint32_t)__builtin_amdgcn_readlane((int)sel_key, 0));
-    const float e = lane < k ? expf(key_value(sel_key) - vmax) : 0.f;
-    const float s = wave_sum_f32(e);
-    // rank among the kept ids (distinct), ascending
-    int pos = 0;
-    for (int r = 0; r < k; ++r) pos += __builtin_amdgcn_readlane(sel_id, r) < sel_id ? 1 : 0;
-    out = lane < k ? (pos << 16) | sel_id : -1;
-    out_w = lane < k ? e / s : 0.f;
-}
-
 template <int NV>
 __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids,
                                            float* __restrict__ w) {
@@ -210,14 +63,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     topk_token<NV>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
-// ==============================================================================================
-// Permutation.  Tokens are cut into blocks of 64; inside a block, bit tl of bm[2e + tl/32] marks
-// that token tl chose expert e.  Because a token's ids are distinct, the stable rank of slot
-// (t, s) inside expert e's segment is (slots of e in earlier blocks) + popcount of the bits of
-// earlier tokens of the same block, so no sort is needed and the result is unique.
-// ==============================================================================================
-constexpr int kPermTB = 64;
-
 __device__ void perm_bitmap(const int32_t* __restrict__ ids, int T, int k, int E, int b, uint32_t* bm) {
     const int t0 = b * kPermTB;
     const int nt = min(kPermTB, T - t0);
@@ -231,33 +76,6 @@ __device__ void perm_bitmap(const int32_t* __restrict__ ids, int T, int k, int E
         }
     }
     __syncthreads();
-}
-
-__device__ __forceinline__ int bits_below(const uint32_t* bm, int e, int tl) {
-    const uint32_t w0 = bm[2 * e], w1 = bm[2 * e + 1];
-    return tl < 32 ? __popc(w0 & ((1u << tl) - 1u)) : __popc(w0) + __popc(w1 & ((1u << (tl - 32)) - 1u));
-}
-
-// rowinfo (optional, with the block's weights w): rowinfo[pos] = (token, weight bits) of the
-// slot placed at pos.
-__device__ void perm_scatter_block(const int32_t* __restrict__ ids, int T, int k, int E, int b, const uint32_t* bm,
-                                   const int* seg_base /* per expert: first position for this block */,
-                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv, const float* w = nullptr,
-                                   int2* __restrict__ rowinfo = nullptr) {
-    const int t0 = b * kPermTB;
-    const int nt = min(kPermTB, T - t0);
-    for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
-        const size_t f = (size_t)t0 * k + i;
-        const int e = ids[f];
-        if (e < 0 || e >= E) {
-            inv[f] = -1;
-            continue;
-        }
-        const int pos = seg_base[e] + bits_below(bm, e, i / k);
-        perm[pos] = (int32_t)f;
-        inv[f] = pos;
-        if (rowinfo) rowinfo[pos] = make_int2(t0 + i / k, __float_as_int(w[i]));
-    }
 }
 
 // Work list of <= BM-row tiles: routed segments in expert order, then the shared segment.
@@ -302,11 +120,7 @@ __global__ __launch_bounds__(1024) void perm_single_kernel(const int32_t* __rest
     perm_single_body(ids, T, k, E, offsets, perm, inv, BM, tiles, ntiles, has_shared, bm, soff, tmp);
 }
 
-// Routing and permutation of a small batch (T <= 64) in one workgroup of 16 waves: each wave
-// selects the experts of its tokens and marks them in the per-expert token bitmaps; one block
-// scan of (count | tiles << 16) per expert then gives the segment offsets and the work-list
-// positions together (counts <= 1024 and tile counts <= 1024 never carry into each other), and
-// every slot is placed at its stable rank (earlier tokens first) inside its expert's segment.
+// Routing and permutation of a small batch (T <= 64) in one workgroup (route_block).
 template <int NV>
 __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __restrict__ logits,
                                                                 const float* __restrict__ logits2, int T, int E, int k,
@@ -315,52 +129,9 @@ __global__ __launch_bounds__(1024) void topk_perm_single_kernel(const float* __r
                                                                 int32_t* __restrict__ perm, int32_t* __restrict__ inv,
                                                                 int BM, Tile* tiles, int32_t* ntiles, int has_shared,
                                                                 int2* rowinfo) {
-    __shared__ uint32_t bm[2 * 1024];
-    __shared__ int soff[1024];
-    __shared__ int tmp[33];
-    __shared__ int32_t sids[64 * 16];
-    __shared__ float sw[64 * 16];
-    for (int i = threadIdx.x; i < 2 * E; i += blockDim.x) bm[i] = 0;
-    __syncthreads();
-    for (int t = threadIdx.x >> 6; t < T; t += 16) {
-        int pid;
-        float wt;
-        wave_topk<NV>(logits + (size_t)t * E, logits2 ? logits2 + (size_t)t * E : nullptr, E, k, pid, wt);
-        if (pid >= 0) {
-            const int pos = pid >> 16, e = pid & 0xffff;
-            ids[(size_t)t * k + pos] = e;
-            w[(size_t)t * k + pos] = wt;
-            sids[t * k + pos] = e;
-            sw[t * k + pos] = wt;
-            atomicOr(&bm[2 * e + (t >> 5)], 1u << (t & 31));
-        }
-    }
-    __syncthreads();
-    const int e = threadIdx.x;
-    const int cnt = e < E ? __popc(bm[2 * e]) + __popc(bm[2 * e + 1]) : 0;
-    const int nt = (cnt + BM - 1) / BM;
-    int total;
-    const int packed = block_excl_scan(cnt | (nt << 16), tmp, &total);
-    const int off = packed & 0xffff, ts = packed >> 16;
-    const int nslots = total & 0xffff, ntot = total >> 16;
-    if (e < E) {
-        offsets[e] = off;
-        soff[e] = off;
-        if (tiles)
-            for (int j = 0; j < nt; ++j) tiles[ts + j] = Tile{e, off + j * BM, min(BM, cnt - j * BM), 0};
-    }
-    if (e == 0) offsets[E] = nslots;
-    if (tiles) {
-        const int nsh = has_shared ? (T + BM - 1) / BM : 0;
-        for (int j = threadIdx.x; j < nsh; j += blockDim.x) tiles[ntot + j] = Tile{E, T * k + j * BM, min(BM, T - j * BM), 0};
-        if (threadIdx.x == 0) *ntiles = ntot + nsh;
-    }
-    for (int i = nslots + threadIdx.x; i < T * k; i += blockDim.x) {
-        perm[i] = -1;
-        if (rowinfo) rowinfo[i] = make_int2(-1, 0);
-    }
-    __syncthreads();
-    perm_scatter_block(sids, T, k, E, 0, bm, soff, perm, inv, sw, rowinfo);
+    __shared__ RouteScratch sm;
+    route_block<NV>(logits, logits2, T, E, k, BM, has_shared, RouteOut{ids, w, offsets, perm, inv, tiles, ntiles, rowinfo},
+                    sm, nullptr, nullptr);
 }
 
 __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
@@ -844,9 +615,29 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
                         nblocks, a.H,  a.w,       a.mpart,     kDcGroups, a.rowinfo, a.max_tiles};
     const long items = (long)a.max_tiles * nblocks;
     ev.begin(kStageUp);
-    const long grid = std::min<long>(cdiv(items, kGuWaves), cu_count());
-    hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, (MX ? 1 : kGuChunk), MX>), dim3((unsigned)std::max<long>(grid, 1)),
-                       dim3(64 * kGuWaves), 0, s, d);
+    const long grid = std::max<long>(std::min<long>(cdiv(items, kGuWaves), cu_count()), 1);
+    if (a.route) {  // the launch routes the batch itself (top-k and permutation in every workgroup)
+        const GuRoute r{a.route->logits, a.route->logits2, a.route->BM, a.route->has_shared, a.route->out};
+        const size_t lds = (size_t)a.max_tiles * sizeof(Tile);
+        const int E = a.E;
+#define LMOE_GU_ROUTED(NV)                                                                                          \
+    hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, (MX ? 1 : kGuChunk), MX, NV>), dim3((unsigned)grid),            \
+                       dim3(64 * kGuWaves), lds, s, d, r)
+        if (E <= 64)
+            LMOE_GU_ROUTED(1);
+        else if (E <= 128)
+            LMOE_GU_ROUTED(2);
+        else if (E <= 256)
+            LMOE_GU_ROUTED(4);
+        else if (E <= 512)
+            LMOE_GU_ROUTED(8);
+        else
+            LMOE_GU_ROUTED(16);
+#undef LMOE_GU_ROUTED
+    } else {
+        hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, (MX ? 1 : kGuChunk), MX, 0>), dim3((unsigned)grid),
+                           dim3(64 * kGuWaves), 0, s, d, GuRoute{});
+    }
     hipError_t err = last();
     if (err != hipSuccess) return err;
     ev.end(kStageUp);

@@ -11,6 +11,20 @@ namespace lmoe {
 
 struct Tile;
 
+// Outputs of the routing of a batch (each may be null): ids/w [T][k], offsets [E+1], perm/inv
+// [T*k], the tile work list and its length, and rowinfo [T*k] = (token, weight bits) of the slot
+// at each permuted position ((-1, 0) if none).
+struct RouteOut {
+    int32_t* ids;
+    float* w;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* inv;
+    Tile* tiles;
+    int32_t* ntiles;
+    int2* rowinfo;
+};
+
 // Optional per-stage event records (the lmoe_forward_opts.stage_events hook).
 struct StageEvents {
     void* const* ev;
@@ -37,6 +51,12 @@ constexpr int kStageUp = 5, kStageDown = 6, kStageCombine = 7;  // LMOE_STAGE_EX
 
 // Batches of at most this many tokens use the weight-streaming (decode) kernels.
 constexpr int kStreamMaxT = 16;
+
+#ifndef LMOE_ROUTE_IN_EXPERTS
+#define LMOE_ROUTE_IN_EXPERTS 1
+#endif
+// Small batches: route inside the gate/up launch (one dependent launch fewer).
+constexpr bool kRouteInExperts = LMOE_ROUTE_IN_EXPERTS != 0;
 
 hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream_t s);
 
@@ -87,6 +107,15 @@ hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, in
 int expert_tile_rows(bool stream_path);
 int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path);
 
+// Routing done inside the small-batch gate/up launch (T <= 64): the logits (hi half, and the lo
+// half of a folded router or null) and where the routing outputs go.
+struct ExpertRoute {
+    const float* logits;
+    const float* logits2;
+    int BM, has_shared;
+    RouteOut out;
+};
+
 struct ExpertArgs {
     const Tile* tiles;
     const int32_t* ntiles;
@@ -105,6 +134,7 @@ struct ExpertArgs {
     float* mpart;      // [decode_groups()][T][L] partial merged rows (decode path)
     const float* w;
     const int2* rowinfo;  // decode path: [T*k] (token, weight bits) per permuted position
+    const ExpertRoute* route;  // decode path: non-null = route inside the gate/up launch
 };
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 
