@@ -61,10 +61,11 @@ class Hip:
         return ms.value
 
 
-def algorithmic_counts(wl, ids: np.ndarray):
+def algorithmic_counts(wl, ids: np.ndarray, T=None):
     """Bytes and flops the method itself needs for one layer step, from the step's own routing."""
     s = wl.shape
-    T, H, L, E, k, F, Fs = wl.T, s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn
+    T = wl.T if T is None else T
+    H, L, E, k, F, Fs = s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn
     nd = int(np.unique(ids).size)
     wb = 2  # bf16 dense weights
     rec = s.mxfp4_record_bytes() if wl.expert == "mxfp4" else 3 * F * L * 2
@@ -83,22 +84,34 @@ def algorithmic_counts(wl, ids: np.ndarray):
                 up_flops=up_flops)
 
 
-def measure(wl, steps, warmup, rotate, profile_stages=True):
-    import torch
-
+def layer_copies(wl, rotate):
+    """`rotate` byte-identical device copies of the workload's layer 0."""
     import lmoe_data as gen
-    import sparse_moe_proj_amd as lm
-    from sparse_moe_proj_amd.device import DeviceLayer, Workspace, to_device
+    from sparse_moe_proj_amd.device import DeviceLayer
 
-    hip = Hip()
     t0 = time.time()
     lw = gen.make_layer(wl, 0)
     log(f"[bench] {wl.name}: generated layer in {time.time() - t0:.1f}s")
     base = DeviceLayer(lw, act=wl.act)
     del lw
-    copies = [base] + [base.clone() for _ in range(rotate - 1)]
-    x = to_device(gen.make_tokens(wl))
-    T = wl.T
+    return [base] + [base.clone() for _ in range(rotate - 1)]
+
+
+def measure(wl, steps, warmup, rotate, profile_stages=True, copies=None, T=None, graphs=True):
+    """Times `steps` forward steps of T tokens (default: the workload's T) over the weight copies."""
+    import torch
+
+    import lmoe_data as gen
+    import sparse_moe_proj_amd as lm
+    from sparse_moe_proj_amd.device import Workspace, to_device
+
+    hip = Hip()
+    if copies is None:
+        copies = layer_copies(wl, rotate)
+    rotate = len(copies)
+    base = copies[0]
+    T = wl.T if T is None else T
+    x = to_device(gen.make_tokens(wl, T=T))
     y = torch.empty((T, wl.shape.hidden), dtype=torch.int16, device="cuda")
     ids = torch.empty((T, wl.shape.top_k), dtype=torch.int32, device="cuda")
     nbytes = lm.lmoe_workspace_bytes(base.cfg, T)
@@ -109,7 +122,7 @@ def measure(wl, steps, warmup, rotate, profile_stages=True):
 
     fwd(base, lm.make_opts(aux_ids=ids))
     torch.cuda.synchronize()
-    counts = algorithmic_counts(wl, ids.cpu().numpy())
+    counts = algorithmic_counts(wl, ids.cpu().numpy(), T)
     for i in range(warmup):
         fwd(copies[i % rotate])
     torch.cuda.synchronize()
@@ -150,6 +163,9 @@ def measure(wl, steps, warmup, rotate, profile_stages=True):
     ms_per_step = 1e3 * (t_end - t_start) / steps
     up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev_pairs]))
 
+    if not graphs:
+        return dict(ms_per_step=ms_per_step, tok_s=T / (ms_per_step / 1e3), up_ms=up_ms, counts=counts,
+                    stages_us=stages_us, weight_bytes_per_copy=base.nbytes(), graph_ms_per_step=None)
     # the same steps replayed from captured HIP graphs (one per weight copy), for comparison
     graphs = []
     for r in range(rotate):
@@ -241,6 +257,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (calibrates HBM traffic counters)")
+    ap.add_argument("--tsweep", default="",
+                    help="comma-separated token counts: also time the workload's layer at each T (a 'tsweep' list)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the latent-MoE block is built and measured on a single MI355X "
@@ -253,7 +271,8 @@ def main():
     torch.cuda.set_device(0)
     wl = gen.WORKLOADS[args.workload]
     assert wl.layers == 1, "the stack workload is measured by its own test"
-    m = measure(wl, args.steps, args.warmup, args.rotate)
+    copies = layer_copies(wl, args.rotate)
+    m = measure(wl, args.steps, args.warmup, args.rotate, copies=copies)
     c = m["counts"]
     mfma_bound = c["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > c["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
     rl = roofline_mfma(c, m["up_ms"]) if mfma_bound else roofline_hbm(c, m["up_ms"], measured_traffic(wl.name))
@@ -282,6 +301,20 @@ def main():
         "stages_us": m["stages_us"],
         "graph_ms_per_step": round(m["graph_ms_per_step"], 5),
     }
+    if args.tsweep:
+        sweep = []
+        for T in [int(v) for v in args.tsweep.split(",") if v]:
+            mt = measure(wl, args.steps, args.warmup, args.rotate, profile_stages=False, copies=copies, T=T,
+                         graphs=False)
+            ct = mt["counts"]
+            sweep.append({"T": T, "tok_s": round(mt["tok_s"], 1), "us_per_step": round(1e3 * mt["ms_per_step"], 2),
+                          "n_distinct_experts": ct["n_distinct_experts"],
+                          "layer_hbm_frac": round(ct["layer_bytes"] / (mt["ms_per_step"] / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
+                          "gate_up_us": round(1e3 * mt["up_ms"], 2),
+                          "gate_up_gbs": round(ct["up_bytes"] / (mt["up_ms"] / 1e3) / 1e9, 1)})
+            log(f"[bench] tsweep {sweep[-1]}")
+        out["tsweep"] = sweep
+    del copies
     if args.secondary:
         del m
         torch.cuda.empty_cache()

@@ -60,6 +60,9 @@ class Shape:
 
 TINY = Shape(hidden=256, latent=128, n_experts=16, top_k=2, ffn=64, shared_ffn=64)
 EDGE0_145B = Shape(hidden=2560, latent=1792, n_experts=512, top_k=10, ffn=640, shared_ffn=640)
+# The 120B model: the pages give only its latent width (1280); the other dimensions are read as
+# the 145B's (same family, same expert pool layout).
+EDGE0_120B = Shape(hidden=2560, latent=1280, n_experts=512, top_k=10, ffn=640, shared_ffn=640)
 
 
 @dataclass(frozen=True)
@@ -84,6 +87,7 @@ WORKLOADS = {
     "prefill_t16384": Workload(4, "prefill_t16384", EDGE0_145B, 16384, "bf16", "bf16", "bf16", "zipf"),
     "stack48_mxfp4_t8": Workload(5, "stack48_mxfp4_t8", EDGE0_145B, 8, "bf16", "bf16", "mxfp4", "zipf",
                                  layers=48, expert_banks=2),
+    "decode120_t8": Workload(6, "decode120_t8", EDGE0_120B, 8, "bf16", "bf16", "bf16", "zipf"),
 }
 
 

@@ -85,9 +85,9 @@ Layout plan(const Dims& d, int T) {
     Layout lo{};
     const size_t act = d.f32 ? 4 : 2;
     const int has_shared = d.Fs > 0;
-    lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx);
     lo.decode_path = !d.f32 && decode_fits(T, d.L, d.F, d.Fs);
-    lo.fused_router = !d.f32 && T <= kStreamMaxT && small_proj_fits(T, d.H);
+    lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx || lo.decode_path);
+    lo.fused_router = !d.f32 && small_proj_fits(T, d.H);
     lo.BM = expert_tile_rows(lo.stream_path);
     lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path);
     lo.Hs = std::max(d.F, d.Fs);
@@ -201,7 +201,8 @@ lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* byte
     if (!bytes) return fail(LMOE_ERR_NULL, "bytes is NULL");
     // the small-batch partials can exceed what a slightly larger batch needs: report the maximum
     // over every T' <= T so that one workspace sized for a largest batch serves all smaller ones
-    *bytes = std::max(plan(d, T).total, plan(d, std::min<int32_t>(T, kStreamMaxT)).total);
+    *bytes = std::max({plan(d, T).total, plan(d, std::min<int32_t>(T, kStreamMaxT)).total,
+                       plan(d, std::min<int32_t>(T, kDecodeMaxT)).total});
     return LMOE_OK;
 }
 

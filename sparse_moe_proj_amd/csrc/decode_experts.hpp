@@ -1,4 +1,4 @@
-// Expert work of a small batch (decode / speculative verify, T <= 16 tokens) in two launches
+// Expert work of a small batch (decode / speculative verify, T <= 64 tokens) in two launches
 // with no dependency between workgroups inside either launch.
 //
 // 1. Gate/up (decode_gu_kernel).  A work item is (tile, block): the tile's tokens (<= 16 rows of
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<M
     using ER = ExpertRows<MX>;
     constexpr int SPL = ER::kSPL;
     extern __shared__ int4 dsm[];
-    __shared__ float macc[W][16][17];  // per wave: [token][latent row of the block] (+1 pad)
+    __shared__ float macc[W][kDecodeMaxT][17];  // per wave: [token][latent row of the block] (+1 pad)
     Tile* stiles = reinterpret_cast<Tile*>(dsm);
     int2* srow = reinterpret_cast<int2*>(dsm + d.max_tiles);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<M
     const int nt = *d.seg.ntiles;
     for (int i = threadIdx.x; i < d.max_tiles; i += 64 * W) stiles[i] = d.seg.tiles[i];
     for (int p = threadIdx.x; p < T * k; p += 64 * W) srow[p] = d.rowinfo[p];
-    for (int i = lane; i < 16 * 17; i += 64) (&macc[wave][0][0])[i] = 0.f;
+    for (int i = lane; i < T * 17; i += 64) (&macc[wave][0][0])[i] = 0.f;
     __syncthreads();
     const int tb = (int)((long)grp * nt / d.groups), te = (int)((long)(grp + 1) * nt / d.groups);
     const int nmine = te - tb > wave ? (te - tb - wave + W - 1) / W : 0;
@@ -297,9 +297,9 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<M
     }
     __syncthreads();
     // thread e: token e / 16, latent row n0 + e % 16; the waves' sums in wave order
-    for (int e = threadIdx.x; e < 256; e += 64 * W) {
+    for (int e = threadIdx.x; e < 16 * T; e += 64 * W) {
         const int t = e >> 4, r = e & 15;
-        if (t < T) {
+        {
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < W; ++w) s += macc[w][t][r];

@@ -448,20 +448,19 @@ hipError_t small_proj_launch(const SmallProj& p, hipStream_t s) {
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k, dim3((unsigned)cdiv(p.N, 16)), dim3(64 * LMOE_SP_WAVES), small_proj_lds(p.T, p.K), s, p);
+    hipLaunchKernelGGL(k, dim3((unsigned)cdiv(p.N, 16)), dim3(64 * LMOE_SP_WAVES), small_proj_lds(p.K), s, p);
     return last();
 }
 
 hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const uint16_t* Gr, const float* br, int T,
                                   int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s) {
-    if (T > kStreamMaxT || small_proj_lds(T, H) > kSmallProjLds) return hipErrorInvalidValue;
+    if (!small_proj_fits(T, H)) return hipErrorInvalidValue;
     SmallProj p{x, nullptr, 0, D, T, L, H, 0, z32, z16, Gr, br, E, logits};
     auto k = small_proj_kernel<LMOE_SP_WAVES, LMOE_SP_SMAX, 0>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k, dim3((unsigned)(cdiv(L, 16) + 2 * cdiv(E, 16))), dim3(64 * LMOE_SP_WAVES), small_proj_lds(T, H), s,
-                       p);
+    hipLaunchKernelGGL(k, dim3((unsigned)(cdiv(L, 16) + 2 * cdiv(E, 16))), dim3(64 * LMOE_SP_WAVES), small_proj_lds(H), s, p);
     return last();
 }
 
@@ -486,13 +485,13 @@ hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int 
 
 hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                                 uint16_t* out16, hipStream_t s) {
-    if (T > kStreamMaxT || small_proj_lds(T, K) > kSmallProjLds) return hipErrorInvalidValue;
+    if (!small_proj_fits(T, K)) return hipErrorInvalidValue;
     return small_proj_launch<1>(SmallProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16}, s);
 }
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                             uint16_t* out16, hipStream_t s, uint16_t* out16lo) {
-    if (T <= kStreamMaxT && small_proj_lds(T, K) <= kSmallProjLds)
+    if (T <= kStreamMaxT && small_proj_fits(T, K))
         return small_proj_launch<0>(SmallProj{x, nullptr, 0, W, T, N, K, mode, out32, out16}, s);
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1, StreamProj, kProjChunk>(StreamProj{x, W, T, N, K, mode, out32, out16},
@@ -601,11 +600,13 @@ constexpr int kDcWaves = LMOE_DC_WAVES, kDcChunk = LMOE_DC_CHUNK, kDcGroups = LM
 
 int decode_groups() { return kDcGroups; }
 
-bool small_proj_fits(int T, int K) { return T <= kStreamMaxT && small_proj_lds(T, K) <= kSmallProjLds; }
+static_assert(16 * kSmallProjGroups >= kDecodeMaxT, "small-batch projections take every decode-path batch");
+
+bool small_proj_fits(int T, int K) { return T <= 16 * kSmallProjGroups && small_proj_lds(K) <= kSmallProjLds; }
 
 bool decode_fits(int T, int L, int F, int Fs) {
     // widths in whole 16-row blocks (a gate/up slice may end inside a segment); U stages its input in LDS
-    return T <= kStreamMaxT && F % 16 == 0 && Fs % 16 == 0 && small_proj_lds(T, L) <= kSmallProjLds;
+    return T <= kDecodeMaxT && F % 16 == 0 && Fs % 16 == 0 && small_proj_fits(T, L);
 }
 
 template <bool MX>

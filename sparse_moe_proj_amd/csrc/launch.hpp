@@ -51,6 +51,9 @@ constexpr int kStageUp = 5, kStageDown = 6, kStageCombine = 7;  // LMOE_STAGE_EX
 
 // Batches of at most this many tokens use the weight-streaming (decode) kernels.
 constexpr int kStreamMaxT = 16;
+// Batches of at most this many tokens take the small-batch expert path (two streaming launches)
+// and, with a folded router, the small-batch projections.
+constexpr int kDecodeMaxT = 64;
 
 #ifndef LMOE_ROUTE_IN_EXPERTS
 #define LMOE_ROUTE_IN_EXPERTS 1

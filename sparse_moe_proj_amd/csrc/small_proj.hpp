@@ -1,11 +1,12 @@
-// Dense projection of a small batch (T <= 16 tokens): out[t][n] = sum_k x[t][k] * W[n][k].
+// Dense projection of a small batch (T <= 64 tokens): out[t][n] = sum_k x[t][k] * W[n][k].
 //
 // The work is reading W once from HBM.  A workgroup owns 16 weight rows; its W waves split K
 // into contiguous ranges and each wave requests all weight units of its range (up to SMAX MFMA
 // steps at a time) before anything else, so the whole range is in flight at once.  While those
-// loads travel, the workgroup stages the activations into LDS as bf16 (XM = 0: a bf16 [T][K]
+// loads travel, the workgroup stages the activations of the first 16 tokens into LDS as bf16 (XM = 0: a bf16 [T][K]
 // input; XM = 1: the sum, in order, of G fp32 partial inputs [G][T][K], rounded once), so the
-// token operand is read from LDS rather than once per wave from L2.  The MFMA is
+// token operand is read from LDS rather than once per wave from L2.  Further groups of 16 tokens
+// are staged in turn and reuse the weights held in registers.  The MFMA is
 // v_mfma_f32_16x16x32_bf16 with the weights as A (16 rows) and the tokens as B (columns past T
 // are zero).  The waves' partial tiles meet in LDS and are summed in wave order.  A second
 // product over the same input (the two halves of the folded router) can share the launch.
@@ -36,12 +37,16 @@ struct SmallProj {
 // Largest staged-activation LDS a small-batch projection takes (plus W KB of static LDS).
 constexpr size_t kSmallProjLds = 128 * 1024;
 
-// LDS bytes of the staged activations: T rows of K/8 16-byte units plus one unit of padding.
-__host__ __device__ inline size_t small_proj_lds(int T, int K) { return (size_t)T * (K / 8 + 1) * 16; }
+// Token groups of 16 (the MFMA's token columns) a launch takes: T <= 16 * kSmallProjGroups.
+constexpr int kSmallProjGroups = 4;
+
+// LDS bytes of the staged activations: one token group, 16 rows of K/8 16-byte units plus one
+// unit of padding per row.
+__host__ __device__ inline size_t small_proj_lds(int K) { return (size_t)16 * (K / 8 + 1) * 16; }
 
 template <int W, int SMAX, int XM>
 __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
-    extern __shared__ uint4 xs[];  // [T][K / 8 + 1]
+    extern __shared__ uint4 xs[];  // [16][K / 8 + 1]: the current token group
     __shared__ float red[W][256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = lane >> 4, j = lane & 15;
@@ -63,68 +68,81 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
             if (b + i < s1) wv[i] = ld16(wrow + (b + i) * 32 + kq * 8);
     };
     if (s0 < s1) loadw(s0);
+    // a wave's whole K range fits in the registers: every token group reuses the same weights
+    const bool single = s1 - s0 <= SMAX;
     const int per = K / 8, xst = per + 1;
-    for (int e = threadIdx.x; e < T * per; e += 64 * W) {
-        const int t = e / per, c = e - t * per;
-        uint4 v;
-        if constexpr (XM == 0) {
-            v = ld16(p.x16 + (size_t)t * K + c * 8);
-        } else {
-            float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int g = 0; g < p.G; ++g) {
-                const float* src = p.xpart + ((size_t)g * T + t) * K + c * 8;
-                const float4 u0 = *reinterpret_cast<const float4*>(src);
-                const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
-                a[0] += u0.x;
-                a[1] += u0.y;
-                a[2] += u0.z;
-                a[3] += u0.w;
-                a[4] += u1.x;
-                a[5] += u1.y;
-                a[6] += u1.z;
-                a[7] += u1.w;
+    const int ngroups = (T + 15) / 16;
+    static_for<kSmallProjGroups>([&](auto G) {
+        constexpr int g = decltype(G)::value;
+        if (g < ngroups) {
+            const int t0 = 16 * g, tn = min(16, T - t0);
+            if (g > 0) {
+                __syncthreads();  // the previous group's LDS reads are done
+                if (!single && s0 < s1) loadw(s0);
             }
-            v = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
-        }
-        xs[t * xst + c] = v;
-    }
-    __syncthreads();
-    f32x4 acc = f32x4{};
-    const bool tok = j < T;
-    for (int b = s0; b < s1; b += SMAX) {
-        if (b != s0) loadw(b);
-#pragma unroll
-        for (int i = 0; i < SMAX; ++i)
-            if (b + i < s1) {
-                const uint4 xv = tok ? xs[j * xst + (b + i) * 4 + kq] : zero4();
-                acc = mfma16(wv[i], xv, acc);
+            for (int e = threadIdx.x; e < tn * per; e += 64 * W) {
+                const int t = e / per, c = e - t * per;
+                uint4 v;
+                if constexpr (XM == 0) {
+                    v = ld16(p.x16 + (size_t)(t0 + t) * K + c * 8);
+                } else {
+                    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                    for (int q = 0; q < p.G; ++q) {
+                        const float* src = p.xpart + ((size_t)q * T + t0 + t) * K + c * 8;
+                        const float4 u0 = *reinterpret_cast<const float4*>(src);
+                        const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+                        a[0] += u0.x;
+                        a[1] += u0.y;
+                        a[2] += u0.z;
+                        a[3] += u0.w;
+                        a[4] += u1.x;
+                        a[5] += u1.y;
+                        a[6] += u1.z;
+                        a[7] += u1.w;
+                    }
+                    v = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
+                }
+                xs[t * xst + c] = v;
             }
-    }
-    // lane (kq, j): rows n0 + 4 kq + r, token j
+            __syncthreads();
+            f32x4 acc = f32x4{};
+            const bool tok = j < tn;
+            for (int b = s0; b < s1; b += SMAX) {
+                if (b != s0) loadw(b);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][(4 * kq + r) * 16 + j] = acc[r];
-    __syncthreads();
-    // thread e: token e / 16, row n0 + e % 16 (16 consecutive outputs of a token per 16 threads)
-    for (int e = threadIdx.x; e < 256; e += 64 * W) {
-        const int t = e >> 4, r = e & 15, n = n0 + r;
-        if (t >= T || n >= nrow) continue;
-        float v = 0.f;
+                for (int i = 0; i < SMAX; ++i)
+                    if (b + i < s1) {
+                        const uint4 xv = tok ? xs[j * xst + (b + i) * 4 + kq] : zero4();
+                        acc = mfma16(wv[i], xv, acc);
+                    }
+            }
+            // lane (kq, j): rows n0 + 4 kq + r, token t0 + j
 #pragma unroll
-        for (int w = 0; w < W; ++w) v += red[w][r * 16 + t];
-        if (rt) {
-            p.logits[((size_t)half * T + t) * p.E + n] = half == 0 && p.bias ? v + p.bias[n] : v;
-            continue;
+            for (int r = 0; r < 4; ++r) red[wave][(4 * kq + r) * 16 + j] = acc[r];
+            __syncthreads();
+            // thread e: token t0 + e / 16, row n0 + e % 16 (16 consecutive outputs of a token)
+            for (int e = threadIdx.x; e < 256; e += 64 * W) {
+                const int t = e >> 4, r = e & 15, n = n0 + r;
+                if (t >= tn || n >= nrow) continue;
+                float v = 0.f;
+#pragma unroll
+                for (int w = 0; w < W; ++w) v += red[w][r * 16 + t];
+                if (rt) {
+                    p.logits[((size_t)half * T + t0 + t) * p.E + n] = half == 0 && p.bias ? v + p.bias[n] : v;
+                    continue;
+                }
+                const size_t o = (size_t)(t0 + t) * p.N + n;
+                if (p.mode == 0) {
+                    p.out32[o] = v;
+                    p.out16[o] = (uint16_t)f2bf(v);
+                } else if (p.mode == 1) {
+                    p.out16[o] = (uint16_t)f2bf(v);
+                } else {
+                    p.out32[o] += v;
+                }
+            }
         }
-        const size_t o = (size_t)t * p.N + n;
-        if (p.mode == 0) {
-            p.out32[o] = v;
-            p.out16[o] = (uint16_t)f2bf(v);
-        } else if (p.mode == 1) {
-            p.out16[o] = (uint16_t)f2bf(v);
-        } else {
-            p.out32[o] += v;
-        }
-    }
+    });
 }
 
 }  // namespace lmoe

@@ -1,6 +1,6 @@
 """GPU parity of the HIP path (through the C ABI) against the CPU oracle.
 
-Covers the five workloads at full size (routing and permutation on every token, outputs on
+Covers the six workloads at full size (routing and permutation on every token, outputs on
 every token up to T=8 and on sampled tokens beyond), plus small shapes that exercise ragged
 tiles, both kernel paths, MXFP4 records, no shared expert, E == k and E == k == 1.
 """
@@ -41,6 +41,25 @@ def test_tiny_f32_full(ws):
 
 def test_decode_t8_full(ws):
     _workload_case("decode_t8", 8, ws)
+
+
+@pytest.fixture(scope="module")
+def layer120():
+    wl = gen.WORKLOADS["decode120_t8"]
+    log("[decode120_t8] generating layer")
+    lw = gen.make_layer(wl, 0)
+    return wl, lw, DeviceLayer(lw, act=wl.act)
+
+
+@pytest.mark.parametrize("T", [8, 1, 3, 16, 33, 64])
+def test_120b_verify_batches(T, ws, layer120):
+    """The 120B latent width (1280) over a sweep of verify-batch sizes (both small-batch paths and
+    the tile path); T = 8 is the workload's own batch."""
+    wl, lw, dl = layer120
+    x = gen.make_tokens(wl) if T == wl.T else gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, wl.act, out, label=f"decode120 T={T}")
 
 
 @pytest.mark.timeout(600)

@@ -359,6 +359,16 @@ def test_page_shapes_pin_the_edge0_block():
     assert round(pool / 1e9, 1) == g["expert_pool_params_billions"]["value"]
 
 
+def test_page_shapes_pin_the_120b_latent_width():
+    with open(os.path.join(HERE, "golden", "page_shapes.json")) as f:
+        g = json.load(f)
+    assert gen.EDGE0_120B.latent == g["latent_width_120b"]["value"]
+    assert gen.EDGE0_145B.latent == g["latent_width_145b_article"]["value"]
+    # the other dimensions are read as the 145B's (the pages give none for the 120B)
+    a, b = gen.EDGE0_120B, gen.EDGE0_145B
+    assert (a.hidden, a.n_experts, a.top_k, a.ffn, a.shared_ffn) == (b.hidden, b.n_experts, b.top_k, b.ffn, b.shared_ffn)
+
+
 @pytest.mark.parametrize("wid", ["tiny_f32", "decode_t8"])
 def test_generator_is_seed_stable(wid):
     wl = gen.WORKLOADS[wid]
