@@ -111,13 +111,15 @@ typedef struct {
 /* Stages of lmoe_forward, in launch order (for lmoe_forward_opts.stage_events). */
 typedef enum {
     LMOE_STAGE_PRENORM = 0,     /* RMSNorm of the fp32 residual into the bf16 block input */
-    LMOE_STAGE_D = 1,           /* z = x D^T (with weights->Gr and T <= 16, also the logits) */
+    LMOE_STAGE_D = 1,           /* z = x D^T (with weights->Gr and T <= 64, also the logits) */
     LMOE_STAGE_ROUTER = 2,      /* logits = z Wr^T + br (not recorded when folded into D) */
-    LMOE_STAGE_TOPK = 3,        /* top_k + softmax over the kept logits, and the permutation */
+    LMOE_STAGE_TOPK = 3,        /* top_k + softmax over the kept logits, and the permutation (for
+                                   T <= 64 inside the EXPERT_UP launch, not recorded) */
     LMOE_STAGE_PERMUTE = 4,     /* (not recorded: the permutation belongs to the TOPK stage) */
-    LMOE_STAGE_EXPERT_UP = 5,   /* SwiGLU gate/up of every segment (shared expert included) */
-    LMOE_STAGE_EXPERT_DOWN = 6, /* down projections; for T <= 16 also the weighted merge */
-    LMOE_STAGE_COMBINE = 7,     /* weighted merge (T > 16) */
+    LMOE_STAGE_EXPERT_UP = 5,   /* SwiGLU gate/up of every segment (shared expert included); for
+                                   T <= 64 the routing first */
+    LMOE_STAGE_EXPERT_DOWN = 6, /* down projections; for T <= 64 also the weighted merge */
+    LMOE_STAGE_COMBINE = 7,     /* weighted merge (T > 64) */
     LMOE_STAGE_U = 8,           /* y = m U^T */
     LMOE_N_STAGES = 9
 } lmoe_stage;
@@ -169,7 +171,7 @@ lmoe_status lmoe_pack_experts(const lmoe_config* cfg, int32_t shared, const void
  * lmoe_fold_router computes G = Wr . D ([n_experts][hidden], fp32 accumulation in ascending
  * latent order) and stores it as two bf16 halves, hi = bf16(G) and lo = bf16(G - hi):
  *   Gr [n_experts][2][hidden]  (lmoe_fold_router_bytes(cfg) bytes; must not overlap D or Wr).
- * With weights->Gr set, lmoe_forward computes the logits of batches of up to 16 tokens as
+ * With weights->Gr set, lmoe_forward computes the logits of batches of up to 64 tokens as
  * x . hi^T + x . lo^T + br in the launch that computes z, one dependent launch fewer than
  * the z-based router.  hi + lo carries G to about 2^-17 relative, the precision the z-based
  * small-batch router keeps for z (a bf16 hi/lo split of the fp32 z).  Larger batches use the

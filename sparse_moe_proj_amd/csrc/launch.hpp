@@ -129,7 +129,7 @@ struct ExpertArgs {
     size_t rec_bytes;
     const void* shared;
     uint16_t* H;
-    uint16_t* Y;       // [T*k + T][L] bf16 expert outputs (T > 16)
+    uint16_t* Y;       // [T*k + T][L] bf16 expert outputs (larger batches)
     int max_tiles;
     bool stream_path;
     bool decode_path;  // small batch: gate/up into H, then down + merge into mpart
