@@ -2,8 +2,8 @@
 
 This module is the only code shared by the HIP path's tests/bench and the CPU
 oracle.  It draws tensors and encodes them in the storage dtypes (fp32, bf16
-bits, MXFP4 bytes); it contains none of the block's arithmetic (no projection,
-routing, SwiGLU, combine, and no MXFP4 *decoding*).
+bits, MXFP4 and NVFP4 bytes); it contains none of the block's arithmetic (no
+projection, routing, SwiGLU, combine, and no 4-bit *decoding*).
 
 Shapes follow the Edge0-145B model-detail page ("模型架构" spec table and the
 Fig. 3 caption): hidden 2560, latent width l = 1792, 512 experts per layer with
@@ -19,6 +19,10 @@ matrix stored output-major with its reduction dimension K contiguous):
       down nibbles [l][F/2], then gate scales [F][l/32], up scales [F][l/32],
       down scales [l][F/32].  Low nibble = even K index.  One e8m0 scale byte
       per 32 consecutive K values.
+  expert record (NVFP4 bytes): the three nibble arrays as for MXFP4, then gate
+      scales [F][l/16], up scales [F][l/16], down scales [l][F/16] (one FP8 e4m3
+      byte per 16 consecutive K values), then the three matrices' fp32 tensor
+      scales (gate, up, down) and 4 zero bytes.
 
 Seeds: SeedSequence([0x4C4D4F45, workload id, layer (or expert bank), tensor
 code, index]) feeding PCG64; normals are drawn in float32 and scaled by
@@ -57,6 +61,10 @@ class Shape:
         f, l = self.ffn, self.latent
         return 3 * (f * l // 2) + 3 * (f * l // 32)
 
+    def nvfp4_record_bytes(self) -> int:
+        f, l = self.ffn, self.latent
+        return 3 * (f * l // 2) + 3 * (f * l // 16) + 16
+
 
 TINY = Shape(hidden=256, latent=128, n_experts=16, top_k=2, ffn=64, shared_ffn=64)
 EDGE0_145B = Shape(hidden=2560, latent=1792, n_experts=512, top_k=10, ffn=640, shared_ffn=640)
@@ -73,7 +81,7 @@ class Workload:
     T: int
     act: str       # 'f32' | 'bf16'   (x and y)
     dense: str     # 'f32' | 'bf16'   (D, U, Wr, shared expert)
-    expert: str    # 'f32' | 'bf16' | 'mxfp4'
+    expert: str    # 'f32' | 'bf16' | 'mxfp4' | 'nvfp4'
     bias: str      # 'zero' | 'zipf'
     zipf_s: float = 1.1
     layers: int = 1
@@ -88,6 +96,7 @@ WORKLOADS = {
     "stack48_mxfp4_t8": Workload(5, "stack48_mxfp4_t8", EDGE0_145B, 8, "bf16", "bf16", "mxfp4", "zipf",
                                  layers=48, expert_banks=2),
     "decode120_t8": Workload(6, "decode120_t8", EDGE0_120B, 8, "bf16", "bf16", "bf16", "zipf"),
+    "decode_nvfp4_t8": Workload(7, "decode_nvfp4_t8", EDGE0_145B, 8, "bf16", "bf16", "nvfp4", "zipf"),
 }
 
 
@@ -159,6 +168,68 @@ def mxfp4_encode(w: np.ndarray):
 
 
 # ---------------------------------------------------------------------------------------------
+# NVFP4 encoder (the pages name the format only).  Elements are FP4 E2M1 as above; every 16
+# consecutive K values share an FP8 E4M3 scale (1 sign, 4 exponent bits with bias 7, 3 mantissa
+# bits, largest finite value 448, no infinities); every matrix has one fp32 tensor scale:
+#     value = E2M1(element) * E4M3(block scale) * tensor_scale.
+# The tensor scale is amax(matrix) / (6 * 448), so the largest block scale lands on 448; a
+# block's scale is E4M3(amax(block) / 6 / tensor_scale) rounded to nearest-even (saturating at
+# 448); elements are w / (block scale * tensor scale) rounded to nearest-even on the E2M1 grid
+# (saturating at +-6).  A block whose scale rounds to 0 stores zeros.
+# ---------------------------------------------------------------------------------------------
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Non-negative float64 -> the nearest E4M3 value (ties to even), saturating at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    _, ex = np.frexp(np.where(x > 0, x, 1.0))
+    e = np.maximum(ex - 1, -6)                       # exponent of the binade (subnormals: -6)
+    step = np.ldexp(1.0, e - 3)                      # 3 mantissa bits
+    q = np.round(x / step) * step                    # numpy rounds half to even
+    return np.minimum(np.where(x > 0, q, 0.0), 448.0)
+
+
+def e4m3_bits(v: np.ndarray) -> np.ndarray:
+    """E4M3 values (non-negative, exactly representable) -> their bytes."""
+    v = np.asarray(v, dtype=np.float64)
+    _, ex = np.frexp(np.where(v > 0, v, 1.0))
+    e = ex - 1
+    normal = (v >= 2.0 ** -6)
+    mant = np.where(normal, np.round((v / np.ldexp(1.0, e) - 1.0) * 8), np.round(v / 2.0 ** -9))
+    expf = np.where(normal, e + 7, 0)
+    b = (expf.astype(np.int64) << 3) | mant.astype(np.int64)
+    return np.where(v > 0, b, 0).astype(np.uint8)
+
+
+def _e2m1_codes(a: np.ndarray) -> np.ndarray:
+    """|values| (already divided by their scale) -> E2M1 magnitude codes, nearest-even, saturating."""
+    code = np.searchsorted(_E2M1_MIDS, a, side="left")
+    at_mid = np.zeros_like(a, dtype=bool)
+    inner = code < 7
+    at_mid[inner] = a[inner] == _E2M1_MIDS[code[inner]]
+    code = code + (at_mid & (code % 2 == 1))
+    return np.minimum(code, 7).astype(np.uint8)
+
+
+def nvfp4_encode(w: np.ndarray):
+    """float32 [rows][K] (K % 16 == 0) -> (nibbles uint8 [rows][K/2], scales uint8 [rows][K/16],
+    tensor scale float32)."""
+    w = np.asarray(w, dtype=np.float32)
+    rows, K = w.shape
+    assert K % 16 == 0
+    amax_t = float(np.abs(w).max())
+    ts = np.float32(amax_t / (6.0 * 448.0)) if amax_t > 0 else np.float32(1.0)
+    blk = w.reshape(rows, K // 16, 16).astype(np.float64)
+    sb = e4m3_round(np.abs(blk).max(axis=2) / 6.0 / float(ts))
+    denom = sb[..., None] * float(ts)
+    a = np.where(denom > 0, np.abs(blk) / np.where(denom > 0, denom, 1.0), 0.0)
+    code = _e2m1_codes(a)
+    sign = (blk < 0).astype(np.uint8) << 3
+    sign[code == 0] = 0
+    nib = (code | sign).reshape(rows, K)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return packed, e4m3_bits(sb).reshape(rows, K // 16), ts
+
+
+# ---------------------------------------------------------------------------------------------
 @dataclass
 class LayerWeights:
     shape: Shape
@@ -190,10 +261,14 @@ def expert_record(shape: Shape, rng: np.random.Generator, dtype: str, ffn: Optio
     a[2 * f * l:] *= np.float32(1.0 / np.sqrt(f))
     if dtype in ("f32", "bf16"):
         return _encode(a, dtype)
+    g, u, d = a[: f * l].reshape(f, l), a[f * l: 2 * f * l].reshape(f, l), a[2 * f * l:].reshape(l, f)
     if dtype == "mxfp4":
-        g, u, d = a[: f * l].reshape(f, l), a[f * l: 2 * f * l].reshape(f, l), a[2 * f * l:].reshape(l, f)
         parts = [mxfp4_encode(m) for m in (g, u, d)]
         return np.concatenate([p[0].ravel() for p in parts] + [p[1].ravel() for p in parts])
+    if dtype == "nvfp4":
+        parts = [nvfp4_encode(m) for m in (g, u, d)]
+        tail = np.array([p[2] for p in parts] + [0.0], dtype=np.float32).view(np.uint8)
+        return np.concatenate([p[0].ravel() for p in parts] + [p[1].ravel() for p in parts] + [tail])
     raise ValueError(dtype)
 
 

@@ -65,6 +65,30 @@ def mxfp4_decode(nibbles: np.ndarray, scales: np.ndarray, rows: int, K: int) -> 
     return val * np.repeat(np.ldexp(1.0, sc), 32, axis=1)
 
 
+def e4m3_decode(b: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 bytes -> float64: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is
+    subnormal (m/8 * 2^-6); S.1111.111 is NaN; there are no infinities."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    e, m = (b >> 3) & 0xF, b & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.ldexp(1.0, e - 10))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(b & 0x80, -mag, mag)
+
+
+def nvfp4_decode(nibbles: np.ndarray, scales: np.ndarray, tensor_scale: float, rows: int, K: int) -> np.ndarray:
+    """NVFP4 -> float64 [rows][K]: value = (-1)^s * E2M1(code) * E4M3(scale byte) * tensor_scale,
+    one E4M3 scale byte per 16 consecutive K values, low nibble = even K index."""
+    nib = np.asarray(nibbles, dtype=np.uint8).reshape(rows, K // 2)
+    codes = np.empty((rows, K), dtype=np.uint8)
+    codes[:, 0::2] = nib & 0x0F
+    codes[:, 1::2] = nib >> 4
+    table = np.array(E2M1_VALUES, dtype=np.float64)
+    mag = table[codes & 0x7]
+    val = np.where(codes & 0x8, -mag, mag)
+    sc = e4m3_decode(np.asarray(scales, dtype=np.uint8).reshape(rows, K // 16))
+    return val * np.repeat(sc, 16, axis=1) * float(tensor_scale)
+
+
 def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
@@ -86,6 +110,15 @@ def expert_matrices(record: np.ndarray, dtype: str, latent: int, ffn: int):
         g = mxfp4_decode(rec[0:nb], rec[3 * nb: 3 * nb + sb], f, l)
         u = mxfp4_decode(rec[nb: 2 * nb], rec[3 * nb + sb: 3 * nb + 2 * sb], f, l)
         d = mxfp4_decode(rec[2 * nb: 3 * nb], rec[3 * nb + 2 * sb: 3 * nb + 3 * sb], l, f)
+        return g, u, d
+    if dtype == "nvfp4":
+        nb = f * l // 2
+        sb = f * l // 16
+        rec = np.asarray(record, dtype=np.uint8)
+        ts = rec[3 * nb + 3 * sb: 3 * nb + 3 * sb + 12].view(np.float32).astype(np.float64)
+        g = nvfp4_decode(rec[0:nb], rec[3 * nb: 3 * nb + sb], ts[0], f, l)
+        u = nvfp4_decode(rec[nb: 2 * nb], rec[3 * nb + sb: 3 * nb + 2 * sb], ts[1], f, l)
+        d = nvfp4_decode(rec[2 * nb: 3 * nb], rec[3 * nb + 2 * sb: 3 * nb + 3 * sb], ts[2], l, f)
         return g, u, d
     raise ValueError(dtype)
 

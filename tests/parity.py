@@ -23,7 +23,7 @@ import sparse_moe_proj_amd as lm
 from sparse_moe_proj_amd.device import DeviceLayer, Workspace, to_device
 
 GAP = 1e-3
-TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 6e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 6e-2, "nvfp4": 6e-2}
 WTOL = 2e-4
 
 
@@ -85,7 +85,7 @@ def check_block(lw, x_host, act, out, sample=None, tol=None, label=""):
     permutation are checked on every token, outputs on `sample` (default: all tokens)."""
     s = lw.shape
     k = s.top_k
-    tol = TOL[lw.expert if lw.expert == "mxfp4" else act] if tol is None else tol
+    tol = TOL[lw.expert if lw.expert in ("mxfp4", "nvfp4") else act] if tol is None else tol
     L = oracle.Layer(lw)
     xo = act_to_f64(x_host, act)
     T = xo.shape[0]

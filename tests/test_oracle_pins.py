@@ -327,6 +327,84 @@ def test_mxfp4_encoder_decoder_round_trip():
     assert np.all(np.abs(d - w) <= np.maximum(step / 2 * scale, np.maximum(np.abs(w) - 6 * scale, 0)) + 1e-12)
 
 
+def test_e4m3_decode_closed_forms():
+    # FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 subnormal)
+    b = np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x3F, 0x7E, 0xB8, 0x80], dtype=np.uint8)
+    want = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, 1.875, 448.0, -1.0, -0.0]
+    np.testing.assert_array_equal(oracle.e4m3_decode(b), want)
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F], np.uint8))[0])
+    # every finite positive code: strictly increasing, each binade 8 evenly spaced values
+    v = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(v) > 0) and v[-1] == 448.0
+    for e in range(1, 16):
+        seg = v[8 * e: 8 * e + 8]
+        np.testing.assert_allclose(np.diff(seg), 2.0 ** (e - 10))
+
+
+def test_e4m3_encoder_against_the_decoder():
+    v = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    # every value rounds to itself and encodes to its own byte
+    np.testing.assert_array_equal(gen.e4m3_round(v), v)
+    np.testing.assert_array_equal(gen.e4m3_bits(v), np.arange(0, 0x7F, dtype=np.uint8))
+    # midpoints go to the even mantissa; above 448 saturates
+    mid = (v[1:] + v[:-1]) / 2
+    r = gen.e4m3_round(mid)
+    codes = gen.e4m3_bits(r)
+    assert np.all(codes % 2 == 0)
+    assert gen.e4m3_round(np.array([500.0, 1e9]))[0] == 448.0
+
+
+def test_nvfp4_decode_hand_built_bytes():
+    codes = list(range(16)) * 2                     # one row, K = 32: two scale blocks
+    nib = np.array([codes[i] | (codes[i + 1] << 4) for i in range(0, 32, 2)], dtype=np.uint8)
+    scales = np.array([0x40, 0x30], dtype=np.uint8)  # 2.0 and 0.5
+    got = oracle.nvfp4_decode(nib, scales, 0.25, 1, 32)[0]
+    mags = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    base = [(-1 if c & 8 else 1) * mags[c & 7] for c in codes]
+    want = np.array([v * 2.0 * 0.25 for v in base[:16]] + [v * 0.5 * 0.25 for v in base[16:]])
+    np.testing.assert_array_equal(got, want)
+
+
+def test_nvfp4_encoder_decoder_round_trip():
+    rng = np.random.default_rng(29)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    ts = 2.0 ** -7
+    # on-grid values: E2M1 * (an E4M3 block scale) * tensor scale, every block holding 6 * its
+    # scale, and one block at the largest scale so that the tensor scale is amax / (6 * 448)
+    bscale = oracle.e4m3_decode(rng.integers(0x20, 0x70, size=(4, 8)).astype(np.uint8))
+    bscale[0, 0] = 448.0
+    vals = rng.choice(grid, size=(4, 128)) * rng.choice([-1, 1], size=(4, 128))
+    vals[:, ::16] = 6.0
+    vals = vals * np.repeat(bscale, 16, axis=1) * ts
+    nib, sc, t = gen.nvfp4_encode(vals.astype(np.float32))
+    assert t == np.float32(np.abs(vals).max() / (6 * 448))
+    np.testing.assert_array_equal(oracle.nvfp4_decode(nib, sc, t, 4, 128), vals)
+    # random normals: within half an E2M1 step of the block scale, plus the scale's own rounding
+    w = rng.standard_normal((16, 256)).astype(np.float32)
+    nib, sc, t = gen.nvfp4_encode(w)
+    d = oracle.nvfp4_decode(nib, sc, t, 16, 256)
+    amax = np.repeat(np.abs(w.reshape(16, 16, 16)).max(axis=2), 16, axis=1)
+    assert np.all(np.abs(d - w) <= amax * (1 / 6 + 1 / 16) + 1e-12)
+    assert np.mean(np.abs(d - w)) / np.mean(np.abs(w)) < 0.12
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_four_bit_record_layout(fmt):
+    """A generated 4-bit record decodes (by the oracle) to the normals it was drawn from, matrix by
+    matrix, within the format's rounding: a misplaced nibble, scale or tensor-scale field would not."""
+    s = gen.Shape(hidden=64, latent=128, n_experts=2, top_k=1, ffn=64, shared_ffn=0)
+    rec = gen.expert_record(s, gen.rng_for(99, 0, gen.T_EXPERT, 0), fmt)
+    ref = gen.expert_record(s, gen.rng_for(99, 0, gen.T_EXPERT, 0), "f32").astype(np.float64)
+    f, l = s.ffn, s.latent
+    want = (ref[: f * l].reshape(f, l), ref[f * l: 2 * f * l].reshape(f, l), ref[2 * f * l:].reshape(l, f))
+    got = oracle.expert_matrices(rec, fmt, l, f)
+    assert rec.size == (s.mxfp4_record_bytes() if fmt == "mxfp4" else s.nvfp4_record_bytes())
+    for g_, w_ in zip(got, want):
+        assert g_.shape == w_.shape
+        rel = np.linalg.norm(g_ - w_) / np.linalg.norm(w_)
+        assert rel < 0.15, rel
+
+
 def test_rmsnorm_closed_form():
     h = np.full((2, 10), 3.0)
     h[1] = -0.5
