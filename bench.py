@@ -68,8 +68,9 @@ def algorithmic_counts(wl, ids: np.ndarray, T=None):
     H, L, E, k, F, Fs = s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn
     nd = int(np.unique(ids).size)
     wb = 2  # bf16 dense weights
-    rec = s.mxfp4_record_bytes() if wl.expert == "mxfp4" else 3 * F * L * 2
-    up_w = (2 * F * L // 2 + 2 * F * L // 32) if wl.expert == "mxfp4" else 2 * F * L * 2
+    rec = {"mxfp4": s.mxfp4_record_bytes(), "nvfp4": s.nvfp4_record_bytes()}.get(wl.expert, 3 * F * L * 2)
+    up_w = {"mxfp4": 2 * F * L // 2 + 2 * F * L // 32,
+            "nvfp4": 2 * F * L // 2 + 2 * F * L // 16 + 8}.get(wl.expert, 2 * F * L * 2)
     dense = (2 * H * L + E * L) * wb + E * 4 + 3 * Fs * L * wb
     xin = T * H * (4 if wl.layers > 1 else 2)
     yout = T * H * (4 if wl.layers > 1 else 2)
@@ -187,6 +188,66 @@ def measure(wl, steps, warmup, rotate, profile_stages=True, copies=None, T=None,
                 stages_us=stages_us, weight_bytes_per_copy=base.nbytes(), graph_ms_per_step=graph_ms)
 
 
+def measure_stack(wl, steps, warmup):
+    """The multi-layer stack (pre-RMSNorm, fp32 residual updated in place): every layer's weights
+    resident at their own HBM addresses (layers sharing an expert bank hold separate copies), a
+    step is one pass of the T tokens through all layers; reported per layer."""
+    import torch
+
+    import lmoe_data as gen
+    import sparse_moe_proj_amd as lm
+    from sparse_moe_proj_amd.device import DeviceLayer, Workspace, to_device
+
+    hip = Hip()
+    t0 = time.time()
+    banks = {b: gen.make_experts(wl, b) for b in range(max(wl.expert_banks, 1))}
+    layers = []
+    for l in range(wl.layers):
+        lw = gen.make_layer(wl, l, experts=banks[gen.expert_bank(wl, l)] if wl.expert_banks else None)
+        layers.append(DeviceLayer(lw, act="bf16"))
+    del banks
+    log(f"[bench] {wl.name}: {wl.layers} layers generated and uploaded in {time.time() - t0:.1f}s")
+    T = wl.T
+    h = to_device(gen.make_residual(wl))
+    ws = Workspace("cuda").get(lm.lmoe_workspace_bytes(layers[0].cfg, T))
+    ids = [torch.empty((T, wl.shape.top_k), dtype=torch.int32, device="cuda") for _ in layers]
+
+    def layer_fwd(dl, opts):
+        lm.check(lm.lmoe_forward(dl.cfg, dl.weights, h, T, h, opts, ws, ws.numel()))
+
+    # routing of one pass (for the algorithmic byte counts), then warmup passes
+    for dl, idt in zip(layers, ids):
+        layer_fwd(dl, lm.make_opts(prenorm=1, residual=1, aux_ids=idt))
+    torch.cuda.synchronize()
+    counts = [algorithmic_counts(wl, idt.cpu().numpy()) for idt in ids]
+    for _ in range(warmup):
+        for dl in layers:
+            layer_fwd(dl, lm.make_opts(prenorm=1, residual=1))
+    torch.cuda.synchronize()
+    opts, evs = [], []
+    for _ in range(steps):
+        for _l in layers:
+            e0, e1 = hip.event(), hip.event()
+            arr = (ctypes.c_void_p * (2 * lm.LMOE_N_STAGES))()
+            arr[2 * STAGE_UP], arr[2 * STAGE_UP + 1] = e0, e1
+            evs.append((e0, e1))
+            opts.append((arr, lm.make_opts(prenorm=1, residual=1, stage_events=arr)))
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    i = 0
+    for _ in range(steps):
+        for dl in layers:
+            layer_fwd(dl, opts[i][1])
+            i += 1
+    torch.cuda.synchronize()
+    ms_per_layer = 1e3 * (time.perf_counter() - t_start) / (steps * wl.layers)
+    up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))
+    mean = {key: float(np.mean([c[key] for c in counts])) for key in ("layer_bytes", "layer_flops", "up_bytes",
+                                                                      "up_flops", "n_distinct_experts")}
+    return dict(ms_per_step=ms_per_layer, tok_s=T / (ms_per_layer / 1e3), up_ms=up_ms, counts=mean,
+                stages_us={}, graph_ms_per_step=None)
+
+
 def cpu_baseline(wl, seconds):
     """The oracle as it stands (float64 numpy), on the host's cores, on whole decode steps."""
     import lmoe_data as gen
@@ -270,9 +331,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     wl = gen.WORKLOADS[args.workload]
-    assert wl.layers == 1, "the stack workload is measured by its own test"
-    copies = layer_copies(wl, args.rotate)
-    m = measure(wl, args.steps, args.warmup, args.rotate, copies=copies)
+    if wl.layers > 1:  # the stack streams its own distinct layers: no weight copies to rotate
+        copies = None
+        m = measure_stack(wl, args.steps, args.warmup)
+        args.rotate = 1
+    else:
+        copies = layer_copies(wl, args.rotate)
+        m = measure(wl, args.steps, args.warmup, args.rotate, copies=copies)
     c = m["counts"]
     mfma_bound = c["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > c["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
     rl = roofline_mfma(c, m["up_ms"]) if mfma_bound else roofline_hbm(c, m["up_ms"], measured_traffic(wl.name))
@@ -299,9 +364,12 @@ def main():
                   "hbm_frac": round(c["layer_bytes"] / layer_s / (HBM_PEAK_GBS * 1e9), 4),
                   "mfma_frac": round(c["layer_flops"] / layer_s / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)},
         "stages_us": m["stages_us"],
-        "graph_ms_per_step": round(m["graph_ms_per_step"], 5),
+        "graph_ms_per_step": round(m["graph_ms_per_step"], 5) if m["graph_ms_per_step"] is not None else None,
     }
-    if args.tsweep:
+    if wl.layers > 1:
+        out["config"]["layers"] = wl.layers
+        out["config"]["timed"] = "eager lmoe_forward calls, all layers in order, per-layer figures"
+    if args.tsweep and copies is not None:
         sweep = []
         for T in [int(v) for v in args.tsweep.split(",") if v]:
             mt = measure(wl, args.steps, args.warmup, args.rotate, profile_stages=False, copies=copies, T=T,

@@ -31,14 +31,21 @@
  *             [ffn][latent/32], up scales [ffn][latent/32], down scales [latent][ffn/32].
  *             Elements are OCP MX FP4 E2M1 (low nibble = even K index), one E8M0 scale
  *             byte (value 2^(byte-127)) per 32 consecutive K values.
+ *         NVFP4 (routed experts only): the three nibble arrays as for MXFP4, then gate scales
+ *             [ffn][latent/16], up scales [ffn][latent/16], down scales [latent][ffn/16], one
+ *             FP8 E4M3 byte per 16 consecutive K values, then the three matrices' fp32
+ *             tensor scales (gate, up, down) and 4 zero bytes; element value =
+ *             E2M1 * E4M3(block scale) * tensor scale.
  *     Routed experts are n_experts records back to back.  The shared expert record uses
  *     the dense dtype and shared_ffn in place of ffn.
  *   - lmoe_forward reads BF16 and MXFP4 records in the PACKED layout that lmoe_pack_experts
  *     writes (same size; F32 records stay row-major).  Packing permutes each matrix into
  *     1 KB tiles of 16 rows: BF16 tiles hold 16 rows x 32 columns, the 16-byte unit of row j
  *     and columns 8q..8q+7 at position 16q + j, tiles ordered by (row block, column step);
- *     MXFP4 nibble tiles hold 16 rows x 128 values (unit of row j, values 32q..32q+31 at
- *     position 16q + j) and each has a 64-byte scale tile in the same order.  A tile is the
+ *     4-bit nibble tiles hold 16 rows x 128 values (unit of row j, values 32q..32q+31 at
+ *     position 16q + j) and each has a scale tile in the same unit order: MXFP4 one byte per
+ *     unit (64 bytes), NVFP4 the unit's two E4M3 bytes (128 bytes); NVFP4 tensor scales stay
+ *     at the end of the record.  A tile is the
  *     register image of one matrix-core operand, so the kernels read it with contiguous 1 KB
  *     wave loads.
  *   - BF16 tensors hold raw bf16 bit patterns (uint16).
@@ -58,8 +65,9 @@
  *   act F32,  dense F32,  expert F32     (plain fp32 path)
  *   act BF16, dense BF16, expert BF16    (bf16 storage, fp32 accumulation)
  *   act BF16, dense BF16, expert MXFP4
+ *   act BF16, dense BF16, expert NVFP4
  * Dimension limits: hidden, latent, ffn, shared_ffn multiples of 64 (shared_ffn may be 0;
- * with MXFP4 experts latent, ffn and shared_ffn must be multiples of 128);
+ * with 4-bit experts latent, ffn and shared_ffn must be multiples of 128);
  * 1 <= top_k <= 16; top_k <= n_experts <= 1024; 0 <= T <= 2^20 with T*top_k < 2^31.
  */
 #ifndef LMOE_H
@@ -83,7 +91,7 @@ typedef enum {
     LMOE_ERR_HIP = 7          /* the HIP runtime reported an error while enqueuing */
 } lmoe_status;
 
-typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1, LMOE_MXFP4 = 2 } lmoe_dtype;
+typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1, LMOE_MXFP4 = 2, LMOE_NVFP4 = 3 } lmoe_dtype;
 
 typedef struct {
     int32_t hidden;       /* H: token width outside the expert pool (2560) */

@@ -20,8 +20,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "lmoe.h")
 
 LMOE_OK, LMOE_ERR_NULL, LMOE_ERR_SHAPE, LMOE_ERR_DTYPE, LMOE_ERR_ALIGN = 0, 1, 2, 3, 4
 LMOE_ERR_WORKSPACE, LMOE_ERR_UNSUPPORTED, LMOE_ERR_HIP = 5, 6, 7
-LMOE_F32, LMOE_BF16, LMOE_MXFP4 = 0, 1, 2
-DTYPES = {"f32": LMOE_F32, "bf16": LMOE_BF16, "mxfp4": LMOE_MXFP4}
+LMOE_F32, LMOE_BF16, LMOE_MXFP4, LMOE_NVFP4 = 0, 1, 2, 3
+DTYPES = {"f32": LMOE_F32, "bf16": LMOE_BF16, "mxfp4": LMOE_MXFP4, "nvfp4": LMOE_NVFP4}
 
 
 class LmoeError(RuntimeError):

@@ -32,7 +32,8 @@ lmoe_status hip_fail(hipError_t e, const char* where) {
 struct Dims {
     int H, L, E, k, F, Fs;
     bool f32;  // fp32 storage end to end
-    bool mx;   // MXFP4 routed experts
+    bool mx;   // 4-bit routed experts (MXFP4 or NVFP4)
+    int fmt;   // routed expert records: 0 bf16 (or fp32), 1 MXFP4, 2 NVFP4
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -40,9 +41,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 lmoe_status check_config(const lmoe_config* cfg, Dims& d) {
     if (!cfg) return fail(LMOE_ERR_NULL, "cfg is NULL");
     const int a = cfg->act_dtype, dn = cfg->dense_dtype, ex = cfg->expert_dtype;
-    if (a < 0 || a > 2 || dn < 0 || dn > 2 || ex < 0 || ex > 2) return fail(LMOE_ERR_DTYPE, "unknown dtype code");
+    if (a < 0 || a > 3 || dn < 0 || dn > 3 || ex < 0 || ex > 3) return fail(LMOE_ERR_DTYPE, "unknown dtype code");
     const bool f32 = a == LMOE_F32 && dn == LMOE_F32 && ex == LMOE_F32;
-    const bool bf = a == LMOE_BF16 && dn == LMOE_BF16 && (ex == LMOE_BF16 || ex == LMOE_MXFP4);
+    const bool bf = a == LMOE_BF16 && dn == LMOE_BF16 && (ex == LMOE_BF16 || ex == LMOE_MXFP4 || ex == LMOE_NVFP4);
     if (!f32 && !bf)
         return fail(LMOE_ERR_UNSUPPORTED, "dtype combination act=%d dense=%d expert=%d is not supported", a, dn, ex);
     d.H = cfg->hidden;
@@ -52,13 +53,14 @@ lmoe_status check_config(const lmoe_config* cfg, Dims& d) {
     d.F = cfg->ffn;
     d.Fs = cfg->shared_ffn;
     d.f32 = f32;
-    d.mx = ex == LMOE_MXFP4;
+    d.mx = ex == LMOE_MXFP4 || ex == LMOE_NVFP4;
+    d.fmt = ex == LMOE_MXFP4 ? 1 : ex == LMOE_NVFP4 ? 2 : 0;
     if (d.H <= 0 || d.L <= 0 || d.F <= 0 || d.H % 64 || d.L % 64 || d.F % 64)
         return fail(LMOE_ERR_SHAPE, "hidden, latent and ffn must be positive multiples of 64 (got %d, %d, %d)", d.H, d.L,
                     d.F);
     if (d.Fs < 0 || d.Fs % 64) return fail(LMOE_ERR_SHAPE, "shared_ffn must be 0 or a multiple of 64 (got %d)", d.Fs);
     if (d.mx && (d.L % 128 || d.F % 128 || d.Fs % 128))
-        return fail(LMOE_ERR_SHAPE, "MXFP4 experts need latent, ffn and shared_ffn to be multiples of 128");
+        return fail(LMOE_ERR_SHAPE, "4-bit experts need latent, ffn and shared_ffn to be multiples of 128");
     if (d.k < 1 || d.k > 16) return fail(LMOE_ERR_SHAPE, "top_k must be in [1, 16] (got %d)", d.k);
     if (d.E < d.k || d.E > 1024) return fail(LMOE_ERR_SHAPE, "n_experts must be in [top_k, 1024] (got %d)", d.E);
     if ((long)d.H * d.L > (1L << 30) || (long)d.F * d.L > (1L << 30) || (long)d.Fs * d.L > (1L << 30))
@@ -130,6 +132,7 @@ size_t permute_ws(const Dims& d, int T) {
 size_t record_bytes(const Dims& d, bool shared) {
     const size_t F = shared ? d.Fs : d.F;
     if (shared || !d.mx) return 3 * F * d.L * (d.f32 ? 4 : 2);
+    if (d.fmt == 2) return 3 * (F * d.L / 2) + 3 * (F * d.L / 16) + 16;  // + three fp32 tensor scales, padded
     return 3 * (F * d.L / 2) + 3 * (F * d.L / 32);
 }
 
@@ -165,7 +168,7 @@ lmoe_status lmoe_pack_experts(const lmoe_config* cfg, int32_t shared, const void
     const size_t rec = record_bytes(d, shared != 0);
     if (overlap(src, rec * n_records, dst, rec * n_records))
         return fail(LMOE_ERR_UNSUPPORTED, "src and dst overlap (packing is not in place)");
-    const hipError_t e = launch_pack(src, dst, rec, n_records, shared ? d.Fs : d.F, d.L, d.mx && !shared,
+    const hipError_t e = launch_pack(src, dst, rec, n_records, shared ? d.Fs : d.F, d.L, shared ? 0 : d.fmt,
                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "pack experts");
     return LMOE_OK;
@@ -385,7 +388,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     float* mpart = static_cast<float*>(at(lo.mpart));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
                  wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
-                 lo.decode_path, d.mx, mpart, wts, rowinfo, route_in_experts ? &route : nullptr};
+                 lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     const int umode = o.residual ? 2 : 1;
     const uint16_t* U = static_cast<const uint16_t*>(wt->U);

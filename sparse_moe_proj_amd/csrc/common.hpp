@@ -56,20 +56,19 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
 }
 
 // ----------------------------------------------------------------------------------------------
-// MXFP4 decoding: 8 E2M1 nibbles (one 32-bit word, low nibble first) times 2^(scale-127)
-// -> 8 bf16 values (16 bytes, the layout of one MFMA operand).
+// 4-bit decoding: 8 E2M1 nibbles (one 32-bit word, low nibble first) times a block scale
+// -> 8 bf16 values (16 bytes, the layout of one MFMA operand).  An E2M1 magnitude has at most
+// two significant bits and both block scales (a power of two; an E4M3 value, at most four
+// significant bits) multiply it exactly, so the bf16 operands are the exact decoded values.
 // ----------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint4 mxfp4_to_bf16x8(uint32_t nib8, uint32_t scale_byte) {
-    // E2M1 magnitude by 3-bit code as bf16 bits: 0, 0.5, 1, 1.5, 2, 3, 4, 6
-    // value = sign * mag * 2^(s-127): the scale multiplies exactly as an exponent add,
-    // done here in fp32 (products of a 2-bit significand and a power of two are exact).
-    const float scale = __uint_as_float((scale_byte == 0 ? 0x00400000u : (scale_byte << 23)));
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t nib8, float scale) {
     uint32_t out[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         uint32_t n0 = (nib8 >> (8 * i)) & 0xFu;
         uint32_t n1 = (nib8 >> (8 * i + 4)) & 0xFu;
-        // magnitudes as fp32 from the code: code c = e*2 + m (e: 2-bit exponent, m: mantissa)
+        // E2M1 magnitudes as fp32 from the code: code c = e*2 + m (e: 2-bit exponent, m: mantissa);
+        // by code: 0, 0.5, 1, 1.5, 2, 3, 4, 6
         auto mag = [](uint32_t c) -> float {
             uint32_t e = (c >> 1) & 3u, m = c & 1u;
             // e == 0: subnormal m * 0.5; else (1 + m/2) * 2^(e-1)
@@ -82,6 +81,21 @@ __device__ __forceinline__ uint4 mxfp4_to_bf16x8(uint32_t nib8, uint32_t scale_b
         out[i] = pack_bf2(v0, v1);
     }
     return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// MXFP4 block scale: E8M0 byte s -> 2^(s - 127) (byte 0 is 2^-127, a float32 subnormal).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s == 0 ? 0x00400000u : (s << 23)); }
+
+// NVFP4 block scale: FP8 E4M3 byte (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+// 0 subnormal, m/8 * 2^-6) -> float32, exactly.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+    const float mag = e == 0 ? (float)m * 0.001953125f /* 2^-9 */ : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (b & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ uint4 mxfp4_to_bf16x8(uint32_t nib8, uint32_t scale_byte) {
+    return fp4x8_to_bf16x8(nib8, e8m0_to_f32(scale_byte));
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -109,6 +123,12 @@ __device__ __forceinline__ void xcd_tile(int& m_tile, int& n_tile) {
     n_tile = l % gridDim.x;
     m_tile = l / gridDim.x;
 }
+
+// A type carried as a value (to pick a template argument from a generic lambda).
+template <class T>
+struct TypeTag {
+    using type = T;
+};
 
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices, so register arrays
 // indexed with them stay in registers however large the unrolled body gets).

@@ -27,7 +27,7 @@
 
 namespace lmoe {
 
-template <bool MX>
+template <int Q>
 struct DecodeExperts {
     SegSpace seg;
     const uint16_t* z16;  // [T][L]
@@ -44,12 +44,21 @@ struct DecodeExperts {
     int max_tiles;        // work-list capacity (entries past *seg.ntiles are not used)
 };
 
+// Row readers: R = ExpertRows<0> (bf16 rows, also the shared expert of a 4-bit layer) or
+// Fp4Rows<Q> (4-bit rows).  The bf16 view of a 4-bit layer's (bf16) shared-expert matrices.
+template <int Q>
+__device__ __forceinline__ void bf16_mats(const typename ExpertRows<Q>::Mat (&m)[3], ExpertRows<0>::Mat (&b)[3]) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) b[i] = ExpertRows<0>::Mat{reinterpret_cast<const uint16_t*>(m[i].p), 1.f};
+}
+
 // ---- gate/up ----------------------------------------------------------------------------------
 // tok: the token of this lane's segment row (row0 + min(j, nrows - 1)).
-template <int W, int CH, bool MXR, bool MX>
-__device__ __forceinline__ void gu_item(const DecodeExperts<MX>& d, const Tile& tl, int f0,
-                                        const typename ExpertRows<MX>::Mat (&mats)[3], int tok) {
-    using ER = ExpertRows<MX>;
+template <int CH, class R, class DE>
+__device__ __forceinline__ void gu_item(const DE& d, const Tile& tl, int f0, const typename R::Mat (&mats)[3],
+                                        int tok) {
+    using ER = R;
+    constexpr bool MXR = true;  // (the readers ignore it)
     constexpr int SPL = ER::kSPL;
     const int lane = threadIdx.x & 63;
     const int kq = lane >> 4;
@@ -95,8 +104,9 @@ __device__ __forceinline__ void gu_item(const DecodeExperts<MX>& d, const Tile& 
     }
     // this lane holds f rows f0 + 4 kq + r (r = 0..3) of segment row j
     if (xok) {
-        const uint2 v = make_uint2(pack_bf2(silu(ag[0]) * au[0], silu(ag[1]) * au[1]),
-                                   pack_bf2(silu(ag[2]) * au[2], silu(ag[3]) * au[3]));
+        const float tg = mats[0].ts, tu = mats[1].ts;  // tensor scales (NVFP4; else 1)
+        const uint2 v = make_uint2(pack_bf2(silu(ag[0] * tg) * (au[0] * tu), silu(ag[1] * tg) * (au[1] * tu)),
+                                   pack_bf2(silu(ag[2] * tg) * (au[2] * tu), silu(ag[3] * tg) * (au[3] * tu)));
         *reinterpret_cast<uint2*>(d.H + (size_t)(tl.row0 + j) * d.Hs + f0 + 4 * kq) = v;
     }
 }
@@ -117,8 +127,9 @@ struct GuRoute {
 // every CU streams the same number of items; blocks past the segment's width are skipped.
 // RNV > 0: the launch routes the batch first (route_block with RNV logits per lane; dynamic LDS
 // holds the work list, max_tiles entries); RNV = 0: the work list comes from global memory.
-template <int W, int CH, bool MX, int RNV>
-__global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<MX> d, const GuRoute r) {
+// CH: weight groups per load chunk of bf16 rows (32 values each); CH4: of 4-bit rows (128 values).
+template <int W, int CH, int CH4, int Q, int RNV>
+__global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<Q> d, const GuRoute r) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15;
     const int T = d.seg.T, k = d.seg.k;
@@ -143,10 +154,10 @@ __global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<M
     for (int item = blockIdx.x + gridDim.x * wave; item < nitems; item += gridDim.x * W) {
         const int tile = item / d.nblocks, blk = item - tile * d.nblocks;
         const Tile tl = tiles[tile];
-        typename ExpertRows<MX>::Mat mats[3];
+        typename ExpertRows<Q>::Mat mats[3];
         int Fseg;
         bool mx;
-        segment_mats<MX>(d.experts, d.rec_bytes, d.shared, tl.seg, d.seg.E, d.F, d.Fs, d.L, mats, Fseg, mx);
+        segment_mats<Q>(d.experts, d.rec_bytes, d.shared, tl.seg, d.seg.E, d.F, d.Fs, d.L, mats, Fseg, mx);
         const int f0 = blk * 16;
         if (f0 >= Fseg) continue;  // widths are multiples of 16
         const int p = tl.row0 + min(j, tl.nrows - 1);
@@ -155,23 +166,89 @@ __global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<M
             tok = tl.seg == d.seg.E ? p - T * k : sm.stok[p];
         else
             tok = d.seg.token_of(tl.seg, p);
-        if (mx)
-            gu_item<W, CH, MX, MX>(d, tl, f0, mats, tok);
-        else
-            gu_item<W, CH, false, MX>(d, tl, f0, mats, tok);
+        if constexpr (Q == 0) {
+            gu_item<CH, ExpertRows<0>>(d, tl, f0, mats, tok);
+        } else if (mx) {
+            gu_item<CH4, Fp4Rows<Q>>(d, tl, f0, mats, tok);
+        } else {
+            ExpertRows<0>::Mat b[3];
+            bf16_mats<Q>(mats, b);
+            gu_item<CH, ExpertRows<0>>(d, tl, f0, b, tok);
+        }
     }
 }
 
 // ---- down + merge -----------------------------------------------------------------------------
+// A wave's tiles i0, i0 + W, ... (positions [ib, ie) of its sequence) as one stream of chunks
+// (CH weight groups of one tile each, read through R) with the next chunk always in flight,
+// across tile boundaries too; each finished tile goes to `combine`.
+template <int CH, class R, class Ctx, class CtxOf, class Combine>
+__device__ __forceinline__ void dc_run(int ib, int ie, CtxOf ctx_of, Combine combine) {
+    constexpr int SPL = R::kSPL;
+    typedef typename R::WRaw WR;
+    const int kq = (threadIdx.x & 63) >> 4;
+    // every call issues the same number of loads (clamped groups), so the waits stay exact
+    auto load = [&](WR (&w)[CH], uint4 (&h)[CH * SPL], const Ctx& c, int ch) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int gi = min(ch * CH + i, c.groups - 1);
+            w[i] = R::template load<true>(c.rw, gi, kq);
+#pragma unroll
+            for (int t = 0; t < SPL; ++t) h[i * SPL + t] = ld16(c.hr + step_k<SPL>(gi * SPL + t, kq));
+        }
+    };
+    auto compute = [&](const WR (&w)[CH], const uint4 (&h)[CH * SPL], const Ctx& c, int ch, f32x4& acc) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            if (ch * CH + i < c.groups)
+#pragma unroll
+                for (int t = 0; t < SPL; ++t)
+                    acc = mfma16(R::template frag<true>(w[i], t), sel4(c.ok, h[i * SPL + t]), acc);
+    };
+    if (ib >= ie) return;
+    Ctx cur = ctx_of(ib), nxt = cur;
+    int i = ib, ch = 0;
+    bool more = true;
+    f32x4 acc = f32x4{};
+    WR wa[CH], wb[CH];
+    uint4 ha[CH * SPL], hb[CH * SPL];
+    // buffers x hold chunk (cur, ch): request the chunk after it into y, then use x
+    auto step = [&](WR (&wx)[CH], uint4 (&hx)[CH * SPL], WR (&wy)[CH], uint4 (&hy)[CH * SPL]) {
+        const bool last = ch + 1 >= cur.nch;
+        const bool next_tile = last && i + 1 < ie;
+        if (next_tile) nxt = ctx_of(i + 1);
+        // past the run's last chunk the request repeats the current one (never used)
+        load(wy, hy, next_tile ? nxt : cur, next_tile ? 0 : (last ? ch : ch + 1));
+        compute(wx, hx, cur, ch, acc);
+        if (last) {
+            combine(acc, cur);
+            acc = f32x4{};
+            if (next_tile) {
+                cur = nxt;
+                ++i;
+                ch = 0;
+            } else {
+                more = false;
+            }
+        } else {
+            ++ch;
+        }
+    };
+    load(wa, ha, cur, 0);
+    while (more) {
+        step(wa, ha, wb, hb);
+        if (!more) break;
+        step(wb, hb, wa, ha);
+    }
+}
+
 // grid (L / 16, G); W waves; dynamic LDS: max_tiles Tiles, then T*k int2 row records.
-// A wave's tiles are one stream of chunks (CH weight loads of one tile each) with the next
-// chunk always in flight, across tile boundaries too; the tile list and the rows' tokens and
-// weights are copied to LDS once, so no chunk waits on a descriptor.  Every wave reaches the
-// barriers (no early return).
-template <int W, int CH, bool MX>
-__global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<MX> d) {
-    using ER = ExpertRows<MX>;
-    constexpr int SPL = ER::kSPL;
+// A wave's tiles stream as chunks with the next one always in flight (dc_run); in a 4-bit layer
+// the routed tiles and the (bf16) shared-expert tiles, which come last in the work list, are two
+// such runs.  The tile list and the rows' tokens and weights are copied to LDS once, so no chunk
+// waits on a descriptor.  Every wave reaches the barriers (no early return).
+template <int W, int CH, int CH4, int Q>
+__global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<Q> d) {
     extern __shared__ int4 dsm[];
     __shared__ float macc[W][kDecodeMaxT][17];  // per wave: [token][latent row of the block] (+1 pad)
     Tile* stiles = reinterpret_cast<Tile*>(dsm);
@@ -188,60 +265,8 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<M
     const int tb = (int)((long)grp * nt / d.groups), te = (int)((long)(grp + 1) * nt / d.groups);
     const int nmine = te - tb > wave ? (te - tb - wave + W - 1) / W : 0;
 
-    struct Ctx {
-        typename ER::Row rw;
-        const uint16_t* hr;
-        int groups, nch, row0, nrows, seg;
-        bool ok, mx;
-    };
-    auto ctx_of = [&](int i) {
-        const Tile tl = stiles[tb + wave + i * W];
-        typename ER::Mat mats[3];
-        int Fseg;
-        bool mx;
-        segment_mats<MX>(d.experts, d.rec_bytes, d.shared, tl.seg, E, d.F, d.Fs, d.L, mats, Fseg, mx);
-        Ctx c;
-        c.rw = ER::row(mats[2], n0 + j, Fseg);
-        c.hr = d.H + (size_t)(tl.row0 + min(j, tl.nrows - 1)) * d.Hs;
-        c.groups = Fseg / (32 * SPL);
-        c.nch = (c.groups + CH - 1) / CH;
-        c.row0 = tl.row0;
-        c.nrows = tl.nrows;
-        c.seg = tl.seg;
-        c.ok = j < tl.nrows;
-        c.mx = mx;
-        return c;
-    };
-    typedef typename ER::WRaw WR;
-    // every call issues the same number of loads (clamped groups), so the waits stay exact
-    auto load = [&](WR (&w)[CH], uint4 (&h)[CH * SPL], const Ctx& c, int ch) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int gi = min(ch * CH + i, c.groups - 1);
-            w[i] = c.mx ? ER::template load<MX>(c.rw, gi, kq) : ER::template load<false>(c.rw, gi, kq);
-#pragma unroll
-            for (int t = 0; t < SPL; ++t) h[i * SPL + t] = ld16(c.hr + step_k<SPL>(gi * SPL + t, kq));
-        }
-    };
-    auto compute = [&](const WR (&w)[CH], const uint4 (&h)[CH * SPL], const Ctx& c, int ch, f32x4& acc) {
-        if (c.mx) {
-#pragma unroll
-            for (int i = 0; i < CH; ++i)
-                if (ch * CH + i < c.groups)
-#pragma unroll
-                    for (int t = 0; t < SPL; ++t)
-                        acc = mfma16(ER::template frag<MX>(w[i], t), sel4(c.ok, h[i * SPL + t]), acc);
-        } else {
-#pragma unroll
-            for (int i = 0; i < CH; ++i)
-                if (ch * CH + i < c.groups)
-#pragma unroll
-                    for (int t = 0; t < SPL; ++t)
-                        acc = mfma16(ER::template frag<false>(w[i], t), sel4(c.ok, h[i * SPL + t]), acc);
-        }
-    };
     // lane (kq, j): latent rows n0 + 4 kq + r of segment row j -> its token and weight
-    auto combine = [&](const f32x4& acc, const Ctx& c) {
+    auto combine = [&](const f32x4& acc, const auto& c) {
         if (!c.ok) return;
         const int p = c.row0 + j;
         int t;
@@ -254,46 +279,61 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<M
             t = ri.x;
             wt = __int_as_float(ri.y);
         }
+        wt *= c.ts;
         if (t >= 0)
 #pragma unroll
             for (int r = 0; r < 4; ++r) macc[wave][t][4 * kq + r] += wt * acc[r];
     };
-
-    if (nmine > 0) {
-        Ctx cur = ctx_of(0), nxt = cur;
-        int i = 0, ch = 0;
-        bool more = true;
-        f32x4 acc = f32x4{};
-        WR wa[CH], wb[CH];
-        uint4 ha[CH * SPL], hb[CH * SPL];
-        // buffers x hold chunk (cur, ch): request the chunk after it into y, then use x
-        auto step = [&](WR (&wx)[CH], uint4 (&hx)[CH * SPL], WR (&wy)[CH], uint4 (&hy)[CH * SPL]) {
-            const bool last = ch + 1 >= cur.nch;
-            const bool next_tile = last && i + 1 < nmine;
-            if (next_tile) nxt = ctx_of(i + 1);
-            // past the wave's last chunk the request repeats the current one (never used)
-            load(wy, hy, next_tile ? nxt : cur, next_tile ? 0 : (last ? ch : ch + 1));
-            compute(wx, hx, cur, ch, acc);
-            if (last) {
-                combine(acc, cur);
-                acc = f32x4{};
-                if (next_tile) {
-                    cur = nxt;
-                    ++i;
-                    ch = 0;
-                } else {
-                    more = false;
-                }
-            } else {
-                ++ch;
-            }
+    // tile context through row reader R (4-bit rows, or bf16 rows)
+    auto make_ctx = [&](auto rtag, int i) {
+        using R = typename decltype(rtag)::type;
+        struct Ctx {
+            typename R::Row rw;
+            const uint16_t* hr;
+            int groups, nch, row0, nrows, seg;
+            bool ok;
+            float ts;  // tensor scale of the down matrix (NVFP4; else 1)
         };
-        load(wa, ha, cur, 0);
-        while (more) {
-            step(wa, ha, wb, hb);
-            if (!more) break;
-            step(wb, hb, wa, ha);
+        const Tile tl = stiles[tb + wave + i * W];
+        typename ExpertRows<Q>::Mat mats[3];
+        int Fseg;
+        bool mx;
+        segment_mats<Q>(d.experts, d.rec_bytes, d.shared, tl.seg, E, d.F, d.Fs, d.L, mats, Fseg, mx);
+        Ctx c;
+        typename R::Mat dm;
+        if constexpr (std::is_same<R, ExpertRows<0>>::value) {
+            dm = ExpertRows<0>::Mat{reinterpret_cast<const uint16_t*>(mats[2].p), 1.f};
+        } else {
+            dm = mats[2];
         }
+        c.rw = R::row(dm, n0 + j, Fseg);
+        c.hr = d.H + (size_t)(tl.row0 + min(j, tl.nrows - 1)) * d.Hs;
+        c.groups = Fseg / (32 * R::kSPL);
+        c.nch = (c.groups + (std::is_same<R, ExpertRows<0>>::value ? CH : CH4) - 1) /
+                (std::is_same<R, ExpertRows<0>>::value ? CH : CH4);
+        c.row0 = tl.row0;
+        c.nrows = tl.nrows;
+        c.seg = tl.seg;
+        c.ok = j < tl.nrows;
+        c.ts = mats[2].ts;
+        return c;
+    };
+    if constexpr (Q == 0) {
+        using R = ExpertRows<0>;
+        auto ctx_of = [&](int i) { return make_ctx(TypeTag<R>{}, i); };
+        dc_run<CH, R, decltype(ctx_of(0))>(0, nmine, ctx_of, combine);
+    } else {
+        // the wave's routed tiles come first, then its shared-expert tiles
+        int ish = nmine;
+        for (int i = 0; i < nmine; ++i)
+            if (stiles[tb + wave + i * W].seg == E) {
+                ish = i;
+                break;
+            }
+        auto ctx4 = [&](int i) { return make_ctx(TypeTag<Fp4Rows<Q>>{}, i); };
+        dc_run<CH4, Fp4Rows<Q>, decltype(ctx4(0))>(0, ish, ctx4, combine);
+        auto ctx16 = [&](int i) { return make_ctx(TypeTag<ExpertRows<0>>{}, i); };
+        dc_run<CH, ExpertRows<0>, decltype(ctx16(0))>(ish, nmine, ctx16, combine);
     }
     __syncthreads();
     // thread e: token e / 16, latent row n0 + e % 16; the waves' sums in wave order

@@ -342,6 +342,12 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_GU_CHUNK
 #define LMOE_GU_CHUNK 4
 #endif
+#ifndef LMOE_GU_CHUNK4
+#define LMOE_GU_CHUNK4 2
+#endif
+#ifndef LMOE_DC_CHUNK4
+#define LMOE_DC_CHUNK4 2
+#endif
 #ifndef LMOE_DC_WAVES
 #define LMOE_DC_WAVES 8
 #endif
@@ -595,8 +601,8 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
 // Small-batch expert launches: gate/up work items of 16 columns dealt over one workgroup of
 // LMOE_GU_WAVES waves per compute unit, then the down projection and merge over LMOE_DC_GROUPS
 // groups of the work list.
-constexpr int kGuWaves = LMOE_GU_WAVES, kGuChunk = LMOE_GU_CHUNK;
-constexpr int kDcWaves = LMOE_DC_WAVES, kDcChunk = LMOE_DC_CHUNK, kDcGroups = LMOE_DC_GROUPS;
+constexpr int kGuWaves = LMOE_GU_WAVES, kGuChunk = LMOE_GU_CHUNK, kGuChunk4 = LMOE_GU_CHUNK4;
+constexpr int kDcWaves = LMOE_DC_WAVES, kDcChunk = LMOE_DC_CHUNK, kDcChunk4 = LMOE_DC_CHUNK4, kDcGroups = LMOE_DC_GROUPS;
 
 int decode_groups() { return kDcGroups; }
 
@@ -609,10 +615,10 @@ bool decode_fits(int T, int L, int F, int Fs) {
     return T <= kDecodeMaxT && F % 16 == 0 && Fs % 16 == 0 && small_proj_fits(T, L);
 }
 
-template <bool MX>
+template <int Q>
 hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
     const int nblocks = (int)cdiv(a.Hs, 16);
-    DecodeExperts<MX> d{seg,    a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs, a.Hs,
+    DecodeExperts<Q> d{seg,    a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs, a.Hs,
                         nblocks, a.H,  a.w,       a.mpart,     kDcGroups, a.rowinfo, a.max_tiles};
     const long items = (long)a.max_tiles * nblocks;
     ev.begin(kStageUp);
@@ -622,7 +628,7 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
         const size_t lds = (size_t)a.max_tiles * sizeof(Tile);
         const int E = a.E;
 #define LMOE_GU_ROUTED(NV)                                                                                          \
-    hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, (MX ? 1 : kGuChunk), MX, NV>), dim3((unsigned)grid),            \
+    hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, NV>), dim3((unsigned)grid),             \
                        dim3(64 * kGuWaves), lds, s, d, r)
         if (E <= 64)
             LMOE_GU_ROUTED(1);
@@ -636,7 +642,7 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
             LMOE_GU_ROUTED(16);
 #undef LMOE_GU_ROUTED
     } else {
-        hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, (MX ? 1 : kGuChunk), MX, 0>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, 0>), dim3((unsigned)grid),
                            dim3(64 * kGuWaves), 0, s, d, GuRoute{});
     }
     hipError_t err = last();
@@ -644,26 +650,26 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     ev.end(kStageUp);
     ev.begin(kStageDown);
     const size_t lds = (size_t)a.max_tiles * sizeof(Tile) + (size_t)a.T * a.k * sizeof(int2);
-    hipLaunchKernelGGL((decode_dc_kernel<kDcWaves, (MX ? 1 : kDcChunk), MX>), dim3(a.L / 16, kDcGroups),
+    hipLaunchKernelGGL((decode_dc_kernel<kDcWaves, kDcChunk, kDcChunk4, Q>), dim3(a.L / 16, kDcGroups),
                        dim3(64 * kDcWaves), lds, s, d);
     if ((err = last()) != hipSuccess) return err;
     ev.end(kStageDown);
     return hipSuccess;
 }
 
-// Larger MXFP4 batches: persistent weight-streaming gate/up, then down (the combine follows).
-template <bool MX>
+// Larger 4-bit batches: persistent weight-streaming gate/up, then down (the combine follows).
+template <int Q>
 hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
     ev.begin(kStageUp);
-    hipError_t err = launch_stream<kUW, kUKS, 2>(StreamUp<MX>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs,
+    hipError_t err = launch_stream<kUW, kUKS, 2>(StreamUp<Q>{seg, a.z16, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs,
                                                               a.Hs, a.H},
                                                  a.max_tiles, Fmax, s);
     if (err != hipSuccess) return err;
     ev.end(kStageUp);
     ev.begin(kStageDown);
-    err = launch_stream<kDW, kDKS, 1>(StreamDown<MX>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y},
+    err = launch_stream<kDW, kDKS, 1>(StreamDown<Q>{seg, a.H, a.experts, a.rec_bytes, sh, a.L, a.F, a.Fs, a.Hs, a.Y},
                                       a.max_tiles, a.L, s);
     if (err != hipSuccess) return err;
     ev.end(kStageDown);
@@ -673,9 +679,12 @@ hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {
     const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E};
     if (a.decode_path)
-        return a.mxfp4 ? launch_decode_experts<true>(a, seg, s, ev) : launch_decode_experts<false>(a, seg, s, ev);
-    if (a.stream_path) return a.mxfp4 ? launch_stream_experts<true>(a, seg, s, ev) : launch_stream_experts<false>(a, seg, s, ev);
-    if (a.mxfp4) return hipErrorInvalidValue;  // the tile path takes bf16 experts only
+        return a.fmt == 2 ? launch_decode_experts<2>(a, seg, s, ev)
+                          : a.fmt == 1 ? launch_decode_experts<1>(a, seg, s, ev) : launch_decode_experts<0>(a, seg, s, ev);
+    if (a.stream_path)
+        return a.fmt == 2 ? launch_stream_experts<2>(a, seg, s, ev)
+                          : a.fmt == 1 ? launch_stream_experts<1>(a, seg, s, ev) : launch_stream_experts<0>(a, seg, s, ev);
+    if (a.fmt != 0) return hipErrorInvalidValue;  // the tile path takes bf16 experts only
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
     if (LMOE_PIPE) {

@@ -133,7 +133,7 @@ struct ExpertArgs {
     int max_tiles;
     bool stream_path;
     bool decode_path;  // small batch: gate/up into H, then down + merge into mpart
-    bool mxfp4;
+    int fmt;           // routed expert records: 0 bf16, 1 MXFP4, 2 NVFP4
     float* mpart;      // [decode_groups()][T][L] partial merged rows (decode path)
     const float* w;
     const int2* rowinfo;  // decode path: [T*k] (token, weight bits) per permuted position
@@ -141,8 +141,9 @@ struct ExpertArgs {
 };
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 
-// Row-major expert records -> packed records (nrec records of rec_bytes; F x L gate/up, L x F down).
-hipError_t launch_pack(const void* src, void* dst, size_t rec_bytes, int nrec, int F, int L, bool mx, hipStream_t s);
+// Row-major expert records -> packed records (nrec records of rec_bytes; F x L gate/up, L x F down;
+// fmt 0 bf16, 1 MXFP4, 2 NVFP4).
+hipError_t launch_pack(const void* src, void* dst, size_t rec_bytes, int nrec, int F, int L, int fmt, hipStream_t s);
 
 // Y: bf16 rows when out_bf16 (the bf16 path), else fp32 rows.
 hipError_t launch_combine(const void* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,

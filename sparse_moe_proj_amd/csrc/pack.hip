@@ -1,6 +1,6 @@
 // Re-layout of expert records from row-major matrices into the packed tile order the expert
 // kernels read (see packed_row in problems.hpp): a pure permutation of 16-byte units (and of
-// scale bytes for MXFP4), record by record.
+// scale units for the 4-bit formats), record by record.
 #include "launch.hpp"
 
 namespace lmoe {
@@ -24,6 +24,8 @@ __global__ __launch_bounds__(256) void pack_matrix_kernel(const uint8_t* __restr
     uint8_t* d = dst + base + packed_unit(n, c, upr) * UB;
     if constexpr (UB == 16)
         *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+    else if constexpr (UB == 2)
+        *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
     else
         *d = *s;
 }
@@ -39,13 +41,25 @@ hipError_t pack_matrix(const uint8_t* src, uint8_t* dst, size_t rec_bytes, int n
 
 }  // namespace
 
-// Records of F x L gate/up and L x F down matrices; mx: MXFP4 nibbles then scales, else bf16.
-hipError_t launch_pack(const void* src, void* dst, size_t rec_bytes, int nrec, int F, int L, bool mx, hipStream_t s) {
+// Records of F x L gate/up and L x F down matrices; fmt 0: bf16; 1: MXFP4 nibbles then E8M0 scales
+// (one byte per 32 values); 2: NVFP4 nibbles, E4M3 scales (one byte per 16 values, moved as
+// 2-byte units: the two blocks of a 32-value unit), then the three fp32 tensor scales (copied).
+hipError_t launch_pack(const void* src, void* dst, size_t rec_bytes, int nrec, int F, int L, int fmt, hipStream_t s) {
     const uint8_t* a = static_cast<const uint8_t*>(src);
     uint8_t* b = static_cast<uint8_t*>(dst);
     const size_t fl = (size_t)F * L;
     hipError_t e;
-    if (!mx) {
+    if (fmt == 2) {
+        const size_t nb = fl / 2, sb = fl / 16;
+        if ((e = pack_matrix<16>(a, b, rec_bytes, nrec, 0, F, L / 32, s)) != hipSuccess) return e;
+        if ((e = pack_matrix<16>(a, b, rec_bytes, nrec, nb, F, L / 32, s)) != hipSuccess) return e;
+        if ((e = pack_matrix<16>(a, b, rec_bytes, nrec, 2 * nb, L, F / 32, s)) != hipSuccess) return e;
+        if ((e = pack_matrix<2>(a, b, rec_bytes, nrec, 3 * nb, F, L / 32, s)) != hipSuccess) return e;
+        if ((e = pack_matrix<2>(a, b, rec_bytes, nrec, 3 * nb + sb, F, L / 32, s)) != hipSuccess) return e;
+        if ((e = pack_matrix<2>(a, b, rec_bytes, nrec, 3 * nb + 2 * sb, L, F / 32, s)) != hipSuccess) return e;
+        return pack_matrix<16>(a, b, rec_bytes, nrec, 3 * nb + 3 * sb, 1, 1, s);  // tensor scales: one unit
+    }
+    if (fmt == 0) {
         if ((e = pack_matrix<16>(a, b, rec_bytes, nrec, 0, F, L / 8, s)) != hipSuccess) return e;
         if ((e = pack_matrix<16>(a, b, rec_bytes, nrec, fl * 2, F, L / 8, s)) != hipSuccess) return e;
         return pack_matrix<16>(a, b, rec_bytes, nrec, 2 * fl * 2, L, F / 8, s);

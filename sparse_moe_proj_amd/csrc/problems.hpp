@@ -397,53 +397,45 @@ struct StreamRouter {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Expert weights for the stream kernels (packed records, see packed_row).
+// Expert weights for the stream kernels (packed records, see packed_row).  Q is the routed
+// experts' format: 0 bf16, 1 MXFP4, 2 NVFP4.
 //   bf16 records: one MFMA step per load (kSPL 1), 16 bytes per lane, 1 KB per wave.
-//   MXFP4 records: four MFMA steps per load (kSPL 4): lane (row, kq) reads 16 bytes of
-//   nibbles = the 32 values k in [128g + 32kq, +32) and their one scale byte; step t of the
-//   group uses values 8t..8t+7 of them.  Packed MXFP4 matrices are 1 KB tiles of 16 rows x 128
-//   values (unit of row j, values 32 q .. 32 q + 31 at position 16 q + j), with a 64-byte scale
-//   tile per nibble tile in the same unit order.  In MXFP4 kernels the (bf16) shared expert is
-//   read in the same k order: 64 bytes per lane per group.
+//   4-bit records: four MFMA steps per load (kSPL 4): lane (row, kq) reads 16 bytes of
+//   nibbles = the 32 values k in [128g + 32kq, +32) and their block scales; step t of the group
+//   uses values 8t..8t+7 of them.  Packed 4-bit matrices are 1 KB tiles of 16 rows x 128 values
+//   (unit of row j, values 32 q .. 32 q + 31 at position 16 q + j), with a scale tile per nibble
+//   tile in the same unit order: MXFP4 one E8M0 byte per unit (64 bytes), NVFP4 two E4M3 bytes
+//   per unit (128 bytes; the scales of its two blocks of 16).  An NVFP4 matrix also has an fp32
+//   tensor scale, which multiplies the fp32 products (Mat::ts; 1 for the other formats).  In
+//   4-bit kernels the (bf16) shared expert is read in the same k order: 64 bytes per lane per
+//   group.
 // ---------------------------------------------------------------------------------------------
 struct WRaw4 { uint4 a[4]; };
 
-template <bool MX>
-struct ExpertRows;
-
-template <>
-struct ExpertRows<false> {
-    static constexpr int kSPL = 1;
-    typedef uint4 WRaw;
-    struct Mat { const uint16_t* p; };  // packed matrix base (see packed_unit)
-    struct Row { const uint16_t* p; };  // row n: its 16-row block plus (n % 16) lane units
-    __device__ static Row row(const Mat& m, int n, int K) {
-        return Row{m.p + (size_t)(n >> 4) * 16 * K + (n & 15) * 8};
-    }
-    template <bool>
-    __device__ static WRaw load(const Row& r, int s, int kq) { return ld16(r.p + s * 512 + kq * 128); }
-    template <bool>
-    __device__ static uint4 frag(const WRaw& w, int) { return w; }
-};
-
-template <>
-struct ExpertRows<true> {
+template <int Q>
+struct ExpertRows {
+    static_assert(Q == 1 || Q == 2, "4-bit formats");
     static constexpr int kSPL = 4;
+    static constexpr int kSB = Q == 1 ? 1 : 2;  // scale bytes per lane unit
     typedef WRaw4 WRaw;
-    struct Mat { const uint8_t* p; const uint8_t* sc; };  // sc == null: bf16 matrix (shared expert)
+    struct Mat { const uint8_t* p; const uint8_t* sc; float ts; };  // sc == null: bf16 matrix (shared expert)
     struct Row { const uint8_t* p; const uint8_t* sc; };
     __device__ static Row row(const Mat& m, int n, int K) {
-        if (m.sc) return Row{m.p + (size_t)(n >> 4) * 8 * K + (n & 15) * 16, m.sc + (size_t)(n >> 4) * (K / 2) + (n & 15)};
+        if (m.sc)
+            return Row{m.p + (size_t)(n >> 4) * 8 * K + (n & 15) * 16,
+                       m.sc + ((size_t)(n >> 4) * (K / 2) + (n & 15)) * kSB};
         return Row{m.p + ((size_t)(n >> 4) * 16 * K + (n & 15) * 8) * 2, nullptr};
     }
-    // group g (128 values): MXFP4 lane kq holds values 32 kq .. + 32 of the group and their
-    // scale; a bf16 row gives the same values as four 16-byte units (steps 4g + kq, units t)
+    // group g (128 values): a 4-bit lane kq holds values 32 kq .. + 32 of the group and their
+    // scales; a bf16 row gives the same values as four 16-byte units (steps 4g + kq, units t)
     template <bool MXR>
     __device__ static WRaw load(const Row& r, int g, int kq) {
         WRaw w;
         if constexpr (MXR) {
             w.a[0] = ld16(r.p + g * 1024 + kq * 256);
-            w.a[1] = make_uint4(r.sc[g * 64 + kq * 16], 0, 0, 0);
+            const uint8_t* sp = r.sc + (g * 64 + kq * 16) * kSB;
+            const uint32_t sv = kSB == 1 ? (uint32_t)*sp : (uint32_t)*reinterpret_cast<const uint16_t*>(sp);
+            w.a[1] = make_uint4(sv, 0, 0, 0);
             w.a[2] = w.a[3] = zero4();
         } else {
             const uint8_t* b = r.p + (size_t)(g * 4 + kq) * 1024;
@@ -458,54 +450,107 @@ struct ExpertRows<true> {
             return w.a[t];
         } else {
             const uint32_t nib = t == 0 ? w.a[0].x : t == 1 ? w.a[0].y : t == 2 ? w.a[0].z : w.a[0].w;
-            return mxfp4_to_bf16x8(nib, w.a[1].x);
+            if constexpr (Q == 1) return fp4x8_to_bf16x8(nib, e8m0_to_f32(w.a[1].x));
+            // steps 0, 1 hold the first block of 16 values, steps 2, 3 the second
+            return fp4x8_to_bf16x8(nib, e4m3_to_f32((w.a[1].x >> (t & 2 ? 8 : 0)) & 0xFFu));
         }
     }
 };
 
+// The 4-bit rows alone, with a compact register image (16 nibble bytes and the unit's scale
+// bits per lane): the small-batch kernels read bf16 rows (the shared expert) through
+// ExpertRows<0> instead, so a 4-bit load needs no room for a bf16 unit.
+template <int Q>
+struct Fp4Rows {
+    static constexpr int kSPL = 4;
+    static constexpr int kSB = ExpertRows<Q>::kSB;
+    struct WRaw { uint4 n; uint32_t s; };
+    typedef typename ExpertRows<Q>::Mat Mat;
+    typedef typename ExpertRows<Q>::Row Row;
+    __device__ static Row row(const Mat& m, int n, int K) { return ExpertRows<Q>::row(m, n, K); }
+    template <bool>
+    __device__ static WRaw load(const Row& r, int g, int kq) {
+        WRaw w;
+        w.n = ld16(r.p + g * 1024 + kq * 256);
+        const uint8_t* sp = r.sc + (g * 64 + kq * 16) * kSB;
+        w.s = kSB == 1 ? (uint32_t)*sp : (uint32_t)*reinterpret_cast<const uint16_t*>(sp);
+        return w;
+    }
+    template <bool>
+    __device__ static uint4 frag(const WRaw& w, int t) {
+        const uint32_t nib = t == 0 ? w.n.x : t == 1 ? w.n.y : t == 2 ? w.n.z : w.n.w;
+        if constexpr (Q == 1) return fp4x8_to_bf16x8(nib, e8m0_to_f32(w.s));
+        return fp4x8_to_bf16x8(nib, e4m3_to_f32((w.s >> (t & 2 ? 8 : 0)) & 0xFFu));
+    }
+};
+
+template <>
+struct ExpertRows<0> {
+    static constexpr int kSPL = 1;
+    typedef uint4 WRaw;
+    struct Mat { const uint16_t* p; float ts; };  // packed matrix base (see packed_unit); ts = 1
+    struct Row { const uint16_t* p; };            // row n: its 16-row block plus (n % 16) lane units
+    __device__ static Row row(const Mat& m, int n, int K) {
+        return Row{m.p + (size_t)(n >> 4) * 16 * K + (n & 15) * 8};
+    }
+    template <bool>
+    __device__ static WRaw load(const Row& r, int s, int kq) { return ld16(r.p + s * 512 + kq * 128); }
+    template <bool>
+    __device__ static uint4 frag(const WRaw& w, int) { return w; }
+};
+
 // Matrices of the segment a tile belongs to: the routed expert `seg` or the shared expert.
-template <bool MX>
+// 4-bit records: the three nibble matrices, the three scale matrices (MXFP4: [rows][K/32]
+// bytes; NVFP4: [rows][K/16]), and for NVFP4 the three fp32 tensor scales.
+template <int Q>
 __device__ __forceinline__ void segment_mats(const void* experts, size_t rec_bytes, const uint16_t* shared, int seg,
-                                             int E, int F, int Fs, int L, typename ExpertRows<MX>::Mat (&m)[3],
+                                             int E, int F, int Fs, int L, typename ExpertRows<Q>::Mat (&m)[3],
                                              int& Fseg, bool& mx) {
     if (seg == E) {
         Fseg = Fs;
         mx = false;
         const size_t fl = (size_t)Fs * L;
-        if constexpr (MX) {
+        if constexpr (Q != 0) {
             const uint8_t* b = reinterpret_cast<const uint8_t*>(shared);
-            m[0] = {b, nullptr};
-            m[1] = {b + fl * 2, nullptr};
-            m[2] = {b + 2 * fl * 2, nullptr};
+            m[0] = {b, nullptr, 1.f};
+            m[1] = {b + fl * 2, nullptr, 1.f};
+            m[2] = {b + 2 * fl * 2, nullptr, 1.f};
         } else {
-            m[0] = {shared};
-            m[1] = {shared + fl};
-            m[2] = {shared + 2 * fl};
+            m[0] = {shared, 1.f};
+            m[1] = {shared + fl, 1.f};
+            m[2] = {shared + 2 * fl, 1.f};
         }
     } else {
         Fseg = F;
-        mx = MX;
+        mx = Q != 0;
         const uint8_t* b = reinterpret_cast<const uint8_t*>(experts) + (size_t)seg * rec_bytes;
         const size_t fl = (size_t)F * L;
-        if constexpr (MX) {
-            const size_t nb = fl / 2, sb = fl / 32;
-            m[0] = {b, b + 3 * nb};
-            m[1] = {b + nb, b + 3 * nb + sb};
-            m[2] = {b + 2 * nb, b + 3 * nb + 2 * sb};
+        if constexpr (Q != 0) {
+            const size_t nb = fl / 2, sb = Q == 1 ? fl / 32 : fl / 16;
+            float ts[3] = {1.f, 1.f, 1.f};
+            if constexpr (Q == 2) {
+                const float* t = reinterpret_cast<const float*>(b + 3 * nb + 3 * sb);
+                ts[0] = t[0];
+                ts[1] = t[1];
+                ts[2] = t[2];
+            }
+            m[0] = {b, b + 3 * nb, ts[0]};
+            m[1] = {b + nb, b + 3 * nb + sb, ts[1]};
+            m[2] = {b + 2 * nb, b + 3 * nb + 2 * sb, ts[2]};
         } else {
             const uint16_t* h = reinterpret_cast<const uint16_t*>(b);
-            m[0] = {h};
-            m[1] = {h + fl};
-            m[2] = {h + 2 * fl};
+            m[0] = {h, 1.f};
+            m[1] = {h + fl, 1.f};
+            m[2] = {h + 2 * fl, 1.f};
         }
     }
 }
 
 // Fused gate/up (NMAT = 2) over a work list of <= 16-row tiles: H = SiLU(z gate^T) * (z up^T).
-template <bool MX>
+template <int Q>
 struct StreamUp {
-    using ER = ExpertRows<MX>;
-    static constexpr bool kMixed = MX;
+    using ER = ExpertRows<Q>;
+    static constexpr bool kMixed = Q != 0;
     static constexpr int kSPL = ER::kSPL;
     typedef typename ER::WRaw WRaw;
     typedef uint4 XRaw;
@@ -526,7 +571,7 @@ struct StreamUp {
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
-        segment_mats<MX>(experts, rec_bytes, shared, t.seg, seg.E, F, Fs, L, c.m, c.F, c.mx);
+        segment_mats<Q>(experts, rec_bytes, shared, t.seg, seg.E, F, Fs, L, c.m, c.F, c.mx);
     }
     __device__ bool mx_rows(const Ctx& c) const { return c.mx; }
     __device__ int n_rows(const Ctx& c) const { return c.F; }
@@ -547,15 +592,16 @@ struct StreamUp {
     __device__ XFrag x_frag(const XRow& r, const XRaw& v) const { return sel4(r.ok, v); }
     __device__ static f32x4 mma(f32x4 a, uint4 w, XFrag xv) { return mfma16(w, xv, a); }
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
-        if (n < c.F && j < c.nrows) H[(size_t)(c.row0 + j) * Hs + n] = (uint16_t)f2bf(silu(v[0]) * v[1]);
+        if (n < c.F && j < c.nrows)
+            H[(size_t)(c.row0 + j) * Hs + n] = (uint16_t)f2bf(silu(v[0] * c.m[0].ts) * (v[1] * c.m[1].ts));
     }
 };
 
 // Down projection over a work list: Y[dest(p)][n] = H[p] . down[n].
-template <bool MX>
+template <int Q>
 struct StreamDown {
-    using ER = ExpertRows<MX>;
-    static constexpr bool kMixed = MX;
+    using ER = ExpertRows<Q>;
+    static constexpr bool kMixed = Q != 0;
     static constexpr int kSPL = ER::kSPL;
     typedef typename ER::WRaw WRaw;
     typedef uint4 XRaw;
@@ -576,7 +622,7 @@ struct StreamDown {
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
-        segment_mats<MX>(experts, rec_bytes, shared, t.seg, seg.E, F, Fs, L, c.m, c.F, c.mx);
+        segment_mats<Q>(experts, rec_bytes, shared, t.seg, seg.E, F, Fs, L, c.m, c.F, c.mx);
     }
     __device__ bool mx_rows(const Ctx& c) const { return c.mx; }
     __device__ int n_rows(const Ctx&) const { return L; }
@@ -595,7 +641,7 @@ struct StreamDown {
     __device__ void epilogue(const Ctx& c, int n, int j, const float* v) const {
         if (n >= L || j >= c.nrows) return;
         const int drow = seg.dest_of(c.seg, c.row0 + j);
-        if (drow >= 0) Y[(size_t)drow * L + n] = (uint16_t)f2bf(v[0]);
+        if (drow >= 0) Y[(size_t)drow * L + n] = (uint16_t)f2bf(v[0] * c.m[2].ts);
     }
 };
 

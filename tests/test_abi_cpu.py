@@ -42,6 +42,8 @@ def test_record_sizes():
     assert lm.lmoe_expert_record_bytes(cfg(), 0) == 3 * 640 * 1792 * 2
     assert lm.lmoe_expert_record_bytes(cfg(expert="mxfp4"), 0) == S.mxfp4_record_bytes() == 1827840
     assert lm.lmoe_expert_record_bytes(cfg(expert="mxfp4"), 1) == 3 * 640 * 1792 * 2  # shared stays bf16
+    assert lm.lmoe_expert_record_bytes(cfg(expert="nvfp4"), 0) == S.nvfp4_record_bytes() == 1935376
+    assert lm.lmoe_expert_record_bytes(cfg(expert="nvfp4"), 1) == 3 * 640 * 1792 * 2
     t = gen.TINY
     c = lm.make_config(t.hidden, t.latent, t.n_experts, t.top_k, t.ffn, t.shared_ffn, "f32", "f32", "f32")
     assert lm.lmoe_expert_record_bytes(c, 0) == 3 * 64 * 128 * 4

@@ -35,7 +35,20 @@ def pack_mx(rec: np.ndarray, F: int, L: int) -> np.ndarray:
     return np.concatenate(out)
 
 
-@pytest.mark.parametrize("expert", ["bf16", "mxfp4"])
+def pack_nv(rec: np.ndarray, F: int, L: int) -> np.ndarray:
+    """NVFP4: nibble tiles as MXFP4; scale tiles hold the two E4M3 bytes of each 32-value unit;
+    the 16-byte tail (three fp32 tensor scales and padding) is unchanged."""
+    nb, sb = F * L // 2, F * L // 16
+    out = []
+    for i, (N, K) in enumerate([(F, L), (F, L), (L, F)]):
+        out.append(tiles(rec[i * nb:(i + 1) * nb].reshape(N, K // 32, 16)))
+    for i, (N, K) in enumerate([(F, L), (F, L), (L, F)]):
+        out.append(tiles(rec[3 * nb + i * sb:3 * nb + (i + 1) * sb].reshape(N, K // 32, 2)))
+    out.append(rec[3 * nb + 3 * sb:])
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("expert", ["bf16", "mxfp4", "nvfp4"])
 def test_pack_matches_layout(expert):
     shape = gen.Shape(256, 256, 5, 2, 128, 384)
     wl = gen.Workload(78, "pack", shape, 0, "bf16", "bf16", expert, "zero")
@@ -51,7 +64,12 @@ def test_pack_matches_layout(expert):
     got = dst.cpu().numpy().view(np.uint8).reshape(5, -1)
     for e in range(5):
         rec = np.ascontiguousarray(lw.experts[e])
-        want = pack_mx(rec.view(np.uint8), 128, 256) if expert == "mxfp4" else pack_bf16(rec, 128, 256)
+        if expert == "mxfp4":
+            want = pack_mx(rec.view(np.uint8), 128, 256)
+        elif expert == "nvfp4":
+            want = pack_nv(rec.view(np.uint8), 128, 256)
+        else:
+            want = pack_bf16(rec, 128, 256)
         assert np.array_equal(got[e], want), f"record {e}"
     want_sh = pack_bf16(np.ascontiguousarray(lw.shared), 384, 256)
     assert np.array_equal(sdst.cpu().numpy().view(np.uint8).reshape(-1), want_sh)

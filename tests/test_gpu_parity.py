@@ -1,8 +1,8 @@
 """GPU parity of the HIP path (through the C ABI) against the CPU oracle.
 
-Covers the six workloads at full size (routing and permutation on every token, outputs on
+Covers the seven workloads at full size (routing and permutation on every token, outputs on
 every token up to T=8 and on sampled tokens beyond), plus small shapes that exercise ragged
-tiles, both kernel paths, MXFP4 records, no shared expert, E == k and E == k == 1.
+tiles, both kernel paths, MXFP4 and NVFP4 records, no shared expert, E == k and E == k == 1.
 """
 import numpy as np
 import pytest
@@ -124,6 +124,20 @@ def test_small_mxfp4(T, ws):
     out = run_forward(dl, upload_tokens(x), ws)
     torch.cuda.synchronize()
     check_block(lw, x, "bf16", out, label=f"small_mxfp4 T={T}")
+
+
+@pytest.mark.parametrize("T", [3, 16, 40, 100])
+def test_small_nvfp4(T, ws):
+    wl, lw = small_layer(SMALL_MX, "bf16", "bf16", "nvfp4")
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"small_nvfp4 T={T}")
+
+
+def test_decode_nvfp4_t8_full(ws):
+    _workload_case("decode_nvfp4_t8", 8, ws)
 
 
 @pytest.mark.parametrize("T", [7, 70])
