@@ -10,6 +10,8 @@
 namespace lmoe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -54,6 +56,10 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
 __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
+// The same shape with fp16 operands (the 4-bit expert rows decode to fp16).
+__device__ __forceinline__ f32x4 mfma16_f16(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
 
 // ----------------------------------------------------------------------------------------------
 // 4-bit decoding: 8 E2M1 nibbles (one 32-bit word, low nibble first) times a block scale
@@ -96,6 +102,52 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 
 __device__ __forceinline__ uint4 mxfp4_to_bf16x8(uint32_t nib8, uint32_t scale_byte) {
     return fp4x8_to_bf16x8(nib8, e8m0_to_f32(scale_byte));
+}
+
+// 8 E2M1 nibbles -> 8 fp16 values times a block scale (fp16 pair `scale2`, both halves equal),
+// by byte lookup: the fp16 of an E2M1 magnitude has a zero low byte, and its high byte for codes
+// 0..7 is 00 38 3C 3E 40 42 44 46; v_perm picks the high bytes of four codes at once (the codes
+// of even and of odd positions), the sign bits are or-ed in, a second round of v_perm interleaves
+// them into fp16 pairs, and one packed fp16 multiply per pair applies the scale.  Exact while the
+// scaled values lie in fp16's normal range (NVFP4 always; MXFP4 for scales in [2^-13, 2^13]).
+__device__ __forceinline__ uint4 fp4x8_to_f16x8(uint32_t w, uint32_t scale2) {
+    constexpr uint32_t lo_tab = 0x3E3C3800u, hi_tab = 0x46444240u;
+    const uint32_t me = w & 0x07070707u, mo = (w >> 4) & 0x07070707u;
+    uint32_t he = __builtin_amdgcn_perm(hi_tab, lo_tab, me);
+    uint32_t ho = __builtin_amdgcn_perm(hi_tab, lo_tab, mo);
+    he |= (w << 4) & 0x80808080u;
+    ho |= w & 0x80808080u;
+    uint32_t o[4];
+    o[0] = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
+    o[1] = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
+    o[2] = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
+    o[3] = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
+    const f16x2 sc = __builtin_bit_cast(f16x2, scale2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, o[i]) * sc);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// fp16 pair (v, v) of a float (round to nearest even).
+__device__ __forceinline__ uint32_t f16x2_splat(float v) {
+    const _Float16 h = (_Float16)v;
+    return __builtin_bit_cast(uint32_t, f16x2{h, h});
+}
+
+// 8 bf16 -> 8 fp16 (exact for values in fp16's normal range).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+    uint32_t o[4];
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)__uint_as_float(in[i] << 16),
+                                                  (_Float16)__uint_as_float(in[i] & 0xFFFF0000u)});
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// fp32 pair -> fp16 pair bits (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
 }
 
 // ----------------------------------------------------------------------------------------------

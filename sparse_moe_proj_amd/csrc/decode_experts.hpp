@@ -4,8 +4,9 @@
 // 1. Gate/up (decode_gu_kernel).  A work item is (tile, block): the tile's tokens (<= 16 rows of
 //    one segment) and 16 consecutive columns f of the SwiGLU width; a wave computes the gate and
 //    up rows of the block against the tokens (K = latent, weights streamed from HBM, double
-//    buffered) and stores SiLU(g) * u as bf16 into
-//        H[segment row][f].
+//    buffered) and stores SiLU(g) * u into
+//        H[segment row][f]
+//    (bf16; fp16 for 4-bit segments, whose rows decode to fp16 MFMA operands).
 //    Items are dealt evenly over the compute units, so every CU streams the same share.
 // 2. Down and merge (decode_dc_kernel).  A workgroup owns 16 latent rows and one group of the
 //    work list (the tiles are split into G contiguous groups).  Its waves take the group's tiles
@@ -90,9 +91,15 @@ __device__ __forceinline__ void gu_item(const DE& d, const Tile& tl, int f0, con
             if (c * CH + i < groups)
 #pragma unroll
                 for (int t = 0; t < SPL; ++t) {
-                    const uint4 xv = sel4(xok, x[i * SPL + t]);
-                    ag = mfma16(ER::template frag<MXR>(g[i], t), xv, ag);
-                    au = mfma16(ER::template frag<MXR>(u[i], t), xv, au);
+                    if constexpr (ER::kF16) {
+                        const uint4 xv = sel4(xok, bf16x8_to_f16x8(x[i * SPL + t]));
+                        ag = mfma16_f16(ER::template frag<MXR>(g[i], t), xv, ag);
+                        au = mfma16_f16(ER::template frag<MXR>(u[i], t), xv, au);
+                    } else {
+                        const uint4 xv = sel4(xok, x[i * SPL + t]);
+                        ag = mfma16(ER::template frag<MXR>(g[i], t), xv, ag);
+                        au = mfma16(ER::template frag<MXR>(u[i], t), xv, au);
+                    }
                 }
     };
     load(ga, ua, xa, 0);
@@ -102,11 +109,15 @@ __device__ __forceinline__ void gu_item(const DE& d, const Tile& tl, int f0, con
         load(ga, ua, xa, c + 2);
         if (c + 1 < nch) compute(gbuf, ubuf, xb, c + 1);
     }
-    // this lane holds f rows f0 + 4 kq + r (r = 0..3) of segment row j
+    // this lane holds f rows f0 + 4 kq + r (r = 0..3) of segment row j; H rows of 4-bit segments
+    // are fp16 (the operand type of their down projection), else bf16
     if (xok) {
         const float tg = mats[0].ts, tu = mats[1].ts;  // tensor scales (NVFP4; else 1)
-        const uint2 v = make_uint2(pack_bf2(silu(ag[0] * tg) * (au[0] * tu), silu(ag[1] * tg) * (au[1] * tu)),
-                                   pack_bf2(silu(ag[2] * tg) * (au[2] * tu), silu(ag[3] * tg) * (au[3] * tu)));
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = silu(ag[r] * tg) * (au[r] * tu);
+        const uint2 v = ER::kF16 ? make_uint2(pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3]))
+                                 : make_uint2(pack_bf2(h[0], h[1]), pack_bf2(h[2], h[3]));
         *reinterpret_cast<uint2*>(d.H + (size_t)(tl.row0 + j) * d.Hs + f0 + 4 * kq) = v;
     }
 }
@@ -202,8 +213,12 @@ __device__ __forceinline__ void dc_run(int ib, int ie, CtxOf ctx_of, Combine com
         for (int i = 0; i < CH; ++i)
             if (ch * CH + i < c.groups)
 #pragma unroll
-                for (int t = 0; t < SPL; ++t)
-                    acc = mfma16(R::template frag<true>(w[i], t), sel4(c.ok, h[i * SPL + t]), acc);
+                for (int t = 0; t < SPL; ++t) {
+                    if constexpr (R::kF16)
+                        acc = mfma16_f16(R::template frag<true>(w[i], t), sel4(c.ok, h[i * SPL + t]), acc);
+                    else
+                        acc = mfma16(R::template frag<true>(w[i], t), sel4(c.ok, h[i * SPL + t]), acc);
+                }
     };
     if (ib >= ie) return;
     Ctx cur = ctx_of(ib), nxt = cur;

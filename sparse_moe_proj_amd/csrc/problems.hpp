@@ -459,12 +459,14 @@ struct ExpertRows {
 
 // The 4-bit rows alone, with a compact register image (16 nibble bytes and the unit's scale
 // bits per lane): the small-batch kernels read bf16 rows (the shared expert) through
-// ExpertRows<0> instead, so a 4-bit load needs no room for a bf16 unit.
+// ExpertRows<0> instead, so a 4-bit load needs no room for a bf16 unit.  These rows decode to
+// fp16 operands (kF16; see fp4x8_to_f16x8), so their MFMAs take fp16 tokens.
 template <int Q>
 struct Fp4Rows {
     static constexpr int kSPL = 4;
+    static constexpr bool kF16 = true;
     static constexpr int kSB = ExpertRows<Q>::kSB;
-    struct WRaw { uint4 n; uint32_t s; };
+    struct WRaw { uint4 n; uint32_t s; };  // s: the block scales as fp16 (MXFP4: one, twice; NVFP4: two)
     typedef typename ExpertRows<Q>::Mat Mat;
     typedef typename ExpertRows<Q>::Row Row;
     __device__ static Row row(const Mat& m, int n, int K) { return ExpertRows<Q>::row(m, n, K); }
@@ -473,20 +475,27 @@ struct Fp4Rows {
         WRaw w;
         w.n = ld16(r.p + g * 1024 + kq * 256);
         const uint8_t* sp = r.sc + (g * 64 + kq * 16) * kSB;
-        w.s = kSB == 1 ? (uint32_t)*sp : (uint32_t)*reinterpret_cast<const uint16_t*>(sp);
+        if constexpr (Q == 1) {
+            w.s = f16x2_splat(e8m0_to_f32(*sp));
+        } else {
+            const uint32_t b = *reinterpret_cast<const uint16_t*>(sp);
+            w.s = pack_f16x2(e4m3_to_f32(b & 0xFFu), e4m3_to_f32(b >> 8));
+        }
         return w;
     }
     template <bool>
     __device__ static uint4 frag(const WRaw& w, int t) {
         const uint32_t nib = t == 0 ? w.n.x : t == 1 ? w.n.y : t == 2 ? w.n.z : w.n.w;
-        if constexpr (Q == 1) return fp4x8_to_bf16x8(nib, e8m0_to_f32(w.s));
-        return fp4x8_to_bf16x8(nib, e4m3_to_f32((w.s >> (t & 2 ? 8 : 0)) & 0xFFu));
+        if constexpr (Q == 1) return fp4x8_to_f16x8(nib, w.s);
+        // steps 0, 1 hold the first block of 16 values, steps 2, 3 the second
+        return fp4x8_to_f16x8(nib, __builtin_amdgcn_perm(w.s, w.s, t & 2 ? 0x03020302u : 0x01000100u));
     }
 };
 
 template <>
 struct ExpertRows<0> {
     static constexpr int kSPL = 1;
+    static constexpr bool kF16 = false;
     typedef uint4 WRaw;
     struct Mat { const uint16_t* p; float ts; };  // packed matrix base (see packed_unit); ts = 1
     struct Row { const uint16_t* p; };            // row n: its 16-row block plus (n % 16) lane units
