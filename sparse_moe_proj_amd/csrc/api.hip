@@ -78,7 +78,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t x16, z32, z16, zlo, logits, ids, w, offsets, perm, inv, rowinfo, hist, base, tiles, ntiles, H, Y, mpart, m, total;
+    size_t x16, z32, z16, z16h, zlo, logits, ids, w, offsets, perm, inv, rowinfo, hist, base, tiles, ntiles, H, Y, mpart, m, total;
     bool stream_path, decode_path, fused_router;
     int max_tiles, BM, Hs, R;
 };
@@ -104,6 +104,7 @@ Layout plan(const Dims& d, int T) {
     lo.x16 = take(d.f32 ? 0 : (size_t)T * d.H * 2);
     lo.z32 = take((size_t)T * d.L * 4);
     lo.z16 = take(d.f32 ? 0 : (size_t)T * d.L * 2);
+    lo.z16h = take(lo.decode_path && d.mx ? (size_t)T * d.L * 2 : 0);  // fp16 z for 4-bit small batches
     lo.zlo = take(d.f32 || T <= kStreamMaxT ? 0 : (size_t)T * d.L * 2);  // low bf16 half of z (router input)
     lo.logits = take((size_t)T * d.E * 4 * (lo.fused_router ? 2 : 1));  // folded router: hi and lo halves
     lo.ids = take((size_t)T * d.k * 4);
@@ -353,16 +354,19 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         x16 = xn;
     }
     uint16_t* z16 = static_cast<uint16_t*>(at(lo.z16));
+    // fp16 z for the 4-bit experts of a small batch, written by the small-batch D launches
+    uint16_t* z16h = lo.decode_path && d.mx ? static_cast<uint16_t*>(at(lo.z16h)) : nullptr;
     if (wt->Gr && lo.fused_router) {  // z and the logits (folded router) in one launch
         ev.begin(LMOE_STAGE_D);
         if ((e = launch_proj_router_bf16(x16, static_cast<const uint16_t*>(wt->D), static_cast<const uint16_t*>(wt->Gr),
-                                         wt->br, T, d.L, d.H, d.E, z32, z16, logits, s)) != hipSuccess)
+                                         wt->br, T, d.L, d.H, d.E, z32, z16, logits, s, z16h)) != hipSuccess)
             return hip_fail(e, "D projection and router logits");
         ev.end(LMOE_STAGE_D);
     } else {
         ev.begin(LMOE_STAGE_D);
         uint16_t* zlo = T > kStreamMaxT ? static_cast<uint16_t*>(at(lo.zlo)) : nullptr;
-        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s, zlo)) !=
+        if (!(T <= kStreamMaxT && small_proj_fits(T, d.H))) z16h = nullptr;  // only the small-batch D launch writes it
+        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s, zlo, z16h)) !=
             hipSuccess)
             return hip_fail(e, "D projection");
         ev.end(LMOE_STAGE_D);
@@ -386,7 +390,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         ev.end(LMOE_STAGE_TOPK);
     }
     float* mpart = static_cast<float*>(at(lo.mpart));
-    ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, wt->experts, record_bytes(d, false),
+    ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, z16h, wt->experts, record_bytes(d, false),
                  wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
                  lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");

@@ -31,7 +31,8 @@ namespace lmoe {
 template <int Q>
 struct DecodeExperts {
     SegSpace seg;
-    const uint16_t* z16;  // [T][L]
+    const uint16_t* z16;   // [T][L]
+    const uint16_t* z16h;  // [T][L] fp16 copy of z16, or null (4-bit rows then convert z16)
     const void* experts;
     size_t rec_bytes;
     const uint16_t* shared;
@@ -67,7 +68,9 @@ __device__ __forceinline__ void gu_item(const DE& d, const Tile& tl, int f0, con
     const int L = d.L;
     const int nrows = tl.nrows;
     const typename ER::Row rg = ER::row(mats[0], f0 + j, L), ru = ER::row(mats[1], f0 + j, L);
-    const uint16_t* xr = d.z16 + (size_t)tok * L;
+    // fp16 operands: the token row from the fp16 copy when there is one, else converted
+    const bool xh = ER::kF16 && d.z16h != nullptr;
+    const uint16_t* xr = (xh ? d.z16h : d.z16) + (size_t)tok * L;
     const bool xok = j < nrows;
     const int groups = L / (32 * SPL);
     const int nch = (groups + CH - 1) / CH;
@@ -92,7 +95,7 @@ __device__ __forceinline__ void gu_item(const DE& d, const Tile& tl, int f0, con
 #pragma unroll
                 for (int t = 0; t < SPL; ++t) {
                     if constexpr (ER::kF16) {
-                        const uint4 xv = sel4(xok, bf16x8_to_f16x8(x[i * SPL + t]));
+                        const uint4 xv = sel4(xok, xh ? x[i * SPL + t] : bf16x8_to_f16x8(x[i * SPL + t]));
                         ag = mfma16_f16(ER::template frag<MXR>(g[i], t), xv, ag);
                         au = mfma16_f16(ER::template frag<MXR>(u[i], t), xv, au);
                     } else {

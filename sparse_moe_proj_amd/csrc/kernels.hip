@@ -343,7 +343,7 @@ inline hipError_t last() { return hipGetLastError(); }
 #define LMOE_GU_CHUNK 4
 #endif
 #ifndef LMOE_GU_CHUNK4
-#define LMOE_GU_CHUNK4 2
+#define LMOE_GU_CHUNK4 1
 #endif
 #ifndef LMOE_DC_CHUNK4
 #define LMOE_DC_CHUNK4 2
@@ -459,9 +459,10 @@ hipError_t small_proj_launch(const SmallProj& p, hipStream_t s) {
 }
 
 hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const uint16_t* Gr, const float* br, int T,
-                                  int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s) {
+                                  int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s,
+                                  uint16_t* z16h) {
     if (!small_proj_fits(T, H)) return hipErrorInvalidValue;
-    SmallProj p{x, nullptr, 0, D, T, L, H, 0, z32, z16, Gr, br, E, logits};
+    SmallProj p{x, nullptr, 0, D, T, L, H, 0, z32, z16, Gr, br, E, logits, z16h};
     auto k = small_proj_kernel<LMOE_SP_WAVES, LMOE_SP_SMAX, 0>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
@@ -492,13 +493,16 @@ hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int 
 hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                                 uint16_t* out16, hipStream_t s) {
     if (!small_proj_fits(T, K)) return hipErrorInvalidValue;
-    return small_proj_launch<1>(SmallProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16}, s);
+    return small_proj_launch<1>(SmallProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0,
+                                          nullptr, nullptr},
+                                s);
 }
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
-                            uint16_t* out16, hipStream_t s, uint16_t* out16lo) {
+                            uint16_t* out16, hipStream_t s, uint16_t* out16lo, uint16_t* out16h) {
     if (T <= kStreamMaxT && small_proj_fits(T, K))
-        return small_proj_launch<0>(SmallProj{x, nullptr, 0, W, T, N, K, mode, out32, out16}, s);
+        return small_proj_launch<0>(
+            SmallProj{x, nullptr, 0, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0, nullptr, out16h}, s);
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1, StreamProj, kProjChunk>(StreamProj{x, W, T, N, K, mode, out32, out16},
                                                                    (int)cdiv(T, 16), N, s);
@@ -618,8 +622,9 @@ bool decode_fits(int T, int L, int F, int Fs) {
 template <int Q>
 hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
     const int nblocks = (int)cdiv(a.Hs, 16);
-    DecodeExperts<Q> d{seg,    a.z16, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared), a.L, a.F, a.Fs, a.Hs,
-                        nblocks, a.H,  a.w,       a.mpart,     kDcGroups, a.rowinfo, a.max_tiles};
+    DecodeExperts<Q> d{seg,     a.z16, a.z16h, a.experts, a.rec_bytes, static_cast<const uint16_t*>(a.shared),
+                       a.L,     a.F,   a.Fs,   a.Hs,      nblocks,     a.H,
+                       a.w,     a.mpart, kDcGroups, a.rowinfo, a.max_tiles};
     const long items = (long)a.max_tiles * nblocks;
     ev.begin(kStageUp);
     const long grid = std::max<long>(std::min<long>(cdiv(items, kGuWaves), cu_count()), 1);

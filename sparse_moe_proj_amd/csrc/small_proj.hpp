@@ -32,6 +32,7 @@ struct SmallProj {
     const float* bias;
     int E;
     float* logits;  // [2][T][E]
+    uint16_t* out16h;  // mode 0, optional: fp16(v) as well (the token operand of 4-bit experts)
 };
 
 // Largest staged-activation LDS a small-batch projection takes (plus W KB of static LDS).
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
                 if (p.mode == 0) {
                     p.out32[o] = v;
                     p.out16[o] = (uint16_t)f2bf(v);
+                    if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
                 } else if (p.mode == 1) {
                     p.out16[o] = (uint16_t)f2bf(v);
                 } else {
