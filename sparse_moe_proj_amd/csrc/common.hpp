@@ -134,6 +134,17 @@ __device__ __forceinline__ uint32_t f16x2_splat(float v) {
     return __builtin_bit_cast(uint32_t, f16x2{h, h});
 }
 
+// Two FP8 E4M3 bytes (bits 0-7 and 8-15 of b) -> an fp16 pair, exactly.  An E4M3 byte's
+// exponent and mantissa fields, moved into an fp16's (sign to bit 15, the 7 other bits to bits
+// 7..13), read as an fp16 whose exponent bias is 15 instead of 7, i.e. 2^-8 times the E4M3 value
+// (its subnormals land on fp16 subnormals the same way); one packed multiply by 256 restores it.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t b) {
+    const uint32_t u = (b & 0xFFu) | ((b & 0xFF00u) << 8);  // byte 0 at bits 0-7, byte 1 at 16-23
+    const uint32_t h = ((u & 0x007F007Fu) << 7) | ((u & 0x00800080u) << 8);
+    const _Float16 k = (_Float16)256.0f;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) * f16x2{k, k});
+}
+
 // 8 bf16 -> 8 fp16 (exact for values in fp16's normal range).
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
     uint32_t o[4];

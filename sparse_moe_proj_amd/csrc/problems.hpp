@@ -466,7 +466,10 @@ struct Fp4Rows {
     static constexpr int kSPL = 4;
     static constexpr bool kF16 = true;
     static constexpr int kSB = ExpertRows<Q>::kSB;
-    struct WRaw { uint4 n; uint32_t s; };  // s: the block scales as fp16 (MXFP4: one, twice; NVFP4: two)
+    // s: the unit's raw scale bits (MXFP4: its E8M0 byte; NVFP4: its two E4M3 bytes).  They are
+    // converted where the fragments are made, not where they are loaded, so that no conversion
+    // waits on a load that is still in flight.
+    struct WRaw { uint4 n; uint32_t s; };
     typedef typename ExpertRows<Q>::Mat Mat;
     typedef typename ExpertRows<Q>::Row Row;
     __device__ static Row row(const Mat& m, int n, int K) { return ExpertRows<Q>::row(m, n, K); }
@@ -475,20 +478,16 @@ struct Fp4Rows {
         WRaw w;
         w.n = ld16(r.p + g * 1024 + kq * 256);
         const uint8_t* sp = r.sc + (g * 64 + kq * 16) * kSB;
-        if constexpr (Q == 1) {
-            w.s = f16x2_splat(e8m0_to_f32(*sp));
-        } else {
-            const uint32_t b = *reinterpret_cast<const uint16_t*>(sp);
-            w.s = pack_f16x2(e4m3_to_f32(b & 0xFFu), e4m3_to_f32(b >> 8));
-        }
+        w.s = Q == 1 ? (uint32_t)*sp : (uint32_t)*reinterpret_cast<const uint16_t*>(sp);
         return w;
     }
     template <bool>
     __device__ static uint4 frag(const WRaw& w, int t) {
         const uint32_t nib = t == 0 ? w.n.x : t == 1 ? w.n.y : t == 2 ? w.n.z : w.n.w;
-        if constexpr (Q == 1) return fp4x8_to_f16x8(nib, w.s);
+        if constexpr (Q == 1) return fp4x8_to_f16x8(nib, f16x2_splat(e8m0_to_f32(w.s)));
         // steps 0, 1 hold the first block of 16 values, steps 2, 3 the second
-        return fp4x8_to_f16x8(nib, __builtin_amdgcn_perm(w.s, w.s, t & 2 ? 0x03020302u : 0x01000100u));
+        const uint32_t s2 = e4m3x2_to_f16x2(w.s);
+        return fp4x8_to_f16x8(nib, __builtin_amdgcn_perm(s2, s2, t & 2 ? 0x03020302u : 0x01000100u));
     }
 };
 

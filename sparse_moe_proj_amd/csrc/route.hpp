@@ -8,26 +8,32 @@
 
 namespace lmoe {
 
+// Inclusive prefix sum over the wave by DPP: three shifts by 1, 2, 3 lanes of the inputs give
+// each lane the sum of its quad-aligned window of 4, shifts by 4 and 8 lanes (upper banks of
+// each row only) extend it to the row, and two row broadcasts (lane 15 into rows 1 and 3, lane
+// 31 into rows 2 and 3) carry the rows' totals.  Lanes without a source add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    int s = x;
+    s += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr 1
+    s += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr 2
+    s += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xF, 0xF, true);  // row_shr 3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xF, 0xE, true);  // row_shr 4, banks 1-3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xF, 0xC, true);  // row_shr 8, banks 2-3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xA, 0xF, false);  // row_bcast 15, rows 1, 3
+    s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xC, 0xF, false);  // row_bcast 31, rows 2, 3
+    return s;
+}
+
 // Exclusive prefix sum over the block (one value per thread, blockDim a multiple of 64, at
 // most 2048 threads).  tmp needs 33 ints of LDS.  Every thread must call it.
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     __syncthreads();
     if (lane == 63) tmp[w] = x;
     __syncthreads();
     if (w == 0) {
-        int t = lane < nw ? tmp[lane] : 0;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(t, o);
-            if (lane >= o) t += y;
-        }
+        const int t = wave_incl_scan(lane < nw ? tmp[lane] : 0);
         if (lane < nw) tmp[lane] = t;
         if (lane == 63) tmp[32] = t;
     }
@@ -83,21 +89,28 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 // expert as (rank among the kept ids in ascending order) << 16 | id, with its softmax weight;
 // other lanes return -1.
 // row2 (optional): a second half of the logits, added to row (the folded router's lo half).
+// The lane's logits (ids lane + 64 j) of a row and of its second half (without one, the row
+// again, which wave_topk_select then ignores), as wave_topk_select takes them.  Only loads are
+// issued (clamped addresses, no branch), so they are in flight together and nothing here waits
+// for them.
 template <int NV>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, const float* __restrict__ row2, int E, int k,
-                                          int& out, float& out_w) {
+__device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, const float* __restrict__ row2, int E,
+                                               float (&v)[NV], float (&v2)[NV]) {
     const int lane = threadIdx.x & 63;
-    // all loads first (clamped addresses, no branch), so they are in flight together
-    float v[NV];
+    const float* r2 = row2 ? row2 : row;
 #pragma unroll
     for (int j = 0; j < NV; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
-    if (row2) {
-        float v2[NV];
 #pragma unroll
-        for (int j = 0; j < NV; ++j) v2[j] = row2[min(lane + 64 * j, E - 1)];
+    for (int j = 0; j < NV; ++j) v2[j] = r2[min(lane + 64 * j, E - 1)];
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_topk_select(const float (&v1)[NV], const float (&v2)[NV], bool has2, int E, int k,
+                                                 int& out, float& out_w) {
+    const int lane = threadIdx.x & 63;
+    float v[NV];
 #pragma unroll
-        for (int j = 0; j < NV; ++j) v[j] += v2[j];
-    }
+    for (int j = 0; j < NV; ++j) v[j] = has2 ? v1[j] + v2[j] : v1[j];
     uint32_t key[NV];
     int id[NV];
 #pragma unroll
@@ -154,6 +167,14 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, const f
     for (int r = 0; r < k; ++r) pos += __builtin_amdgcn_readlane(sel_id, r) < sel_id ? 1 : 0;
     out = lane < k ? (pos << 16) | sel_id : -1;
     out_w = lane < k ? e / s : 0.f;
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, const float* __restrict__ row2, int E, int k,
+                                          int& out, float& out_w) {
+    float v[NV], v2[NV];
+    wave_topk_load<NV>(row, row2, E, v, v2);
+    wave_topk_select<NV>(v, v2, row2 != nullptr, E, k, out, out_w);
 }
 
 // ==============================================================================================
@@ -213,12 +234,17 @@ template <int NV>
 __device__ void route_block(const float* __restrict__ logits, const float* __restrict__ logits2, int T, int E, int k,
                             int BM, int has_shared, const RouteOut& g, RouteScratch& sm, Tile* stiles, int* sntiles) {
     const int nthr = blockDim.x, nwaves = nthr >> 6;
+    const int tw = threadIdx.x >> 6;
+    float v[NV], v2[NV];
+    // the wave's first token's logits are requested before the bitmaps are cleared
+    if (tw < T) wave_topk_load<NV>(logits + (size_t)tw * E, logits2 ? logits2 + (size_t)tw * E : nullptr, E, v, v2);
     for (int i = threadIdx.x; i < 2 * E; i += nthr) sm.bm[i] = 0;
     __syncthreads();
-    for (int t = threadIdx.x >> 6; t < T; t += nwaves) {
+    for (int t = tw; t < T; t += nwaves) {
         int pid;
         float wt;
-        wave_topk<NV>(logits + (size_t)t * E, logits2 ? logits2 + (size_t)t * E : nullptr, E, k, pid, wt);
+        if (t != tw) wave_topk_load<NV>(logits + (size_t)t * E, logits2 ? logits2 + (size_t)t * E : nullptr, E, v, v2);
+        wave_topk_select<NV>(v, v2, logits2 != nullptr, E, k, pid, wt);
         if (pid >= 0) {
             const int pos = pid >> 16, e = pid & 0xffff;
             if (g.ids) g.ids[(size_t)t * k + pos] = e;
