@@ -346,7 +346,11 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     }
 
     const uint16_t* x16 = static_cast<const uint16_t*>(x);
-    if (o.prenorm) {
+    // small batches whose D launch stages its input in LDS form bf16(RMSNorm(h)) there
+    const bool fused_d_router = wt->Gr && lo.fused_router;
+    const bool norm_in_d = o.prenorm && (fused_d_router || (T <= kStreamMaxT && small_proj_fits(T, d.H)));
+    const float* hnorm = norm_in_d ? static_cast<const float*>(x) : nullptr;
+    if (o.prenorm && !norm_in_d) {
         uint16_t* xn = static_cast<uint16_t*>(at(lo.x16));
         ev.begin(LMOE_STAGE_PRENORM);
         if ((e = launch_rmsnorm(static_cast<const float*>(x), T, d.H, xn, s)) != hipSuccess) return hip_fail(e, "rmsnorm");
@@ -356,18 +360,18 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     uint16_t* z16 = static_cast<uint16_t*>(at(lo.z16));
     // fp16 z for the 4-bit experts of a small batch, written by the small-batch D launches
     uint16_t* z16h = lo.decode_path && d.mx ? static_cast<uint16_t*>(at(lo.z16h)) : nullptr;
-    if (wt->Gr && lo.fused_router) {  // z and the logits (folded router) in one launch
+    if (fused_d_router) {  // z and the logits (folded router) in one launch
         ev.begin(LMOE_STAGE_D);
         if ((e = launch_proj_router_bf16(x16, static_cast<const uint16_t*>(wt->D), static_cast<const uint16_t*>(wt->Gr),
-                                         wt->br, T, d.L, d.H, d.E, z32, z16, logits, s, z16h)) != hipSuccess)
+                                         wt->br, T, d.L, d.H, d.E, z32, z16, logits, s, z16h, hnorm)) != hipSuccess)
             return hip_fail(e, "D projection and router logits");
         ev.end(LMOE_STAGE_D);
     } else {
         ev.begin(LMOE_STAGE_D);
         uint16_t* zlo = T > kStreamMaxT ? static_cast<uint16_t*>(at(lo.zlo)) : nullptr;
         if (!(T <= kStreamMaxT && small_proj_fits(T, d.H))) z16h = nullptr;  // only the small-batch D launch writes it
-        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s, zlo, z16h)) !=
-            hipSuccess)
+        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s, zlo, z16h,
+                                  hnorm)) != hipSuccess)
             return hip_fail(e, "D projection");
         ev.end(LMOE_STAGE_D);
         ev.begin(LMOE_STAGE_ROUTER);

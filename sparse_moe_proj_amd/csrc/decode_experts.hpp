@@ -192,6 +192,202 @@ __global__ __launch_bounds__(64 * W) void decode_gu_kernel(const DecodeExperts<Q
     }
 }
 
+// ---- gate/up with K split over the waves ----------------------------------------------------
+// The same items in another arrangement: item i goes to workgroup i % grid, and all W waves of
+// the workgroup work on it, wave w taking the contiguous run [G w / W, G (w + 1) / W) of the G
+// weight groups along K (the latent dimension), at most MG groups.  Each wave's partial gate and
+// up products (16 f rows x 16 segment rows) go to LDS; after one barrier per item, 256 threads
+// sum them in wave order and store SiLU(g) * u.  The next item's weights and token rows are
+// requested before the current item's products are reduced (two register sets), so every wave
+// keeps its share of the weight stream in flight from item to item, and the per-item ALU work
+// (4-bit decode, MFMA) is spread over all four SIMDs.
+template <int W>
+struct GuRed { float v[2][W][2][16 * 17]; };  // [buffer][wave][gate, up][f row * 17 + segment row]
+
+// Items [first, end) of the workgroup's sequence (first, first + grid, ...) whose rows R reads.
+template <int W, int MG, class R, int Q, class ItemOf>
+__device__ __forceinline__ void gu_split_run(const DecodeExperts<Q>& d, int first, int end, ItemOf item_of,
+                                             GuRed<W>& red, int& buf) {
+    constexpr int SPL = R::kSPL;
+    typedef typename R::WRaw WR;
+    typedef decltype(item_of(0)) Ctx;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kq = lane >> 4, j = lane & 15;
+    const int G = d.L / (32 * SPL);
+    const int ga = G * wave / W, gb = G * (wave + 1) / W;
+    const int grid = gridDim.x;
+    // the next item at or after m that has rows in its segment (the same for every wave)
+    auto next_valid = [&](int m, Ctx& c) {
+        for (; m < end; m += grid) {
+            c = item_of(m);
+            if (c.valid) return m;
+        }
+        return end;
+    };
+    // every call issues the same loads (clamped to a valid group), so the waits stay exact
+    auto load = [&](WR (&w)[MG][2], uint4 (&x)[MG * SPL], const Ctx& c) {
+#pragma unroll
+        for (int i = 0; i < MG; ++i) {
+            const int gi = max(min(ga + i, gb - 1), 0);
+            w[i][0] = R::template load<true>(c.rg, gi, kq);
+            w[i][1] = R::template load<true>(c.ru, gi, kq);
+#pragma unroll
+            for (int t = 0; t < SPL; ++t) x[i * SPL + t] = ld16(c.xr + step_k<SPL>(gi * SPL + t, kq));
+        }
+    };
+    auto finish = [&](const WR (&w)[MG][2], const uint4 (&x)[MG * SPL], const Ctx& c) {
+        f32x4 ag = f32x4{}, au = f32x4{};
+        const bool xok = j < c.nrows;
+#pragma unroll
+        for (int i = 0; i < MG; ++i)
+            if (ga + i < gb)
+#pragma unroll
+                for (int t = 0; t < SPL; ++t) {
+                    if constexpr (R::kF16) {
+                        const uint4 xv = sel4(xok, c.xh ? x[i * SPL + t] : bf16x8_to_f16x8(x[i * SPL + t]));
+                        ag = mfma16_f16(R::template frag<true>(w[i][0], t), xv, ag);
+                        au = mfma16_f16(R::template frag<true>(w[i][1], t), xv, au);
+                    } else {
+                        const uint4 xv = sel4(xok, x[i * SPL + t]);
+                        ag = mfma16(R::template frag<true>(w[i][0], t), xv, ag);
+                        au = mfma16(R::template frag<true>(w[i][1], t), xv, au);
+                    }
+                }
+        // lane (kq, j) holds f rows 4 kq + r of segment row j
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            red.v[buf][wave][0][(4 * kq + r) * 17 + j] = ag[r];
+            red.v[buf][wave][1][(4 * kq + r) * 17 + j] = au[r];
+        }
+        __syncthreads();
+        // thread e: segment row e / 16, f row e % 16 (16 consecutive outputs of a row)
+        if (threadIdx.x < 256) {
+            const int sr = threadIdx.x >> 4, fr = threadIdx.x & 15;
+            if (sr < c.nrows) {
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int v = 0; v < W; ++v) {
+                    g += red.v[buf][v][0][fr * 17 + sr];
+                    u += red.v[buf][v][1][fr * 17 + sr];
+                }
+                const float h = silu(g * c.tg) * (u * c.tu);
+                d.H[(size_t)(c.row0 + sr) * d.Hs + c.f0 + fr] =
+                    R::kF16 ? __builtin_bit_cast(uint16_t, (_Float16)h) : (uint16_t)f2bf(h);
+            }
+        }
+        buf ^= 1;
+    };
+    Ctx cur, nxt;
+    int m = next_valid(first, cur);
+    if (m >= end) return;
+    WR wa[MG][2], wb[MG][2];
+    uint4 xa[MG * SPL], xb[MG * SPL];
+    load(wa, xa, cur);
+    while (true) {
+        int mn = next_valid(m + grid, nxt);
+        if (mn < end) load(wb, xb, nxt);
+        finish(wa, xa, cur);
+        if (mn >= end) return;
+        cur = nxt;
+        m = mn;
+        mn = next_valid(m + grid, nxt);
+        if (mn < end) load(wa, xa, nxt);
+        finish(wb, xb, cur);
+        if (mn >= end) return;
+        cur = nxt;
+        m = mn;
+    }
+}
+
+// grid: one workgroup per compute unit; W waves.  RNV as for decode_gu_kernel.  MG: largest run
+// of bf16 weight groups (32 values) a wave takes, MG4: of 4-bit groups (128 values).
+template <int W, int MG, int MG4, int Q, int RNV>
+__global__ __launch_bounds__(64 * W) void decode_gu_split_kernel(const DecodeExperts<Q> d, const GuRoute r) {
+    const int j = threadIdx.x & 15;
+    const int T = d.seg.T, k = d.seg.k, E = d.seg.E;
+    extern __shared__ int4 gdsm[];
+    __shared__ typename std::conditional<(RNV > 0), RouteScratch, int>::type sm;
+    __shared__ int sntiles;
+    __shared__ GuRed<W> red;
+    Tile* stiles = reinterpret_cast<Tile*>(gdsm);
+    int nt;
+    const Tile* tiles;
+    if constexpr (RNV > 0) {
+        RouteOut out{};
+        if (blockIdx.x == 0) out = r.out;
+        route_block<RNV>(r.logits, r.logits2, T, E, k, r.BM, r.has_shared, out, sm, stiles, &sntiles);
+        __syncthreads();
+        nt = sntiles;
+        tiles = stiles;
+    } else {
+        nt = *d.seg.ntiles;
+        tiles = d.seg.tiles;
+    }
+    // items of tiles [0, nr) are routed, the rest (the shared expert's tiles, last in the list)
+    // are not: in a 4-bit layer the two kinds are read through different row readers
+    int nr = nt;
+    if constexpr (Q != 0)
+        while (nr > 0 && tiles[nr - 1].seg == E) --nr;
+    auto item_of = [&](auto rtag, int item) {
+        using R = typename decltype(rtag)::type;
+        struct Ctx {
+            typename R::Row rg, ru;
+            const uint16_t* xr;
+            int row0, nrows, f0;
+            float tg, tu;
+            bool valid, xh;
+        };
+        Ctx c;
+        const int tile = item / d.nblocks, blk = item - tile * d.nblocks;
+        const Tile tl = tiles[tile];
+        typename ExpertRows<Q>::Mat mats[3];
+        int Fseg;
+        bool mx;
+        segment_mats<Q>(d.experts, d.rec_bytes, d.shared, tl.seg, E, d.F, d.Fs, d.L, mats, Fseg, mx);
+        c.f0 = blk * 16;
+        c.valid = c.f0 < Fseg;  // widths are multiples of 16
+        const int p = tl.row0 + min(j, tl.nrows - 1);
+        int tok;
+        if constexpr (RNV > 0)
+            tok = tl.seg == E ? p - T * k : sm.stok[p];
+        else
+            tok = d.seg.token_of(tl.seg, p);
+        if constexpr (std::is_same<R, ExpertRows<0>>::value) {
+            ExpertRows<0>::Mat b[3];
+            if constexpr (Q != 0)
+                bf16_mats<Q>(mats, b);
+            else
+                for (int i = 0; i < 3; ++i) b[i] = mats[i];
+            c.rg = R::row(b[0], c.f0 + j, d.L);
+            c.ru = R::row(b[1], c.f0 + j, d.L);
+        } else {
+            c.rg = R::row(mats[0], c.f0 + j, d.L);
+            c.ru = R::row(mats[1], c.f0 + j, d.L);
+        }
+        c.xh = R::kF16 && d.z16h != nullptr;
+        c.xr = (c.xh ? d.z16h : d.z16) + (size_t)tok * d.L;
+        c.row0 = tl.row0;
+        c.nrows = tl.nrows;
+        c.tg = mats[0].ts;
+        c.tu = mats[1].ts;
+        return c;
+    };
+    int buf = 0;
+    const int nitems = nt * d.nblocks, nrouted = nr * d.nblocks;
+    if constexpr (Q == 0) {
+        auto of = [&](int item) { return item_of(TypeTag<ExpertRows<0>>{}, item); };
+        gu_split_run<W, MG, ExpertRows<0>>(d, blockIdx.x, nitems, of, red, buf);
+    } else {
+        auto of4 = [&](int item) { return item_of(TypeTag<Fp4Rows<Q>>{}, item); };
+        gu_split_run<W, MG4, Fp4Rows<Q>>(d, blockIdx.x, nrouted, of4, red, buf);
+        // the workgroup's first shared item: the first of its sequence at or after nrouted
+        const int g = gridDim.x;
+        const int fs = nrouted + (int)(((unsigned)blockIdx.x + g - (unsigned)(nrouted % g)) % g);
+        auto of16 = [&](int item) { return item_of(TypeTag<ExpertRows<0>>{}, item); };
+        gu_split_run<W, MG, ExpertRows<0>>(d, fs, nitems, of16, red, buf);
+    }
+}
+
 // ---- down + merge -----------------------------------------------------------------------------
 // A wave's tiles i0, i0 + W, ... (positions [ib, ie) of its sequence) as one stream of chunks
 // (CH weight groups of one tile each, read through R) with the next chunk always in flight,

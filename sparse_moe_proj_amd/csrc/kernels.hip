@@ -342,6 +342,9 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_GU_CHUNK
 #define LMOE_GU_CHUNK 4
 #endif
+#ifndef LMOE_GU_SPLIT
+#define LMOE_GU_SPLIT 1
+#endif
 #ifndef LMOE_GU_CHUNK4
 #define LMOE_GU_CHUNK4 1
 #endif
@@ -460,14 +463,23 @@ hipError_t small_proj_launch(const SmallProj& p, hipStream_t s) {
 
 hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const uint16_t* Gr, const float* br, int T,
                                   int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s,
-                                  uint16_t* z16h) {
+                                  uint16_t* z16h, const float* hnorm) {
     if (!small_proj_fits(T, H)) return hipErrorInvalidValue;
-    SmallProj p{x, nullptr, 0, D, T, L, H, 0, z32, z16, Gr, br, E, logits, z16h};
-    auto k = small_proj_kernel<LMOE_SP_WAVES, LMOE_SP_SMAX, 0>;
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k, dim3((unsigned)(cdiv(L, 16) + 2 * cdiv(E, 16))), dim3(64 * LMOE_SP_WAVES), small_proj_lds(H), s, p);
+    SmallProj p{x, hnorm, 0, D, T, L, H, 0, z32, z16, Gr, br, E, logits, z16h};
+    const dim3 grid((unsigned)(cdiv(L, 16) + 2 * cdiv(E, 16)));
+    if (hnorm) {
+        auto k = small_proj_kernel<LMOE_SP_WAVES, LMOE_SP_SMAX, 2>;
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(k, grid, dim3(64 * LMOE_SP_WAVES), small_proj_lds(H), s, p);
+    } else {
+        auto k = small_proj_kernel<LMOE_SP_WAVES, LMOE_SP_SMAX, 0>;
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(k, grid, dim3(64 * LMOE_SP_WAVES), small_proj_lds(H), s, p);
+    }
     return last();
 }
 
@@ -499,10 +511,12 @@ hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, in
 }
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
-                            uint16_t* out16, hipStream_t s, uint16_t* out16lo, uint16_t* out16h) {
-    if (T <= kStreamMaxT && small_proj_fits(T, K))
-        return small_proj_launch<0>(
-            SmallProj{x, nullptr, 0, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0, nullptr, out16h}, s);
+                            uint16_t* out16, hipStream_t s, uint16_t* out16lo, uint16_t* out16h, const float* hnorm) {
+    if (T <= kStreamMaxT && small_proj_fits(T, K)) {
+        const SmallProj p{x, hnorm, 0, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0, nullptr, out16h};
+        return hnorm ? small_proj_launch<2>(p, s) : small_proj_launch<0>(p, s);
+    }
+    if (hnorm) return hipErrorInvalidValue;  // the caller normalises first for the other forms
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1, StreamProj, kProjChunk>(StreamProj{x, W, T, N, K, mode, out32, out16},
                                                                    (int)cdiv(T, 16), N, s);
@@ -606,6 +620,8 @@ int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
 // LMOE_GU_WAVES waves per compute unit, then the down projection and merge over LMOE_DC_GROUPS
 // groups of the work list.
 constexpr int kGuWaves = LMOE_GU_WAVES, kGuChunk = LMOE_GU_CHUNK, kGuChunk4 = LMOE_GU_CHUNK4;
+// K-split gate/up: largest runs of bf16 (32-value) and 4-bit (128-value) weight groups per wave
+constexpr int kGuMG = 7, kGuMG4 = 2;
 constexpr int kDcWaves = LMOE_DC_WAVES, kDcChunk = LMOE_DC_CHUNK, kDcChunk4 = LMOE_DC_CHUNK4, kDcGroups = LMOE_DC_GROUPS;
 
 int decode_groups() { return kDcGroups; }
@@ -627,14 +643,23 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
                        a.w,     a.mpart, kDcGroups, a.rowinfo, a.max_tiles};
     const long items = (long)a.max_tiles * nblocks;
     ev.begin(kStageUp);
-    const long grid = std::max<long>(std::min<long>(cdiv(items, kGuWaves), cu_count()), 1);
+    // The K-split form when every wave's run of weight groups fits its registers and there are at
+    // most as many items as waves on the chip (measured: at T = 1 it keeps all waves busy and
+    // saves a fifth of the step; at T >= 8 one item per wave streams as fast or faster).
+    const bool split = LMOE_GU_SPLIT && a.L / 32 <= kGuWaves * kGuMG &&
+                       (Q == 0 || a.L / 128 <= kGuWaves * kGuMG4) && items <= (long)cu_count() * kGuWaves;
+    const long grid = std::max<long>(std::min<long>(split ? items : cdiv(items, kGuWaves), cu_count()), 1);
     if (a.route) {  // the launch routes the batch itself (top-k and permutation in every workgroup)
         const GuRoute r{a.route->logits, a.route->logits2, a.route->BM, a.route->has_shared, a.route->out};
         const size_t lds = (size_t)a.max_tiles * sizeof(Tile);
         const int E = a.E;
 #define LMOE_GU_ROUTED(NV)                                                                                          \
-    hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, NV>), dim3((unsigned)grid),             \
-                       dim3(64 * kGuWaves), lds, s, d, r)
+    if (split)                                                                                                      \
+        hipLaunchKernelGGL((decode_gu_split_kernel<kGuWaves, kGuMG, kGuMG4, Q, NV>), dim3((unsigned)grid),         \
+                           dim3(64 * kGuWaves), lds, s, d, r);                                                      \
+    else                                                                                                            \
+        hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, NV>), dim3((unsigned)grid),         \
+                           dim3(64 * kGuWaves), lds, s, d, r)
         if (E <= 64)
             LMOE_GU_ROUTED(1);
         else if (E <= 128)
@@ -646,6 +671,9 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
         else
             LMOE_GU_ROUTED(16);
 #undef LMOE_GU_ROUTED
+    } else if (split) {
+        hipLaunchKernelGGL((decode_gu_split_kernel<kGuWaves, kGuMG, kGuMG4, Q, 0>), dim3((unsigned)grid),
+                           dim3(64 * kGuWaves), 0, s, d, GuRoute{});
     } else {
         hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, 0>), dim3((unsigned)grid),
                            dim3(64 * kGuWaves), 0, s, d, GuRoute{});

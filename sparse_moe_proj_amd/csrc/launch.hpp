@@ -66,8 +66,11 @@ hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream
 // mode 0: out32 = xW^T and out16 = bf16(out32); 1: out16 = bf16(xW^T); 2: out32 += xW^T
 // out16lo (mode 0, T > kStreamMaxT, optional): also write the low bf16 half of the output.
 // out16h (mode 0, small batches, optional): also write fp16 of the output.
+// hnorm (small batches staged in LDS only, i.e. T <= kStreamMaxT and small_proj_fits): the input
+// is bf16(RMSNorm(hnorm)) of an fp32 residual [T][K] (unit gain, eps 1e-6) instead of x.
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
-                            uint16_t* out16, hipStream_t s, uint16_t* out16lo = nullptr, uint16_t* out16h = nullptr);
+                            uint16_t* out16, hipStream_t s, uint16_t* out16lo = nullptr, uint16_t* out16h = nullptr,
+                            const float* hnorm = nullptr);
 
 // zhi/zlo (T > kStreamMaxT, optional): the bf16 halves of z written by the D projection.
 hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
@@ -99,9 +102,10 @@ int decode_groups();
 
 // Small batch: z = x D^T (z32 and bf16 z16) and the folded router's logits in one launch:
 // logits [2][T][E], logits[0] = x hi^T + br, logits[1] = x lo^T (the top-k adds them).
+// hnorm (optional): x is bf16(RMSNorm(hnorm)) of an fp32 residual [T][H], formed while staging.
 hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const uint16_t* Gr, const float* br, int T,
                                   int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s,
-                                  uint16_t* z16h = nullptr);
+                                  uint16_t* z16h = nullptr, const float* hnorm = nullptr);
 // Gr [E][2][H] = hi and lo bf16 halves of Wr . D (fp32 accumulation).
 hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int L, int H, uint16_t* Gr, hipStream_t s);
 

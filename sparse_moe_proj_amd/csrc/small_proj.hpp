@@ -3,9 +3,11 @@
 // The work is reading W once from HBM.  A workgroup owns 16 weight rows; its W waves split K
 // into contiguous ranges and each wave requests all weight units of its range (up to SMAX MFMA
 // steps at a time) before anything else, so the whole range is in flight at once.  While those
-// loads travel, the workgroup stages the activations of the first 16 tokens into LDS as bf16 (XM = 0: a bf16 [T][K]
-// input; XM = 1: the sum, in order, of G fp32 partial inputs [G][T][K], rounded once), so the
-// token operand is read from LDS rather than once per wave from L2.  Further groups of 16 tokens
+// loads travel, the workgroup stages the activations of the first 16 tokens into LDS as bf16
+// (XM = 0: a bf16 [T][K] input; XM = 1: the sum, in order, of G fp32 partial inputs [G][T][K],
+// rounded once; XM = 2: bf16(RMSNorm(h)) of an fp32 residual h [T][K] with unit gain, each
+// token's sum of squares taken by one wave in a fixed order), so the token operand is read from
+// LDS rather than once per wave from L2.  Further groups of 16 tokens
 // are staged in turn and reuse the weights held in registers.  The MFMA is
 // v_mfma_f32_16x16x32_bf16 with the weights as A (16 rows) and the tokens as B (columns past T
 // are zero).  The waves' partial tiles meet in LDS and are summed in wave order.  A second
@@ -18,7 +20,7 @@ namespace lmoe {
 
 struct SmallProj {
     const uint16_t* x16;  // XM 0: [T][K] bf16
-    const float* xpart;   // XM 1: [G][T][K] fp32
+    const float* xpart;   // XM 1: [G][T][K] fp32; XM 2: the residual h [T][K] fp32
     int G;
     const uint16_t* W;    // [N][K] bf16
     int T, N, K, mode;    // mode 0: out32 = v, out16 = bf16(v); 1: out16 = bf16(v); 2: out32 += v
@@ -33,6 +35,7 @@ struct SmallProj {
     int E;
     float* logits;  // [2][T][E]
     uint16_t* out16h;  // mode 0, optional: fp16(v) as well (the token operand of 4-bit experts)
+    float eps = 1e-6f;  // XM 2: the RMSNorm epsilon
 };
 
 // Largest staged-activation LDS a small-batch projection takes (plus W KB of static LDS).
@@ -49,6 +52,7 @@ template <int W, int SMAX, int XM>
 __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
     extern __shared__ uint4 xs[];  // [16][K / 8 + 1]: the current token group
     __shared__ float red[W][256];
+    __shared__ float rnorm[16];  // XM 2: 1 / rms of the group's tokens
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = lane >> 4, j = lane & 15;
     const int K = p.K, T = p.T;
@@ -81,11 +85,32 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
                 __syncthreads();  // the previous group's LDS reads are done
                 if (!single && s0 < s1) loadw(s0);
             }
+            if constexpr (XM == 2) {
+                for (int t = wave; t < tn; t += W) {
+                    const float4* row = reinterpret_cast<const float4*>(p.xpart + (size_t)(t0 + t) * K);
+                    float ss = 0.f;
+                    for (int c = lane; c < K / 4; c += 64) {
+                        const float4 u = row[c];
+                        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+                    }
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+                    if (lane == 0) rnorm[t] = 1.0f / sqrtf(ss / (float)K + p.eps);
+                }
+                __syncthreads();
+            }
             for (int e = threadIdx.x; e < tn * per; e += 64 * W) {
                 const int t = e / per, c = e - t * per;
                 uint4 v;
                 if constexpr (XM == 0) {
                     v = ld16(p.x16 + (size_t)(t0 + t) * K + c * 8);
+                } else if constexpr (XM == 2) {
+                    const float* src = p.xpart + (size_t)(t0 + t) * K + c * 8;
+                    const float4 u0 = *reinterpret_cast<const float4*>(src);
+                    const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+                    const float r = rnorm[t];
+                    v = make_uint4(pack_bf2(u0.x * r, u0.y * r), pack_bf2(u0.z * r, u0.w * r), pack_bf2(u1.x * r, u1.y * r),
+                                   pack_bf2(u1.z * r, u1.w * r));
                 } else {
                     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                     for (int q = 0; q < p.G; ++q) {

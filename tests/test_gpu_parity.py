@@ -97,6 +97,32 @@ def test_small_bf16_router_unfolded(T, ws):
     check_block(lw, x, "bf16", out, label=f"small_bf16 unfolded T={T}")
 
 
+@pytest.mark.parametrize("fold", [True, False])
+@pytest.mark.parametrize("T", [5, 40, 100])
+def test_small_prenorm_residual(T, fold, ws):
+    """Pre-RMSNorm input and fp32 residual update (the stack's layer form) on each D path: the
+    normalisation formed while staging the D launch (T <= 16, or with the folded router up to
+    64 tokens) or by its own launch (otherwise)."""
+    wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
+    dl = DeviceLayer(lw, act="bf16", fold=fold)
+    k = lw.shape.top_k
+    h = gen.make_residual(wl, T=T).astype(np.float32)
+    hbuf = to_device(h)
+    out = run_forward(dl, hbuf, ws, prenorm=1, residual=1, y=hbuf)
+    torch.cuda.synchronize()
+    L = oracle.Layer(lw)
+    xo = oracle.round_to_bf16(oracle.rmsnorm(h.astype(np.float64)))
+    ids_o, _, gap_o, logits_o = oracle.route(xo @ L.D.T, L.Wr, L.br, k)
+    ids_g = host(out["ids"])
+    same, _ = check_routing(ids_g, ids_o, gap_o, logits_o, k)
+    forced = {t: ids_g[t] for t in range(T) if not same[t]}
+    o = oracle.block_forward(L, xo, forced_ids=forced)
+    y_gpu = host(hbuf).astype(np.float64) - h.astype(np.float64)
+    err = normwise_rel(y_gpu, o["y"]).max()
+    log(f"[prenorm T={T} fold={fold}] rel={err:.3e} differing={int((~same).sum())}")
+    assert err <= TOL["bf16"]
+
+
 def test_fold_router_halves():
     """hi + lo of the folded router carries G = Wr . D to the precision the halves allow."""
     wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
