@@ -52,6 +52,9 @@ class Shape:
     top_k: int
     ffn: int
     shared_ffn: int  # 0 = no shared expert
+    # Expert groups with their own D/U pair: experts g*E/G .. (g+1)*E/G - 1 form group g, D is
+    # [G*latent][hidden] (group g's rows g*latent ..), U is [hidden][G*latent] (its columns).
+    groups: int = 1
 
     def record_elems(self, ffn: Optional[int] = None) -> int:
         f = self.ffn if ffn is None else ffn
@@ -71,6 +74,9 @@ EDGE0_145B = Shape(hidden=2560, latent=1792, n_experts=512, top_k=10, ffn=640, s
 # The 120B model: the pages give only its latent width (1280); the other dimensions are read as
 # the 145B's (same family, same expert pool layout).
 EDGE0_120B = Shape(hidden=2560, latent=1280, n_experts=512, top_k=10, ffn=640, shared_ffn=640)
+# The release report's description of the sharing (section "Edge0 的内部机制"): every 64 experts
+# form a group that shares one pair of large matrices, so 512 experts have 8 D/U pairs.
+EDGE0_145B_G64 = Shape(hidden=2560, latent=1792, n_experts=512, top_k=10, ffn=640, shared_ffn=640, groups=8)
 
 
 @dataclass(frozen=True)
@@ -97,6 +103,7 @@ WORKLOADS = {
                                  layers=48, expert_banks=2),
     "decode120_t8": Workload(6, "decode120_t8", EDGE0_120B, 8, "bf16", "bf16", "bf16", "zipf"),
     "decode_nvfp4_t8": Workload(7, "decode_nvfp4_t8", EDGE0_145B, 8, "bf16", "bf16", "nvfp4", "zipf"),
+    "decode_group64_t8": Workload(8, "decode_group64_t8", EDGE0_145B_G64, 8, "bf16", "bf16", "bf16", "zipf"),
 }
 
 
@@ -307,9 +314,10 @@ def make_layer(wl: Workload, layer: int = 0, threads: Optional[int] = None,
     """One layer's weights.  `experts` may pass in the already drawn records of this layer's
     expert bank (expert_bank(wl, layer)) so that banks shared by several layers are drawn once."""
     s = wl.shape
-    H, L, E = s.hidden, s.latent, s.n_experts
-    D = _encode(normal_f32(rng_for(wl.wid, layer, T_D), L * H, 1.0 / np.sqrt(H)), wl.dense).reshape(L, H)
-    U = _encode(normal_f32(rng_for(wl.wid, layer, T_U), H * L, 1.0 / np.sqrt(L)), wl.dense).reshape(H, L)
+    H, L, E, G = s.hidden, s.latent, s.n_experts, s.groups
+    # with expert groups: G stacked D matrices [G*L][H]; U [H][G*L], each group's U ~ N(0, 1/L)
+    D = _encode(normal_f32(rng_for(wl.wid, layer, T_D), G * L * H, 1.0 / np.sqrt(H)), wl.dense).reshape(G * L, H)
+    U = _encode(normal_f32(rng_for(wl.wid, layer, T_U), H * G * L, 1.0 / np.sqrt(L)), wl.dense).reshape(H, G * L)
     Wr = _encode(normal_f32(rng_for(wl.wid, layer, T_WR), E * L, 1.0 / np.sqrt(L)), wl.dense).reshape(E, L)
     br = router_bias(wl, layer)
     shared = None

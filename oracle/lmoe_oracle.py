@@ -17,6 +17,14 @@ readings taken here (softmax over the selected logits, lower id wins exact ties,
 ascending expert id, shared expert weight 1, bias-free projections except the router) are
 the plainest ones consistent with the caption and are listed with the design notes.
 
+The release report "1450 亿参数端侧模型 Edge0-145B 开源" (section "Edge0 的内部机制", paragraph
+"架构：在稀疏专家之间共享大型矩阵") describes the sharing per group instead: every 64 experts form a group sharing one pair of large
+matrices.  With G groups (shape.groups; 1 is the model-detail page's form) group g owns D_g
+and U_g; expert e is in group e // (E / G); its router row and its SwiGLU read that group's
+latent z_g = x D_g^T, its weighted output joins that group's merged row m_g, and
+y = sum_g m_g U_g^T.  The pages do not place the shared expert; it is read here as a member
+of group 0 (z_0 in, m_0 out), which for G = 1 is the form above.
+
 Every function below is written in the order the caption describes, with no blocking or
 fusion: one numpy matmul per projection, explicit loops over tokens and chosen experts.
 """
@@ -137,12 +145,24 @@ def swiglu(z: np.ndarray, gate: np.ndarray, up: np.ndarray, down: np.ndarray) ->
     return (silu(z @ gate.T) * (z @ up.T)) @ down.T
 
 
-def route(z: np.ndarray, Wr: np.ndarray, br: np.ndarray, k: int):
-    """Router: logits = z Wr^T + br; keep the k largest (a lower expert id wins an exact tie);
-    weights = softmax over the k kept logits (equal to a softmax over all E renormalised over
-    the kept ones).  Returns ids [T][k] in ascending expert id, weights [T][k] in the same
-    order, the 10th/11th gap lambda_(k) - lambda_(k+1) per token (inf when E == k), and logits."""
-    logits = z @ Wr.T + br[None, :]
+def router_logits(z: np.ndarray, Wr: np.ndarray, br: np.ndarray, groups: int = 1) -> np.ndarray:
+    """logits[t][e] = z_{g(e)}[t] . Wr[e] + br[e]; z is [T][groups * latent] (group g's latent
+    in columns g*latent ..), expert e in group e // (E / groups)."""
+    E, L = Wr.shape
+    Eg = E // groups
+    logits = np.empty((z.shape[0], E))
+    for g in range(groups):
+        logits[:, g * Eg:(g + 1) * Eg] = z[:, g * L:(g + 1) * L] @ Wr[g * Eg:(g + 1) * Eg].T
+    return logits + br[None, :]
+
+
+def route(z: np.ndarray, Wr: np.ndarray, br: np.ndarray, k: int, groups: int = 1):
+    """Router: logits = z Wr^T + br (per expert group, see router_logits); keep the k largest
+    (a lower expert id wins an exact tie); weights = softmax over the k kept logits (equal to a
+    softmax over all E renormalised over the kept ones).  Returns ids [T][k] in ascending expert
+    id, weights [T][k] in the same order, the 10th/11th gap lambda_(k) - lambda_(k+1) per token
+    (inf when E == k), and logits."""
+    logits = router_logits(z, Wr, br, groups)
     T, E = logits.shape
     order = np.argsort(-logits, axis=1, kind="stable")   # stable: equal values keep id order
     chosen = np.sort(order[:, :k], axis=1)
@@ -209,8 +229,10 @@ def block_forward(layer: Layer, x: np.ndarray, forced_ids: dict | None = None):
     choice (the weights are then the softmax over those experts' logits).
     Returns dict(y, z, ids, w, gap, logits, m)."""
     s = layer.shape
-    z = x @ layer.D.T                                   # D: hidden -> latent
-    ids, w, gap, logits = route(z, layer.Wr, layer.br, s.top_k)
+    G, L = s.groups, s.latent
+    Eg = s.n_experts // G
+    z = x @ layer.D.T                                   # D: hidden -> latent (each group's D_g)
+    ids, w, gap, logits = route(z, layer.Wr, layer.br, s.top_k, G)
     if forced_ids:
         ids = ids.copy()
         w = w.copy()
@@ -221,14 +243,16 @@ def block_forward(layer: Layer, x: np.ndarray, forced_ids: dict | None = None):
             ids[t] = fid
             w[t] = ee / ee.sum()
     T = x.shape[0]
-    m = np.zeros((T, s.latent))
+    m = np.zeros((T, G * L))                            # m_g in columns g*L ..
     if layer.shared is not None:
-        m += swiglu(z, *layer.shared)                   # shared expert, weight 1
+        m[:, :L] += swiglu(z[:, :L], *layer.shared)     # shared expert, weight 1 (group 0)
     for t in range(T):
         for slot in range(s.top_k):                     # slots in ascending expert id
-            g, u, d = layer.expert(int(ids[t, slot]))
-            m[t] += w[t, slot] * swiglu(z[t:t + 1], g, u, d)[0]
-    y = m @ layer.U.T                                   # U: latent -> hidden
+            e = int(ids[t, slot])
+            c = (e // Eg) * L                           # the expert's group
+            g, u, d = layer.expert(e)
+            m[t, c:c + L] += w[t, slot] * swiglu(z[t:t + 1, c:c + L], g, u, d)[0]
+    y = m @ layer.U.T                                   # U: latent -> hidden (sum over groups)
     return dict(y=y, z=z, ids=ids, w=w, gap=gap, logits=logits, m=m)
 
 

@@ -22,12 +22,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 def make_f32_layer(shape, seed, shared=True, same_experts=False, br=None):
     rng = np.random.default_rng(seed)
-    H, L, E, F = shape.hidden, shape.latent, shape.n_experts, shape.ffn
+    H, L, E, F, G = shape.hidden, shape.latent, shape.n_experts, shape.ffn, shape.groups
 
     def mat(r, c, fan):
         return (rng.standard_normal((r, c)) / math.sqrt(fan)).astype(np.float32)
 
-    D, U, Wr = mat(L, H, H), mat(H, L, L), mat(E, L, L)
+    D, U, Wr = mat(G * L, H, H), mat(H, G * L, L), mat(E, L, L)
     if br is None:
         br = (0.3 * rng.standard_normal(E)).astype(np.float32)
 
@@ -48,9 +48,12 @@ def py_silu(v):
 
 
 def brute_forward(lw, x):
-    """Scalar-loop latent-MoE block in pure Python floats."""
+    """Scalar-loop latent-MoE block in pure Python floats.  With expert groups, expert e is in
+    group e // (E / G), which owns D rows and U columns g*L .. g*L + L - 1; the shared expert
+    is in group 0."""
     s = lw.shape
-    H, L, E, k, F = s.hidden, s.latent, s.n_experts, s.top_k, s.ffn
+    H, L, E, k, F, G = s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.groups
+    Eg = E // G
     D = lw.D.astype(float).tolist()
     U = lw.U.astype(float).tolist()
     Wr = lw.Wr.astype(float).tolist()
@@ -74,8 +77,8 @@ def brute_forward(lw, x):
 
     out = []
     for xt in x.astype(float).tolist():
-        zt = [sum(xt[i] * D[j][i] for i in range(H)) for j in range(L)]
-        lam = [sum(zt[i] * Wr[e][i] for i in range(L)) + br[e] for e in range(E)]
+        zg = [[sum(xt[i] * D[g * L + j][i] for i in range(H)) for j in range(L)] for g in range(G)]
+        lam = [sum(zg[e // Eg][i] * Wr[e][i] for i in range(L)) + br[e] for e in range(E)]
         top = sorted(range(E), key=lambda e: (-lam[e], e))[:k]
         # full softmax over all experts, then renormalise over the kept ones
         mx = max(lam)
@@ -83,15 +86,16 @@ def brute_forward(lw, x):
         z_all = sum(p)
         p = [v / z_all for v in p]
         norm = sum(p[e] for e in top)
-        m = [0.0] * L
+        m = [[0.0] * L for _ in range(G)]
         if lw.shared is not None:
-            so = expert_out(zt, split(lw.shared, s.shared_ffn), s.shared_ffn)
-            m = [a + b for a, b in zip(m, so)]
+            so = expert_out(zg[0], split(lw.shared, s.shared_ffn), s.shared_ffn)
+            m[0] = [a + b for a, b in zip(m[0], so)]
         for e in sorted(top):
-            yo = expert_out(zt, split(lw.experts[e], F), F)
+            g = e // Eg
+            yo = expert_out(zg[g], split(lw.experts[e], F), F)
             wgt = p[e] / norm
-            m = [a + wgt * b for a, b in zip(m, yo)]
-        out.append([sum(m[i] * U[r][i] for i in range(L)) for r in range(H)])
+            m[g] = [a + wgt * b for a, b in zip(m[g], yo)]
+        out.append([sum(m[g][i] * U[r][g * L + i] for g in range(G) for i in range(L)) for r in range(H)])
     return np.array(out)
 
 
@@ -112,6 +116,52 @@ def test_forward_brute_force_no_shared_rect_shapes():
     x = np.random.default_rng(4).standard_normal((4, s.hidden)).astype(np.float32)
     got = oracle.block_forward(oracle.Layer(lw), x.astype(np.float64))["y"]
     np.testing.assert_allclose(got, brute_forward(lw, x), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("G", [2, 3])
+def test_grouped_forward_matches_scalar_brute_force(G):
+    # the launch blog's form: every group of experts owns its own D/U pair
+    s = gen.Shape(hidden=6, latent=4, n_experts=3 * G, top_k=3, ffn=3, shared_ffn=2, groups=G)
+    lw = make_f32_layer(s, 11 + G)
+    x = np.random.default_rng(12).standard_normal((4, s.hidden)).astype(np.float32)
+    got = oracle.block_forward(oracle.Layer(lw), x.astype(np.float64))["y"]
+    np.testing.assert_allclose(got, brute_forward(lw, x), rtol=1e-12, atol=1e-13)
+
+
+def test_grouped_with_tied_pairs_equals_one_pair():
+    # every group holding the same D and U: y = sum_g U m_g = U sum_g m_g, the one-pair block
+    G = 4
+    s1 = gen.Shape(hidden=8, latent=6, n_experts=8, top_k=3, ffn=4, shared_ffn=4)
+    lw1 = make_f32_layer(s1, 21)
+    sg = gen.Shape(hidden=8, latent=6, n_experts=8, top_k=3, ffn=4, shared_ffn=4, groups=G)
+    lwg = gen.LayerWeights(sg, "f32", "f32", np.concatenate([lw1.D] * G, axis=0), np.concatenate([lw1.U] * G, axis=1),
+                           lw1.Wr, lw1.br, lw1.shared, lw1.experts)
+    x = np.random.default_rng(22).standard_normal((5, 8))
+    a = oracle.block_forward(oracle.Layer(lw1), x)
+    b = oracle.block_forward(oracle.Layer(lwg), x)
+    assert np.array_equal(a["ids"], b["ids"])
+    np.testing.assert_allclose(b["y"], a["y"], rtol=1e-12, atol=1e-13)
+
+
+def test_group_locality():
+    # tokens routed only inside group 1 (no shared expert) depend on U's group-1 columns alone
+    G, L = 3, 5
+    s = gen.Shape(hidden=7, latent=L, n_experts=6, top_k=2, ffn=3, shared_ffn=0, groups=G)
+    br = np.zeros(6, np.float32)
+    br[2:4] = 50.0  # experts 2, 3 = group 1
+    lw = make_f32_layer(s, 31, shared=False, br=br)
+    x = np.random.default_rng(32).standard_normal((4, 7))
+    y = oracle.block_forward(oracle.Layer(lw), x)
+    assert np.all(y["ids"] == [2, 3])
+    U2 = lw.U.copy()
+    U2[:, :L] = 0
+    U2[:, 2 * L:] = 0
+    y2 = oracle.block_forward(oracle.Layer(gen.LayerWeights(s, "f32", "f32", lw.D, U2, lw.Wr, lw.br, None, lw.experts)), x)
+    np.testing.assert_array_equal(y2["y"], y["y"])
+    U3 = lw.U.copy()
+    U3[:, L:2 * L] = 0
+    y3 = oracle.block_forward(oracle.Layer(gen.LayerWeights(s, "f32", "f32", lw.D, U3, lw.Wr, lw.br, None, lw.experts)), x)
+    assert np.all(y3["y"] == 0)
 
 
 def test_topk_bruteforce_with_exact_ties():
@@ -445,6 +495,16 @@ def test_page_shapes_pin_the_120b_latent_width():
     # the other dimensions are read as the 145B's (the pages give none for the 120B)
     a, b = gen.EDGE0_120B, gen.EDGE0_145B
     assert (a.hidden, a.n_experts, a.top_k, a.ffn, a.shared_ffn) == (b.hidden, b.n_experts, b.top_k, b.ffn, b.shared_ffn)
+
+
+def test_page_shapes_pin_the_expert_groups():
+    with open(os.path.join(HERE, "golden", "page_shapes.json")) as f:
+        g = json.load(f)
+    s = gen.EDGE0_145B_G64
+    assert s.n_experts // s.groups == g["experts_per_group"]["value"]
+    assert s.n_experts == g["experts_per_layer"]["value"]
+    assert (s.hidden, s.latent, s.top_k, s.ffn) == (gen.EDGE0_145B.hidden, gen.EDGE0_145B.latent, gen.EDGE0_145B.top_k,
+                                                    gen.EDGE0_145B.ffn)
 
 
 @pytest.mark.parametrize("wid", ["tiny_f32", "decode_t8"])
