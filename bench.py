@@ -66,18 +66,19 @@ def algorithmic_counts(wl, ids: np.ndarray, T=None):
     s = wl.shape
     T = wl.T if T is None else T
     H, L, E, k, F, Fs = s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn
+    G = s.groups  # expert groups, each with its own D and U (all of them read: z of every group is formed)
     nd = int(np.unique(ids).size)
     wb = 2  # bf16 dense weights
     rec = {"mxfp4": s.mxfp4_record_bytes(), "nvfp4": s.nvfp4_record_bytes()}.get(wl.expert, 3 * F * L * 2)
     up_w = {"mxfp4": 2 * F * L // 2 + 2 * F * L // 32,
             "nvfp4": 2 * F * L // 2 + 2 * F * L // 16 + 8}.get(wl.expert, 2 * F * L * 2)
-    dense = (2 * H * L + E * L) * wb + E * 4 + 3 * Fs * L * wb
+    dense = (2 * H * L * G + E * L) * wb + E * 4 + 3 * Fs * L * wb
     xin = T * H * (4 if wl.layers > 1 else 2)
     yout = T * H * (4 if wl.layers > 1 else 2)
     layer_bytes = dense + nd * rec + xin + yout
-    flops_tok = 2 * (H * L + L * E + k * 3 * F * L + 3 * Fs * L + L * H)
+    flops_tok = 2 * (H * L * G + L * E + k * 3 * F * L + 3 * Fs * L + L * H * G)
     rows = T * k + (T if Fs else 0)
-    up_bytes = nd * up_w + 2 * Fs * L * wb + T * L * 2 + rows * max(F, Fs) * 2
+    up_bytes = nd * up_w + 2 * Fs * L * wb + T * L * G * 2 + rows * max(F, Fs) * 2
     up_flops = 2 * (T * k * 2 * F * L + (T * 2 * Fs * L if Fs else 0))
     # gate/up launch: the gate and up rows of every touched expert and of the shared expert once,
     # the latent tokens in, SiLU(g) * u out (bf16, one row of the SwiGLU width per segment row)

@@ -19,11 +19,21 @@
  *   - shared expert: weight 1, added to the routed sum before U;
  *   - merged m_t = shared_t + sum over slots (ascending expert id) of w_{t,s} * expert_s(z_t).
  *
+ * Expert groups (lmoe_config.groups = G > 1): the sharing as the release report "1450 亿参数
+ * 端侧模型 Edge0-145B 开源" describes it (section "Edge0 的内部机制": every 64 experts form a group
+ * sharing one pair of large matrices).  Experts g*E/G .. (g+1)*E/G - 1 form group g, which owns
+ * D_g and U_g; z_g = x D_g^T; expert e's router row and SwiGLU read its group's z_g, its
+ * weighted output joins that group's merged row m_g, and y = sum_g m_g U_g^T.  The shared
+ * expert counts as a member of group 0 (a reading: the pages do not place it).  G = 0 or 1 is
+ * the single pair above.
+ *
  * Conventions for every call
  *   - Every tensor argument is a caller-owned DEVICE pointer, row-major with the innermost
  *     dimension contiguous, 16-byte aligned.  Every weight matrix is stored output-major
  *     with its reduction dimension contiguous:
  *         D  [latent][hidden]     U  [hidden][latent]     Wr [n_experts][latent]
+ *     With G expert groups, D is [G*latent][hidden] (group g's rows g*latent ..) and U is
+ *     [hidden][G*latent] (group g's columns g*latent ..).
  *   - An expert record (routed experts and the shared expert) is contiguous:
  *         F32/BF16: gate [ffn][latent], up [ffn][latent], down [latent][ffn] elements;
  *         MXFP4 (routed experts only): gate nibbles [ffn][latent/2], up nibbles
@@ -69,6 +79,9 @@
  * Dimension limits: hidden, latent, ffn, shared_ffn multiples of 64 (shared_ffn may be 0;
  * with 4-bit experts latent, ffn and shared_ffn must be multiples of 128);
  * 1 <= top_k <= 16; top_k <= n_experts <= 1024; 0 <= T <= 2^20 with T*top_k < 2^31.
+ * Expert groups: 1 <= groups <= 64 dividing n_experts; groups > 1 needs act and dense BF16
+ * and a folded router (weights.Gr; otherwise LMOE_ERR_UNSUPPORTED), and lmoe_route, which
+ * takes an fp32 latent, supports one group only.
  */
 #ifndef LMOE_H
 #define LMOE_H
@@ -103,6 +116,7 @@ typedef struct {
     int32_t act_dtype;    /* lmoe_dtype of x, y (and of the block's internal activations) */
     int32_t dense_dtype;  /* lmoe_dtype of D, U, Wr and the shared expert */
     int32_t expert_dtype; /* lmoe_dtype of the routed expert records */
+    int32_t groups;       /* G: expert groups with their own D/U pair (0 or 1: one pair per layer) */
 } lmoe_config;
 
 typedef struct {
@@ -140,7 +154,8 @@ typedef struct {
      * With prenorm and residual both set, x and y may be the same buffer. */
     int32_t residual;
     /* Optional exports (NULL = skip), all device buffers: */
-    float* aux_z;          /* [T][latent] fp32 latent z = x D^T (router input) */
+    float* aux_z;          /* [T][latent] fp32 latent z = x D^T (router input); with G expert
+                              groups [T][G*latent], group g's latent in columns g*latent .. */
     int32_t* aux_ids;      /* [T][top_k] chosen experts, ascending id */
     float* aux_w;          /* [T][top_k] routing weights, same order */
     int32_t* aux_offsets;  /* [n_experts + 1] segment starts of the permutation */
@@ -177,13 +192,16 @@ lmoe_status lmoe_pack_experts(const lmoe_config* cfg, int32_t shared, const void
  * Router folding (a weight step before lmoe_forward; BF16 dense weights only).  The router
  * logits are linear in the block input: z . Wr^T = x . (Wr D)^T with z = x . D^T.
  * lmoe_fold_router computes G = Wr . D ([n_experts][hidden], fp32 accumulation in ascending
- * latent order) and stores it as two bf16 halves, hi = bf16(G) and lo = bf16(G - hi):
+ * latent order; with expert groups, row e of G is Wr[e] . D_{group of e}) and stores it as
+ * two bf16 halves, hi = bf16(G) and lo = bf16(G - hi):
  *   Gr [n_experts][2][hidden]  (lmoe_fold_router_bytes(cfg) bytes; must not overlap D or Wr).
  * With weights->Gr set, lmoe_forward computes the logits of batches of up to 64 tokens as
  * x . hi^T + x . lo^T + br in the launch that computes z, one dependent launch fewer than
  * the z-based router.  hi + lo carries G to about 2^-17 relative, the precision the z-based
  * small-batch router keeps for z (a bf16 hi/lo split of the fp32 z).  Larger batches use the
- * z-based router either way.  F32 configurations return LMOE_ERR_UNSUPPORTED.
+ * z-based router, except with expert groups, where every batch takes its logits from x and
+ * the folded router (a GEMM over both halves).  F32 configurations return
+ * LMOE_ERR_UNSUPPORTED.
  */
 size_t lmoe_fold_router_bytes(const lmoe_config* cfg);
 lmoe_status lmoe_fold_router(const lmoe_config* cfg, const void* D, const void* Wr, void* Gr, void* stream);

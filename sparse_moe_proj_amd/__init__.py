@@ -32,7 +32,7 @@ class LmoeError(RuntimeError):
 
 class lmoe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("hidden", "latent", "n_experts", "top_k", "ffn", "shared_ffn",
-                                              "act_dtype", "dense_dtype", "expert_dtype")]
+                                              "act_dtype", "dense_dtype", "expert_dtype", "groups")]
 
 
 class lmoe_weights(ctypes.Structure):
@@ -106,8 +106,9 @@ def _stream(s):
     return s.cuda_stream
 
 
-def make_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, act="bf16", dense="bf16", expert="bf16"):
-    return lmoe_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, DTYPES[act], DTYPES[dense], DTYPES[expert])
+def make_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, act="bf16", dense="bf16", expert="bf16", groups=1):
+    return lmoe_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, DTYPES[act], DTYPES[dense], DTYPES[expert],
+                       int(groups))
 
 
 def make_weights(D, U, Wr, br, shared, experts, Gr=None):

@@ -31,6 +31,7 @@ lmoe_status hip_fail(hipError_t e, const char* where) {
 
 struct Dims {
     int H, L, E, k, F, Fs;
+    int G, Eg, Lz;  // expert groups, experts per group, z width G * L
     bool f32;  // fp32 storage end to end
     bool mx;   // 4-bit routed experts (MXFP4 or NVFP4)
     int fmt;   // routed expert records: 0 bf16 (or fp32), 1 MXFP4, 2 NVFP4
@@ -65,12 +66,20 @@ lmoe_status check_config(const lmoe_config* cfg, Dims& d) {
     if (d.E < d.k || d.E > 1024) return fail(LMOE_ERR_SHAPE, "n_experts must be in [top_k, 1024] (got %d)", d.E);
     if ((long)d.H * d.L > (1L << 30) || (long)d.F * d.L > (1L << 30) || (long)d.Fs * d.L > (1L << 30))
         return fail(LMOE_ERR_SHAPE, "a weight matrix exceeds 2^30 elements");
+    d.G = cfg->groups > 1 ? cfg->groups : 1;
+    if (cfg->groups < 0 || d.G > 64 || d.E % d.G)
+        return fail(LMOE_ERR_SHAPE, "groups must be in [0, 64] and divide n_experts (got %d)", cfg->groups);
+    if (d.G > 1 && f32) return fail(LMOE_ERR_UNSUPPORTED, "expert groups need bf16 activations and dense weights");
+    d.Eg = d.E / d.G;
+    d.Lz = d.G * d.L;
+    if ((long)d.H * d.Lz > (1L << 30)) return fail(LMOE_ERR_SHAPE, "D or U exceeds 2^30 elements");
     return LMOE_OK;
 }
 
 lmoe_status check_T(const Dims& d, int32_t T) {
     if (T < 0 || T > (1 << 20)) return fail(LMOE_ERR_SHAPE, "T must be in [0, 2^20] (got %d)", T);
     if ((long)T * d.k >= (1L << 31) - (1L << 24)) return fail(LMOE_ERR_SHAPE, "T * top_k too large");
+    if ((long)T * d.Lz * 2 >= (1L << 32)) return fail(LMOE_ERR_SHAPE, "T * groups * latent too large");
     return LMOE_OK;
 }
 
@@ -90,6 +99,8 @@ Layout plan(const Dims& d, int T) {
     lo.decode_path = !d.f32 && decode_fits(T, d.L, d.F, d.Fs);
     lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx || lo.decode_path);
     lo.fused_router = !d.f32 && small_proj_fits(T, d.H);
+    // expert groups take the logits from x and the folded router for every batch (two halves)
+    const bool halves = lo.fused_router || d.G > 1;
     lo.BM = expert_tile_rows(lo.stream_path);
     lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path);
     lo.Hs = std::max(d.F, d.Fs);
@@ -102,11 +113,11 @@ Layout plan(const Dims& d, int T) {
         return at;
     };
     lo.x16 = take(d.f32 ? 0 : (size_t)T * d.H * 2);
-    lo.z32 = take((size_t)T * d.L * 4);
-    lo.z16 = take(d.f32 ? 0 : (size_t)T * d.L * 2);
-    lo.z16h = take(lo.decode_path && d.mx ? (size_t)T * d.L * 2 : 0);  // fp16 z for 4-bit small batches
-    lo.zlo = take(d.f32 || T <= kStreamMaxT ? 0 : (size_t)T * d.L * 2);  // low bf16 half of z (router input)
-    lo.logits = take((size_t)T * d.E * 4 * (lo.fused_router ? 2 : 1));  // folded router: hi and lo halves
+    lo.z32 = take((size_t)T * d.Lz * 4);
+    lo.z16 = take(d.f32 ? 0 : (size_t)T * d.Lz * 2);
+    lo.z16h = take(lo.decode_path && d.mx ? (size_t)T * d.Lz * 2 : 0);  // fp16 z for 4-bit small batches
+    lo.zlo = take(d.f32 || T <= kStreamMaxT ? 0 : (size_t)T * d.Lz * 2);  // low bf16 half of z (router input)
+    lo.logits = take((size_t)T * d.E * 4 * (halves ? 2 : 1));  // folded router: hi and lo halves
     lo.ids = take((size_t)T * d.k * 4);
     lo.w = take((size_t)T * d.k * 4);
     lo.offsets = take((size_t)(d.E + 1) * 4);
@@ -119,8 +130,10 @@ Layout plan(const Dims& d, int T) {
     lo.ntiles = take(4);
     lo.H = take((size_t)lo.R * lo.Hs * act);
     lo.Y = take(lo.decode_path ? 0 : (size_t)lo.R * d.L * (d.f32 ? 4 : 2));
-    lo.mpart = take(lo.decode_path ? (size_t)decode_groups() * T * d.L * 4 : 0);
-    lo.m = take(lo.decode_path ? 0 : (size_t)T * d.L * act);
+    lo.mpart = take(lo.decode_path ? (size_t)decode_groups() * T * d.Lz * 4 : 0);
+    // merged rows (larger batches), or with expert groups the small-batch partials summed in bf16
+    // when the U launch cannot stage them itself
+    lo.m = take(lo.decode_path ? (small_proj_fits(T, d.Lz) ? 0 : (size_t)T * d.Lz * 2) : (size_t)T * d.Lz * act);
     lo.total = o;
     return lo;
 }
@@ -189,10 +202,10 @@ lmoe_status lmoe_fold_router(const lmoe_config* cfg, const void* D, const void* 
     if (!D || !Wr || !Gr) return fail(LMOE_ERR_NULL, "D, Wr and Gr must be non-NULL");
     if (!aligned16(D) || !aligned16(Wr) || !aligned16(Gr)) return fail(LMOE_ERR_ALIGN, "D, Wr and Gr must be 16-byte aligned");
     const size_t gb = (size_t)d.E * 2 * d.H * 2;
-    if (overlap(Gr, gb, D, (size_t)d.L * d.H * 2) || overlap(Gr, gb, Wr, (size_t)d.E * d.L * 2))
+    if (overlap(Gr, gb, D, (size_t)d.Lz * d.H * 2) || overlap(Gr, gb, Wr, (size_t)d.E * d.L * 2))
         return fail(LMOE_ERR_UNSUPPORTED, "Gr overlaps D or Wr");
     const hipError_t e = launch_fold_router(static_cast<const uint16_t*>(D), static_cast<const uint16_t*>(Wr), d.E, d.L,
-                                            d.H, static_cast<uint16_t*>(Gr), static_cast<hipStream_t>(stream));
+                                            d.H, static_cast<uint16_t*>(Gr), static_cast<hipStream_t>(stream), d.Eg);
     if (e != hipSuccess) return hip_fail(e, "fold router");
     return LMOE_OK;
 }
@@ -227,6 +240,7 @@ lmoe_status lmoe_route(const lmoe_config* cfg, const lmoe_weights* weights, cons
     if (st != LMOE_OK) return st;
     if ((st = check_T(d, T)) != LMOE_OK) return st;
     if (!weights) return fail(LMOE_ERR_NULL, "weights is NULL");
+    if (d.G > 1) return fail(LMOE_ERR_UNSUPPORTED, "lmoe_route takes one latent (one expert group)");
     if (T == 0) return LMOE_OK;
     if (!weights->Wr || !z || !ids || !w || !ws) return fail(LMOE_ERR_NULL, "Wr, z, ids, w and ws must be non-NULL");
     if (!aligned16(weights->Wr) || !aligned16(z) || !aligned16(ids) || !aligned16(w) || !aligned16(ws) ||
@@ -280,6 +294,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     if (!x || !y || !wt->D || !wt->U || !wt->Wr || !wt->experts)
         return fail(LMOE_ERR_NULL, "x, y, D, U, Wr and experts must be non-NULL");
     if (d.Fs > 0 && !wt->shared) return fail(LMOE_ERR_NULL, "shared_ffn > 0 but the shared expert record is NULL");
+    if (d.G > 1 && !wt->Gr) return fail(LMOE_ERR_UNSUPPORTED, "expert groups need the folded router (weights->Gr)");
     const void* ptrs[] = {x, y, wt->D, wt->U, wt->Wr, wt->Gr, wt->experts, wt->shared, ws, o.aux_z, o.aux_ids, o.aux_w,
                           o.aux_offsets, o.aux_perm};
     for (const void* p : ptrs)
@@ -363,26 +378,29 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     if (fused_d_router) {  // z and the logits (folded router) in one launch
         ev.begin(LMOE_STAGE_D);
         if ((e = launch_proj_router_bf16(x16, static_cast<const uint16_t*>(wt->D), static_cast<const uint16_t*>(wt->Gr),
-                                         wt->br, T, d.L, d.H, d.E, z32, z16, logits, s, z16h, hnorm)) != hipSuccess)
+                                         wt->br, T, d.Lz, d.H, d.E, z32, z16, logits, s, z16h, hnorm)) != hipSuccess)
             return hip_fail(e, "D projection and router logits");
         ev.end(LMOE_STAGE_D);
     } else {
         ev.begin(LMOE_STAGE_D);
         uint16_t* zlo = T > kStreamMaxT ? static_cast<uint16_t*>(at(lo.zlo)) : nullptr;
         if (!(T <= kStreamMaxT && small_proj_fits(T, d.H))) z16h = nullptr;  // only the small-batch D launch writes it
-        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.L, d.H, 0, z32, z16, s, zlo, z16h,
+        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.Lz, d.H, 0, z32, z16, s, zlo, z16h,
                                   hnorm)) != hipSuccess)
             return hip_fail(e, "D projection");
         ev.end(LMOE_STAGE_D);
         ev.begin(LMOE_STAGE_ROUTER);
-        if ((e = launch_router_bf16(z32, static_cast<const uint16_t*>(wt->Wr), wt->br, T, d.E, d.L, logits, s,
-                                    zlo ? z16 : nullptr, zlo)) != hipSuccess)
-            return hip_fail(e, "router logits");
+        if (d.G > 1)  // each expert reads its own group's latent: the logits come from x and Gr
+            e = launch_router_x(x16, static_cast<const uint16_t*>(wt->Gr), wt->br, T, d.E, d.H, logits, s);
+        else
+            e = launch_router_bf16(z32, static_cast<const uint16_t*>(wt->Wr), wt->br, T, d.E, d.L, logits, s,
+                                   zlo ? z16 : nullptr, zlo);
+        if (e != hipSuccess) return hip_fail(e, "router logits");
         ev.end(LMOE_STAGE_ROUTER);
     }
     // top-k and permutation: for small batches inside the gate/up launch, else one launch for
     // T <= 64 (the TOPK stage events bracket both) or several
-    const float* logits2 = wt->Gr && lo.fused_router ? logits + (size_t)T * d.E : nullptr;
+    const float* logits2 = fused_d_router || d.G > 1 ? logits + (size_t)T * d.E : nullptr;
     int2* rowinfo = lo.decode_path ? static_cast<int2*>(at(lo.rowinfo)) : nullptr;
     const ExpertRoute route{logits, logits2, lo.BM, has_shared, RouteOut{ids, wts, offsets, perm, inv, tiles, ntiles, rowinfo}};
     const bool route_in_experts = lo.decode_path && kRouteInExperts;
@@ -396,24 +414,32 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     float* mpart = static_cast<float*>(at(lo.mpart));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, z16h, wt->experts, record_bytes(d, false),
                  wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
-                 lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr};
+                 lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr, d.Eg, d.Lz};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     const int umode = o.residual ? 2 : 1;
     const uint16_t* U = static_cast<const uint16_t*>(wt->U);
     if (lo.decode_path) {  // the down launch merged the rows into partials; U sums them
         ev.begin(LMOE_STAGE_U);
-        if ((e = launch_proj_partials(mpart, decode_groups(), U, T, d.H, d.L, umode, static_cast<float*>(y),
-                                      static_cast<uint16_t*>(y), s)) != hipSuccess)
-            return hip_fail(e, "U projection");
+        if (small_proj_fits(T, d.Lz)) {
+            e = launch_proj_partials(mpart, decode_groups(), U, T, d.H, d.Lz, umode, static_cast<float*>(y),
+                                     static_cast<uint16_t*>(y), s);
+        } else {  // expert groups: the partials summed first, then U over every group's columns
+            uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
+            e = launch_sum_partials(mpart, decode_groups(), T, d.Lz, m16, s);
+            if (e == hipSuccess)
+                e = launch_proj_bf16(m16, U, T, d.H, d.Lz, umode, static_cast<float*>(y), static_cast<uint16_t*>(y), s);
+        }
+        if (e != hipSuccess) return hip_fail(e, "U projection");
         ev.end(LMOE_STAGE_U);
         return ev.err != hipSuccess ? hip_fail(ev.err, "stage event record") : LMOE_OK;
     }
     uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
     ev.begin(LMOE_STAGE_COMBINE);
-    if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, true, m16, s)) != hipSuccess) return hip_fail(e, "combine");
+    if ((e = launch_combine(Y, wts, T, d.k, d.L, has_shared, true, m16, s, ids, d.G, d.Eg)) != hipSuccess)
+        return hip_fail(e, "combine");
     ev.end(LMOE_STAGE_COMBINE);
     ev.begin(LMOE_STAGE_U);
-    if ((e = launch_proj_bf16(m16, U, T, d.H, d.L, umode, static_cast<float*>(y), static_cast<uint16_t*>(y), s)) !=
+    if ((e = launch_proj_bf16(m16, U, T, d.H, d.Lz, umode, static_cast<float*>(y), static_cast<uint16_t*>(y), s)) !=
         hipSuccess)
         return hip_fail(e, "U projection");
     ev.end(LMOE_STAGE_U);

@@ -40,7 +40,7 @@ struct DecodeExperts {
     int nblocks;       // 16-row blocks of the widest segment: ceil(Hs / 16)
     uint16_t* H;       // [T*k + T][Hs] bf16, segment-row order
     const float* w;    // [T][k] routing weights (slot order)
-    float* mpart;      // [G][T][L]
+    float* mpart;      // [G][T][zp] (zp = seg.zp: the latent width times the expert groups)
     int groups;        // G
     const int2* rowinfo;  // [T*k] (token, weight bits) of the routed row at each position
     int max_tiles;        // work-list capacity (entries past *seg.ntiles are not used)
@@ -70,7 +70,7 @@ __device__ __forceinline__ void gu_item(const DE& d, const Tile& tl, int f0, con
     const typename ER::Row rg = ER::row(mats[0], f0 + j, L), ru = ER::row(mats[1], f0 + j, L);
     // fp16 operands: the token row from the fp16 copy when there is one, else converted
     const bool xh = ER::kF16 && d.z16h != nullptr;
-    const uint16_t* xr = (xh ? d.z16h : d.z16) + (size_t)tok * L;
+    const uint16_t* xr = (xh ? d.z16h : d.z16) + d.seg.z_off(tl.seg, tok, L);
     const bool xok = j < nrows;
     const int groups = L / (32 * SPL);
     const int nch = (groups + CH - 1) / CH;
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(64 * W) void decode_gu_split_kernel(const DecodeExp
             c.ru = R::row(mats[1], c.f0 + j, d.L);
         }
         c.xh = R::kF16 && d.z16h != nullptr;
-        c.xr = (c.xh ? d.z16h : d.z16) + (size_t)tok * d.L;
+        c.xr = (c.xh ? d.z16h : d.z16) + d.seg.z_off(tl.seg, tok, d.L);
         c.row0 = tl.row0;
         c.nrows = tl.nrows;
         c.tg = mats[0].ts;
@@ -456,7 +456,8 @@ __device__ __forceinline__ void dc_run(int ib, int ie, CtxOf ctx_of, Combine com
     }
 }
 
-// grid (L / 16, G); W waves; dynamic LDS: max_tiles Tiles, then T*k int2 row records.
+// grid (L / 16, G, expert groups); W waves; dynamic LDS: max_tiles Tiles, then T*k int2 row
+// records, then max_tiles ints (with expert groups: the indices of the group's tiles).
 // A wave's tiles stream as chunks with the next one always in flight (dc_run); in a 4-bit layer
 // the routed tiles and the (bf16) shared-expert tiles, which come last in the work list, are two
 // such runs.  The tile list and the rows' tokens and weights are copied to LDS once, so no chunk
@@ -465,17 +466,42 @@ template <int W, int CH, int CH4, int Q>
 __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<Q> d) {
     extern __shared__ int4 dsm[];
     __shared__ float macc[W][kDecodeMaxT][17];  // per wave: [token][latent row of the block] (+1 pad)
+    __shared__ int sng;
     Tile* stiles = reinterpret_cast<Tile*>(dsm);
     int2* srow = reinterpret_cast<int2*>(dsm + d.max_tiles);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = lane >> 4, j = lane & 15;
-    const int n0 = blockIdx.x * 16, grp = blockIdx.y;
+    const int n0 = blockIdx.x * 16, grp = blockIdx.y, xg = blockIdx.z;
     const int T = d.seg.T, k = d.seg.k, E = d.seg.E;
-    const int nt = *d.seg.ntiles;
+    int* sidx = reinterpret_cast<int*>(srow + T * k);
+    const int ntall = *d.seg.ntiles;
     for (int i = threadIdx.x; i < d.max_tiles; i += 64 * W) stiles[i] = d.seg.tiles[i];
     for (int p = threadIdx.x; p < T * k; p += 64 * W) srow[p] = d.rowinfo[p];
     for (int i = lane; i < T * 17; i += 64) (&macc[wave][0][0])[i] = 0.f;
     __syncthreads();
+    // with expert groups the workgroup takes only the tiles of its group xg (the shared expert is
+    // in group 0): wave 0 lists them in work-list order
+    const bool grouped = gridDim.z > 1;
+    if (grouped) {
+        if (wave == 0) {
+            int cnt = 0;
+            for (int base = 0; base < ntall; base += 64) {
+                const int i = base + lane;
+                bool in = false;
+                if (i < ntall) {
+                    const int sg = stiles[i].seg;
+                    in = (sg == E ? 0 : sg / d.seg.Eg) == xg;
+                }
+                const uint64_t b = __ballot(in);
+                if (in) sidx[cnt + __popcll(b & ((1ull << lane) - 1ull))] = i;
+                cnt += __popcll(b);
+            }
+            if (lane == 0) sng = cnt;
+        }
+        __syncthreads();
+    }
+    const int nt = grouped ? sng : ntall;
+    auto tile_at = [&](int i) -> const Tile& { return stiles[grouped ? sidx[i] : i]; };
     const int tb = (int)((long)grp * nt / d.groups), te = (int)((long)(grp + 1) * nt / d.groups);
     const int nmine = te - tb > wave ? (te - tb - wave + W - 1) / W : 0;
 
@@ -508,7 +534,7 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<Q
             bool ok;
             float ts;  // tensor scale of the down matrix (NVFP4; else 1)
         };
-        const Tile tl = stiles[tb + wave + i * W];
+        const Tile tl = tile_at(tb + wave + i * W);
         typename ExpertRows<Q>::Mat mats[3];
         int Fseg;
         bool mx;
@@ -540,7 +566,7 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<Q
         // the wave's routed tiles come first, then its shared-expert tiles
         int ish = nmine;
         for (int i = 0; i < nmine; ++i)
-            if (stiles[tb + wave + i * W].seg == E) {
+            if (tile_at(tb + wave + i * W).seg == E) {
                 ish = i;
                 break;
             }
@@ -557,7 +583,7 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<Q
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < W; ++w) s += macc[w][t][r];
-            d.mpart[((size_t)grp * T + t) * d.L + n0 + r] = s;
+            d.mpart[((size_t)grp * T + t) * d.seg.zp + (size_t)xg * d.L + n0 + r] = s;
         }
     }
 }

@@ -44,23 +44,25 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* __restri
 }
 
 template <int NV>
-__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids,
-                                           float* __restrict__ w) {
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, const float* __restrict__ row2, int E, int k,
+                                           int32_t* __restrict__ ids, float* __restrict__ w) {
     int pid;
     float wt;
-    wave_topk<NV>(row, nullptr, E, k, pid, wt);
+    wave_topk<NV>(row, row2, E, k, pid, wt);
     if (pid >= 0) {
         ids[pid >> 16] = pid & 0xffff;
         w[pid >> 16] = wt;
     }
 }
 
+// logits2 (optional): a second [T][E] half added to logits (the folded router's lo half)
 template <int NV>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                   int32_t* __restrict__ ids, float* __restrict__ w) {
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, const float* __restrict__ logits2,
+                                                   int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    topk_token<NV>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+    topk_token<NV>(logits + (size_t)t * E, logits2 ? logits2 + (size_t)t * E : nullptr, E, k, ids + (size_t)t * k,
+                   w + (size_t)t * k);
 }
 
 __device__ void perm_bitmap(const int32_t* __restrict__ ids, int T, int k, int E, int b, uint32_t* bm) {
@@ -198,15 +200,21 @@ __device__ __forceinline__ float4 load_y4(const void* Y, size_t off) {
     }
 }
 
+// grid (L / 1024, T, expert groups): group g's merged row m_g goes to columns g * L .. of m
+// [T][groups * L]; a slot counts for group ids / Eg (ids null: one group), the shared expert
+// for group 0.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const float* __restrict__ w, int T,
-                                                      int k, int L, int has_shared, void* __restrict__ m) {
-    const int t = blockIdx.y;
+                                                      int k, int L, int has_shared, void* __restrict__ m,
+                                                      const int32_t* __restrict__ ids, int Eg) {
+    const int t = blockIdx.y, g = blockIdx.z;
     const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (c >= L) return;
+    const size_t mp = (size_t)gridDim.z * L;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (has_shared) acc = load_y4<OUT_BF16>(Y, ((size_t)T * k + t) * L + c);
+    if (has_shared && g == 0) acc = load_y4<OUT_BF16>(Y, ((size_t)T * k + t) * L + c);
     for (int s = 0; s < k; ++s) {
+        if (ids && ids[(size_t)t * k + s] / Eg != g) continue;
         const float ws = w[(size_t)t * k + s];
         const float4 y = load_y4<OUT_BF16>(Y, ((size_t)t * k + s) * L + c);
         acc.x += ws * y.x;
@@ -216,11 +224,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
     }
     if (OUT_BF16) {
         uint2 o = make_uint2(pack_bf2(acc.x, acc.y), pack_bf2(acc.z, acc.w));
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(m) + (size_t)t * L + c) = o;
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(m) + t * mp + (size_t)g * L + c) = o;
     } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(m) + (size_t)t * L + c) = acc;
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(m) + t * mp + (size_t)g * L + c) = acc;
     }
 }
+
+// m16 [T][K] = bf16(sum over g of part[g][T][K]), in g order (the small-batch merged partials
+// when the U launch cannot stage them itself).
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int G, int T, int K,
+                                                           uint16_t* __restrict__ m16) {
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4, n = (size_t)T * K;
+    if (i >= n) return;
+    float4 a = *reinterpret_cast<const float4*>(part + i);
+    for (int g = 1; g < G; ++g) {
+        const float4 b = *reinterpret_cast<const float4*>(part + (size_t)g * n + i);
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    *reinterpret_cast<uint2*>(m16 + i) = make_uint2(pack_bf2(a.x, a.y), pack_bf2(a.z, a.w));
+}
+
 
 // ==============================================================================================
 // plain fp32 path (fp32 storage end to end): one thread per output element, sequential K.
@@ -484,21 +510,25 @@ hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const u
 }
 
 // G = Wr . D in fp32 (ascending latent order), stored as hi = bf16(G), lo = bf16(G - hi):
-// Gr [E][2][H].  One thread per (e, h); the block's 256 h share the Wr row.
+// Gr [E][2][H].  One thread per (e, h); the block's 256 h share the Wr row.  With expert groups
+// (Eg experts each) row e uses its group's D, rows (e / Eg) * L ...
 __global__ __launch_bounds__(256) void fold_router_kernel(const uint16_t* __restrict__ D, const uint16_t* __restrict__ Wr,
-                                                          int E, int L, int H, uint16_t* __restrict__ Gr) {
+                                                          int E, int L, int H, int Eg, uint16_t* __restrict__ Gr) {
     const int h = blockIdx.x * 256 + threadIdx.x, e = blockIdx.y;
     if (h >= H) return;
     const uint16_t* wr = Wr + (size_t)e * L;
+    const uint16_t* dg = D + (size_t)(e / Eg) * L * H;
     float acc = 0.f;
-    for (int l = 0; l < L; ++l) acc = fmaf(bf2f(wr[l]), bf2f(D[(size_t)l * H + h]), acc);
+    for (int l = 0; l < L; ++l) acc = fmaf(bf2f(wr[l]), bf2f(dg[(size_t)l * H + h]), acc);
     const uint32_t hi = f2bf(acc);
     Gr[(size_t)e * 2 * H + h] = (uint16_t)hi;
     Gr[(size_t)e * 2 * H + H + h] = (uint16_t)f2bf(acc - bf2f(hi));
 }
 
-hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int L, int H, uint16_t* Gr, hipStream_t s) {
-    hipLaunchKernelGGL(fold_router_kernel, dim3((unsigned)cdiv(H, 256), (unsigned)E), dim3(256), 0, s, D, Wr, E, L, H, Gr);
+hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int L, int H, uint16_t* Gr, hipStream_t s,
+                              int Eg) {
+    hipLaunchKernelGGL(fold_router_kernel, dim3((unsigned)cdiv(H, 256), (unsigned)E), dim3(256), 0, s, D, Wr, E, L, H,
+                       Eg > 0 ? Eg : E, Gr);
     return last();
 }
 
@@ -545,18 +575,29 @@ hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* b
     return last();
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+// The router logits of a batch from x and the folded router Gr [E][2][K] (its rows as a [2E][K]
+// matrix): logits[h][t][e] = x[t] . Gr[e][h] (+ br[e] for h = 0).
+hipError_t launch_router_x(const uint16_t* x, const uint16_t* Gr, const float* br, int T, int E, int K, float* logits,
+                           hipStream_t s) {
+    TileProj<TileL> p{x, Gr, T, 2 * E, K, 3, logits, nullptr, nullptr, br};
+    hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileProj<TileL>>), dim3(cdiv(2 * E, TileL::kBN), cdiv(T, TileL::kBM)),
+                       dim3(256), 0, s, p);
+    return last();
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s,
+                       const float* logits2) {
     const dim3 g(cdiv(T, 4)), b(256);
     if (E <= 64)
-        hipLaunchKernelGGL(topk_kernel<1>, g, b, 0, s, logits, T, E, k, ids, w);
+        hipLaunchKernelGGL(topk_kernel<1>, g, b, 0, s, logits, logits2, T, E, k, ids, w);
     else if (E <= 128)
-        hipLaunchKernelGGL(topk_kernel<2>, g, b, 0, s, logits, T, E, k, ids, w);
+        hipLaunchKernelGGL(topk_kernel<2>, g, b, 0, s, logits, logits2, T, E, k, ids, w);
     else if (E <= 256)
-        hipLaunchKernelGGL(topk_kernel<4>, g, b, 0, s, logits, T, E, k, ids, w);
+        hipLaunchKernelGGL(topk_kernel<4>, g, b, 0, s, logits, logits2, T, E, k, ids, w);
     else if (E <= 512)
-        hipLaunchKernelGGL(topk_kernel<8>, g, b, 0, s, logits, T, E, k, ids, w);
+        hipLaunchKernelGGL(topk_kernel<8>, g, b, 0, s, logits, logits2, T, E, k, ids, w);
     else
-        hipLaunchKernelGGL(topk_kernel<16>, g, b, 0, s, logits, T, E, k, ids, w);
+        hipLaunchKernelGGL(topk_kernel<16>, g, b, 0, s, logits, logits2, T, E, k, ids, w);
     return last();
 }
 
@@ -585,8 +626,8 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
                                int32_t* ntiles, int has_shared, hipStream_t s, const float* logits2, int2* rowinfo) {
     if (T > kPermTB) {
-        if (logits2 || rowinfo) return hipErrorInvalidValue;  // small-batch launch only
-        hipError_t e = launch_topk(logits, T, E, k, ids, w, s);
+        if (rowinfo) return hipErrorInvalidValue;  // small-batch launch only
+        hipError_t e = launch_topk(logits, T, E, k, ids, w, s, logits2);
         if (e != hipSuccess) return e;
         return launch_permute(ids, T, k, E, hist, base, offsets, perm, inv, BM, tiles, ntiles, has_shared, s);
     }
@@ -682,8 +723,10 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     if (err != hipSuccess) return err;
     ev.end(kStageUp);
     ev.begin(kStageDown);
-    const size_t lds = (size_t)a.max_tiles * sizeof(Tile) + (size_t)a.T * a.k * sizeof(int2);
-    hipLaunchKernelGGL((decode_dc_kernel<kDcWaves, kDcChunk, kDcChunk4, Q>), dim3(a.L / 16, kDcGroups),
+    const size_t lds =
+        (size_t)a.max_tiles * sizeof(Tile) + (size_t)a.T * a.k * sizeof(int2) + (size_t)a.max_tiles * sizeof(int);
+    const unsigned xgroups = (unsigned)(seg.zp / a.L);
+    hipLaunchKernelGGL((decode_dc_kernel<kDcWaves, kDcChunk, kDcChunk4, Q>), dim3(a.L / 16, kDcGroups, xgroups),
                        dim3(64 * kDcWaves), lds, s, d);
     if ((err = last()) != hipSuccess) return err;
     ev.end(kStageDown);
@@ -710,7 +753,7 @@ hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
 }
 
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {
-    const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E};
+    const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E, a.Eg > 0 ? a.Eg : a.E, a.zp > 0 ? a.zp : a.L};
     if (a.decode_path)
         return a.fmt == 2 ? launch_decode_experts<2>(a, seg, s, ev)
                           : a.fmt == 1 ? launch_decode_experts<1>(a, seg, s, ev) : launch_decode_experts<0>(a, seg, s, ev);
@@ -764,13 +807,20 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
     return hipSuccess;
 }
 
+hipError_t launch_sum_partials(const float* part, int G, int T, int K, uint16_t* m16, hipStream_t s) {
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)cdiv((size_t)T * K / 4, 256)), dim3(256), 0, s, part, G, T, K,
+                       m16);
+    return last();
+}
+
 hipError_t launch_combine(const void* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
-                          hipStream_t s) {
-    const dim3 grid(cdiv(L / 4, 256), T);
+                          hipStream_t s, const int32_t* ids, int groups, int Eg) {
+    const dim3 grid(cdiv(L / 4, 256), T, groups > 1 ? groups : 1);
+    const int32_t* gids = groups > 1 ? ids : nullptr;
     if (out_bf16)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, Y, w, T, k, L, has_shared, m);
+        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, Y, w, T, k, L, has_shared, m, gids, Eg);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, Y, w, T, k, L, has_shared, m);
+        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, Y, w, T, k, L, has_shared, m, gids, Eg);
     return last();
 }
 

@@ -76,7 +76,17 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
 hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
                               hipStream_t s, const uint16_t* zhi = nullptr, const uint16_t* zlo = nullptr);
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+// logits2 (optional): a second [T][E] half added to logits.
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s,
+                       const float* logits2 = nullptr);
+
+// logits [2][T][E] of a batch from x [T][K] bf16 and the folded router Gr [E][2][K]: half h is
+// x . Gr[e][h], br (optional) added to half 0.
+hipError_t launch_router_x(const uint16_t* x, const uint16_t* Gr, const float* br, int T, int E, int K, float* logits,
+                           hipStream_t s);
+
+// m16 [T][K] bf16 = the sum, in order, of G fp32 partials [G][T][K] (K a multiple of 4).
+hipError_t launch_sum_partials(const float* part, int G, int T, int K, uint16_t* m16, hipStream_t s);
 
 int perm_blocks(int T);
 
@@ -85,8 +95,8 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist
                           int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
                           hipStream_t s);
 
-// top-k followed by the permutation; one fused launch when T <= 64.  logits2 (T <= 64 only):
-// a second [T][E] half added to logits (the folded router's lo half).  rowinfo (T <= 64
+// top-k followed by the permutation; one fused launch when T <= 64.  logits2 (optional): a
+// second [T][E] half added to logits (the folded router's lo half).  rowinfo (T <= 64
 // only): [T*k] (token, weight bits) of the slot at each permuted position, (-1, 0) if none.
 hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* hist,
                                int32_t* base, int32_t* offsets, int32_t* perm, int32_t* inv, int BM, Tile* tiles,
@@ -106,8 +116,10 @@ int decode_groups();
 hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const uint16_t* Gr, const float* br, int T,
                                   int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s,
                                   uint16_t* z16h = nullptr, const float* hnorm = nullptr);
-// Gr [E][2][H] = hi and lo bf16 halves of Wr . D (fp32 accumulation).
-hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int L, int H, uint16_t* Gr, hipStream_t s);
+// Gr [E][2][H] = hi and lo bf16 halves of Wr . D (fp32 accumulation); with expert groups of Eg
+// experts, row e uses D rows (e / Eg) * L .. (Eg = 0: one group).
+hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int L, int H, uint16_t* Gr, hipStream_t s,
+                              int Eg = 0);
 
 // U projection of a small batch whose input is the sum (in order) of G fp32 partials [G][T][K].
 hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
@@ -141,10 +153,12 @@ struct ExpertArgs {
     bool stream_path;
     bool decode_path;  // small batch: gate/up into H, then down + merge into mpart
     int fmt;           // routed expert records: 0 bf16, 1 MXFP4, 2 NVFP4
-    float* mpart;      // [decode_groups()][T][L] partial merged rows (decode path)
+    float* mpart;      // [decode_groups()][T][zp] partial merged rows (decode path)
     const float* w;
     const int2* rowinfo;  // decode path: [T*k] (token, weight bits) per permuted position
     const ExpertRoute* route;  // decode path: non-null = route inside the gate/up launch
+    int Eg = 0;  // experts per expert group (0: one group)
+    int zp = 0;  // row pitch of z16 / z16h / mpart: L times the expert groups (0: L)
 };
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 
@@ -152,9 +166,10 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
 // fmt 0 bf16, 1 MXFP4, 2 NVFP4).
 hipError_t launch_pack(const void* src, void* dst, size_t rec_bytes, int nrec, int F, int L, int fmt, hipStream_t s);
 
-// Y: bf16 rows when out_bf16 (the bf16 path), else fp32 rows.
+// Y: bf16 rows when out_bf16 (the bf16 path), else fp32 rows.  With expert groups (groups > 1,
+// Eg experts each, ids [T][k]) m is [T][groups * L], group g's merged row in columns g * L ..
 hipError_t launch_combine(const void* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
-                          hipStream_t s);
+                          hipStream_t s, const int32_t* ids = nullptr, int groups = 1, int Eg = 0);
 
 // fp32 path. mode 0: out = xW^T (+bias); 2: out += xW^T
 hipError_t launch_proj_f32(const float* x, const float* W, const float* bias, int T, int N, int K, int mode, float* out,

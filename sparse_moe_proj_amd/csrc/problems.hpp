@@ -39,9 +39,16 @@ struct SegSpace {
     const int32_t* ntiles;  // number of valid entries
     const int32_t* perm;    // [T*k]
     int32_t T, k, E;
+    // Expert groups with their own D: z is [T][zp] with group g's latent in columns g*L ..;
+    // expert seg is in group seg / Eg, the shared expert in group 0 (one group: Eg = E, zp = L).
+    int32_t Eg, zp;
     // a dropped slot (perm = -1) maps to token 0: its rows are computed but never stored
     __device__ __forceinline__ int token_of(int seg, int p) const { return seg == E ? p - T * k : max(perm[p], 0) / k; }
     __device__ __forceinline__ int dest_of(int seg, int p) const { return seg == E ? p : perm[p]; }
+    // element offset of segment row p's token operand in z (latent width L)
+    __device__ __forceinline__ size_t z_off(int seg, int tok, int L) const {
+        return (size_t)tok * zp + (seg == E ? 0 : (size_t)(seg / Eg) * L);
+    }
 };
 
 // =============================================================================================
@@ -50,7 +57,9 @@ struct SegSpace {
 using Tile128 = TileShape<128, 128, 2, 2>;
 using Tile256 = TileShape<256, 256, 2, 2>;
 
-// Dense projection C[t][n] = x[t] . W[n]; mode 0: z32 + z16 (D), 1: bf16 y (U), 2: y += (U, fp32 residual)
+// Dense projection C[t][n] = x[t] . W[n]; mode 0: z32 + z16 (D), 1: bf16 y (U), 2: y += (U, fp32
+// residual), 3: router halves from the folded router (W = Gr as [2E][K] rows, n = 2e + h):
+// out32[h][t][e] = v (+ bias[e] for h = 0)
 template <class S>
 struct TileProj {
     const uint16_t* x;  // [M][K] bf16
@@ -59,6 +68,7 @@ struct TileProj {
     float* out32;
     uint16_t* out16;
     uint16_t* out16lo;  // mode 0, optional: bf16(v - bf16(v)), the low half of the router input
+    const float* bias = nullptr;  // mode 3
     struct Ctx { int m0, n0; };
     typedef const uint16_t* RowA;
     typedef const uint16_t* RowB;
@@ -90,6 +100,9 @@ struct TileProj {
                             out32[o] = v;
                             out16[o] = (uint16_t)hi;
                             if (out16lo) out16lo[o] = (uint16_t)lo;
+                        } else if (mode == 3) {
+                            const int e = n >> 1, h = n & 1;
+                            out32[((size_t)h * M + m) * (N >> 1) + e] = h == 0 && bias ? v + bias[e] : v;
                         } else if (mode == 1) {
                             out16[o] = (uint16_t)f2bf(v);
                         } else {
@@ -201,7 +214,7 @@ struct TileUp {
     }
     __device__ RowA row_a(const Ctx& c, int r) const {
         if (r >= c.nrows) return nullptr;
-        return z16 + (size_t)seg.token_of(c.seg, c.row0 + r) * L;
+        return z16 + seg.z_off(c.seg, seg.token_of(c.seg, c.row0 + r), L);
     }
     __device__ RowB row_b(const Ctx& c, int r) const {
         const int wc = r / S::kWN, rr = r % S::kWN;
@@ -588,7 +601,7 @@ struct StreamUp {
     __device__ RowW row_w(const Ctx& c, int n) const { return RowW{ER::row(c.m[0], n, L), ER::row(c.m[1], n, L)}; }
     __device__ XRow x_row(const Ctx& c, int j) const {
         const int tok = seg.token_of(c.seg, c.row0 + min(j, c.nrows - 1));
-        return TokRow{z16 + (size_t)tok * L, j < c.nrows};
+        return TokRow{z16 + seg.z_off(c.seg, tok, L), j < c.nrows};
     }
     template <bool MXR>
     __device__ WRaw load_w(const Ctx&, const RowW& r, int m, int g, int kq) const {
@@ -703,10 +716,11 @@ struct PipeUp : TileUp<S> {
     __device__ int k_stages(const typename B::Ctx&) const { return B::L / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx&) const { return reinterpret_cast<const uint8_t*>(B::z16); }
     __device__ const uint8_t* b_base(const typename B::Ctx& c) const { return reinterpret_cast<const uint8_t*>(c.g); }
-    // gathered token rows: byte offsets into z16 stay below 2^32 for T <= 2^20 rows of latent <= 2048
+    // gathered token rows: byte offsets into z16 stay below 2^32 (T * zp * 2 < 2^32 is checked
+    // on the host)
     __device__ uint32_t src_a(const typename B::Ctx& c, int i, int lane) const {
         const int r = min(rowmajor_row(i, lane), c.nrows - 1);
-        return rowmajor_off((uint32_t)B::seg.token_of(c.seg, c.row0 + r) * B::L * 2, i, lane);
+        return rowmajor_off((uint32_t)(B::seg.z_off(c.seg, B::seg.token_of(c.seg, c.row0 + r), B::L) * 2), i, lane);
     }
     __device__ uint32_t src_b(const typename B::Ctx& c, int i, int lane) const {
         const int r = (i >> 1) * 16;  // first B-tile row of this copy (16 rows: one matrix, one f block)

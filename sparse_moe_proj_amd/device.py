@@ -68,7 +68,7 @@ class DeviceLayer:
             self.experts = to_device(lw.experts, device)
         s = self.shape
         self.cfg = make_config(s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn, self.act, self.dense,
-                               self.expert)
+                               self.expert, getattr(s, "groups", 1))
         if _copy_of is None and pack and self.expert != "f32":
             self.experts = pack_records(self.cfg, self.experts, False)
             if self.shared is not None:

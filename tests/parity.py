@@ -50,7 +50,7 @@ def run_forward(dl: DeviceLayer, x: torch.Tensor, ws: Workspace | None = None, p
     T = x.shape[0]
     dev = x.device
     out = dict(
-        z=torch.empty((T, s.latent), dtype=torch.float32, device=dev),
+        z=torch.empty((T, s.groups * s.latent), dtype=torch.float32, device=dev),
         ids=torch.empty((T, s.top_k), dtype=torch.int32, device=dev),
         w=torch.empty((T, s.top_k), dtype=torch.float32, device=dev),
         offsets=torch.empty((s.n_experts + 1,), dtype=torch.int32, device=dev),
@@ -90,7 +90,7 @@ def check_block(lw, x_host, act, out, sample=None, tol=None, label=""):
     xo = act_to_f64(x_host, act)
     T = xo.shape[0]
     z = xo @ L.D.T
-    ids_o, w_o, gap_o, logits_o = oracle.route(z, L.Wr, L.br, k)
+    ids_o, w_o, gap_o, logits_o = oracle.route(z, L.Wr, L.br, k, s.groups)
     ids_g = host(out["ids"])
     same, excluded = check_routing(ids_g, ids_o, gap_o, logits_o, k)
 

@@ -73,6 +73,9 @@ def test_workspace_sizes_monotone():
     (dict(expert="mxfp4", shared_ffn=64), lm.LMOE_ERR_SHAPE),
     (dict(act="f32"), lm.LMOE_ERR_UNSUPPORTED),
     (dict(expert="f32"), lm.LMOE_ERR_UNSUPPORTED),
+    (dict(groups=3), lm.LMOE_ERR_SHAPE),
+    (dict(groups=-1), lm.LMOE_ERR_SHAPE),
+    (dict(groups=128, n_experts=1024), lm.LMOE_ERR_SHAPE),
 ])
 def test_bad_config_rejected(kw, code):
     n = ctypes.c_size_t(0)
@@ -140,6 +143,24 @@ def test_single_hip_runtime_in_process():
     with open("/proc/self/maps") as f:
         libs = {line.split()[-1] for line in f if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+def test_expert_groups_checked():
+    t = gen.TINY
+    g8 = cfg(groups=8)
+    n1, n8 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lm.lib.lmoe_workspace_bytes(ctypes.byref(cfg()), 64, ctypes.byref(n1)) == lm.LMOE_OK
+    assert lm.lib.lmoe_workspace_bytes(ctypes.byref(g8), 64, ctypes.byref(n8)) == lm.LMOE_OK
+    assert n8.value > n1.value  # z and the merged partials are eight latents wide
+    # no folded router: unsupported; lmoe_route takes one latent only
+    assert lm.lmoe_forward(g8, full_weights(), FAKE, 8, FAKE + (1 << 30), None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_UNSUPPORTED
+    assert lm.lmoe_route(g8, full_weights(), FAKE, 8, FAKE, FAKE, FAKE, 1 << 30, 0) == lm.LMOE_ERR_UNSUPPORTED
+    f32 = lm.make_config(t.hidden, t.latent, t.n_experts, t.top_k, t.ffn, t.shared_ffn, "f32", "f32", "f32", groups=2)
+    assert lm.lmoe_forward(f32, full_weights(), FAKE, 8, FAKE + (1 << 30), None, FAKE, 1 << 40, 0) == lm.LMOE_ERR_UNSUPPORTED
+    # the fold reads all eight D matrices: Gr placed inside them overlaps
+    far = FAKE + (1 << 36)
+    d_bytes = 8 * S.latent * S.hidden * 2
+    assert lm.lmoe_fold_router(g8, FAKE, far, FAKE + d_bytes - 4096, 0) == lm.LMOE_ERR_UNSUPPORTED
 
 
 def test_fold_router_arguments_checked():

@@ -123,6 +123,45 @@ def test_small_prenorm_residual(T, fold, ws):
     assert err <= TOL["bf16"]
 
 
+SMALL_G = gen.Shape(hidden=256, latent=192, n_experts=24, top_k=3, ffn=128, shared_ffn=64, groups=4)
+SMALL_G_MX = gen.Shape(hidden=256, latent=256, n_experts=24, top_k=3, ffn=128, shared_ffn=128, groups=3)
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 64, 100, 300])
+def test_small_expert_groups(T, ws):
+    """Expert groups with their own D/U pair (small batches and every larger-batch path)."""
+    wl, lw = small_layer(SMALL_G, "bf16", "bf16", "bf16")
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"small_groups T={T}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("T", [3, 40, 100])
+def test_small_expert_groups_4bit(fmt, T, ws):
+    wl, lw = small_layer(SMALL_G_MX, "bf16", "bf16", fmt)
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"small_groups_{fmt} T={T}")
+
+
+def test_expert_groups_need_the_folded_router(ws):
+    wl, lw = small_layer(SMALL_G, "bf16", "bf16", "bf16")
+    dl = DeviceLayer(lw, act="bf16", fold=False)
+    x = upload_tokens(gen.make_tokens(wl, T=4))
+    buf = ws.get(lm.lmoe_workspace_bytes(dl.cfg, 4))
+    y = torch.empty((4, wl.shape.hidden), dtype=torch.int16, device="cuda")
+    assert lm.lmoe_forward(dl.cfg, dl.weights, x, 4, y, None, buf, buf.numel()) == lm.LMOE_ERR_UNSUPPORTED
+
+
+def test_decode_group64_t8_full(ws):
+    _workload_case("decode_group64_t8", 8, ws)
+
+
 def test_fold_router_halves():
     """hi + lo of the folded router carries G = Wr . D to the precision the halves allow."""
     wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
