@@ -104,6 +104,7 @@ WORKLOADS = {
     "decode120_t8": Workload(6, "decode120_t8", EDGE0_120B, 8, "bf16", "bf16", "bf16", "zipf"),
     "decode_nvfp4_t8": Workload(7, "decode_nvfp4_t8", EDGE0_145B, 8, "bf16", "bf16", "nvfp4", "zipf"),
     "decode_group64_t8": Workload(8, "decode_group64_t8", EDGE0_145B_G64, 8, "bf16", "bf16", "bf16", "zipf"),
+    "prefill_mxfp4_t16384": Workload(9, "prefill_mxfp4_t16384", EDGE0_145B, 16384, "bf16", "bf16", "mxfp4", "zipf"),
 }
 
 

@@ -87,8 +87,9 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t x16, z32, z16, z16h, zlo, logits, ids, w, offsets, perm, inv, rowinfo, hist, base, tiles, ntiles, H, Y, mpart, m, total;
-    bool stream_path, decode_path, fused_router;
+    size_t x16, z32, z16, z16h, zlo, logits, ids, w, offsets, perm, inv, rowinfo, hist, base, tiles, ntiles, H, Y, mpart, m,
+        deq, deq_ts, total;
+    bool stream_path, decode_path, fused_router, deq_path;
     int max_tiles, BM, Hs, R;
 };
 
@@ -97,7 +98,11 @@ Layout plan(const Dims& d, int T) {
     const size_t act = d.f32 ? 4 : 2;
     const int has_shared = d.Fs > 0;
     lo.decode_path = !d.f32 && decode_fits(T, d.L, d.F, d.Fs);
-    lo.stream_path = !d.f32 && (T <= kStreamMaxT || d.mx || lo.decode_path);
+    // 4-bit records stream through the weight-streaming kernels up to kDequantMinT tokens; larger
+    // batches decode the touched records to bf16 once and take the tile GEMMs
+    const bool deq = d.mx && !lo.decode_path && T >= kDequantMinT;
+    lo.deq_path = deq;
+    lo.stream_path = !d.f32 && (T <= kStreamMaxT || (d.mx && !deq) || lo.decode_path);
     lo.fused_router = !d.f32 && small_proj_fits(T, d.H);
     // expert groups take the logits from x and the folded router for every batch (two halves)
     const bool halves = lo.fused_router || d.G > 1;
@@ -134,6 +139,8 @@ Layout plan(const Dims& d, int T) {
     // merged rows (larger batches), or with expert groups the small-batch partials summed in bf16
     // when the U launch cannot stage them itself
     lo.m = take(lo.decode_path ? (small_proj_fits(T, d.Lz) ? 0 : (size_t)T * d.Lz * 2) : (size_t)T * d.Lz * act);
+    lo.deq = take(deq ? (size_t)d.E * 3 * d.F * d.L * 2 : 0);  // decoded bf16 records
+    lo.deq_ts = take(deq ? (size_t)d.E * 3 * 4 : 0);
     lo.total = o;
     return lo;
 }
@@ -414,7 +421,9 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     float* mpart = static_cast<float*>(at(lo.mpart));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, z16h, wt->experts, record_bytes(d, false),
                  wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
-                 lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr, d.Eg, d.Lz};
+                 lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr, d.Eg, d.Lz,
+                 lo.deq_path ? static_cast<uint16_t*>(at(lo.deq)) : nullptr,
+                 lo.deq_path ? static_cast<float*>(at(lo.deq_ts)) : nullptr, offsets};
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     const int umode = o.residual ? 2 : 1;
     const uint16_t* U = static_cast<const uint16_t*>(wt->U);

@@ -733,6 +733,59 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     return hipSuccess;
 }
 
+// Large 4-bit batches: the records of the experts that received tokens are decoded once into
+// packed bf16 records (the exact values: an E2M1 value times an E8M0 or E4M3 block scale has at
+// most 6 significant bits), and the bf16 pipelined GEMMs run on them; an NVFP4 record's fp32
+// tensor scales go to ts [E][3] and multiply the products in the epilogues.
+// Thread u of expert blockIdx.y decodes 16-byte unit u of the record (gate, up, then down): 32
+// values of one row, which are four bf16 units of the bf16 tile holding the same columns.
+template <int Q>
+__global__ __launch_bounds__(256) void dequant_experts_kernel(const uint8_t* __restrict__ src, size_t rec4,
+                                                              const int32_t* __restrict__ offsets, int F, int L,
+                                                              uint16_t* __restrict__ dst, float* __restrict__ ts) {
+    const int e = blockIdx.y;
+    if (offsets[e + 1] == offsets[e]) return;  // no tokens: the record is not read
+    constexpr int kSB = Q == 1 ? 1 : 2;
+    const size_t FL = (size_t)F * L, upm = FL / 32;  // units per matrix
+    const uint8_t* rec = src + (size_t)e * rec4;
+    uint16_t* out = dst + (size_t)e * 3 * FL;
+    if (blockIdx.x == 0 && threadIdx.x < 3)
+        ts[3 * e + threadIdx.x] = Q == 2 ? reinterpret_cast<const float*>(rec + 3 * (FL / 2) + 3 * (FL / 16))[threadIdx.x] : 1.f;
+    const size_t u = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= 3 * upm) return;
+    const int m = (int)(u / upm);
+    const size_t v = u - (size_t)m * upm;
+    const int K = m < 2 ? L : F;                       // gate/up [F][L], down [L][F]
+    const int gpr = K / 128;                           // 128-value groups per row block
+    const size_t rb = v / ((size_t)gpr * 64);
+    const int rem = (int)(v - rb * gpr * 64), g = rem >> 6, pos = rem & 63, q4 = pos >> 4, j = pos & 15;
+    const uint4 nib = *reinterpret_cast<const uint4*>(rec + (size_t)m * (FL / 2) + rb * 8 * K + g * 1024 + pos * 16);
+    const uint8_t* sp = rec + 3 * (FL / 2) + ((size_t)m * upm + (rb * gpr + g) * 64 + pos) * kSB;
+    float s0, s1;
+    if constexpr (Q == 1) {
+        s0 = s1 = e8m0_to_f32(*sp);
+    } else {
+        s0 = e4m3_to_f32(sp[0]);
+        s1 = e4m3_to_f32(sp[1]);
+    }
+    uint16_t* o = out + (size_t)m * FL + rb * 16 * K + (size_t)(g * 4 + q4) * 512 + j * 8;
+    const uint32_t w[4] = {nib.x, nib.y, nib.z, nib.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(o + q * 128) = fp4x8_to_bf16x8(w[q], q < 2 ? s0 : s1);
+}
+
+hipError_t launch_dequant_experts(const void* src, size_t rec4, const int32_t* offsets, int E, int F, int L, int fmt,
+                                  uint16_t* dst, float* ts, hipStream_t s) {
+    const dim3 grid((unsigned)cdiv((size_t)3 * F * L / 32, 256), (unsigned)E);
+    if (fmt == 2)
+        hipLaunchKernelGGL(dequant_experts_kernel<2>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(src), rec4,
+                           offsets, F, L, dst, ts);
+    else
+        hipLaunchKernelGGL(dequant_experts_kernel<1>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(src), rec4,
+                           offsets, F, L, dst, ts);
+    return last();
+}
+
 // Larger 4-bit batches: persistent weight-streaming gate/up, then down (the combine follows).
 template <int Q>
 hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
@@ -760,12 +813,22 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
     if (a.stream_path)
         return a.fmt == 2 ? launch_stream_experts<2>(a, seg, s, ev)
                           : a.fmt == 1 ? launch_stream_experts<1>(a, seg, s, ev) : launch_stream_experts<0>(a, seg, s, ev);
-    if (a.fmt != 0) return hipErrorInvalidValue;  // the tile path takes bf16 experts only
+    // the tile path takes bf16 records: a 4-bit layer's are decoded first into a.deq
+    const uint16_t* ex = static_cast<const uint16_t*>(a.experts);
+    size_t rec = a.rec_bytes / 2;
+    ev.begin(kStageUp);  // the decode of 4-bit records counts to the gate/up stage
+    if (a.fmt != 0) {
+        if (!a.deq || !a.deq_ts) return hipErrorInvalidValue;
+        hipError_t err = launch_dequant_experts(a.experts, a.rec_bytes, a.offsets, a.E, a.F, a.L, a.fmt, a.deq, a.deq_ts, s);
+        if (err != hipSuccess) return err;
+        ex = a.deq;
+        rec = (size_t)3 * a.F * a.L;
+    }
+    const float* tsc = a.fmt != 0 ? a.deq_ts : nullptr;
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
     if (LMOE_PIPE) {
-        ev.begin(kStageUp);
-        PipeUp<PipeL> up{{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H}};
+        PipeUp<PipeL> up{{seg, a.z16, ex, sh, rec, a.L, a.F, a.Fs, a.Hs, a.H, tsc}};
         const int nn_up = (int)cdiv(Fmax, PipeL::kBN / 2);
         if (LMOE_PIPE_PERSIST) {
             auto k = pipe_gemm_persistent<PipeL, PipeUp<PipeL>>;
@@ -778,7 +841,7 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
         if (err != hipSuccess) return err;
         ev.end(kStageUp);
         ev.begin(kStageDown);
-        PipeDown<PipeL> dn{{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y}};
+        PipeDown<PipeL> dn{{seg, a.H, ex, sh, rec, a.L, a.F, a.Fs, a.Hs, a.Y, tsc}};
         const int nn_dn = (int)cdiv(a.L, PipeL::kBN);
         if (LMOE_PIPE_PERSIST) {
             auto k = pipe_gemm_persistent<PipeL, PipeDown<PipeL>>;
@@ -791,15 +854,14 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
         ev.end(kStageDown);
         return hipSuccess;
     }
-    ev.begin(kStageUp);
-    TileUp<TileL> up{seg, a.z16, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.H};
+    TileUp<TileL> up{seg, a.z16, ex, sh, rec, a.L, a.F, a.Fs, a.Hs, a.H, tsc};
     hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileUp<TileL>>), dim3(cdiv(Fmax, TileL::kBN / 2), a.max_tiles),
                        dim3(256), 0, s, up);
     hipError_t err = last();
     if (err != hipSuccess) return err;
     ev.end(kStageUp);
     ev.begin(kStageDown);
-    TileDown<TileL> dn{seg, a.H, (const uint16_t*)a.experts, sh, a.rec_bytes / 2, a.L, a.F, a.Fs, a.Hs, a.Y};
+    TileDown<TileL> dn{seg, a.H, ex, sh, rec, a.L, a.F, a.Fs, a.Hs, a.Y, tsc};
     hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileDown<TileL>>), dim3(cdiv(a.L, TileL::kBN), a.max_tiles),
                        dim3(256), 0, s, dn);
     if ((err = last()) != hipSuccess) return err;

@@ -159,7 +159,17 @@ struct ExpertArgs {
     const ExpertRoute* route;  // decode path: non-null = route inside the gate/up launch
     int Eg = 0;  // experts per expert group (0: one group)
     int zp = 0;  // row pitch of z16 / z16h / mpart: L times the expert groups (0: L)
+    // 4-bit records on the tile path (large batches): decoded bf16 records [E][3 F L] and the
+    // records' tensor scales [E][3]; offsets [E + 1] says which experts have tokens
+    uint16_t* deq = nullptr;
+    float* deq_ts = nullptr;
+    const int32_t* offsets = nullptr;
 };
+
+// Large 4-bit batches: minimum T at which the records of the experts with tokens are decoded to
+// bf16 once and the bf16 tile GEMMs run (below it the weight-streaming kernels read the 4-bit
+// records directly).
+constexpr int kDequantMinT = 1024;
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 
 // Row-major expert records -> packed records (nrec records of rec_bytes; F x L gate/up, L x F down;

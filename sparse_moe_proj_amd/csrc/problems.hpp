@@ -192,7 +192,8 @@ struct TileUp {
     size_t rec;               // elements per routed record
     int L, F, Fs, Hs;
     uint16_t* H;              // [R][Hs]
-    struct Ctx { int seg, row0, nrows, F, f0; const uint16_t* g; const uint16_t* u; };
+    const float* ts = nullptr;  // [E][3] tensor scales of the routed records (gate, up, down), or null (1)
+    struct Ctx { int seg, row0, nrows, F, f0; const uint16_t* g; const uint16_t* u; float tg, tu; };
     typedef const uint16_t* RowA;
     typedef const uint16_t* RowB;
     __device__ bool tile(int bx, int by, Ctx& c) const {
@@ -201,12 +202,17 @@ struct TileUp {
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
+        c.tg = c.tu = 1.f;
         if (t.seg == seg.E) {
             c.F = Fs;
             c.g = shared;
         } else {
             c.F = F;
             c.g = experts + (size_t)t.seg * rec;
+            if (ts) {
+                c.tg = ts[3 * t.seg];
+                c.tu = ts[3 * t.seg + 1];
+            }
         }
         c.u = c.g + (size_t)c.F * L;
         c.f0 = by * kFPerTile;
@@ -237,7 +243,7 @@ struct TileUp {
                     const int m = rb + i * 32 + frag32_row(r, lane);
                     if (m < c.nrows && f < c.F)
                         H[(size_t)(c.row0 + m) * Hs + f] =
-                            (uint16_t)f2bf(silu(acc[i][j][r]) * acc[i][j + NB / 2][r]);
+                            (uint16_t)f2bf(silu(acc[i][j][r] * c.tg) * (acc[i][j + NB / 2][r] * c.tu));
                 }
             });
         });
@@ -254,7 +260,8 @@ struct TileDown {
     size_t rec;
     int L, F, Fs, Hs;
     uint16_t* Y;  // [R][L] bf16
-    struct Ctx { int seg, row0, nrows, F, n0; const uint16_t* d; };
+    const float* ts = nullptr;  // [E][3] tensor scales of the routed records, or null (1)
+    struct Ctx { int seg, row0, nrows, F, n0; const uint16_t* d; float td; };
     typedef const uint16_t* RowA;
     typedef const uint16_t* RowB;
     __device__ bool tile(int bx, int by, Ctx& c) const {
@@ -263,12 +270,14 @@ struct TileDown {
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
+        c.td = 1.f;
         if (t.seg == seg.E) {
             c.F = Fs;
             c.d = shared + 2 * (size_t)Fs * L;
         } else {
             c.F = F;
             c.d = experts + (size_t)t.seg * rec + 2 * (size_t)F * L;
+            if (ts) c.td = ts[3 * t.seg + 2];
         }
         c.n0 = by * S::kBN;
         return c.n0 < L;
@@ -290,7 +299,7 @@ struct TileDown {
                     const size_t dst = (size_t)drow * L;
                     static_for<NB>([&](auto j) {
                         const int n = c.n0 + cb + j * 32 + frag32_col(lane);
-                        if (n < L) Y[dst + n] = (uint16_t)f2bf(acc[i][j][r]);
+                        if (n < L) Y[dst + n] = (uint16_t)f2bf(acc[i][j][r] * c.td);
                     });
                 }
             }
@@ -786,7 +795,7 @@ struct PipeDown : TileDown<S> {
                     const size_t dst = (size_t)drow * B::L;
                     static_for<NB>([&](auto j) {
                         const int n = c.n0 + cb + j * 32 + frag32_col(lane);
-                        if (n < B::L) B::Y[dst + n] = (uint16_t)f2bf(acc[i][j][r]);
+                        if (n < B::L) B::Y[dst + n] = (uint16_t)f2bf(acc[i][j][r] * c.td);
                     });
                 }
             }

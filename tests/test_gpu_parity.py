@@ -72,6 +72,11 @@ def test_prefill_t16384_sampled(ws):
     _workload_case("prefill_t16384", 96, ws)
 
 
+def test_prefill_mxfp4_t16384_sampled(ws):
+    # 4-bit records decoded once to bf16 for the tile GEMMs (large batches)
+    _workload_case("prefill_mxfp4_t16384", 64, ws)
+
+
 SMALL = gen.Shape(hidden=256, latent=192, n_experts=24, top_k=3, ffn=128, shared_ffn=64)
 
 
@@ -181,7 +186,7 @@ def test_fold_router_halves():
 SMALL_MX = gen.Shape(hidden=256, latent=256, n_experts=24, top_k=3, ffn=128, shared_ffn=128)
 
 
-@pytest.mark.parametrize("T", [3, 16, 40])
+@pytest.mark.parametrize("T", [3, 16, 40, 100, 1100])
 def test_small_mxfp4(T, ws):
     wl, lw = small_layer(SMALL_MX, "bf16", "bf16", "mxfp4")
     dl = DeviceLayer(lw, act="bf16")
@@ -191,7 +196,7 @@ def test_small_mxfp4(T, ws):
     check_block(lw, x, "bf16", out, label=f"small_mxfp4 T={T}")
 
 
-@pytest.mark.parametrize("T", [3, 16, 40, 100])
+@pytest.mark.parametrize("T", [3, 16, 40, 100, 1100])
 def test_small_nvfp4(T, ws):
     wl, lw = small_layer(SMALL_MX, "bf16", "bf16", "nvfp4")
     dl = DeviceLayer(lw, act="bf16")
