@@ -171,7 +171,8 @@ typedef struct {
  * Returns 0 for an invalid configuration. */
 size_t lmoe_expert_record_bytes(const lmoe_config* cfg, int32_t shared);
 
-/* Workspace bytes lmoe_forward needs for T tokens (monotone in T). */
+/* Workspace bytes lmoe_forward needs for T tokens (monotone in T).  With 4-bit routed experts
+ * and T >= 384 it includes n_experts decoded bf16 records (3 * ffn * latent * 2 bytes each). */
 lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes);
 
 /* Workspace bytes lmoe_permute needs for T tokens. */

@@ -168,8 +168,12 @@ struct ExpertArgs {
 
 // Large 4-bit batches: minimum T at which the records of the experts with tokens are decoded to
 // bf16 once and the bf16 tile GEMMs run (below it the weight-streaming kernels read the 4-bit
-// records directly).
-constexpr int kDequantMinT = 1024;
+// records directly).  Measured at the 145B shape with MXFP4 records: streaming is faster at
+// T = 256 (542 vs 580 us), decoding at T = 512 (655 vs 795 us) and beyond.
+#ifndef LMOE_DEQUANT_MIN_T
+#define LMOE_DEQUANT_MIN_T 384
+#endif
+constexpr int kDequantMinT = LMOE_DEQUANT_MIN_T;
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 
 // Row-major expert records -> packed records (nrec records of rec_bytes; F x L gate/up, L x F down;
