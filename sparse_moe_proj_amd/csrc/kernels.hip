@@ -483,7 +483,9 @@ hipError_t small_proj_launch(const SmallProj& p, hipStream_t s) {
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k, dim3((unsigned)cdiv(p.N, 16)), dim3(64 * LMOE_SP_WAVES), small_proj_lds(p.K), s, p);
+    // one workgroup per row block up to one per CU; beyond that the workgroups take several
+    hipLaunchKernelGGL(k, dim3((unsigned)std::min<long>(cdiv(p.N, 16), cu_count())), dim3(64 * LMOE_SP_WAVES),
+                       small_proj_lds(p.K), s, p);
     return last();
 }
 
@@ -492,7 +494,7 @@ hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const u
                                   uint16_t* z16h, const float* hnorm) {
     if (!small_proj_fits(T, H)) return hipErrorInvalidValue;
     SmallProj p{x, hnorm, 0, D, T, L, H, 0, z32, z16, Gr, br, E, logits, z16h};
-    const dim3 grid((unsigned)(cdiv(L, 16) + 2 * cdiv(E, 16)));
+    const dim3 grid((unsigned)std::min<long>(cdiv(L, 16) + 2 * cdiv(E, 16), cu_count()));
     if (hnorm) {
         auto k = small_proj_kernel<LMOE_SP_WAVES, LMOE_SP_SMAX, 2>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),

@@ -48,6 +48,10 @@ constexpr int kSmallProjGroups = 4;
 // unit of padding per row.
 __host__ __device__ inline size_t small_proj_lds(int K) { return (size_t)16 * (K / 8 + 1) * 16; }
 
+// Row blocks (16 weight rows each: the ceil(N / 16) blocks of W, then the router's hi and lo
+// blocks) are dealt to the workgroups (block b to workgroup b % grid); a workgroup with several
+// blocks requests the next block's weights before it reduces the current one, and a batch of at
+// most 16 tokens is staged once for all of them.
 template <int W, int SMAX, int XM>
 __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
     extern __shared__ uint4 xs[];  // [16][K / 8 + 1]: the current token group
@@ -58,118 +62,146 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
     const int K = p.K, T = p.T;
     const int ns = K / 32;
     const int nbw = (p.N + 15) / 16, nbe = (p.E + 15) / 16;
-    const bool rt = (int)blockIdx.x >= nbw;
-    const int rb = rt ? (int)blockIdx.x - nbw : (int)blockIdx.x;
-    const int half = rt && rb >= nbe ? 1 : 0;  // which half of the Gr rows
-    const int n0 = (rb - half * nbe) * 16;
-    const int nrow = rt ? p.E : p.N;
+    const int nblk = nbw + (p.Gr ? 2 * nbe : 0);
     const int s0 = wave * ns / W, s1 = (wave + 1) * ns / W;
-    const uint16_t* wrow =
-        rt ? p.Gr + ((size_t)min(n0 + j, nrow - 1) * 2 + half) * K : p.W + (size_t)min(n0 + j, nrow - 1) * K;
-    uint4 wv[SMAX];
-    auto loadw = [&](int b) {
-#pragma unroll
-        for (int i = 0; i < SMAX; ++i)
-            if (b + i < s1) wv[i] = ld16(wrow + (b + i) * 32 + kq * 8);
-    };
-    if (s0 < s1) loadw(s0);
     // a wave's whole K range fits in the registers: every token group reuses the same weights
     const bool single = s1 - s0 <= SMAX;
     const int per = K / 8, xst = per + 1;
     const int ngroups = (T + 15) / 16;
-    static_for<kSmallProjGroups>([&](auto G) {
-        constexpr int g = decltype(G)::value;
-        if (g < ngroups) {
-            const int t0 = 16 * g, tn = min(16, T - t0);
-            if (g > 0) {
-                __syncthreads();  // the previous group's LDS reads are done
-                if (!single && s0 < s1) loadw(s0);
-            }
-            if constexpr (XM == 2) {
-                for (int t = wave; t < tn; t += W) {
-                    const float4* row = reinterpret_cast<const float4*>(p.xpart + (size_t)(t0 + t) * K);
-                    float ss = 0.f;
-                    for (int c = lane; c < K / 4; c += 64) {
-                        const float4 u = row[c];
-                        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
-                    }
+    struct Blk {
+        const uint16_t* wrow;  // this lane's weight row
+        int n0, half, nrow;
+        bool rt;               // a router block (half 0: hi rows, 1: lo rows)
+    };
+    auto blk_of = [&](int b) {
+        Blk o;
+        o.rt = b >= nbw;
+        const int rb = o.rt ? b - nbw : b;
+        o.half = o.rt && rb >= nbe ? 1 : 0;
+        o.n0 = (rb - o.half * nbe) * 16;
+        o.nrow = o.rt ? p.E : p.N;
+        o.wrow = o.rt ? p.Gr + ((size_t)min(o.n0 + j, o.nrow - 1) * 2 + o.half) * K
+                      : p.W + (size_t)min(o.n0 + j, o.nrow - 1) * K;
+        return o;
+    };
+    uint4 wv[SMAX];
+    auto loadw = [&](const uint16_t* wrow, int b) {
 #pragma unroll
-                    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-                    if (lane == 0) rnorm[t] = 1.0f / sqrtf(ss / (float)K + p.eps);
+        for (int i = 0; i < SMAX; ++i)
+            if (b + i < s1) wv[i] = ld16(wrow + (b + i) * 32 + kq * 8);
+    };
+    int b = blockIdx.x;
+    Blk cur = blk_of(b);
+    if (s0 < s1) loadw(cur.wrow, s0);
+    bool first = true;
+    while (true) {
+        const int bn = b + (int)gridDim.x;
+        const bool more = bn < nblk;
+        const Blk nxt = blk_of(more ? bn : b);
+        static_for<kSmallProjGroups>([&](auto G) {
+            constexpr int g = decltype(G)::value;
+            if (g < ngroups) {
+                const int t0 = 16 * g, tn = min(16, T - t0);
+                if (g > 0 || !first) {
+                    __syncthreads();  // the previous group's or block's LDS reads are done
+                    if (g > 0 && !single && s0 < s1) loadw(cur.wrow, s0);
+                }
+                // the staged tokens of a single group stay valid for the workgroup's next blocks
+                if (ngroups > 1 || first) {
+                    if constexpr (XM == 2) {
+                        for (int t = wave; t < tn; t += W) {
+                            const float4* row = reinterpret_cast<const float4*>(p.xpart + (size_t)(t0 + t) * K);
+                            float ss = 0.f;
+                            for (int c = lane; c < K / 4; c += 64) {
+                                const float4 u = row[c];
+                                ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+                            }
+#pragma unroll
+                            for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+                            if (lane == 0) rnorm[t] = 1.0f / sqrtf(ss / (float)K + p.eps);
+                        }
+                        __syncthreads();
+                    }
+                    for (int e = threadIdx.x; e < tn * per; e += 64 * W) {
+                        const int t = e / per, c = e - t * per;
+                        uint4 v;
+                        if constexpr (XM == 0) {
+                            v = ld16(p.x16 + (size_t)(t0 + t) * K + c * 8);
+                        } else if constexpr (XM == 2) {
+                            const float* src = p.xpart + (size_t)(t0 + t) * K + c * 8;
+                            const float4 u0 = *reinterpret_cast<const float4*>(src);
+                            const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+                            const float r = rnorm[t];
+                            v = make_uint4(pack_bf2(u0.x * r, u0.y * r), pack_bf2(u0.z * r, u0.w * r),
+                                           pack_bf2(u1.x * r, u1.y * r), pack_bf2(u1.z * r, u1.w * r));
+                        } else {
+                            float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                            for (int q = 0; q < p.G; ++q) {
+                                const float* src = p.xpart + ((size_t)q * T + t0 + t) * K + c * 8;
+                                const float4 u0 = *reinterpret_cast<const float4*>(src);
+                                const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+                                a[0] += u0.x;
+                                a[1] += u0.y;
+                                a[2] += u0.z;
+                                a[3] += u0.w;
+                                a[4] += u1.x;
+                                a[5] += u1.y;
+                                a[6] += u1.z;
+                                a[7] += u1.w;
+                            }
+                            v = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]),
+                                           pack_bf2(a[6], a[7]));
+                        }
+                        xs[t * xst + c] = v;
+                    }
                 }
                 __syncthreads();
-            }
-            for (int e = threadIdx.x; e < tn * per; e += 64 * W) {
-                const int t = e / per, c = e - t * per;
-                uint4 v;
-                if constexpr (XM == 0) {
-                    v = ld16(p.x16 + (size_t)(t0 + t) * K + c * 8);
-                } else if constexpr (XM == 2) {
-                    const float* src = p.xpart + (size_t)(t0 + t) * K + c * 8;
-                    const float4 u0 = *reinterpret_cast<const float4*>(src);
-                    const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
-                    const float r = rnorm[t];
-                    v = make_uint4(pack_bf2(u0.x * r, u0.y * r), pack_bf2(u0.z * r, u0.w * r), pack_bf2(u1.x * r, u1.y * r),
-                                   pack_bf2(u1.z * r, u1.w * r));
-                } else {
-                    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                    for (int q = 0; q < p.G; ++q) {
-                        const float* src = p.xpart + ((size_t)q * T + t0 + t) * K + c * 8;
-                        const float4 u0 = *reinterpret_cast<const float4*>(src);
-                        const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
-                        a[0] += u0.x;
-                        a[1] += u0.y;
-                        a[2] += u0.z;
-                        a[3] += u0.w;
-                        a[4] += u1.x;
-                        a[5] += u1.y;
-                        a[6] += u1.z;
-                        a[7] += u1.w;
+                f32x4 acc = f32x4{};
+                const bool tok = j < tn;
+                for (int b2 = s0; b2 < s1; b2 += SMAX) {
+                    if (b2 != s0) loadw(cur.wrow, b2);
+#pragma unroll
+                    for (int i = 0; i < SMAX; ++i)
+                        if (b2 + i < s1) {
+                            const uint4 xv = tok ? xs[j * xst + (b2 + i) * 4 + kq] : zero4();
+                            acc = mfma16(wv[i], xv, acc);
+                        }
+                }
+                // the last group: the next block's weights are requested before this one is reduced
+                if (g == ngroups - 1 && more && s0 < s1) loadw(nxt.wrow, s0);
+                // lane (kq, j): rows n0 + 4 kq + r, token t0 + j
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[wave][(4 * kq + r) * 16 + j] = acc[r];
+                __syncthreads();
+                // thread e: token t0 + e / 16, row n0 + e % 16 (16 consecutive outputs of a token)
+                for (int e = threadIdx.x; e < 256; e += 64 * W) {
+                    const int t = e >> 4, r = e & 15, n = cur.n0 + r;
+                    if (t >= tn || n >= cur.nrow) continue;
+                    float v = 0.f;
+#pragma unroll
+                    for (int w = 0; w < W; ++w) v += red[w][r * 16 + t];
+                    if (cur.rt) {
+                        p.logits[((size_t)cur.half * T + t0 + t) * p.E + n] = cur.half == 0 && p.bias ? v + p.bias[n] : v;
+                        continue;
                     }
-                    v = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
-                }
-                xs[t * xst + c] = v;
-            }
-            __syncthreads();
-            f32x4 acc = f32x4{};
-            const bool tok = j < tn;
-            for (int b = s0; b < s1; b += SMAX) {
-                if (b != s0) loadw(b);
-#pragma unroll
-                for (int i = 0; i < SMAX; ++i)
-                    if (b + i < s1) {
-                        const uint4 xv = tok ? xs[j * xst + (b + i) * 4 + kq] : zero4();
-                        acc = mfma16(wv[i], xv, acc);
+                    const size_t o = (size_t)(t0 + t) * p.N + n;
+                    if (p.mode == 0) {
+                        p.out32[o] = v;
+                        p.out16[o] = (uint16_t)f2bf(v);
+                        if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                    } else if (p.mode == 1) {
+                        p.out16[o] = (uint16_t)f2bf(v);
+                    } else {
+                        p.out32[o] += v;
                     }
-            }
-            // lane (kq, j): rows n0 + 4 kq + r, token t0 + j
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave][(4 * kq + r) * 16 + j] = acc[r];
-            __syncthreads();
-            // thread e: token t0 + e / 16, row n0 + e % 16 (16 consecutive outputs of a token)
-            for (int e = threadIdx.x; e < 256; e += 64 * W) {
-                const int t = e >> 4, r = e & 15, n = n0 + r;
-                if (t >= tn || n >= nrow) continue;
-                float v = 0.f;
-#pragma unroll
-                for (int w = 0; w < W; ++w) v += red[w][r * 16 + t];
-                if (rt) {
-                    p.logits[((size_t)half * T + t0 + t) * p.E + n] = half == 0 && p.bias ? v + p.bias[n] : v;
-                    continue;
-                }
-                const size_t o = (size_t)(t0 + t) * p.N + n;
-                if (p.mode == 0) {
-                    p.out32[o] = v;
-                    p.out16[o] = (uint16_t)f2bf(v);
-                    if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
-                } else if (p.mode == 1) {
-                    p.out16[o] = (uint16_t)f2bf(v);
-                } else {
-                    p.out32[o] += v;
                 }
             }
-        }
-    });
+        });
+        if (!more) break;
+        first = false;
+        b = bn;
+        cur = nxt;
+    }
 }
 
 }  // namespace lmoe
