@@ -9,8 +9,10 @@
 // A copy instruction moves 1 KB: lane l writes LDS position l of the instruction's block, and
 // the lane picks its global source so that
 //   * a row-major operand block holds 8 rows x 128 bytes (a full cache line per row), with the
-//     16-byte chunks of row r stored XOR-swizzled by (r & 7), which keeps fragment reads free of
-//     bank conflicts;
+//     16-byte chunks of row r stored XOR-swizzled by ((r >> 1) & 7): a fragment read takes one
+//     chunk from each of 16 consecutive rows, and a row's 32 banks are set by its parity and the
+//     chunk, so the 8 rows of each parity must use 8 different chunks (swizzling by (r & 7) gave
+//     rows r and r + 8 the same banks);
 //   * a packed operand (weights stored as 16-row x 32-column tiles, see packed_row) keeps its
 //     tile order: a 16-row block of one stage is two consecutive tiles, 2 KB contiguous in HBM.
 // A problem type P supplies, per operand, a base pointer for the workgroup and, per lane and copy
@@ -52,7 +54,7 @@ __device__ __forceinline__ int rowmajor_row(int i, int lane) { return 8 * i + (l
 // Byte offset of this lane's 16-byte chunk of copy instruction i at stage 0, for a row-major
 // source row that starts `row_bytes` bytes after the operand base.
 __device__ __forceinline__ uint32_t rowmajor_off(uint32_t row_bytes, int i, int lane) {
-    const int chunk = (lane & 7) ^ (rowmajor_row(i, lane) & 7);
+    const int chunk = (lane & 7) ^ ((rowmajor_row(i, lane) >> 1) & 7);
     return row_bytes + chunk * 16;
 }
 
@@ -102,7 +104,7 @@ __device__ __forceinline__ int frag_pos(int row, int u) {
     if constexpr (PACKED)
         return ((row >> 4) * 2 + (u >> 2)) * 64 + (u & 3) * 16 + (row & 15);
     else
-        return row * 8 + (u ^ (row & 7));
+        return row * 8 + (u ^ ((row >> 1) & 7));
 }
 
 // LDS byte address of a pointer into a __shared__ array.

@@ -4,8 +4,8 @@
 // [N][K]), which is the operand layout of v_mfma_f32_32x32x16_bf16: every lane reads 16
 // contiguous bytes of one row.  One workgroup = 4 waves (256 threads) computes a BM x BN tile
 // with BK = 64; global -> register -> LDS staging is double buffered with one barrier per
-// k-tile, and LDS rows (128 B) are stored with their 16-B chunks XOR-swizzled by (row & 7)
-// so that the 32 rows a fragment read touches spread over the LDS banks.
+// k-tile, and LDS rows (128 B) are stored with their 16-B chunks XOR-swizzled by ((row >> 1) & 7)
+// so that the 16 consecutive rows a fragment read touches at a time spread over all LDS banks.
 //
 // A problem type P supplies the tile mapping, row addressing, loads (which may gather rows,
 // dequantise or split fp32 into hi/lo bf16 pairs) and the epilogue.
@@ -28,7 +28,7 @@ struct TileShape {
     static_assert(kAPerThread >= 1 && kBPerThread >= 1, "tile too small");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 template <class S, class P>
 __global__ __launch_bounds__(256) void tile_gemm_kernel(const P p) {
