@@ -1,6 +1,6 @@
 // Pipelined bf16 MFMA GEMM for batches of many tokens: C[m][n] = sum_k A[m][k] * B[n][k].
 //
-// One workgroup of 4 waves computes a BM x BN tile (each wave (BM/2) x (BN/2) with
+// One workgroup of WR x WC waves computes a BM x BN tile (each wave (BM/WR) x (BN/WC) with
 // v_mfma_f32_32x32x16_bf16).  K advances in stages of 64 columns.  Each stage's operands are
 // copied straight from global memory into LDS with global_load_lds_dwordx4 (no register
 // staging), NS stages deep, so the copies of the next NS-1 stages are in flight while one
@@ -25,14 +25,15 @@
 
 namespace lmoe {
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, int WR = 2, int WC = 2>
 struct PipeShape {
     static constexpr int kBM = BM, kBN = BN, kNS = NS;
-    static constexpr int kWM = BM / 2, kWN = BN / 2;  // wave tile
+    static constexpr int kWR = WR, kWC = WC, kWaves = WR * WC, kThreads = 64 * WR * WC;
+    static constexpr int kWM = BM / WR, kWN = BN / WC;  // wave tile
     static constexpr int kMB = kWM / 32, kNB = kWN / 32;
-    static constexpr int kAI = BM / 8, kBI = BN / 8;      // 1 KB copy instructions per stage
-    static constexpr int kAIW = kAI / 4, kBIW = kBI / 4;  // per wave
-    static_assert(kAI % 4 == 0 && kBI % 4 == 0, "copies split over 4 waves");
+    static constexpr int kAI = BM / 8, kBI = BN / 8;                // 1 KB copy instructions per stage
+    static constexpr int kAIW = kAI / kWaves, kBIW = kBI / kWaves;  // per wave
+    static_assert(kAI % kWaves == 0 && kBI % kWaves == 0, "copies split over the waves");
     static constexpr int kLoadsPerStage = kAIW + kBIW;
     static constexpr int kStageUnits = (BM + BN) * 8;  // 16-byte units per stage
     static_assert(NS * kStageUnits * 16 <= 160 * 1024, "LDS budget");
@@ -224,7 +225,7 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
     constexpr int NS = S::kNS;
     constexpr int LPS = S::kLoadsPerStage;
     static_assert(NS >= 2 && NS <= 4, "two to four stages");
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / S::kWC, wn = wave % S::kWC;
 #pragma unroll
     for (int i = 0; i < S::kMB; ++i)
 #pragma unroll
@@ -283,7 +284,7 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
 
 // One tile per workgroup; grid (N tiles, M tiles upper bound), XCD-aware order.
 template <class S, class P>
-__global__ __launch_bounds__(256) void pipe_gemm_kernel(const P p) {
+__global__ __launch_bounds__(S::kThreads) void pipe_gemm_kernel(const P p) {
     __shared__ uint4 st0[S::kStageUnits], st1[S::kStageUnits];
     __shared__ uint4 st2[S::kNS >= 3 ? S::kStageUnits : 1], st3[S::kNS == 4 ? S::kStageUnits : 1];
     typename P::Ctx ctx;
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(256) void pipe_gemm_kernel(const P p) {
     xcd_tile(m_tile, n_tile);
     if (!p.tile(m_tile, n_tile, ctx)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rb = (wave >> 1) * S::kWM, cb = (wave & 1) * S::kWN;
+    const int rb = (wave / S::kWC) * S::kWM, cb = (wave % S::kWC) * S::kWN;
     const int nk = p.k_stages(ctx);
     const PipeCopies<S> c = pipe_copies<S>(p, ctx, wave, lane);
     pipe_prologue<S, P>(c, nk, st0, st1, st2, wave);
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256) void pipe_gemm_kernel(const P p) {
 // together.  No global load is issued after the prefetch until the next K loop (a wait for such
 // a load would also wait for the prefetch).
 template <class S, class P>
-__global__ __launch_bounds__(256) void pipe_gemm_persistent(const P p, int n_tiles) {
+__global__ __launch_bounds__(S::kThreads) void pipe_gemm_persistent(const P p, int n_tiles) {
     __shared__ uint4 st0[S::kStageUnits], st1[S::kStageUnits];
     __shared__ uint4 st2[S::kNS >= 3 ? S::kStageUnits : 1], st3[S::kNS == 4 ? S::kStageUnits : 1];
     const int total = p.m_tiles() * n_tiles;
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(256) void pipe_gemm_persistent(const P p, int n_til
     const int nwx = ((int)gridDim.x - x + g - 1) / g;  // workgroups in this group
     const int lo = (int)((long)total * x / g), hi = (int)((long)total * (x + 1) / g);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rb = (wave >> 1) * S::kWM, cb = (wave & 1) * S::kWN;
+    const int rb = (wave / S::kWC) * S::kWM, cb = (wave % S::kWC) * S::kWN;
 
     // the next valid tile at or after l (uniform over the workgroup); false when none is left
     auto next_tile = [&](int& l, typename P::Ctx& ctx) {

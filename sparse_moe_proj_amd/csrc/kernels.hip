@@ -407,8 +407,14 @@ inline hipError_t last() { return hipGetLastError(); }
 #ifndef LMOE_PIPE_NS
 #define LMOE_PIPE_NS 3
 #endif
+#ifndef LMOE_PIPE_WR  // wave grid of a pipelined GEMM workgroup (rows x columns of wave tiles)
+#define LMOE_PIPE_WR 2
+#endif
+#ifndef LMOE_PIPE_WC
+#define LMOE_PIPE_WC 4
+#endif
 #ifndef LMOE_PIPE_PROJ
-#define LMOE_PIPE_PROJ 0
+#define LMOE_PIPE_PROJ 1
 #endif
 #ifndef LMOE_PIPE_PERSIST
 #define LMOE_PIPE_PERSIST 1
@@ -428,7 +434,7 @@ using TileL = TileShape<LMOE_TILE_M, LMOE_TILE_N, 2, 2>;
 #ifndef LMOE_PIPE
 #define LMOE_PIPE 1
 #endif
-using PipeL = PipeShape<LMOE_PIPE_M, LMOE_PIPE_N, LMOE_PIPE_NS>;
+using PipeL = PipeShape<LMOE_PIPE_M, LMOE_PIPE_N, LMOE_PIPE_NS, LMOE_PIPE_WR, LMOE_PIPE_WC>;
 
 // Persistent launch: at most LMOE_STREAM_GRID workgroups walk max_tiles x row-group items.
 template <int W, int KS, int NMAT, class P, int CH0 = kChunk>
@@ -556,7 +562,7 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
         PipeProj<PipeL> p{{x, W, T, N, K, mode, out32, out16, out16lo}};
         const int nn = (int)cdiv(N, PipeL::kBN);
         auto k = pipe_gemm_persistent<PipeL, PipeProj<PipeL>>;
-        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, 256), (long)cdiv(T, PipeL::kBM) * nn)), dim3(256), 0,
+        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeL::kThreads), (long)cdiv(T, PipeL::kBM) * nn)), dim3(PipeL::kThreads), 0,
                            s, p, nn);
         return last();
     }
@@ -834,10 +840,10 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
         const int nn_up = (int)cdiv(Fmax, PipeL::kBN / 2);
         if (LMOE_PIPE_PERSIST) {
             auto k = pipe_gemm_persistent<PipeL, PipeUp<PipeL>>;
-            hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, 256), (long)a.max_tiles * nn_up)), dim3(256), 0,
+            hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeL::kThreads), (long)a.max_tiles * nn_up)), dim3(PipeL::kThreads), 0,
                                s, up, nn_up);
         } else {
-            hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeUp<PipeL>>), dim3(nn_up, a.max_tiles), dim3(256), 0, s, up);
+            hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeUp<PipeL>>), dim3(nn_up, a.max_tiles), dim3(PipeL::kThreads), 0, s, up);
         }
         hipError_t err = last();
         if (err != hipSuccess) return err;
@@ -847,10 +853,10 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
         const int nn_dn = (int)cdiv(a.L, PipeL::kBN);
         if (LMOE_PIPE_PERSIST) {
             auto k = pipe_gemm_persistent<PipeL, PipeDown<PipeL>>;
-            hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, 256), (long)a.max_tiles * nn_dn)), dim3(256), 0,
+            hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeL::kThreads), (long)a.max_tiles * nn_dn)), dim3(PipeL::kThreads), 0,
                                s, dn, nn_dn);
         } else {
-            hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeDown<PipeL>>), dim3(nn_dn, a.max_tiles), dim3(256), 0, s, dn);
+            hipLaunchKernelGGL((pipe_gemm_kernel<PipeL, PipeDown<PipeL>>), dim3(nn_dn, a.max_tiles), dim3(PipeL::kThreads), 0, s, dn);
         }
         if ((err = last()) != hipSuccess) return err;
         ev.end(kStageDown);
