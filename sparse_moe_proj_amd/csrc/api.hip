@@ -136,9 +136,9 @@ Layout plan(const Dims& d, int T) {
     lo.H = take((size_t)lo.R * lo.Hs * act);
     lo.Y = take(lo.decode_path ? 0 : (size_t)lo.R * d.L * (d.f32 ? 4 : 2));
     lo.mpart = take(lo.decode_path ? (size_t)decode_groups() * T * d.Lz * 4 : 0);
-    // merged rows (larger batches), or with expert groups the small-batch partials summed in bf16
-    // when the U launch cannot stage them itself
-    lo.m = take(lo.decode_path ? (small_proj_fits(T, d.Lz) ? 0 : (size_t)T * d.Lz * 2) : (size_t)T * d.Lz * act);
+    // merged rows (larger batches), or with expert groups and small batches whose U launch cannot
+    // stage all groups at once, the U products of the groups [G][T][H] fp32
+    lo.m = take(lo.decode_path ? (small_proj_fits(T, d.Lz) ? 0 : (size_t)d.G * T * d.H * 4) : (size_t)T * d.Lz * act);
     lo.deq = take(deq ? (size_t)d.E * 3 * d.F * d.L * 2 : 0);  // decoded bf16 records
     lo.deq_ts = take(deq ? (size_t)d.E * 3 * 4 : 0);
     lo.total = o;
@@ -432,11 +432,9 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         if (small_proj_fits(T, d.Lz)) {
             e = launch_proj_partials(mpart, decode_groups(), U, T, d.H, d.Lz, umode, static_cast<float*>(y),
                                      static_cast<uint16_t*>(y), s);
-        } else {  // expert groups: the partials summed first, then U over every group's columns
-            uint16_t* m16 = static_cast<uint16_t*>(at(lo.m));
-            e = launch_sum_partials(mpart, decode_groups(), T, d.Lz, m16, s);
-            if (e == hipSuccess)
-                e = launch_proj_bf16(m16, U, T, d.H, d.Lz, umode, static_cast<float*>(y), static_cast<uint16_t*>(y), s);
+        } else {  // expert groups: U_g . m_g per group (K = latent each), then the sum over groups
+            e = launch_proj_partials_kgroups(mpart, decode_groups(), U, T, d.H, d.L, d.G, static_cast<float*>(at(lo.m)),
+                                             umode, static_cast<float*>(y), static_cast<uint16_t*>(y), s);
         }
         if (e != hipSuccess) return hip_fail(e, "U projection");
         ev.end(LMOE_STAGE_U);

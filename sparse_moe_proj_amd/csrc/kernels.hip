@@ -230,22 +230,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y
     }
 }
 
-// m16 [T][K] = bf16(sum over g of part[g][T][K]), in g order (the small-batch merged partials
-// when the U launch cannot stage them itself).
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ part, int G, int T, int K,
-                                                           uint16_t* __restrict__ m16) {
-    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4, n = (size_t)T * K;
-    if (i >= n) return;
-    float4 a = *reinterpret_cast<const float4*>(part + i);
-    for (int g = 1; g < G; ++g) {
-        const float4 b = *reinterpret_cast<const float4*>(part + (size_t)g * n + i);
-        a.x += b.x;
-        a.y += b.y;
-        a.z += b.z;
-        a.w += b.w;
-    }
-    *reinterpret_cast<uint2*>(m16 + i) = make_uint2(pack_bf2(a.x, a.y), pack_bf2(a.z, a.w));
-}
 
 
 // ==============================================================================================
@@ -490,8 +474,9 @@ hipError_t small_proj_launch(const SmallProj& p, hipStream_t s) {
         hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallProjLds);
     if (attr != hipSuccess) return attr;
     // one workgroup per row block up to one per CU; beyond that the workgroups take several
-    hipLaunchKernelGGL(k, dim3((unsigned)std::min<long>(cdiv(p.N, 16), cu_count())), dim3(64 * LMOE_SP_WAVES),
-                       small_proj_lds(p.K), s, p);
+    // (a multiple of KG: workgroup w takes K group w % KG)
+    const long grid = std::max<long>(std::min<long>(cdiv(p.N, 16) * p.KG, cu_count()) / p.KG * p.KG, p.KG);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * LMOE_SP_WAVES), small_proj_lds(p.K), s, p);
     return last();
 }
 
@@ -546,6 +531,31 @@ hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, in
     return small_proj_launch<1>(SmallProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0,
                                           nullptr, nullptr},
                                 s);
+}
+
+// y = sum over the KG K groups of part[kg] (in order): mode 1: out16 = bf16(y); 2: out32 += y.
+__global__ __launch_bounds__(256) void sum_groups_kernel(const float* __restrict__ part, int KG, int T, int N, int mode,
+                                                         float* __restrict__ out32, uint16_t* __restrict__ out16) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x, n = (size_t)T * N;
+    if (i >= n) return;
+    float v = 0.f;
+    for (int g = 0; g < KG; ++g) v += part[(size_t)g * n + i];
+    if (mode == 2)
+        out32[i] += v;
+    else
+        out16[i] = (uint16_t)f2bf(v);
+}
+
+hipError_t launch_proj_partials_kgroups(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int KG,
+                                        float* part, int mode, float* out32, uint16_t* out16, hipStream_t s) {
+    if (!small_proj_fits(T, K)) return hipErrorInvalidValue;
+    SmallProj p{nullptr, xpart, G, W, T, N, K, 3, part, nullptr, nullptr, nullptr, 0, nullptr, nullptr};
+    p.KG = KG;
+    hipError_t e = small_proj_launch<1>(p, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sum_groups_kernel, dim3((unsigned)cdiv((size_t)T * N, 256)), dim3(256), 0, s, part, KG, T, N, mode,
+                       out32, out16);
+    return last();
 }
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
@@ -877,11 +887,6 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
     return hipSuccess;
 }
 
-hipError_t launch_sum_partials(const float* part, int G, int T, int K, uint16_t* m16, hipStream_t s) {
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)cdiv((size_t)T * K / 4, 256)), dim3(256), 0, s, part, G, T, K,
-                       m16);
-    return last();
-}
 
 hipError_t launch_combine(const void* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
                           hipStream_t s, const int32_t* ids, int groups, int Eg) {

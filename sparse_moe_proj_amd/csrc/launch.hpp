@@ -85,8 +85,6 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 hipError_t launch_router_x(const uint16_t* x, const uint16_t* Gr, const float* br, int T, int E, int K, float* logits,
                            hipStream_t s);
 
-// m16 [T][K] bf16 = the sum, in order, of G fp32 partials [G][T][K] (K a multiple of 4).
-hipError_t launch_sum_partials(const float* part, int G, int T, int K, uint16_t* m16, hipStream_t s);
 
 int perm_blocks(int T);
 
@@ -120,6 +118,12 @@ hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const u
 // experts, row e uses D rows (e / Eg) * L .. (Eg = 0: one group).
 hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int L, int H, uint16_t* Gr, hipStream_t s,
                               int Eg = 0);
+
+// U projection of a small batch with expert groups: input rows of KG * K columns, the sum (in
+// order) of G fp32 partials [G][T][KG * K]; one launch multiplies each K group into part
+// [KG][T][N] fp32, a second sums the groups in order (mode 1: bf16 out16; 2: out32 +=).
+hipError_t launch_proj_partials_kgroups(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int KG,
+                                        float* part, int mode, float* out32, uint16_t* out16, hipStream_t s);
 
 // U projection of a small batch whose input is the sum (in order) of G fp32 partials [G][T][K].
 hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,

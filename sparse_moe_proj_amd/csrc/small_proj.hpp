@@ -23,7 +23,8 @@ struct SmallProj {
     const float* xpart;   // XM 1: [G][T][K] fp32; XM 2: the residual h [T][K] fp32
     int G;
     const uint16_t* W;    // [N][K] bf16
-    int T, N, K, mode;    // mode 0: out32 = v, out16 = bf16(v); 1: out16 = bf16(v); 2: out32 += v
+    int T, N, K, mode;    // mode 0: out32 = v, out16 = bf16(v); 1: out16 = bf16(v); 2: out32 += v;
+                          // 3: out32[kg][T][N] = v, the product over K group kg (below)
     float* out32;
     uint16_t* out16;
     // Optional second product in the same launch (Gr != null), from Gr [E][2][K] bf16 (hi, lo
@@ -36,6 +37,11 @@ struct SmallProj {
     float* logits;  // [2][T][E]
     uint16_t* out16h;  // mode 0, optional: fp16(v) as well (the token operand of 4-bit experts)
     float eps = 1e-6f;  // XM 2: the RMSNorm epsilon
+    // K groups (mode 3, no router rows): W and the input rows are KG * K wide; block b of the
+    // KG * ceil(N / 16) row blocks multiplies columns kg * K .. of both, kg = b / ceil(N / 16).
+    // Workgroup w takes the blocks of K group w % KG only (the grid is a multiple of KG), so its
+    // staged input columns serve all of its blocks.
+    int KG = 1;
 };
 
 // Largest staged-activation LDS a small-batch projection takes (plus W KB of static LDS).
@@ -62,7 +68,8 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
     const int K = p.K, T = p.T;
     const int ns = K / 32;
     const int nbw = (p.N + 15) / 16, nbe = (p.E + 15) / 16;
-    const int nblk = nbw + (p.Gr ? 2 * nbe : 0);
+    const int KP = p.KG * K;  // row pitch of W and of the input rows
+    const int nblk = nbw * p.KG + (p.Gr ? 2 * nbe : 0);
     const int s0 = wave * ns / W, s1 = (wave + 1) * ns / W;
     // a wave's whole K range fits in the registers: every token group reuses the same weights
     const bool single = s1 - s0 <= SMAX;
@@ -70,18 +77,19 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
     const int ngroups = (T + 15) / 16;
     struct Blk {
         const uint16_t* wrow;  // this lane's weight row
-        int n0, half, nrow;
+        int n0, half, nrow, kg;
         bool rt;               // a router block (half 0: hi rows, 1: lo rows)
     };
     auto blk_of = [&](int b) {
         Blk o;
-        o.rt = b >= nbw;
-        const int rb = o.rt ? b - nbw : b;
+        o.rt = b >= nbw * p.KG;
+        o.kg = o.rt ? 0 : b / nbw;
+        const int rb = o.rt ? b - nbw * p.KG : b - o.kg * nbw;
         o.half = o.rt && rb >= nbe ? 1 : 0;
         o.n0 = (rb - o.half * nbe) * 16;
         o.nrow = o.rt ? p.E : p.N;
         o.wrow = o.rt ? p.Gr + ((size_t)min(o.n0 + j, o.nrow - 1) * 2 + o.half) * K
-                      : p.W + (size_t)min(o.n0 + j, o.nrow - 1) * K;
+                      : p.W + (size_t)min(o.n0 + j, o.nrow - 1) * KP + (size_t)o.kg * K;
         return o;
     };
     uint4 wv[SMAX];
@@ -90,13 +98,19 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
         for (int i = 0; i < SMAX; ++i)
             if (b + i < s1) wv[i] = ld16(wrow + (b + i) * 32 + kq * 8);
     };
-    int b = blockIdx.x;
+    // this workgroup's blocks: K group kg0, row blocks r0, r0 + step, ... (KG = 1: every block)
+    const int kg0 = (int)blockIdx.x % p.KG, step = (int)gridDim.x / p.KG;
+    const int nrb = p.KG == 1 ? nblk : nbw;
+    int r = (int)blockIdx.x / p.KG;
+    int b = kg0 * nbw + r;
     Blk cur = blk_of(b);
     if (s0 < s1) loadw(cur.wrow, s0);
     bool first = true;
+    int staged_kg = -1;  // the K group whose input columns are staged
     while (true) {
-        const int bn = b + (int)gridDim.x;
-        const bool more = bn < nblk;
+        const int rn = r + step;
+        const bool more = rn < nrb;
+        const int bn = kg0 * nbw + rn;
         const Blk nxt = blk_of(more ? bn : b);
         static_for<kSmallProjGroups>([&](auto G) {
             constexpr int g = decltype(G)::value;
@@ -106,8 +120,10 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
                     __syncthreads();  // the previous group's or block's LDS reads are done
                     if (g > 0 && !single && s0 < s1) loadw(cur.wrow, s0);
                 }
-                // the staged tokens of a single group stay valid for the workgroup's next blocks
-                if (ngroups > 1 || first) {
+                // the staged tokens of a single group stay valid for the workgroup's next blocks of
+                // the same K group
+                if (ngroups > 1 || first || staged_kg != cur.kg) {
+                    staged_kg = cur.kg;
                     if constexpr (XM == 2) {
                         for (int t = wave; t < tn; t += W) {
                             const float4* row = reinterpret_cast<const float4*>(p.xpart + (size_t)(t0 + t) * K);
@@ -137,7 +153,7 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
                         } else {
                             float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                             for (int q = 0; q < p.G; ++q) {
-                                const float* src = p.xpart + ((size_t)q * T + t0 + t) * K + c * 8;
+                                const float* src = p.xpart + ((size_t)q * T + t0 + t) * KP + (size_t)cur.kg * K + c * 8;
                                 const float4 u0 = *reinterpret_cast<const float4*>(src);
                                 const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
                                 a[0] += u0.x;
@@ -191,6 +207,8 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
                         if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
                     } else if (p.mode == 1) {
                         p.out16[o] = (uint16_t)f2bf(v);
+                    } else if (p.mode == 3) {
+                        p.out32[(size_t)cur.kg * T * p.N + o] = v;
                     } else {
                         p.out32[o] += v;
                     }
@@ -199,6 +217,7 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
         });
         if (!more) break;
         first = false;
+        r = rn;
         b = bn;
         cur = nxt;
     }
