@@ -200,33 +200,35 @@ __device__ __forceinline__ float4 load_y4(const void* Y, size_t off) {
     }
 }
 
-// grid (L / 1024, T, expert groups): group g's merged row m_g goes to columns g * L .. of m
-// [T][groups * L]; a slot counts for group ids / Eg (ids null: one group), the shared expert
-// for group 0.
+// grid (L / 1024, min(T, 65535), expert groups), tokens t = blockIdx.y, + gridDim.y, ...: group
+// g's merged row m_g goes to columns g * L .. of m [T][groups * L]; a slot counts for group
+// ids / Eg (ids null: one group), the shared expert for group 0.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const float* __restrict__ w, int T,
                                                       int k, int L, int has_shared, void* __restrict__ m,
                                                       const int32_t* __restrict__ ids, int Eg) {
-    const int t = blockIdx.y, g = blockIdx.z;
+    const int g = blockIdx.z;
     const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (c >= L) return;
     const size_t mp = (size_t)gridDim.z * L;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (has_shared && g == 0) acc = load_y4<OUT_BF16>(Y, ((size_t)T * k + t) * L + c);
-    for (int s = 0; s < k; ++s) {
-        if (ids && ids[(size_t)t * k + s] / Eg != g) continue;
-        const float ws = w[(size_t)t * k + s];
-        const float4 y = load_y4<OUT_BF16>(Y, ((size_t)t * k + s) * L + c);
-        acc.x += ws * y.x;
-        acc.y += ws * y.y;
-        acc.z += ws * y.z;
-        acc.w += ws * y.w;
-    }
-    if (OUT_BF16) {
-        uint2 o = make_uint2(pack_bf2(acc.x, acc.y), pack_bf2(acc.z, acc.w));
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(m) + t * mp + (size_t)g * L + c) = o;
-    } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(m) + t * mp + (size_t)g * L + c) = acc;
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (has_shared && g == 0) acc = load_y4<OUT_BF16>(Y, ((size_t)T * k + t) * L + c);
+        for (int s = 0; s < k; ++s) {
+            if (ids && ids[(size_t)t * k + s] / Eg != g) continue;
+            const float ws = w[(size_t)t * k + s];
+            const float4 y = load_y4<OUT_BF16>(Y, ((size_t)t * k + s) * L + c);
+            acc.x += ws * y.x;
+            acc.y += ws * y.y;
+            acc.z += ws * y.z;
+            acc.w += ws * y.w;
+        }
+        if (OUT_BF16) {
+            uint2 o = make_uint2(pack_bf2(acc.x, acc.y), pack_bf2(acc.z, acc.w));
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(m) + t * mp + (size_t)g * L + c) = o;
+        } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(m) + t * mp + (size_t)g * L + c) = acc;
+        }
     }
 }
 
@@ -890,7 +892,7 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
 
 hipError_t launch_combine(const void* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
                           hipStream_t s, const int32_t* ids, int groups, int Eg) {
-    const dim3 grid(cdiv(L / 4, 256), T, groups > 1 ? groups : 1);
+    const dim3 grid(cdiv(L / 4, 256), std::min(T, 65535), groups > 1 ? groups : 1);
     const int32_t* gids = groups > 1 ? ids : nullptr;
     if (out_bf16)
         hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, Y, w, T, k, L, has_shared, m, gids, Eg);
