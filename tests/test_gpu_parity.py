@@ -284,6 +284,26 @@ def test_determinism_and_batch_invariance(ws):
         assert torch.equal(d["y"], a["y"][p]), f"token permutation (T={T})"
 
 
+@pytest.mark.parametrize("case", ["groups_t8", "groups_t300", "mxfp4_t1100", "nvfp4_t500"])
+def test_determinism_other_paths(case, ws):
+    """Run-to-run bitwise equality and token-permutation equivariance on the expert-group paths
+    and the large 4-bit batch path (records decoded once to bf16)."""
+    shape, fmt, T = {"groups_t8": (SMALL_G, "bf16", 8), "groups_t300": (SMALL_G, "bf16", 300),
+                     "mxfp4_t1100": (SMALL_MX, "mxfp4", 1100), "nvfp4_t500": (SMALL_MX, "nvfp4", 500)}[case]
+    wl, lw = small_layer(shape, "bf16", "bf16", fmt, wid=81)
+    dl = DeviceLayer(lw, act="bf16")
+    xt = upload_tokens(gen.make_tokens(wl, T=T, salt=2))
+    a = run_forward(dl, xt, ws)
+    b = run_forward(dl, xt, ws)
+    torch.cuda.synchronize()
+    for key in ("y", "z", "ids", "w", "offsets", "perm"):
+        assert torch.equal(a[key], b[key]), f"run-to-run difference in {key} ({case})"
+    p = torch.randperm(T, generator=torch.Generator().manual_seed(1)).cuda()
+    d = run_forward(dl, xt[p].contiguous(), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(d["y"], a["y"][p]), f"token permutation ({case})"
+
+
 def test_zero_tokens_noop(ws):
     wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
     dl = DeviceLayer(lw, act="bf16")
