@@ -2,6 +2,7 @@
 // Everything here runs on the host and only enqueues work on the caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <string>
 
@@ -88,10 +89,15 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t x16, z32, z16, z16h, zlo, logits, ids, w, offsets, perm, inv, rowinfo, hist, base, tiles, ntiles, H, Y, mpart, m,
-        deq, deq_ts, total;
-    bool stream_path, decode_path, fused_router, deq_path;
+        deq, deq_ts, z8, z8s, z4, z4s, h8, h8s, total;
+    bool stream_path, decode_path, fused_router, deq_path, mx_path;
     int max_tiles, BM, Hs, R;
 };
+
+bool mx_mfma_enabled() {
+    const char* v = getenv("LMOE_MX_MFMA");
+    return !(v && v[0] == '0');
+}
 
 Layout plan(const Dims& d, int T) {
     Layout lo{};
@@ -100,9 +106,12 @@ Layout plan(const Dims& d, int T) {
     lo.decode_path = !d.f32 && decode_fits(T, d.L, d.F, d.Fs);
     // 4-bit records stream through the weight-streaming kernels up to kDequantMinT tokens; larger
     // batches decode the touched records to bf16 once and take the tile GEMMs
-    const bool deq = d.mx && !lo.decode_path && T >= kDequantMinT;
+    const bool big4 = d.mx && !lo.decode_path && T >= kDequantMinT;
+    // MXFP4 takes the block-scaled MFMA kernels unless LMOE_MX_MFMA=0 asks for the decode to bf16
+    lo.mx_path = big4 && d.fmt == 1 && mx_mfma_enabled();
+    const bool deq = big4 && !lo.mx_path;
     lo.deq_path = deq;
-    lo.stream_path = !d.f32 && (T <= kStreamMaxT || (d.mx && !deq) || lo.decode_path);
+    lo.stream_path = !d.f32 && (T <= kStreamMaxT || (d.mx && !big4) || lo.decode_path);
     lo.fused_router = !d.f32 && small_proj_fits(T, d.H);
     // expert groups take the logits from x and the folded router for every batch (two halves)
     const bool halves = lo.fused_router || d.G > 1;
@@ -141,6 +150,12 @@ Layout plan(const Dims& d, int T) {
     lo.m = take(lo.decode_path ? (small_proj_fits(T, d.Lz) ? 0 : (size_t)d.G * T * d.H * 4) : (size_t)T * d.Lz * act);
     lo.deq = take(deq ? (size_t)d.E * 3 * d.F * d.L * 2 : 0);  // decoded bf16 records
     lo.deq_ts = take(deq ? (size_t)d.E * 3 * 4 : 0);
+    lo.z8 = take(lo.mx_path ? (size_t)T * d.Lz : 0);
+    lo.z8s = take(lo.mx_path ? (size_t)T * d.Lz / 32 : 0);
+    lo.z4 = take(lo.mx_path ? (size_t)T * d.Lz / 2 : 0);
+    lo.z4s = take(lo.mx_path ? (size_t)T * d.Lz / 32 : 0);
+    lo.h8 = take(lo.mx_path ? (size_t)T * d.k * d.F : 0);
+    lo.h8s = take(lo.mx_path ? (size_t)T * d.k * d.F / 32 : 0);
     lo.total = o;
     return lo;
 }
@@ -424,6 +439,15 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
                  lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr, d.Eg, d.Lz,
                  lo.deq_path ? static_cast<uint16_t*>(at(lo.deq)) : nullptr,
                  lo.deq_path ? static_cast<float*>(at(lo.deq_ts)) : nullptr, offsets};
+    if (lo.mx_path) {
+        a.mx_path = true;
+        a.z8 = static_cast<uint8_t*>(at(lo.z8));
+        a.z8s = static_cast<uint8_t*>(at(lo.z8s));
+        a.z4 = static_cast<uint8_t*>(at(lo.z4));
+        a.z4s = static_cast<uint8_t*>(at(lo.z4s));
+        a.h8 = static_cast<uint8_t*>(at(lo.h8));
+        a.h8s = static_cast<uint8_t*>(at(lo.h8s));
+    }
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     const int umode = o.residual ? 2 : 1;
     const uint16_t* U = static_cast<const uint16_t*>(wt->U);

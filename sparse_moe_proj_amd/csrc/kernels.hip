@@ -3,6 +3,7 @@
 #include <limits.h>
 
 #include "decode_experts.hpp"
+#include "experts_mx.hpp"
 #include "gemm_stream.hpp"
 #include "gemm_tile.hpp"
 #include "launch.hpp"
@@ -825,6 +826,72 @@ hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     return hipSuccess;
 }
 
+// Large MXFP4 batches on the block-scaled MFMA: z to MXFP8 plus an MXFP4 residual, then the routed
+// gate/up (H to MXFP8 in its epilogue) and down products from the stored records; the shared expert's (bf16)
+// segment takes the bf16 kernels.
+#ifndef LMOE_MX_NS
+#define LMOE_MX_NS 3
+#endif
+using MxUpL = MxShape<128, 256, LMOE_MX_NS, 2, 4, true>;
+using MxDnL = MxShape<128, 256, LMOE_MX_NS, 2, 4, false>;
+static_assert(MxUpL::kBM == PipeL::kBM && MxDnL::kBM == PipeL::kBM, "the work list's tile rows");
+
+hipError_t launch_experts_mx(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
+    if (!a.z8 || !a.z8s || !a.z4 || !a.z4s || !a.h8 || !a.h8s || a.fmt != 1 || a.L % 128 || a.F % 128)
+        return hipErrorInvalidValue;
+    const int nsh = a.shared ? (int)cdiv(a.T, PipeL::kBM) : 0;
+    SegSpace rs = seg;
+    rs.part = 1;
+    rs.nsh = nsh;
+    SegSpace ss = rs;
+    ss.part = 2;
+    const uint8_t* ex = static_cast<const uint8_t*>(a.experts);
+    const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
+    const int zp = a.zp > 0 ? a.zp : a.L;
+    ev.begin(kStageUp);
+    const size_t nblk = (size_t)a.T * zp / 32;
+    hipLaunchKernelGGL(quant_mx_kernel, dim3((unsigned)cdiv(nblk, 256)), dim3(256), 0, s, a.z16, nblk, a.z8, a.z8s,
+                       a.z4, a.z4s);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    {
+        MxUp<MxUpL> up{rs, a.z8, a.z8s, a.z4, a.z4s, ex, a.rec_bytes, a.L, a.F, a.h8, a.h8s};
+        const int nn = (int)cdiv(a.F, MxUpL::kBN / 2);
+        auto k = mx_gemm_persistent<MxUpL, MxUp<MxUpL>>;
+        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, MxUpL::kThreads), (long)a.max_tiles * nn)),
+                           dim3(MxUpL::kThreads), 0, s, up, nn);
+        if ((err = last()) != hipSuccess) return err;
+    }
+    if (nsh > 0) {
+        PipeUp<PipeL> up{{ss, a.z16, sh, sh, 0, a.L, a.F, a.Fs, a.Hs, a.H, nullptr}};
+        const int nn = (int)cdiv(a.Fs, PipeL::kBN / 2);
+        auto k = pipe_gemm_persistent<PipeL, PipeUp<PipeL>>;
+        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeL::kThreads), (long)nsh * nn)),
+                           dim3(PipeL::kThreads), 0, s, up, nn);
+        if ((err = last()) != hipSuccess) return err;
+    }
+    ev.end(kStageUp);
+    ev.begin(kStageDown);
+    {
+        MxDown<MxDnL> dn{rs, a.h8, a.h8s, ex, a.rec_bytes, a.L, a.F, a.Y};
+        const int nn = (int)cdiv(a.L, MxDnL::kBN);
+        auto k = mx_gemm_persistent<MxDnL, MxDown<MxDnL>>;
+        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, MxDnL::kThreads), (long)a.max_tiles * nn)),
+                           dim3(MxDnL::kThreads), 0, s, dn, nn);
+        if ((err = last()) != hipSuccess) return err;
+    }
+    if (nsh > 0) {
+        PipeDown<PipeL> dn{{ss, a.H, sh, sh, 0, a.L, a.F, a.Fs, a.Hs, a.Y, nullptr}};
+        const int nn = (int)cdiv(a.L, PipeL::kBN);
+        auto k = pipe_gemm_persistent<PipeL, PipeDown<PipeL>>;
+        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeL::kThreads), (long)nsh * nn)),
+                           dim3(PipeL::kThreads), 0, s, dn, nn);
+        if ((err = last()) != hipSuccess) return err;
+    }
+    ev.end(kStageDown);
+    return hipSuccess;
+}
+
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev) {
     const SegSpace seg{a.tiles, a.ntiles, a.perm, a.T, a.k, a.E, a.Eg > 0 ? a.Eg : a.E, a.zp > 0 ? a.zp : a.L};
     if (a.decode_path)
@@ -833,6 +900,7 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
     if (a.stream_path)
         return a.fmt == 2 ? launch_stream_experts<2>(a, seg, s, ev)
                           : a.fmt == 1 ? launch_stream_experts<1>(a, seg, s, ev) : launch_stream_experts<0>(a, seg, s, ev);
+    if (a.mx_path) return launch_experts_mx(a, seg, s, ev);
     // the tile path takes bf16 records: a 4-bit layer's are decoded first into a.deq
     const uint16_t* ex = static_cast<const uint16_t*>(a.experts);
     size_t rec = a.rec_bytes / 2;

@@ -168,6 +168,16 @@ struct ExpertArgs {
     uint16_t* deq = nullptr;
     float* deq_ts = nullptr;
     const int32_t* offsets = nullptr;
+    // MXFP4 records on the block-scaled MFMA path (large batches): z as MXFP8 [T][zp] values and
+    // [T][zp / 32] scales plus its MXFP4 residual [T][zp / 2] and [T][zp / 32], the routed rows of
+    // H as MXFP8 [T k][F] and [T k][F / 32]
+    bool mx_path = false;
+    uint8_t* z8 = nullptr;
+    uint8_t* z8s = nullptr;
+    uint8_t* z4 = nullptr;
+    uint8_t* z4s = nullptr;
+    uint8_t* h8 = nullptr;
+    uint8_t* h8s = nullptr;
 };
 
 // Large 4-bit batches: minimum T at which the records of the experts with tokens are decoded to

@@ -42,6 +42,11 @@ struct SegSpace {
     // Expert groups with their own D: z is [T][zp] with group g's latent in columns g*L ..;
     // expert seg is in group seg / Eg, the shared expert in group 0 (one group: Eg = E, zp = L).
     int32_t Eg, zp;
+    // which tiles of the list a launch takes: 0 all, 1 the routed ones, 2 the shared segment's
+    // (the last nsh entries of the list)
+    int32_t part = 0, nsh = 0;
+    __device__ __forceinline__ int count() const { return part == 0 ? *ntiles : part == 1 ? *ntiles - nsh : nsh; }
+    __device__ __forceinline__ Tile at(int i) const { return tiles[part == 2 ? *ntiles - nsh + i : i]; }
     // a dropped slot (perm = -1) maps to token 0: its rows are computed but never stored
     __device__ __forceinline__ int token_of(int seg, int p) const { return seg == E ? p - T * k : max(perm[p], 0) / k; }
     __device__ __forceinline__ int dest_of(int seg, int p) const { return seg == E ? p : perm[p]; }
@@ -197,8 +202,8 @@ struct TileUp {
     typedef const uint16_t* RowA;
     typedef const uint16_t* RowB;
     __device__ bool tile(int bx, int by, Ctx& c) const {
-        if (bx >= *seg.ntiles) return false;
-        const Tile t = seg.tiles[bx];
+        if (bx >= seg.count()) return false;
+        const Tile t = seg.at(bx);
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
@@ -265,8 +270,8 @@ struct TileDown {
     typedef const uint16_t* RowA;
     typedef const uint16_t* RowB;
     __device__ bool tile(int bx, int by, Ctx& c) const {
-        if (bx >= *seg.ntiles) return false;
-        const Tile t = seg.tiles[bx];
+        if (bx >= seg.count()) return false;
+        const Tile t = seg.at(bx);
         c.seg = t.seg;
         c.row0 = t.row0;
         c.nrows = t.nrows;
@@ -721,7 +726,7 @@ template <class S>
 struct PipeUp : TileUp<S> {
     using B = TileUp<S>;
     static constexpr bool kAPacked = false, kBPacked = true;
-    __device__ int m_tiles() const { return *B::seg.ntiles; }
+    __device__ int m_tiles() const { return B::seg.count(); }
     __device__ int k_stages(const typename B::Ctx&) const { return B::L / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx&) const { return reinterpret_cast<const uint8_t*>(B::z16); }
     __device__ const uint8_t* b_base(const typename B::Ctx& c) const { return reinterpret_cast<const uint8_t*>(c.g); }
@@ -753,7 +758,7 @@ template <class S>
 struct PipeDown : TileDown<S> {
     using B = TileDown<S>;
     static constexpr bool kAPacked = false, kBPacked = true;
-    __device__ int m_tiles() const { return *B::seg.ntiles; }
+    __device__ int m_tiles() const { return B::seg.count(); }
     __device__ int k_stages(const typename B::Ctx& c) const { return c.F / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
         return reinterpret_cast<const uint8_t*>(B::H + (size_t)c.row0 * B::Hs);

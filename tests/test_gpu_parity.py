@@ -196,6 +196,25 @@ def test_small_mxfp4(T, ws):
     check_block(lw, x, "bf16", out, label=f"small_mxfp4 T={T}")
 
 
+SMALL_MX_NOSH = gen.Shape(hidden=256, latent=384, n_experts=24, top_k=3, ffn=256, shared_ffn=0)
+
+
+@pytest.mark.parametrize("path", ["mx_mfma", "decode_bf16"])
+@pytest.mark.parametrize("shape,T", [("mx", 384), ("mx", 700), ("mx_nosh", 512), ("mx_nosh", 1500),
+                                     ("groups", 400), ("groups", 900)])
+def test_large_mxfp4_paths(path, shape, T, ws, monkeypatch):
+    """Both large-batch MXFP4 paths: the block-scaled MFMA kernels (MXFP8 activations) and the
+    decode of the records to bf16; with and without a shared expert, and with expert groups."""
+    monkeypatch.setenv("LMOE_MX_MFMA", "1" if path == "mx_mfma" else "0")
+    sh = {"mx": SMALL_MX, "mx_nosh": SMALL_MX_NOSH, "groups": SMALL_G_MX}[shape]
+    wl, lw = small_layer(sh, "bf16", "bf16", "mxfp4")
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl, T=T, salt=T + 7)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"large_mxfp4 {path} {shape} T={T}")
+
+
 @pytest.mark.parametrize("T", [3, 16, 40, 100, 383, 400, 1100])
 def test_small_nvfp4(T, ws):
     wl, lw = small_layer(SMALL_MX, "bf16", "bf16", "nvfp4")
