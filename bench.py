@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "latent-MoE layer tok/s: decode T=8 (%HBM BW), 16K prefill (%MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 (the block-scaled MXFP8 x MXFP4 products run at the fp8 rate)
+MX_MIN_T = 384  # batches from which MXFP4 experts take the large-batch kernels (kDequantMinT in the library)
 STAGE_UP = 5
 
 
@@ -299,10 +301,20 @@ def roofline_hbm(counts, up_ms, traffic=None):
             "bytes_per_launch": counts["up_bytes"], "avg_launch_us": round(up_ms * 1e3, 2)}
 
 
-def roofline_mfma(counts, up_ms):
+def mx_mfma_path(wl):
+    """Whether the workload's expert products take the block-scaled MXFP8 x MXFP4 MFMA kernels."""
+    return wl.expert == "mxfp4" and wl.T >= MX_MIN_T and os.environ.get("LMOE_MX_MFMA", "1")[:1] != "0"
+
+
+def roofline_mfma(counts, up_ms, wl=None):
     achieved = counts["up_flops"] / (up_ms / 1e3) / 1e12
-    return {"bound": "mfma", "kernel": "expert gate/up (pipe_gemm_persistent PipeUp)", "achieved": round(achieved, 1),
-            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+    if wl is not None and mx_mfma_path(wl):
+        kernel, peak = ("expert gate/up (mx_gemm_persistent MxUp, MXFP8 z + MXFP4 residual x MXFP4 records; "
+                        "with the z quantization and the bf16 shared expert)"), MFMA_FP8_PEAK_TFLOPS
+    else:
+        kernel, peak = "expert gate/up (pipe_gemm_persistent PipeUp)", MFMA_BF16_PEAK_TFLOPS
+    return {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1),
+            "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
             "traffic": None, "flops_per_launch": counts["up_flops"], "avg_launch_us": round(up_ms * 1e3, 2)}
 
 
@@ -341,7 +353,7 @@ def main():
         m = measure(wl, args.steps, args.warmup, args.rotate, copies=copies)
     c = m["counts"]
     mfma_bound = c["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > c["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
-    rl = roofline_mfma(c, m["up_ms"]) if mfma_bound else roofline_hbm(c, m["up_ms"], measured_traffic(wl.name))
+    rl = roofline_mfma(c, m["up_ms"], wl) if mfma_bound else roofline_hbm(c, m["up_ms"], measured_traffic(wl.name))
     layer_s = m["ms_per_step"] / 1e3
     out = {
         "metric": METRIC,
@@ -354,7 +366,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8 x mxfp4" if mx_mfma_path(wl) else "bf16",
         "data": "synthetic (seeded N(0,1/fan_in) weights, N(0,1) tokens, Zipf(1.1) router bias)",
         "config": {"workload": wl.name, "T": wl.T, "hidden": wl.shape.hidden, "latent": wl.shape.latent,
                    "n_experts": wl.shape.n_experts, "top_k": wl.shape.top_k, "ffn": wl.shape.ffn,

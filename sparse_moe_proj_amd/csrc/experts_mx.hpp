@@ -253,13 +253,18 @@ __device__ __forceinline__ void mx_k_loop(const MxCopies<S>& c, int nk, f32x16 (
                 for (int i = 0; i < 2; ++i) la[i] = AO + 16 * ((arow[i] >> 4) * 64 + (2 * s + g) * 16 + (arow[i] & 15));
                 uint4 lf[2];
                 mx_read_frags_lo(aa, ba, la, af, bfv, lf);
+                // the four products of z's MXFP8 part, then the four of its residual, so that no
+                // MFMA waits for the one before it
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
+                    for (int j = 0; j < 2; ++j)
                         acc[i][j] = mfma_mx<2 * s>(af[i][0], af[i][1], bfv[j], sa[i], sb[j][s], acc[i][j]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
                         acc[i][j] = mfma_mx44<2 * s>(lf[i], bfv[j], sl[i], sb[j][s], acc[i][j]);
-                    }
             } else {
                 mx_read_frags(aa, ba, af, bfv);
 #pragma unroll
@@ -391,16 +396,24 @@ __device__ __forceinline__ uint32_t mx4_scale_bits(float amax) {
 
 // z (bf16 [rows][K], K % 32 == 0, rows contiguous) -> MXFP8: E4M3 [rows][K] and E8M0 [rows][K / 32];
 // with q4 (two-term form), also the residual z - MXFP8(z) (exact in fp32) as MXFP4: E2M1
-// [rows][K / 2] (low nibble = even K) and E8M0 [rows][K / 32].  One thread per block of 32 values.
+// [rows][K / 2] (low nibble = even K) and E8M0 [rows][K / 32].  One thread per block of 32 values;
+// a workgroup's 256 blocks (16 KB) are read with coalesced loads into LDS first (the 16-byte
+// chunks of block t at 4 t + (c ^ (t & 3)), so the per-thread reads are free of bank conflicts).
 __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* __restrict__ src, size_t nblocks,
                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ qs,
                                                        uint8_t* __restrict__ q4, uint8_t* __restrict__ q4s) {
-    const size_t b = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (b >= nblocks) return;
-    const uint4* in = reinterpret_cast<const uint4*>(src + b * 32);
+    __shared__ uint4 sm[1024];
+    const size_t b0 = (size_t)blockIdx.x * 256;
+    const int nb = (int)min((size_t)256, nblocks - b0);
+    const uint4* in = reinterpret_cast<const uint4*>(src + b0 * 32);
+    for (int j = threadIdx.x; j < nb * 4; j += 256) sm[(j & ~3) | ((j & 3) ^ ((j >> 2) & 3))] = in[j];
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t >= nb) return;
+    const size_t b = b0 + t;
     uint4 w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = in[i];
+    for (int i = 0; i < 4; ++i) w[i] = sm[4 * t + (i ^ (t & 3))];
     float v[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -829,11 +829,14 @@ hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
 // Large MXFP4 batches on the block-scaled MFMA: z to MXFP8 plus an MXFP4 residual, then the routed
 // gate/up (H to MXFP8 in its epilogue) and down products from the stored records; the shared expert's (bf16)
 // segment takes the bf16 kernels.
-#ifndef LMOE_MX_NS
-#define LMOE_MX_NS 3
+#ifndef LMOE_MX_NS_UP
+#define LMOE_MX_NS_UP 2
 #endif
-using MxUpL = MxShape<128, 256, LMOE_MX_NS, 2, 4, true>;
-using MxDnL = MxShape<128, 256, LMOE_MX_NS, 2, 4, false>;
+#ifndef LMOE_MX_NS_DN
+#define LMOE_MX_NS_DN 3
+#endif
+using MxUpL = MxShape<128, 256, LMOE_MX_NS_UP, 2, 4, true>;
+using MxDnL = MxShape<128, 256, LMOE_MX_NS_DN, 2, 4, false>;
 static_assert(MxUpL::kBM == PipeL::kBM && MxDnL::kBM == PipeL::kBM, "the work list's tile rows");
 
 hipError_t launch_experts_mx(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
