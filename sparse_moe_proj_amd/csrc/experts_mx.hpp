@@ -19,8 +19,8 @@
 //   A: BM rows x 128 bytes (row-major, 16-byte chunks swizzled by (row >> 1) & 7);
 //   B: BN / 16 packed 1 KB tiles (16 rows x 128 values: unit (row j, 32-value block q) at 16 q + j);
 //   the A scales (4 bytes per row) and the B scale tiles (64 bytes per 16-row block, one byte per
-//   unit in the same order), each wave copying one 256-byte dword block of them, so every wave
-//   issues the same number of copies per stage;
+//   unit in the same order), each of the first kSW waves copying one 256-byte dword block of
+//   them (the waits of the other waves count one copy fewer per stage);
 //   with LO (gate/up), a second A operand: the residual of each z row after its MXFP8 rounding,
 //   as MXFP4 (BM rows x 64 bytes, copied into packed-tile order like B) and its scales, so that
 //   z = hi + lo carries about 6 significant bits instead of 4 (see quant_mx_kernel).
@@ -47,7 +47,8 @@ struct MxShape {
     static_assert(kSAW + kSBW + (LO ? kSAW : 0) <= kWaves, "one scale copy per wave");
     static constexpr int kLI = LO ? BM / 16 : 0, kLIW = kLI / kWaves;  // residual copies (1 KB: 16 rows)
     static_assert(!LO || kLI % kWaves == 0, "residual copies split over the waves");
-    static constexpr int kLoadsPerStage = kAIW + kBIW + 1 + kLIW;
+    static constexpr int kSW = kSAW + kSBW + (LO ? kSAW : 0);  // waves that copy scales
+    static constexpr int kLoadsPerStage = kAIW + kBIW + 1 + kLIW;  // of such a wave (the others: one fewer)
     // 16-byte units of a stage: A, B, one 256-byte scale block per wave, the residual operand
     static constexpr int kAU = BM * 8, kBU = BN * 4, kSU = kWaves * 16, kLU = LO ? BM * 4 : 0;
     static constexpr int kStageUnits = kAU + kBU + kSU + kLU;
@@ -101,7 +102,7 @@ __device__ __forceinline__ void mx_issue(const MxCopies<S>& c, uint4* buf, int k
 #pragma unroll
     for (int i = 0; i < S::kBIW; ++i)
         lds_copy16(c.bbase + (c.bs[i] + (uint32_t)(kt * kMxBStep)), buf + S::kAU + (wave * S::kBIW + i) * 64);
-    lds_copy4(c.sbase + (c.ss + (uint32_t)(kt * c.sstep)), buf + S::kAU + S::kBU + wave * 16);
+    if (wave < S::kSW) lds_copy4(c.sbase + (c.ss + (uint32_t)(kt * c.sstep)), buf + S::kAU + S::kBU + wave * 16);
     if constexpr (S::kLo) {
 #pragma unroll
         for (int i = 0; i < S::kLIW; ++i)
@@ -276,9 +277,13 @@ __device__ __forceinline__ void mx_k_loop(const MxCopies<S>& c, int nk, f32x16 (
         });
     };
 
+    const bool scale_wave = wave < S::kSW;
 #define LMOE_MX_STEP(S_, CUR_, NEXT_)                                            \
     if (kt + S_ < nk) {                                                          \
-        wait_stage<LPS, NS>(min(nk - 1 - (kt + S_), NS - 2));                    \
+        if (scale_wave)                                                          \
+            wait_stage<LPS, NS>(min(nk - 1 - (kt + S_), NS - 2));                \
+        else                                                                     \
+            wait_stage<LPS - 1, NS>(min(nk - 1 - (kt + S_), NS - 2));            \
         stage_barrier();                                                         \
         if (kt + S_ + NS - 1 < nk) mx_issue<S>(c, NEXT_, kt + S_ + NS - 1, wave); \
         compute(CUR_);                                                           \
@@ -397,8 +402,9 @@ __device__ __forceinline__ uint32_t mx4_scale_bits(float amax) {
 // z (bf16 [rows][K], K % 32 == 0, rows contiguous) -> MXFP8: E4M3 [rows][K] and E8M0 [rows][K / 32];
 // with q4 (two-term form), also the residual z - MXFP8(z) (exact in fp32) as MXFP4: E2M1
 // [rows][K / 2] (low nibble = even K) and E8M0 [rows][K / 32].  One thread per block of 32 values;
-// a workgroup's 256 blocks (16 KB) are read with coalesced loads into LDS first (the 16-byte
-// chunks of block t at 4 t + (c ^ (t & 3)), so the per-thread reads are free of bank conflicts).
+// a workgroup's 256 blocks (16 KB) are read with coalesced loads into LDS first, chunk c of block t
+// at 4 t + ((c + t / 4) & 3): the 16 lanes of one 16-byte read then hit 16 different 16-byte bank
+// groups, so the per-thread reads are free of bank conflicts.
 __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* __restrict__ src, size_t nblocks,
                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ qs,
                                                        uint8_t* __restrict__ q4, uint8_t* __restrict__ q4s) {
@@ -406,14 +412,14 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* __restric
     const size_t b0 = (size_t)blockIdx.x * 256;
     const int nb = (int)min((size_t)256, nblocks - b0);
     const uint4* in = reinterpret_cast<const uint4*>(src + b0 * 32);
-    for (int j = threadIdx.x; j < nb * 4; j += 256) sm[(j & ~3) | ((j & 3) ^ ((j >> 2) & 3))] = in[j];
+    for (int j = threadIdx.x; j < nb * 4; j += 256) sm[(j & ~3) | (((j & 3) + (j >> 4)) & 3)] = in[j];
     __syncthreads();
     const int t = threadIdx.x;
     if (t >= nb) return;
     const size_t b = b0 + t;
     uint4 w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = sm[4 * t + (i ^ (t & 3))];
+    for (int i = 0; i < 4; ++i) w[i] = sm[4 * t + ((i + (t >> 2)) & 3)];
     float v[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -617,7 +623,7 @@ struct MxDown {
             off = (uint32_t)((size_t)3 * F * L / 2 + (size_t)2 * F * L / 32 + (size_t)b_nb(c, d >> 4) * (F / 2)) +
                   (d & 15) * 4;
             step = kMxSBStep;
-        } else {
+        } else {  // A scales of rows 64 w + lane (waves past the B scales copy none; any valid source)
             const int w = wave < S::kSAW ? wave : 0;
             base = h8s;
             off = (uint32_t)(c.row0 + min(w * 64 + lane, c.nrows - 1)) * (F / 32);
