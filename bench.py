@@ -30,7 +30,7 @@ METRIC = "latent-MoE layer tok/s: decode T=8 (%HBM BW), 16K prefill (%MFMA peak)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 (the block-scaled MXFP8 x MXFP4 products run at the fp8 rate)
-MX_MIN_T = 384  # batches from which MXFP4 experts take the large-batch kernels (kDequantMinT in the library)
+MX_MIN_T = 96  # batches from which MXFP4 experts take the block-scaled MFMA kernels (kMxMinT in the library)
 STAGE_UP = 5
 
 
@@ -303,7 +303,8 @@ def roofline_hbm(counts, up_ms, traffic=None):
 
 def mx_mfma_path(wl):
     """Whether the workload's expert products take the block-scaled MXFP8 x MXFP4 MFMA kernels."""
-    return wl.expert == "mxfp4" and wl.T >= MX_MIN_T and os.environ.get("LMOE_MX_MFMA", "1")[:1] != "0"
+    min_t = int(os.environ.get("LMOE_MX_MIN_T", "0") or 0) or MX_MIN_T
+    return wl.expert == "mxfp4" and wl.T >= max(min_t, 17) and os.environ.get("LMOE_MX_MFMA", "1")[:1] != "0"
 
 
 def roofline_mfma(counts, up_ms, wl=None):

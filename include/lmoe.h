@@ -171,13 +171,15 @@ typedef struct {
  * Returns 0 for an invalid configuration. */
 size_t lmoe_expert_record_bytes(const lmoe_config* cfg, int32_t shared);
 
-/* Workspace bytes lmoe_forward needs for T tokens (monotone in T).  With 4-bit routed experts
- * and T >= 384: MXFP4 layers take the block-scaled MFMA kernels (CDNA4 v_mfma_scale_*_f8f6f4,
- * the records used as stored) and the workspace holds z as MXFP8 plus an MXFP4 residual and H as
- * MXFP8 (about T * (1.56 * latent * groups + 1.03 * top_k * ffn) bytes more); NVFP4 layers, and
- * MXFP4 layers when the environment variable LMOE_MX_MFMA is "0" (read by this query and by
- * lmoe_forward: keep it unchanged between them), decode the records of the experts with tokens
- * to bf16 and the workspace includes n_experts such records (3 * ffn * latent * 2 bytes each). */
+/* Workspace bytes lmoe_forward needs for T tokens (monotone in T).  MXFP4 layers take the
+ * block-scaled MFMA kernels (CDNA4 v_mfma_scale_*_f8f6f4, the records used as stored) from
+ * T = 96 (65 <= T < 96: the weight-streaming kernels); the workspace then holds z as MXFP8 plus an
+ * MXFP4 residual and H as MXFP8 (about T * (1.56 * latent * groups + 1.03 * top_k * ffn) bytes
+ * more).  NVFP4 layers with T >= 384, and MXFP4 layers with T >= 384 when the environment
+ * variable LMOE_MX_MFMA is "0", decode the records of the experts with tokens to bf16 and the
+ * workspace includes n_experts such records (3 * ffn * latent * 2 bytes each).  LMOE_MX_MFMA and
+ * LMOE_MX_MIN_T (the MXFP4 threshold, for measurements) are read by this query and by
+ * lmoe_forward: keep them unchanged between the two. */
 lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes);
 
 /* Workspace bytes lmoe_permute needs for T tokens. */

@@ -99,6 +99,14 @@ bool mx_mfma_enabled() {
     return !(v && v[0] == '0');
 }
 
+// Smallest batch for the block-scaled MFMA path of MXFP4 layers (LMOE_MX_MIN_T overrides it,
+// for measurements; never below kStreamMaxT + 1).
+int mx_min_t() {
+    const char* v = getenv("LMOE_MX_MIN_T");
+    const int t = v ? atoi(v) : kMxMinT;
+    return std::max(t > 0 ? t : kMxMinT, kStreamMaxT + 1);
+}
+
 Layout plan(const Dims& d, int T) {
     Layout lo{};
     const size_t act = d.f32 ? 4 : 2;
@@ -106,10 +114,11 @@ Layout plan(const Dims& d, int T) {
     lo.decode_path = !d.f32 && decode_fits(T, d.L, d.F, d.Fs);
     // 4-bit records stream through the weight-streaming kernels up to kDequantMinT tokens; larger
     // batches decode the touched records to bf16 once and take the tile GEMMs
-    const bool big4 = d.mx && !lo.decode_path && T >= kDequantMinT;
-    // MXFP4 takes the block-scaled MFMA kernels unless LMOE_MX_MFMA=0 asks for the decode to bf16
-    lo.mx_path = big4 && d.fmt == 1 && mx_mfma_enabled();
-    const bool deq = big4 && !lo.mx_path;
+    // MXFP4 takes the block-scaled MFMA kernels from mx_min_t() tokens unless LMOE_MX_MFMA=0 asks
+    // for the decode to bf16 (from kDequantMinT, as NVFP4)
+    lo.mx_path = d.fmt == 1 && !lo.decode_path && mx_mfma_enabled() && T >= mx_min_t();
+    const bool deq = d.mx && !lo.decode_path && !lo.mx_path && T >= kDequantMinT;
+    const bool big4 = lo.mx_path || deq;
     lo.deq_path = deq;
     lo.stream_path = !d.f32 && (T <= kStreamMaxT || (d.mx && !big4) || lo.decode_path);
     lo.fused_router = !d.f32 && small_proj_fits(T, d.H);

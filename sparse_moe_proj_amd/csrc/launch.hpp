@@ -188,6 +188,13 @@ struct ExpertArgs {
 #define LMOE_DEQUANT_MIN_T 384
 #endif
 constexpr int kDequantMinT = LMOE_DEQUANT_MIN_T;
+// MXFP4 layers: minimum T of the block-scaled MFMA path (no record decode, so it pays off earlier).
+// Measured at the 145B shape (us per layer, weight-streaming kernels vs this path): T = 96 362 vs
+// 338, 128 423 vs 352, 192 497 vs 424, 256 580 vs 442, 320 630 vs 456.
+#ifndef LMOE_MX_MIN_T
+#define LMOE_MX_MIN_T 96
+#endif
+constexpr int kMxMinT = LMOE_MX_MIN_T;
 hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& ev);
 
 // Row-major expert records -> packed records (nrec records of rec_bytes; F x L gate/up, L x F down;

@@ -200,11 +200,14 @@ SMALL_MX_NOSH = gen.Shape(hidden=256, latent=384, n_experts=24, top_k=3, ffn=256
 
 
 @pytest.mark.parametrize("path", ["mx_mfma", "decode_bf16"])
-@pytest.mark.parametrize("shape,T", [("mx", 384), ("mx", 700), ("mx_nosh", 512), ("mx_nosh", 1500),
-                                     ("groups", 400), ("groups", 900)])
+@pytest.mark.parametrize("shape,T", [("mx", 96), ("mx", 300), ("mx", 384), ("mx", 700), ("mx_nosh", 200),
+                                     ("mx_nosh", 512), ("mx_nosh", 1500), ("groups", 150), ("groups", 400),
+                                     ("groups", 900)])
 def test_large_mxfp4_paths(path, shape, T, ws, monkeypatch):
-    """Both large-batch MXFP4 paths: the block-scaled MFMA kernels (MXFP8 activations) and the
-    decode of the records to bf16; with and without a shared expert, and with expert groups."""
+    """MXFP4 batches past the small-batch kernels: the block-scaled MFMA kernels (MXFP8
+    activations, from 96 tokens) and, with them switched off (LMOE_MX_MFMA=0), the weight-streaming
+    kernels below 384 tokens and the decode of the records to bf16 from 384; with and without a
+    shared expert, and with expert groups."""
     monkeypatch.setenv("LMOE_MX_MFMA", "1" if path == "mx_mfma" else "0")
     sh = {"mx": SMALL_MX, "mx_nosh": SMALL_MX_NOSH, "groups": SMALL_G_MX}[shape]
     wl, lw = small_layer(sh, "bf16", "bf16", "mxfp4")
