@@ -18,9 +18,9 @@
 // deep, one barrier per stage, persistent workgroups.  A stage holds
 //   A: BM rows x 128 bytes (row-major, 16-byte chunks swizzled by (row >> 1) & 7);
 //   B: BN / 16 packed 1 KB tiles (16 rows x 128 values: unit (row j, 32-value block q) at 16 q + j);
-//   the A scales (4 bytes per row) and the B scale tiles (64 bytes per 16-row block, one byte per
-//   unit in the same order), each of the first kSW waves copying one 256-byte dword block of
-//   them (the waits of the other waves count one copy fewer per stage);
+//   the A scales (4 bytes per row, dword copies by BM / 64 waves) and the B scale tiles (64 bytes
+//   per 16-row block, one byte per unit in the same order; one 16-byte-per-lane copy by one wave);
+//   the waits of the waves that copy no scales count one copy fewer per stage;
 //   with LO (gate/up), a second A operand: the residual of each z row after its MXFP8 rounding,
 //   as MXFP4 (BM rows x 64 bytes, copied into packed-tile order like B) and its scales, so that
 //   z = hi + lo carries about 6 significant bits instead of 4 (see quant_mx_kernel).
@@ -43,11 +43,12 @@ struct MxShape {
     static constexpr int kAI = BM / 8, kBI = BN / 16;  // 1 KB copies per stage
     static constexpr int kAIW = kAI / kWaves, kBIW = kBI / kWaves;
     static_assert(kAI % kWaves == 0 && kBI % kWaves == 0, "copies split over the waves");
-    static constexpr int kSAW = BM / 64, kSBW = BN / 64;  // waves copying A scales, B scales
-    static_assert(kSAW + kSBW + (LO ? kSAW : 0) <= kWaves, "one scale copy per wave");
+    static constexpr int kSAW = BM / 64;  // waves copying A scales (then one wave the B scales)
+    static_assert(BN == 256, "the B scale tiles of a stage are one 1 KB copy");
+    static_assert(kSAW + 1 + (LO ? kSAW : 0) <= kWaves, "one scale copy per wave");
     static constexpr int kLI = LO ? BM / 16 : 0, kLIW = kLI / kWaves;  // residual copies (1 KB: 16 rows)
     static_assert(!LO || kLI % kWaves == 0, "residual copies split over the waves");
-    static constexpr int kSW = kSAW + kSBW + (LO ? kSAW : 0);  // waves that copy scales
+    static constexpr int kSW = kSAW + 1 + (LO ? kSAW : 0);  // waves that copy scales
     static constexpr int kLoadsPerStage = kAIW + kBIW + 1 + kLIW;  // of such a wave (the others: one fewer)
     // 16-byte units of a stage: A, B, one 256-byte scale block per wave, the residual operand
     static constexpr int kAU = BM * 8, kBU = BN * 4, kSU = kWaves * 16, kLU = LO ? BM * 4 : 0;
@@ -71,7 +72,7 @@ struct MxCopies {
     const uint8_t* sbase;  // this wave's scale source
     const uint8_t* lbase;  // residual operand (LO)
     uint32_t as[S::kAIW], bs[S::kBIW], ls[S::kLIW > 0 ? S::kLIW : 1], ss;
-    int sstep;
+    int sstep, sdst;  // scale source step per stage; destination (16-byte units past A and B)
 };
 
 // Copy sources: P gives a_base/b_base, src_a/src_b as for the bf16 kernel (A rows of 128 bytes,
@@ -86,6 +87,8 @@ __device__ __forceinline__ MxCopies<S> mx_copies(const P& p, const typename P::C
 #pragma unroll
     for (int i = 0; i < S::kBIW; ++i) c.bs[i] = p.src_b(ctx, wave * S::kBIW + i, lane);
     p.scale_src(ctx, wave, lane, c.sbase, c.ss, c.sstep);
+    // A scales (rows 64 w ..), the B scale tiles, then the residual's scales (rows 64 (w - kSAW - 1) ..)
+    c.sdst = wave <= S::kSAW ? wave * 16 : S::kSAW * 16 + S::kBN / 4 + (wave - S::kSAW - 1) * 16;
     if constexpr (S::kLo) {
         c.lbase = p.lo_base(ctx);
 #pragma unroll
@@ -102,7 +105,13 @@ __device__ __forceinline__ void mx_issue(const MxCopies<S>& c, uint4* buf, int k
 #pragma unroll
     for (int i = 0; i < S::kBIW; ++i)
         lds_copy16(c.bbase + (c.bs[i] + (uint32_t)(kt * kMxBStep)), buf + S::kAU + (wave * S::kBIW + i) * 64);
-    if (wave < S::kSW) lds_copy4(c.sbase + (c.ss + (uint32_t)(kt * c.sstep)), buf + S::kAU + S::kBU + wave * 16);
+    if (wave < S::kSW) {
+        const uint8_t* g = c.sbase + (c.ss + (uint32_t)(kt * c.sstep));
+        if (wave == S::kSAW)
+            lds_copy16(g, buf + S::kAU + S::kBU + c.sdst);
+        else
+            lds_copy4(g, buf + S::kAU + S::kBU + c.sdst);
+    }
     if constexpr (S::kLo) {
 #pragma unroll
         for (int i = 0; i < S::kLIW; ++i)
@@ -531,15 +540,14 @@ struct MxUp {
         return (uint32_t)((size_t)mat * F * L / 2 + (size_t)nb * 8 * L) + lane * 16;
     }
     __device__ void scale_src(const Ctx& c, int wave, int lane, const uint8_t*& base, uint32_t& off, int& step) const {
-        if (wave >= S::kSAW && wave < S::kSAW + S::kSBW) {
-            const int d = (wave - S::kSAW) * 64 + lane;  // dword d of the stage's B scale tiles
+        if (wave == S::kSAW) {  // lane l: 16 bytes (units of block l % 4) of B-tile block l / 4's scales
             int mat, nb;
-            b_block(c, d >> 4, mat, nb);
+            b_block(c, lane >> 2, mat, nb);
             base = c.r;
-            off = (uint32_t)((size_t)3 * F * L / 2 + (size_t)mat * F * L / 32 + (size_t)nb * (L / 2)) + (d & 15) * 4;
+            off = (uint32_t)((size_t)3 * F * L / 2 + (size_t)mat * F * L / 32 + (size_t)nb * (L / 2)) + (lane & 3) * 16;
             step = kMxSBStep;
-        } else if (wave >= S::kSAW + S::kSBW) {  // residual scales of rows 64 w + lane
-            const int w = wave - S::kSAW - S::kSBW;
+        } else if (wave > S::kSAW) {  // residual scales of rows 64 w + lane
+            const int w = wave - S::kSAW - 1;
             base = z4s;
             off = tok_off(c, w * 64 + lane) / 32;
             step = kMxSAStep;
@@ -617,11 +625,10 @@ struct MxDown {
         return (uint32_t)((size_t)F * L + (size_t)b_nb(c, i) * 8 * F) + lane * 16;
     }
     __device__ void scale_src(const Ctx& c, int wave, int lane, const uint8_t*& base, uint32_t& off, int& step) const {
-        if (wave >= S::kSAW && wave < S::kSAW + S::kSBW) {
-            const int d = (wave - S::kSAW) * 64 + lane;
+        if (wave == S::kSAW) {
             base = c.r;
-            off = (uint32_t)((size_t)3 * F * L / 2 + (size_t)2 * F * L / 32 + (size_t)b_nb(c, d >> 4) * (F / 2)) +
-                  (d & 15) * 4;
+            off = (uint32_t)((size_t)3 * F * L / 2 + (size_t)2 * F * L / 32 + (size_t)b_nb(c, lane >> 2) * (F / 2)) +
+                  (lane & 3) * 16;
             step = kMxSBStep;
         } else {  // A scales of rows 64 w + lane (waves past the B scales copy none; any valid source)
             const int w = wave < S::kSAW ? wave : 0;
