@@ -186,7 +186,7 @@ def test_fold_router_halves():
 SMALL_MX = gen.Shape(hidden=256, latent=256, n_experts=24, top_k=3, ffn=128, shared_ffn=128)
 
 
-@pytest.mark.parametrize("T", [3, 16, 40, 100, 383, 400, 1100])
+@pytest.mark.parametrize("T", [3, 16, 40, 80, 100, 383, 400, 1100])
 def test_small_mxfp4(T, ws):
     wl, lw = small_layer(SMALL_MX, "bf16", "bf16", "mxfp4")
     dl = DeviceLayer(lw, act="bf16")
