@@ -189,51 +189,87 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 // ==============================================================================================
 // combine: m[t] = Y[T*k + t] (shared, weight 1) + sum_s w[t][s] * Y[t*k + s], slots in order
 // ==============================================================================================
-// Y rows bf16 (BF16: bf16 path, bf16 out) or fp32 (fp32 path, fp32 out)
+// 8 consecutive values of Y as they are stored (BF16: bf16 path, bf16 out; else the fp32 path,
+// fp32 out), and as fp32
 template <bool BF16>
-__device__ __forceinline__ float4 load_y4(const void* Y, size_t off) {
+struct Y8 {
+    typename std::conditional<BF16, uint4, float4>::type a, b;
+};
+template <bool BF16>
+__device__ __forceinline__ Y8<BF16> load_y8(const void* Y, size_t off) {
+    Y8<BF16> r;
     if constexpr (BF16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Y) + off);
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                           __uint_as_float(u.y & 0xffff0000u));
+        r.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Y) + off);
     } else {
-        return *reinterpret_cast<const float4*>(static_cast<const float*>(Y) + off);
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(Y) + off);
+        r.a = p[0];
+        r.b = p[1];
+    }
+    return r;
+}
+template <bool BF16>
+__device__ __forceinline__ void y8_f32(const Y8<BF16>& r, float (&v)[8]) {
+    if constexpr (BF16) {
+        const uint32_t u[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(u[i] << 16);
+            v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    } else {
+        v[0] = r.a.x, v[1] = r.a.y, v[2] = r.a.z, v[3] = r.a.w;
+        v[4] = r.b.x, v[5] = r.b.y, v[6] = r.b.z, v[7] = r.b.w;
     }
 }
 
-// grid (L / 1024, min(T, 65535), expert groups), tokens t = blockIdx.y, + gridDim.y, ...: group
+// grid (L / 2048, min(T, 65535), expert groups), tokens t = blockIdx.y, + gridDim.y, ...: group
 // g's merged row m_g goes to columns g * L .. of m [T][groups * L]; a slot counts for group
-// ids / Eg (ids null: one group), the shared expert for group 0.
+// ids / Eg (ids null: one group), the shared expert for group 0.  A thread sums 8 columns: the
+// shared row, then the slots in order (fp32); the rows of up to 8 slots are requested before
+// any of them is added, so their loads are in flight together.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const float* __restrict__ w, int T,
                                                       int k, int L, int has_shared, void* __restrict__ m,
                                                       const int32_t* __restrict__ ids, int Eg) {
+    constexpr int CH = 8;
     const int g = blockIdx.z;
-    const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
     if (c >= L) return;
     const size_t mp = (size_t)gridDim.z * L;
     for (int t = blockIdx.y; t < T; t += gridDim.y) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (has_shared && g == 0) acc = load_y4<OUT_BF16>(Y, ((size_t)T * k + t) * L + c);
-        for (int s = 0; s < k; ++s) {
-            if (ids && ids[(size_t)t * k + s] / Eg != g) continue;
-            const float ws = w[(size_t)t * k + s];
-            const float4 y = load_y4<OUT_BF16>(Y, ((size_t)t * k + s) * L + c);
-            acc.x += ws * y.x;
-            acc.y += ws * y.y;
-            acc.z += ws * y.z;
-            acc.w += ws * y.w;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (has_shared && g == 0) y8_f32<OUT_BF16>(load_y8<OUT_BF16>(Y, ((size_t)T * k + t) * L + c), acc);
+        for (int s0 = 0; s0 < k; s0 += CH) {
+            Y8<OUT_BF16> raw[CH];
+            float ws[CH];
+            bool use[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int s = s0 + i;
+                use[i] = s < k && (!ids || ids[(size_t)t * k + s] / Eg == g);
+                ws[i] = use[i] ? w[(size_t)t * k + s] : 0.f;
+                if (use[i]) raw[i] = load_y8<OUT_BF16>(Y, ((size_t)t * k + s) * L + c);
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                if (!use[i]) continue;
+                float y[8];
+                y8_f32<OUT_BF16>(raw[i], y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += ws[i] * y[e];
+            }
         }
         if (OUT_BF16) {
-            uint2 o = make_uint2(pack_bf2(acc.x, acc.y), pack_bf2(acc.z, acc.w));
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(m) + t * mp + (size_t)g * L + c) = o;
+            const uint4 o = make_uint4(pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]), pack_bf2(acc[4], acc[5]),
+                                       pack_bf2(acc[6], acc[7]));
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(m) + t * mp + (size_t)g * L + c) = o;
         } else {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(m) + t * mp + (size_t)g * L + c) = acc;
+            float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(m) + t * mp + (size_t)g * L + c);
+            o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
     }
 }
-
-
 
 // ==============================================================================================
 // plain fp32 path (fp32 storage end to end): one thread per output element, sequential K.
@@ -963,7 +999,7 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
 
 hipError_t launch_combine(const void* Y, const float* w, int T, int k, int L, int has_shared, bool out_bf16, void* m,
                           hipStream_t s, const int32_t* ids, int groups, int Eg) {
-    const dim3 grid(cdiv(L / 4, 256), std::min(T, 65535), groups > 1 ? groups : 1);
+    const dim3 grid(cdiv(L / 8, 256), std::min(T, 65535), groups > 1 ? groups : 1);
     const int32_t* gids = groups > 1 ? ids : nullptr;
     if (out_bf16)
         hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, Y, w, T, k, L, has_shared, m, gids, Eg);
