@@ -61,6 +61,28 @@ def test_workspace_sizes_monotone():
     assert lm.lmoe_permute_workspace_bytes(c, 65) > 0
 
 
+@pytest.mark.parametrize("expert", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("mx_mfma", ["1", "0"])
+def test_workspace_monotone_4bit_paths(expert, mx_mfma, monkeypatch):
+    """4-bit layers change kernels at 65 (small-batch -> weight streaming), at 96 (MXFP4: the
+    block-scaled MFMA path, whose MXFP8 activations need workspace) and at 384 (the decode of the
+    records to bf16: n_experts decoded records); the size query stays monotone in T across all."""
+    monkeypatch.setenv("LMOE_MX_MFMA", mx_mfma)
+    c = lm.make_config(2560, 1792, 512, 10, 640, 640, "bf16", "bf16", expert)
+    prev = 0
+    for T in list(range(60, 100)) + [383, 384, 385, 4096, 16384]:
+        n = lm.lmoe_workspace_bytes(c, T)
+        assert n >= prev, (T, prev, n)
+        prev = n
+    decoded = 512 * 3 * 640 * 1792 * 2
+    big = lm.lmoe_workspace_bytes(c, 384) - lm.lmoe_workspace_bytes(c, 383)
+    if expert == "mxfp4" and mx_mfma == "1":
+        assert big < decoded  # no decoded records on the block-scaled MFMA path
+        assert lm.lmoe_workspace_bytes(c, 96) > lm.lmoe_workspace_bytes(c, 95)  # MXFP8 activations from 96
+    else:
+        assert big >= decoded
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(hidden=100), lm.LMOE_ERR_SHAPE),
     (dict(latent=0), lm.LMOE_ERR_SHAPE),
