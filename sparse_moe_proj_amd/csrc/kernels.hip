@@ -1,5 +1,6 @@
 // Kernels of the latent-MoE block other than the MFMA GEMM templates, and the host-side
 // launch wrappers for everything (no allocation, no synchronisation: enqueue only).
+#include <hip/hip_ext.h>
 #include <limits.h>
 
 #include "decode_experts.hpp"
@@ -740,7 +741,8 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
                        a.L,     a.F,   a.Fs,   a.Hs,      nblocks,     a.H,
                        a.w,     a.mpart, kDcGroups, a.rowinfo, a.max_tiles};
     const long items = (long)a.max_tiles * nblocks;
-    ev.begin(kStageUp);
+    // the gate/up stage's events are taken by the launch itself (kernel time only)
+    hipEvent_t e0 = ev.start(kStageUp), e1 = ev.stop(kStageUp);
     // The K-split form when every wave's run of weight groups fits its registers and there are at
     // most as many items as waves on the chip (measured: at T = 1 it keeps all waves busy and
     // saves a fifth of the step; at T >= 8 one item per wave streams as fast or faster).
@@ -753,11 +755,11 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
         const int E = a.E;
 #define LMOE_GU_ROUTED(NV)                                                                                          \
     if (split)                                                                                                      \
-        hipLaunchKernelGGL((decode_gu_split_kernel<kGuWaves, kGuMG, kGuMG4, Q, NV>), dim3((unsigned)grid),         \
-                           dim3(64 * kGuWaves), lds, s, d, r);                                                      \
+        hipExtLaunchKernelGGL((decode_gu_split_kernel<kGuWaves, kGuMG, kGuMG4, Q, NV>), dim3((unsigned)grid),      \
+                              dim3(64 * kGuWaves), (uint32_t)lds, s, e0, e1, 0u, d, r);                             \
     else                                                                                                            \
-        hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, NV>), dim3((unsigned)grid),         \
-                           dim3(64 * kGuWaves), lds, s, d, r)
+        hipExtLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, NV>), dim3((unsigned)grid),      \
+                              dim3(64 * kGuWaves), (uint32_t)lds, s, e0, e1, 0u, d, r)
         if (E <= 64)
             LMOE_GU_ROUTED(1);
         else if (E <= 128)
@@ -770,15 +772,14 @@ hipError_t launch_decode_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
             LMOE_GU_ROUTED(16);
 #undef LMOE_GU_ROUTED
     } else if (split) {
-        hipLaunchKernelGGL((decode_gu_split_kernel<kGuWaves, kGuMG, kGuMG4, Q, 0>), dim3((unsigned)grid),
-                           dim3(64 * kGuWaves), 0, s, d, GuRoute{});
+        hipExtLaunchKernelGGL((decode_gu_split_kernel<kGuWaves, kGuMG, kGuMG4, Q, 0>), dim3((unsigned)grid),
+                              dim3(64 * kGuWaves), 0u, s, e0, e1, 0u, d, GuRoute{});
     } else {
-        hipLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, 0>), dim3((unsigned)grid),
-                           dim3(64 * kGuWaves), 0, s, d, GuRoute{});
+        hipExtLaunchKernelGGL((decode_gu_kernel<kGuWaves, kGuChunk, kGuChunk4, Q, 0>), dim3((unsigned)grid),
+                              dim3(64 * kGuWaves), 0u, s, e0, e1, 0u, d, GuRoute{});
     }
     hipError_t err = last();
     if (err != hipSuccess) return err;
-    ev.end(kStageUp);
     ev.begin(kStageDown);
     const size_t lds =
         (size_t)a.max_tiles * sizeof(Tile) + (size_t)a.T * a.k * sizeof(int2) + (size_t)a.max_tiles * sizeof(int);

@@ -46,6 +46,10 @@ struct StageEvents {
     }
     void begin(int stage) { rec(2 * stage); }
     void end(int stage) { rec(2 * stage + 1); }
+    // the stage's events for a launch that records them itself (hipExtLaunchKernelGGL: the
+    // timestamps bracket the kernel's execution, not the dispatch before it); null when not timing
+    hipEvent_t start(int stage) const { return ev && !capturing ? static_cast<hipEvent_t>(ev[2 * stage]) : nullptr; }
+    hipEvent_t stop(int stage) const { return ev && !capturing ? static_cast<hipEvent_t>(ev[2 * stage + 1]) : nullptr; }
 };
 constexpr int kStageUp = 5, kStageDown = 6, kStageCombine = 7;  // LMOE_STAGE_EXPERT_UP / _DOWN / COMBINE
 
