@@ -61,15 +61,17 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 }
 
 // Maximum over the wave, returned uniform: DPP within each row of 16 lanes (swap neighbours,
-// swap pairs, rotate by 4, rotate by 8), then the four row maxima through scalar reads.
+// swap pairs, rotate by 4, rotate by 8), then the two row broadcasts of wave_incl_scan (lane 15
+// into rows 1 and 3, lane 31 into rows 2 and 3; other rows take max with 0), so lane 63 holds
+// the maximum of all four rows and one scalar read returns it.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
-    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
-    return max(max(r0, r1), max(r2, r3));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast 15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast 31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Sum over the wave in a fixed order (same DPP tree as wave_max_u32), returned uniform.
