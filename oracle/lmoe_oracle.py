@@ -42,16 +42,24 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def round_to_bf16(v: np.ndarray) -> np.ndarray:
-    """float64 -> nearest bf16 value (ties to even), returned as float64.
+# Largest finite bf16 value, (2 - 2^-7) * 2^127 (bf16 keeps float32's 8 exponent bits and 7 of
+# its 23 stored significand bits).
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
 
-    Used only where the method itself rounds to bf16 (the stack's block input).  The value is
-    first rounded to float32 (nearest-even), then to 8 significand bits, nearest-even."""
-    f = np.ascontiguousarray(np.asarray(v, dtype=np.float64).astype(np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """float64 -> the nearest bf16 value (ties to even), returned as float64; one rounding of the
+    exact value, with no float32 step in between.
+
+    Used only where the method itself rounds to bf16 (the stack's block input).  bf16 has 8
+    significant bits, so the spacing of the values around v in [2^(e-1), 2^e) is 2^(e-8); below
+    the smallest normal 2^-126 the spacing stays 2^-133 (subnormals).  Values beyond the largest
+    finite bf16 by half a spacing or more become infinities."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)                                   # |v| in [2^(e-1), 2^e)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))           # spacing of bf16 values there
+    r = np.rint(v / q) * q                               # v / q is exact; rint: ties to even
+    return np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, v), r)
 
 
 # E2M1 magnitudes by 3-bit code (OCP Microscaling Formats v1.0, FP4 E2M1): exponent bias 1,

@@ -6,9 +6,12 @@ cases that reduce to a textbook dense SwiGLU or a standard MoE, and library rout
 for the element formats.  Together they are chosen so that a dropped term, a wrong sign or
 index, or a transposed operand anywhere in the oracle fails at least one of them.
 """
+import bisect
 import json
 import math
 import os
+import struct
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -47,10 +50,12 @@ def py_silu(v):
     return v / (1.0 + math.exp(-v))
 
 
-def brute_forward(lw, x):
+def brute_forward(lw, x, forced=None, details=False):
     """Scalar-loop latent-MoE block in pure Python floats.  With expert groups, expert e is in
     group e // (E / G), which owns D rows and U columns g*L .. g*L + L - 1; the shared expert
-    is in group 0."""
+    is in group 0.  forced maps a token row to the experts it must use instead of its top k (in
+    any order; the weights are then the full softmax renormalised over those experts).  With
+    details, returns (y, ids, w) with each token's experts in ascending id."""
     s = lw.shape
     H, L, E, k, F, G = s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.groups
     Eg = E // G
@@ -75,11 +80,13 @@ def brute_forward(lw, x):
             h.append(py_silu(a) * b)
         return [sum(h[j] * d[r][j] for j in range(f)) for r in range(L)]
 
-    out = []
-    for xt in x.astype(float).tolist():
+    out, all_ids, all_w = [], [], []
+    for t, xt in enumerate(x.astype(float).tolist()):
         zg = [[sum(xt[i] * D[g * L + j][i] for i in range(H)) for j in range(L)] for g in range(G)]
         lam = [sum(zg[e // Eg][i] * Wr[e][i] for i in range(L)) + br[e] for e in range(E)]
         top = sorted(range(E), key=lambda e: (-lam[e], e))[:k]
+        if forced and t in forced:
+            top = [int(e) for e in forced[t]]
         # full softmax over all experts, then renormalise over the kept ones
         mx = max(lam)
         p = [math.exp(v - mx) for v in lam]
@@ -96,6 +103,10 @@ def brute_forward(lw, x):
             wgt = p[e] / norm
             m[g] = [a + wgt * b for a, b in zip(m[g], yo)]
         out.append([sum(m[g][i] * U[r][g * L + i] for g in range(G) for i in range(L)) for r in range(H)])
+        all_ids.append(sorted(top))
+        all_w.append([p[e] / norm for e in sorted(top)])
+    if details:
+        return np.array(out), np.array(all_ids), np.array(all_w)
     return np.array(out)
 
 
@@ -471,6 +482,115 @@ def test_stack_step_with_zero_block_is_identity():
     out = oracle.stack_step(oracle.Layer(lw), h)
     np.testing.assert_array_equal(out["h_next"], h)
     np.testing.assert_array_equal(out["x"], oracle.round_to_bf16(oracle.rmsnorm(h)))
+
+
+def test_forced_ids_match_scalar_brute_force():
+    """block_forward(forced_ids=...) on tokens whose forced sets differ from their top k, given
+    out of order: ids come back ascending, weights are the softmax over the forced experts'
+    logits (the full softmax renormalised over them), the output uses exactly those experts."""
+    s = gen.Shape(hidden=6, latent=5, n_experts=7, top_k=3, ffn=3, shared_ffn=2)
+    lw = make_f32_layer(s, 41)
+    x = np.random.default_rng(42).standard_normal((4, s.hidden)).astype(np.float32)
+    L = oracle.Layer(lw)
+    free = oracle.block_forward(L, x.astype(np.float64))
+    forced = {}
+    for t in (0, 2, 3):
+        rest = [e for e in range(7) if e not in free["ids"][t]]
+        # keep one routed expert, swap in two others, listed in descending id
+        forced[t] = sorted([int(free["ids"][t][1]), rest[0], rest[-1]], reverse=True)
+    got = oracle.block_forward(L, x.astype(np.float64), forced_ids=forced)
+    y, ids, w = brute_forward(lw, x, forced=forced, details=True)
+    np.testing.assert_array_equal(got["ids"], ids)
+    np.testing.assert_allclose(got["w"], w, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(got["y"], y, rtol=1e-12, atol=1e-13)
+    # the token left to the router is untouched by the others' forcing
+    np.testing.assert_array_equal(got["ids"][1], free["ids"][1])
+    np.testing.assert_array_equal(got["y"][1], free["y"][1])
+    assert all(not np.array_equal(got["ids"][t], free["ids"][t]) for t in forced)
+
+
+# Every finite non-negative bf16 value (bit patterns 0x0000 .. 0x7F7F), exactly, for the
+# enumeration below.
+_BF16_POS = None
+
+
+def _bf16_values():
+    global _BF16_POS
+    if _BF16_POS is None:
+        bits = np.arange(0, 0x7F80, dtype=np.uint32) << np.uint32(16)
+        _BF16_POS = [Fraction(float(v)) for v in bits.view(np.float32)]
+    return _BF16_POS
+
+
+def py_bf16_nearest(v: float) -> float:
+    """Nearest bf16 value of the exact double v by enumeration: locate v among all finite bf16
+    values, compare the exact distances to its two neighbours, ties to the even bit pattern, and
+    overflow to infinity from half a step above the largest finite value."""
+    if v != v or v == 0.0:
+        return v
+    vals = _bf16_values()
+    a = Fraction(abs(v))
+    top = vals[-1] + (vals[-1] - vals[-2]) / 2
+    if a >= top:
+        return math.copysign(math.inf, v)
+    i = bisect.bisect_left(vals, a)
+    if i < len(vals) and vals[i] == a:
+        r = i
+    else:
+        lo, hi = i - 1, min(i, len(vals) - 1)
+        dl, dh = a - vals[lo], vals[hi] - a
+        r = lo if dl < dh or (dl == dh and lo % 2 == 0) else hi
+    return math.copysign(float(vals[r]), v)
+
+
+def test_round_to_bf16_is_one_rounding_of_the_exact_value():
+    u = 2.0 ** -8  # half a bf16 step at 1
+    cases = [
+        (1 + u + 2.0 ** -30, 1 + 2 * u),   # just above the midpoint; via float32 it would tie and fall to 1
+        (1 + u, 1.0),                       # exact midpoint: to the even significand
+        (1 + 3 * u, 1 + 4 * u),             # midpoint between odd 1 + 2u and even 1 + 4u
+        (1 + u - 2.0 ** -40, 1.0),
+        (-(1 + u + 2.0 ** -30), -(1 + 2 * u)),
+        (2.0 ** -134, 0.0),                 # half the smallest subnormal: to even (zero)
+        (3 * 2.0 ** -134, 2.0 ** -132),     # between subnormals 1 and 2 (units of 2^-133)
+        (oracle.BF16_MAX + 2.0 ** 119, math.inf),
+        (oracle.BF16_MAX + 2.0 ** 119 - 2.0 ** 100, oracle.BF16_MAX),
+    ]
+    for v, want in cases:
+        assert oracle.round_to_bf16(np.array([v]))[0] == want, v
+        assert py_bf16_nearest(v) == want, v
+    # random doubles over a wide range of exponents with low bits below float32's precision
+    rng = np.random.default_rng(44)
+    v = rng.standard_normal(3000) * np.ldexp(1.0, rng.integers(-140, 120, 3000))
+    v[:1000] = (v[:1000].astype(np.float32).astype(np.float64) * (1 + 2.0 ** -30))
+    got = oracle.round_to_bf16(v)
+    want = np.array([py_bf16_nearest(float(a)) for a in v])
+    np.testing.assert_array_equal(got, want)
+
+
+def _f32(v: float) -> float:
+    return struct.unpack("f", struct.pack("f", v))[0]
+
+
+def test_stack_step_matches_scalar_brute_force():
+    """One residual layer: h_next = fp32(h + block(bf16(RMSNorm(h)))), every piece in scalar
+    Python (the block by brute_forward, the bf16 rounding by enumeration)."""
+    s = gen.Shape(hidden=8, latent=5, n_experts=6, top_k=2, ffn=3, shared_ffn=3)
+    lw = make_f32_layer(s, 45)
+    lw.U = lw.U * np.float32(4)  # a block output comparable to h
+    rng = np.random.default_rng(46)
+    h = (rng.standard_normal((3, 8)) * np.array([[1.0], [30.0], [0.01]])).astype(np.float32).astype(np.float64)
+    out = oracle.stack_step(oracle.Layer(lw), h)
+    x = []
+    for row in h.tolist():
+        rms = math.sqrt(sum(a * a for a in row) / len(row) + 1e-6)
+        x.append([py_bf16_nearest(a / rms) for a in row])
+    x = np.array(x)
+    np.testing.assert_array_equal(out["x"], x)
+    y = brute_forward(lw, x)
+    want = np.array([[_f32(a + b) for a, b in zip(hr, yr)] for hr, yr in zip(h.tolist(), y.tolist())])
+    assert np.abs(y).max() > 0.1 * np.abs(h).min()
+    np.testing.assert_allclose(out["h_next"], want, rtol=1e-12, atol=0)
 
 
 def test_page_shapes_pin_the_edge0_block():
