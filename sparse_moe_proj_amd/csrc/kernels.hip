@@ -520,9 +520,33 @@ hipError_t small_proj_launch(const SmallProj& p, hipStream_t s) {
     return last();
 }
 
+#ifndef LMOE_ROWS_PROJ
+#define LMOE_ROWS_PROJ 1
+#endif
+// Whether rows_proj_kernel takes a small-batch projection of reduction width K (its K range per
+// wave fits the registers) with G partial inputs (XM 1).
+bool rows_proj_fits(int T, int K, int XM, int G = 1) {
+    return LMOE_ROWS_PROJ && T <= 16 * kSmallProjGroups && K % 32 == 0 &&
+           (K / 32 + LMOE_SP_WAVES - 1) / LMOE_SP_WAVES <= rows_proj_smax(XM) && G <= kRowsMaxG;
+}
+
+// rows_proj_kernel over R = N (+ 2E router rows) rows: an even share of consecutive rows per CU.
+template <int XM>
+hipError_t rows_proj_launch(RowsProj p, hipStream_t s) {
+    const long R = (long)p.N + (p.Gr ? 2L * p.E : 0);
+    p.rpw = (int)cdiv(R, cu_count());
+    p.eps = 1e-6f;
+    hipLaunchKernelGGL((rows_proj_kernel<LMOE_SP_WAVES, XM>), dim3(cdiv(R, p.rpw)), dim3(64 * LMOE_SP_WAVES), 0, s, p);
+    return last();
+}
+
 hipError_t launch_proj_router_bf16(const uint16_t* x, const uint16_t* D, const uint16_t* Gr, const float* br, int T,
                                   int L, int H, int E, float* z32, uint16_t* z16, float* logits, hipStream_t s,
                                   uint16_t* z16h, const float* hnorm) {
+    if (rows_proj_fits(T, H, hnorm ? 2 : 0)) {
+        const RowsProj p{x, hnorm, 0, D, T, L, H, 0, z32, z16, z16h, Gr, br, E, logits, 0, 0.f};
+        return hnorm ? rows_proj_launch<2>(p, s) : rows_proj_launch<0>(p, s);
+    }
     if (!small_proj_fits(T, H)) return hipErrorInvalidValue;
     SmallProj p{x, hnorm, 0, D, T, L, H, 0, z32, z16, Gr, br, E, logits, z16h};
     const dim3 grid((unsigned)std::min<long>(cdiv(L, 16) + 2 * cdiv(E, 16), cu_count()));
@@ -567,6 +591,9 @@ hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int 
 
 hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                                 uint16_t* out16, hipStream_t s) {
+    if (rows_proj_fits(T, K, 1, G))
+        return rows_proj_launch<1>(
+            RowsProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16, nullptr, nullptr, nullptr, 0, nullptr, 0, 0.f}, s);
     if (!small_proj_fits(T, K)) return hipErrorInvalidValue;
     return small_proj_launch<1>(SmallProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0,
                                           nullptr, nullptr},
@@ -600,6 +627,10 @@ hipError_t launch_proj_partials_kgroups(const float* xpart, int G, const uint16_
 
 hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                             uint16_t* out16, hipStream_t s, uint16_t* out16lo, uint16_t* out16h, const float* hnorm) {
+    if (T <= kStreamMaxT && rows_proj_fits(T, K, hnorm ? 2 : 0) && mode != 3) {
+        const RowsProj p{x, hnorm, 0, W, T, N, K, mode, out32, out16, out16h, nullptr, nullptr, 0, nullptr, 0, 0.f};
+        return hnorm ? rows_proj_launch<2>(p, s) : rows_proj_launch<0>(p, s);
+    }
     if (T <= kStreamMaxT && small_proj_fits(T, K)) {
         const SmallProj p{x, hnorm, 0, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0, nullptr, out16h};
         return hnorm ? small_proj_launch<2>(p, s) : small_proj_launch<0>(p, s);

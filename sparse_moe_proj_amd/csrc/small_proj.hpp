@@ -224,3 +224,216 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
 }
 
 }  // namespace lmoe
+
+namespace lmoe {
+
+// ==============================================================================================
+// Small-batch projection with the weight rows dealt evenly over the compute units.
+//
+// The same product as small_proj_kernel (out[t][n] = sum_k x[t][k] W[n][k], T <= 64), for a
+// launch that reads every weight byte once: the R rows (W's N rows, then, with a folded router,
+// the 2E rows of Gr [E][2][K] as one [2E][K] matrix) are cut into `rpw` consecutive rows per
+// workgroup, one workgroup per compute unit, so each unit streams the same share (at the 145B
+// shape 11 rows of 2560 for D and the router together, 10 rows of 1792 for U) instead of whole
+// 16-row blocks on some units and none on others.  A workgroup takes its rows 16 at a time as
+// the MFMA's A operand (rows past its range are zero); its W waves split K into contiguous step
+// ranges.  Each wave loads the token operand of its own K range straight into registers (token
+// j of the group in lane j, as the B operand), issued before its weight loads, so the tokens
+// arrive first and no LDS staging pass sits between the loads and the MFMAs.  The XM modes are
+// those of small_proj_kernel: 0 bf16 x; 1 the in-order sum of G fp32 partial inputs, rounded
+// once to bf16; 2 bf16(RMSNorm(h)) of an fp32 residual h (each token's sum of squares: per lane
+// over its steps in order, over the lane's four K chunks as (a + b) + (c + d), then over the waves
+// in order).  The waves' partial tiles meet in LDS and are summed in wave order.
+// ==============================================================================================
+constexpr int kRowsMaxG = 2;  // XM 1: partial inputs held in registers per step
+
+// MFMA steps (32 K values) a wave holds in registers, by input mode: K <= 32 * waves * steps
+// (the raw token loads of all steps, the weights and the bf16 operands are in flight together).
+__host__ __device__ constexpr int rows_proj_smax(int XM) { return XM == 0 ? 12 : XM == 1 ? 7 : 10; }
+
+struct RowsProj {
+    const uint16_t* x16;  // XM 0: [T][K] bf16
+    const float* xf;      // XM 1: [G][T][K] fp32 partials; XM 2: the residual h [T][K] fp32
+    int G;
+    const uint16_t* W;    // [N][K] bf16
+    int T, N, K, mode;    // mode 0: out32 = v, out16 = bf16(v) (out16h = fp16(v) if set); 1: out16 =
+                          // bf16(v); 2: out32 += v
+    float* out32;
+    uint16_t* out16;
+    uint16_t* out16h;
+    const uint16_t* Gr;   // optional [E][2][K]: logits[h][t][e] = x[t] . Gr[e][h] (+ bias[e] for h = 0)
+    const float* bias;
+    int E;
+    float* logits;        // [2][T][E]
+    int rpw;              // rows per workgroup
+    float eps;            // XM 2: the RMSNorm epsilon
+};
+
+template <int W, int XM>
+__global__ __launch_bounds__(64 * W) void rows_proj_kernel(const RowsProj p) {
+    constexpr int kRowsSmax = rows_proj_smax(XM);
+    constexpr int XR = XM == 0 ? 1 : XM == 2 ? 2 : 2 * kRowsMaxG;  // 16-byte loads per step
+    __shared__ float red[W][256];
+    __shared__ float ssq[W][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kq = lane >> 4, j = lane & 15;
+    const int K = p.K, T = p.T;
+    const int ns = K / 32;
+    const int s0 = wave * ns / W, nst = (wave + 1) * ns / W - s0;
+    const int R = p.N + (p.Gr ? 2 * p.E : 0);
+    const int rbeg = (int)blockIdx.x * p.rpw, rend = min(R, rbeg + p.rpw);
+    const int ngroups = (T + 15) / 16;
+    uint4 xr[kRowsSmax][XR];
+    uint4 wv[kRowsSmax];
+    uint4 xv[kRowsSmax];
+
+    // the token operand of group g: raw loads of token t0 + j, K chunk kq of every step
+    auto load_x = [&](int g) {
+        const int t = 16 * g + j;
+        const bool ok = t < T;
+#pragma unroll
+        for (int i = 0; i < kRowsSmax; ++i) {
+            if (i >= nst) break;
+            const int k0 = (s0 + i) * 32 + kq * 8;
+            if constexpr (XM == 0) {
+                xr[i][0] = ok ? ld16(p.x16 + (size_t)t * K + k0) : zero4();
+            } else if constexpr (XM == 2) {
+                const float* src = p.xf + (size_t)t * K + k0;
+                xr[i][0] = ok ? ld16(src) : zero4();
+                xr[i][1] = ok ? ld16(src + 4) : zero4();
+            } else {
+#pragma unroll
+                for (int q = 0; q < kRowsMaxG; ++q) {
+                    const float* src = p.xf + ((size_t)q * T + t) * K + k0;
+                    const bool l = ok && q < p.G;
+                    xr[i][2 * q] = l ? ld16(src) : zero4();
+                    xr[i][2 * q + 1] = l ? ld16(src + 4) : zero4();
+                }
+            }
+        }
+    };
+    // raw loads -> bf16 B operands (XM 2: needs every wave's sum of squares; one barrier)
+    auto make_x = [&]() {
+        if constexpr (XM == 0) {
+#pragma unroll
+            for (int i = 0; i < kRowsSmax; ++i)
+                if (i < nst) xv[i] = xr[i][0];
+        } else if constexpr (XM == 1) {
+#pragma unroll
+            for (int i = 0; i < kRowsSmax; ++i) {
+                if (i >= nst) break;
+                float a[8];
+                const float* u0 = reinterpret_cast<const float*>(&xr[i][0]);
+                const float* u1 = reinterpret_cast<const float*>(&xr[i][1]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    a[c] = u0[c];
+                    a[4 + c] = u1[c];
+                }
+#pragma unroll
+                for (int q = 1; q < kRowsMaxG; ++q) {
+                    const float* v0 = reinterpret_cast<const float*>(&xr[i][2 * q]);
+                    const float* v1 = reinterpret_cast<const float*>(&xr[i][2 * q + 1]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        a[c] += v0[c];
+                        a[4 + c] += v1[c];
+                    }
+                }
+                xv[i] = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
+            }
+        } else {
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < kRowsSmax; ++i) {
+                if (i >= nst) break;
+                const float* u = reinterpret_cast<const float*>(&xr[i][0]);
+                const float* v = reinterpret_cast<const float*>(&xr[i][1]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ss += u[c] * u[c];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ss += v[c] * v[c];
+            }
+            // lanes j, j + 16, j + 32, j + 48 hold token j's K chunks 0..3: lane j sums them in order
+            const float b = __shfl_xor(ss, 16), c = __shfl_xor(ss, 32), d = __shfl_xor(ss, 48);
+            if (kq == 0) ssq[wave][j] = (ss + b) + (c + d);
+            __syncthreads();
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) tot += ssq[w][j];
+            const float r = 1.0f / sqrtf(tot / (float)K + p.eps);
+#pragma unroll
+            for (int i = 0; i < kRowsSmax; ++i) {
+                if (i >= nst) break;
+                const float* u = reinterpret_cast<const float*>(&xr[i][0]);
+                const float* v2 = reinterpret_cast<const float*>(&xr[i][1]);
+                xv[i] = make_uint4(pack_bf2(u[0] * r, u[1] * r), pack_bf2(u[2] * r, u[3] * r), pack_bf2(v2[0] * r, v2[1] * r),
+                                   pack_bf2(v2[2] * r, v2[3] * r));
+            }
+        }
+    };
+    auto wrow = [&](int n) -> const uint16_t* {
+        return n < p.N ? p.W + (size_t)n * K : p.Gr + (size_t)(n - p.N) * K;
+    };
+    auto load_w = [&](int n0) {
+        const int nr = min(16, rend - n0);
+        const bool rv = j < nr;
+        const uint16_t* wr = wrow(n0 + (rv ? j : 0));
+#pragma unroll
+        for (int i = 0; i < kRowsSmax; ++i) {
+            if (i >= nst) break;
+            wv[i] = rv ? ld16(wr + (s0 + i) * 32 + kq * 8) : zero4();
+        }
+    };
+
+    if (rbeg >= rend) return;
+    load_x(0);  // tokens first: they are needed by every MFMA
+    load_w(rbeg);
+    bool have_x = false;  // xv holds group 0 (kept across blocks when there is one group)
+    for (int n0 = rbeg; n0 < rend; n0 += 16) {
+        const int nr = min(16, rend - n0);
+        for (int g = 0; g < ngroups; ++g) {
+            const int t0 = 16 * g, tn = min(16, T - t0);
+            if (!(have_x && ngroups == 1)) {
+                if (n0 != rbeg || g != 0) load_x(g);
+                make_x();
+                have_x = true;
+            }
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int i = 0; i < kRowsSmax; ++i)
+                if (i < nst) acc = mfma16(wv[i], xv[i], acc);
+            // the next block's weights are requested before this one is reduced
+            if (g == ngroups - 1 && n0 + 16 < rend) load_w(n0 + 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][(4 * kq + r) * 16 + j] = acc[r];
+            __syncthreads();
+            if (threadIdx.x < 256) {
+                const int t = threadIdx.x >> 4, r = threadIdx.x & 15, n = n0 + r;
+                if (t < tn && r < nr) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int w = 0; w < W; ++w) v += red[w][r * 16 + t];
+                    if (n >= p.N) {
+                        const int q = n - p.N, e = q >> 1, h = q & 1;
+                        p.logits[((size_t)h * T + t0 + t) * p.E + e] = h == 0 && p.bias ? v + p.bias[e] : v;
+                    } else {
+                        const size_t o = (size_t)(t0 + t) * p.N + n;
+                        if (p.mode == 0) {
+                            p.out32[o] = v;
+                            p.out16[o] = (uint16_t)f2bf(v);
+                            if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                        } else if (p.mode == 1) {
+                            p.out16[o] = (uint16_t)f2bf(v);
+                        } else {
+                            p.out32[o] += v;
+                        }
+                    }
+                }
+            }
+            __syncthreads();  // red (and ssq) are reused
+        }
+    }
+}
+
+}  // namespace lmoe
