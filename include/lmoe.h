@@ -254,6 +254,27 @@ lmoe_status lmoe_permute(const lmoe_config* cfg, const int32_t* ids, int32_t T, 
 lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* weights, const void* x, int32_t T, void* y,
                          const lmoe_forward_opts* opts, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Allocation-free form of lmoe_forward, for callers that cannot allocate device memory or
+ * manage a workspace: code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results as lmoe_forward without ws/ws_bytes: its
+ * workspace is a static device array of LMOE_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on (from the loading of its code object until the process ends), found on
+ * the first call on each device (the device current on the calling thread, which must be the
+ * stream's device).  The call allocates nothing and frees nothing.
+ *   - T must need at most LMOE_NOALLOC_SCRATCH_BYTES of workspace (lmoe_workspace_bytes): every
+ *     batch of up to 64 tokens at the Edge0-145B shape with bf16, MXFP4 or NVFP4 experts, with
+ *     one or 8 expert groups, fits (3.4 MB and 22.2 MB at T = 64); larger requests return
+ *     LMOE_ERR_WORKSPACE before anything is enqueued.
+ *   - Every call on one GPU uses that GPU's one array, which keeps the last call's contents
+ *     (nothing in it needs to start at zero).  Calls on one GPU must therefore be ordered (one
+ *     stream, or events between streams): calls that overlap in time on one GPU race and give
+ *     undefined results.
+ */
+#define LMOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+lmoe_status lmoe_forward_noalloc(const lmoe_config* cfg, const lmoe_weights* weights, const void* x, int32_t T,
+                                 void* y, const lmoe_forward_opts* opts, void* stream);
+
 /* Static text for a status code. */
 const char* lmoe_status_str(lmoe_status status);
 

@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
@@ -185,6 +186,34 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     const char* pa = static_cast<const char*>(a);
     const char* pb = static_cast<const char*>(b);
     return pa < pb + nb && pb < pa + na;
+}
+
+// Workspace of lmoe_forward_noalloc: one array per GPU, allocated when the code object is loaded
+// and held until the process ends.  Host code never passes its name to a kernel (that would be a
+// host-side stand-in, not a device address): it uses the address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[LMOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The device address of the current device's scratch array, looked up once per device (with
+// that device current) and kept.
+lmoe_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(LMOE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(LMOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LMOE_OK;
 }
 
 }  // namespace
@@ -484,6 +513,22 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         return hip_fail(e, "U projection");
     ev.end(LMOE_STAGE_U);
     return ev.err != hipSuccess ? hip_fail(ev.err, "stage event record") : LMOE_OK;
+}
+
+lmoe_status lmoe_forward_noalloc(const lmoe_config* cfg, const lmoe_weights* weights, const void* x, int32_t T, void* y,
+                                 const lmoe_forward_opts* opts, void* stream) {
+    Dims d;
+    lmoe_status st = check_config(cfg, d);
+    if (st != LMOE_OK) return st;
+    if ((st = check_T(d, T)) != LMOE_OK) return st;
+    const size_t need = plan(d, T).total;
+    if (need > (size_t)LMOE_NOALLOC_SCRATCH_BYTES)
+        return fail(LMOE_ERR_WORKSPACE,
+                    "T = %d needs %zu workspace bytes, more than the %zu bytes of the allocation-free entry point",
+                    T, need, (size_t)LMOE_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (T > 0 && (st = scratch_address(&ws)) != LMOE_OK) return st;
+    return lmoe_forward(cfg, weights, x, T, y, opts, ws, (size_t)LMOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 const char* lmoe_status_str(lmoe_status status) {

@@ -212,3 +212,17 @@ def test_pack_arguments_checked():
     assert lm.lmoe_pack_experts(c, 0, FAKE + 4, FAKE + (1 << 34), 4, 0) == lm.LMOE_ERR_ALIGN
     assert lm.lmoe_pack_experts(c, 0, FAKE, FAKE + rec, 4, 0) == lm.LMOE_ERR_UNSUPPORTED  # overlap
     assert lm.lmoe_pack_experts(c, 0, None, None, 0, 0) == lm.LMOE_OK  # nothing to do
+
+
+def test_noalloc_checks_arguments_on_the_host():
+    """The allocation-free entry point refuses a batch whose workspace exceeds its static array
+    (and bad shapes) before it looks for a device; T = 0 is a no-op."""
+    too_big = 4096
+    assert lm.lmoe_workspace_bytes(cfg(), too_big) > lm.LMOE_NOALLOC_SCRATCH_BYTES
+    assert lm.lmoe_workspace_bytes(cfg(), 64) <= lm.LMOE_NOALLOC_SCRATCH_BYTES
+    assert lm.lmoe_workspace_bytes(cfg(groups=8), 64) <= lm.LMOE_NOALLOC_SCRATCH_BYTES
+    st = lm.lmoe_forward_noalloc(cfg(), full_weights(), FAKE, too_big, FAKE + (1 << 36), None, 0)
+    assert st == lm.LMOE_ERR_WORKSPACE and "allocation-free" in lm.last_error()
+    assert lm.lmoe_forward_noalloc(cfg(), full_weights(), FAKE, -1, FAKE, None, 0) == lm.LMOE_ERR_SHAPE
+    nothing = lm.make_weights(None, None, None, None, None, None)
+    assert lm.lmoe_forward_noalloc(cfg(), nothing, None, 0, None, None, 0) == lm.LMOE_OK
