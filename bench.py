@@ -5,9 +5,23 @@ A step is one lmoe_forward (D projection, router, top-k, permutation, expert Swi
 shared expert, combine, U projection) over one batch of synthetic tokens already resident
 in HBM.  The timed steps are enqueued back to back on one stream and cycle through
 `--rotate` byte-identical copies of the layer's weights at different HBM addresses, so the
-256 MB last-level cache cannot serve a step from the previous one.  HIP events recorded by
-the library around the dominant kernel of every timed step give its duration.  The same
-steps replayed from captured HIP graphs are timed afterwards and reported beside it.
+256 MB last-level cache cannot serve a step from the previous one.
+
+What is measured:
+  * value / ms_per_step: exactly --steps eager steps after --warmup untimed ones, bracketed by
+    device synchronisation (wall clock);
+  * roofline: the dominant kernel (decode: the gate/up launch; prefill: the expert gate/up
+    GEMM), its duration from HIP events the library attaches to that launch in every timed
+    step, against the published peak and against the rate this part reaches in a plain
+    streaming-read or matrix-core loop (libpeaks.so, timed in the same run); the whole layer's
+    fraction beside it;
+  * timing: at least --graph-reps replays of captured HIP graphs (after 20 untimed ones), each
+    bracketed by events: median, p10, p90;
+  * clocks: the shader clock read by the matrix-core loop (s_memtime against the 100 MHz
+    real-time counter) and, where the driver exposes it, the current SCLK level sampled while
+    the graph replays run;
+  * cpu_baseline: the oracle on the host's cores for the headline workload, and oracle_baselines
+    for every workload on a bounded sample, with the CPU model and host memory.
 
 Workloads (lmoe_data.WORKLOADS): decode_t8 (default, HBM-bound), prefill_t4096,
 prefill_t16384 (MFMA-bound; measured as the secondary line by default), stack48_mxfp4_t8.
@@ -63,6 +77,197 @@ class Hip:
         return ms.value
 
 
+def host_info():
+    """CPU model, host memory and the cores this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    mem_gb = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    mem_gb = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return {"cpu_model": model, "host_mem_gib": mem_gb, "cores_available": cores}
+
+
+class SclkSampler:
+    """Samples the GPU's current SCLK level (the line the driver marks with '*' in pp_dpm_sclk)
+    from a thread while the measured work runs; inactive where the file is not readable."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.path = None
+        for p in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            try:
+                with open(p) as f:
+                    if "*" in f.read():
+                        self.path = p
+                        break
+            except OSError:
+                continue
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if self.path else None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if "*" in line:
+                        tok = [t for t in line.replace(":", " ").split() if t.lower().endswith("mhz")]
+                        return int(tok[0][:-3]) if tok else None
+        except (OSError, ValueError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self._thread:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        a = np.array(self.samples)
+        return {"source": self.path, "samples": int(a.size), "median_mhz": float(np.median(a)),
+                "min_mhz": int(a.min()), "max_mhz": int(a.max())}
+
+
+def measure_peaks():
+    """Rates this part reaches in plain loops (libpeaks.so): HBM streaming read, bf16 32x32x16 and
+    scaled FP8 x FP4 32x32x64 matrix-core issue, with the shader clock read inside the loops."""
+    import torch
+    path = os.path.join(ROOT, "sparse_moe_proj_amd", "libpeaks.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python sparse_moe_proj_amd/build.py` first")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.peak_stream_read.argtypes = [P, ctypes.c_size_t, P, ctypes.c_int, P]
+    lib.peak_mfma.argtypes = [ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, P]
+    per_wave = lib.peak_mfma_per_wave()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    out = {"compute_units": cus}
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return ts
+
+    nbytes = 4 << 30  # well beyond the 256 MB last-level cache
+    buf = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    best = None
+    for wg_per_cu in (4, 8, 16):
+        grid = cus * wg_per_cu
+        sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+
+        def run():
+            assert lib.peak_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, stream.cuda_stream) == 0
+
+        ms = float(np.median(timed(run, 7)[2:]))
+        gbs = nbytes / (ms / 1e3) / 1e9
+        if best is None or gbs > best["GBs"]:
+            best = {"GBs": round(gbs, 1), "bytes": nbytes, "workgroups": grid, "ms": round(ms, 4)}
+    out["stream_read"] = best
+    del buf
+    for kind, name, flop in ((0, "mfma_bf16_32x32x16", 32768), (1, "mfma_scale_fp8xfp4_32x32x64", 131072)):
+        res = torch.zeros(cus * 256, dtype=torch.float32, device="cuda")
+        clk = torch.zeros(4, dtype=torch.int64, device="cuda")
+        iters = 4000 if kind == 0 else 2000
+
+        def run():
+            assert lib.peak_mfma(kind, res.data_ptr(), iters, clk.data_ptr(), cus, stream.cuda_stream) == 0
+
+        ms = float(np.median(timed(run, 7)[2:]))
+        flops = cus * 4 * iters * per_wave * flop
+        c = clk.cpu().numpy().astype(np.int64)
+        sclk = (c[2] - c[0]) / ((c[3] - c[1]) / 100e6) / 1e6 if c[3] > c[1] else None
+        out[name] = {"TFLOPs": round(flops / (ms / 1e3) / 1e12, 1), "ms": round(ms, 4),
+                     "sclk_mhz_in_loop": round(sclk, 1) if sclk else None}
+    return out
+
+
+def graph_timing(run_graph, samples, warmup=20, group_us=1000.0):
+    """Replays of captured HIP graphs (`run_graph(i)` launches replay i) on the current stream.
+
+    An event recorded between two replays costs the step about 4.6 us at decode size (measured:
+    79.3 us per replay with an event around every replay, 74.7 us without), so the spread is taken
+    over `samples` groups of g consecutive replays each (g = ceil(group_us / step), at least 1):
+    events bracket each group, a sample is the group's time / g, and median, p10 and p90 are
+    over the samples (g * samples >= 100 replays).  Then the same number of replays runs with
+    events only at its two ends (mean), and a further untimed run of about 200 ms has the SCLK
+    level sampled (reading the driver's clock file while timing could perturb what is timed)."""
+    import torch
+    for i in range(warmup):
+        run_graph(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(10):
+        run_graph(i)
+    b.record()
+    torch.cuda.synchronize()
+    step_us = 1e3 * a.elapsed_time(b) / 10
+    g = max(1, int(np.ceil(group_us / step_us)))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(samples + 1)]
+    evs[0].record()
+    for i in range(samples):
+        for j in range(g):
+            run_graph(i * g + j)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    us = np.array([1e3 * evs[i].elapsed_time(evs[i + 1]) / g for i in range(samples)])
+    n = samples * g
+    a.record()
+    for i in range(n):
+        run_graph(i)
+    b.record()
+    torch.cuda.synchronize()
+    mean_run = 1e3 * a.elapsed_time(b) / n
+    with SclkSampler() as sampler:
+        for i in range(max(1, int(2e5 / step_us))):
+            run_graph(i)
+        torch.cuda.synchronize()
+    return {"replays": n, "samples": samples, "replays_per_sample": g,
+            "median_us": round(float(np.median(us)), 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+            "p90_us": round(float(np.percentile(us, 90)), 2), "mean_us": round(mean_run, 2),
+            "sclk": sampler.summary()}
+
+
 def algorithmic_counts(wl, ids: np.ndarray, T=None):
     """Bytes and flops the method itself needs for one layer step, from the step's own routing."""
     s = wl.shape
@@ -101,7 +306,7 @@ def layer_copies(wl, rotate):
     return [base] + [base.clone() for _ in range(rotate - 1)]
 
 
-def measure(wl, steps, warmup, rotate, profile_stages=True, copies=None, T=None, graphs=True):
+def measure(wl, steps, warmup, rotate, profile_stages=True, copies=None, T=None, graphs=True, graph_reps=100):
     """Times `steps` forward steps of T tokens (default: the workload's T) over the weight copies."""
     import torch
 
@@ -169,8 +374,8 @@ def measure(wl, steps, warmup, rotate, profile_stages=True, copies=None, T=None,
 
     if not graphs:
         return dict(ms_per_step=ms_per_step, tok_s=T / (ms_per_step / 1e3), up_ms=up_ms, counts=counts,
-                    stages_us=stages_us, weight_bytes_per_copy=base.nbytes(), graph_ms_per_step=None)
-    # the same steps replayed from captured HIP graphs (one per weight copy), for comparison
+                    stages_us=stages_us, weight_bytes_per_copy=base.nbytes(), graph=None)
+    # the same steps replayed from captured HIP graphs (one per weight copy): per-replay events
     graphs = []
     for r in range(rotate):
         g = torch.cuda.CUDAGraph()
@@ -179,16 +384,9 @@ def measure(wl, steps, warmup, rotate, profile_stages=True, copies=None, T=None,
             fwd(copies[r])
         graphs.append(g)
     torch.cuda.synchronize()
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    g0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % rotate].replay()
-    torch.cuda.synchronize()
-    graph_ms = 1e3 * (time.perf_counter() - g0) / steps
+    gt = graph_timing(lambda i: graphs[i % rotate].replay(), max(graph_reps, 100))
     return dict(ms_per_step=ms_per_step, tok_s=T / (ms_per_step / 1e3), up_ms=up_ms, counts=counts,
-                stages_us=stages_us, weight_bytes_per_copy=base.nbytes(), graph_ms_per_step=graph_ms)
+                stages_us=stages_us, weight_bytes_per_copy=base.nbytes(), graph=gt)
 
 
 def measure_stack(wl, steps, warmup):
@@ -248,33 +446,92 @@ def measure_stack(wl, steps, warmup):
     mean = {key: float(np.mean([c[key] for c in counts])) for key in ("layer_bytes", "layer_flops", "up_bytes",
                                                                       "up_flops", "n_distinct_experts")}
     return dict(ms_per_step=ms_per_layer, tok_s=T / (ms_per_layer / 1e3), up_ms=up_ms, counts=mean,
-                stages_us={}, graph_ms_per_step=None)
+                stages_us={}, graph=None)
 
 
-def cpu_baseline(wl, seconds):
-    """The oracle as it stands (float64 numpy), on the host's cores, on whole decode steps."""
-    import lmoe_data as gen
-    import oracle
+class LazyExperts:
+    """A layer's routed expert records, each drawn from its own seed on first access: the oracle
+    reads only the records of the experts its tokens route to."""
+
+    def __init__(self, wl, bank):
+        self.wl, self.bank, self.cache = wl, bank, {}
+
+    def __getitem__(self, e):
+        import lmoe_data as gen
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = gen.expert_record(self.wl.shape, gen.rng_for(self.wl.wid, self.bank, gen.T_EXPERT, e),
+                                              self.wl.expert)
+        return self.cache[e]
+
+    def draw(self, ids):
+        from concurrent.futures import ThreadPoolExecutor
+
+        import lmoe_data as gen
+        with ThreadPoolExecutor(gen.n_threads()) as ex:
+            list(ex.map(self.__getitem__, sorted(set(int(e) for e in np.asarray(ids).ravel()))))
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    lw = gen.make_layer(wl, 0)
-    x = oracle.decode(gen.make_tokens(wl), wl.act)
-    reps, tok = 0, 0
+        return os.cpu_count() or 1
+
+
+def oracle_rate(wl, seconds, ntok=None):
+    """The oracle as it stands (float64 numpy) on one layer of `wl`, on the host's cores: passes over
+    the workload's T tokens (ntok None) or over its first ntok tokens (tokens are independent units
+    of the block, so a sample of them does the same work per token).  Generating the data and drawing
+    the routed experts' records happen before the timed passes; every timed pass builds a fresh
+    oracle.Layer, so promoting the touched weights to float64 is inside."""
+    import lmoe_data as gen
+    import oracle
+    lazy = LazyExperts(wl, gen.expert_bank(wl, 0))
+    lw = gen.make_layer(wl, 0, experts=lazy)
+    T = wl.T if ntok is None else min(ntok, wl.T)
+    if wl.layers > 1:  # one layer of the stack: bf16(RMSNorm(h)) in, the fp32 residual updated
+        h = gen.make_residual(wl, T=T).astype(np.float64)
+        x = oracle.round_to_bf16(oracle.rmsnorm(h))
+
+        def step(L):
+            return oracle.stack_step(L, h)
+    else:
+        x = oracle.decode(gen.make_tokens(wl, T=T), wl.act)
+
+        def step(L):
+            return oracle.block_forward(L, x)
+    L0 = oracle.Layer(lw)
+    lazy.draw(oracle.route(x @ L0.D.T, L0.Wr, L0.br, wl.shape.top_k, wl.shape.groups)[0])
+    passes = 0
     t0 = time.perf_counter()
     while True:
-        L = oracle.Layer(lw)  # includes promoting the touched weights to float64
-        oracle.block_forward(L, x)
-        reps += 1
-        tok += x.shape[0]
+        step(oracle.Layer(lw))
+        passes += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(tok / dt, 3), "unit": "tok/s per layer", "cores": int(cores), "kind": "oracle",
-            "sample": f"{reps} whole {wl.name} steps (T={x.shape[0]}), float64 numpy, weights promoted per step",
-            "seconds": round(dt, 2)}
+    what = "whole steps" if T == wl.T else f"the first {T} of its {wl.T} tokens per pass"
+    if wl.layers > 1:
+        what = f"one layer of the {wl.layers}-layer stack, T={T}"
+    return {"workload": wl.name, "value": round(passes * T / dt, 3), "unit": "tok/s per layer", "tokens_per_pass": T,
+            "passes": passes, "seconds": round(dt, 2), "sample": what}
+
+
+def cpu_baseline(wl, seconds):
+    """The headline workload's oracle rate (bounded in time) with the host it ran on."""
+    r = oracle_rate(wl, seconds)
+    hi = host_info()
+    return {"value": r["value"], "unit": r["unit"], "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{r['passes']} passes of {r['sample']} (T={r['tokens_per_pass']}), float64 numpy, weights "
+                      f"promoted per pass", "seconds": r["seconds"], "cpu_model": hi["cpu_model"],
+            "host_mem_gib": hi["host_mem_gib"]}
+
+
+# every workload the layer is specified on, with the oracle's token sample (None: whole steps)
+ORACLE_SAMPLES = (("tiny_f32", None, 2.0), ("decode_t8", None, 3.0), ("prefill_t4096", 16, 3.0),
+                  ("prefill_t16384", 16, 3.0), ("stack48_mxfp4_t8", None, 3.0))
 
 
 def measured_traffic(workload):
@@ -293,12 +550,20 @@ def measured_traffic(workload):
     return rec["traffic_bytes"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
-def roofline_hbm(counts, up_ms, traffic=None):
+def roofline_hbm(counts, up_ms, layer_s, peaks=None, traffic=None):
+    """The decode gate/up launch against HBM: algorithmic bytes / its mean duration, as a fraction of
+    the published 8 TB/s (frac) and of the streaming-read rate measured in the same run; the
+    whole layer's fraction beside it."""
     achieved = counts["up_bytes"] / (up_ms / 1e3) / 1e9
+    layer_gbs = counts["layer_bytes"] / layer_s / 1e9
+    meas = peaks["stream_read"]["GBs"] if peaks else None
     return {"bound": "hbm", "kernel": "decode_gu_kernel (expert gate/up and SwiGLU)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "bytes_per_launch": counts["up_bytes"], "avg_launch_us": round(up_ms * 1e3, 2)}
+            "bytes_per_launch": counts["up_bytes"], "avg_launch_us": round(up_ms * 1e3, 2),
+            "measured_peak": meas, "frac_of_measured": round(achieved / meas, 4) if meas else None,
+            "layer_achieved": round(layer_gbs, 1), "layer_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+            "layer_frac_of_measured": round(layer_gbs / meas, 4) if meas else None}
 
 
 def mx_mfma_path(wl):
@@ -307,29 +572,57 @@ def mx_mfma_path(wl):
     return wl.expert == "mxfp4" and wl.T >= max(min_t, 17) and os.environ.get("LMOE_MX_MFMA", "1")[:1] != "0"
 
 
-def roofline_mfma(counts, up_ms, wl=None):
+def roofline_mfma(counts, up_ms, layer_s, peaks=None, wl=None):
+    """The prefill expert gate/up launch against the matrix cores: algorithmic flops / its mean
+    duration, as a fraction of the published peak of its operand type (frac) and of the issue rate
+    a plain MFMA loop of the same instruction reaches in the same run; the layer beside it (bf16)."""
     achieved = counts["up_flops"] / (up_ms / 1e3) / 1e12
+    layer_tf = counts["layer_flops"] / layer_s / 1e12
     if wl is not None and mx_mfma_path(wl):
-        kernel, peak = ("expert gate/up (mx_gemm_persistent MxUp, MXFP8 z + MXFP4 residual x MXFP4 records; "
-                        "with the z quantization and the bf16 shared expert)"), MFMA_FP8_PEAK_TFLOPS
+        kernel, peak, key = ("expert gate/up (mx_gemm_persistent MxUp, MXFP8 z + MXFP4 residual x MXFP4 records; "
+                             "with the z quantization and the bf16 shared expert)"), MFMA_FP8_PEAK_TFLOPS, \
+            "mfma_scale_fp8xfp4_32x32x64"
     else:
-        kernel, peak = "expert gate/up (pipe_gemm_persistent PipeUp)", MFMA_BF16_PEAK_TFLOPS
+        kernel, peak, key = "expert gate/up (pipe_gemm_persistent PipeUp)", MFMA_BF16_PEAK_TFLOPS, "mfma_bf16_32x32x16"
+    meas = peaks[key]["TFLOPs"] if peaks else None
+    meas_bf16 = peaks["mfma_bf16_32x32x16"]["TFLOPs"] if peaks else None
     return {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1),
             "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-            "traffic": None, "flops_per_launch": counts["up_flops"], "avg_launch_us": round(up_ms * 1e3, 2)}
+            "traffic": None, "flops_per_launch": counts["up_flops"], "avg_launch_us": round(up_ms * 1e3, 2),
+            "measured_peak": meas, "frac_of_measured": round(achieved / meas, 4) if meas else None,
+            "layer_achieved": round(layer_tf, 1), "layer_frac": round(layer_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "layer_frac_of_measured": round(layer_tf / meas_bf16, 4) if meas_bf16 else None}
+
+
+def roofline_of(wl, c, m, peaks):
+    layer_s = m["ms_per_step"] / 1e3
+    mfma_bound = c["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > c["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        return roofline_mfma(c, m["up_ms"], layer_s, peaks, wl)
+    return roofline_hbm(c, m["up_ms"], layer_s, peaks, measured_traffic(wl.name))
+
+
+def layer_line(c, m):
+    layer_s = m["ms_per_step"] / 1e3
+    return {"bytes": c["layer_bytes"], "flops": c["layer_flops"], "n_distinct_experts": c["n_distinct_experts"],
+            "hbm_frac": round(c["layer_bytes"] / layer_s / (HBM_PEAK_GBS * 1e9), 4),
+            "mfma_frac": round(c["layer_flops"] / layer_s / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t8")
     ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--graph-samples", type=int, default=100,
+                    help="timed samples of HIP-graph replays (groups of about 1 ms; at least 100 replays)")
     ap.add_argument("--secondary", default="prefill_t16384", help="second workload line ('' = none)")
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the streaming-read and MFMA-loop measurements")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (calibrates HBM traffic counters)")
     ap.add_argument("--tsweep", default="",
@@ -351,11 +644,12 @@ def main():
         args.rotate = 1
     else:
         copies = layer_copies(wl, args.rotate)
-        m = measure(wl, args.steps, args.warmup, args.rotate, copies=copies)
+        m = measure(wl, args.steps, args.warmup, args.rotate, copies=copies, graph_reps=args.graph_samples)
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks()
+        log(f"[bench] measured peaks {json.dumps(peaks)}")
     c = m["counts"]
-    mfma_bound = c["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > c["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
-    rl = roofline_mfma(c, m["up_ms"], wl) if mfma_bound else roofline_hbm(c, m["up_ms"], measured_traffic(wl.name))
-    layer_s = m["ms_per_step"] / 1e3
     out = {
         "metric": METRIC,
         "value": round(m["tok_s"], 1),
@@ -373,15 +667,16 @@ def main():
                    "n_experts": wl.shape.n_experts, "top_k": wl.shape.top_k, "ffn": wl.shape.ffn,
                    "shared_ffn": wl.shape.shared_ffn, "router_bias": wl.bias, "weights": wl.expert,
                    "weight_copies": args.rotate, "timed": "eager lmoe_forward calls on one stream"},
-        "roofline": rl,
-        "layer": {"bytes": c["layer_bytes"], "flops": c["layer_flops"], "n_distinct_experts": c["n_distinct_experts"],
-                  "hbm_frac": round(c["layer_bytes"] / layer_s / (HBM_PEAK_GBS * 1e9), 4),
-                  "mfma_frac": round(c["layer_flops"] / layer_s / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)},
+        "roofline": roofline_of(wl, c, m, peaks),
+        "layer": layer_line(c, m),
+        "timing": m["graph"],
         "stages_us": m["stages_us"],
-        "graph_ms_per_step": round(m["graph_ms_per_step"], 5) if m["graph_ms_per_step"] is not None else None,
+        "peaks_measured": peaks,
+        "host": host_info(),
     }
     if wl.layers > 1:
         out["config"]["layers"] = wl.layers
+        out["config"]["expert_banks"] = wl.expert_banks
         out["config"]["timed"] = "eager lmoe_forward calls, all layers in order, per-layer figures"
     if args.tsweep and copies is not None:
         sweep = []
@@ -401,19 +696,15 @@ def main():
         del m
         torch.cuda.empty_cache()
         wl2 = gen.WORKLOADS[args.secondary]
-        m2 = measure(wl2, args.secondary_steps, 3, 2)
+        m2 = measure(wl2, args.secondary_steps, 3, 2, graph_reps=args.graph_samples)
         c2 = m2["counts"]
-        s2 = m2["ms_per_step"] / 1e3
         out["secondary"] = {
             "workload": wl2.name, "T": wl2.T, "value": round(m2["tok_s"], 1), "unit": "tok/s per layer",
             "ms_per_step": round(m2["ms_per_step"], 4),
-            "roofline": roofline_mfma(c2, m2["up_ms"]),
-            "layer": {"flops": c2["layer_flops"], "bytes": c2["layer_bytes"],
-                      "n_distinct_experts": c2["n_distinct_experts"],
-                      "mfma_frac": round(c2["layer_flops"] / s2 / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
-                      "hbm_frac": round(c2["layer_bytes"] / s2 / (HBM_PEAK_GBS * 1e9), 4)},
+            "roofline": roofline_of(wl2, c2, m2, peaks),
+            "layer": layer_line(c2, m2),
+            "timing": m2["graph"],
             "stages_us": m2["stages_us"],
-            "graph_ms_per_step": round(m2["graph_ms_per_step"], 4),
         }
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -424,6 +715,8 @@ def main():
         out["calib_copy_bytes"] = n
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        out["oracle_baselines"] = [oracle_rate(gen.WORKLOADS[name], sec, ntok) for name, ntok, sec in ORACLE_SAMPLES]
+        log(f"[bench] oracle baselines {json.dumps(out['oracle_baselines'])}")
     print(json.dumps(out), flush=True)
 
 

@@ -108,6 +108,15 @@ def check_block(lw, x_host, act, out, sample=None, tol=None, label=""):
 
     if sample is None:
         sample = np.arange(T)
+    elif isinstance(sample, str) and sample.startswith("tiles:"):
+        # every expert tile of the GPU's own work list, plus first, last, ragged and random tokens
+        rows, n_extra = (int(v) for v in sample[len("tiles:"):].split(","))
+        perm_g = host(out["perm"])[: T * k]
+        toks, tiles = tile_cover_tokens(host(out["offsets"]), perm_g, T, k, s.n_experts, rows, s.shared_ffn > 0)
+        sample = np.array(sorted(toks | set(sample_tokens(T, n_extra).tolist())))
+        assert_tiles_covered(tiles, sample, perm_g, k, s.n_experts)
+        log(f"[{label}] output sample covers all {len(tiles)} tiles of {rows} rows "
+            f"({sum(1 for t in tiles if t[0] == s.n_experts)} shared) with {sample.size} tokens")
     sample = np.asarray(sample)
     forced = {i: ids_g[t] for i, t in enumerate(sample) if not same[t]}
     L.prefetch(np.concatenate([ids_o[sample].ravel(), ids_g[sample].ravel()]))
@@ -119,6 +128,36 @@ def check_block(lw, x_host, act, out, sample=None, tol=None, label=""):
         f"excluded={int(excluded.sum())} differing={int((~same).sum())} dw={dw:.2e} zrel={zrel:.2e}")
     assert err.max() <= tol, f"output rel err {err.max()} > {tol} (token {sample[err.argmax()]})"
     return dict(max_rel=float(err.max()), excluded=int(excluded.sum()), differing=int((~same).sum()))
+
+
+def tile_cover_tokens(offsets, perm, T, k, E, rows, has_shared=True):
+    """Tokens whose outputs cover every `rows`-row tile of the expert work: for each expert
+    segment [offsets[e], offsets[e+1]) cut into tiles of `rows` positions, the token of the tile's
+    last position (so each segment's ragged last tile is included), and for the shared segment
+    (all T tokens, in tiles of `rows` tokens) the last token of each tile.  Returns (tokens,
+    tiles) with tiles = [(segment, first position, end position)] for the coverage check."""
+    toks, tiles = set(), []
+    offsets = np.asarray(offsets)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        for p0 in range(a, b, rows):
+            p1 = min(p0 + rows, b)
+            toks.add(int(perm[p1 - 1]) // k)
+            tiles.append((e, p0, p1))
+    if has_shared:
+        for t0 in range(0, T, rows):
+            t1 = min(t0 + rows, T)
+            toks.add(t1 - 1)
+            tiles.append((E, t0, t1))
+    return toks, tiles
+
+
+def assert_tiles_covered(tiles, sample, perm, k, E):
+    """Every tile holds at least one position whose token is in the sample."""
+    chosen = set(int(t) for t in sample)
+    for seg, p0, p1 in tiles:
+        rows = range(p0, p1) if seg == E else (int(perm[p]) // k for p in range(p0, p1))
+        assert any(t in chosen for t in rows), f"tile of segment {seg} at {p0}..{p1} has no checked token"
 
 
 def sample_tokens(T, n, seed=0):

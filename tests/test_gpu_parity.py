@@ -1,7 +1,8 @@
 """GPU parity of the HIP path (through the C ABI) against the CPU oracle.
 
-Covers the seven workloads at full size (routing and permutation on every token, outputs on
-every token up to T=8 and on sampled tokens beyond), plus small shapes that exercise ragged
+Covers the workloads at full size (routing and permutation on every token; outputs on every
+token up to T=8, for the prefill workloads on tokens that cover every 128-row expert tile of the
+GPU's own work list and every shared-expert tile), plus small shapes that exercise ragged
 tiles, both kernel paths, MXFP4 and NVFP4 records, no shared expert, E == k and E == k == 1.
 """
 import numpy as np
@@ -23,7 +24,14 @@ def ws():
     return Workspace("cuda")
 
 
-def _workload_case(name, n_sample, ws):
+# rows of the large-batch expert tiles (the pipelined and the block-scaled GEMMs' 128-row tiles)
+TILE_ROWS = 128
+
+
+def _workload_case(name, n_sample, ws, tiles=False):
+    """One workload's layer at full size.  tiles: the outputs are checked on tokens that cover every
+    expert tile of the GPU's own work list (and every shared-expert tile) plus n_sample first,
+    last, ragged and random tokens; otherwise on n_sample such tokens (all when T <= n_sample)."""
     wl = gen.WORKLOADS[name]
     log(f"[{name}] generating layer")
     lw = gen.make_layer(wl, 0)
@@ -31,7 +39,7 @@ def _workload_case(name, n_sample, ws):
     x = gen.make_tokens(wl)
     out = run_forward(dl, upload_tokens(x), ws)
     torch.cuda.synchronize()
-    sample = sample_tokens(wl.T, n_sample)
+    sample = f"tiles:{TILE_ROWS},{n_sample}" if tiles else sample_tokens(wl.T, n_sample)
     return check_block(lw, x, wl.act, out, sample=sample, label=name)
 
 
@@ -63,18 +71,20 @@ def test_120b_verify_batches(T, ws, layer120):
 
 
 @pytest.mark.timeout(600)
-def test_prefill_t4096_sampled(ws):
-    _workload_case("prefill_t4096", 96, ws)
+def test_prefill_t4096_every_tile(ws):
+    _workload_case("prefill_t4096", 96, ws, tiles=True)
 
 
 @pytest.mark.timeout(900)
-def test_prefill_t16384_sampled(ws):
-    _workload_case("prefill_t16384", 96, ws)
+def test_prefill_t16384_every_tile(ws):
+    _workload_case("prefill_t16384", 96, ws, tiles=True)
 
 
-def test_prefill_mxfp4_t16384_sampled(ws):
-    # 4-bit records decoded once to bf16 for the tile GEMMs (large batches)
-    _workload_case("prefill_mxfp4_t16384", 64, ws)
+@pytest.mark.timeout(900)
+def test_prefill_mxfp4_t16384_every_tile(ws):
+    # MXFP4 records on the block-scaled MFMA (z as MXFP8 plus an MXFP4 residual), the default
+    # path for MXFP4 batches from 96 tokens
+    _workload_case("prefill_mxfp4_t16384", 64, ws, tiles=True)
 
 
 SMALL = gen.Shape(hidden=256, latent=192, n_experts=24, top_k=3, ffn=128, shared_ffn=64)
