@@ -125,8 +125,8 @@ Layout plan(const Dims& d, int T) {
     lo.fused_router = !d.f32 && small_proj_fits(T, d.H);
     // expert groups take the logits from x and the folded router for every batch (two halves)
     const bool halves = lo.fused_router || d.G > 1;
-    lo.BM = expert_tile_rows(lo.stream_path);
-    lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path);
+    lo.BM = expert_tile_rows(lo.stream_path, lo.mx_path);
+    lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path, lo.mx_path);
     lo.Hs = std::max(d.F, d.Fs);
     lo.R = T * d.k + (has_shared ? T : 0);
     const size_t nb = (size_t)perm_blocks(T);

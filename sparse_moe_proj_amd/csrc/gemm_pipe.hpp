@@ -218,10 +218,13 @@ __device__ __forceinline__ void pipe_prologue(const PipeCopies<S>& c, int nk, ui
 // The K loop of one tile whose prologue stages are in flight: for stage kt + s, wait for this
 // wave's copies of it, barrier (every wave's copies landed and every wave is done with the
 // previous stage), refill the buffer the previous stage used with stage kt + s + NS - 1,
-// multiply stage kt + s.  Accumulates into acc (zeroed here).
+// multiply stage kt + s.  Accumulates into acc (zeroed here).  mrows: the tile's rows that hold
+// data (the others only pad it): a wave multiplies only its 32-row blocks that reach into them,
+// and a wave with none reads no fragments (it still takes part in the copies and barriers).
 template <class S, class P>
 __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x16 (&acc)[S::kMB][S::kNB],
-                                            uint4* st0, uint4* st1, uint4* st2, uint4* st3, int wave, int lane) {
+                                            uint4* st0, uint4* st1, uint4* st2, uint4* st3, int wave, int lane,
+                                            int mrows) {
     constexpr int NS = S::kNS;
     constexpr int LPS = S::kLoadsPerStage;
     static_assert(NS >= 2 && NS <= 4, "two to four stages");
@@ -233,7 +236,9 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
 
     const int fr = lane & 31;
     const int fq = lane >> 5;
+    const int nvb = min(S::kMB, max(0, (mrows - wm * S::kWM + 31) / 32));  // 32-row blocks with data
     auto compute = [&](const uint4* buf) {
+        if (nvb == 0) return;
         const uint32_t A = lds_addr(buf);
         const uint32_t B = A + S::kBM * 8 * 16;
 #pragma unroll
@@ -248,8 +253,9 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
             lds_read_frags<S::kMB, S::kNB>(aa, ba, af, bfv);
 #pragma unroll
             for (int i = 0; i < S::kMB; ++i)
+                if (i < nvb)
 #pragma unroll
-                for (int j = 0; j < S::kNB; ++j) acc[i][j] = mfma32(af[i], bfv[j], acc[i][j]);
+                    for (int j = 0; j < S::kNB; ++j) acc[i][j] = mfma32(af[i], bfv[j], acc[i][j]);
         }
     };
 
@@ -297,8 +303,9 @@ __global__ __launch_bounds__(S::kThreads) void pipe_gemm_kernel(const P p) {
     const PipeCopies<S> c = pipe_copies<S>(p, ctx, wave, lane);
     pipe_prologue<S, P>(c, nk, st0, st1, st2, wave);
     f32x16 acc[S::kMB][S::kNB];
-    pipe_k_loop<S, P>(c, nk, acc, st0, st1, st2, st3, wave, lane);
+    pipe_k_loop<S, P>(c, nk, acc, st0, st1, st2, st3, wave, lane, p.valid_rows(ctx));
     const auto prep = p.template prep<S::kMB>(ctx, rb, lane);
+    __syncthreads();  // a problem's prep may stage rows in LDS for the store
     p.template store<S::kMB, S::kNB>(ctx, acc, prep, rb, cb, lane);
 }
 
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(S::kThreads) void pipe_gemm_persistent(const P p, i
     pipe_prologue<S, P>(c, nk, st0, st1, st2, wave);
     f32x16 acc[S::kMB][S::kNB];
     while (true) {
-        pipe_k_loop<S, P>(c, nk, acc, st0, st1, st2, st3, wave, lane);
+        pipe_k_loop<S, P>(c, nk, acc, st0, st1, st2, st3, wave, lane, p.valid_rows(ctx));
         const auto prep = p.template prep<S::kMB>(ctx, rb, lane);
         int ln = l + nwx;
         typename P::Ctx nctx;

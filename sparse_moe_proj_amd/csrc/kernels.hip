@@ -459,6 +459,40 @@ using TileL = TileShape<LMOE_TILE_M, LMOE_TILE_N, 2, 2>;
 #define LMOE_PIPE 1
 #endif
 using PipeL = PipeShape<LMOE_PIPE_M, LMOE_PIPE_N, LMOE_PIPE_NS, LMOE_PIPE_WR, LMOE_PIPE_WC>;
+// The dense projections of large batches (D, U): every tile is full (no segments), so they may
+// take a taller tile than the experts' work list allows.
+#ifndef LMOE_PROJ_PIPE_M
+#define LMOE_PROJ_PIPE_M LMOE_PIPE_M
+#endif
+#ifndef LMOE_PROJ_PIPE_N
+#define LMOE_PROJ_PIPE_N LMOE_PIPE_N
+#endif
+#ifndef LMOE_PROJ_PIPE_NS
+#define LMOE_PROJ_PIPE_NS LMOE_PIPE_NS
+#endif
+#ifndef LMOE_PROJ_PIPE_WR
+#define LMOE_PROJ_PIPE_WR LMOE_PIPE_WR
+#endif
+#ifndef LMOE_PROJ_PIPE_WC
+#define LMOE_PROJ_PIPE_WC LMOE_PIPE_WC
+#endif
+using PipeP = PipeShape<LMOE_PROJ_PIPE_M, LMOE_PROJ_PIPE_N, LMOE_PROJ_PIPE_NS, LMOE_PROJ_PIPE_WR, LMOE_PROJ_PIPE_WC>;
+// Big tiles of the large-batch bf16 expert GEMMs: 256 x 256 with 8 waves of 128 x 64, two stages
+// (128 KB of LDS).  A 128 x 256 tile moves 48 KB from L2 into LDS per 64-column stage for 4.2
+// MFLOP, about 100 GB/s per CU at the matrix cores' rate; the 256 x 256 tile halves the bytes per
+// flop.  Segments take whole big tiles and put their last rows in a 128-row tile when at most 128
+// are left (so the padding stays that of 128-row tiles).
+#ifndef LMOE_BIG_TILES
+#define LMOE_BIG_TILES 1
+#endif
+#ifndef LMOE_BIG_WR
+#define LMOE_BIG_WR 2
+#endif
+#ifndef LMOE_BIG_WC
+#define LMOE_BIG_WC 4
+#endif
+using PipeB = PipeShape<256, LMOE_PIPE_N, 2, LMOE_BIG_WR, LMOE_BIG_WC>;
+static_assert(PipeB::kBN == PipeL::kBN, "big and small tiles cover the same columns per tile");
 
 // Persistent launch: at most LMOE_STREAM_GRID workgroups walk max_tiles x row-group items.
 template <int W, int KS, int NMAT, class P, int CH0 = kChunk>
@@ -640,11 +674,22 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
         return launch_stream<kPW, kPKS, 1, StreamProj, kProjChunk>(StreamProj{x, W, T, N, K, mode, out32, out16},
                                                                    (int)cdiv(T, 16), N, s);
     if (LMOE_PIPE_PROJ) {
-        PipeProj<PipeL> p{{x, W, T, N, K, mode, out32, out16, out16lo}};
-        const int nn = (int)cdiv(N, PipeL::kBN);
-        auto k = pipe_gemm_persistent<PipeL, PipeProj<PipeL>>;
-        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeL::kThreads), (long)cdiv(T, PipeL::kBM) * nn)), dim3(PipeL::kThreads), 0,
-                           s, p, nn);
+        // 256-row tiles halve the bytes per flop but come in half as many: take them when the
+        // rounds of tiles over the CUs, weighted by a 256-row tile's measured cost (1.67 times a
+        // 128-row tile's: 102 vs 61 us per round at 16384 x 1792 x 2560), come out lower
+        const long nn = cdiv(N, PipeP::kBN), cus = cu_count();
+        const long r1 = cdiv(cdiv(T, PipeP::kBM) * nn, cus), r2 = cdiv(cdiv(T, PipeB::kBM) * nn, cus);
+        if (PipeB::kBN == PipeP::kBN && PipeB::kBM > PipeP::kBM && 167 * r2 < 100 * r1) {
+            PipeProj<PipeB> p{{x, W, T, N, K, mode, out32, out16, out16lo}};
+            auto k = pipe_gemm_persistent<PipeB, PipeProj<PipeB>>;
+            hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeB::kThreads), (long)cdiv(T, PipeB::kBM) * nn)),
+                               dim3(PipeB::kThreads), 0, s, p, (int)nn);
+            return last();
+        }
+        PipeProj<PipeP> p{{x, W, T, N, K, mode, out32, out16, out16lo}};
+        auto k = pipe_gemm_persistent<PipeP, PipeProj<PipeP>>;
+        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeP::kThreads), (long)cdiv(T, PipeP::kBM) * nn)),
+                           dim3(PipeP::kThreads), 0, s, p, (int)nn);
         return last();
     }
     TileProj<TileL> p{x, W, T, N, K, mode, out32, out16, out16lo};
@@ -738,10 +783,15 @@ hipError_t launch_topk_permute(const float* logits, int T, int E, int k, int32_t
     return last();
 }
 
-int expert_tile_rows(bool stream_path) { return stream_path ? 16 : (LMOE_PIPE ? PipeL::kBM : TileL::kBM); }
+int expert_tile_rows(bool stream_path, bool mx_path) {
+    if (stream_path) return 16;
+    if (mx_path) return PipeL::kBM;  // the block-scaled kernels' tile rows (checked with their shapes)
+    if (!LMOE_PIPE) return TileL::kBM;
+    return LMOE_PIPE_PERSIST && LMOE_BIG_TILES ? PipeB::kBM : PipeL::kBM;
+}
 
-int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path) {
-    const long BM = expert_tile_rows(stream_path);
+int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path, bool mx_path) {
+    const long BM = expert_tile_rows(stream_path, mx_path);
     const long tk = (long)T * k;
     return (int)(cdiv(tk, BM) + std::min<long>(E, tk) + (has_shared ? cdiv(T, BM) : 0));
 }
@@ -910,7 +960,7 @@ static_assert(MxUpL::kBM == PipeL::kBM && MxDnL::kBM == PipeL::kBM, "the work li
 hipError_t launch_experts_mx(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
     if (!a.z8 || !a.z8s || !a.z4 || !a.z4s || !a.h8 || !a.h8s || a.fmt != 1 || a.L % 128 || a.F % 128)
         return hipErrorInvalidValue;
-    const int nsh = a.shared ? (int)cdiv(a.T, PipeL::kBM) : 0;
+    const int nsh = a.shared ? (int)cdiv(a.T, MxUpL::kBM) : 0;
     SegSpace rs = seg;
     rs.part = 1;
     rs.nsh = nsh;
@@ -986,6 +1036,24 @@ hipError_t launch_experts_bf16(const ExpertArgs& a, hipStream_t s, StageEvents& 
     const float* tsc = a.fmt != 0 ? a.deq_ts : nullptr;
     const int Fmax = std::max(a.F, a.Fs);
     const uint16_t* sh = static_cast<const uint16_t*>(a.shared);
+    if (LMOE_PIPE && LMOE_PIPE_PERSIST && LMOE_BIG_TILES) {  // 256-row tiles (expert_tile_rows)
+        const int nn_up = (int)cdiv(Fmax, PipeB::kBN / 2), nn_dn = (int)cdiv(a.L, PipeB::kBN);
+        auto ku = pipe_gemm_persistent<PipeB, PipeUp<PipeB>>;
+        hipLaunchKernelGGL(ku, dim3(std::min<long>(resident_blocks(ku, PipeB::kThreads), (long)a.max_tiles * nn_up)),
+                           dim3(PipeB::kThreads), 0, s, PipeUp<PipeB>{{seg, a.z16, ex, sh, rec, a.L, a.F, a.Fs, a.Hs, a.H, tsc}},
+                           nn_up);
+        hipError_t err = last();
+        if (err != hipSuccess) return err;
+        ev.end(kStageUp);
+        ev.begin(kStageDown);
+        auto kd = pipe_gemm_persistent<PipeB, PipeDown<PipeB>>;
+        hipLaunchKernelGGL(kd, dim3(std::min<long>(resident_blocks(kd, PipeB::kThreads), (long)a.max_tiles * nn_dn)),
+                           dim3(PipeB::kThreads), 0, s,
+                           PipeDown<PipeB>{{seg, a.H, ex, sh, rec, a.L, a.F, a.Fs, a.Hs, a.Y, tsc}}, nn_dn);
+        if ((err = last()) != hipSuccess) return err;
+        ev.end(kStageDown);
+        return hipSuccess;
+    }
     if (LMOE_PIPE) {
         PipeUp<PipeL> up{{seg, a.z16, ex, sh, rec, a.L, a.F, a.Fs, a.Hs, a.H, tsc}};
         const int nn_up = (int)cdiv(Fmax, PipeL::kBN / 2);

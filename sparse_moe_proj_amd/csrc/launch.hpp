@@ -133,8 +133,10 @@ hipError_t launch_proj_partials_kgroups(const float* xpart, int G, const uint16_
 hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                                 uint16_t* out16, hipStream_t s);
 
-int expert_tile_rows(bool stream_path);
-int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path);
+// Rows of the expert work list's tiles: 16 (small batches), 128 (the block-scaled MXFP4 kernels),
+// else the rows of the large-batch bf16 GEMM tiles (256).
+int expert_tile_rows(bool stream_path, bool mx_path);
+int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path, bool mx_path);
 
 // Routing done inside the small-batch gate/up launch (T <= 64): the logits (hi half, and the lo
 // half of a folded router or null) and where the routing outputs go.

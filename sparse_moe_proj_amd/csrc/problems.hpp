@@ -697,6 +697,7 @@ struct PipeProj : TileProj<S> {
     using B = TileProj<S>;
     static constexpr bool kAPacked = false, kBPacked = false;
     __device__ int m_tiles() const { return (B::M + S::kBM - 1) / S::kBM; }
+    __device__ int valid_rows(const typename B::Ctx& c) const { return min(S::kBM, B::M - c.m0); }
     __device__ int k_stages(const typename B::Ctx&) const { return B::K / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
         return reinterpret_cast<const uint8_t*>(B::x + (size_t)c.m0 * B::K);
@@ -727,6 +728,7 @@ struct PipeUp : TileUp<S> {
     using B = TileUp<S>;
     static constexpr bool kAPacked = false, kBPacked = true;
     __device__ int m_tiles() const { return B::seg.count(); }
+    __device__ int valid_rows(const typename B::Ctx& c) const { return c.nrows; }
     __device__ int k_stages(const typename B::Ctx&) const { return B::L / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx&) const { return reinterpret_cast<const uint8_t*>(B::z16); }
     __device__ const uint8_t* b_base(const typename B::Ctx& c) const { return reinterpret_cast<const uint8_t*>(c.g); }
@@ -759,6 +761,7 @@ struct PipeDown : TileDown<S> {
     using B = TileDown<S>;
     static constexpr bool kAPacked = false, kBPacked = true;
     __device__ int m_tiles() const { return B::seg.count(); }
+    __device__ int valid_rows(const typename B::Ctx& c) const { return c.nrows; }
     __device__ int k_stages(const typename B::Ctx& c) const { return c.F / 64; }
     __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
         return reinterpret_cast<const uint8_t*>(B::H + (size_t)c.row0 * B::Hs);
@@ -772,21 +775,36 @@ struct PipeDown : TileDown<S> {
         const int nb = min(c.n0 + (i >> 1) * 16, B::L - 16) >> 4;
         return packed_off(nb, i, c.F, lane);
     }
-    // destination row of every accumulator row this lane holds (-1: none), read before the store
+    // Destination row of every accumulator row (-1: none), read before the store (the next tile's
+    // copies are issued in between, and a wait for a later global load would wait for them too).
+    // Wave tiles of up to 64 rows keep this lane's rows in registers; taller ones (the 256-row
+    // tiles) keep the tile's rows in LDS, written by the workgroup and read after the barrier that
+    // the persistent kernel places between prep and store.
+    static constexpr bool kPrepLds = S::kMB > 2;
+    __device__ static int* prep_rows() {
+        __shared__ int rows[S::kBM];
+        return rows;
+    }
     template <int MB>
     struct PrepT {
-        int drow[MB][16];
+        int drow[kPrepLds ? 1 : MB][16];
     };
     template <int MB>
     __device__ __forceinline__ PrepT<MB> prep(const typename B::Ctx& c, int rb, int lane) const {
         PrepT<MB> q;
+        if constexpr (kPrepLds) {
+            int* rows = prep_rows();
+            for (int m = threadIdx.x; m < S::kBM; m += S::kThreads)
+                rows[m] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
+        } else {
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+            for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = rb + i * 32 + frag32_row(r, lane);
-                q.drow[i][r] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const int m = rb + i * 32 + frag32_row(r, lane);
+                    q.drow[i][r] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
+                }
+        }
         return q;
     }
     template <int MB, int NB>
@@ -795,7 +813,8 @@ struct PipeDown : TileDown<S> {
         static_for<MB>([&](auto i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int drow = q.drow[i][r];  // a dropped slot (-1) owns no output row
+                // a dropped slot (-1) owns no output row
+                const int drow = kPrepLds ? prep_rows()[rb + i * 32 + frag32_row(r, lane)] : q.drow[kPrepLds ? 0 : i][r];
                 if (drow >= 0) {
                     const size_t dst = (size_t)drow * B::L;
                     static_for<NB>([&](auto j) {

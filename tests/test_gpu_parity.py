@@ -90,7 +90,7 @@ def test_prefill_mxfp4_t16384_every_tile(ws):
 SMALL = gen.Shape(hidden=256, latent=192, n_experts=24, top_k=3, ffn=128, shared_ffn=64)
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 17, 100, 300])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 100, 300, 700, 1500])
 def test_small_bf16_ragged(T, ws):
     wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
     dl = DeviceLayer(lw, act="bf16")
