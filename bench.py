@@ -384,7 +384,7 @@ def measure(wl, steps, warmup, rotate, profile_stages=True, copies=None, T=None,
             fwd(copies[r])
         graphs.append(g)
     torch.cuda.synchronize()
-    gt = graph_timing(lambda i: graphs[i % rotate].replay(), max(graph_reps, 100))
+    gt = graph_timing(lambda i: graphs[i % rotate].replay(), max(graph_reps, 100))  # >= 100 replays
     return dict(ms_per_step=ms_per_step, tok_s=T / (ms_per_step / 1e3), up_ms=up_ms, counts=counts,
                 stages_us=stages_us, weight_bytes_per_copy=base.nbytes(), graph=gt)
 
@@ -617,7 +617,8 @@ def main():
     ap.add_argument("--workload", default="decode_t8")
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--graph-samples", type=int, default=100,
-                    help="timed samples of HIP-graph replays (groups of about 1 ms; at least 100 replays)")
+                    help="timed samples of HIP-graph replays (groups of about 1 ms; at least 100 replays); "
+                         "0 skips the graph timing (profiler passes)")
     ap.add_argument("--secondary", default="prefill_t16384", help="second workload line ('' = none)")
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -644,7 +645,8 @@ def main():
         args.rotate = 1
     else:
         copies = layer_copies(wl, args.rotate)
-        m = measure(wl, args.steps, args.warmup, args.rotate, copies=copies, graph_reps=args.graph_samples)
+        m = measure(wl, args.steps, args.warmup, args.rotate, copies=copies, graph_reps=args.graph_samples,
+                    graphs=args.graph_samples > 0)
     peaks = None
     if not args.no_peaks:
         peaks = measure_peaks()
@@ -696,7 +698,7 @@ def main():
         del m
         torch.cuda.empty_cache()
         wl2 = gen.WORKLOADS[args.secondary]
-        m2 = measure(wl2, args.secondary_steps, 3, 2, graph_reps=args.graph_samples)
+        m2 = measure(wl2, args.secondary_steps, 3, 2, graph_reps=args.graph_samples, graphs=args.graph_samples > 0)
         c2 = m2["counts"]
         out["secondary"] = {
             "workload": wl2.name, "T": wl2.T, "value": round(m2["tok_s"], 1), "unit": "tok/s per layer",
