@@ -301,7 +301,7 @@ def layer_copies(wl, rotate):
     t0 = time.time()
     lw = gen.make_layer(wl, 0)
     log(f"[bench] {wl.name}: generated layer in {time.time() - t0:.1f}s")
-    base = DeviceLayer(lw, act=wl.act)
+    base = DeviceLayer(lw, act=wl.act, mx_mfma_min_t=MX_MFMA_MIN_T)
     del lw
     return [base] + [base.clone() for _ in range(rotate - 1)]
 
@@ -405,7 +405,7 @@ def measure_stack(wl, steps, warmup):
     layers = []
     for l in range(wl.layers):
         lw = gen.make_layer(wl, l, experts=banks[gen.expert_bank(wl, l)] if wl.expert_banks else None)
-        layers.append(DeviceLayer(lw, act="bf16"))
+        layers.append(DeviceLayer(lw, act="bf16", mx_mfma_min_t=MX_MFMA_MIN_T))
     del banks
     log(f"[bench] {wl.name}: {wl.layers} layers generated and uploaded in {time.time() - t0:.1f}s")
     T = wl.T
@@ -566,10 +566,15 @@ def roofline_hbm(counts, up_ms, layer_s, peaks=None, traffic=None):
             "layer_frac_of_measured": round(layer_gbs / meas, 4) if meas else None}
 
 
+# lmoe_config.mx_mfma_min_t of every layer the benchmark builds (--mx-mfma-min-t)
+MX_MFMA_MIN_T = 0
+
+
 def mx_mfma_path(wl):
     """Whether the workload's expert products take the block-scaled MXFP8 x MXFP4 MFMA kernels."""
-    min_t = int(os.environ.get("LMOE_MX_MIN_T", "0") or 0) or MX_MIN_T
-    return wl.expert == "mxfp4" and wl.T >= max(min_t, 17) and os.environ.get("LMOE_MX_MFMA", "1")[:1] != "0"
+    if wl.expert != "mxfp4" or MX_MFMA_MIN_T < 0:
+        return False
+    return wl.T >= max(MX_MFMA_MIN_T or MX_MIN_T, 65)
 
 
 def roofline_mfma(counts, up_ms, layer_s, peaks=None, wl=None):
@@ -624,6 +629,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the streaming-read and MFMA-loop measurements")
+    ap.add_argument("--mx-mfma-min-t", type=int, default=0,
+                    help="lmoe_config.mx_mfma_min_t of MXFP4 layers (0: the library's default, -1: off)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (calibrates HBM traffic counters)")
     ap.add_argument("--tsweep", default="",
@@ -634,6 +641,8 @@ def main():
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    global MX_MFMA_MIN_T
+    MX_MFMA_MIN_T = args.mx_mfma_min_t
     import torch
     import lmoe_data as gen
     assert torch.cuda.is_available(), "bench.py needs a GPU"

@@ -67,7 +67,9 @@
  *     Launch failures reported by the HIP runtime map to LMOE_ERR_HIP.  Faults that
  *     happen while kernels run surface at the caller's next synchronisation.
  *   - NaN/Inf inputs are not checked; outputs are then undefined, but every kernel stays
- *     within the bounds of the buffers described here.
+ *     within the bounds of the buffers described here.  Batches of up to 64 tokens with 4-bit
+ *     routed experts carry z and the SwiGLU rows in fp16 (11 significant bits) for those
+ *     experts: magnitudes above 65504 saturate there (they stay finite but lose their size).
  *   - For identical inputs, configuration, T and device, outputs are bitwise identical
  *     (no floating-point atomics, fixed reduction orders).
  *
@@ -117,6 +119,12 @@ typedef struct {
     int32_t dense_dtype;  /* lmoe_dtype of D, U, Wr and the shared expert */
     int32_t expert_dtype; /* lmoe_dtype of the routed expert records */
     int32_t groups;       /* G: expert groups with their own D/U pair (0 or 1: one pair per layer) */
+    /* MXFP4 routed experts: the smallest batch that takes the block-scaled MFMA kernels (CDNA4
+     * v_mfma_scale_f32_32x32x64_f8f6f4 with the records as stored and MXFP8 activations).
+     * 0 = 96 (the measured crossover against the weight-streaming kernels); -1 = never (batches of
+     * 65 .. 383 tokens then take the weight-streaming kernels and larger ones decode the touched
+     * records to bf16); values from 1 to 64 count as 65.  Ignored for other expert dtypes. */
+    int32_t mx_mfma_min_t;
 } lmoe_config;
 
 typedef struct {
@@ -148,7 +156,10 @@ typedef enum {
 
 typedef struct {
     /* prenorm = 1: x is an fp32 residual stream h [T][hidden]; the block input is
-     * bf16(RMSNorm(h)) with unit gain and eps 1e-6 (requires act BF16). */
+     * bf16(RMSNorm(h)) with unit gain and eps 1e-6 (requires act BF16).  A learned gain g is
+     * not an argument: it scales the columns of D (D diag(g)), so a caller folds it into D (and
+     * then into the folded router) once; the only difference is where the block input is
+     * rounded to bf16 (before the gain instead of after it). */
     int32_t prenorm;
     /* residual = 1: y is fp32 [T][hidden] and is updated in place, y += block output.
      * With prenorm and residual both set, x and y may be the same buffer. */
@@ -173,13 +184,12 @@ size_t lmoe_expert_record_bytes(const lmoe_config* cfg, int32_t shared);
 
 /* Workspace bytes lmoe_forward needs for T tokens (monotone in T).  MXFP4 layers take the
  * block-scaled MFMA kernels (CDNA4 v_mfma_scale_*_f8f6f4, the records used as stored) from
- * T = 96 (65 <= T < 96: the weight-streaming kernels); the workspace then holds z as MXFP8 plus an
- * MXFP4 residual and H as MXFP8 (about T * (1.56 * latent * groups + 1.03 * top_k * ffn) bytes
- * more).  NVFP4 layers with T >= 384, and MXFP4 layers with T >= 384 when the environment
- * variable LMOE_MX_MFMA is "0", decode the records of the experts with tokens to bf16 and the
- * workspace includes n_experts such records (3 * ffn * latent * 2 bytes each).  LMOE_MX_MFMA and
- * LMOE_MX_MIN_T (the MXFP4 threshold, for measurements) are read by this query and by
- * lmoe_forward: keep them unchanged between the two. */
+ * cfg->mx_mfma_min_t tokens (default 96; below it, from 65 tokens, the weight-streaming kernels);
+ * the workspace then holds z as MXFP8 plus an MXFP4 residual and H as MXFP8 (about
+ * T * (1.56 * latent * groups + 1.03 * top_k * ffn) bytes more).  NVFP4 layers with T >= 384, and
+ * MXFP4 layers with T >= 384 when mx_mfma_min_t is -1, decode the records of the experts with
+ * tokens to bf16 and the workspace includes n_experts such records (3 * ffn * latent * 2 bytes
+ * each).  The result depends on the configuration and T only. */
 lmoe_status lmoe_workspace_bytes(const lmoe_config* cfg, int32_t T, size_t* bytes);
 
 /* Workspace bytes lmoe_permute needs for T tokens. */
@@ -229,7 +239,9 @@ lmoe_status lmoe_route(const lmoe_config* cfg, const lmoe_weights* weights, cons
 
 /*
  * Token -> expert permutation used to group each expert's tokens into one contiguous
- * segment.  Flat slot index f = t*top_k + s.
+ * segment.  The pages do not describe this step: it is this library's own (the grouping that
+ * its expert kernels read), exported so that it can be checked on its own against a stable
+ * sort.  Flat slot index f = t*top_k + s.
  *   ids     [T][top_k] int32 in: expert of each slot; the ids of one token must be distinct.
  *   offsets [n_experts + 1] int32 out: offsets[e] = first position of expert e's segment
  *           (exclusive prefix sum of the per-expert counts), offsets[n_experts] = number of

@@ -32,7 +32,7 @@ class LmoeError(RuntimeError):
 
 class lmoe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("hidden", "latent", "n_experts", "top_k", "ffn", "shared_ffn",
-                                              "act_dtype", "dense_dtype", "expert_dtype", "groups")]
+                                              "act_dtype", "dense_dtype", "expert_dtype", "groups", "mx_mfma_min_t")]
 
 
 class lmoe_weights(ctypes.Structure):
@@ -107,9 +107,11 @@ def _stream(s):
     return s.cuda_stream
 
 
-def make_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, act="bf16", dense="bf16", expert="bf16", groups=1):
+def make_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, act="bf16", dense="bf16", expert="bf16", groups=1,
+                mx_mfma_min_t=0):
+    """lmoe_config; mx_mfma_min_t: 0 = the library's default (96), -1 = no block-scaled MFMA path."""
     return lmoe_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, DTYPES[act], DTYPES[dense], DTYPES[expert],
-                       int(groups))
+                       int(groups), int(mx_mfma_min_t))
 
 
 def make_weights(D, U, Wr, br, shared, experts, Gr=None):

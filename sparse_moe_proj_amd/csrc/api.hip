@@ -2,6 +2,7 @@
 // Everything here runs on the host and only enqueues work on the caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdint.h>
 #include <stdlib.h>
 
 #include <mutex>
@@ -37,6 +38,7 @@ struct Dims {
     bool f32;  // fp32 storage end to end
     bool mx;   // 4-bit routed experts (MXFP4 or NVFP4)
     int fmt;   // routed expert records: 0 bf16 (or fp32), 1 MXFP4, 2 NVFP4
+    int mx_min_t;  // MXFP4: smallest batch of the block-scaled MFMA kernels (INT32_MAX: never)
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -75,6 +77,10 @@ lmoe_status check_config(const lmoe_config* cfg, Dims& d) {
     d.Eg = d.E / d.G;
     d.Lz = d.G * d.L;
     if ((long)d.H * d.Lz > (1L << 30)) return fail(LMOE_ERR_SHAPE, "D or U exceeds 2^30 elements");
+    if (cfg->mx_mfma_min_t < -1)
+        return fail(LMOE_ERR_SHAPE, "mx_mfma_min_t must be -1, 0 or a batch size (got %d)", cfg->mx_mfma_min_t);
+    d.mx_min_t = cfg->mx_mfma_min_t < 0 ? INT32_MAX
+                                        : std::max(cfg->mx_mfma_min_t == 0 ? kMxMinT : cfg->mx_mfma_min_t, kDecodeMaxT + 1);
     return LMOE_OK;
 }
 
@@ -95,19 +101,6 @@ struct Layout {
     int max_tiles, BM, Hs, R;
 };
 
-bool mx_mfma_enabled() {
-    const char* v = getenv("LMOE_MX_MFMA");
-    return !(v && v[0] == '0');
-}
-
-// Smallest batch for the block-scaled MFMA path of MXFP4 layers (LMOE_MX_MIN_T overrides it,
-// for measurements; never below kStreamMaxT + 1).
-int mx_min_t() {
-    const char* v = getenv("LMOE_MX_MIN_T");
-    const int t = v ? atoi(v) : kMxMinT;
-    return std::max(t > 0 ? t : kMxMinT, kStreamMaxT + 1);
-}
-
 Layout plan(const Dims& d, int T) {
     Layout lo{};
     const size_t act = d.f32 ? 4 : 2;
@@ -115,9 +108,9 @@ Layout plan(const Dims& d, int T) {
     lo.decode_path = !d.f32 && decode_fits(T, d.L, d.F, d.Fs);
     // 4-bit records stream through the weight-streaming kernels up to kDequantMinT tokens; larger
     // batches decode the touched records to bf16 once and take the tile GEMMs
-    // MXFP4 takes the block-scaled MFMA kernels from mx_min_t() tokens unless LMOE_MX_MFMA=0 asks
-    // for the decode to bf16 (from kDequantMinT, as NVFP4)
-    lo.mx_path = d.fmt == 1 && !lo.decode_path && mx_mfma_enabled() && T >= mx_min_t();
+    // MXFP4 takes the block-scaled MFMA kernels from d.mx_min_t tokens (never: the decode to bf16
+    // from kDequantMinT, as NVFP4)
+    lo.mx_path = d.fmt == 1 && !lo.decode_path && T >= d.mx_min_t;
     const bool deq = d.mx && !lo.decode_path && !lo.mx_path && T >= kDequantMinT;
     const bool big4 = lo.mx_path || deq;
     lo.deq_path = deq;

@@ -145,20 +145,25 @@ __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) * f16x2{k, k});
 }
 
-// 8 bf16 -> 8 fp16 (exact for values in fp16's normal range).
+// float -> fp16 (round to nearest even), magnitudes beyond the largest finite fp16 (65504)
+// saturating to it instead of becoming infinities.  The 4-bit small-batch kernels carry z and
+// the SwiGLU rows in fp16; activations past that range lose their size but stay finite.
+__device__ __forceinline__ _Float16 f16_sat(float v) { return (_Float16)fminf(fmaxf(v, -65504.f), 65504.f); }
+
+// 8 bf16 -> 8 fp16 (exact for values in fp16's normal range; saturating beyond it).
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
     uint32_t o[4];
     const uint32_t in[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        o[i] = __builtin_bit_cast(uint32_t, f16x2{(_Float16)__uint_as_float(in[i] << 16),
-                                                  (_Float16)__uint_as_float(in[i] & 0xFFFF0000u)});
+        o[i] = __builtin_bit_cast(uint32_t, f16x2{f16_sat(__uint_as_float(in[i] << 16)),
+                                                  f16_sat(__uint_as_float(in[i] & 0xFFFF0000u))});
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// fp32 pair -> fp16 pair bits (round to nearest even).
+// fp32 pair -> fp16 pair bits (round to nearest even, saturating).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)lo, (_Float16)hi});
+    return __builtin_bit_cast(uint32_t, f16x2{f16_sat(lo), f16_sat(hi)});
 }
 
 // ----------------------------------------------------------------------------------------------

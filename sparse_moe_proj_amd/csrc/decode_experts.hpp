@@ -272,7 +272,7 @@ __device__ __forceinline__ void gu_split_run(const DecodeExperts<Q>& d, int firs
                 }
                 const float h = silu(g * c.tg) * (u * c.tu);
                 d.H[(size_t)(c.row0 + sr) * d.Hs + c.f0 + fr] =
-                    R::kF16 ? __builtin_bit_cast(uint16_t, (_Float16)h) : (uint16_t)f2bf(h);
+                    R::kF16 ? __builtin_bit_cast(uint16_t, f16_sat(h)) : (uint16_t)f2bf(h);
             }
         }
         buf ^= 1;

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
                     if (p.mode == 0) {
                         p.out32[o] = v;
                         p.out16[o] = (uint16_t)f2bf(v);
-                        if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                        if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, f16_sat(v));
                     } else if (p.mode == 1) {
                         p.out16[o] = (uint16_t)f2bf(v);
                     } else if (p.mode == 3) {
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(64 * W) void rows_proj_kernel(const RowsProj p) {
                         if (p.mode == 0) {
                             p.out32[o] = v;
                             p.out16[o] = (uint16_t)f2bf(v);
-                            if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                            if (p.out16h) p.out16h[o] = __builtin_bit_cast(uint16_t, f16_sat(v));
                         } else if (p.mode == 1) {
                             p.out16[o] = (uint16_t)f2bf(v);
                         } else {

@@ -48,9 +48,10 @@ class DeviceLayer:
     """One layer's weights resident in HBM (tensors kept alive by this object).  Expert records
     are uploaded row-major and packed on the device (fp32 records stay row-major).  pack=False
     keeps them as given: only for callers that use the routing entry points alone.  With bf16
-    dense weights the folded router is computed too unless fold=False."""
+    dense weights the folded router is computed too unless fold=False.  mx_mfma_min_t goes to
+    lmoe_config (MXFP4 layers: 0 = default threshold of the block-scaled MFMA path, -1 = off)."""
 
-    def __init__(self, lw=None, act="bf16", device="cuda", _copy_of=None, pack=True, fold=True):
+    def __init__(self, lw=None, act="bf16", device="cuda", _copy_of=None, pack=True, fold=True, mx_mfma_min_t=0):
         self.Gr = None
         if _copy_of is not None:
             src = _copy_of
@@ -67,8 +68,9 @@ class DeviceLayer:
             self.shared = to_device(lw.shared, device)
             self.experts = to_device(lw.experts, device)
         s = self.shape
+        mx_min = src.cfg.mx_mfma_min_t if _copy_of is not None else mx_mfma_min_t
         self.cfg = make_config(s.hidden, s.latent, s.n_experts, s.top_k, s.ffn, s.shared_ffn, self.act, self.dense,
-                               self.expert, getattr(s, "groups", 1))
+                               self.expert, getattr(s, "groups", 1), mx_min)
         if _copy_of is None and pack and self.expert != "f32":
             self.experts = pack_records(self.cfg, self.experts, False)
             if self.shared is not None:

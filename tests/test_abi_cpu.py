@@ -63,12 +63,12 @@ def test_workspace_sizes_monotone():
 
 @pytest.mark.parametrize("expert", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("mx_mfma", ["1", "0"])
-def test_workspace_monotone_4bit_paths(expert, mx_mfma, monkeypatch):
+def test_workspace_monotone_4bit_paths(expert, mx_mfma):
     """4-bit layers change kernels at 65 (small-batch -> weight streaming), at 96 (MXFP4: the
     block-scaled MFMA path, whose MXFP8 activations need workspace) and at 384 (the decode of the
-    records to bf16: n_experts decoded records); the size query stays monotone in T across all."""
-    monkeypatch.setenv("LMOE_MX_MFMA", mx_mfma)
-    c = lm.make_config(2560, 1792, 512, 10, 640, 640, "bf16", "bf16", expert)
+    records to bf16: n_experts decoded records); the size query stays monotone in T across all.
+    mx_mfma 0 switches the block-scaled path off through lmoe_config.mx_mfma_min_t = -1."""
+    c = lm.make_config(2560, 1792, 512, 10, 640, 640, "bf16", "bf16", expert, 1, 0 if mx_mfma == "1" else -1)
     prev = 0
     for T in list(range(60, 100)) + [383, 384, 385, 4096, 16384]:
         n = lm.lmoe_workspace_bytes(c, T)
@@ -226,3 +226,17 @@ def test_noalloc_checks_arguments_on_the_host():
     assert lm.lmoe_forward_noalloc(cfg(), full_weights(), FAKE, -1, FAKE, None, 0) == lm.LMOE_ERR_SHAPE
     nothing = lm.make_weights(None, None, None, None, None, None)
     assert lm.lmoe_forward_noalloc(cfg(), nothing, None, 0, None, None, 0) == lm.LMOE_OK
+
+
+def test_mx_threshold_is_a_config_field():
+    """The block-scaled MXFP4 path's threshold comes from lmoe_config (never the environment): the
+    workspace grows where the MXFP8 activations appear, at the configured batch size."""
+    for t0 in (0, 200):
+        c = lm.make_config(2560, 1792, 512, 10, 640, 640, "bf16", "bf16", "mxfp4", 1, t0)
+        at = 96 if t0 == 0 else 200
+        jump = lm.lmoe_workspace_bytes(c, at) - lm.lmoe_workspace_bytes(c, at - 1)
+        step = lm.lmoe_workspace_bytes(c, at + 1) - lm.lmoe_workspace_bytes(c, at)
+        assert jump > 5 * step, (t0, jump, step)
+    bad = lm.make_config(2560, 1792, 512, 10, 640, 640, "bf16", "bf16", "mxfp4", 1, -2)
+    n = ctypes.c_size_t(0)
+    assert lm.lib.lmoe_workspace_bytes(ctypes.byref(bad), 8, ctypes.byref(n)) == lm.LMOE_ERR_SHAPE
