@@ -401,11 +401,14 @@ def measure_stack(wl, steps, warmup):
 
     hip = Hip()
     t0 = time.time()
-    banks = {b: gen.make_experts(wl, b) for b in range(max(wl.expert_banks, 1))}
+    banks = {b: gen.make_experts(wl, b) for b in range(wl.expert_banks)}
     layers = []
     for l in range(wl.layers):
         lw = gen.make_layer(wl, l, experts=banks[gen.expert_bank(wl, l)] if wl.expert_banks else None)
         layers.append(DeviceLayer(lw, act="bf16", mx_mfma_min_t=MX_MFMA_MIN_T))
+        del lw
+        if l % 8 == 7:
+            log(f"[bench] {wl.name}: {l + 1} layers generated and uploaded ({time.time() - t0:.1f}s)")
     del banks
     log(f"[bench] {wl.name}: {wl.layers} layers generated and uploaded in {time.time() - t0:.1f}s")
     T = wl.T
@@ -687,7 +690,7 @@ def main():
     }
     if wl.layers > 1:
         out["config"]["layers"] = wl.layers
-        out["config"]["expert_banks"] = wl.expert_banks
+        out["config"]["expert_sets"] = wl.expert_banks or wl.layers  # distinct sets of 512 routed experts
         out["config"]["timed"] = "eager lmoe_forward calls, all layers in order, per-layer figures"
     if args.tsweep and copies is not None:
         sweep = []

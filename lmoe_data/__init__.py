@@ -91,7 +91,7 @@ class Workload:
     bias: str      # 'zero' | 'zipf'
     zipf_s: float = 1.1
     layers: int = 1
-    expert_banks: int = 0  # >0: layer l's routed experts are drawn from bank l % expert_banks
+    expert_banks: int = 0  # >0: layer l's routed experts are drawn from bank l % expert_banks; 0: its own
 
 
 WORKLOADS = {
@@ -100,7 +100,7 @@ WORKLOADS = {
     "prefill_t4096": Workload(3, "prefill_t4096", EDGE0_145B, 4096, "bf16", "bf16", "bf16", "zero"),
     "prefill_t16384": Workload(4, "prefill_t16384", EDGE0_145B, 16384, "bf16", "bf16", "bf16", "zipf"),
     "stack48_mxfp4_t8": Workload(5, "stack48_mxfp4_t8", EDGE0_145B, 8, "bf16", "bf16", "mxfp4", "zipf",
-                                 layers=48, expert_banks=2),
+                                 layers=48),
     "decode120_t8": Workload(6, "decode120_t8", EDGE0_120B, 8, "bf16", "bf16", "bf16", "zipf"),
     "decode_nvfp4_t8": Workload(7, "decode_nvfp4_t8", EDGE0_145B, 8, "bf16", "bf16", "nvfp4", "zipf"),
     "decode_group64_t8": Workload(8, "decode_group64_t8", EDGE0_145B_G64, 8, "bf16", "bf16", "bf16", "zipf"),
@@ -147,32 +147,42 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
 # block of 32).  The shared exponent is floor(log2(amax)) - 2 (2 = emax of E2M1), elements are
 # rounded to nearest-even on the E2M1 grid and saturate at +-6.  An all-zero block gets scale byte 0.
 # ---------------------------------------------------------------------------------------------
-_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float64)
+# E2M1 rounding midpoints (between consecutive grid values 0, .5, 1, 1.5, 2, 3, 4, 6) and, for each,
+# whether a value exactly on it rounds up: a tie goes to the even code, i.e. up at odd indices.
+_E2M1_MIDS = ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True), (5.0, False))
+
+
+def _e2m1_codes(a: np.ndarray) -> np.ndarray:
+    """|values| (already divided by their scale, float32 or float64) -> E2M1 magnitude codes,
+    nearest-even, saturating at 6: the number of midpoints the value lies above (or on, for the
+    midpoints whose tie rounds up).  Every midpoint is exact in both float types."""
+    code = np.zeros(a.shape, dtype=np.uint8)
+    for m, up in _E2M1_MIDS:
+        code += (a >= m) if up else (a > m)
+    return code
 
 
 def mxfp4_encode(w: np.ndarray):
-    """float32 [rows][K] (K % 32 == 0) -> (nibbles uint8 [rows][K/2], scales uint8 [rows][K/32])."""
+    """float32 [rows][K] (K % 32 == 0) -> (nibbles uint8 [rows][K/2], scales uint8 [rows][K/32]).
+
+    Works in float32: the rescale by 2^-shared is a power-of-two product, exact unless the result
+    falls below the float32 normal range, where it is far below the first midpoint either way."""
     w = np.asarray(w, dtype=np.float32)
     rows, K = w.shape
     assert K % 32 == 0
-    blk = w.reshape(rows, K // 32, 32).astype(np.float64)
-    amax = np.abs(blk).max(axis=2)
+    blk = w.reshape(rows, K // 32, 32)
+    mag = np.abs(blk)
+    amax = mag.max(axis=2)
     _, ex = np.frexp(amax)                      # amax = m * 2^ex, m in [0.5, 1)
     shared = np.where(amax > 0, ex - 1 - 2, -127)
-    shared = np.clip(shared, -127, 127).astype(np.int64)
+    shared = np.clip(shared, -127, 127)
     scales = (shared + 127).astype(np.uint8)
-    a = np.abs(np.ldexp(blk, -shared[..., None]))   # exact power-of-two rescale
-    code = np.searchsorted(_E2M1_MIDS, a, side="left")  # number of midpoints strictly below a
-    at_mid = np.zeros_like(a, dtype=bool)
-    inner = code < 7
-    at_mid[inner] = a[inner] == _E2M1_MIDS[code[inner]]
-    code = code + (at_mid & (code % 2 == 1))        # a tie goes to the even code
-    code = np.minimum(code, 7).astype(np.uint8)
-    sign = (blk < 0).astype(np.uint8) << 3
-    sign[code == 0] = 0                              # -0 is stored as +0
-    nib = (code | sign).reshape(rows, K)
-    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
-    return packed, scales.reshape(rows, K // 32)
+    mag *= np.ldexp(np.float32(1.0), -shared).astype(np.float32)[..., None]
+    code = _e2m1_codes(mag)
+    code |= (np.signbit(blk) & (code != 0)).view(np.uint8) << 3   # -0 is stored as +0
+    nib = code.reshape(rows, K)
+    packed = nib[:, 0::2] | (nib[:, 1::2] << 4)
+    return packed, scales
 
 
 # ---------------------------------------------------------------------------------------------
@@ -205,16 +215,6 @@ def e4m3_bits(v: np.ndarray) -> np.ndarray:
     expf = np.where(normal, e + 7, 0)
     b = (expf.astype(np.int64) << 3) | mant.astype(np.int64)
     return np.where(v > 0, b, 0).astype(np.uint8)
-
-
-def _e2m1_codes(a: np.ndarray) -> np.ndarray:
-    """|values| (already divided by their scale) -> E2M1 magnitude codes, nearest-even, saturating."""
-    code = np.searchsorted(_E2M1_MIDS, a, side="left")
-    at_mid = np.zeros_like(a, dtype=bool)
-    inner = code < 7
-    at_mid[inner] = a[inner] == _E2M1_MIDS[code[inner]]
-    code = code + (at_mid & (code % 2 == 1))
-    return np.minimum(code, 7).astype(np.uint8)
 
 
 def nvfp4_encode(w: np.ndarray):

@@ -1,4 +1,5 @@
-"""The 48-layer FFN-only stack with MXFP4 experts at T = 8 (pre-RMSNorm, fp32 residual).
+"""The 48-layer FFN-only stack with MXFP4 experts at T = 8 (pre-RMSNorm, fp32 residual), every
+layer with its own D, U, router, bias, shared expert and 512 routed experts (24,576 records).
 
 Each layer is checked on the oracle's own residual stream: the oracle runs the whole stack
 in float64 (carrying h in float32, as the stack does), and layer l of the GPU receives the
@@ -21,17 +22,13 @@ pytestmark = pytest.mark.gpu
 def test_stack48_mxfp4_teacher_forced():
     wl = gen.WORKLOADS["stack48_mxfp4_t8"]
     k = wl.shape.top_k
-    banks = {}
-    log("[stack] drawing expert banks")
-    for b in range(wl.expert_banks):
-        banks[b] = gen.make_experts(wl, b)
     h0 = gen.make_residual(wl).astype(np.float64)
     ws = Workspace("cuda")
     h = h0.copy()
     worst = 0.0
     gpu_layers = []
     for l in range(wl.layers):
-        lw = gen.make_layer(wl, l, experts=banks[gen.expert_bank(wl, l)])
+        lw = gen.make_layer(wl, l)
         dl = DeviceLayer(lw, act="bf16")
         gpu_layers.append(dl)
         # oracle layer l on its own stream
@@ -55,7 +52,8 @@ def test_stack48_mxfp4_teacher_forced():
         if forced:
             o = oracle.block_forward(L, xo)  # the oracle's own stream continues with its own routing
         h = (h + o["y"]).astype(np.float32).astype(np.float64)
-        if l % 8 == 0 or l == wl.layers - 1:
+        del lw, L, o
+        if l % 4 == 0 or l == wl.layers - 1:
             log(f"[stack] layer {l}: rel={err:.3e} excluded={int(excl.sum())} differing={int((~same).sum())} "
                 f"rms(h)={np.sqrt(np.mean(h * h)):.3f}")
     log(f"[stack] worst layer rel err {worst:.3e}")

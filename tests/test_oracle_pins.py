@@ -388,6 +388,35 @@ def test_mxfp4_encoder_decoder_round_trip():
     assert np.all(np.abs(d - w) <= np.maximum(step / 2 * scale, np.maximum(np.abs(w) - 6 * scale, 0)) + 1e-12)
 
 
+def test_mxfp4_encoder_ties_go_to_even():
+    """Values exactly between two E2M1 grid points take the even code (OCP MX v1.0 rounding):
+    0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4, at any block scale;
+    just off a midpoint they go to the nearer point."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    to = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for s in (-20, -3, 0, 7):
+        row = np.zeros(64)
+        row[0] = 6.0                                   # amax = 6 * 2^s fixes the shared exponent at s
+        row[1:8] = mids
+        row[8:15] = [-m for m in mids]
+        row[15:22] = np.nextafter(np.array(mids, dtype=np.float32), np.float32(0))
+        row[22:29] = np.nextafter(np.array(mids, dtype=np.float32), np.float32(9))
+        row[32] = -6.0
+        row[33:40] = mids
+        w = (row * 2.0 ** s).astype(np.float32)[None, :]
+        nib, sc = gen.mxfp4_encode(w)
+        assert list(sc[0]) == [127 + s, 127 + s]
+        d = oracle.mxfp4_decode(nib, sc, 1, 64)[0] / 2.0 ** s
+        np.testing.assert_array_equal(d[1:8], to)
+        np.testing.assert_array_equal(d[8:15], [-v for v in to])
+        below = [max(g for g in grid if g < m) for m in mids]
+        above = [min(g for g in grid if g > m) for m in mids]
+        np.testing.assert_array_equal(d[15:22], below)
+        np.testing.assert_array_equal(d[22:29], above)
+        np.testing.assert_array_equal(d[33:40], to)
+
+
 def test_e4m3_decode_closed_forms():
     # FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 subnormal)
     b = np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x3F, 0x7E, 0xB8, 0x80], dtype=np.uint8)
