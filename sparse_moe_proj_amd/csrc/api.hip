@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 #include <string>
@@ -96,7 +97,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t x16, z32, z16, z16h, zlo, logits, ids, w, offsets, perm, inv, rowinfo, hist, base, tiles, ntiles, H, Y, mpart, m,
-        deq, deq_ts, z8, z8s, z4, z4s, h8, h8s, total;
+        deq, deq_ts, z8, z8s, z4, z4s, h8, h8s, h4, h4s, h16, total;
     bool stream_path, decode_path, fused_router, deq_path, mx_path;
     int max_tiles, BM, Hs, R;
 };
@@ -159,6 +160,9 @@ Layout plan(const Dims& d, int T) {
     lo.z4s = take(lo.mx_path ? (size_t)T * d.Lz / 32 : 0);
     lo.h8 = take(lo.mx_path ? (size_t)T * d.k * d.F : 0);
     lo.h8s = take(lo.mx_path ? (size_t)T * d.k * d.F / 32 : 0);
+    lo.h4 = take(lo.mx_path ? (size_t)T * d.k * d.F / 2 : 0);
+    lo.h4s = take(lo.mx_path ? (size_t)T * d.k * d.F / 32 : 0);
+    lo.h16 = take(lo.mx_path ? (size_t)T * d.k * d.F * 2 : 0);
     lo.total = o;
     return lo;
 }
@@ -333,22 +337,25 @@ lmoe_status lmoe_permute(const lmoe_config* cfg, const int32_t* ids, int32_t T, 
     return LMOE_OK;
 }
 
-lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const void* x, int32_t T, void* y,
-                         const lmoe_forward_opts* opts, void* ws, size_t ws_bytes, void* stream) {
-    Dims d;
+}  // extern "C"
+
+namespace {
+
+// Every host-side check of lmoe_forward's arguments except the workspace's (shared with
+// lmoe_forward_noalloc, which runs them before it looks up its device array).
+lmoe_status check_forward(const lmoe_config* cfg, const lmoe_weights* wt, const void* x, int32_t T, const void* y,
+                          const lmoe_forward_opts& o, Dims& d) {
     lmoe_status st = check_config(cfg, d);
     if (st != LMOE_OK) return st;
     if ((st = check_T(d, T)) != LMOE_OK) return st;
     if (!wt) return fail(LMOE_ERR_NULL, "weights is NULL");
-    const lmoe_forward_opts none{};
-    const lmoe_forward_opts& o = opts ? *opts : none;
     if (o.prenorm && d.f32) return fail(LMOE_ERR_UNSUPPORTED, "prenorm needs act BF16 (the block input is bf16(RMSNorm(h)))");
     if (T == 0) return LMOE_OK;
     if (!x || !y || !wt->D || !wt->U || !wt->Wr || !wt->experts)
         return fail(LMOE_ERR_NULL, "x, y, D, U, Wr and experts must be non-NULL");
     if (d.Fs > 0 && !wt->shared) return fail(LMOE_ERR_NULL, "shared_ffn > 0 but the shared expert record is NULL");
     if (d.G > 1 && !wt->Gr) return fail(LMOE_ERR_UNSUPPORTED, "expert groups need the folded router (weights->Gr)");
-    const void* ptrs[] = {x, y, wt->D, wt->U, wt->Wr, wt->Gr, wt->experts, wt->shared, ws, o.aux_z, o.aux_ids, o.aux_w,
+    const void* ptrs[] = {x, y, wt->D, wt->U, wt->Wr, wt->Gr, wt->experts, wt->shared, o.aux_z, o.aux_ids, o.aux_w,
                           o.aux_offsets, o.aux_perm};
     for (const void* p : ptrs)
         if (!aligned16(p)) return fail(LMOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
@@ -357,6 +364,21 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     const size_t ybytes = (size_t)T * d.H * ((o.residual || d.f32) ? 4 : 2);
     if (overlap(x, xbytes, y, ybytes) && !(x == y && o.prenorm && o.residual))
         return fail(LMOE_ERR_UNSUPPORTED, "x and y overlap (only x == y with prenorm and residual is allowed)");
+    return LMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const void* x, int32_t T, void* y,
+                         const lmoe_forward_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+    Dims d;
+    const lmoe_forward_opts none{};
+    const lmoe_forward_opts& o = opts ? *opts : none;
+    lmoe_status st = check_forward(cfg, wt, x, T, y, o, d);
+    if (st != LMOE_OK || T == 0) return st;
+    if (!aligned16(ws)) return fail(LMOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     const Layout lo = plan(d, T);
     if (!ws || ws_bytes < lo.total)
         return fail(LMOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : 0, lo.total);
@@ -478,6 +500,9 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         a.z4s = static_cast<uint8_t*>(at(lo.z4s));
         a.h8 = static_cast<uint8_t*>(at(lo.h8));
         a.h8s = static_cast<uint8_t*>(at(lo.h8s));
+        a.h4 = static_cast<uint8_t*>(at(lo.h4));
+        a.h4s = static_cast<uint8_t*>(at(lo.h4s));
+        a.h16 = static_cast<uint16_t*>(at(lo.h16));
     }
     if ((e = launch_experts_bf16(a, s, ev)) != hipSuccess) return hip_fail(e, "experts");
     const int umode = o.residual ? 2 : 1;
@@ -511,21 +536,24 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
 lmoe_status lmoe_forward_noalloc(const lmoe_config* cfg, const lmoe_weights* weights, const void* x, int32_t T, void* y,
                                  const lmoe_forward_opts* opts, void* stream) {
     Dims d;
-    lmoe_status st = check_config(cfg, d);
-    if (st != LMOE_OK) return st;
-    if ((st = check_T(d, T)) != LMOE_OK) return st;
+    const lmoe_forward_opts none{};
+    lmoe_status st = check_forward(cfg, weights, x, T, y, opts ? *opts : none, d);
+    if (st != LMOE_OK || T == 0) return st;
     const size_t need = plan(d, T).total;
     if (need > (size_t)LMOE_NOALLOC_SCRATCH_BYTES)
         return fail(LMOE_ERR_WORKSPACE,
                     "T = %d needs %zu workspace bytes, more than the %zu bytes of the allocation-free entry point",
                     T, need, (size_t)LMOE_NOALLOC_SCRATCH_BYTES);
     void* ws = nullptr;
-    if (T > 0 && (st = scratch_address(&ws)) != LMOE_OK) return st;
+    if ((st = scratch_address(&ws)) != LMOE_OK) return st;
     return lmoe_forward(cfg, weights, x, T, y, opts, ws, (size_t)LMOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 const char* lmoe_status_str(lmoe_status status) {
-    switch (status) {
+    // read as an integer: a C caller may pass any int, which C++ does not allow an enum to hold
+    int32_t v;
+    memcpy(&v, &status, sizeof v);
+    switch (v) {
         case LMOE_OK: return "ok";
         case LMOE_ERR_NULL: return "required pointer is NULL";
         case LMOE_ERR_SHAPE: return "dimension out of range or inconsistent";

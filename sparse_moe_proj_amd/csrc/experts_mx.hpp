@@ -2,9 +2,10 @@
 //
 // The routed experts' gate/up and down products take their MXFP4 records as they are stored
 // (E2M1 values with one E8M0 scale per 32 values along K) as the B operand, and the activations
-// as MXFP8 (E4M3 values with one E8M0 scale per 32 values of a row) as the A operand: z is
-// quantized once per token, H in the gate/up epilogue.  The MFMA applies both block scales, so
-// no 4-bit value is decoded in software.
+// as MXFP8 (E4M3 values with one E8M0 scale per 32 values of a row) plus the MXFP4 residual of
+// that rounding as two A operands: z is quantized once per token, H (written in bf16 by the
+// gate/up epilogue) once per routed row.  The MFMA applies both block scales, so no 4-bit value
+// is decoded in software.
 //
 // Operand lane layouts of the 32x32x64 form with A in FP8 and B in FP4 (lane l, g = l / 32):
 //   A: row l % 32; bytes 0..15 hold K 16g .. 16g + 15, bytes 16..31 hold K 32 + 16g .. 32 + 16g + 15;
@@ -21,9 +22,9 @@
 //   the A scales (4 bytes per row, dword copies by BM / 64 waves) and the B scale tiles (64 bytes
 //   per 16-row block, one byte per unit in the same order; one 16-byte-per-lane copy by one wave);
 //   the waits of the waves that copy no scales count one copy fewer per stage;
-//   with LO (gate/up), a second A operand: the residual of each z row after its MXFP8 rounding,
+//   with LO, a second A operand: the residual of each activation row after its MXFP8 rounding,
 //   as MXFP4 (BM rows x 64 bytes, copied into packed-tile order like B) and its scales, so that
-//   z = hi + lo carries about 6 significant bits instead of 4 (see quant_mx_kernel).
+//   z = hi + lo (and H = hi + lo) carries about 6 significant bits instead of 4 (see quant_mx_kernel).
 #pragma once
 
 #include "gemm_pipe.hpp"
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* __restric
 // nb * 8 K + kg * 1024 of its matrix, its scale tile at nb * K / 2 + kg * 64 of its scale matrix.
 // ---------------------------------------------------------------------------------------------
 
-// Gate/up: H8 = MXFP8(SiLU(z gate^T) * (z up^T)) over routed rows, z taken as its MXFP8 part plus
+// Gate/up: H = bf16(SiLU(z gate^T) * (z up^T)) over routed rows, z taken as its MXFP8 part plus
 // its MXFP4 residual (shape with LO); the B tile of a wave column holds 32 gate rows, then the 32
 // up rows of the same f.
 template <class S>
@@ -498,8 +499,7 @@ struct MxUp {
     const uint8_t* experts;
     size_t rec;  // bytes per record
     int L, F;
-    uint8_t* h8;   // [T k][F] E4M3 by segment row
-    uint8_t* h8s;  // [T k][F / 32]
+    uint16_t* h16;  // [T k][F] bf16 by segment row
     struct Ctx { int seg, row0, nrows, f0; const uint8_t* r; };
     __device__ int m_tiles() const { return seg.count(); }
     __device__ bool tile(int bx, int by, Ctx& c) const {
@@ -560,43 +560,32 @@ struct MxUp {
     struct Prep {};
     template <int MB>
     __device__ Prep prep(const Ctx&, int, int) const { return {}; }
-    // SwiGLU, then MXFP8 per 32 columns of a row: the 32 columns of one accumulator block are
-    // the 32 lanes of one half-wave, so the block's amax is a 5-step butterfly over them.
+    // SwiGLU in bf16 rows (quant_mx_kernel then makes H's MXFP8 part and residual for the down
+    // product: one pass over H, cheaper than the block maxima and byte stores in this epilogue)
     template <int MB, int NB>
     __device__ __forceinline__ void store(const Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb, int lane) const {
         const int f = c.f0 + (cb / S::kWN) * kHalf + frag32_col(lane);
         static_for<MB>([&](auto i) {
             __builtin_amdgcn_sched_barrier(0);
-            float v[16], a[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                v[r] = silu(acc[i][0][r]) * acc[i][1][r];
-                a[r] = fabsf(v[r]);
-            }
-#pragma unroll
-            for (int d = 1; d < 32; d <<= 1)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) a[r] = fmaxf(a[r], __shfl_xor(a[r], d, 64));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = rb + i * 32 + frag32_row(r, lane);
-                if (m < c.nrows && f < F) {
-                    const uint32_t sb = mx8_scale_bits(a[r]);
-                    const size_t row = (size_t)(c.row0 + m);
-                    h8[row * F + f] = (uint8_t)f32_to_e4m3(v[r] * mx8_inv_scale(sb));
-                    if ((lane & 31) == 0) h8s[row * (F / 32) + f / 32] = (uint8_t)sb;
-                }
+                if (m < c.nrows && f < F)
+                    h16[(size_t)(c.row0 + m) * F + f] = (uint16_t)f2bf(silu(acc[i][0][r]) * acc[i][1][r]);
             }
         });
     }
 };
 
-// Down: Y[dest(p)][n] = bf16(H8[p] . down[n]) over routed rows.
+// Down: Y[dest(p)][n] = bf16(H[p] . down[n]) over routed rows, H taken as its MXFP8 part plus
+// (shape with LO) its MXFP4 residual.
 template <class S>
 struct MxDown {
     SegSpace seg;
     const uint8_t* h8;
     const uint8_t* h8s;
+    const uint8_t* h4;   // residual (LO)
+    const uint8_t* h4s;
     const uint8_t* experts;
     size_t rec;
     int L, F;
@@ -620,6 +609,11 @@ struct MxDown {
         const int r = min(rowmajor_row(i, lane), c.nrows - 1);
         return rowmajor_off((uint32_t)r * F, i, lane);
     }
+    // residual: copy i takes rows 16 i .. 16 i + 15 (as MxUp's)
+    __device__ const uint8_t* lo_base(const Ctx& c) const { return h4 + (size_t)c.row0 * (F / 2); }
+    __device__ uint32_t src_lo(const Ctx& c, int i, int lane) const {
+        return (uint32_t)min(16 * i + (lane & 15), c.nrows - 1) * (F / 2) + (lane >> 4) * 16;
+    }
     __device__ int b_nb(const Ctx& c, int b) const { return min(c.n0 + b * 16, L - 16) >> 4; }
     __device__ uint32_t src_b(const Ctx& c, int i, int lane) const {
         return (uint32_t)((size_t)F * L + (size_t)b_nb(c, i) * 8 * F) + lane * 16;
@@ -630,27 +624,45 @@ struct MxDown {
             off = (uint32_t)((size_t)3 * F * L / 2 + (size_t)2 * F * L / 32 + (size_t)b_nb(c, lane >> 2) * (F / 2)) +
                   (lane & 3) * 16;
             step = kMxSBStep;
-        } else {  // A scales of rows 64 w + lane (waves past the B scales copy none; any valid source)
+        } else if (S::kLo && wave > S::kSAW && wave < S::kSW) {  // residual scales of rows 64 w + lane
+            const int w = wave - S::kSAW - 1;
+            base = h4s;
+            off = (uint32_t)(c.row0 + min(w * 64 + lane, c.nrows - 1)) * (F / 32);
+            step = kMxSAStep;
+        } else {  // A scales of rows 64 w + lane (waves past the scale waves copy none; any valid source)
             const int w = wave < S::kSAW ? wave : 0;
             base = h8s;
             off = (uint32_t)(c.row0 + min(w * 64 + lane, c.nrows - 1)) * (F / 32);
             step = kMxSAStep;
         }
     }
+    // destination rows of the tile: in registers, or (with the residual operand, whose fragments
+    // leave no registers for them) in LDS, written before the barrier that precedes the stores
+    static constexpr bool kPrepLds = S::kLo;
+    __device__ static int* prep_rows() {
+        __shared__ int rows[S::kBM];
+        return rows;
+    }
     template <int MB>
     struct PrepT {
-        int drow[MB][16];
+        int drow[kPrepLds ? 1 : MB][16];
     };
     template <int MB>
     __device__ __forceinline__ PrepT<MB> prep(const Ctx& c, int rb, int lane) const {
         PrepT<MB> q;
+        if constexpr (kPrepLds) {
+            int* rows = prep_rows();
+            for (int m = threadIdx.x; m < S::kBM; m += S::kThreads)
+                rows[m] = m < c.nrows ? seg.dest_of(c.seg, c.row0 + m) : -1;
+        } else {
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+            for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = rb + i * 32 + frag32_row(r, lane);
-                q.drow[i][r] = m < c.nrows ? seg.dest_of(c.seg, c.row0 + m) : -1;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const int m = rb + i * 32 + frag32_row(r, lane);
+                    q.drow[i][r] = m < c.nrows ? seg.dest_of(c.seg, c.row0 + m) : -1;
+                }
+        }
         return q;
     }
     template <int MB, int NB>
@@ -659,7 +671,7 @@ struct MxDown {
         static_for<MB>([&](auto i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int drow = q.drow[i][r];
+                const int drow = kPrepLds ? prep_rows()[rb + i * 32 + frag32_row(r, lane)] : q.drow[kPrepLds ? 0 : i][r];
                 if (drow >= 0) {
                     const size_t dst = (size_t)drow * L;
                     static_for<NB>([&](auto j) {

@@ -944,9 +944,10 @@ hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
     return hipSuccess;
 }
 
-// Large MXFP4 batches on the block-scaled MFMA: z to MXFP8 plus an MXFP4 residual, then the routed
-// gate/up (H to MXFP8 in its epilogue) and down products from the stored records; the shared expert's (bf16)
-// segment takes the bf16 kernels.
+// Large MXFP4 batches on the block-scaled MFMA: z to MXFP8 plus an MXFP4 residual, the routed
+// gate/up product (H in bf16), H to MXFP8 plus an MXFP4 residual, and the down product, both
+// products from the stored records; the shared expert's (bf16) segment takes the bf16 kernels.
+// LMOE_MX_H_LO=0 builds the down product without H's residual term (for measurement).
 #ifndef LMOE_MX_NS_UP
 #define LMOE_MX_NS_UP 2
 #endif
@@ -954,11 +955,15 @@ hipError_t launch_stream_experts(const ExpertArgs& a, const SegSpace& seg, hipSt
 #define LMOE_MX_NS_DN 3
 #endif
 using MxUpL = MxShape<128, 256, LMOE_MX_NS_UP, 2, 4, true>;
-using MxDnL = MxShape<128, 256, LMOE_MX_NS_DN, 2, 4, false>;
+#ifndef LMOE_MX_H_LO
+#define LMOE_MX_H_LO 1
+#endif
+using MxDnL = MxShape<128, 256, LMOE_MX_NS_DN, 2, 4, LMOE_MX_H_LO != 0>;
 static_assert(MxUpL::kBM == PipeL::kBM && MxDnL::kBM == PipeL::kBM, "the work list's tile rows");
 
 hipError_t launch_experts_mx(const ExpertArgs& a, const SegSpace& seg, hipStream_t s, StageEvents& ev) {
-    if (!a.z8 || !a.z8s || !a.z4 || !a.z4s || !a.h8 || !a.h8s || a.fmt != 1 || a.L % 128 || a.F % 128)
+    if (!a.z8 || !a.z8s || !a.z4 || !a.z4s || !a.h8 || !a.h8s || !a.h16 || (MxDnL::kLo && (!a.h4 || !a.h4s)) ||
+        a.fmt != 1 || a.L % 128 || a.F % 128)
         return hipErrorInvalidValue;
     const int nsh = a.shared ? (int)cdiv(a.T, MxUpL::kBM) : 0;
     SegSpace rs = seg;
@@ -976,7 +981,7 @@ hipError_t launch_experts_mx(const ExpertArgs& a, const SegSpace& seg, hipStream
     hipError_t err = last();
     if (err != hipSuccess) return err;
     {
-        MxUp<MxUpL> up{rs, a.z8, a.z8s, a.z4, a.z4s, ex, a.rec_bytes, a.L, a.F, a.h8, a.h8s};
+        MxUp<MxUpL> up{rs, a.z8, a.z8s, a.z4, a.z4s, ex, a.rec_bytes, a.L, a.F, a.h16};
         const int nn = (int)cdiv(a.F, MxUpL::kBN / 2);
         auto k = mx_gemm_persistent<MxUpL, MxUp<MxUpL>>;
         hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, MxUpL::kThreads), (long)a.max_tiles * nn)),
@@ -993,8 +998,12 @@ hipError_t launch_experts_mx(const ExpertArgs& a, const SegSpace& seg, hipStream
     }
     ev.end(kStageUp);
     ev.begin(kStageDown);
+    const size_t hblk = (size_t)a.T * a.k * a.F / 32;  // the routed rows of H
+    hipLaunchKernelGGL(quant_mx_kernel, dim3((unsigned)cdiv(hblk, 256)), dim3(256), 0, s, a.h16, hblk, a.h8, a.h8s,
+                       MxDnL::kLo ? a.h4 : nullptr, a.h4s);
+    if ((err = last()) != hipSuccess) return err;
     {
-        MxDown<MxDnL> dn{rs, a.h8, a.h8s, ex, a.rec_bytes, a.L, a.F, a.Y};
+        MxDown<MxDnL> dn{rs, a.h8, a.h8s, a.h4, a.h4s, ex, a.rec_bytes, a.L, a.F, a.Y};
         const int nn = (int)cdiv(a.L, MxDnL::kBN);
         auto k = mx_gemm_persistent<MxDnL, MxDown<MxDnL>>;
         hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, MxDnL::kThreads), (long)a.max_tiles * nn)),

@@ -176,7 +176,8 @@ struct ExpertArgs {
     const int32_t* offsets = nullptr;
     // MXFP4 records on the block-scaled MFMA path (large batches): z as MXFP8 [T][zp] values and
     // [T][zp / 32] scales plus its MXFP4 residual [T][zp / 2] and [T][zp / 32], the routed rows of
-    // H as MXFP8 [T k][F] and [T k][F / 32]
+    // H in bf16 [T k][F], then as MXFP8 [T k][F] and [T k][F / 32] plus its MXFP4 residual
+    // [T k][F / 2] and [T k][F / 32]
     bool mx_path = false;
     uint8_t* z8 = nullptr;
     uint8_t* z8s = nullptr;
@@ -184,6 +185,9 @@ struct ExpertArgs {
     uint8_t* z4s = nullptr;
     uint8_t* h8 = nullptr;
     uint8_t* h8s = nullptr;
+    uint8_t* h4 = nullptr;
+    uint8_t* h4s = nullptr;
+    uint16_t* h16 = nullptr;
 };
 
 // Large 4-bit batches: minimum T at which the records of the experts with tokens are decoded to

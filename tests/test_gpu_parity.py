@@ -82,7 +82,7 @@ def test_prefill_t16384_every_tile(ws):
 
 @pytest.mark.timeout(900)
 def test_prefill_mxfp4_t16384_every_tile(ws):
-    # MXFP4 records on the block-scaled MFMA (z as MXFP8 plus an MXFP4 residual), the default
+    # MXFP4 records on the block-scaled MFMA (z and H each as MXFP8 plus an MXFP4 residual), the default
     # path for MXFP4 batches from 96 tokens
     _workload_case("prefill_mxfp4_t16384", 64, ws, tiles=True)
 
@@ -225,6 +225,23 @@ def test_large_mxfp4_paths(path, shape, T, ws):
     out = run_forward(dl, upload_tokens(x), ws)
     torch.cuda.synchronize()
     check_block(lw, x, "bf16", out, label=f"large_mxfp4 {path} {shape} T={T}")
+
+
+MX_NOSH_4K = gen.Shape(hidden=1024, latent=1024, n_experts=64, top_k=8, ffn=512, shared_ffn=0)
+
+
+@pytest.mark.timeout(600)
+def test_mxfp4_no_shared_every_token_t4096(ws):
+    """The default MXFP4 path for large batches (block-scaled MFMA, z and H each as MXFP8 plus an
+    MXFP4 residual) on a shape without a shared expert, where no exact bf16 term dilutes the
+    activation rounding: every one of 4096 tokens against the oracle."""
+    wl = gen.Workload(93, "mx_nosh_t4096", MX_NOSH_4K, 4096, "bf16", "bf16", "mxfp4", "zipf")
+    lw = gen.make_layer(wl, 0)
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label="mxfp4 no shared expert T=4096")
 
 
 @pytest.mark.parametrize("T", [3, 16, 40, 100, 383, 400, 1100])
