@@ -148,7 +148,7 @@ Layout plan(const Dims& d, int T) {
     lo.ntiles = take(4);
     lo.H = take((size_t)lo.R * lo.Hs * act);
     lo.Y = take(lo.decode_path ? 0 : (size_t)lo.R * d.L * (d.f32 ? 4 : 2));
-    lo.mpart = take(lo.decode_path ? (size_t)decode_groups() * T * d.Lz * 4 : 0);
+    lo.mpart = take(lo.decode_path ? (size_t)decode_groups() * T * d.Lz * 2 : 0);
     // merged rows (larger batches), or with expert groups and small batches whose U launch cannot
     // stage all groups at once, the U products of the groups [G][T][H] fp32
     lo.m = take(lo.decode_path ? (small_proj_fits(T, d.Lz) ? 0 : (size_t)d.G * T * d.H * 4) : (size_t)T * d.Lz * act);
@@ -486,7 +486,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
             return hip_fail(e, "top-k / permute");
         ev.end(LMOE_STAGE_TOPK);
     }
-    float* mpart = static_cast<float*>(at(lo.mpart));
+    uint16_t* mpart = static_cast<uint16_t*>(at(lo.mpart));
     ExpertArgs a{tiles, ntiles, perm, T, d.k, d.E, d.L, d.F, d.Fs, lo.Hs, z16, z16h, wt->experts, record_bytes(d, false),
                  wt->shared, static_cast<uint16_t*>(at(lo.H)), static_cast<uint16_t*>(Y), lo.max_tiles, lo.stream_path,
                  lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr, d.Eg, d.Lz,

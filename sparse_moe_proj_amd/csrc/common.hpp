@@ -30,6 +30,15 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+// a[0..7] += the 8 bf16 values of u (low half of each dword first)
+__device__ __forceinline__ void add_bf16x8(float (&a)[8], const uint4& u) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[2 * i] += bf2f(w[i] & 0xFFFFu);
+        a[2 * i + 1] += bf2f(w[i] >> 16);
+    }
+}
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 

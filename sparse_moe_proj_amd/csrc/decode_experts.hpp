@@ -15,7 +15,7 @@
 //    times its routing weight (1 for the shared expert), to the wave's per-token accumulator in
 //    LDS.  The waves' accumulators are
 //    then summed in wave order and written as the group's partial merged rows
-//        mpart[g][t][latent]  (fp32).
+//        mpart[g][t][latent]  (bf16).
 //    The U projection sums the G partials (in group order) while staging its input.
 //
 // Every sum runs in a fixed order (tiles in work-list order within a wave, waves in order,
@@ -40,7 +40,7 @@ struct DecodeExperts {
     int nblocks;       // 16-row blocks of the widest segment: ceil(Hs / 16)
     uint16_t* H;       // [T*k + T][Hs] bf16, segment-row order
     const float* w;    // [T][k] routing weights (slot order)
-    float* mpart;      // [G][T][zp] (zp = seg.zp: the latent width times the expert groups)
+    uint16_t* mpart;   // [G][T][zp] bf16 (zp = seg.zp: the latent width times the expert groups)
     int groups;        // G
     const int2* rowinfo;  // [T*k] (token, weight bits) of the routed row at each position
     int max_tiles;        // work-list capacity (entries past *seg.ntiles are not used)
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(64 * W) void decode_dc_kernel(const DecodeExperts<Q
             float s = 0.f;
 #pragma unroll
             for (int w = 0; w < W; ++w) s += macc[w][t][r];
-            d.mpart[((size_t)grp * T + t) * d.seg.zp + (size_t)xg * d.L + n0 + r] = s;
+            d.mpart[((size_t)grp * T + t) * d.seg.zp + (size_t)xg * d.L + n0 + r] = (uint16_t)f2bf(s);
         }
     }
 }

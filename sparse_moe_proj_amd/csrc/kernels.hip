@@ -623,13 +623,13 @@ hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int 
     return last();
 }
 
-hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
+hipError_t launch_proj_partials(const uint16_t* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                                 uint16_t* out16, hipStream_t s) {
     if (rows_proj_fits(T, K, 1, G))
         return rows_proj_launch<1>(
-            RowsProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16, nullptr, nullptr, nullptr, 0, nullptr, 0, 0.f}, s);
+            RowsProj{xpart, nullptr, G, W, T, N, K, mode, out32, out16, nullptr, nullptr, nullptr, 0, nullptr, 0, 0.f}, s);
     if (!small_proj_fits(T, K)) return hipErrorInvalidValue;
-    return small_proj_launch<1>(SmallProj{nullptr, xpart, G, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0,
+    return small_proj_launch<1>(SmallProj{xpart, nullptr, G, W, T, N, K, mode, out32, out16, nullptr, nullptr, 0,
                                           nullptr, nullptr},
                                 s);
 }
@@ -647,10 +647,10 @@ __global__ __launch_bounds__(256) void sum_groups_kernel(const float* __restrict
         out16[i] = (uint16_t)f2bf(v);
 }
 
-hipError_t launch_proj_partials_kgroups(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int KG,
+hipError_t launch_proj_partials_kgroups(const uint16_t* xpart, int G, const uint16_t* W, int T, int N, int K, int KG,
                                         float* part, int mode, float* out32, uint16_t* out16, hipStream_t s) {
     if (!small_proj_fits(T, K)) return hipErrorInvalidValue;
-    SmallProj p{nullptr, xpart, G, W, T, N, K, 3, part, nullptr, nullptr, nullptr, 0, nullptr, nullptr};
+    SmallProj p{xpart, nullptr, G, W, T, N, K, 3, part, nullptr, nullptr, nullptr, 0, nullptr, nullptr};
     p.KG = KG;
     hipError_t e = small_proj_launch<1>(p, s);
     if (e != hipSuccess) return e;

@@ -124,13 +124,13 @@ hipError_t launch_fold_router(const uint16_t* D, const uint16_t* Wr, int E, int 
                               int Eg = 0);
 
 // U projection of a small batch with expert groups: input rows of KG * K columns, the sum (in
-// order) of G fp32 partials [G][T][KG * K]; one launch multiplies each K group into part
+// order, in fp32) of G bf16 partials [G][T][KG * K]; one launch multiplies each K group into part
 // [KG][T][N] fp32, a second sums the groups in order (mode 1: bf16 out16; 2: out32 +=).
-hipError_t launch_proj_partials_kgroups(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int KG,
+hipError_t launch_proj_partials_kgroups(const uint16_t* xpart, int G, const uint16_t* W, int T, int N, int K, int KG,
                                         float* part, int mode, float* out32, uint16_t* out16, hipStream_t s);
 
-// U projection of a small batch whose input is the sum (in order) of G fp32 partials [G][T][K].
-hipError_t launch_proj_partials(const float* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
+// U projection of a small batch whose input is the sum (in order, in fp32) of G bf16 partials [G][T][K].
+hipError_t launch_proj_partials(const uint16_t* xpart, int G, const uint16_t* W, int T, int N, int K, int mode, float* out32,
                                 uint16_t* out16, hipStream_t s);
 
 // Rows of the expert work list's tiles: 16 (small batches), 128 (the block-scaled MXFP4 kernels),
@@ -163,7 +163,7 @@ struct ExpertArgs {
     bool stream_path;
     bool decode_path;  // small batch: gate/up into H, then down + merge into mpart
     int fmt;           // routed expert records: 0 bf16, 1 MXFP4, 2 NVFP4
-    float* mpart;      // [decode_groups()][T][zp] partial merged rows (decode path)
+    uint16_t* mpart;   // [decode_groups()][T][zp] partial merged rows in bf16 (decode path)
     const float* w;
     const int2* rowinfo;  // decode path: [T*k] (token, weight bits) per permuted position
     const ExpertRoute* route;  // decode path: non-null = route inside the gate/up launch

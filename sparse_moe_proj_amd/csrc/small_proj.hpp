@@ -4,7 +4,7 @@
 // into contiguous ranges and each wave requests all weight units of its range (up to SMAX MFMA
 // steps at a time) before anything else, so the whole range is in flight at once.  While those
 // loads travel, the workgroup stages the activations of the first 16 tokens into LDS as bf16
-// (XM = 0: a bf16 [T][K] input; XM = 1: the sum, in order, of G fp32 partial inputs [G][T][K],
+// (XM = 0: a bf16 [T][K] input; XM = 1: the fp32 sum, in order, of G bf16 partial inputs [G][T][K],
 // rounded once; XM = 2: bf16(RMSNorm(h)) of an fp32 residual h [T][K] with unit gain, each
 // token's sum of squares taken by one wave in a fixed order), so the token operand is read from
 // LDS rather than once per wave from L2.  Further groups of 16 tokens
@@ -19,8 +19,8 @@
 namespace lmoe {
 
 struct SmallProj {
-    const uint16_t* x16;  // XM 0: [T][K] bf16
-    const float* xpart;   // XM 1: [G][T][K] fp32; XM 2: the residual h [T][K] fp32
+    const uint16_t* x16;  // XM 0: [T][K] bf16; XM 1: [G][T][K] bf16 partials (summed in fp32)
+    const float* xpart;   // XM 2: the residual h [T][K] fp32
     int G;
     const uint16_t* W;    // [N][K] bf16
     int T, N, K, mode;    // mode 0: out32 = v, out16 = bf16(v); 1: out16 = bf16(v); 2: out32 += v;
@@ -153,17 +153,8 @@ __global__ __launch_bounds__(64 * W) void small_proj_kernel(const SmallProj p) {
                         } else {
                             float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                             for (int q = 0; q < p.G; ++q) {
-                                const float* src = p.xpart + ((size_t)q * T + t0 + t) * KP + (size_t)cur.kg * K + c * 8;
-                                const float4 u0 = *reinterpret_cast<const float4*>(src);
-                                const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
-                                a[0] += u0.x;
-                                a[1] += u0.y;
-                                a[2] += u0.z;
-                                a[3] += u0.w;
-                                a[4] += u1.x;
-                                a[5] += u1.y;
-                                a[6] += u1.z;
-                                a[7] += u1.w;
+                                const uint4 u = ld16(p.x16 + ((size_t)q * T + t0 + t) * KP + (size_t)cur.kg * K + c * 8);
+                                add_bf16x8(a, u);
                             }
                             v = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]),
                                            pack_bf2(a[6], a[7]));
@@ -252,8 +243,8 @@ constexpr int kRowsMaxG = 2;  // XM 1: partial inputs held in registers per step
 __host__ __device__ constexpr int rows_proj_smax(int XM) { return XM == 0 ? 12 : XM == 1 ? 7 : 10; }
 
 struct RowsProj {
-    const uint16_t* x16;  // XM 0: [T][K] bf16
-    const float* xf;      // XM 1: [G][T][K] fp32 partials; XM 2: the residual h [T][K] fp32
+    const uint16_t* x16;  // XM 0: [T][K] bf16; XM 1: [G][T][K] bf16 partials (summed in fp32)
+    const float* xf;      // XM 2: the residual h [T][K] fp32
     int G;
     const uint16_t* W;    // [N][K] bf16
     int T, N, K, mode;    // mode 0: out32 = v, out16 = bf16(v) (out16h = fp16(v) if set); 1: out16 =
@@ -272,7 +263,7 @@ struct RowsProj {
 template <int W, int XM>
 __global__ __launch_bounds__(64 * W) void rows_proj_kernel(const RowsProj p) {
     constexpr int kRowsSmax = rows_proj_smax(XM);
-    constexpr int XR = XM == 0 ? 1 : XM == 2 ? 2 : 2 * kRowsMaxG;  // 16-byte loads per step
+    constexpr int XR = XM == 0 ? 1 : XM == 2 ? 2 : kRowsMaxG;  // 16-byte loads per step
     __shared__ float red[W][256];
     __shared__ float ssq[W][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -303,12 +294,8 @@ __global__ __launch_bounds__(64 * W) void rows_proj_kernel(const RowsProj p) {
                 xr[i][1] = ok ? ld16(src + 4) : zero4();
             } else {
 #pragma unroll
-                for (int q = 0; q < kRowsMaxG; ++q) {
-                    const float* src = p.xf + ((size_t)q * T + t) * K + k0;
-                    const bool l = ok && q < p.G;
-                    xr[i][2 * q] = l ? ld16(src) : zero4();
-                    xr[i][2 * q + 1] = l ? ld16(src + 4) : zero4();
-                }
+                for (int q = 0; q < kRowsMaxG; ++q)
+                    xr[i][q] = ok && q < p.G ? ld16(p.x16 + ((size_t)q * T + t) * K + k0) : zero4();
             }
         }
     };
@@ -322,24 +309,9 @@ __global__ __launch_bounds__(64 * W) void rows_proj_kernel(const RowsProj p) {
 #pragma unroll
             for (int i = 0; i < kRowsSmax; ++i) {
                 if (i >= nst) break;
-                float a[8];
-                const float* u0 = reinterpret_cast<const float*>(&xr[i][0]);
-                const float* u1 = reinterpret_cast<const float*>(&xr[i][1]);
+                float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    a[c] = u0[c];
-                    a[4 + c] = u1[c];
-                }
-#pragma unroll
-                for (int q = 1; q < kRowsMaxG; ++q) {
-                    const float* v0 = reinterpret_cast<const float*>(&xr[i][2 * q]);
-                    const float* v1 = reinterpret_cast<const float*>(&xr[i][2 * q + 1]);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        a[c] += v0[c];
-                        a[4 + c] += v1[c];
-                    }
-                }
+                for (int q = 0; q < kRowsMaxG; ++q) add_bf16x8(a, xr[i][q]);
                 xv[i] = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
             }
         } else {
