@@ -119,7 +119,7 @@ Layout plan(const Dims& d, int T) {
     lo.fused_router = !d.f32 && small_proj_fits(T, d.H);
     // expert groups take the logits from x and the folded router for every batch (two halves)
     const bool halves = lo.fused_router || d.G > 1;
-    lo.BM = expert_tile_rows(lo.stream_path, lo.mx_path);
+    lo.BM = expert_tile_rows(lo.stream_path, lo.mx_path, T, d.k, d.E);
     lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path, lo.mx_path);
     lo.Hs = std::max(d.F, d.Fs);
     lo.R = T * d.k + (has_shared ? T : 0);
@@ -492,6 +492,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
                  lo.decode_path, d.fmt, mpart, wts, rowinfo, route_in_experts ? &route : nullptr, d.Eg, d.Lz,
                  lo.deq_path ? static_cast<uint16_t*>(at(lo.deq)) : nullptr,
                  lo.deq_path ? static_cast<float*>(at(lo.deq_ts)) : nullptr, offsets};
+    a.tile_rows = lo.BM;
     if (lo.mx_path) {
         a.mx_path = true;
         a.z8 = static_cast<uint8_t*>(at(lo.z8));

@@ -135,7 +135,7 @@ hipError_t launch_proj_partials(const uint16_t* xpart, int G, const uint16_t* W,
 
 // Rows of the expert work list's tiles: 16 (small batches), 128 (the block-scaled MXFP4 kernels),
 // else the rows of the large-batch bf16 GEMM tiles (256).
-int expert_tile_rows(bool stream_path, bool mx_path);
+int expert_tile_rows(bool stream_path, bool mx_path, int T, int k, int E);
 int expert_max_tiles(int T, int k, int E, int has_shared, bool stream_path, bool mx_path);
 
 // Routing done inside the small-batch gate/up launch (T <= 64): the logits (hi half, and the lo
@@ -188,6 +188,7 @@ struct ExpertArgs {
     uint8_t* h4 = nullptr;
     uint8_t* h4s = nullptr;
     uint16_t* h16 = nullptr;
+    int tile_rows = 0;  // rows of the work list's tiles (expert_tile_rows)
 };
 
 // Large 4-bit batches: minimum T at which the records of the experts with tokens are decoded to

@@ -90,8 +90,10 @@ def test_prefill_mxfp4_t16384_every_tile(ws):
 SMALL = gen.Shape(hidden=256, latent=192, n_experts=24, top_k=3, ffn=128, shared_ffn=64)
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 17, 100, 300, 700, 1500])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 100, 300, 700, 1500, 2100, 3001])
 def test_small_bf16_ragged(T, ws):
+    """Both small-batch paths, the 16-row streaming tiles and the pipelined GEMMs on 128-row
+    tiles and (from T k >= 256 E: T = 2100, 3001) on 256-row tiles, with ragged last tiles."""
     wl, lw = small_layer(SMALL, "bf16", "bf16", "bf16")
     dl = DeviceLayer(lw, act="bf16")
     x = gen.make_tokens(wl, T=T, salt=T)
