@@ -1,20 +1,21 @@
 // Pipelined bf16 MFMA GEMM for batches of many tokens: C[m][n] = sum_k A[m][k] * B[n][k].
 //
 // One workgroup of WR x WC waves computes a BM x BN tile (each wave (BM/WR) x (BN/WC) with
-// v_mfma_f32_32x32x16_bf16).  K advances in stages of 64 columns.  Each stage's operands are
-// copied straight from global memory into LDS with global_load_lds_dwordx4 (no register
-// staging), NS stages deep, so the copies of the next NS-1 stages are in flight while one
-// stage is multiplied; one barrier per stage.
+// v_mfma_f32_32x32x16_bf16).  K advances in stages of BK columns (64, or 32 for a deeper
+// pipeline in the same LDS).  Each stage's operands are copied straight from global memory into
+// LDS with global_load_lds_dwordx4 (no register staging), NS stages deep, so the copies of the
+// next NS-1 stages are in flight while one stage is multiplied; one barrier per stage.
 //
 // A copy instruction moves 1 KB: lane l writes LDS position l of the instruction's block, and
 // the lane picks its global source so that
-//   * a row-major operand block holds 8 rows x 128 bytes (a full cache line per row), with the
-//     16-byte chunks of row r stored XOR-swizzled by ((r >> 1) & 7): a fragment read takes one
-//     chunk from each of 16 consecutive rows, and a row's 32 banks are set by its parity and the
-//     chunk, so the 8 rows of each parity must use 8 different chunks (swizzling by (r & 7) gave
-//     rows r and r + 8 the same banks);
+//   * a row-major operand block holds 512/BK rows x 2 BK bytes (BK = 64: a full cache line per
+//     row), with the U = BK/8 16-byte chunks of row r stored XOR-swizzled by (r U / 16) mod U: a
+//     fragment read takes one chunk from each of 16 consecutive rows, the 64 banks of 4 bytes
+//     hold 16/U rows side by side, so the U rows of those 16 that share banks must use U
+//     different chunks (for BK = 64 the swizzle (r >> 1) & 7; swizzling by (r & 7) gave rows r
+//     and r + 8 the same banks);
 //   * a packed operand (weights stored as 16-row x 32-column tiles, see packed_row) keeps its
-//     tile order: a 16-row block of one stage is two consecutive tiles, 2 KB contiguous in HBM.
+//     tile order: a 16-row block of one stage is BK/32 consecutive 1 KB tiles, contiguous in HBM.
 // A problem type P supplies, per operand, a base pointer for the workgroup and, per lane and copy
 // instruction, the 32-bit byte offset of the stage-0 source (rows outside the problem are
 // clamped to valid rows; their results are never stored), whether each operand is packed
@@ -25,23 +26,24 @@
 
 namespace lmoe {
 
-template <int BM, int BN, int NS, int WR = 2, int WC = 2>
+template <int BM, int BN, int NS, int WR = 2, int WC = 2, int BK = 64>
 struct PipeShape {
-    static constexpr int kBM = BM, kBN = BN, kNS = NS;
+    static constexpr int kBM = BM, kBN = BN, kNS = NS, kBK = BK;
+    static constexpr int kU = BK / 8;  // 16-byte units of a row per stage
+    static_assert(BK == 64 || BK == 32, "stages of 64 or 32 columns");
     static constexpr int kWR = WR, kWC = WC, kWaves = WR * WC, kThreads = 64 * WR * WC;
     static constexpr int kWM = BM / WR, kWN = BN / WC;  // wave tile
     static constexpr int kMB = kWM / 32, kNB = kWN / 32;
-    static constexpr int kAI = BM / 8, kBI = BN / 8;                // 1 KB copy instructions per stage
+    static constexpr int kAI = BM * kU / 64, kBI = BN * kU / 64;    // 1 KB copy instructions per stage
     static constexpr int kAIW = kAI / kWaves, kBIW = kBI / kWaves;  // per wave
     static_assert(kAI % kWaves == 0 && kBI % kWaves == 0, "copies split over the waves");
     static constexpr int kLoadsPerStage = kAIW + kBIW;
-    static constexpr int kStageUnits = (BM + BN) * 8;  // 16-byte units per stage
+    static constexpr int kStageUnits = (BM + BN) * kU;  // 16-byte units per stage
     static_assert(NS * kStageUnits * 16 <= 160 * 1024, "LDS budget");
+    // byte step from one stage to the next: a row-major row advances BK columns, a packed 16-row
+    // block BK/32 tiles of 1 KB
+    static constexpr int kRowMajorStep = 2 * BK, kPackedStep = 32 * BK;
 };
-
-// Byte step from one stage to the next: row-major rows advance 64 columns (128 bytes); a
-// packed 16-row block advances two 1 KB tiles.
-constexpr int kRowMajorStep = 128, kPackedStep = 2048;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -49,20 +51,32 @@ __device__ __forceinline__ void lds_copy16(const void* g, uint4* lds_block) {
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_block, 16, 0, 0);
 }
 
-// Row of copy instruction i for this lane (row-major operands: rows 8i .. 8i+7).
-__device__ __forceinline__ int rowmajor_row(int i, int lane) { return 8 * i + (lane >> 3); }
+// Swizzle of row r's 16-byte chunks in a row-major stage block of U chunks per row.
+template <int U = 8>
+__device__ __forceinline__ int rowmajor_swz(int r) { return (r * U / 16) & (U - 1); }
+
+// Row of copy instruction i for this lane (row-major operands: rows (64/U) i .. (64/U) i + 64/U - 1).
+template <int U = 8>
+__device__ __forceinline__ int rowmajor_row(int i, int lane) { return (64 / U) * i + lane / U; }
 
 // Byte offset of this lane's 16-byte chunk of copy instruction i at stage 0, for a row-major
 // source row that starts `row_bytes` bytes after the operand base.
+template <int U = 8>
 __device__ __forceinline__ uint32_t rowmajor_off(uint32_t row_bytes, int i, int lane) {
-    const int chunk = (lane & 7) ^ ((rowmajor_row(i, lane) >> 1) & 7);
+    const int chunk = (lane & (U - 1)) ^ rowmajor_swz<U>(rowmajor_row<U>(i, lane));
     return row_bytes + chunk * 16;
 }
 
-// Byte offset (from the packed matrix base) of copy instruction i: tile (i & 1) of 16-row block nb.
+// Byte offset (from the packed matrix base) of copy instruction i: tile i mod (U/4) of 16-row
+// block nb (the stage's U/4 tiles of that block).
+template <int U = 8>
 __device__ __forceinline__ uint32_t packed_off(int nb, int i, int K, int lane) {
-    return (uint32_t)(((nb * (K / 32) + (i & 1)) * 64 + lane) * 16);
+    return (uint32_t)(((nb * (K / 32) + i % (U / 4)) * 64 + lane) * 16);
 }
+
+// First 16-row block of packed copy instruction i
+template <int U = 8>
+__device__ __forceinline__ int packed_block(int i) { return i / (U / 4); }
 
 // Workgroup barrier without a memory fence: the copies a stage needs are waited for explicitly
 // (vmcnt), so the fence that __syncthreads implies would only drain the copies still in flight.
@@ -99,13 +113,13 @@ __device__ __forceinline__ void wait_stage(int left) {
         wait_vm<0>();
 }
 
-// 16-byte unit of (row, 8-column unit u of the stage) in an operand block
-template <bool PACKED>
+// 16-byte unit of (row, 8-column unit u of the stage) in an operand block of U units per row
+template <bool PACKED, int U = 8>
 __device__ __forceinline__ int frag_pos(int row, int u) {
     if constexpr (PACKED)
-        return ((row >> 4) * 2 + (u >> 2)) * 64 + (u & 3) * 16 + (row & 15);
+        return ((row >> 4) * (U / 4) + (u >> 2)) * 64 + (u & 3) * 16 + (row & 15);
     else
-        return row * 8 + (u ^ ((row >> 1) & 7));
+        return row * U + (u ^ rowmajor_swz<U>(row));
 }
 
 // LDS byte address of a pointer into a __shared__ array.
@@ -194,14 +208,14 @@ __device__ __forceinline__ PipeCopies<S> pipe_copies(const P& p, const typename 
 // Stage kt of the tile into stage buffer buf (A block of BM rows, then B block of BN rows).
 template <class S, class P>
 __device__ __forceinline__ void pipe_issue(const PipeCopies<S>& c, uint4* buf, int kt, int wave) {
-    constexpr int kAStep = P::kAPacked ? kPackedStep : kRowMajorStep;
-    constexpr int kBStep = P::kBPacked ? kPackedStep : kRowMajorStep;
+    constexpr int kAStep = P::kAPacked ? S::kPackedStep : S::kRowMajorStep;
+    constexpr int kBStep = P::kBPacked ? S::kPackedStep : S::kRowMajorStep;
 #pragma unroll
     for (int i = 0; i < S::kAIW; ++i)
         lds_copy16(c.abase + (c.as[i] + (uint32_t)(kt * kAStep)), buf + (wave * S::kAIW + i) * 64);
 #pragma unroll
     for (int i = 0; i < S::kBIW; ++i)
-        lds_copy16(c.bbase + (c.bs[i] + (uint32_t)(kt * kBStep)), buf + S::kBM * 8 + (wave * S::kBIW + i) * 64);
+        lds_copy16(c.bbase + (c.bs[i] + (uint32_t)(kt * kBStep)), buf + S::kBM * S::kU + (wave * S::kBIW + i) * 64);
 }
 
 // Stages 0 .. NS-2 of a tile with nk stages into the first stage buffers.
@@ -240,15 +254,17 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
     auto compute = [&](const uint4* buf) {
         if (nvb == 0) return;
         const uint32_t A = lds_addr(buf);
-        const uint32_t B = A + S::kBM * 8 * 16;
+        const uint32_t B = A + S::kBM * S::kU * 16;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < S::kBK / 16; ++ks) {
             const int u = 2 * ks + fq;
             uint32_t aa[S::kMB], ba[S::kNB];
 #pragma unroll
-            for (int i = 0; i < S::kMB; ++i) aa[i] = A + 16 * frag_pos<P::kAPacked>(wm * S::kWM + i * 32 + fr, u);
+            for (int i = 0; i < S::kMB; ++i)
+                aa[i] = A + 16 * frag_pos<P::kAPacked, S::kU>(wm * S::kWM + i * 32 + fr, u);
 #pragma unroll
-            for (int j = 0; j < S::kNB; ++j) ba[j] = B + 16 * frag_pos<P::kBPacked>(wn * S::kWN + j * 32 + fr, u);
+            for (int j = 0; j < S::kNB; ++j)
+                ba[j] = B + 16 * frag_pos<P::kBPacked, S::kU>(wn * S::kWN + j * 32 + fr, u);
             uint4 af[S::kMB], bfv[S::kNB];
             lds_read_frags<S::kMB, S::kNB>(aa, ba, af, bfv);
 #pragma unroll

@@ -491,7 +491,13 @@ using PipeP = PipeShape<LMOE_PROJ_PIPE_M, LMOE_PROJ_PIPE_N, LMOE_PROJ_PIPE_NS, L
 #ifndef LMOE_BIG_WC
 #define LMOE_BIG_WC 4
 #endif
-using PipeB = PipeShape<256, LMOE_PIPE_N, 2, LMOE_BIG_WR, LMOE_BIG_WC>;
+#ifndef LMOE_BIG_BK
+#define LMOE_BIG_BK 64
+#endif
+#ifndef LMOE_BIG_NS
+#define LMOE_BIG_NS 2
+#endif
+using PipeB = PipeShape<256, LMOE_PIPE_N, LMOE_BIG_NS, LMOE_BIG_WR, LMOE_BIG_WC, LMOE_BIG_BK>;
 static_assert(PipeB::kBN == PipeL::kBN, "big and small tiles cover the same columns per tile");
 
 // Persistent launch: at most LMOE_STREAM_GRID workgroups walk max_tiles x row-group items.

@@ -698,7 +698,7 @@ struct PipeProj : TileProj<S> {
     static constexpr bool kAPacked = false, kBPacked = false;
     __device__ int m_tiles() const { return (B::M + S::kBM - 1) / S::kBM; }
     __device__ int valid_rows(const typename B::Ctx& c) const { return min(S::kBM, B::M - c.m0); }
-    __device__ int k_stages(const typename B::Ctx&) const { return B::K / 64; }
+    __device__ int k_stages(const typename B::Ctx&) const { return B::K / S::kBK; }
     __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
         return reinterpret_cast<const uint8_t*>(B::x + (size_t)c.m0 * B::K);
     }
@@ -706,12 +706,12 @@ struct PipeProj : TileProj<S> {
         return reinterpret_cast<const uint8_t*>(B::W + (size_t)c.n0 * B::K);
     }
     __device__ uint32_t src_a(const typename B::Ctx& c, int i, int lane) const {
-        const int r = min(rowmajor_row(i, lane), B::M - 1 - c.m0);
-        return rowmajor_off((uint32_t)r * B::K * 2, i, lane);
+        const int r = min(rowmajor_row<S::kU>(i, lane), B::M - 1 - c.m0);
+        return rowmajor_off<S::kU>((uint32_t)r * B::K * 2, i, lane);
     }
     __device__ uint32_t src_b(const typename B::Ctx& c, int i, int lane) const {
-        const int r = min(rowmajor_row(i, lane), B::N - 1 - c.n0);
-        return rowmajor_off((uint32_t)r * B::K * 2, i, lane);
+        const int r = min(rowmajor_row<S::kU>(i, lane), B::N - 1 - c.n0);
+        return rowmajor_off<S::kU>((uint32_t)r * B::K * 2, i, lane);
     }
     struct Prep {};
     template <int MB>
@@ -729,22 +729,23 @@ struct PipeUp : TileUp<S> {
     static constexpr bool kAPacked = false, kBPacked = true;
     __device__ int m_tiles() const { return B::seg.count(); }
     __device__ int valid_rows(const typename B::Ctx& c) const { return c.nrows; }
-    __device__ int k_stages(const typename B::Ctx&) const { return B::L / 64; }
+    __device__ int k_stages(const typename B::Ctx&) const { return B::L / S::kBK; }
     __device__ const uint8_t* a_base(const typename B::Ctx&) const { return reinterpret_cast<const uint8_t*>(B::z16); }
     __device__ const uint8_t* b_base(const typename B::Ctx& c) const { return reinterpret_cast<const uint8_t*>(c.g); }
     // gathered token rows: byte offsets into z16 stay below 2^32 (T * zp * 2 < 2^32 is checked
     // on the host)
     __device__ uint32_t src_a(const typename B::Ctx& c, int i, int lane) const {
-        const int r = min(rowmajor_row(i, lane), c.nrows - 1);
-        return rowmajor_off((uint32_t)(B::seg.z_off(c.seg, B::seg.token_of(c.seg, c.row0 + r), B::L) * 2), i, lane);
+        const int r = min(rowmajor_row<S::kU>(i, lane), c.nrows - 1);
+        return rowmajor_off<S::kU>((uint32_t)(B::seg.z_off(c.seg, B::seg.token_of(c.seg, c.row0 + r), B::L) * 2), i,
+                                   lane);
     }
     __device__ uint32_t src_b(const typename B::Ctx& c, int i, int lane) const {
-        const int r = (i >> 1) * 16;  // first B-tile row of this copy (16 rows: one matrix, one f block)
+        const int r = packed_block<S::kU>(i) * 16;  // first B-tile row of this copy (16 rows: one matrix, one f block)
         const int wc = r / S::kWN, rr = r % S::kWN;
         const int f = c.f0 + wc * B::kHalf + rr % B::kHalf;
         const int nb = min(f, c.F - 16) >> 4;
         const uint32_t mat = rr >= B::kHalf ? (uint32_t)c.F * B::L * 2 : 0u;  // up follows gate
-        return mat + packed_off(nb, i, B::L, lane);
+        return mat + packed_off<S::kU>(nb, i, B::L, lane);
     }
     struct Prep {};
     template <int MB>
@@ -762,18 +763,18 @@ struct PipeDown : TileDown<S> {
     static constexpr bool kAPacked = false, kBPacked = true;
     __device__ int m_tiles() const { return B::seg.count(); }
     __device__ int valid_rows(const typename B::Ctx& c) const { return c.nrows; }
-    __device__ int k_stages(const typename B::Ctx& c) const { return c.F / 64; }
+    __device__ int k_stages(const typename B::Ctx& c) const { return c.F / S::kBK; }
     __device__ const uint8_t* a_base(const typename B::Ctx& c) const {
         return reinterpret_cast<const uint8_t*>(B::H + (size_t)c.row0 * B::Hs);
     }
     __device__ const uint8_t* b_base(const typename B::Ctx& c) const { return reinterpret_cast<const uint8_t*>(c.d); }
     __device__ uint32_t src_a(const typename B::Ctx& c, int i, int lane) const {
-        const int r = min(rowmajor_row(i, lane), c.nrows - 1);
-        return rowmajor_off((uint32_t)r * B::Hs * 2, i, lane);
+        const int r = min(rowmajor_row<S::kU>(i, lane), c.nrows - 1);
+        return rowmajor_off<S::kU>((uint32_t)r * B::Hs * 2, i, lane);
     }
     __device__ uint32_t src_b(const typename B::Ctx& c, int i, int lane) const {
-        const int nb = min(c.n0 + (i >> 1) * 16, B::L - 16) >> 4;
-        return packed_off(nb, i, c.F, lane);
+        const int nb = min(c.n0 + packed_block<S::kU>(i) * 16, B::L - 16) >> 4;
+        return packed_off<S::kU>(nb, i, c.F, lane);
     }
     // Destination row of every accumulator row (-1: none), read before the store (the next tile's
     // copies are issued in between, and a wait for a later global load would wait for them too).
