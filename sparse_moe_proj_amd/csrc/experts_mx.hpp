@@ -385,23 +385,6 @@ __device__ __forceinline__ uint32_t mx8_scale_bits(float amax) {
 // 1 / scale for a biased scale exponent sb (0 .. 246)
 __device__ __forceinline__ float mx8_inv_scale(uint32_t sb) { return __uint_as_float((254u - sb) << 23); }
 
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-    const uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = fminf(fabsf(v), 448.f);
-    if (a < 0.015625f) return s | (uint32_t)__builtin_rintf(a * 512.f);  // subnormals (steps of 2^-9)
-    uint32_t u = __float_as_uint(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the 23-bit significand to 3 bits, ties to even
-    return s | ((u >> 20) - (120u << 3));
-}
-
-// E2M1 (OCP FP4): nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code; beyond 6: 6.
-__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
-    const uint32_t s = (__float_as_uint(v) >> 28) & 8u;
-    const float a = fabsf(v);
-    const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-                     : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
-    return s | c;
-}
 // MXFP4 scale: the smallest power of two 2^E with amax / 2^E <= 6 (as mx8_scale_bits, for E2M1)
 __device__ __forceinline__ uint32_t mx4_scale_bits(float amax) {
     const uint32_t u = __float_as_uint(amax);
@@ -445,34 +428,38 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* __restric
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
     const uint32_t sb = mx8_scale_bits(amax);
     const float inv = mx8_inv_scale(sb);
-    uint32_t c[32];
+    // E4M3 codes by the conversion instruction, four per dword (first value in the low byte); it
+    // rounds to nearest even as the software rounding of the format does (checked bit for bit on
+    // every bf16 value of the range and the fp32 values beside each), and |v / scale| <= 448 by
+    // the choice of the scale, so nothing saturates
+    uint32_t c[8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) c[i] = f32_to_e4m3(v[i] * inv);
+    for (int i = 0; i < 8; ++i) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i] * inv, v[4 * i + 1] * inv, 0, false);
+        c[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i + 2] * inv, v[4 * i + 3] * inv, lo, true);
+    }
     uint4* out = reinterpret_cast<uint4*>(q + b * 32);
-    out[0] = make_uint4(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24,
-                        c[8] | c[9] << 8 | c[10] << 16 | c[11] << 24, c[12] | c[13] << 8 | c[14] << 16 | c[15] << 24);
-    out[1] = make_uint4(c[16] | c[17] << 8 | c[18] << 16 | c[19] << 24, c[20] | c[21] << 8 | c[22] << 16 | c[23] << 24,
-                        c[24] | c[25] << 8 | c[26] << 16 | c[27] << 24, c[28] | c[29] << 8 | c[30] << 16 | c[31] << 24);
+    out[0] = make_uint4(c[0], c[1], c[2], c[3]);
+    out[1] = make_uint4(c[4], c[5], c[6], c[7]);
     qs[b] = (uint8_t)sb;
     if (!q4) return;
     const float scale = e8m0_to_f32(sb);
     float r[32], ramax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        r[i] = v[i] - e4m3_to_f32(c[i]) * scale;
+    static_for<32>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        r[i] = v[i] - __builtin_amdgcn_cvt_f32_fp8((int)c[i / 4], i % 4) * scale;
         ramax = fmaxf(ramax, fabsf(r[i]));
-    }
+    });
     const uint32_t s4 = mx4_scale_bits(ramax);
     const float inv4 = mx8_inv_scale(s4);
-    uint32_t n[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x |= f32_to_e2m1(r[8 * i + j] * inv4) << (4 * j);
-        n[i] = x;
-    }
-    *reinterpret_cast<uint4*>(q4 + b * 16) = make_uint4(n[0], n[1], n[2], n[3]);
+    // E2M1 codes two per byte (even value in the low nibble), by the conversion instruction with a
+    // unit scale on the pre-scaled values (|r / scale| <= 6 by the choice of the scale)
+    int n[4] = {0, 0, 0, 0};
+    static_for<16>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        n[m / 4] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(n[m / 4], r[2 * m] * inv4, r[2 * m + 1] * inv4, 1.0f, m % 4);
+    });
+    *reinterpret_cast<uint4*>(q4 + b * 16) = make_uint4((uint32_t)n[0], (uint32_t)n[1], (uint32_t)n[2], (uint32_t)n[3]);
     q4s[b] = (uint8_t)s4;
 }
 
