@@ -106,61 +106,50 @@ __device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, co
     for (int j = 0; j < NV; ++j) v2[j] = r2[min(lane + 64 * j, E - 1)];
 }
 
-template <int NV>
-__device__ __forceinline__ void wave_topk_select(const float (&v1)[NV], const float (&v2)[NV], bool has2, int E, int k,
-                                                 int& out, float& out_w) {
+// The k rounds over the lanes' sorted runs: each round takes the wave-wide maximum of the lanes'
+// first keys h[0] (the lowest id among equal maxima), lane r records it (key, id), and the winning
+// lane drops its first key.  H keys per lane take part; returns false when some lane has won H
+// times (its next key was not in the race, so the result may be wrong and the caller must run
+// the rounds over the whole sorted run).
+template <int H>
+__device__ __forceinline__ bool wave_topk_rounds(uint32_t (&h)[H], int (&hid)[H], int k, bool check,
+                                                 uint32_t& sel_key, int& sel_id) {
     const int lane = threadIdx.x & 63;
-    float v[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = has2 ? v1[j] + v2[j] : v1[j];
-    uint32_t key[NV];
-    int id[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        // NaN counts as -inf (never ahead of a number); ids past E get key 0, below every value
-        const float x = v[j] == v[j] ? v[j] : -INFINITY;
-        key[j] = lane + 64 * j < E ? order_key(x) : 0u;
-        id[j] = lane + 64 * j;
-    }
-    // stable descending sort of the lane's keys (odd-even transposition, strict comparisons)
-#pragma unroll
-    for (int ph = 0; ph < NV; ++ph)
-#pragma unroll
-        for (int j = ph & 1; j + 1 < NV; j += 2) {
-            const bool sw = key[j + 1] > key[j];
-            const uint32_t ka = key[j], kb = key[j + 1];
-            const int ia = id[j], ib = id[j + 1];
-            key[j] = sw ? kb : ka;
-            key[j + 1] = sw ? ka : kb;
-            id[j] = sw ? ib : ia;
-            id[j + 1] = sw ? ia : ib;
-        }
-    uint32_t sel_key = 0;
-    int sel_id = -1;
+    int wins = 0;
+    sel_key = 0;
+    sel_id = -1;
 #pragma unroll 1
     for (int r = 0; r < k; ++r) {
-        const uint32_t m = wave_max_u32(key[0]);
-        const uint64_t cand = __ballot(key[0] == m);
+        const uint32_t m = wave_max_u32(h[0]);
+        const uint64_t cand = __ballot(h[0] == m);
         int win = __ffsll((unsigned long long)cand) - 1;
         if (__popcll(cand) > 1) {  // equal maxima: the lowest id among the candidates
-            const uint32_t lo = ~wave_max_u32(key[0] == m ? ~(uint32_t)id[0] : 0u);
-            win = __ffsll((unsigned long long)__ballot(key[0] == m && (uint32_t)id[0] == lo)) - 1;
+            const uint32_t lo = ~wave_max_u32(h[0] == m ? ~(uint32_t)hid[0] : 0u);
+            win = __ffsll((unsigned long long)__ballot(h[0] == m && (uint32_t)hid[0] == lo)) - 1;
         }
-        const int wid = __builtin_amdgcn_readlane(id[0], win);
+        const int wid = __builtin_amdgcn_readlane(hid[0], win);
         if (lane == r) {
             sel_key = m;
             sel_id = wid;
         }
         if (lane == win) {
 #pragma unroll
-            for (int j = 0; j + 1 < NV; ++j) {
-                key[j] = key[j + 1];
-                id[j] = id[j + 1];
+            for (int j = 0; j + 1 < H; ++j) {
+                h[j] = h[j + 1];
+                hid[j] = hid[j + 1];
             }
-            key[NV - 1] = 0u;
+            h[H - 1] = 0u;
+            ++wins;
         }
     }
-    // the first winner holds the largest kept logit; weights over the kept logits
+    return !check || __ballot(wins >= H) == 0ull;
+}
+
+// Softmax over the kept logits (lanes 0 .. k-1 hold them in selection order) and each kept id's
+// rank among the kept ids in ascending order.
+__device__ __forceinline__ void wave_topk_finish(uint32_t sel_key, int sel_id, int k, int& out, float& out_w) {
+    const int lane = threadIdx.x & 63;
+    // the first winner holds the largest kept logit
     const float vmax = key_value((uint32_t)__builtin_amdgcn_readlane((int)sel_key, 0));
     const float e = lane < k ? expf(key_value(sel_key) - vmax) : 0.f;
     const float s = wave_sum_f32(e);
@@ -169,6 +158,71 @@ __device__ __forceinline__ void wave_topk_select(const float (&v1)[NV], const fl
     for (int r = 0; r < k; ++r) pos += __builtin_amdgcn_readlane(sel_id, r) < sel_id ? 1 : 0;
     out = lane < k ? (pos << 16) | sel_id : -1;
     out_w = lane < k ? e / s : 0.f;
+}
+
+// Stable descending order of a lane's first P keys: P bubble passes from the end, each moving the
+// largest remaining key to the front with strict comparisons (equal keys keep their order, i.e.
+// ascending id).  P = N gives the whole run sorted.
+template <int N, int P>
+__device__ __forceinline__ void lane_sort_prefix(uint32_t (&key)[N], int (&id)[N]) {
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int j = N - 2; j >= p; --j) {
+            const bool sw = key[j + 1] > key[j];
+            const uint32_t ka = key[j], kb = key[j + 1];
+            const int ia = id[j], ib = id[j + 1];
+            key[j] = sw ? kb : ka;
+            key[j + 1] = sw ? ka : kb;
+            id[j] = sw ? ib : ia;
+            id[j + 1] = sw ? ia : ib;
+        }
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_topk_select(const float (&v1)[NV], const float (&v2)[NV], bool has2, int E, int k,
+                                                 int& out, float& out_w) {
+    const int lane = threadIdx.x & 63;
+    uint32_t key[NV];
+    int id[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const float v = has2 ? v1[j] + v2[j] : v1[j];
+        // NaN counts as -inf (never ahead of a number); ids past E get key 0, below every value
+        const float x = v == v ? v : -INFINITY;
+        key[j] = lane + 64 * j < E ? order_key(x) : 0u;
+        id[j] = lane + 64 * j;
+    }
+    uint32_t sel_key;
+    int sel_id;
+    // Most rounds take a lane's first few keys only: the first H keys of each lane race, which is
+    // exact unless some lane wins H times; then the rounds run again over the whole sorted run.
+    constexpr int H = NV < 4 ? NV : 4;
+    if constexpr (H == NV) {
+        lane_sort_prefix<NV, NV>(key, id);
+        wave_topk_rounds<NV>(key, id, k, false, sel_key, sel_id);
+    } else {
+        uint32_t kf[NV];
+        int idf[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            kf[j] = key[j];
+            idf[j] = id[j];
+        }
+        lane_sort_prefix<NV, H>(key, id);
+        uint32_t hk[H];
+        int hi[H];
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            hk[j] = key[j];
+            hi[j] = id[j];
+        }
+        if (!wave_topk_rounds<H>(hk, hi, k, true, sel_key, sel_id)) {
+            lane_sort_prefix<NV, NV>(kf, idf);
+            wave_topk_rounds<NV>(kf, idf, k, false, sel_key, sel_id);
+        }
+    }
+    wave_topk_finish(sel_key, sel_id, k, out, out_w);
 }
 
 template <int NV>
