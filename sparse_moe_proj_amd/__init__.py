@@ -115,7 +115,11 @@ def make_config(hidden, latent, n_experts, top_k, ffn, shared_ffn, act="bf16", d
 
 
 def make_weights(D, U, Wr, br, shared, experts, Gr=None):
-    return lmoe_weights(_p(D), _p(U), _p(Wr), _p(br), _p(shared), _p(experts), _p(Gr))
+    """The struct of device pointers; it also holds references to the tensors given, so that a
+    temporary (make_weights(..., to_device(a), ...)) stays allocated while the struct is in use."""
+    w = lmoe_weights(_p(D), _p(U), _p(Wr), _p(br), _p(shared), _p(experts), _p(Gr))
+    w._keep = (D, U, Wr, br, shared, experts, Gr)
+    return w
 
 
 LMOE_N_STAGES = 9
@@ -126,8 +130,10 @@ def make_opts(prenorm=0, residual=0, aux_z=None, aux_ids=None, aux_w=None, aux_o
               stage_events=None):
     """stage_events: None or a ctypes array of 2 * LMOE_N_STAGES hipEvent_t handles (keep it alive)."""
     ev = ctypes.cast(stage_events, ctypes.c_void_p).value if stage_events is not None else None
-    return lmoe_forward_opts(int(prenorm), int(residual), _p(aux_z), _p(aux_ids), _p(aux_w), _p(aux_offsets),
-                             _p(aux_perm), ev)
+    o = lmoe_forward_opts(int(prenorm), int(residual), _p(aux_z), _p(aux_ids), _p(aux_w), _p(aux_offsets),
+                          _p(aux_perm), ev)
+    o._keep = (aux_z, aux_ids, aux_w, aux_offsets, aux_perm, stage_events)
+    return o
 
 
 def last_error() -> str:

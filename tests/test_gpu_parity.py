@@ -102,6 +102,32 @@ def test_small_bf16_ragged(T, ws):
     check_block(lw, x, "bf16", out, label=f"small_bf16 T={T}")
 
 
+ROUTE_512 = gen.Shape(hidden=256, latent=128, n_experts=512, top_k=10, ffn=128, shared_ffn=128)
+
+
+@pytest.mark.parametrize("expert", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("T", [8, 40])
+def test_many_winners_in_one_lane_whole_block(T, expert, ws):
+    """The routing inside the small-batch gate/up launch when one lane of the top-k wave holds 8
+    of the 10 kept experts (ids 5 + 64 j), which takes the top-k's exact fallback: the router
+    weights are zero, so every token's logits are the bias, built with those 8 experts and two
+    others far above the rest (ties among the kept ones only)."""
+    wl, lw = small_layer(ROUTE_512, "bf16", "bf16", expert)
+    E = ROUTE_512.n_experts
+    lw.Wr = np.zeros_like(lw.Wr)
+    br = np.random.default_rng(5).uniform(-3.0, 0.0, E).astype(np.float32)
+    br[[5 + 64 * j for j in range(8)]] = [14, 14, 13, 12, 12, 11, 10, 10]
+    br[[6, 200]] = [9.5, 9.0]
+    lw.br = br
+    dl = DeviceLayer(lw, act="bf16")
+    x = gen.make_tokens(wl, T=T, salt=T)
+    out = run_forward(dl, upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    want = sorted([5 + 64 * j for j in range(8)] + [6, 200])
+    assert (host(out["ids"]) == np.array(want)[None, :]).all()
+    check_block(lw, x, "bf16", out, label=f"one-lane winners {expert} T={T}")
+
+
 @pytest.mark.parametrize("T", [1, 5, 16])
 def test_small_bf16_router_unfolded(T, ws):
     """Small batches without the folded router take the z-based router launch."""

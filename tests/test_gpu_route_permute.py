@@ -60,6 +60,38 @@ def test_route_exact_ties_pick_lower_id():
         assert host(ids)[t].tolist() == want
 
 
+@pytest.mark.parametrize("T", [50, 100])
+@pytest.mark.parametrize("k", [10, 16])
+def test_route_many_winners_in_one_lane(T, k):
+    """The wave top-k races each lane's leading keys and falls back to the whole sorted run when
+    one lane (ids e = c mod 64 share lane c) holds several of the winners: tokens whose top k put
+    3, 4, 5 or 8 of the kept experts in one lane, with exact ties inside that lane and across
+    lanes (Wr = identity, so the logits equal the integer-valued z exactly)."""
+    E = L = 512
+    shape = gen.Shape(hidden=64, latent=L, n_experts=E, top_k=k, ffn=64, shared_ffn=0)
+    cfg = lm.make_config(shape.hidden, L, E, k, 64, 0, "bf16", "bf16", "bf16")
+    Wr_bits = gen.bf16_bits(np.eye(E, L, dtype=np.float32))
+    rng = np.random.default_rng(11 + T + k)
+    z = rng.integers(-4, 4, size=(T, L)).astype(np.float32)
+    for t in range(T):
+        c, n_lane = t % 64, (3, 4, 5, 8)[t % 4]
+        for j in range(n_lane):                   # n_lane high values in lane c, some equal
+            z[t, c + 64 * j] = 20 + (j // 2)
+        z[t, (c + 1) % 64] = 20                   # ties with the lane's lowest high values
+        z[t, (c + 7) % 64 + 64] = 21
+    Wr_d, z_d = to_device(Wr_bits), to_device(z)
+    weights = lm.make_weights(None, None, Wr_d, None, None, None)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(T * E * 4, dtype=torch.uint8, device="cuda")
+    lm.check(lm.lmoe_route(cfg, weights, z_d, T, ids, w, ws, ws.numel()))
+    torch.cuda.synchronize()
+    got = host(ids)
+    for t in range(T):
+        want = sorted(sorted(range(E), key=lambda e: (-z[t, e], e))[:k])
+        assert got[t].tolist() == want, (t, got[t].tolist(), want)
+
+
 @pytest.mark.parametrize("T,E,k,skew", [(1, 512, 10, 0.0), (8, 512, 10, 1.1), (64, 512, 10, 0.0), (65, 512, 10, 1.1),
                                         (1000, 16, 2, 0.0), (4096, 512, 10, 1.1), (16384, 512, 10, 1.1),
                                         (300, 1024, 16, 0.5), (77, 5, 5, 0.0)])
