@@ -40,7 +40,18 @@ __device__ __forceinline__ void add_bf16x8(float (&a)[8], const uint4& u) {
     }
 }
 
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU with the hardware reciprocal (v_rcp_f32, about 1 ulp): x / (1 + e^-x) as x * rcp(1 + e^-x).
+// Large negative x give e^-x = inf, rcp(inf) = 0 and a zero result.
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
+
+// bf16 of f, rounded to nearest even by gfx950's conversion instruction (v_cvt_pk_bf16_f32), for
+// values that are only stored (the routing inputs keep the integer rounding of f2bf).
+__device__ __forceinline__ uint16_t bf16_rn(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack_bf2_rn(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 
 // 16 bytes reinterpreted as 8 bf16 MFMA operands.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -19,7 +19,11 @@
 // A problem type P supplies, per operand, a base pointer for the workgroup and, per lane and copy
 // instruction, the 32-bit byte offset of the stage-0 source (rows outside the problem are
 // clamped to valid rows; their results are never stored), whether each operand is packed
-// (which fixes the step per stage), the number of stages and the epilogue.
+// (which fixes the step per stage), the number of stages and the epilogue.  The MFMAs take the B
+// fragment as their first operand, so each 32 x 32 accumulator block holds the transposed
+// product: register r of lane l is row l % 32 and column 8 (r / 4) + 4 (l / 32) + r % 4 of the
+// block, four consecutive columns of one row per group of four registers, which the epilogues
+// store 8 or 16 bytes at a time.
 #pragma once
 
 #include "common.hpp"
@@ -271,7 +275,7 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
             for (int i = 0; i < S::kMB; ++i)
                 if (i < nvb)
 #pragma unroll
-                    for (int j = 0; j < S::kNB; ++j) acc[i][j] = mfma32(af[i], bfv[j], acc[i][j]);
+                    for (int j = 0; j < S::kNB; ++j) acc[i][j] = mfma32(bfv[j], af[i], acc[i][j]);
         }
     };
 

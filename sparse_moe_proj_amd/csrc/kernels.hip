@@ -82,13 +82,23 @@ __device__ void perm_bitmap(const int32_t* __restrict__ ids, int T, int k, int E
     __syncthreads();
 }
 
-// Work list of <= BM-row tiles: routed segments in expert order, then the shared segment.
-__device__ void write_tiles(int e_cnt, int e_off, int e, int E, int T, int k, int BM, int has_shared, Tile* tiles,
-                            int32_t* ntiles, int* tmp) {
-    const int nt = e < E ? (e_cnt + BM - 1) / BM : 0;
+// Work list of <= BM-row tiles: routed segments in expert order, then the shared segment.  The
+// calling thread holds experts e0 .. e0+N-1 (slot counts cnt), whose segments start at off and
+// follow one another; every thread of the block must call it.
+template <int N>
+__device__ void write_tiles(const int (&cnt)[N], int off, int e0, int E, int T, int k, int BM, int has_shared,
+                            Tile* tiles, int32_t* ntiles, int* tmp) {
+    int nt = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) nt += e0 + j < E ? (cnt[j] + BM - 1) / BM : 0;
     int ntot;
-    const int ts = block_excl_scan(nt, tmp, &ntot);
-    for (int j = 0; j < nt; ++j) tiles[ts + j] = Tile{e, e_off + j * BM, min(BM, e_cnt - j * BM), 0};
+    int ts = block_excl_scan(nt, tmp, &ntot);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        if (e0 + j >= E) break;
+        for (int r = 0; r < cnt[j]; r += BM) tiles[ts++] = Tile{e0 + j, off + r, min(BM, cnt[j] - r), 0};
+        off += cnt[j];
+    }
     const int nsh = has_shared ? (T + BM - 1) / BM : 0;
     for (int j = threadIdx.x; j < nsh; j += blockDim.x) tiles[ntot + j] = Tile{E, T * k + j * BM, min(BM, T - j * BM), 0};
     if (threadIdx.x == 0) *ntiles = ntot + nsh;
@@ -109,7 +119,7 @@ __device__ void perm_single_body(const int32_t* ids, int T, int k, int E, int32_
     }
     if (e == 0) offsets[E] = total;
     for (int i = total + threadIdx.x; i < T * k; i += blockDim.x) perm[i] = -1;
-    if (tiles) write_tiles(cnt, off, e, E, T, k, BM, has_shared, tiles, ntiles, tmp);
+    if (tiles) write_tiles<1>({cnt}, off, e, E, T, k, BM, has_shared, tiles, ntiles, tmp);
     __syncthreads();
     perm_scatter_block(ids, T, k, E, 0, bm, soff, perm, inv);
 }
@@ -146,43 +156,89 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
         hist[(size_t)blockIdx.x * E + e] = __popc(bm[2 * e]) + __popc(bm[2 * e + 1]);
 }
 
-__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int nb, int T, int k, int E,
-                                                         int32_t* __restrict__ base, int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ perm, int BM, Tile* tiles,
-                                                         int32_t* ntiles, int has_shared) {
-    __shared__ int tmp[33];
-    const int e = threadIdx.x;
-    int cnt = 0;
-    if (e < E) {
-        // per expert, the running count over token blocks; loads in batches of 32 in flight
-        for (int b0 = 0; b0 < nb; b0 += 32) {
-            int h[32];
+// Per expert, the inclusive running count of its slots over the token blocks: incl[b][e] = sum of
+// hist[0..b][e], so row nb-1 holds each expert's total.  Workgroup g takes experts [64g, 64g+64);
+// its 16 waves split the blocks into 16 parts, each thread sums its part of one expert's column,
+// the parts' sums meet in LDS, and each thread writes its part's running counts from the sum of
+// the parts before it.
+constexpr int kScanEPB = 64;
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ hist, int nb, int E,
+                                                         int32_t* __restrict__ incl) {
+    constexpr int kP = 1024 / kScanEPB, kBatch = 16;
+    __shared__ int psum[1024];  // [part][expert of the workgroup]
+    const int el = threadIdx.x % kScanEPB, part = threadIdx.x / kScanEPB;
+    const int e = blockIdx.x * kScanEPB + el;
+    const bool act = e < E;
+    const int b_lo = act ? (int)((long)nb * part / kP) : 0, b_hi = act ? (int)((long)nb * (part + 1) / kP) : 0;
+    auto batch = [&](int b0, int (&h)[kBatch]) {
 #pragma unroll
-            for (int u = 0; u < 32; ++u) h[u] = hist[(size_t)min(b0 + u, nb - 1) * E + e];
+        for (int u = 0; u < kBatch; ++u) h[u] = hist[(size_t)min(b0 + u, b_hi - 1) * E + e];
+    };
+    int sum = 0;
+    for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
+        int h[kBatch];
+        batch(b0, h);
 #pragma unroll
-            for (int u = 0; u < 32; ++u)
-                if (b0 + u < nb) {
-                    base[(size_t)(b0 + u) * E + e] = cnt;
-                    cnt += h[u];
-                }
-        }
+        for (int u = 0; u < kBatch; ++u)
+            if (b0 + u < b_hi) sum += h[u];
     }
-    int total;
-    const int off = block_excl_scan(e < E ? cnt : 0, tmp, &total);
-    if (e < E) offsets[e] = off;
-    if (e == 0) offsets[E] = total;
-    for (int i = total + threadIdx.x; i < T * k; i += blockDim.x) perm[i] = -1;
-    if (tiles) write_tiles(cnt, off, e, E, T, k, BM, has_shared, tiles, ntiles, tmp);
+    psum[threadIdx.x] = sum;
+    __syncthreads();
+    if (!act) return;
+    int run = 0;
+    for (int q = 0; q < part; ++q) run += psum[q * kScanEPB + el];
+    for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
+        int h[kBatch];
+        batch(b0, h);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (b0 + u < b_hi) {
+                run += h[u];
+                incl[(size_t)(b0 + u) * E + e] = run;
+            }
+    }
 }
 
-__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                           const int32_t* __restrict__ base,
-                                                           const int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+// Block b scatters the slots of its tokens.  Every block scans the experts' totals (the last row
+// of incl, four experts a thread) into the segment offsets; block b's first position for expert e
+// is offsets[e] + incl[b-1][e].  Block 0 also writes the offsets and the work list, and the blocks
+// together mark the positions past the last routed slot (perm = -1).
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E, int nb,
+                                                           const int32_t* __restrict__ incl,
+                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ inv, int BM, Tile* tiles,
+                                                           int32_t* ntiles, int has_shared) {
+    constexpr int kEPT = 1024 / 256;
     __shared__ uint32_t bm[2 * 1024];
     __shared__ int sbase[1024];
+    __shared__ int tmp[33];
+    // the totals and the previous block's running counts load while the bitmap is built
+    const int32_t* tot = incl + (size_t)(nb - 1) * E;
+    const int32_t* prev = incl + (size_t)max((int)blockIdx.x - 1, 0) * E;
+    const int e0 = threadIdx.x * kEPT;
+    int c[kEPT], pb[kEPT], s = 0;
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+        c[j] = e0 + j < E ? tot[e0 + j] : 0;
+        pb[j] = e0 + j < E && blockIdx.x > 0 ? prev[e0 + j] : 0;
+    }
     perm_bitmap(ids, T, k, E, blockIdx.x, bm);
-    for (int e = threadIdx.x; e < E; e += blockDim.x) sbase[e] = offsets[e] + base[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) s += c[j];
+    int total;
+    const int off0 = block_excl_scan(s, tmp, &total);
+    int off = off0;
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+        if (e0 + j < E) {
+            sbase[e0 + j] = off + pb[j];
+            if (blockIdx.x == 0) offsets[e0 + j] = off;
+        }
+        off += c[j];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) offsets[E] = total;
+    for (int i = total + blockIdx.x * blockDim.x + threadIdx.x; i < T * k; i += gridDim.x * blockDim.x) perm[i] = -1;
+    if (blockIdx.x == 0 && tiles) write_tiles<kEPT>(c, off0, e0, E, T, k, BM, has_shared, tiles, ntiles, tmp);
     __syncthreads();
     perm_scatter_block(ids, T, k, E, blockIdx.x, bm, sbase, perm, inv);
 }
@@ -754,11 +810,11 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist
     hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, hist);
     hipError_t err = last();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, T, k, E, base, offsets, perm, BM, tiles,
-                       ntiles, has_shared);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(cdiv(E, kScanEPB)), dim3(1024), 0, s, hist, nb, E, base);
     err = last();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, base, offsets, perm, inv);
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(256), 0, s, ids, T, k, E, nb, base, offsets, perm, inv, BM,
+                       tiles, ntiles, has_shared);
     return last();
 }
 

@@ -92,7 +92,8 @@ hipError_t launch_router_x(const uint16_t* x, const uint16_t* Gr, const float* b
 
 int perm_blocks(int T);
 
-// tiles may be null (no work list).  hist/base: [perm_blocks(T)][E] ints (unused when T <= 64).
+// tiles may be null (no work list).  hist/base: [perm_blocks(T)][E] ints (unused when T <= 64):
+// per block of 64 tokens, each expert's slot count, and its inclusive running count.
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* hist, int32_t* base, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int BM, Tile* tiles, int32_t* ntiles, int has_shared,
                           hipStream_t s);

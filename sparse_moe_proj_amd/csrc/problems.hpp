@@ -716,10 +716,71 @@ struct PipeProj : TileProj<S> {
     struct Prep {};
     template <int MB>
     __device__ Prep prep(const typename B::Ctx&, int, int) const { return {}; }
+    // The outputs of TileProj's modes from the transposed accumulators: a lane holds one row of
+    // each 32-row block and four consecutive n per register group, so modes 0-2 store 4 values
+    // at a time (N is a multiple of 64 and every tensor 16-byte aligned); mode 3 interleaves
+    // the router halves (n = 2e + h) and stores them one by one.
+    template <int MD, int MB, int NB>
+    __device__ __forceinline__ void store_mode(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], int rb, int cb,
+                                               int lane) const {
+        const int h4 = 4 * (lane >> 5);
+        static_for<MB>([&](auto i) {
+            const int m = c.m0 + rb + i * 32 + (lane & 31);
+            if (m < B::M) {
+                static_for<NB>([&](auto j) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int n = c.n0 + cb + j * 32 + 8 * r4 + h4;
+                        const f32x16& a = acc[i][j];
+                        const float v[4] = {a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+                        const size_t o = (size_t)m * B::N + n;
+                        if constexpr (MD == 3) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) {
+                                const int nt = n + t, e = nt >> 1, h = nt & 1;
+                                if (nt < B::N)
+                                    B::out32[((size_t)h * B::M + m) * (B::N >> 1) + e] =
+                                        h == 0 && B::bias ? v[t] + B::bias[e] : v[t];
+                            }
+                        } else if (n < B::N) {
+                            if constexpr (MD == 0) {
+                                uint32_t hi[4], lo[4];
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) split_hi_lo(v[t], hi[t], lo[t]);
+                                *reinterpret_cast<float4*>(B::out32 + o) = make_float4(v[0], v[1], v[2], v[3]);
+                                *reinterpret_cast<uint2*>(B::out16 + o) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+                                if (B::out16lo)
+                                    *reinterpret_cast<uint2*>(B::out16lo + o) =
+                                        make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+                            } else if constexpr (MD == 1) {
+                                *reinterpret_cast<uint2*>(B::out16 + o) =
+                                    make_uint2(pack_bf2_rn(v[0], v[1]), pack_bf2_rn(v[2], v[3]));
+                            } else {
+                                float4* q = reinterpret_cast<float4*>(B::out32 + o);
+                                float4 r = *q;
+                                r.x += v[0];
+                                r.y += v[1];
+                                r.z += v[2];
+                                r.w += v[3];
+                                *q = r;
+                            }
+                        }
+                    }
+                });
+            }
+        });
+    }
     template <int MB, int NB>
     __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
                                           int lane) const {
-        B::template epilogue<MB, NB>(c, acc, rb, cb, lane);
+        if (B::mode == 0)
+            store_mode<0>(c, acc, rb, cb, lane);
+        else if (B::mode == 1)
+            store_mode<1>(c, acc, rb, cb, lane);
+        else if (B::mode == 2)
+            store_mode<2>(c, acc, rb, cb, lane);
+        else
+            store_mode<3>(c, acc, rb, cb, lane);
     }
 };
 
@@ -750,10 +811,33 @@ struct PipeUp : TileUp<S> {
     struct Prep {};
     template <int MB>
     __device__ Prep prep(const typename B::Ctx&, int, int) const { return {}; }
+    // H[row][f] = bf16(silu(gate * tg) * (up * tu)) from the transposed accumulators: a lane holds
+    // one row of each 32-row block and four consecutive f per register group (one 8-byte store).
     template <int MB, int NB>
     __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
                                           int lane) const {
-        B::template epilogue<MB, NB>(c, acc, rb, cb, lane);
+        static_assert(NB % 2 == 0 && NB * 16 == B::kHalf, "gate blocks then up blocks per wave column");
+        const int h4 = 4 * (lane >> 5);
+        static_for<MB>([&](auto i) {
+            const int m = rb + i * 32 + (lane & 31);
+            if (m < c.nrows) {
+                uint16_t* hrow = B::H + (size_t)(c.row0 + m) * B::Hs;
+                static_for<NB / 2>([&](auto j) {
+                    const int fb = c.f0 + (cb / S::kWN) * B::kHalf + j * 32 + h4;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int f = fb + 8 * q;
+                        if (f < c.F) {
+                            float h[4];
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                h[t] = silu(acc[i][j][4 * q + t] * c.tg) * (acc[i][j + NB / 2][4 * q + t] * c.tu);
+                            *reinterpret_cast<uint2*>(hrow + f) = make_uint2(pack_bf2_rn(h[0], h[1]), pack_bf2_rn(h[2], h[3]));
+                        }
+                    }
+                });
+            }
+        });
     }
 };
 
@@ -776,53 +860,44 @@ struct PipeDown : TileDown<S> {
         const int nb = min(c.n0 + packed_block<S::kU>(i) * 16, B::L - 16) >> 4;
         return packed_off<S::kU>(nb, i, c.F, lane);
     }
-    // Destination row of every accumulator row (-1: none), read before the store (the next tile's
-    // copies are issued in between, and a wait for a later global load would wait for them too).
-    // Wave tiles of up to 64 rows keep this lane's rows in registers; taller ones (the 256-row
-    // tiles) keep the tile's rows in LDS, written by the workgroup and read after the barrier that
-    // the persistent kernel places between prep and store.
-    static constexpr bool kPrepLds = S::kMB > 2;
-    __device__ static int* prep_rows() {
-        __shared__ int rows[S::kBM];
-        return rows;
-    }
+    // Destination row of this lane's row in each 32-row block (-1: none; transposed accumulators,
+    // one row per block), read before the store: the next tile's copies are issued in between,
+    // and a wait for a global load issued after them would wait for the copies too.
     template <int MB>
     struct PrepT {
-        int drow[kPrepLds ? 1 : MB][16];
+        int drow[MB];
     };
     template <int MB>
     __device__ __forceinline__ PrepT<MB> prep(const typename B::Ctx& c, int rb, int lane) const {
         PrepT<MB> q;
-        if constexpr (kPrepLds) {
-            int* rows = prep_rows();
-            for (int m = threadIdx.x; m < S::kBM; m += S::kThreads)
-                rows[m] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
-        } else {
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = rb + i * 32 + frag32_row(r, lane);
-                    q.drow[i][r] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
-                }
+        for (int i = 0; i < MB; ++i) {
+            const int m = rb + i * 32 + (lane & 31);
+            q.drow[i] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
         }
         return q;
     }
+    // Y[dest][n] = bf16(acc * td), four consecutive n per 8-byte store; a dropped slot (-1) owns no
+    // output row.
     template <int MB, int NB>
     __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], const PrepT<MB>& q, int rb,
                                           int cb, int lane) const {
+        const int h4 = 4 * (lane >> 5);
         static_for<MB>([&](auto i) {
+            if (q.drow[i] >= 0) {
+                uint16_t* yrow = B::Y + (size_t)q.drow[i] * B::L;
+                static_for<NB>([&](auto j) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                // a dropped slot (-1) owns no output row
-                const int drow = kPrepLds ? prep_rows()[rb + i * 32 + frag32_row(r, lane)] : q.drow[kPrepLds ? 0 : i][r];
-                if (drow >= 0) {
-                    const size_t dst = (size_t)drow * B::L;
-                    static_for<NB>([&](auto j) {
-                        const int n = c.n0 + cb + j * 32 + frag32_col(lane);
-                        if (n < B::L) B::Y[dst + n] = (uint16_t)f2bf(acc[i][j][r] * c.td);
-                    });
-                }
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int n = c.n0 + cb + j * 32 + 8 * r4 + h4;
+                        if (n < B::L) {
+                            const f32x16& v = acc[i][j];
+                            *reinterpret_cast<uint2*>(yrow + n) =
+                                make_uint2(pack_bf2_rn(v[4 * r4] * c.td, v[4 * r4 + 1] * c.td),
+                                           pack_bf2_rn(v[4 * r4 + 2] * c.td, v[4 * r4 + 3] * c.td));
+                        }
+                    }
+                });
             }
         });
     }
