@@ -188,6 +188,28 @@ __device__ __forceinline__ void lds_read_frags(const uint32_t (&aa)[MB], const u
     }
 }
 
+// LDS writes and reads of a tile's staged output (outside the K loop).  The reads wait for
+// themselves in the same block (early-clobber outputs), for the reason given above.
+__device__ __forceinline__ void lds_write_b64(uint32_t addr, uint2 v) {
+    __asm__ volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_wait() { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_read8_b128(const uint32_t (&a)[8], uint4 (&v)[8]) {
+    __asm__ volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
 // Copy sources of one tile for this lane: a uniform base per operand and per-lane 32-bit byte
 // offsets of the stage-0 source of each copy instruction this wave issues.
 template <class S>
@@ -326,7 +348,10 @@ __global__ __launch_bounds__(S::kThreads) void pipe_gemm_kernel(const P p) {
     pipe_k_loop<S, P>(c, nk, acc, st0, st1, st2, st3, wave, lane, p.valid_rows(ctx));
     const auto prep = p.template prep<S::kMB>(ctx, rb, lane);
     __syncthreads();  // a problem's prep may stage rows in LDS for the store
-    p.template store<S::kMB, S::kNB>(ctx, acc, prep, rb, cb, lane);
+    if constexpr (P::kLdsStore)
+        p.template store_lds<S>(ctx, acc, prep, rb, cb, lane, wave, st0, st1, st2, [] {});
+    else
+        p.template store<S::kMB, S::kNB>(ctx, acc, prep, rb, cb, lane);
 }
 
 // Persistent form: gridDim.x workgroups (about one per CU) walk the tiles that exist (the M-tile
@@ -378,8 +403,16 @@ __global__ __launch_bounds__(S::kThreads) void pipe_gemm_persistent(const P p, i
             nc = pipe_copies<S>(p, nctx, wave, lane);
         }
         stage_barrier();  // every wave is done with this tile's stage buffers
-        if (more) pipe_prologue<S, P>(nc, nnk, st0, st1, st2, wave);
-        p.template store<S::kMB, S::kNB>(ctx, acc, prep, rb, cb, lane);
+        if constexpr (P::kLdsStore) {
+            // the store stages the tile in the stage buffers and issues the next tile's first
+            // stages as soon as the buffers they fill have been read back
+            p.template store_lds<S>(ctx, acc, prep, rb, cb, lane, wave, st0, st1, st2, [&] {
+                if (more) pipe_prologue<S, P>(nc, nnk, st0, st1, st2, wave);
+            });
+        } else {
+            if (more) pipe_prologue<S, P>(nc, nnk, st0, st1, st2, wave);
+            p.template store<S::kMB, S::kNB>(ctx, acc, prep, rb, cb, lane);
+        }
         if (!more) break;
         l = ln;
         ctx = nctx;

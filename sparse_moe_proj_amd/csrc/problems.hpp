@@ -695,7 +695,7 @@ namespace lmoe {
 template <class S>
 struct PipeProj : TileProj<S> {
     using B = TileProj<S>;
-    static constexpr bool kAPacked = false, kBPacked = false;
+    static constexpr bool kAPacked = false, kBPacked = false, kLdsStore = false;
     __device__ int m_tiles() const { return (B::M + S::kBM - 1) / S::kBM; }
     __device__ int valid_rows(const typename B::Ctx& c) const { return min(S::kBM, B::M - c.m0); }
     __device__ int k_stages(const typename B::Ctx&) const { return B::K / S::kBK; }
@@ -787,7 +787,7 @@ struct PipeProj : TileProj<S> {
 template <class S>
 struct PipeUp : TileUp<S> {
     using B = TileUp<S>;
-    static constexpr bool kAPacked = false, kBPacked = true;
+    static constexpr bool kAPacked = false, kBPacked = true, kLdsStore = false;
     __device__ int m_tiles() const { return B::seg.count(); }
     __device__ int valid_rows(const typename B::Ctx& c) const { return c.nrows; }
     __device__ int k_stages(const typename B::Ctx&) const { return B::L / S::kBK; }
@@ -844,7 +844,7 @@ struct PipeUp : TileUp<S> {
 template <class S>
 struct PipeDown : TileDown<S> {
     using B = TileDown<S>;
-    static constexpr bool kAPacked = false, kBPacked = true;
+    static constexpr bool kAPacked = false, kBPacked = true, kLdsStore = true;
     __device__ int m_tiles() const { return B::seg.count(); }
     __device__ int valid_rows(const typename B::Ctx& c) const { return c.nrows; }
     __device__ int k_stages(const typename B::Ctx& c) const { return c.F / S::kBK; }
@@ -860,46 +860,85 @@ struct PipeDown : TileDown<S> {
         const int nb = min(c.n0 + packed_block<S::kU>(i) * 16, B::L - 16) >> 4;
         return packed_off<S::kU>(nb, i, c.F, lane);
     }
-    // Destination row of this lane's row in each 32-row block (-1: none; transposed accumulators,
-    // one row per block), read before the store: the next tile's copies are issued in between,
-    // and a wait for a global load issued after them would wait for the copies too.
-    template <int MB>
-    struct PrepT {
-        int drow[MB];
-    };
-    template <int MB>
-    __device__ __forceinline__ PrepT<MB> prep(const typename B::Ctx& c, int rb, int lane) const {
-        PrepT<MB> q;
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            const int m = rb + i * 32 + (lane & 31);
-            q.drow[i] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
-        }
-        return q;
+    // Destination row of every row of the tile (-1: none) in LDS, written before the barrier that
+    // precedes the store (the store reads the rows of other waves).
+    __device__ static int* prep_rows() {
+        __shared__ int rows[S::kBM];
+        return rows;
     }
-    // Y[dest][n] = bf16(acc * td), four consecutive n per 8-byte store; a dropped slot (-1) owns no
-    // output row.
-    template <int MB, int NB>
-    __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], const PrepT<MB>& q, int rb,
-                                          int cb, int lane) const {
-        const int h4 = 4 * (lane >> 5);
-        static_for<MB>([&](auto i) {
-            if (q.drow[i] >= 0) {
-                uint16_t* yrow = B::Y + (size_t)q.drow[i] * B::L;
+    struct Prep {};
+    template <int MB>
+    __device__ __forceinline__ Prep prep(const typename B::Ctx& c, int, int) const {
+        int* rows = prep_rows();
+        for (int m = threadIdx.x; m < S::kBM; m += S::kThreads)
+            rows[m] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
+        return {};
+    }
+    // Y[dest][n] = bf16(acc * td), staged through LDS so that every store instruction writes whole
+    // row segments: half h of the tile (the 128 rows of the waves with wm = h) goes into stage
+    // buffer h (buffer 2 for the second half when a tile's prologue also fills buffer 1), BN = 256
+    // bf16 = 32 chunks of 16 bytes a row, chunk c of row r at position c ^ (r % 32) (the writes,
+    // 8 bytes of one row per lane, and the reads, two whole rows per instruction, spread over
+    // the banks).  Then thread t reads and stores chunk t % 32 of rows t / 32 + 16 k (k < 8) of
+    // each half.  issue_next() runs once the first buffer has been read back.
+    template <class SS, int MB, int NB, class F>
+    __device__ __forceinline__ void store_lds(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
+                                              int lane, int wave, uint4* st0, uint4* st1, uint4* st2,
+                                              F&& issue_next) const {
+        static_assert(SS::kBN == 256 && SS::kWR == 2 && SS::kThreads == 512, "256-column tiles, two wave rows");
+        static_assert(SS::kBM / 2 * 512 <= SS::kStageUnits * 16, "half a tile fits a stage buffer");
+        constexpr int kRows = SS::kBM / 2;  // rows of a half
+        const int wm = wave / SS::kWC;
+        const uint32_t hbase[2] = {lds_addr(st0), lds_addr(SS::kNS >= 3 ? st2 : st1)};
+        {
+            const uint32_t base = hbase[wm];
+            const int h8 = 8 * (lane >> 5);
+            static_for<MB>([&](auto i) {
+                const int rl = i * 32 + (lane & 31);  // row within the half
                 static_for<NB>([&](auto j) {
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
-                        const int n = c.n0 + cb + j * 32 + 8 * r4 + h4;
-                        if (n < B::L) {
-                            const f32x16& v = acc[i][j];
-                            *reinterpret_cast<uint2*>(yrow + n) =
-                                make_uint2(pack_bf2_rn(v[4 * r4] * c.td, v[4 * r4 + 1] * c.td),
-                                           pack_bf2_rn(v[4 * r4 + 2] * c.td, v[4 * r4 + 3] * c.td));
-                        }
+                        const int ch = (cb + j * 32) / 8 + r4;
+                        const f32x16& v = acc[i][j];
+                        lds_write_b64(base + rl * 512 + ((ch ^ (rl & 31)) * 16) + h8,
+                                      make_uint2(pack_bf2_rn(v[4 * r4] * c.td, v[4 * r4 + 1] * c.td),
+                                                 pack_bf2_rn(v[4 * r4 + 2] * c.td, v[4 * r4 + 3] * c.td)));
                     }
                 });
+            });
+        }
+        lds_wait();
+        stage_barrier();
+        const int t = threadIdx.x, ch = t & 31, r0 = t >> 5;  // rows r0 + 16 k of each half
+        constexpr int kPer = kRows / 16;                        // rows per thread and half
+        static_assert(kPer <= 8, "at most 8 chunks per thread and half");
+        int drow[2][kPer];
+        const int* rows = prep_rows();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) drow[h][k] = rows[h * kRows + r0 + 16 * k];
+        const int n = c.n0 + ch * 8;
+        auto half = [&](int h) {
+            uint32_t a[8];
+            uint4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r = r0 + 16 * (k < kPer ? k : 0);
+                a[k] = hbase[h] + r * 512 + ((ch ^ (r & 31)) * 16);
             }
-        });
+            lds_read8_b128(a, v);
+            return [=, &drow](auto after_read) {
+                after_read();
+#pragma unroll
+                for (int k = 0; k < kPer; ++k)
+                    if (drow[h][k] >= 0 && n < B::L) *reinterpret_cast<uint4*>(B::Y + (size_t)drow[h][k] * B::L + n) = v[k];
+            };
+        };
+        auto store0 = half(0);
+        stage_barrier();  // every wave has read the first half back
+        store0(issue_next);
+        half(1)([] {});
     }
 };
 
