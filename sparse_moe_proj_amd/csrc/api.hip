@@ -460,7 +460,10 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
         ev.begin(LMOE_STAGE_D);
         uint16_t* zlo = T > kStreamMaxT ? static_cast<uint16_t*>(at(lo.zlo)) : nullptr;
         if (!(T <= kStreamMaxT && small_proj_fits(T, d.H))) z16h = nullptr;  // only the small-batch D launch writes it
-        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.Lz, d.H, 0, z32, z16, s, zlo, z16h,
+        // with the router reading the bf16 halves (zlo) and the experts z16, fp32 z is only
+        // written when the caller asks for it
+        float* zf = zlo && !o.aux_z ? nullptr : z32;
+        if ((e = launch_proj_bf16(x16, static_cast<const uint16_t*>(wt->D), T, d.Lz, d.H, 0, zf, z16, s, zlo, z16h,
                                   hnorm)) != hipSuccess)
             return hip_fail(e, "D projection");
         ev.end(LMOE_STAGE_D);

@@ -40,6 +40,15 @@ __device__ __forceinline__ void add_bf16x8(float (&a)[8], const uint4& u) {
     }
 }
 
+// v through an opaque move (a VGPR copy the compiler cannot see through): values computed from
+// it are recomputed where they are used, not hoisted out of a kernel's outer loop and kept (or
+// spilled) across it.
+__device__ __forceinline__ int opaque(int v) {
+    int r;
+    __asm__ volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
 // SiLU with the hardware reciprocal (v_rcp_f32, about 1 ulp): x / (1 + e^-x) as x * rcp(1 + e^-x).
 // Large negative x give e^-x = inf, rcp(inf) = 0 and a zero result.
 __device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }

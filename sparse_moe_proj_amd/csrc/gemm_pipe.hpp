@@ -210,6 +210,77 @@ __device__ __forceinline__ void lds_read8_b128(const uint32_t (&a)[8], uint4 (&v
         : "memory");
 }
 
+// A tile of bf16 outputs stored through the stage buffers, so that every store instruction
+// writes whole row segments (the transposed accumulators give each lane 8 bytes of one row).
+// Half h of the tile (the BM/2 rows of the waves with wm = h; WR = 2) goes into stage buffer h
+// (buffer 2 for the second half when a tile's prologue also fills buffer 1) as rows of C chunks
+// of 16 bytes, chunk c of row r at position c ^ (r % C): the writes (8 bytes of one row per
+// lane) and the reads (whole rows) spread over the banks.
+//   put(i, j, r4) -> uint2: the 4 bf16 of accumulator group r4 of block (i, j) of this lane,
+//       staged in chunk chunk_of(j, r4) of its row (blocks j < NJ are written);
+//   row_of(r) -> the output row of tile row r, or -1 for none (read after the first barrier);
+//   out + row * stride + col0 + 8 c receives chunk c of a row whose col0 + 8 c < ncols.
+// Thread t then reads and stores chunk t % C of rows t / C + (512 / C) k of each half.  With
+// RELEASE, issue_next() runs once every wave has read the first half back (the next tile's first
+// stages then fill buffer 0 while the second half is stored).
+template <class SS, int C, int NJ, bool RELEASE, int MB, int NB, class Put, class ChunkOf, class RowOf, class F>
+__device__ __forceinline__ void staged_store_bf16(int lane, int wave, uint4* st0, uint4* st1, uint4* st2, Put&& put,
+                                                  ChunkOf&& chunk_of, RowOf&& row_of, uint16_t* out, size_t stride,
+                                                  int col0, int ncols, F&& issue_next) {
+    static_assert(SS::kWR == 2 && SS::kThreads == 512 && (C == 16 || C == 32), "two wave rows, 16 or 32 chunks");
+    constexpr int kRows = SS::kBM / 2;             // rows of a half
+    constexpr int kRowBytes = 16 * C;
+    static_assert(kRows * kRowBytes <= SS::kStageUnits * 16, "half a tile fits a stage buffer");
+    constexpr int kStep = 512 / C;                 // rows read per pass of the workgroup
+    constexpr int kPer = kRows / kStep;            // chunks per thread and half
+    static_assert(kPer >= 1 && kPer <= 8, "1 to 8 chunks per thread and half");
+    const int wm = wave / SS::kWC;
+    const uint32_t hbase[2] = {lds_addr(st0), lds_addr(SS::kNS >= 3 ? st2 : st1)};
+    lane = opaque(lane);  // the per-lane addresses below are recomputed per tile, not kept across tiles
+    {
+        const uint32_t base = hbase[wm];
+        const int h8 = 8 * (lane >> 5);
+        static_for<MB>([&](auto i) {
+            const int rl = i * 32 + (lane & 31);
+            static_for<NJ>([&](auto j) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    lds_write_b64(base + rl * kRowBytes + ((chunk_of(j, r4) ^ (rl & (C - 1))) * 16) + h8, put(i, j, r4));
+            });
+        });
+    }
+    lds_wait();
+    stage_barrier();
+    const int t = opaque(threadIdx.x), ch = t % C, r0 = t / C;
+    int row[2][kPer];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) row[h][k] = row_of(h * kRows + r0 + kStep * k);
+    const int col = col0 + 8 * ch;
+    auto half = [&](int h, auto&& after_read) {
+        uint32_t a[8];
+        uint4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int r = r0 + kStep * (k < kPer ? k : 0);
+            a[k] = hbase[h] + r * kRowBytes + ((ch ^ (r & (C - 1))) * 16);
+        }
+        lds_read8_b128(a, v);
+        after_read();
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            if (row[h][k] >= 0 && col < ncols) *reinterpret_cast<uint4*>(out + (size_t)row[h][k] * stride + col) = v[k];
+    };
+    half(0, [&] {
+        if constexpr (RELEASE) {
+            stage_barrier();  // every wave has read the first half back
+            issue_next();
+        }
+    });
+    half(1, [] {});
+}
+
 // Copy sources of one tile for this lane: a uniform base per operand and per-lane 32-bit byte
 // offsets of the stage-0 source of each copy instruction this wave issues.
 template <class S>
@@ -400,7 +471,7 @@ __global__ __launch_bounds__(S::kThreads) void pipe_gemm_persistent(const P p, i
         PipeCopies<S> nc;
         if (more) {
             nnk = p.k_stages(nctx);
-            nc = pipe_copies<S>(p, nctx, wave, lane);
+            nc = pipe_copies<S>(p, nctx, wave, opaque(lane));  // per-lane terms recomputed per tile
         }
         stage_barrier();  // every wave is done with this tile's stage buffers
         if constexpr (P::kLdsStore) {

@@ -68,6 +68,7 @@ constexpr bool kRouteInExperts = LMOE_ROUTE_IN_EXPERTS != 0;
 hipError_t launch_rmsnorm(const float* h, int T, int H, uint16_t* x16, hipStream_t s);
 
 // mode 0: out32 = xW^T and out16 = bf16(out32); 1: out16 = bf16(xW^T); 2: out32 += xW^T
+// (mode 0, T > kStreamMaxT: out32 may be null, then only the bf16 outputs are written)
 // out16lo (mode 0, T > kStreamMaxT, optional): also write the low bf16 half of the output.
 // out16h (mode 0, small batches, optional): also write fp16 of the output.
 // hnorm (small batches staged in LDS only, i.e. T <= kStreamMaxT and small_proj_fits): the input

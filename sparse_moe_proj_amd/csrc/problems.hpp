@@ -62,7 +62,7 @@ struct SegSpace {
 using Tile128 = TileShape<128, 128, 2, 2>;
 using Tile256 = TileShape<256, 256, 2, 2>;
 
-// Dense projection C[t][n] = x[t] . W[n]; mode 0: z32 + z16 (D), 1: bf16 y (U), 2: y += (U, fp32
+// Dense projection C[t][n] = x[t] . W[n]; mode 0: z32 (optional) + z16 (D), 1: bf16 y (U), 2: y += (U, fp32
 // residual), 3: router halves from the folded router (W = Gr as [2E][K] rows, n = 2e + h):
 // out32[h][t][e] = v (+ bias[e] for h = 0)
 template <class S>
@@ -102,7 +102,7 @@ struct TileProj {
                         if (mode == 0) {
                             uint32_t hi, lo;
                             split_hi_lo(v, hi, lo);
-                            out32[o] = v;
+                            if (out32) out32[o] = v;
                             out16[o] = (uint16_t)hi;
                             if (out16lo) out16lo[o] = (uint16_t)lo;
                         } else if (mode == 3) {
@@ -695,7 +695,7 @@ namespace lmoe {
 template <class S>
 struct PipeProj : TileProj<S> {
     using B = TileProj<S>;
-    static constexpr bool kAPacked = false, kBPacked = false, kLdsStore = false;
+    static constexpr bool kAPacked = false, kBPacked = false, kLdsStore = true;
     __device__ int m_tiles() const { return (B::M + S::kBM - 1) / S::kBM; }
     __device__ int valid_rows(const typename B::Ctx& c) const { return min(S::kBM, B::M - c.m0); }
     __device__ int k_stages(const typename B::Ctx&) const { return B::K / S::kBK; }
@@ -747,7 +747,8 @@ struct PipeProj : TileProj<S> {
                                 uint32_t hi[4], lo[4];
 #pragma unroll
                                 for (int t = 0; t < 4; ++t) split_hi_lo(v[t], hi[t], lo[t]);
-                                *reinterpret_cast<float4*>(B::out32 + o) = make_float4(v[0], v[1], v[2], v[3]);
+                                if (B::out32)
+                                    *reinterpret_cast<float4*>(B::out32 + o) = make_float4(v[0], v[1], v[2], v[3]);
                                 *reinterpret_cast<uint2*>(B::out16 + o) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
                                 if (B::out16lo)
                                     *reinterpret_cast<uint2*>(B::out16lo + o) =
@@ -770,6 +771,62 @@ struct PipeProj : TileProj<S> {
             }
         });
     }
+    // bf16 outputs staged through LDS (staged_store_bf16): mode 1, and the high half of mode 0
+    // without the fp32 output; the other forms store from the accumulators once the next tile's
+    // first stages are issued.
+    template <class SS, int MB, int NB, class F>
+    __device__ __forceinline__ void store_lds(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep p, int rb, int cb,
+                                              int lane, int wave, uint4* st0, uint4* st1, uint4* st2,
+                                              F&& issue_next) const {
+        static_assert(SS::kBN == 256, "256-column tiles");
+        auto chunk_of = [&](int j, int r4) { return (cb + j * 32) / 8 + r4; };
+        auto row_of = [&](int r) { return c.m0 + r < B::M ? c.m0 + r : -1; };
+        if (B::mode == 1) {
+            staged_store_bf16<SS, 32, NB, true, MB, NB>(
+                lane, wave, st0, st1, st2,
+                [&](int i, int j, int r4) {
+                    const f32x16& v = acc[i][j];
+                    return make_uint2(pack_bf2_rn(v[4 * r4], v[4 * r4 + 1]), pack_bf2_rn(v[4 * r4 + 2], v[4 * r4 + 3]));
+                },
+                chunk_of, row_of, B::out16, (size_t)B::N, c.n0, B::N, issue_next);
+        } else if (B::mode == 0 && !B::out32) {
+            // the low halves straight from the accumulators (8 bytes a lane), then the high halves
+            // staged
+            if (B::out16lo) {
+                const int h4 = 4 * (lane >> 5);
+                static_for<MB>([&](auto i) {
+                    const int m = c.m0 + rb + i * 32 + (lane & 31);
+                    if (m < B::M)
+                        static_for<NB>([&](auto j) {
+#pragma unroll
+                            for (int r4 = 0; r4 < 4; ++r4) {
+                                const int n = c.n0 + cb + j * 32 + 8 * r4 + h4;
+                                if (n < B::N) {
+                                    uint32_t hi[4], lo[4];
+#pragma unroll
+                                    for (int t = 0; t < 4; ++t) split_hi_lo(acc[i][j][4 * r4 + t], hi[t], lo[t]);
+                                    *reinterpret_cast<uint2*>(B::out16lo + (size_t)m * B::N + n) =
+                                        make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+                                }
+                            }
+                        });
+                });
+            }
+            staged_store_bf16<SS, 32, NB, true, MB, NB>(
+                lane, wave, st0, st1, st2,
+                [&](int i, int j, int r4) {
+                    const f32x16& v = acc[i][j];
+                    uint32_t hi[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) hi[t] = f2bf(v[4 * r4 + t]);
+                    return make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+                },
+                chunk_of, row_of, B::out16, (size_t)B::N, c.n0, B::N, issue_next);
+        } else {
+            issue_next();
+            store<MB, NB>(c, acc, p, rb, cb, lane);
+        }
+    }
     template <int MB, int NB>
     __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
                                           int lane) const {
@@ -787,7 +844,7 @@ struct PipeProj : TileProj<S> {
 template <class S>
 struct PipeUp : TileUp<S> {
     using B = TileUp<S>;
-    static constexpr bool kAPacked = false, kBPacked = true, kLdsStore = false;
+    static constexpr bool kAPacked = false, kBPacked = true, kLdsStore = true;
     __device__ int m_tiles() const { return B::seg.count(); }
     __device__ int valid_rows(const typename B::Ctx& c) const { return c.nrows; }
     __device__ int k_stages(const typename B::Ctx&) const { return B::L / S::kBK; }
@@ -811,33 +868,26 @@ struct PipeUp : TileUp<S> {
     struct Prep {};
     template <int MB>
     __device__ Prep prep(const typename B::Ctx&, int, int) const { return {}; }
-    // H[row][f] = bf16(silu(gate * tg) * (up * tu)) from the transposed accumulators: a lane holds
-    // one row of each 32-row block and four consecutive f per register group (one 8-byte store).
-    template <int MB, int NB>
-    __device__ __forceinline__ void store(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
-                                          int lane) const {
-        static_assert(NB % 2 == 0 && NB * 16 == B::kHalf, "gate blocks then up blocks per wave column");
-        const int h4 = 4 * (lane >> 5);
-        static_for<MB>([&](auto i) {
-            const int m = rb + i * 32 + (lane & 31);
-            if (m < c.nrows) {
-                uint16_t* hrow = B::H + (size_t)(c.row0 + m) * B::Hs;
-                static_for<NB / 2>([&](auto j) {
-                    const int fb = c.f0 + (cb / S::kWN) * B::kHalf + j * 32 + h4;
+    // H[row][f] = bf16(silu(gate * tg) * (up * tu)), staged through LDS (staged_store_bf16): a
+    // 256-column tile holds 128 gate and 128 up columns, so its H tile is 128 columns (16 chunks)
+    // wide, the gate blocks j < NB / 2 of wave column wn giving H columns wn * kHalf + 32 j ..
+    template <class SS, int MB, int NB, class F>
+    __device__ __forceinline__ void store_lds(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
+                                              int lane, int wave, uint4* st0, uint4* st1, uint4* st2,
+                                              F&& issue_next) const {
+        static_assert(NB % 2 == 0 && NB * 16 == B::kHalf && SS::kBN == 256, "gate blocks then up blocks per wave column");
+        const int wn = cb / SS::kWN;
+        staged_store_bf16<SS, 16, NB / 2, true, MB, NB>(
+            lane, wave, st0, st1, st2,
+            [&](int i, int j, int r4) {
+                float h[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int f = fb + 8 * q;
-                        if (f < c.F) {
-                            float h[4];
-#pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                h[t] = silu(acc[i][j][4 * q + t] * c.tg) * (acc[i][j + NB / 2][4 * q + t] * c.tu);
-                            *reinterpret_cast<uint2*>(hrow + f) = make_uint2(pack_bf2_rn(h[0], h[1]), pack_bf2_rn(h[2], h[3]));
-                        }
-                    }
-                });
-            }
-        });
+                for (int t = 0; t < 4; ++t)
+                    h[t] = silu(acc[i][j][4 * r4 + t] * c.tg) * (acc[i][j + NB / 2][4 * r4 + t] * c.tu);
+                return make_uint2(pack_bf2_rn(h[0], h[1]), pack_bf2_rn(h[2], h[3]));
+            },
+            [&](int j, int r4) { return (wn * B::kHalf + j * 32) / 8 + r4; },
+            [&](int r) { return r < c.nrows ? c.row0 + r : -1; }, B::H, (size_t)B::Hs, c.f0, c.F, issue_next);
     }
 };
 
@@ -874,71 +924,23 @@ struct PipeDown : TileDown<S> {
             rows[m] = m < c.nrows ? B::seg.dest_of(c.seg, c.row0 + m) : -1;
         return {};
     }
-    // Y[dest][n] = bf16(acc * td), staged through LDS so that every store instruction writes whole
-    // row segments: half h of the tile (the 128 rows of the waves with wm = h) goes into stage
-    // buffer h (buffer 2 for the second half when a tile's prologue also fills buffer 1), BN = 256
-    // bf16 = 32 chunks of 16 bytes a row, chunk c of row r at position c ^ (r % 32) (the writes,
-    // 8 bytes of one row per lane, and the reads, two whole rows per instruction, spread over
-    // the banks).  Then thread t reads and stores chunk t % 32 of rows t / 32 + 16 k (k < 8) of
-    // each half.  issue_next() runs once the first buffer has been read back.
+    // Y[dest][n] = bf16(acc * td), staged through LDS (staged_store_bf16: whole row segments per
+    // store instruction).
     template <class SS, int MB, int NB, class F>
     __device__ __forceinline__ void store_lds(const typename B::Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb,
                                               int lane, int wave, uint4* st0, uint4* st1, uint4* st2,
                                               F&& issue_next) const {
-        static_assert(SS::kBN == 256 && SS::kWR == 2 && SS::kThreads == 512, "256-column tiles, two wave rows");
-        static_assert(SS::kBM / 2 * 512 <= SS::kStageUnits * 16, "half a tile fits a stage buffer");
-        constexpr int kRows = SS::kBM / 2;  // rows of a half
-        const int wm = wave / SS::kWC;
-        const uint32_t hbase[2] = {lds_addr(st0), lds_addr(SS::kNS >= 3 ? st2 : st1)};
-        {
-            const uint32_t base = hbase[wm];
-            const int h8 = 8 * (lane >> 5);
-            static_for<MB>([&](auto i) {
-                const int rl = i * 32 + (lane & 31);  // row within the half
-                static_for<NB>([&](auto j) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int ch = (cb + j * 32) / 8 + r4;
-                        const f32x16& v = acc[i][j];
-                        lds_write_b64(base + rl * 512 + ((ch ^ (rl & 31)) * 16) + h8,
-                                      make_uint2(pack_bf2_rn(v[4 * r4] * c.td, v[4 * r4 + 1] * c.td),
-                                                 pack_bf2_rn(v[4 * r4 + 2] * c.td, v[4 * r4 + 3] * c.td)));
-                    }
-                });
-            });
-        }
-        lds_wait();
-        stage_barrier();
-        const int t = threadIdx.x, ch = t & 31, r0 = t >> 5;  // rows r0 + 16 k of each half
-        constexpr int kPer = kRows / 16;                        // rows per thread and half
-        static_assert(kPer <= 8, "at most 8 chunks per thread and half");
-        int drow[2][kPer];
+        static_assert(SS::kBN == 256, "256-column tiles");
         const int* rows = prep_rows();
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) drow[h][k] = rows[h * kRows + r0 + 16 * k];
-        const int n = c.n0 + ch * 8;
-        auto half = [&](int h) {
-            uint32_t a[8];
-            uint4 v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int r = r0 + 16 * (k < kPer ? k : 0);
-                a[k] = hbase[h] + r * 512 + ((ch ^ (r & 31)) * 16);
-            }
-            lds_read8_b128(a, v);
-            return [=, &drow](auto after_read) {
-                after_read();
-#pragma unroll
-                for (int k = 0; k < kPer; ++k)
-                    if (drow[h][k] >= 0 && n < B::L) *reinterpret_cast<uint4*>(B::Y + (size_t)drow[h][k] * B::L + n) = v[k];
-            };
-        };
-        auto store0 = half(0);
-        stage_barrier();  // every wave has read the first half back
-        store0(issue_next);
-        half(1)([] {});
+        staged_store_bf16<SS, 32, NB, true, MB, NB>(
+            lane, wave, st0, st1, st2,
+            [&](int i, int j, int r4) {
+                const f32x16& v = acc[i][j];
+                return make_uint2(pack_bf2_rn(v[4 * r4] * c.td, v[4 * r4 + 1] * c.td),
+                                  pack_bf2_rn(v[4 * r4 + 2] * c.td, v[4 * r4 + 3] * c.td));
+            },
+            [&](int j, int r4) { return (cb + j * 32) / 8 + r4; }, [&](int r) { return rows[r]; }, B::Y, (size_t)B::L,
+            c.n0, B::L, issue_next);
     }
 };
 
