@@ -117,8 +117,9 @@ Layout plan(const Dims& d, int T) {
     lo.deq_path = deq;
     lo.stream_path = !d.f32 && (T <= kStreamMaxT || (d.mx && !big4) || lo.decode_path);
     lo.fused_router = !d.f32 && small_proj_fits(T, d.H);
-    // expert groups take the logits from x and the folded router for every batch (two halves)
-    const bool halves = lo.fused_router || d.G > 1;
+    // expert groups take the logits from x and the folded router for every batch, and batches
+    // above kStreamMaxT multiply the two bf16 halves of z separately: two halves of logits
+    const bool halves = lo.fused_router || d.G > 1 || (!d.f32 && T > kStreamMaxT);
     lo.BM = expert_tile_rows(lo.stream_path, lo.mx_path, T, d.k, d.E);
     lo.max_tiles = expert_max_tiles(T, d.k, d.E, has_shared, lo.stream_path, lo.mx_path);
     lo.Hs = std::max(d.F, d.Fs);
@@ -478,7 +479,7 @@ lmoe_status lmoe_forward(const lmoe_config* cfg, const lmoe_weights* wt, const v
     }
     // top-k and permutation: for small batches inside the gate/up launch, else one launch for
     // T <= 64 (the TOPK stage events bracket both) or several
-    const float* logits2 = fused_d_router || d.G > 1 ? logits + (size_t)T * d.E : nullptr;
+    const float* logits2 = fused_d_router || d.G > 1 || T > kStreamMaxT ? logits + (size_t)T * d.E : nullptr;
     int2* rowinfo = lo.decode_path ? static_cast<int2*>(at(lo.rowinfo)) : nullptr;
     const ExpertRoute route{logits, logits2, lo.BM, has_shared, RouteOut{ids, wts, offsets, perm, inv, tiles, ntiles, rowinfo}};
     const bool route_in_experts = lo.decode_path && kRouteInExperts;

@@ -765,6 +765,15 @@ hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* b
     if (T <= kStreamMaxT)
         return launch_stream<kPW, kPKS, 1, StreamRouter, kProjChunk>(StreamRouter{z, Wr, br, T, E, L, logits},
                                                                      (int)cdiv(T, 16), E, s);
+    if (zhi && zlo) {
+        // the two halves' logits: logits (hi, + br) and logits + T * E (lo)
+        PipeRouter<PipeP> p{zhi, zlo, Wr, br, T, E, L, logits};
+        const long nn = cdiv(E, PipeP::kBN);
+        auto k = pipe_gemm_persistent<PipeP, PipeRouter<PipeP>>;
+        hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeP::kThreads), 2 * (long)cdiv(T, PipeP::kBM) * nn)),
+                           dim3(PipeP::kThreads), 0, s, p, (int)nn);
+        return last();
+    }
     TileRouter<TileL> p{z, Wr, br, T, E, L, logits, zhi, zlo};
     hipLaunchKernelGGL((tile_gemm_kernel<TileL, TileRouter<TileL>>), dim3(cdiv(E, TileL::kBN), cdiv(T, TileL::kBM)),
                        dim3(256), 0, s, p);

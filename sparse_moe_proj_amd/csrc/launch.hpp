@@ -77,7 +77,8 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
                             uint16_t* out16, hipStream_t s, uint16_t* out16lo = nullptr, uint16_t* out16h = nullptr,
                             const float* hnorm = nullptr);
 
-// zhi/zlo (T > kStreamMaxT, optional): the bf16 halves of z written by the D projection.
+// zhi/zlo (T > kStreamMaxT, optional): the bf16 halves of z written by the D projection; then
+// logits holds [2][T][E]: the hi half's logits (+ br) and the lo half's, which the top-k adds.
 hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* br, int T, int E, int L, float* logits,
                               hipStream_t s, const uint16_t* zhi = nullptr, const uint16_t* zlo = nullptr);
 

@@ -841,6 +841,77 @@ struct PipeProj : TileProj<S> {
     }
 };
 
+// Router logits of a batch from the two bf16 halves of z (hi = bf16(z), lo = bf16(z - hi)):
+// out[h][m][n] = z_h[m] . W[n] (+ bias[n] for h = 0); the top-k adds the two halves.  The halves
+// are two M ranges of one launch (tiles [0, mt) multiply hi, [mt, 2 mt) lo).
+template <class S>
+struct PipeRouter {
+    const uint16_t* zhi;  // [M][K] bf16
+    const uint16_t* zlo;  // [M][K] bf16
+    const uint16_t* W;    // [N][K] bf16 router rows
+    const float* bias;    // [N] or null
+    int M, N, K;
+    float* out;  // [2][M][N]
+    static constexpr bool kAPacked = false, kBPacked = false, kLdsStore = false;
+    struct Ctx { int m0, n0, h; };
+    __device__ int mt() const { return (M + S::kBM - 1) / S::kBM; }
+    __device__ int m_tiles() const { return 2 * mt(); }
+    __device__ bool tile(int bx, int by, Ctx& c) const {
+        const int t = mt();
+        c.h = bx >= t ? 1 : 0;
+        c.m0 = (bx - c.h * t) * S::kBM;
+        c.n0 = by * S::kBN;
+        return c.m0 < M && c.n0 < N;
+    }
+    __device__ int valid_rows(const Ctx& c) const { return min(S::kBM, M - c.m0); }
+    __device__ int k_stages(const Ctx&) const { return K / S::kBK; }
+    __device__ const uint8_t* a_base(const Ctx& c) const {
+        return reinterpret_cast<const uint8_t*>((c.h ? zlo : zhi) + (size_t)c.m0 * K);
+    }
+    __device__ const uint8_t* b_base(const Ctx& c) const { return reinterpret_cast<const uint8_t*>(W + (size_t)c.n0 * K); }
+    __device__ uint32_t src_a(const Ctx& c, int i, int lane) const {
+        const int r = min(rowmajor_row<S::kU>(i, lane), M - 1 - c.m0);
+        return rowmajor_off<S::kU>((uint32_t)r * K * 2, i, lane);
+    }
+    __device__ uint32_t src_b(const Ctx& c, int i, int lane) const {
+        const int r = min(rowmajor_row<S::kU>(i, lane), N - 1 - c.n0);
+        return rowmajor_off<S::kU>((uint32_t)r * K * 2, i, lane);
+    }
+    struct Prep {};
+    template <int MB>
+    __device__ Prep prep(const Ctx&, int, int) const { return {}; }
+    // four consecutive n of one row per lane and register group (16-byte stores when N is a
+    // multiple of 4, else one by one)
+    template <int MB, int NB>
+    __device__ __forceinline__ void store(const Ctx& c, f32x16 (&acc)[MB][NB], Prep, int rb, int cb, int lane) const {
+        const int h4 = 4 * (lane >> 5);
+        const bool vec = (N & 3) == 0;
+        const float* bz = c.h == 0 ? bias : nullptr;
+        static_for<MB>([&](auto i) {
+            const int m = c.m0 + rb + i * 32 + (lane & 31);
+            if (m < M) {
+                float* orow = out + ((size_t)c.h * M + m) * N;
+                static_for<NB>([&](auto j) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int n = c.n0 + cb + j * 32 + 8 * r4 + h4;
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * r4 + t] + (bz && n + t < N ? bz[n + t] : 0.f);
+                        if (vec) {
+                            if (n < N) *reinterpret_cast<float4*>(orow + n) = make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                if (n + t < N) orow[n + t] = v[t];
+                        }
+                    }
+                });
+            }
+        });
+    }
+};
+
 template <class S>
 struct PipeUp : TileUp<S> {
     using B = TileUp<S>;
