@@ -132,7 +132,9 @@ __device__ __forceinline__ void mx_prologue(const MxCopies<S>& c, int nk, uint4*
 }
 
 // The scale reads of one stage (2 A rows: one dword each; 2 B rows: the bytes of blocks g and
-// 2 + g), waited for in the same block (see lds_read_frags for why these reads are asm).
+// 2 + g), in one asm block that also waits for them (early-clobber outputs): the copies into the
+// other stage buffers are in flight meanwhile, and the block keeps the compiler from waiting for
+// them as well.
 __device__ __forceinline__ void mx_read_scales(uint32_t a0, uint32_t a1, uint32_t b00, uint32_t b01, uint32_t b10,
                                                uint32_t b11, uint32_t (&sa)[2], uint32_t (&sb)[2][2]) {
     __asm__ volatile(

@@ -131,65 +131,10 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint4*)p;
 }
 
-// Fragment reads of one k step: MB + NB ds_read_b128 in one block that also waits for them.
-// The copies into other stage buffers are still in flight at this point; keeping these reads out
-// of the compiler's view stops it from waiting for those copies (it cannot tell the buffers
-// apart across the K loop's back edge).  Outputs are early-clobber, so no register of an address
-// still to be used receives data, and the block returns only once every read has landed.
-template <int MB, int NB>
-__device__ __forceinline__ void lds_read_frags(const uint32_t (&aa)[MB], const uint32_t (&ba)[NB], uint4 (&af)[MB],
-                                               uint4 (&bf)[NB]) {
-    if constexpr (MB == 2 && NB == 4) {
-        __asm__ volatile(
-            "ds_read_b128 %0, %6\n\t"
-            "ds_read_b128 %1, %7\n\t"
-            "ds_read_b128 %2, %8\n\t"
-            "ds_read_b128 %3, %9\n\t"
-            "ds_read_b128 %4, %10\n\t"
-            "ds_read_b128 %5, %11\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
-            : "v"(aa[0]), "v"(aa[1]), "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]));
-    } else if constexpr (MB == 4 && NB == 2) {
-        __asm__ volatile(
-            "ds_read_b128 %0, %6\n\t"
-            "ds_read_b128 %1, %7\n\t"
-            "ds_read_b128 %2, %8\n\t"
-            "ds_read_b128 %3, %9\n\t"
-            "ds_read_b128 %4, %10\n\t"
-            "ds_read_b128 %5, %11\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1])
-            : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]), "v"(ba[0]), "v"(ba[1]));
-    } else if constexpr (MB == 2 && NB == 2) {
-        __asm__ volatile(
-            "ds_read_b128 %0, %4\n\t"
-            "ds_read_b128 %1, %5\n\t"
-            "ds_read_b128 %2, %6\n\t"
-            "ds_read_b128 %3, %7\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(bf[0]), "=&v"(bf[1])
-            : "v"(aa[0]), "v"(aa[1]), "v"(ba[0]), "v"(ba[1]));
-    } else {
-        static_assert(MB == 4 && NB == 4, "wave tiles of 64 or 128 rows and columns");
-        __asm__ volatile(
-            "ds_read_b128 %0, %8\n\t"
-            "ds_read_b128 %1, %9\n\t"
-            "ds_read_b128 %2, %10\n\t"
-            "ds_read_b128 %3, %11\n\t"
-            "ds_read_b128 %4, %12\n\t"
-            "ds_read_b128 %5, %13\n\t"
-            "ds_read_b128 %6, %14\n\t"
-            "ds_read_b128 %7, %15\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]),
-              "=&v"(bf[3])
-            : "v"(aa[0]), "v"(aa[1]), "v"(aa[2]), "v"(aa[3]), "v"(ba[0]), "v"(ba[1]), "v"(ba[2]), "v"(ba[3]));
-    }
-}
-
-// LDS writes and reads of a tile's staged output (outside the K loop).  The reads wait for
-// themselves in the same block (early-clobber outputs), for the reason given above.
+// LDS writes and reads of a tile's staged output (outside the K loop).  The reads run while the
+// next tile's first copies fill another stage buffer; in asm, with their wait in the same block
+// (early-clobber outputs, so no address register still in use receives data), they keep the
+// compiler from waiting for those copies as well.
 __device__ __forceinline__ void lds_write_b64(uint32_t addr, uint2 v) {
     __asm__ volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
@@ -348,27 +293,54 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
     const int fr = lane & 31;
     const int fq = lane >> 5;
     const int nvb = min(S::kMB, max(0, (mrows - wm * S::kWM + 31) / 32));  // 32-row blocks with data
-    auto compute = [&](const uint4* buf) {
-        if (nvb == 0) return;
-        const uint32_t A = lds_addr(buf);
-        const uint32_t B = A + S::kBM * S::kU * 16;
+    // A tile whose every 32-row block holds data (all but a segment's last tile) multiplies with
+    // plain LDS loads, which the compiler waits for exactly (lgkmcnt): the first k step's
+    // fragments are requested right after the barrier, ahead of the next stage's copies, and
+    // each k step's MFMAs are interleaved with the loads of the next k step's fragments.
+    auto frag_a = [&](int i, int ks) { return frag_pos<P::kAPacked, S::kU>(wm * S::kWM + i * 32 + fr, 2 * ks + fq); };
+    auto frag_b = [&](int j, int ks) {
+        return S::kBM * S::kU + frag_pos<P::kBPacked, S::kU>(wn * S::kWN + j * 32 + fr, 2 * ks + fq);
+    };
+    constexpr int NKS = S::kBK / 16;
+    // One stage for a wave whose first NV 32-row blocks hold data (NV = kMB but in a segment's
+    // last tile), without branches: the A fragments of the other blocks are neither read nor
+    // multiplied, and a wave with NV = 0 only issues its share of the copies.
+    auto step = [&](auto nvc, const uint4* buf, uint4* nbuf, int nkt) {
+        constexpr int NV = decltype(nvc)::value;
+        // fa[i] is reloaded with the next k step's fragment as soon as its MFMAs are issued; the
+        // B fragments, which every MFMA of a k step reads, alternate between two sets
+        uint4 fa[S::kMB], fb[2][S::kNB];
+        if constexpr (NV > 0) {
 #pragma unroll
-        for (int ks = 0; ks < S::kBK / 16; ++ks) {
-            const int u = 2 * ks + fq;
-            uint32_t aa[S::kMB], ba[S::kNB];
+            for (int i = 0; i < NV; ++i) fa[i] = buf[frag_a(i, 0)];
 #pragma unroll
-            for (int i = 0; i < S::kMB; ++i)
-                aa[i] = A + 16 * frag_pos<P::kAPacked, S::kU>(wm * S::kWM + i * 32 + fr, u);
+            for (int j = 0; j < S::kNB; ++j) fb[0][j] = buf[frag_b(j, 0)];
+        }
+        if (nkt >= 0) pipe_issue<S, P>(c, nbuf, nkt, wave);
+        if constexpr (NV > 0) {
+            static_for<NKS>([&](auto ksc) {
+                constexpr int ks = decltype(ksc)::value, cur = ks & 1, nxt = cur ^ 1;
+                constexpr bool more = ks + 1 < NKS;
+                if constexpr (more)
 #pragma unroll
-            for (int j = 0; j < S::kNB; ++j)
-                ba[j] = B + 16 * frag_pos<P::kBPacked, S::kU>(wn * S::kWN + j * 32 + fr, u);
-            uint4 af[S::kMB], bfv[S::kNB];
-            lds_read_frags<S::kMB, S::kNB>(aa, ba, af, bfv);
+                    for (int j = 0; j < S::kNB; ++j) fb[nxt][j] = buf[frag_b(j, ks + 1)];
 #pragma unroll
-            for (int i = 0; i < S::kMB; ++i)
-                if (i < nvb)
+                for (int i = 0; i < NV; ++i) {
 #pragma unroll
-                    for (int j = 0; j < S::kNB; ++j) acc[i][j] = mfma32(bfv[j], af[i], acc[i][j]);
+                    for (int j = 0; j < S::kNB; ++j) acc[i][j] = mfma32(fb[cur][j], fa[i], acc[i][j]);
+                    if constexpr (more) fa[i] = buf[frag_a(i, ks + 1)];
+                }
+            });
+            // order of the region after the copies, per k step: the next B fragments, then each
+            // row block's MFMAs followed by the load of its next A fragment
+            static_for<NKS>([&](auto ksc) {
+                constexpr bool more = decltype(ksc)::value + 1 < NKS;
+                if constexpr (more) __builtin_amdgcn_sched_group_barrier(0x100, S::kNB, 0);  // DS read
+                static_for<NV>([&](auto) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, S::kNB, 0);  // MFMA
+                    if constexpr (more) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                });
+            });
         }
     };
 
@@ -376,28 +348,34 @@ __device__ __forceinline__ void pipe_k_loop(const PipeCopies<S>& c, int nk, f32x
     if (kt + S_ < nk) {                                                             \
         wait_stage<LPS, NS>(min(nk - 1 - (kt + S_), NS - 2));                       \
         stage_barrier();                                                            \
-        if (kt + S_ + NS - 1 < nk) pipe_issue<S, P>(c, NEXT_, kt + S_ + NS - 1, wave); \
-        compute(CUR_);                                                              \
+        const int nkt = kt + S_ + NS - 1 < nk ? kt + S_ + NS - 1 : -1;              \
+        step(nvc, CUR_, NEXT_, nkt);                                                \
     }
-    if constexpr (NS == 4) {
-        for (int kt = 0; kt < nk; kt += 4) {
-            LMOE_PIPE_STEP(0, st0, st3)
-            LMOE_PIPE_STEP(1, st1, st0)
-            LMOE_PIPE_STEP(2, st2, st1)
-            LMOE_PIPE_STEP(3, st3, st2)
+    // the number of data blocks is fixed for the tile: one compact K loop per value
+    auto run = [&](auto nvc) {
+        if constexpr (NS == 4) {
+            for (int kt = 0; kt < nk; kt += 4) {
+                LMOE_PIPE_STEP(0, st0, st3)
+                LMOE_PIPE_STEP(1, st1, st0)
+                LMOE_PIPE_STEP(2, st2, st1)
+                LMOE_PIPE_STEP(3, st3, st2)
+            }
+        } else if constexpr (NS == 3) {
+            for (int kt = 0; kt < nk; kt += 3) {
+                LMOE_PIPE_STEP(0, st0, st2)
+                LMOE_PIPE_STEP(1, st1, st0)
+                LMOE_PIPE_STEP(2, st2, st1)
+            }
+        } else {
+            for (int kt = 0; kt < nk; kt += 2) {
+                LMOE_PIPE_STEP(0, st0, st1)
+                LMOE_PIPE_STEP(1, st1, st0)
+            }
         }
-    } else if constexpr (NS == 3) {
-        for (int kt = 0; kt < nk; kt += 3) {
-            LMOE_PIPE_STEP(0, st0, st2)
-            LMOE_PIPE_STEP(1, st1, st0)
-            LMOE_PIPE_STEP(2, st2, st1)
-        }
-    } else {
-        for (int kt = 0; kt < nk; kt += 2) {
-            LMOE_PIPE_STEP(0, st0, st1)
-            LMOE_PIPE_STEP(1, st1, st0)
-        }
-    }
+    };
+    static_for<S::kMB + 1>([&](auto nvc) {
+        if (nvb == decltype(nvc)::value) run(nvc);
+    });
 #undef LMOE_PIPE_STEP
 }
 
