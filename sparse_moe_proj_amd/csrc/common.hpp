@@ -133,25 +133,24 @@ __device__ __forceinline__ uint4 mxfp4_to_bf16x8(uint32_t nib8, uint32_t scale_b
     return fp4x8_to_bf16x8(nib8, e8m0_to_f32(scale_byte));
 }
 
-// 8 E2M1 nibbles -> 8 fp16 values times a block scale (fp16 pair `scale2`, both halves equal),
-// by byte lookup: the fp16 of an E2M1 magnitude has a zero low byte, and its high byte for codes
-// 0..7 is 00 38 3C 3E 40 42 44 46; v_perm picks the high bytes of four codes at once (the codes
-// of even and of odd positions), the sign bits are or-ed in, a second round of v_perm interleaves
-// them into fp16 pairs, and one packed fp16 multiply per pair applies the scale.  Exact while the
-// scaled values lie in fp16's normal range (NVFP4 always; MXFP4 for scales in [2^-13, 2^13]).
+// 8 E2M1 nibbles (value i in bits 4i .. 4i + 3) -> 8 fp16 values (pairs in value order) times a
+// power of two, by gfx950's conversion instruction (one per byte: the lower nibble becomes the
+// low half).  The instruction applies only the exponent of its fp32 scale operand, so `pow2` must
+// be a power of two (an E8M0 block scale); the results are then exact, fp16 subnormals included
+// (checked against a table of every byte value, scales 2^-15 .. 1).
+__device__ __forceinline__ uint4 fp4x8_to_f16x8_pow2(uint32_t w, float pow2) {
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 0)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 2)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, 3)));
+}
+
+// 8 E2M1 nibbles -> 8 fp16 values times any block scale (fp16 pair `scale2`, both halves equal):
+// the exact fp16 E2M1 values, then one packed fp16 multiply per pair.
 __device__ __forceinline__ uint4 fp4x8_to_f16x8(uint32_t w, uint32_t scale2) {
-    constexpr uint32_t lo_tab = 0x3E3C3800u, hi_tab = 0x46444240u;
-    const uint32_t me = w & 0x07070707u, mo = (w >> 4) & 0x07070707u;
-    uint32_t he = __builtin_amdgcn_perm(hi_tab, lo_tab, me);
-    uint32_t ho = __builtin_amdgcn_perm(hi_tab, lo_tab, mo);
-    he |= (w << 4) & 0x80808080u;
-    ho |= w & 0x80808080u;
-    uint32_t o[4];
-    o[0] = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
-    o[1] = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
-    o[2] = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
-    o[3] = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
+    const uint4 v = fp4x8_to_f16x8_pow2(w, 1.f);
     const f16x2 sc = __builtin_bit_cast(f16x2, scale2);
+    uint32_t o[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, o[i]) * sc);
     return make_uint4(o[0], o[1], o[2], o[3]);

@@ -511,7 +511,7 @@ struct Fp4Rows {
     template <bool>
     __device__ static uint4 frag(const WRaw& w, int t) {
         const uint32_t nib = t == 0 ? w.n.x : t == 1 ? w.n.y : t == 2 ? w.n.z : w.n.w;
-        if constexpr (Q == 1) return fp4x8_to_f16x8(nib, f16x2_splat(e8m0_to_f32(w.s)));
+        if constexpr (Q == 1) return fp4x8_to_f16x8_pow2(nib, e8m0_to_f32(w.s));
         // steps 0, 1 hold the first block of 16 values, steps 2, 3 the second
         const uint32_t s2 = e4m3x2_to_f16x2(w.s);
         return fp4x8_to_f16x8(nib, __builtin_amdgcn_perm(s2, s2, t & 2 ? 0x03020302u : 0x01000100u));
