@@ -554,6 +554,13 @@ using PipeP = PipeShape<LMOE_PROJ_PIPE_M, LMOE_PROJ_PIPE_N, LMOE_PROJ_PIPE_NS, L
 #define LMOE_BIG_NS 2
 #endif
 using PipeB = PipeShape<256, LMOE_PIPE_N, LMOE_BIG_NS, LMOE_BIG_WR, LMOE_BIG_WC, LMOE_BIG_BK>;
+// cost of a round of 256-row tiles over the CUs, in hundredths of a round of 128-row tiles
+// (measured at 16384 x 1792 x 2560: 102 against 61 us per round; at 160 the U projection of
+// 16384 tokens, 3 rounds against 5, takes the 256-row tiles: 160 against 167 us)
+#ifndef LMOE_BIG_ROUND_COST
+#define LMOE_BIG_ROUND_COST 160
+#endif
+constexpr long kBigRoundCost = LMOE_BIG_ROUND_COST;
 static_assert(PipeB::kBN == PipeL::kBN, "big and small tiles cover the same columns per tile");
 
 // Persistent launch: at most LMOE_STREAM_GRID workgroups walk max_tiles x row-group items.
@@ -737,11 +744,11 @@ hipError_t launch_proj_bf16(const uint16_t* x, const uint16_t* W, int T, int N, 
                                                                    (int)cdiv(T, 16), N, s);
     if (LMOE_PIPE_PROJ) {
         // 256-row tiles halve the bytes per flop but come in half as many: take them when the
-        // rounds of tiles over the CUs, weighted by a 256-row tile's measured cost (1.67 times a
-        // 128-row tile's: 102 vs 61 us per round at 16384 x 1792 x 2560), come out lower
+        // rounds of tiles over the CUs, weighted by a round of 256-row tiles' cost (kBigRoundCost),
+        // come out lower
         const long nn = cdiv(N, PipeP::kBN), cus = cu_count();
         const long r1 = cdiv(cdiv(T, PipeP::kBM) * nn, cus), r2 = cdiv(cdiv(T, PipeB::kBM) * nn, cus);
-        if (PipeB::kBN == PipeP::kBN && PipeB::kBM > PipeP::kBM && 167 * r2 < 100 * r1) {
+        if (PipeB::kBN == PipeP::kBN && PipeB::kBM > PipeP::kBM && kBigRoundCost * r2 < 100 * r1) {
             PipeProj<PipeB> p{{x, W, T, N, K, mode, out32, out16, out16lo}};
             auto k = pipe_gemm_persistent<PipeB, PipeProj<PipeB>>;
             hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeB::kThreads), (long)cdiv(T, PipeB::kBM) * nn)),
@@ -766,9 +773,18 @@ hipError_t launch_router_bf16(const float* z, const uint16_t* Wr, const float* b
         return launch_stream<kPW, kPKS, 1, StreamRouter, kProjChunk>(StreamRouter{z, Wr, br, T, E, L, logits},
                                                                      (int)cdiv(T, 16), E, s);
     if (zhi && zlo) {
-        // the two halves' logits: logits (hi, + br) and logits + T * E (lo)
+        // the two halves' logits: logits (hi, + br) and logits + T * E (lo); 256-row tiles when
+        // their rounds over the CUs come out cheaper, by the projections' measured weighting
+        const long nn = cdiv(E, PipeP::kBN), cus = cu_count();
+        const long r1 = cdiv(2 * cdiv(T, PipeP::kBM) * nn, cus), r2 = cdiv(2 * cdiv(T, PipeB::kBM) * nn, cus);
+        if (PipeB::kBN == PipeP::kBN && PipeB::kBM > PipeP::kBM && kBigRoundCost * r2 < 100 * r1) {
+            PipeRouter<PipeB> p{zhi, zlo, Wr, br, T, E, L, logits};
+            auto k = pipe_gemm_persistent<PipeB, PipeRouter<PipeB>>;
+            hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeB::kThreads), 2 * (long)cdiv(T, PipeB::kBM) * nn)),
+                               dim3(PipeB::kThreads), 0, s, p, (int)nn);
+            return last();
+        }
         PipeRouter<PipeP> p{zhi, zlo, Wr, br, T, E, L, logits};
-        const long nn = cdiv(E, PipeP::kBN);
         auto k = pipe_gemm_persistent<PipeP, PipeRouter<PipeP>>;
         hipLaunchKernelGGL(k, dim3(std::min<long>(resident_blocks(k, PipeP::kThreads), 2 * (long)cdiv(T, PipeP::kBM) * nn)),
                            dim3(PipeP::kThreads), 0, s, p, (int)nn);
