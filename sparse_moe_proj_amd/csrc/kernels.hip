@@ -282,39 +282,41 @@ __device__ __forceinline__ void y8_f32(const Y8<BF16>& r, float (&v)[8]) {
 // grid (L / 2048, min(T, 65535), expert groups), tokens t = blockIdx.y, + gridDim.y, ...: group
 // g's merged row m_g goes to columns g * L .. of m [T][groups * L]; a slot counts for group
 // ids / Eg (ids null: one group), the shared expert for group 0.  A thread sums 8 columns: the
-// shared row, then the slots in order (fp32); the rows of up to 8 slots are requested before
-// any of them is added, so their loads are in flight together.
+// shared row, then the slots in order (fp32); all of a token's rows are requested (16-byte
+// loads) before the first is added, so their loads are in flight together.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ Y, const float* __restrict__ w, int T,
                                                       int k, int L, int has_shared, void* __restrict__ m,
                                                       const int32_t* __restrict__ ids, int Eg) {
-    constexpr int CH = 8;
+    constexpr int KM = 16;  // top_k <= 16
     const int g = blockIdx.z;
     const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
     if (c >= L) return;
     const size_t mp = (size_t)gridDim.z * L;
     for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        // every row of the token (shared expert, then the slots) is requested before any is used,
+        // so a token costs one round trip; the sum keeps the order shared, slot 0, 1, ...
+        const bool sh = has_shared && g == 0;
+        Y8<OUT_BF16> rsh;
+        if (sh) rsh = load_y8<OUT_BF16>(Y, ((size_t)T * k + t) * L + c);
+        Y8<OUT_BF16> raw[KM];
+        float ws[KM];
+        bool use[KM];
+#pragma unroll
+        for (int s = 0; s < KM; ++s) {
+            use[s] = s < k && (!ids || ids[(size_t)t * k + s] / Eg == g);
+            ws[s] = use[s] ? w[(size_t)t * k + s] : 0.f;
+            if (use[s]) raw[s] = load_y8<OUT_BF16>(Y, ((size_t)t * k + s) * L + c);
+        }
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (has_shared && g == 0) y8_f32<OUT_BF16>(load_y8<OUT_BF16>(Y, ((size_t)T * k + t) * L + c), acc);
-        for (int s0 = 0; s0 < k; s0 += CH) {
-            Y8<OUT_BF16> raw[CH];
-            float ws[CH];
-            bool use[CH];
+        if (sh) y8_f32<OUT_BF16>(rsh, acc);
 #pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                const int s = s0 + i;
-                use[i] = s < k && (!ids || ids[(size_t)t * k + s] / Eg == g);
-                ws[i] = use[i] ? w[(size_t)t * k + s] : 0.f;
-                if (use[i]) raw[i] = load_y8<OUT_BF16>(Y, ((size_t)t * k + s) * L + c);
-            }
+        for (int s = 0; s < KM; ++s) {
+            if (!use[s]) continue;
+            float y[8];
+            y8_f32<OUT_BF16>(raw[s], y);
 #pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                if (!use[i]) continue;
-                float y[8];
-                y8_f32<OUT_BF16>(raw[i], y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += ws[i] * y[e];
-            }
+            for (int e = 0; e < 8; ++e) acc[e] += ws[s] * y[e];
         }
         if (OUT_BF16) {
             const uint4 o = make_uint4(pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]), pack_bf2(acc[4], acc[5]),
