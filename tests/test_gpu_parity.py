@@ -286,6 +286,56 @@ def test_decode_nvfp4_t8_full(ws):
     _workload_case("decode_nvfp4_t8", 8, ws)
 
 
+def _scale_bf16(x, s):
+    """bf16 bits x times the power of two s (exact: only the exponents change)."""
+    f = (x.astype(np.uint32) << 16).view(np.float32) * np.float32(s)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _routed_swiglu_max(lw, x):
+    """Largest |SiLU(z G_e) * (z V_e)| over every token's routed experts (oracle, float64): the
+    magnitudes the 4-bit small-batch path holds in fp16."""
+    L = oracle.Layer(lw)
+    z = oracle.decode(x, "bf16") @ L.D.T
+    ids = oracle.route(z, L.Wr, L.br, lw.shape.top_k, lw.shape.groups)[0]
+    m = 0.0
+    for t in range(z.shape[0]):
+        for e in ids[t]:
+            g, u, _ = L.expert(int(e))
+            with np.errstate(over="ignore"):  # exp(-v) of a large negative gate: SiLU is -0 there
+                m = max(m, float(np.abs(oracle.silu(z[t] @ g.T) * (z[t] @ u.T)).max()))
+    return m
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_small_4bit_large_activations(fmt, ws):
+    """Tokens 32 times larger: z and SiLU(g) * u run to thousands, still inside fp16, which the
+    4-bit small-batch path carries them in; outputs within the 4-bit tolerance."""
+    wl, lw = small_layer(SMALL_MX, "bf16", "bf16", fmt)
+    x = _scale_bf16(gen.make_tokens(wl, T=8, salt=5), 32.0)
+    m = _routed_swiglu_max(lw, x)
+    assert 1e3 < m < 65504, m
+    out = run_forward(DeviceLayer(lw, act="bf16"), upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    check_block(lw, x, "bf16", out, label=f"small_{fmt} tokens x32 (max |SiLU(g) u| {m:.0f})")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_small_4bit_fp16_saturation_stays_finite(fmt, ws):
+    """Tokens 8192 times larger: SiLU(g) * u of the routed experts exceeds fp16's 65504, and the
+    4-bit small-batch path saturates it instead of overflowing, so every output stays finite (the
+    values lose their size there and are not compared)."""
+    wl, lw = small_layer(SMALL_MX, "bf16", "bf16", fmt)
+    x = _scale_bf16(gen.make_tokens(wl, T=8, salt=5), 8192.0)
+    m = _routed_swiglu_max(lw, x)
+    assert m > 65504, m
+    out = run_forward(DeviceLayer(lw, act="bf16"), upload_tokens(x), ws)
+    torch.cuda.synchronize()
+    y = oracle.decode(host(out["y"]), "bf16")
+    log(f"[small_{fmt} tokens x8192] max |SiLU(g) u| {m:.3e}, max |y| {np.abs(y).max():.3e}")
+    assert np.all(np.isfinite(y))
+
+
 @pytest.mark.parametrize("T", [7, 70])
 def test_small_f32(T, ws):
     wl, lw = small_layer(SMALL, "f32", "f32", "f32")
