@@ -252,15 +252,22 @@ template <bool BF16>
 struct Y8 {
     typename std::conditional<BF16, uint4, float4>::type a, b;
 };
+// The rows are read once per step: non-temporal loads, so that they do not push the merged rows
+// (read next by the U projection) out of the caches (16K tokens: combine 144 -> 110 us, U 158 ->
+// 152 us against plain loads).
 template <bool BF16>
 __device__ __forceinline__ Y8<BF16> load_y8(const void* Y, size_t off) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
     Y8<BF16> r;
     if constexpr (BF16) {
-        r.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Y) + off);
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Y) + off));
+        r.a = make_uint4(v.x, v.y, v.z, v.w);
     } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(Y) + off);
-        r.a = p[0];
-        r.b = p[1];
+        const f32x4v* p = reinterpret_cast<const f32x4v*>(static_cast<const float*>(Y) + off);
+        const f32x4v v0 = __builtin_nontemporal_load(p), v1 = __builtin_nontemporal_load(p + 1);
+        r.a = make_float4(v0.x, v0.y, v0.z, v0.w);
+        r.b = make_float4(v1.x, v1.y, v1.z, v1.w);
     }
     return r;
 }

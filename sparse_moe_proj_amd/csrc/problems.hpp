@@ -15,6 +15,23 @@
 namespace lmoe {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Non-temporal 16-byte load, for data streamed once per step: the expert weight rows of the
+// small-batch kernels (gate/up and down).  Plain loads of those rows left the caches to them and
+// pushed out what the step reads again (decode_t8: gate/up 37.8 -> 34.7 us, down 20.0 -> 19.1 us,
+// step 73 -> 68 us); the D and U projections' rows gained nothing from it and keep plain loads.
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+#ifndef LMOE_WEIGHT_NT
+#define LMOE_WEIGHT_NT 1
+#endif
+#if LMOE_WEIGHT_NT
+#define LMOE_WLOAD ld16_nt
+#else
+#define LMOE_WLOAD ld16
+#endif
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
 
 // 8 consecutive fp32 values -> hi (lo = false) or lo (lo = true) halves as 8 bf16.
@@ -503,9 +520,14 @@ struct Fp4Rows {
     template <bool>
     __device__ static WRaw load(const Row& r, int g, int kq) {
         WRaw w;
-        w.n = ld16(r.p + g * 1024 + kq * 256);
+        w.n = LMOE_WLOAD(r.p + g * 1024 + kq * 256);
         const uint8_t* sp = r.sc + (g * 64 + kq * 16) * kSB;
+#if LMOE_WEIGHT_NT
+        w.s = Q == 1 ? (uint32_t)__builtin_nontemporal_load(sp)
+                     : (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sp));
+#else
         w.s = Q == 1 ? (uint32_t)*sp : (uint32_t)*reinterpret_cast<const uint16_t*>(sp);
+#endif
         return w;
     }
     template <bool>
@@ -529,7 +551,7 @@ struct ExpertRows<0> {
         return Row{m.p + (size_t)(n >> 4) * 16 * K + (n & 15) * 8};
     }
     template <bool>
-    __device__ static WRaw load(const Row& r, int s, int kq) { return ld16(r.p + s * 512 + kq * 128); }
+    __device__ static WRaw load(const Row& r, int s, int kq) { return LMOE_WLOAD(r.p + s * 512 + kq * 128); }
     template <bool>
     __device__ static uint4 frag(const WRaw& w, int) { return w; }
 };
